@@ -1,0 +1,12 @@
+"""gated_delta_rule_decay_amd: the gated delta rule-2 (GDN-2) token mixer on MI355X.
+
+The compute path is a HIP library for gfx950 (``libgdn2.so``, C ABI declared
+in ``include/gdn2.h``): a chunkwise-parallel forward and an O(1)-memory
+recurrent decode step.  ``chunk_fwd`` and ``recurrent_step`` below only
+marshal torch tensors into that ABI; importing this package does not load
+the library, calling either function does (and fails loudly if it is not
+built).
+"""
+from .binding import chunk_fwd, recurrent_step, chunk_fwd_workspace, library_path, abi_version  # noqa: F401
+
+__all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_workspace", "library_path", "abi_version"]

@@ -1,0 +1,211 @@
+"""Thin Python binding of the C ABI in include/gdn2.h (argument marshalling only).
+
+``chunk_fwd`` and ``recurrent_step`` take torch CUDA (HIP) tensors, check
+dtype / shape / device / contiguity, and pass raw device pointers plus
+torch's current stream to ``libgdn2.so``.  Every step of the computation runs
+in the library's gfx950 kernels; there is no CPU or torch fallback: if the
+library is missing or a call fails, these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libgdn2.so")
+
+GDN2_F32, GDN2_BF16 = 0, 1
+GDN2_GATE_HEAD, GDN2_GATE_KEY = 0, 1
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_UNSUPPORTED",
+          5: "ERR_ALIAS", 6: "ERR_WORKSPACE", 7: "ERR_HIP"}
+
+# Every entry point include/gdn2.h declares.
+EXPORTS = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace",
+           "gdn2_chunk_fwd", "gdn2_recurrent_step")
+
+
+class Gdn2Desc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("heads", ctypes.c_int64),
+        ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("chunk", ctypes.c_int64),
+        ("qkv_dtype", ctypes.c_int32), ("decay_kind", ctypes.c_int32),
+        ("erase_kind", ctypes.c_int32), ("write_kind", ctypes.c_int32),
+        ("tie_write_to_erase", ctypes.c_int32), ("q_scale", ctypes.c_float),
+    ]
+
+
+class Gdn2Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({_status_str(status)})")
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libgdn2.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise ImportError(
+                    f"{_LIB_PATH} is missing: build it with "
+                    "`python -m gated_delta_rule_decay_amd.build`")
+            lib = ctypes.CDLL(_LIB_PATH)
+            vp, fp = ctypes.c_void_p, ctypes.c_void_p
+            dp = ctypes.POINTER(Gdn2Desc)
+            lib.gdn2_abi_version.restype = ctypes.c_int
+            lib.gdn2_abi_version.argtypes = []
+            lib.gdn2_status_str.restype = ctypes.c_char_p
+            lib.gdn2_status_str.argtypes = [ctypes.c_int]
+            lib.gdn2_chunk_fwd_workspace.restype = ctypes.c_int
+            lib.gdn2_chunk_fwd_workspace.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
+            lib.gdn2_chunk_fwd.restype = ctypes.c_int
+            lib.gdn2_chunk_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp,
+                                           ctypes.c_size_t, vp]
+            lib.gdn2_recurrent_step.restype = ctypes.c_int
+            lib.gdn2_recurrent_step.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp]
+            _lib = lib
+    return _lib
+
+
+def _status_str(status: int) -> str:
+    try:
+        return load_library().gdn2_status_str(int(status)).decode()
+    except Exception:  # pragma: no cover
+        return "?"
+
+
+def abi_version() -> int:
+    return int(load_library().gdn2_abi_version())
+
+
+def make_desc(batch, seqlen, heads, dk, dv, chunk=64, qkv_dtype=GDN2_BF16,
+              decay_kind=GDN2_GATE_KEY, erase_kind=GDN2_GATE_KEY, write_kind=GDN2_GATE_KEY,
+              tied=False, q_scale=1.0) -> Gdn2Desc:
+    return Gdn2Desc(batch, seqlen, heads, dk, dv, chunk, qkv_dtype, decay_kind, erase_kind,
+                    write_kind, 1 if tied else 0, q_scale)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(t, name, shape, dtypes, device):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _gate_kind(g, tok_shape, dk, name):
+    if g.dim() == len(tok_shape) + 1 and g.shape[-1] == dk:
+        return GDN2_GATE_KEY, tuple(tok_shape) + (dk,)
+    if g.dim() == len(tok_shape):
+        return GDN2_GATE_HEAD, tuple(tok_shape)
+    raise ValueError(f"{name} shape {tuple(g.shape)} is neither {tuple(tok_shape) + (dk,)} "
+                     f"nor {tuple(tok_shape)}")
+
+
+def _desc_for(q, k, v, log_decay, erase, write, tok_shape, batch, seqlen, heads, chunk, q_scale):
+    import torch
+    dk, dv = k.shape[-1], v.shape[-1]
+    dev = k.device
+    if k.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    for t, n, d in ((q, "q", dk), (k, "k", dk), (v, "v", dv)):
+        _check(t, n, tuple(tok_shape) + (d,), (k.dtype,), dev)
+    la_kind, la_shape = _gate_kind(log_decay, tok_shape, dk, "log_decay")
+    eb_kind, eb_shape = _gate_kind(erase, tok_shape, dk, "erase")
+    _check(log_decay, "log_decay", la_shape, (torch.float32,), dev)
+    _check(erase, "erase", eb_shape, (torch.float32,), dev)
+    wr_kind = eb_kind
+    if write is not None:
+        wr_kind, wr_shape = _gate_kind(write, tok_shape, dk, "write")
+        _check(write, "write", wr_shape, (torch.float32,), dev)
+    return make_desc(batch, seqlen, heads, dk, dv, chunk,
+                     GDN2_BF16 if k.dtype == torch.bfloat16 else GDN2_F32,
+                     la_kind, eb_kind, wr_kind, write is None, q_scale)
+
+
+def chunk_fwd_workspace(desc: Gdn2Desc) -> int:
+    n = ctypes.c_size_t(0)
+    st = load_library().gdn2_chunk_fwd_workspace(ctypes.byref(desc), ctypes.byref(n))
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_chunk_fwd_workspace")
+    return int(n.value)
+
+
+def chunk_fwd(q, k, v, log_decay, erase, write=None, state0=None, chunk=64, q_scale=1.0,
+              out=None, state_out=None, return_state=True):
+    """Chunkwise GDN-2 forward on the GPU.
+
+    q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32, one dtype); gates fp32
+    [B,T,H,dk] or [B,T,H]; write None ties it to erase; state0 [B,H,dk,dv]
+    fp32 or None.  Returns (o [B,T,H,dv] fp32, final state or None).
+    """
+    import torch
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    desc = _desc_for(q, k, v, log_decay, erase, write, (B, T, H), B, T, H, chunk, q_scale)
+    dev = k.device
+    if state0 is not None:
+        _check(state0, "state0", (B, H, dk, dv), (torch.float32,), dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _check(out, "out", (B, T, H, dv), (torch.float32,), dev)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif state_out is not None:
+        _check(state_out, "state_out", (B, H, dk, dv), (torch.float32,), dev)
+    ws_bytes = chunk_fwd_workspace(desc)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    st = load_library().gdn2_chunk_fwd(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(erase),
+        _ptr(write), _ptr(state0), _ptr(out), _ptr(state_out), _ptr(ws), ws_bytes, _stream())
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_chunk_fwd")
+    return out, state_out
+
+
+def recurrent_step(q, k, v, log_decay, erase, write, state, q_scale=1.0, out=None):
+    """One decode step for N sequences; updates ``state`` [N,H,dk,dv] in place.
+
+    q, k [N,H,dk], v [N,H,dv]; gates [N,H,dk] or [N,H]; write None = tied.
+    Returns o [N,H,dv] fp32.
+    """
+    import torch
+    N, H, dk = k.shape
+    dv = v.shape[-1]
+    desc = _desc_for(q, k, v, log_decay, erase, write, (N, H), N, 1, H, 64, q_scale)
+    _check(state, "state", (N, H, dk, dv), (torch.float32,), k.device)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=torch.float32, device=k.device)
+    else:
+        _check(out, "out", (N, H, dv), (torch.float32,), k.device)
+    st = load_library().gdn2_recurrent_step(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(erase),
+        _ptr(write), _ptr(state), _ptr(out), _stream())
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_recurrent_step")
+    return out

@@ -1,0 +1,196 @@
+// api.hip -- the C ABI declared in include/gdn2.h: host-side validation,
+// then dispatch to the gfx950 kernels on the caller's stream.
+//
+// Validation never touches the GPU, so every error path is reachable (and
+// tested) on a machine without one.  No allocation, no global mutable state.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "gdn2.h"
+#include "kernels.h"
+
+namespace {
+
+using gdn2::ChunkArgs;
+using gdn2::StepArgs;
+
+struct Span {
+    uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+
+Span span_of(const void *p, int64_t bytes) {
+    Span s;
+    if (p && bytes > 0) {
+        s.lo = reinterpret_cast<uintptr_t>(p);
+        s.hi = s.lo + static_cast<uintptr_t>(bytes);
+    }
+    return s;
+}
+
+bool overlap(const Span &a, const Span &b) {
+    return a.lo != a.hi && b.lo != b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+// a*b*... with an overflow check against int64 (result in *out).
+bool mul_ok(int64_t a, int64_t b, int64_t *out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+gdn2_status check_common(const gdn2_desc *d) {
+    if (!d) return GDN2_ERR_NULL;
+    if (d->batch < 0 || d->seqlen < 0 || d->heads < 1 || d->dk < 1 || d->dv < 1)
+        return GDN2_ERR_SHAPE;
+    if (d->qkv_dtype != GDN2_F32 && d->qkv_dtype != GDN2_BF16) return GDN2_ERR_DTYPE;
+    auto kind_ok = [](int32_t k) { return k == GDN2_GATE_HEAD || k == GDN2_GATE_KEY; };
+    if (!kind_ok(d->decay_kind) || !kind_ok(d->erase_kind) ||
+        (!d->tie_write_to_erase && !kind_ok(d->write_kind)))
+        return GDN2_ERR_SHAPE;
+    if (d->dk > 128 || d->dv > 128) return GDN2_ERR_UNSUPPORTED;
+    // every tensor's byte size must fit in int64
+    int64_t x;
+    const int64_t dmax = d->dk > d->dv ? d->dk : d->dv;
+    if (!mul_ok(d->batch, d->seqlen, &x) || !mul_ok(x, d->heads, &x) || !mul_ok(x, dmax, &x) ||
+        !mul_ok(x, 8, &x))
+        return GDN2_ERR_SHAPE;
+    if (!mul_ok(d->batch, d->heads, &x) || !mul_ok(x, d->dk, &x) || !mul_ok(x, d->dv, &x) ||
+        !mul_ok(x, 8, &x))
+        return GDN2_ERR_SHAPE;
+    return GDN2_OK;
+}
+
+struct Sizes {
+    int64_t tok;     // B*T*H token-heads
+    int64_t qk, v;   // bytes of q (=k) and v
+    int64_t la, eb, wr;
+    int64_t o, st;   // bytes of o and of one state tensor
+};
+
+Sizes sizes_of(const gdn2_desc *d, int64_t T) {
+    Sizes s;
+    const int64_t esz = d->qkv_dtype == GDN2_BF16 ? 2 : 4;
+    s.tok = d->batch * T * d->heads;
+    s.qk = s.tok * d->dk * esz;
+    s.v = s.tok * d->dv * esz;
+    s.la = s.tok * (d->decay_kind == GDN2_GATE_KEY ? d->dk : 1) * 4;
+    s.eb = s.tok * (d->erase_kind == GDN2_GATE_KEY ? d->dk : 1) * 4;
+    s.wr = d->tie_write_to_erase ? 0 : s.tok * (d->write_kind == GDN2_GATE_KEY ? d->dk : 1) * 4;
+    s.o = s.tok * d->dv * 4;
+    s.st = d->batch * d->heads * d->dk * d->dv * 4;
+    return s;
+}
+
+gdn2_status hip_status(hipError_t e) { return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int gdn2_abi_version(void) { return GDN2_ABI_VERSION; }
+
+const char *gdn2_status_str(int status) {
+    switch (status) {
+        case GDN2_OK: return "ok";
+        case GDN2_ERR_NULL: return "a required pointer is NULL";
+        case GDN2_ERR_SHAPE: return "invalid sizes or gate kinds";
+        case GDN2_ERR_DTYPE: return "unknown q/k/v dtype";
+        case GDN2_ERR_UNSUPPORTED: return "valid request without a kernel in this build";
+        case GDN2_ERR_ALIAS: return "an output overlaps an input";
+        case GDN2_ERR_WORKSPACE: return "workspace too small";
+        case GDN2_ERR_HIP: return "a HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+gdn2_status gdn2_chunk_fwd_workspace(const gdn2_desc *desc, size_t *bytes) {
+    if (!bytes) return GDN2_ERR_NULL;
+    gdn2_status st = check_common(desc);
+    if (st != GDN2_OK) return st;
+    if (desc->chunk != 16 && desc->chunk != 32 && desc->chunk != 64) return GDN2_ERR_UNSUPPORTED;
+    *bytes = 0;
+    return GDN2_OK;
+}
+
+gdn2_status gdn2_chunk_fwd(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                           const float *log_decay, const float *erase, const float *write,
+                           const float *state0, float *o, float *state_out, void *workspace,
+                           size_t ws_bytes, void *stream) {
+    size_t need = 0;
+    gdn2_status st = gdn2_chunk_fwd_workspace(d, &need);
+    if (st != GDN2_OK) return st;
+    if (ws_bytes < need || (need > 0 && !workspace)) return GDN2_ERR_WORKSPACE;
+    const int64_t T = d->seqlen;
+    const bool work = d->batch * T > 0;
+    if (work && (!q || !k || !v || !log_decay || !erase || !o)) return GDN2_ERR_NULL;
+    if (work && !d->tie_write_to_erase && !write) return GDN2_ERR_NULL;
+    const Sizes sz = sizes_of(d, T);
+    const Span in[] = {span_of(q, sz.qk), span_of(k, sz.qk), span_of(v, sz.v),
+                       span_of(log_decay, sz.la), span_of(erase, sz.eb),
+                       span_of(d->tie_write_to_erase ? nullptr : write, sz.wr)};
+    const Span s_in = span_of(state0, sz.st), s_out = span_of(state_out, sz.st);
+    const Span o_sp = span_of(o, sz.o);
+    for (const Span &x : in) {
+        if (overlap(o_sp, x) || overlap(s_out, x)) return GDN2_ERR_ALIAS;
+    }
+    if (overlap(o_sp, s_in) || overlap(o_sp, s_out)) return GDN2_ERR_ALIAS;
+    if (overlap(s_out, s_in) && s_out.lo != s_in.lo) return GDN2_ERR_ALIAS;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!work) {
+        // nothing to read but the initial state
+        if (state_out && state_out != state0)
+            return hip_status(gdn2::launch_state_copy(state0, state_out, sz.st / 4, s));
+        return GDN2_OK;
+    }
+    ChunkArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.la = log_decay; a.eb = erase; a.wr = d->tie_write_to_erase ? nullptr : write;
+    a.s0 = state0; a.o = o; a.s_out = state_out;
+    a.B = d->batch; a.T = T; a.H = d->heads; a.dk = d->dk; a.dv = d->dv;
+    a.C = static_cast<int>(d->chunk);
+    a.bf16 = d->qkv_dtype == GDN2_BF16;
+    a.la_key = d->decay_kind == GDN2_GATE_KEY;
+    a.eb_key = d->erase_kind == GDN2_GATE_KEY;
+    a.wr_key = d->tie_write_to_erase ? a.eb_key : d->write_kind == GDN2_GATE_KEY;
+    a.q_scale = d->q_scale;
+    if (a.B * a.H > 0x7fffffffLL) return GDN2_ERR_UNSUPPORTED;
+    if (gdn2::chunk_mfma_supported(a)) return hip_status(gdn2::launch_chunk_mfma(a, s));
+    return hip_status(gdn2::launch_chunk_general(a, s));
+}
+
+gdn2_status gdn2_recurrent_step(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                                const float *log_decay, const float *erase, const float *write,
+                                float *state, float *o, void *stream) {
+    gdn2_status st = check_common(d);
+    if (st != GDN2_OK) return st;
+    if (d->seqlen != 1) return GDN2_ERR_SHAPE;
+    if (d->batch == 0) return GDN2_OK;
+    if (!q || !k || !v || !log_decay || !erase || !state || !o) return GDN2_ERR_NULL;
+    if (!d->tie_write_to_erase && !write) return GDN2_ERR_NULL;
+    const Sizes sz = sizes_of(d, 1);
+    const Span in[] = {span_of(q, sz.qk), span_of(k, sz.qk), span_of(v, sz.v),
+                       span_of(log_decay, sz.la), span_of(erase, sz.eb),
+                       span_of(d->tie_write_to_erase ? nullptr : write, sz.wr)};
+    const Span s_sp = span_of(state, sz.st), o_sp = span_of(o, sz.o);
+    for (const Span &x : in) {
+        if (overlap(o_sp, x) || overlap(s_sp, x)) return GDN2_ERR_ALIAS;
+    }
+    if (overlap(o_sp, s_sp)) return GDN2_ERR_ALIAS;
+    if (d->batch * d->heads > 0x7fffffffLL) return GDN2_ERR_UNSUPPORTED;
+    StepArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.la = log_decay; a.eb = erase; a.wr = d->tie_write_to_erase ? nullptr : write;
+    a.state = state; a.o = o;
+    a.N = d->batch; a.H = d->heads; a.dk = d->dk; a.dv = d->dv;
+    a.bf16 = d->qkv_dtype == GDN2_BF16;
+    a.la_key = d->decay_kind == GDN2_GATE_KEY;
+    a.eb_key = d->erase_kind == GDN2_GATE_KEY;
+    a.wr_key = d->tie_write_to_erase ? a.eb_key : d->write_kind == GDN2_GATE_KEY;
+    a.q_scale = d->q_scale;
+    return hip_status(gdn2::launch_step(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

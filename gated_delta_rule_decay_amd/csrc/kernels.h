@@ -1,0 +1,49 @@
+// kernels.h -- internal interface between the C-ABI layer (api.hip) and the
+// gfx950 kernels.  Not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn2 {
+
+// Everything a chunked-forward launch needs; pointers are device memory.
+struct ChunkArgs {
+    const void *q, *k, *v;          // [B,T,H,dk] / [B,T,H,dv], bf16 or fp32
+    const float *la, *eb, *wr;      // gates; wr == nullptr when tied
+    const float *s0;                // [B,H,dk,dv] or nullptr (zeros)
+    float *o;                       // [B,T,H,dv]
+    float *s_out;                   // [B,H,dk,dv] or nullptr
+    int64_t B, T, H, dk, dv;
+    int C;                          // chunk length requested
+    int bf16;                       // q/k/v element type
+    int la_key, eb_key, wr_key;     // 1: per key channel, 0: per token-head
+    float q_scale;
+};
+
+struct StepArgs {
+    const void *q, *k, *v;          // [N,H,dk] / [N,H,dv]
+    const float *la, *eb, *wr;      // [N,H,dk] or [N,H]; wr == nullptr when tied
+    float *state;                   // [N,H,dk,dv], in place
+    float *o;                       // [N,H,dv]
+    int64_t N, H, dk, dv;
+    int bf16;
+    int la_key, eb_key, wr_key;
+    float q_scale;
+};
+
+// General chunked forward: fp32 arithmetic on the vector ALU, any dk, dv in
+// 1..128, internal chunk <= C chosen to fit LDS.  Returns a hipError_t.
+hipError_t launch_chunk_general(const ChunkArgs &a, hipStream_t s);
+
+// bf16, dk = dv = 128, C = 64: the MFMA path.
+bool chunk_mfma_supported(const ChunkArgs &a);
+hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);
+
+// Recurrent decode step.
+hipError_t launch_step(const StepArgs &a, hipStream_t s);
+
+// state_out <- state0 (or zeros when state0 is null); n floats.
+hipError_t launch_state_copy(const float *src, float *dst, int64_t n, hipStream_t s);
+
+}  // namespace gdn2

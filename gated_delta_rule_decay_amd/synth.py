@@ -97,11 +97,8 @@ def round_to_bf16(x: np.ndarray):
 
 
 def _softplus(x: np.ndarray) -> np.ndarray:
-    out = np.empty_like(x)
-    big = x > 30.0
-    out[big] = x[big]
-    out[~big] = np.log1p(np.exp(x[~big]))
-    return out
+    """log(1 + exp(x)) in fp64 without overflow."""
+    return np.logaddexp(0.0, x)
 
 
 def _sigmoid(x: np.ndarray) -> np.ndarray:

@@ -1,0 +1,154 @@
+/*
+ * gdn2.h -- C ABI of the MI355X (gfx950) gated delta rule-2 library.
+ *
+ * The operation (per batch b, head h; state S in R^{dk x dv}, key-by-value:
+ * rows are key channels, columns value channels), for each token t:
+ *
+ *     Sbar = Diag(a_t) S                 decay first; a_t = exp(log_decay_t)
+ *     m    = Sbar^T k_t                  the key read of the decayed state
+ *     S    = Sbar - (b_t .* k_t) m^T + (w_t .* k_t) v_t^T
+ *     o_t  = S^T (q_scale * q_t)         the query read of the updated state
+ *
+ * Sources: the "Gated DeltaNet-2" blog summary ("Core Mechanism": separate
+ * channel-wise erase gate b_t and write gate w_t, channel-wise decay, the
+ * chunkwise WY training algorithm and O(1)-memory recurrent inference); the
+ * "Gated DeltaNet" page ("Decay first, then compute the write error": the
+ * read and the subtraction use the decayed state); the course slides
+ * ("Worked case -- full trace": decay, read, correct, then read with q).
+ * Both gates act on the key axis.  Tying b = w = beta (scalar) gives Gated
+ * DeltaNet, per-channel decay with tied scalar beta gives KDA, a = 1 gives
+ * the delta rule (gist.science summary, "Technische Samenvatting", sec. 1).
+ *
+ * Conventions shared by every call:
+ *  - Every data pointer is DEVICE memory (hipMalloc'd or torch CUDA
+ *    tensors) owned by the caller; the library allocates nothing, keeps no
+ *    global mutable state and is safe to call from several host threads.
+ *  - All tensors are contiguous, row-major, last index fastest:
+ *        q, k           [B, T, H, dk]    bf16 or fp32 (desc->qkv_dtype)
+ *        v              [B, T, H, dv]    same dtype as q, k
+ *        o              [B, T, H, dv]    fp32
+ *        log_decay      [B, T, H, dk] fp32 if decay_kind == GDN2_GATE_KEY,
+ *                       [B, T, H]     fp32 if GDN2_GATE_HEAD
+ *        erase, write   same rule with erase_kind / write_kind
+ *        state tensors  [B, H, dk, dv]   fp32
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns without synchronising.  Device faults surface at
+ *    the caller's next synchronisation.
+ *  - Host-side validation runs before any HIP call: on any status other
+ *    than GDN2_OK nothing has been enqueued and no output was touched
+ *    (GDN2_ERR_HIP aside, which reports a failed launch).
+ *  - Preconditions not checked (they would need a device pass): log_decay
+ *    finite and <= 0 (decay gate in (0, 1], course slides "Stability"),
+ *    erase/write in [0, 1], all values finite.  On the bf16 path derived
+ *    operands are held in fp16 inside the kernel, which also asks
+ *    |v| < 2^15 and a state that stays below 2^15 in magnitude.
+ */
+#ifndef GDN2_H
+#define GDN2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN2_ABI_VERSION 1
+
+typedef enum gdn2_status {
+    GDN2_OK = 0,
+    GDN2_ERR_NULL = 1,        /* a required pointer (or desc) is NULL            */
+    GDN2_ERR_SHAPE = 2,       /* negative / zero / overflowing sizes            */
+    GDN2_ERR_DTYPE = 3,       /* unknown qkv_dtype                               */
+    GDN2_ERR_UNSUPPORTED = 4, /* valid request this build has no kernel for      */
+    GDN2_ERR_ALIAS = 5,       /* an output overlaps an input (see each call)     */
+    GDN2_ERR_WORKSPACE = 6,   /* workspace smaller than the query reported      */
+    GDN2_ERR_HIP = 7          /* a HIP launch or copy failed                     */
+} gdn2_status;
+
+typedef enum gdn2_dtype { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
+
+typedef enum gdn2_gate_kind {
+    GDN2_GATE_HEAD = 0, /* one value per token-head, shared by all key channels */
+    GDN2_GATE_KEY = 1   /* one value per key channel                            */
+} gdn2_gate_kind;
+
+/* Problem description.  For gdn2_recurrent_step `batch` is the number of
+ * sequences N and `seqlen` must be 1. */
+typedef struct gdn2_desc {
+    int64_t batch;      /* B >= 0 */
+    int64_t seqlen;     /* T >= 0 */
+    int64_t heads;      /* H >= 1 */
+    int64_t dk;         /* key channels,   1..128 */
+    int64_t dv;         /* value channels, 1..128 */
+    int64_t chunk;      /* chunk length C of the chunkwise algorithm: 16, 32 or 64 */
+    int32_t qkv_dtype;  /* gdn2_dtype of q, k, v */
+    int32_t decay_kind; /* gdn2_gate_kind of log_decay */
+    int32_t erase_kind; /* gdn2_gate_kind of erase      */
+    int32_t write_kind; /* gdn2_gate_kind of write (ignored when tied) */
+    int32_t tie_write_to_erase; /* nonzero: w := b and `write` is ignored */
+    float q_scale;      /* multiplies q; 1.0 for the plain read */
+} gdn2_desc;
+
+/* GDN2_ABI_VERSION of the loaded library. */
+int gdn2_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char *gdn2_status_str(int status);
+
+/* Device workspace, in bytes, that gdn2_chunk_fwd needs for `desc`
+ * (0 when it needs none).  Same validation as gdn2_chunk_fwd. */
+gdn2_status gdn2_chunk_fwd_workspace(const gdn2_desc *desc, size_t *bytes);
+
+/*
+ * Chunkwise-parallel forward over whole sequences (training / prefill).
+ *
+ * The "Gated DeltaNet-2" blog summary ("Core Mechanism") and the
+ * gist.science summary ("Technische Samenvatting", section 3) describe the
+ * algorithm: the cumulative per-channel decay of each chunk is absorbed
+ * into the erase and write factors, a unit-lower-triangular solve gives the
+ * chunk's auxiliary matrices, and dense chunk contractions carry the state
+ * from chunk to chunk.  The result equals running the recurrence above
+ * token by token (up to rounding); the chunk length only changes speed.
+ *
+ *   q, k, v      inputs, see layouts above.
+ *   log_decay    log of the decay gate (<= 0).
+ *   erase        erase gate b.
+ *   write        write gate w; ignored (may be NULL) when
+ *                desc->tie_write_to_erase is set.
+ *   state0       initial state [B,H,dk,dv] fp32, or NULL for zeros.
+ *   o            output [B,T,H,dv] fp32 (must not overlap any input).
+ *   state_out    final state [B,H,dk,dv] fp32, or NULL to skip.  It may be
+ *                exactly state0 (updated in place); any other overlap with
+ *                an input is GDN2_ERR_ALIAS.
+ *   workspace    device scratch of ws_bytes >= gdn2_chunk_fwd_workspace();
+ *                may be NULL when that is 0.
+ * With T == 0 nothing is read but state0, o is untouched and state_out
+ * receives state0 (or zeros).
+ */
+gdn2_status gdn2_chunk_fwd(const gdn2_desc *desc,
+                           const void *q, const void *k, const void *v,
+                           const float *log_decay, const float *erase, const float *write,
+                           const float *state0, float *o, float *state_out,
+                           void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * One recurrent decode step for N = desc->batch sequences (desc->seqlen must
+ * be 1): the O(1)-memory inference form ("Gated DeltaNet-2" blog summary,
+ * "Core Mechanism"; the fixed-size state of the divagr.com explainer, part
+ * 5).  The fp32 state [N,H,dk,dv] is read and rewritten in place.
+ *
+ *   q, k [N,H,dk], v [N,H,dv] (qkv_dtype); gates [N,H,dk] or [N,H] fp32;
+ *   write ignored when tied; state in/out; o [N,H,dv] fp32, must not overlap
+ *   the state or any input.
+ */
+gdn2_status gdn2_recurrent_step(const gdn2_desc *desc,
+                                const void *q, const void *k, const void *v,
+                                const float *log_decay, const float *erase, const float *write,
+                                float *state, float *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN2_H */

@@ -15,3 +15,12 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    """Name each GPU case on stdout before it runs (flushed), so a run that
+    dies on the GPU still says which case it was in."""
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu case] {request.node.nodeid}", flush=True)
+    yield

@@ -1,0 +1,134 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/gdn2.h declares, and rejects bad requests on the host before any
+HIP call.  No test here launches a kernel; the device pointers below are
+never dereferenced (validation only compares addresses)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gated_delta_rule_decay_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn2.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bd.library_path()):
+        from gated_delta_rule_decay_amd.build import build_library
+        build_library()
+    return bd.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn2_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(bd.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gdn2_abi_version() == 1
+    for s in range(8):
+        assert lib.gdn2_status_str(s)
+    assert lib.gdn2_status_str(0) == b"ok"
+
+
+def test_desc_layout_matches_header():
+    # six int64, five int32, one float: 72 bytes, no padding surprises
+    assert ctypes.sizeof(bd.Gdn2Desc) == 72
+    assert bd.Gdn2Desc.q_scale.offset == 68
+
+
+# Fake, well-separated device addresses for the inputs and outputs.
+BASE = 1 << 40
+SLOT = 1 << 32
+Q, K, V, LA, EB, WR, S0, O, SO, WS = (BASE + i * SLOT for i in range(10))
+
+
+def fwd(lib, desc, q=Q, k=K, v=V, la=LA, eb=EB, wr=WR, s0=S0, o=O, so=SO, ws=None, wsb=0):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gdn2_chunk_fwd(None if desc is None else ctypes.byref(desc), vp(q), vp(k), vp(v),
+                              vp(la), vp(eb), vp(wr), vp(s0), vp(o), vp(so), vp(ws), wsb, None)
+
+
+def step(lib, desc, q=Q, k=K, v=V, la=LA, eb=EB, wr=WR, st=S0, o=O):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gdn2_recurrent_step(None if desc is None else ctypes.byref(desc), vp(q), vp(k),
+                                   vp(v), vp(la), vp(eb), vp(wr), vp(st), vp(o), None)
+
+
+def good(**kw):
+    base = dict(batch=2, seqlen=128, heads=4, dk=128, dv=128, chunk=64)
+    base.update(kw)
+    return bd.make_desc(**base)
+
+
+def test_null_arguments(lib):
+    assert fwd(lib, None) == 1
+    assert fwd(lib, good(), q=None) == 1
+    assert fwd(lib, good(), o=None) == 1
+    assert fwd(lib, good(), la=None) == 1
+    assert fwd(lib, good(tied=False), wr=None) == 1
+    n = ctypes.c_size_t(0)
+    assert lib.gdn2_chunk_fwd_workspace(None, ctypes.byref(n)) == 1
+    assert lib.gdn2_chunk_fwd_workspace(ctypes.byref(good()), None) == 1
+    assert step(lib, None) == 1
+    assert step(lib, good(seqlen=1), st=None) == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), 2), (dict(seqlen=-5), 2), (dict(heads=0), 2), (dict(dk=0), 2),
+    (dict(dv=0), 2), (dict(dk=129), 4), (dict(dv=256), 4), (dict(chunk=8), 4),
+    (dict(chunk=128), 4), (dict(qkv_dtype=7), 3), (dict(decay_kind=2), 2),
+    (dict(erase_kind=-1), 2), (dict(batch=1 << 40, seqlen=1 << 30), 2),
+])
+def test_bad_descriptors(lib, kw, status):
+    assert fwd(lib, good(**kw)) == status
+
+
+def test_write_kind_ignored_when_tied(lib):
+    n = ctypes.c_size_t(99)
+    d = good(tied=True, write_kind=9)
+    assert lib.gdn2_chunk_fwd_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value == 0
+
+
+def test_aliasing(lib):
+    d = good()
+    assert fwd(lib, d, o=Q + 16) == 5          # o inside q
+    assert fwd(lib, d, so=V) == 5              # state_out on v
+    assert fwd(lib, d, so=S0 + 64) == 5        # partial overlap with state0
+    assert fwd(lib, d, o=SO) == 5              # o on state_out
+    assert fwd(lib, d, o=S0 + 4) == 5          # o on state0
+    d1 = good(seqlen=1)
+    assert step(lib, d1, o=S0 + 8) == 5        # decode output inside the state
+    assert step(lib, d1, st=K) == 5            # state on k
+
+
+def test_empty_calls_touch_nothing(lib):
+    # T == 0 with the state updated in place: nothing to enqueue at all
+    assert fwd(lib, good(seqlen=0), so=S0) == 0
+    assert fwd(lib, good(seqlen=0), so=None) == 0
+    assert fwd(lib, good(batch=0), so=None) == 0
+    assert step(lib, good(batch=0, seqlen=1)) == 0
+
+
+def test_decode_needs_one_token(lib):
+    assert step(lib, good(seqlen=2)) == 2
+    assert step(lib, good(seqlen=0)) == 2
+
+
+def test_workspace_query(lib):
+    for d in (good(), good(qkv_dtype=0, dk=32, dv=32, chunk=16), good(tied=True, decay_kind=0)):
+        n = ctypes.c_size_t(123)
+        assert lib.gdn2_chunk_fwd_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
+        assert n.value == 0

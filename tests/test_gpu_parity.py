@@ -1,0 +1,234 @@
+"""GPU parity: the HIP library against the fp64 oracle, element by element.
+
+Every case draws seeded inputs with the workloads' recipe, runs the library
+through its C ABI (via the binding) on the GPU, runs the oracle on exactly the
+same values on the CPU, and bounds the relative L2 error of o and of the
+final state: 1e-5 for fp32 q/k/v, 2e-3 for bf16 q/k/v.  Small cases span
+several chunks and a ragged last chunk; full-size cases run the launch the
+bench times and check sampled (batch, head) chains, which are independent.
+"""
+import numpy as np
+import pytest
+
+from gated_delta_rule_decay_amd import synth
+from tests.parity_util import (TOL_BF16, TOL_F32, gpu_chunk, oracle_chunk, pick_chains,
+                               rel_l2, to_device)
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def _tol(w):
+    return TOL_F32 if w.qkv_dtype == "f32" else TOL_BF16
+
+
+def _check(w, inp, chunk, q_scale=1.0):
+    o, S = gpu_chunk(inp, chunk, q_scale=q_scale)
+    o_ref, S_ref = oracle_chunk(inp, q_scale=q_scale)
+    eo, es = rel_l2(o, o_ref), rel_l2(S, S_ref)
+    print(f"  rel_l2 o={eo:.3e} S={es:.3e} (tol {_tol(w):.0e})", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+    assert eo <= _tol(w) and es <= _tol(w)
+    return o, S
+
+
+def test_tiny_fp32_workload():
+    w = W[0]
+    _check(w, synth.make_inputs(w, wid=0), w.chunk)
+
+
+@pytest.mark.parametrize("wid,B,T,H", [(1, 1, 200, 2), (2, 1, 200, 2), (2, 2, 131, 1),
+                                       (3, 1, 4200, 1)])
+def test_reduced_bf16_workloads(wid, B, T, H):
+    w = W[wid].scaled(B=B, T=T, H=H)
+    _check(w, synth.make_inputs(w, seed=1000 + wid * 7 + T), w.chunk)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_fp32_full_width(chunk):
+    w = W[2].scaled(B=1, T=150, H=2, qkv_dtype="f32")
+    _check(w, synth.make_inputs(w, seed=77 + chunk), chunk)
+
+
+@pytest.mark.parametrize("dtype,dk,dv,T", [("f32", 48, 80, 37), ("bf16", 64, 64, 100),
+                                           ("f32", 1, 3, 20), ("bf16", 128, 32, 70)])
+def test_odd_shapes(dtype, dk, dv, T):
+    w = W[2].scaled(B=2, T=T, H=1, dk=dk, dv=dv, qkv_dtype=dtype, chunk=32)
+    _check(w, synth.make_inputs(w, seed=dk * 1000 + dv + T), 32)
+
+
+@pytest.mark.parametrize("gates,tied", [("head", False), ("key", True), ("head", True)])
+def test_gate_kinds(gates, tied):
+    w = W[2].scaled(B=1, T=160, H=2, gates=gates, tied=tied)
+    _check(w, synth.make_inputs(w, seed=5 + tied), 64)
+
+
+def test_q_scale_and_zero_state():
+    w = W[2].scaled(B=1, T=96, H=2, s0_std=0.0)
+    _check(w, synth.make_inputs(w, seed=9), 64, q_scale=0.125)
+
+
+def test_edge_lengths():
+    import torch
+    from gated_delta_rule_decay_amd import chunk_fwd
+
+    for T in (1, 63, 64, 65):
+        w = W[2].scaled(B=1, T=T, H=1)
+        _check(w, synth.make_inputs(w, seed=T), 64)
+    # T == 0: the final state is the initial state, o untouched
+    w = W[2].scaled(B=1, T=0, H=2)
+    d = to_device(synth.make_inputs(w, seed=3))
+    o, S = chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(S, d["S0"]) and o.numel() == 0
+
+
+def test_in_place_state_and_resume():
+    import torch
+    from gated_delta_rule_decay_amd import chunk_fwd
+
+    w = W[2].scaled(B=1, T=256, H=2)
+    inp = synth.make_inputs(w, seed=11)
+    d = to_device(inp)
+    o_full, S_full = chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"],
+                               d["S0"])
+    # two calls, the second resuming in place from the first's final state
+    st = d["S0"].clone()
+    sl = lambda x, a, b: None if x is None else x[:, a:b].contiguous()
+    o1, _ = chunk_fwd(*(sl(d[n], 0, 128) for n in ("q", "k", "v", "log_decay", "erase", "write")),
+                      st, state_out=st)
+    o2, _ = chunk_fwd(*(sl(d[n], 128, 256) for n in ("q", "k", "v", "log_decay", "erase", "write")),
+                      st, state_out=st)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_chunk(inp)
+    assert rel_l2(torch.cat([o1, o2], 1).cpu().numpy(), o_ref) <= TOL_BF16
+    assert rel_l2(st.cpu().numpy(), S_ref) <= TOL_BF16
+    assert rel_l2(S_full.cpu().numpy(), S_ref) <= TOL_BF16
+
+
+def test_run_to_run_bitwise():
+    w = W[2].scaled(B=2, T=300, H=2)
+    inp = synth.make_inputs(w, seed=12)
+    o1, S1 = gpu_chunk(inp, 64)
+    o2, S2 = gpu_chunk(inp, 64)
+    assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
+
+
+def _decode_run(w, steps, seed, sample_heads=None):
+    """Run `steps` decode steps on the GPU; returns o per step and the final
+    state, plus the inputs of the sampled heads stacked over time."""
+    import torch
+    from gated_delta_rule_decay_amd import recurrent_step
+
+    import concurrent.futures as cf
+
+    S0 = synth.make_decode_state(w, seed=seed)
+    state = torch.from_numpy(S0).cuda()
+    outs, keep = [], {n: [] for n in ("q", "k", "v", "log_decay", "erase", "write")}
+    pool = cf.ThreadPoolExecutor(max_workers=8)
+    batch = 64
+    pending = [pool.submit(synth.make_decode_step, w, t, seed) for t in range(min(batch, steps))]
+    for t in range(steps):
+        inp = pending[t % batch].result()
+        if t + batch < steps:
+            pending[t % batch] = pool.submit(synth.make_decode_step, w, t + batch, seed)
+        d = to_device(inp)
+        o = recurrent_step(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], state)
+        sel = (slice(None),) if sample_heads is None else (sample_heads[:, 0], sample_heads[:, 1])
+        outs.append(o.cpu().numpy()[sel])
+        for n in keep:
+            if inp[n] is not None:
+                keep[n].append(inp[n][sel])
+    pool.shutdown()
+    torch.cuda.synchronize()
+    Sg = state.cpu().numpy()
+    if sample_heads is not None:
+        Sg = Sg[sample_heads[:, 0], sample_heads[:, 1]]
+        S0 = S0[sample_heads[:, 0], sample_heads[:, 1]]
+    return np.stack(outs, 1), Sg, S0, {n: (np.stack(v, 1) if v else None) for n, v in keep.items()}
+
+
+def _decode_oracle(S0, seq):
+    """Oracle over the decode sequence: each sampled head is its own chain."""
+    from oracle.oracle import gdn2_forward
+
+    add_h = lambda x: None if x is None else x[:, :, None]
+    # seq arrays are [n, steps, ...] -> [B=n, T=steps, H=1, ...]
+    if S0.ndim == 3:
+        S0 = S0[:, None]
+    o, S = gdn2_forward(add_h(seq["q"]), add_h(seq["k"]), add_h(seq["v"]), add_h(seq["log_decay"]),
+                        add_h(seq["erase"]), add_h(seq["write"]), S0)
+    return o[:, :, 0], S[:, 0]
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(128, 128, "bf16"), (128, 128, "f32"), (40, 24, "f32")])
+def test_decode_small(dk, dv, dtype):
+    w = W[4].scaled(B=3, H=2, dk=dk, dv=dv, qkv_dtype=dtype)
+    o, S, S0, seq = _decode_run(w, 9, seed=dk + dv)
+    n = w.B * w.H
+    flat = lambda x: None if x is None else x.reshape((n,) + x.shape[2:])
+    # reorder [N, steps, H, ...] -> [N*H, steps, ...]: every head is a chain
+    seqf = {k_: None if v_ is None else np.moveaxis(v_, 2, 1).reshape((n, 9) + v_.shape[3:])
+            for k_, v_ in seq.items()}
+    o_ref, S_ref = _decode_oracle(flat(S0), seqf)
+    o_g = np.moveaxis(o, 2, 1).reshape((n, 9, dv))
+    tol = TOL_F32 if dtype == "f32" else TOL_BF16
+    assert rel_l2(o_g, o_ref) <= tol
+    assert rel_l2(flat(S), S_ref) <= tol
+
+
+def test_decode_steps_equal_chunked_forward():
+    import torch
+    from gated_delta_rule_decay_amd import chunk_fwd, recurrent_step
+
+    w = W[2].scaled(B=2, T=70, H=2)
+    inp = synth.make_inputs(w, seed=21)
+    d = to_device(inp)
+    o_c, S_c = chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"])
+    st = d["S0"].clone()
+    outs = []
+    for t in range(w.T):
+        g = lambda x: None if x is None else x[:, t].contiguous()
+        outs.append(recurrent_step(g(d["q"]), g(d["k"]), g(d["v"]), g(d["log_decay"]),
+                                   g(d["erase"]), g(d["write"]), st))
+    torch.cuda.synchronize()
+    o_d = torch.stack(outs, 1)
+    assert rel_l2(o_d.cpu().numpy(), o_c.cpu().numpy()) <= TOL_BF16
+    assert rel_l2(st.cpu().numpy(), S_c.cpu().numpy()) <= TOL_BF16
+
+
+# ---- full sizes: the exact launches the bench times, sampled chains -------
+
+@pytest.mark.parametrize("wid,nchains", [(1, 3), (2, 3), (3, 2)])
+def test_full_size_sampled_chains(wid, nchains):
+    import torch
+    from gated_delta_rule_decay_amd import chunk_fwd
+
+    w = W[wid]
+    inp = synth.make_inputs(w, wid=wid)
+    d = to_device(inp)
+    o, S = chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"],
+                     chunk=w.chunk)
+    torch.cuda.synchronize()
+    chains = pick_chains(w, nchains, seed=wid)
+    bi = [c[0] for c in chains]
+    hi = [c[1] for c in chains]
+    o_s = o[bi, :, hi].cpu().numpy()          # [n, T, dv]
+    S_s = S[bi, hi].cpu().numpy()
+    o_ref, S_ref = oracle_chunk(inp, chains=chains)
+    eo, es = rel_l2(o_s, o_ref), rel_l2(S_s, S_ref)
+    print(f"  {w.name}: rel_l2 o={eo:.3e} S={es:.3e}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16
+    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+
+
+def test_full_size_decode_sampled_heads():
+    w = W[4]
+    r = np.random.Generator(np.random.PCG64(4))
+    heads = np.stack([r.choice(w.B, 4, replace=False), r.choice(w.H, 4)], 1)
+    o, S, S0, seq = _decode_run(w, w.decode_steps, seed=None, sample_heads=heads)
+    o_ref, S_ref = _decode_oracle(S0, seq)
+    eo, es = rel_l2(o, o_ref), rel_l2(S, S_ref)
+    print(f"  decode 1024 steps: rel_l2 o={eo:.3e} S={es:.3e}", flush=True)
+    assert eo <= TOL_BF16 and es <= TOL_BF16

@@ -1,0 +1,258 @@
+"""Throughput of the GDN-2 chunked forward (and of the decode step) on one GPU.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step is one chunked forward over the whole batch of the full GDN-2
+workload (B=8, H=16, T=4096, dk=dv=128, C=64, bf16 q/k/v, fp32 per-channel
+decay/erase/write gates and state, S0 ~ N(0, 0.1)), inputs resident in HBM.
+``value`` is tokens/s (B*T per step).  The same run also times the recurrent
+decode step (256 sequences x 16 heads, fp32 state in HBM, in place) and the
+Gated DeltaNet mode (scalar gates, B=4), each reported beside ``value`` with
+its own roofline, and times the fp64 CPU oracle on the full workload.
+
+Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 matrix
+PROFILES = os.path.join(ROOT, "profiles")
+CHUNK_SOURCES = ("chunk_mfma.hip", "chunk_general.hip", "kernels.h", "common.h")
+DECODE_SOURCES = ("decode.hip", "kernels.h", "common.h")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_delta_rule_decay_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def chunk_bytes(w) -> int:
+    """Algorithmic HBM bytes of one chunked forward: every input once, o once,
+    S0 read and S_T written once."""
+    e = 2 if w.qkv_dtype == "bf16" else 4
+    gate = w.dk * 4 if w.gates == "key" else 4
+    n_gates = 2 if w.tied else 3
+    per_tok = (2 * w.dk + w.dv) * e + n_gates * gate + w.dv * 4
+    state = w.B * w.H * w.dk * w.dv * 4
+    s0 = state if w.s0_std > 0 else 0
+    return w.B * w.T * w.H * per_tok + s0 + state
+
+
+def chunk_flops(w) -> int:
+    """Algorithmic flops of one chunked forward, full C x C tiles counted:
+    16 C^2 d + 8 C d^2 per chunk-head (untied), 8 C^2 d + 6 C d^2 (tied)."""
+    C, d = w.chunk, w.dk
+    per_chunk = (8 * C * C * d + 6 * C * d * d) if w.tied else (16 * C * C * d + 8 * C * d * d)
+    return w.B * w.H * (w.T // C) * per_chunk
+
+
+def decode_bytes(w) -> int:
+    e = 2 if w.qkv_dtype == "bf16" else 4
+    per_head = (2 * w.dk + w.dv) * e + 3 * w.dk * 4 + w.dv * 4
+    return w.B * w.H * (2 * w.dk * w.dv * 4 + per_head)
+
+
+def read_traffic(kernel: str, workload: str, src_hash: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if the summary
+    in profiles/ was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def to_dev(inp, torch):
+    out = {}
+    for n in ("q", "k", "v"):
+        bits = inp.get(n + "_bf16")
+        if bits is not None:
+            out[n] = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        else:
+            out[n] = torch.from_numpy(inp[n]).cuda()
+    for n in ("log_decay", "erase", "write", "S0"):
+        out[n] = None if inp.get(n) is None else torch.from_numpy(inp[n]).cuda()
+    return out
+
+
+def time_chunk(w, wid, steps, warmup, torch, chunk_fwd):
+    log(f"[bench] generating {w.name} inputs")
+    inp = synth_make(w, wid)
+    d = to_dev(inp, torch)
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
+    st = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    args = (d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"])
+    for _ in range(warmup):
+        chunk_fwd(*args, chunk=w.chunk, out=o, state_out=st)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"[bench] timing {steps} steps of {w.name}")
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        chunk_fwd(*args, chunk=w.chunk, out=o, state_out=st)
+    ev1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / steps
+    ms_kernel = ev0.elapsed_time(ev1) / steps
+    return inp, ms_step, ms_kernel
+
+
+def synth_make(w, wid):
+    from gated_delta_rule_decay_amd import synth
+    return synth.make_inputs(w, wid=wid)
+
+
+def roofline_hbm(bytes_alg, ms, traffic=None):
+    ach = bytes_alg / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--no-extra", action="store_true", help="time only the main workload")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(every chain is independent, see the design notes on sharding)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gated_delta_rule_decay_amd import binding, chunk_fwd, recurrent_step, synth
+
+    binding.load_library()  # raises if the HIP library is not built
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    W = synth.WORKLOADS
+    w = W[2]
+    inp, ms_step, ms_kernel = time_chunk(w, 2, args.steps, args.warmup, torch, chunk_fwd)
+    tokens = w.B * w.T
+    value = tokens / (ms_step * 1e-3)
+    bytes_alg = chunk_bytes(w)
+    flops_alg = chunk_flops(w)
+    chunk_hash = source_hash(CHUNK_SOURCES)
+    traffic = read_traffic("chunk_fwd", w.name, chunk_hash)
+    result = {
+        "metric": "tokens/s for chunked GDN-2 fwd (H=16,dk=dv=128,T=4k) + decode; % roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in; f16 MFMA operands, f32 accumulate, f32 state",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: chunked forward B={w.B} H={w.H} T={w.T} "
+                               f"dk=dv={w.dk} C={w.chunk}, per-channel decay/erase/write",
+                   "global_batch": w.B, "seq_len": w.T, "heads": w.H, "dk": w.dk, "dv": w.dv,
+                   "chunk": w.chunk, "parallelism": "single GPU"},
+        "roofline": roofline_hbm(bytes_alg, ms_kernel, traffic),
+        "kernel_ms": round(ms_kernel, 4),
+        "algorithmic_bytes_per_launch": bytes_alg,
+        "algorithmic_flops_per_launch": flops_alg,
+        "mfma_frac_of_algorithmic_flops": round(flops_alg / (ms_kernel * 1e-3) / 1e12
+                                                / MFMA_PEAK_TFLOPS, 4),
+        "chunk_source_hash": chunk_hash,
+    }
+    del inp
+
+    if not args.no_extra:
+        # Gated DeltaNet mode: scalar gates tied, zero initial state, B=4
+        w1 = W[1]
+        _, ms1, k1 = time_chunk(w1, 1, args.steps, args.warmup, torch, chunk_fwd)
+        result["gdn_mode"] = {"workload": w1.name, "value": round(w1.B * w1.T / (ms1 * 1e-3), 1),
+                              "unit": "tokens/s", "ms_per_step": round(ms1, 4),
+                              "roofline": roofline_hbm(chunk_bytes(w1), k1)}
+        # decode: 256 sequences x 16 heads, state in place, a pool of distinct step inputs
+        w4 = W[4]
+        log("[bench] decode setup")
+        state = torch.from_numpy(synth.make_decode_state(w4)).cuda()
+        pool = [to_dev(synth.make_decode_step(w4, t), torch) for t in range(8)]
+        o4 = torch.empty((w4.B, w4.H, w4.dv), dtype=torch.float32, device="cuda")
+        call = lambda d: recurrent_step(d["q"], d["k"], d["v"], d["log_decay"], d["erase"],
+                                        d["write"], state, out=o4)
+        for t in range(3):
+            call(pool[t % len(pool)])
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = args.decode_steps
+        t0 = time.perf_counter()
+        ev0.record()
+        for t in range(n):
+            call(pool[t % len(pool)])
+        ev1.record()
+        torch.cuda.synchronize()
+        ms_dec = (time.perf_counter() - t0) * 1e3 / n
+        k_dec = ev0.elapsed_time(ev1) / n
+        result["decode"] = {
+            "workload": f"{w4.name}: {w4.B} sequences x H={w4.H}, dk=dv={w4.dk}, fp32 state "
+                        f"in HBM updated in place, {n} consecutive steps",
+            "value": round(w4.B / (ms_dec * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(ms_dec, 4), "kernel_ms": round(k_dec, 4),
+            "roofline": roofline_hbm(decode_bytes(w4), k_dec,
+                                     read_traffic("recurrent_step", w4.name,
+                                                  source_hash(DECODE_SOURCES))),
+            "algorithmic_bytes_per_launch": decode_bytes(w4),
+        }
+        del state, pool
+
+    if not args.no_cpu:
+        from oracle.oracle import available_cores, gdn2_forward
+
+        cores = min(16, available_cores())
+        log(f"[bench] timing the fp64 oracle on {cores} threads")
+        inp = synth_make(w, 2)
+        t0 = time.perf_counter()
+        gdn2_forward(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"],
+                     inp["S0"], threads=cores)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(tokens / dt, 1), "unit": "tokens/s",
+                                  "cores": cores, "kind": "oracle",
+                                  "sample": f"the whole {w.name} workload ({w.B * w.H} chains x "
+                                            f"{w.T} tokens), fp64 token recurrence, {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -232,3 +232,50 @@ def test_full_size_decode_sampled_heads():
     eo, es = rel_l2(o, o_ref), rel_l2(S, S_ref)
     print(f"  decode 1024 steps: rel_l2 o={eo:.3e} S={es:.3e}", flush=True)
     assert eo <= TOL_BF16 and es <= TOL_BF16
+
+
+# ---- degenerate gates: the fast path's exact fallback and the limits -------
+
+def _bf16_case(seed, T=200, H=2, B=1, tied=False, gates="key"):
+    w = W[2].scaled(B=B, T=T, H=H, tied=tied, gates=gates)
+    return w, synth.make_inputs(w, seed=seed)
+
+
+def test_near_zero_decay_spikes():
+    # a -> 0 on a few tokens and channels: exp(-1000) is 0, the old state is gone there
+    w, inp = _bf16_case(31)
+    inp["log_decay"][:, 70:73, :, :40] = -1000.0
+    inp["log_decay"][:, 130, :, :] = -1000.0
+    _check(w, inp, 64)
+
+
+def test_strong_uniform_decay():
+    # every token decays every channel by e^-3: factors leave fp16 range inside a block
+    w, inp = _bf16_case(32)
+    inp["log_decay"][:, 64:128] = -3.0
+    _check(w, inp, 64)
+    w, inp = _bf16_case(33, tied=True, gates="head")
+    inp["log_decay"][:] = -2.5
+    _check(w, inp, 64)
+
+
+def test_no_decay_is_delta_rule():
+    w, inp = _bf16_case(34)
+    inp["log_decay"][:] = 0.0
+    _check(w, inp, 64)
+
+
+def test_hold_keeps_state():
+    # a = 1 and b = w = 0: the state is held (exactly, since every write is zero)
+    import torch
+    from gated_delta_rule_decay_amd import chunk_fwd
+
+    w, inp = _bf16_case(35)
+    inp["log_decay"][:] = 0.0
+    inp["erase"][:] = 0.0
+    inp["write"][:] = 0.0
+    d = to_device(inp)
+    o, S = chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(S, d["S0"])
+    _check(w, inp, 64)

@@ -146,6 +146,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extra", action="store_true", help="time only the main workload")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (untimed) whose memory counters "
+                         "calibrate the profiler's byte counts")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -203,7 +206,8 @@ def main():
         _, ms1, k1 = time_chunk(w1, 1, args.steps, args.warmup, torch, chunk_fwd)
         result["gdn_mode"] = {"workload": w1.name, "value": round(w1.B * w1.T / (ms1 * 1e-3), 1),
                               "unit": "tokens/s", "ms_per_step": round(ms1, 4),
-                              "roofline": roofline_hbm(chunk_bytes(w1), k1)}
+                              "roofline": roofline_hbm(chunk_bytes(w1), k1,
+                                                       read_traffic("chunk_fwd", w1.name, chunk_hash))}
         # decode: 256 sequences x 16 heads, state in place, a pool of distinct step inputs
         w4 = W[4]
         log("[bench] decode setup")
@@ -236,6 +240,15 @@ def main():
             "algorithmic_bytes_per_launch": decode_bytes(w4),
         }
         del state, pool
+
+    if args.calib_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")  # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["calib_copy_bytes"] = src.numel() * 4
+        del src, dst
 
     if not args.no_cpu:
         from oracle.oracle import available_cores, gdn2_forward

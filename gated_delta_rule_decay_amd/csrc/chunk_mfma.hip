@@ -149,6 +149,46 @@ __device__ __forceinline__ f4 mfma_f32_block(const float *X, int xp, const float
     return acc;
 }
 
+// In-place inverse of a unit-lower-triangular 16x16 block I + N held (N
+// strictly lower, zero diagonal) in LDS at `na` with row pitch AP:
+// (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) since N^16 = 0.  One wave;
+// `sa`, `sb` are two private 16x16 fp32 scratch blocks.  The result is written
+// back to `na` (fp32) and to `th` (fp16, row pitch SP).
+__device__ __forceinline__ void invert_unit_lower16(float *na, _Float16 *th, float *sa, float *sb, int lr,
+                                                    int lg) {
+    f4 nn, eye;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        nn[e] = na[(4 * lg + e) * AP + lr];
+        eye[e] = (4 * lg + e == lr) ? 1.f : 0.f;
+    }
+    // a wave's LDS writes are seen by its later reads, so no barrier is needed
+    const f4 n2 = mfma_f32_block(na, AP, na, AP, splat(0.f), lr, lg);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sa[(4 * lg + e) * 16 + lr] = n2[e];
+    const f4 n3 = mfma_f32_block(na, AP, sa, 16, splat(0.f), lr, lg);
+    const f4 t1 = eye - nn + n2 - n3;  // (I - N)(I + N^2)
+    const f4 n4 = mfma_f32_block(sa, 16, sa, 16, splat(0.f), lr, lg);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        sb[(4 * lg + e) * 16 + lr] = t1[e];
+        sa[(4 * lg + e) * 16 + lr] = n4[e];
+    }
+    const f4 t2 = mfma_f32_block(sb, 16, sa, 16, t1, lr, lg);  // T1 (I + N^4)
+    const f4 n8 = mfma_f32_block(sa, 16, sa, 16, splat(0.f), lr, lg);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        sb[(4 * lg + e) * 16 + lr] = t2[e];
+        sa[(4 * lg + e) * 16 + lr] = n8[e];
+    }
+    const f4 t3 = mfma_f32_block(sb, 16, sa, 16, t2, lr, lg);  // T2 (I + N^8)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        na[(4 * lg + e) * AP + lr] = t3[e];
+        th[(4 * lg + e) * SP + lr] = (_Float16)t3[e];
+    }
+}
+
 // Buffer descriptor over the rows t0..t0+C-1 of one (batch, head) chain of a
 // [B,T,H,width] tensor: rows at or past T fall outside num_records, so the
 // hardware returns zeros for them and the loads need no branch.
@@ -406,6 +446,12 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
                     S.r16[r * SP + s] = (_Float16)(incl ? aR[e] : 0.f);
                     if (!TIED) S.p16[r * SP + s] = (_Float16)(incl ? aP[e] : 0.f);
                 }
+                // a diagonal tile's wave inverts it right away (overlapping the
+                // off-diagonal tiles of the other waves); scratch blocks 4..7
+                // do not overlap the cross-block factor table still in use
+                if (i == j)
+                    invert_unit_lower16(&S.af[(16 * i) * AP + 16 * i], &S.t16[(16 * i) * SP + 16 * i],
+                                        S.scr[4 + 2 * wv], S.scr[5 + 2 * wv], lr, lg);
             }
         }
         __syncthreads();
@@ -425,74 +471,51 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
         load_raw<VT, TIED, KEYG>(R, a, b, h, t0 + C, col0, seg, cq, tid);
 
         if (!wide) {
-            // ---- solve, diagonal blocks: waves 0..3 invert one 16x16 block
-            //      (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8), N strictly
-            //      lower (N^16 = 0), on the fp32 matrix unit
-            if (wv < 4) {
-                const int i = wv;
-                float *na = &S.af[(16 * i) * AP + 16 * i];  // N, then Tm_ii
-                float *sa = S.scr[2 * i], *sb = S.scr[2 * i + 1];
-                f4 nn, eye;
+            // ---- solve Tm = (I + A)^-1, all fp32 (diagonal blocks were
+            //      inverted in the Gram phase).
+            // Off-diagonal blocks from the 2x2 split into 32x32 halves,
+            // Tm = [[T_A, 0], [-T_B A_BL T_A, T_B]], on the fp32 matrix unit.
+            // Level 1: T_10 = -T_11 A_10 T_00 and T_32 = -T_33 A_32 T_22.
+            auto blk = [&](int bi, int bj) { return &S.af[(16 * bi) * AP + 16 * bj]; };
+            auto store_t = [&](int bi, int bj, f4 t, bool keep32) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    nn[e] = na[(4 * lg + e) * AP + lr];
-                    eye[e] = (4 * lg + e == lr) ? 1.f : 0.f;
+                    const int r = 16 * bi + 4 * lg + e, c = 16 * bj + lr;
+                    if (keep32) S.af[r * AP + c] = t[e];
+                    S.t16[r * SP + c] = (_Float16)t[e];
                 }
-                // same-wave LDS writes are seen by its later reads
-                const f4 n2 = mfma_f32_block(na, AP, na, AP, splat(0.f), lr, lg);
+            };
+            if (wv < 2) {
+                const int d = 2 * wv;  // (1,0) from blocks 0,1; (3,2) from blocks 2,3
+                float *wt = S.scr[wv];
+                const f4 w = mfma_f32_block(blk(d + 1, d), AP, blk(d, d), AP, splat(0.f), lr, lg);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sa[(4 * lg + e) * 16 + lr] = n2[e];
-                const f4 n3 = mfma_f32_block(na, AP, sa, 16, splat(0.f), lr, lg);
-                const f4 t1 = eye - nn + n2 - n3;  // (I - N)(I + N^2)
-                const f4 n4 = mfma_f32_block(sa, 16, sa, 16, splat(0.f), lr, lg);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sb[(4 * lg + e) * 16 + lr] = t1[e];
-                    sa[(4 * lg + e) * 16 + lr] = n4[e];
-                }
-                const f4 t2 = mfma_f32_block(sb, 16, sa, 16, t1, lr, lg);  // T1 (I + N^4)
-                const f4 n8 = mfma_f32_block(sa, 16, sa, 16, splat(0.f), lr, lg);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sb[(4 * lg + e) * 16 + lr] = t2[e];
-                    sa[(4 * lg + e) * 16 + lr] = n8[e];
-                }
-                const f4 t3 = mfma_f32_block(sb, 16, sa, 16, t2, lr, lg);  // T2 (I + N^8)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    na[(4 * lg + e) * AP + lr] = t3[e];
-                    S.t16[(16 * i + 4 * lg + e) * SP + 16 * i + lr] = (_Float16)t3[e];
-                }
+                for (int e = 0; e < 4; ++e) wt[(4 * lg + e) * 16 + lr] = w[e];
+                // the same wave reads back what it wrote: LDS keeps a wave's order
+                const f4 t = -mfma_f32_block(blk(d + 1, d + 1), AP, wt, 16, splat(0.f), lr, lg);
+                // A_10 / A_32 are not needed again: overwrite in place
+                store_t(d + 1, d, t, true);
             }
             __syncthreads();
-            // ---- solve, off-diagonal blocks, one block row at a time:
-            //      Tm_ij = -Tm_ii * sum_{k=j}^{i-1} A_ik Tm_kj, wave j per block
-            for (int i = 1; i < 4; ++i) {
-                f4 t = splat(0.f);
-                if (wv < i) {
-                    const int j = wv;
-                    f4 w = splat(0.f);
-                    for (int k = j; k < i; ++k)
-                        w = mfma_f32_block(&S.af[(16 * i) * AP + 16 * k], AP, &S.af[(16 * k) * AP + 16 * j], AP,
-                                           w, lr, lg);
-                    float *wt = S.scr[j];
+            // Level 2: W = A_BL T_A (2x2 blocks), one block per wave 0..3
+            if (wv < 4) {
+                const int wi = 2 + (wv >> 1), wj = wv & 1;  // W block (row wi of A, col wj of T_A)
+                f4 w = mfma_f32_block(blk(wi, 1), AP, blk(1, wj), AP, splat(0.f), lr, lg);  // A_wi1 T_1wj
+                if (wj == 0) w = mfma_f32_block(blk(wi, 0), AP, blk(0, 0), AP, w, lr, lg);  // + A_wi0 T_00
+                float *wt = S.scr[wv];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) wt[(4 * lg + e) * 16 + lr] = w[e];
-                    // the same wave reads back what it wrote: LDS keeps a wave's order
-                    t = -mfma_f32_block(&S.af[(16 * i) * AP + 16 * i], AP, wt, 16, splat(0.f), lr, lg);
-                }
-                __syncthreads();  // every block of this row has read its A_ik
-                if (wv < i) {
-                    const int j = wv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * i + 4 * lg + e, s = 16 * j + lr;
-                        S.af[r * AP + s] = t[e];
-                        S.t16[r * SP + s] = (_Float16)t[e];
-                    }
-                }
-                __syncthreads();
+                for (int e = 0; e < 4; ++e) wt[(4 * lg + e) * 16 + lr] = w[e];
             }
+            __syncthreads();
+            // Level 3: lower-left quarter = -T_B W, one block per wave 0..3
+            if (wv < 4) {
+                const int ti = 2 + (wv >> 1), tj = wv & 1;
+                // row ti of T_B: T_22 (ti = 2) or [T_32, T_33] (ti = 3); W blocks scr[wj + 2*row]
+                f4 t = mfma_f32_block(blk(ti, ti), AP, S.scr[tj + 2 * (ti - 2)], 16, splat(0.f), lr, lg);
+                if (ti == 3) t = mfma_f32_block(blk(3, 2), AP, S.scr[tj], 16, t, lr, lg);
+                store_t(ti, tj, -t, false);
+            }
+            __syncthreads();  // Tm ready in fp16; af region free for X / -M
 
             // Chunk-row outputs (X, M, O: C x VT): wave wv owns row block
             // rb = wv/2 and NCTW value tiles, so its row-side fragment is read

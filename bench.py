@@ -29,7 +29,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 matrix
 PROFILES = os.path.join(ROOT, "profiles")
-CHUNK_SOURCES = ("chunk_mfma.hip", "chunk_general.hip", "kernels.h", "common.h")
+CHUNK_SOURCES = ("chunk_split.hip", "chunk_common.h", "chunk_mfma.hip", "chunk_general.hip",
+                 "kernels.h", "common.h")
 DECODE_SOURCES = ("decode.hip", "kernels.h", "common.h")
 
 
@@ -103,22 +104,36 @@ def to_dev(inp, torch):
     return out
 
 
-def time_chunk(w, wid, steps, warmup, torch, chunk_fwd):
-    log(f"[bench] generating {w.name} inputs")
-    inp = synth_make(w, wid)
+def time_chunk(w, wid, steps, warmup, torch, chunk_fwd, one_pass=False, inp=None):
+    """Time `steps` chunked forwards of workload w with inputs, outputs and
+    the two-pass workspace resident in HBM.  Returns (inputs, wall ms per
+    step, HIP-event ms per step on the launch stream)."""
+    from gated_delta_rule_decay_amd import binding
+
+    if inp is None:
+        log(f"[bench] generating {w.name} inputs")
+        inp = synth_make(w, wid)
     d = to_dev(inp, torch)
     o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
     st = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    ws = False
+    if not one_pass:
+        desc = binding.make_desc(w.B, w.T, w.H, w.dk, w.dv, w.chunk,
+                                 binding.GDN2_BF16 if w.qkv_dtype == "bf16" else binding.GDN2_F32,
+                                 int(w.gates == "key"), int(w.gates == "key"), int(w.gates == "key"),
+                                 w.tied)
+        n = binding.chunk_fwd_workspace(desc)
+        ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else False
     args = (d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"])
     for _ in range(warmup):
-        chunk_fwd(*args, chunk=w.chunk, out=o, state_out=st)
+        chunk_fwd(*args, chunk=w.chunk, out=o, state_out=st, workspace=ws)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"[bench] timing {steps} steps of {w.name}")
+    log(f"[bench] timing {steps} steps of {w.name}" + (" (one pass)" if one_pass else ""))
     t0 = time.perf_counter()
     ev0.record()
     for _ in range(steps):
-        chunk_fwd(*args, chunk=w.chunk, out=o, state_out=st)
+        chunk_fwd(*args, chunk=w.chunk, out=o, state_out=st, workspace=ws)
     ev1.record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -197,7 +212,14 @@ def main():
         "mfma_frac_of_algorithmic_flops": round(flops_alg / (ms_kernel * 1e-3) / 1e12
                                                 / MFMA_PEAK_TFLOPS, 4),
         "chunk_source_hash": chunk_hash,
+        "chunk_path": "two-pass: chunk_prep_kernel (every chunk's state-independent products, "
+                      "in parallel, into a workspace) then chunk_scan_kernel (the scan over chunks)",
     }
+    if not args.no_extra:
+        _, ms1p, k1p = time_chunk(w, 2, max(2, args.steps // 4), 1, torch, chunk_fwd, one_pass=True,
+                                  inp=inp)
+        result["one_pass"] = {"ms_per_step": round(ms1p, 4), "kernel_ms": round(k1p, 4),
+                              "value": round(tokens / (ms1p * 1e-3), 1), "unit": "tokens/s"}
     del inp
 
     if not args.no_extra:

@@ -156,12 +156,15 @@ def chunk_fwd_workspace(desc: Gdn2Desc) -> int:
 
 
 def chunk_fwd(q, k, v, log_decay, erase, write=None, state0=None, chunk=64, q_scale=1.0,
-              out=None, state_out=None, return_state=True):
+              out=None, state_out=None, return_state=True, workspace=True):
     """Chunkwise GDN-2 forward on the GPU.
 
     q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32, one dtype); gates fp32
     [B,T,H,dk] or [B,T,H]; write None ties it to erase; state0 [B,H,dk,dv]
-    fp32 or None.  Returns (o [B,T,H,dv] fp32, final state or None).
+    fp32 or None.  ``workspace``: True allocates the two-pass scratch when
+    the request has a two-pass kernel, False runs in one pass, or a uint8
+    device tensor of at least chunk_fwd_workspace() bytes to use.
+    Returns (o [B,T,H,dv] fp32, final state or None).
     """
     import torch
     B, T, H, dk = k.shape
@@ -178,8 +181,13 @@ def chunk_fwd(q, k, v, log_decay, erase, write=None, state0=None, chunk=64, q_sc
         state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     elif state_out is not None:
         _check(state_out, "state_out", (B, H, dk, dv), (torch.float32,), dev)
-    ws_bytes = chunk_fwd_workspace(desc)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    ws, ws_bytes = None, 0
+    if workspace is True:
+        ws_bytes = chunk_fwd_workspace(desc)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    elif workspace is not False and workspace is not None:
+        _check(workspace, "workspace", tuple(workspace.shape), (torch.uint8,), dev)
+        ws, ws_bytes = workspace, workspace.numel()
     st = load_library().gdn2_chunk_fwd(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(erase),
         _ptr(write), _ptr(state0), _ptr(out), _ptr(state_out), _ptr(ws), ws_bytes, _stream())

@@ -85,6 +85,33 @@ Sizes sizes_of(const gdn2_desc *d, int64_t T) {
 
 gdn2_status hip_status(hipError_t e) { return e == hipSuccess ? GDN2_OK : GDN2_ERR_HIP; }
 
+// Kernel arguments of a validated descriptor.  `tied` decides whether the
+// write gate pointer is kept (the kernels read a null write gate as tied).
+ChunkArgs args_of(const gdn2_desc *d, const void *q, const void *k, const void *v, const float *la,
+                  const float *eb, const float *wr, const float *s0, float *o, float *s_out) {
+    ChunkArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.la = la; a.eb = eb; a.wr = d->tie_write_to_erase ? nullptr : wr;
+    a.s0 = s0; a.o = o; a.s_out = s_out;
+    a.B = d->batch; a.T = d->seqlen; a.H = d->heads; a.dk = d->dk; a.dv = d->dv;
+    a.C = static_cast<int>(d->chunk);
+    a.bf16 = d->qkv_dtype == GDN2_BF16;
+    a.la_key = d->decay_kind == GDN2_GATE_KEY;
+    a.eb_key = d->erase_kind == GDN2_GATE_KEY;
+    a.wr_key = d->tie_write_to_erase ? a.eb_key : d->write_kind == GDN2_GATE_KEY;
+    a.q_scale = d->q_scale;
+    return a;
+}
+
+// Whether the two-pass matrix-core path covers the request (it then needs a
+// workspace of chunk_split_workspace bytes).
+bool split_path(const gdn2_desc *d) {
+    static const float placeholder = 0.f;  // stands for an untied write gate
+    const ChunkArgs a = args_of(d, nullptr, nullptr, nullptr, nullptr, nullptr, &placeholder, nullptr,
+                                nullptr, nullptr);
+    return d->batch * d->seqlen > 0 && gdn2::chunk_split_supported(a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -110,7 +137,7 @@ gdn2_status gdn2_chunk_fwd_workspace(const gdn2_desc *desc, size_t *bytes) {
     gdn2_status st = check_common(desc);
     if (st != GDN2_OK) return st;
     if (desc->chunk != 16 && desc->chunk != 32 && desc->chunk != 64) return GDN2_ERR_UNSUPPORTED;
-    *bytes = 0;
+    *bytes = split_path(desc) ? gdn2::chunk_split_workspace(desc->batch, desc->heads, desc->seqlen) : 0;
     return GDN2_OK;
 }
 
@@ -121,7 +148,11 @@ gdn2_status gdn2_chunk_fwd(const gdn2_desc *d, const void *q, const void *k, con
     size_t need = 0;
     gdn2_status st = gdn2_chunk_fwd_workspace(d, &need);
     if (st != GDN2_OK) return st;
-    if (ws_bytes < need || (need > 0 && !workspace)) return GDN2_ERR_WORKSPACE;
+    // no workspace: the single-pass kernels; a workspace must be large enough
+    // and 256-byte aligned
+    const bool use_ws = workspace != nullptr && ws_bytes > 0;
+    if (use_ws && (ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0))
+        return GDN2_ERR_WORKSPACE;
     const int64_t T = d->seqlen;
     const bool work = d->batch * T > 0;
     if (work && (!q || !k || !v || !log_decay || !erase || !o)) return GDN2_ERR_NULL;
@@ -137,6 +168,12 @@ gdn2_status gdn2_chunk_fwd(const gdn2_desc *d, const void *q, const void *k, con
     }
     if (overlap(o_sp, s_in) || overlap(o_sp, s_out)) return GDN2_ERR_ALIAS;
     if (overlap(s_out, s_in) && s_out.lo != s_in.lo) return GDN2_ERR_ALIAS;
+    if (use_ws) {
+        const Span ws = span_of(workspace, static_cast<int64_t>(ws_bytes));
+        for (const Span &x : in)
+            if (overlap(ws, x)) return GDN2_ERR_ALIAS;
+        if (overlap(ws, o_sp) || overlap(ws, s_in) || overlap(ws, s_out)) return GDN2_ERR_ALIAS;
+    }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (!work) {
@@ -145,18 +182,9 @@ gdn2_status gdn2_chunk_fwd(const gdn2_desc *d, const void *q, const void *k, con
             return hip_status(gdn2::launch_state_copy(state0, state_out, sz.st / 4, s));
         return GDN2_OK;
     }
-    ChunkArgs a;
-    a.q = q; a.k = k; a.v = v;
-    a.la = log_decay; a.eb = erase; a.wr = d->tie_write_to_erase ? nullptr : write;
-    a.s0 = state0; a.o = o; a.s_out = state_out;
-    a.B = d->batch; a.T = T; a.H = d->heads; a.dk = d->dk; a.dv = d->dv;
-    a.C = static_cast<int>(d->chunk);
-    a.bf16 = d->qkv_dtype == GDN2_BF16;
-    a.la_key = d->decay_kind == GDN2_GATE_KEY;
-    a.eb_key = d->erase_kind == GDN2_GATE_KEY;
-    a.wr_key = d->tie_write_to_erase ? a.eb_key : d->write_kind == GDN2_GATE_KEY;
-    a.q_scale = d->q_scale;
+    const ChunkArgs a = args_of(d, q, k, v, log_decay, erase, write, state0, o, state_out);
     if (a.B * a.H > 0x7fffffffLL) return GDN2_ERR_UNSUPPORTED;
+    if (use_ws && need > 0) return hip_status(gdn2::launch_chunk_split(a, workspace, s));
     if (gdn2::chunk_mfma_supported(a)) return hip_status(gdn2::launch_chunk_mfma(a, s));
     return hip_status(gdn2::launch_chunk_general(a, s));
 }

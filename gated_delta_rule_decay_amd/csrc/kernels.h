@@ -40,6 +40,13 @@ hipError_t launch_chunk_general(const ChunkArgs &a, hipStream_t s);
 bool chunk_mfma_supported(const ChunkArgs &a);
 hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);
 
+// bf16, dk = dv = 128, C = 64, two passes through a device workspace: the
+// chunk-local products of every chunk in parallel, then the scan over chunks.
+// Same coverage as the single-pass MFMA path.
+bool chunk_split_supported(const ChunkArgs &a);
+size_t chunk_split_workspace(int64_t B, int64_t H, int64_t T);
+hipError_t launch_chunk_split(const ChunkArgs &a, void *ws, hipStream_t s);
+
 // Recurrent decode step.
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
 

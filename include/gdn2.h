@@ -96,8 +96,11 @@ int gdn2_abi_version(void);
 /* Static, human-readable name of a status code. */
 const char *gdn2_status_str(int status);
 
-/* Device workspace, in bytes, that gdn2_chunk_fwd needs for `desc`
- * (0 when it needs none).  Same validation as gdn2_chunk_fwd. */
+/* Device workspace, in bytes, for the two-pass form of gdn2_chunk_fwd on
+ * `desc`; 0 when the request has no two-pass kernel (it then always runs in
+ * one pass).  The two-pass form covers bf16 q/k/v, dk = dv = 128, chunk 64
+ * and gates all of one kind; it needs B*H*ceil(T/64) records of about
+ * 97 KiB.  Same validation as gdn2_chunk_fwd. */
 gdn2_status gdn2_chunk_fwd_workspace(const gdn2_desc *desc, size_t *bytes);
 
 /*
@@ -121,8 +124,15 @@ gdn2_status gdn2_chunk_fwd_workspace(const gdn2_desc *desc, size_t *bytes);
  *   state_out    final state [B,H,dk,dv] fp32, or NULL to skip.  It may be
  *                exactly state0 (updated in place); any other overlap with
  *                an input is GDN2_ERR_ALIAS.
- *   workspace    device scratch of ws_bytes >= gdn2_chunk_fwd_workspace();
- *                may be NULL when that is 0.
+ *   workspace    NULL (or ws_bytes 0): run in one pass, no scratch.
+ *                Otherwise device scratch of ws_bytes >=
+ *                gdn2_chunk_fwd_workspace(), 256-byte aligned, else
+ *                GDN2_ERR_WORKSPACE; it must not overlap any other argument
+ *                (GDN2_ERR_ALIAS).  The two-pass form first computes every
+ *                chunk's state-independent products in parallel into it,
+ *                then scans the chunks; its contents need no initialisation
+ *                and are undefined afterwards.  Calls that share one
+ *                workspace must not overlap in time.
  * With T == 0 nothing is read but state0, o is untouched and state_out
  * receives state0 (or zeros).
  */

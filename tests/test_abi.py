@@ -99,7 +99,7 @@ def test_write_kind_ignored_when_tied(lib):
     n = ctypes.c_size_t(99)
     d = good(tied=True, write_kind=9)
     assert lib.gdn2_chunk_fwd_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
-    assert n.value == 0
+    assert n.value == split_bytes(2, 4, 128)
 
 
 def test_aliasing(lib):
@@ -127,8 +127,36 @@ def test_decode_needs_one_token(lib):
     assert step(lib, good(seqlen=0)) == 2
 
 
+def split_bytes(B, H, T):
+    """Two-pass workspace: per (chain, chunk) a 96 KiB fp16 record, 128 fp32
+    chunk-end decays and one int flag, each region 256-byte aligned."""
+    a = lambda x: (x + 255) // 256 * 256
+    n = B * H * ((T + 63) // 64)
+    return a(n * 98304) + a(n * 512) + a(n * 4)
+
+
+def query(lib, d):
+    n = ctypes.c_size_t(123)
+    assert lib.gdn2_chunk_fwd_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
+    return n.value
+
+
 def test_workspace_query(lib):
-    for d in (good(), good(qkv_dtype=0, dk=32, dv=32, chunk=16), good(tied=True, decay_kind=0)):
-        n = ctypes.c_size_t(123)
-        assert lib.gdn2_chunk_fwd_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
-        assert n.value == 0
+    # the two-pass path covers bf16, dk = dv = 128, C = 64, gates of one kind
+    assert query(lib, good()) == split_bytes(2, 4, 128)
+    assert query(lib, good(seqlen=100)) == split_bytes(2, 4, 100)
+    assert query(lib, good(tied=True, decay_kind=0, erase_kind=0)) == split_bytes(2, 4, 128)
+    # everything else runs single-pass and needs none
+    for d in (good(qkv_dtype=0, dk=32, dv=32, chunk=16), good(tied=True, decay_kind=0),
+              good(dk=64), good(chunk=32), good(seqlen=0), good(batch=0)):
+        assert query(lib, d) == 0
+
+
+def test_workspace_checks(lib):
+    d = good()
+    need = split_bytes(2, 4, 128)
+    assert fwd(lib, d, ws=WS, wsb=need - 1) == 6       # too small
+    assert fwd(lib, d, ws=WS + 16, wsb=need) == 6      # not 256-byte aligned
+    assert fwd(lib, d, ws=Q, wsb=need) == 5            # on top of q
+    assert fwd(lib, d, ws=O - 256, wsb=need) == 5      # runs into o
+    assert fwd(lib, d, ws=SO - need + 256, wsb=need) == 5  # runs into state_out

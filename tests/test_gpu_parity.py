@@ -23,8 +23,13 @@ def _tol(w):
     return TOL_F32 if w.qkv_dtype == "f32" else TOL_BF16
 
 
-def _check(w, inp, chunk, q_scale=1.0):
-    o, S = gpu_chunk(inp, chunk, q_scale=q_scale)
+# The bf16 / dk = dv = 128 / C = 64 requests have two kernels: the two-pass
+# form (with a workspace, the default) and the single-pass one (none).
+PATHS = [pytest.param(True, id="two-pass"), pytest.param(False, id="one-pass")]
+
+
+def _check(w, inp, chunk, q_scale=1.0, ws=True):
+    o, S = gpu_chunk(inp, chunk, q_scale=q_scale, workspace=ws)
     o_ref, S_ref = oracle_chunk(inp, q_scale=q_scale)
     eo, es = rel_l2(o, o_ref), rel_l2(S, S_ref)
     print(f"  rel_l2 o={eo:.3e} S={es:.3e} (tol {_tol(w):.0e})", flush=True)
@@ -38,11 +43,12 @@ def test_tiny_fp32_workload():
     _check(w, synth.make_inputs(w, wid=0), w.chunk)
 
 
+@pytest.mark.parametrize("ws", PATHS)
 @pytest.mark.parametrize("wid,B,T,H", [(1, 1, 200, 2), (2, 1, 200, 2), (2, 2, 131, 1),
                                        (3, 1, 4200, 1)])
-def test_reduced_bf16_workloads(wid, B, T, H):
+def test_reduced_bf16_workloads(wid, B, T, H, ws):
     w = W[wid].scaled(B=B, T=T, H=H)
-    _check(w, synth.make_inputs(w, seed=1000 + wid * 7 + T), w.chunk)
+    _check(w, synth.make_inputs(w, seed=1000 + wid * 7 + T), w.chunk, ws=ws)
 
 
 @pytest.mark.parametrize("chunk", [16, 32, 64])
@@ -58,24 +64,27 @@ def test_odd_shapes(dtype, dk, dv, T):
     _check(w, synth.make_inputs(w, seed=dk * 1000 + dv + T), 32)
 
 
+@pytest.mark.parametrize("ws", PATHS)
 @pytest.mark.parametrize("gates,tied", [("head", False), ("key", True), ("head", True)])
-def test_gate_kinds(gates, tied):
+def test_gate_kinds(gates, tied, ws):
     w = W[2].scaled(B=1, T=160, H=2, gates=gates, tied=tied)
-    _check(w, synth.make_inputs(w, seed=5 + tied), 64)
+    _check(w, synth.make_inputs(w, seed=5 + tied), 64, ws=ws)
 
 
-def test_q_scale_and_zero_state():
+@pytest.mark.parametrize("ws", PATHS)
+def test_q_scale_and_zero_state(ws):
     w = W[2].scaled(B=1, T=96, H=2, s0_std=0.0)
-    _check(w, synth.make_inputs(w, seed=9), 64, q_scale=0.125)
+    _check(w, synth.make_inputs(w, seed=9), 64, q_scale=0.125, ws=ws)
 
 
-def test_edge_lengths():
+@pytest.mark.parametrize("ws", PATHS)
+def test_edge_lengths(ws):
     import torch
     from gated_delta_rule_decay_amd import chunk_fwd
 
     for T in (1, 63, 64, 65):
         w = W[2].scaled(B=1, T=T, H=1)
-        _check(w, synth.make_inputs(w, seed=T), 64)
+        _check(w, synth.make_inputs(w, seed=T), 64, ws=ws)
     # T == 0: the final state is the initial state, o untouched
     w = W[2].scaled(B=1, T=0, H=2)
     d = to_device(synth.make_inputs(w, seed=3))
@@ -107,11 +116,12 @@ def test_in_place_state_and_resume():
     assert rel_l2(S_full.cpu().numpy(), S_ref) <= TOL_BF16
 
 
-def test_run_to_run_bitwise():
+@pytest.mark.parametrize("ws", PATHS)
+def test_run_to_run_bitwise(ws):
     w = W[2].scaled(B=2, T=300, H=2)
     inp = synth.make_inputs(w, seed=12)
-    o1, S1 = gpu_chunk(inp, 64)
-    o2, S2 = gpu_chunk(inp, 64)
+    o1, S1 = gpu_chunk(inp, 64, workspace=ws)
+    o2, S2 = gpu_chunk(inp, 64, workspace=ws)
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
 
 
@@ -241,31 +251,35 @@ def _bf16_case(seed, T=200, H=2, B=1, tied=False, gates="key"):
     return w, synth.make_inputs(w, seed=seed)
 
 
-def test_near_zero_decay_spikes():
+@pytest.mark.parametrize("ws", PATHS)
+def test_near_zero_decay_spikes(ws):
     # a -> 0 on a few tokens and channels: exp(-1000) is 0, the old state is gone there
     w, inp = _bf16_case(31)
     inp["log_decay"][:, 70:73, :, :40] = -1000.0
     inp["log_decay"][:, 130, :, :] = -1000.0
-    _check(w, inp, 64)
+    _check(w, inp, 64, ws=ws)
 
 
-def test_strong_uniform_decay():
+@pytest.mark.parametrize("ws", PATHS)
+def test_strong_uniform_decay(ws):
     # every token decays every channel by e^-3: factors leave fp16 range inside a block
     w, inp = _bf16_case(32)
     inp["log_decay"][:, 64:128] = -3.0
-    _check(w, inp, 64)
+    _check(w, inp, 64, ws=ws)
     w, inp = _bf16_case(33, tied=True, gates="head")
     inp["log_decay"][:] = -2.5
-    _check(w, inp, 64)
+    _check(w, inp, 64, ws=ws)
 
 
-def test_no_decay_is_delta_rule():
+@pytest.mark.parametrize("ws", PATHS)
+def test_no_decay_is_delta_rule(ws):
     w, inp = _bf16_case(34)
     inp["log_decay"][:] = 0.0
-    _check(w, inp, 64)
+    _check(w, inp, 64, ws=ws)
 
 
-def test_hold_keeps_state():
+@pytest.mark.parametrize("ws", PATHS)
+def test_hold_keeps_state(ws):
     # a = 1 and b = w = 0: the state is held (exactly, since every write is zero)
     import torch
     from gated_delta_rule_decay_amd import chunk_fwd
@@ -275,7 +289,44 @@ def test_hold_keeps_state():
     inp["erase"][:] = 0.0
     inp["write"][:] = 0.0
     d = to_device(inp)
-    o, S = chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"])
+    o, S = chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"],
+                     workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(S, d["S0"])
-    _check(w, inp, 64)
+    _check(w, inp, 64, ws=ws)
+
+
+# ---- the two-pass form's own cases ---------------------------------------
+
+def test_workspace_reused_across_sizes():
+    # one caller-owned workspace, stale records from a larger call first
+    import torch
+    from gated_delta_rule_decay_amd import chunk_fwd_workspace
+    from gated_delta_rule_decay_amd.binding import make_desc
+
+    need = chunk_fwd_workspace(make_desc(2, 300, 2, 128, 128))
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    for B, T, H, seed in ((2, 300, 2, 41), (1, 70, 2, 42), (1, 1, 1, 43)):
+        w = W[2].scaled(B=B, T=T, H=H)
+        _check(w, synth.make_inputs(w, seed=seed), 64, ws=ws)
+    with pytest.raises(Exception):
+        _check(W[2].scaled(B=2, T=400, H=2), synth.make_inputs(W[2].scaled(B=2, T=400, H=2), seed=44),
+               64, ws=ws)
+
+
+def test_large_state_runs_exactly():
+    # |S| beyond the fp16 operand range: those chunks take the exact recurrence
+    w, inp = _bf16_case(45, T=200)
+    inp["S0"] = inp["S0"] * 3.0e5
+    _check(w, inp, 64, ws=True)
+
+
+def test_large_grams_run_exactly():
+    # queries scaled by 2^10 (exact in bf16) and a write gate of ~1000: every
+    # operand stays in fp16 range but the query Grams do not, so the chunks
+    # are flagged and recomputed exactly
+    w, inp = _bf16_case(46, T=150)
+    inp["q"] = inp["q"] * 1024.0
+    inp["q_bf16"] = (inp["q_bf16"].astype(np.uint32) + (10 << 7)).astype(np.uint16)
+    inp["write"] = inp["write"] * 1000.0
+    _check(w, inp, 64, ws=True)

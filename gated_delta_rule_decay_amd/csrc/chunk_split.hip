@@ -19,7 +19,7 @@
 // 512-lane workgroup per task, persistent, with the next task's inputs
 // prefetched into registers -- and writes W, Qe, Etil^T, G and Oe as fp16
 // fragments in exactly the register order the scan's MFMA operands take,
-// plus e^gC and a flag.  Pass 2 (chunk_scan_kernel) gives each wave one
+// plus e^gC (which also carries the exact-path mark).  Pass 2 (chunk_scan_kernel) gives each wave one
 // chain and 16*NB value columns; the fp32 state slice (128 x 16*NB) stays in
 // MFMA accumulators, every operand is one coalesced 16-byte load per lane,
 // and waves never synchronise, so a chain's value columns proceed on as
@@ -29,6 +29,8 @@
 // range is flagged by pass 1; pass 2 runs it as the exact fp32 token
 // recurrence on the raw inputs instead (so does a chunk whose state or erase
 // read would overflow fp16).
+#include <utility>
+
 #include "chunk_common.h"
 
 namespace gdn2 {
@@ -44,9 +46,13 @@ using namespace mfma;
 //                                    of block kb in slots 8m..8m+7
 //   EtT    [it 8][kb 2][lane 64][8]  lane i+16m: key channel 16it+i, tokens
 //                                    of block kb in slots 8m..8m+7
-//   G      [ct 8][it 8][lane 64][4]  accumulator tile: lane j+16m holds
-//                                    G[16it+4m+e][16ct+j]
-//   Oe     [ct 8][rt 4][lane 64][4]  lane j+16m holds Oe[16rt+4m+e][16ct+j]
+//   G      [ct 8][ip 4][lane 64][8]  accumulator tiles it = 2ip, 2ip+1: lane
+//                                    j+16m holds G[16it+4m+e][16ct+j] in
+//                                    elements 4(it&1)+e
+//   OeT    [ct 8][rp 2][lane 64][8]  transposed tiles rt = 2rp, 2rp+1: lane
+//                                    t+16m holds Oe[16rt+t][16ct+4m+e] in
+//                                    elements 4(rt&1)+e (four adjacent value
+//                                    columns of one token)
 constexpr int64_t OFF_W = 0;
 constexpr int64_t OFF_Q = 8192;
 constexpr int64_t OFF_E = 16384;
@@ -57,8 +63,8 @@ constexpr float MAX_RESULT = 30000.f;  // largest |fp16 value| a record may hold
 
 struct SplitWs {
     _Float16 *frag;  // [task][REC]
-    float *gam;      // [task][D]   e^gC per key channel
-    int *flag;       // [task]      1: run the chunk exactly
+    float *gam;      // [task][D]   e^gC per key channel; -1 in channel 0 marks
+                     //             a chunk to be run as the exact recurrence
 };
 
 struct PrepSmem {
@@ -182,7 +188,7 @@ __device__ __forceinline__ bool wq_tiles(const PrepSmem &S, _Float16 *rec, int k
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             wt[st][cc] = mfma32(tn[st][0], kbf[cc][0], splat(0.f));
-            if (st >= 2) wt[st][cc] = mfma32(tn[st][1], kbf[cc][RH], wt[st][cc]);
+            if (st >= 2) wt[st][cc] = mfma32(tn[st][RH], kbf[cc][RH], wt[st][cc]);
         }
     bool big = false;
 #pragma unroll
@@ -235,7 +241,8 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
     }
 
     for (; task < ntask; task += gridDim.x) {
-        __syncthreads();  // previous task done with every buffer
+        __syncthreads();  // previous task done with every buffer (and with S.wide)
+        if (tid == 0) S.wide = 0;
         // lane coordinates, re-derived every task so that the LDS addresses
         // built from them are not hoisted out of the loop (and spilled)
         int tl = tid;
@@ -373,21 +380,26 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             __syncthreads();  // U complete in u16
             if (next < ntask) load_part<2, TIED>(R, a, pn, tid);
 
-            // ---- (4) Oe[:, ct] = P V - R U -> HBM ----------------------------
+            // ---- (4) Oe^T[ct, :] = V^T P^T - U^T R^T -> HBM (transposed, so
+            //      the scan's output tiles hold adjacent columns per lane)
             {
                 const _Float16 *pp = TIED ? S.r16 : S.p16;
                 const h8 ub0 = join(to_h4(uacc[0]), to_h4(uacc[1])), ub1 = join(to_h4(uacc[2]), to_h4(uacc[3]));
+                f4 acc[4];
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
-                    f4 acc = splat(0.f);
+                    acc[rt] = splat(0.f);
 #pragma unroll
                     for (int ks = 0; ks <= (rt >> 1); ++ks) {
-                        acc = mfma32(*reinterpret_cast<const h8 *>(&pp[(16 * rt + lr) * SP + 32 * ks + 8 * lg]), vb[ks], acc);
-                        acc = mfma32(perm_frag(S.r16, rt, ks, lr, lg), ks ? -ub1 : -ub0, acc);
+                        acc[rt] = mfma32(vb[ks], *reinterpret_cast<const h8 *>(&pp[(16 * rt + lr) * SP + 32 * ks + 8 * lg]), acc[rt]);
+                        acc[rt] = mfma32(ks ? -ub1 : -ub0, perm_frag(S.r16, rt, ks, lr, lg), acc[rt]);
                     }
-                    big |= out_of_range(acc);
-                    *reinterpret_cast<h4 *>(rec + OFF_O + ((ct * 4 + rt) * 64 + lane) * 4) = to_h4(acc);
+                    big |= out_of_range(acc[rt]);
                 }
+#pragma unroll
+                for (int rp = 0; rp < 2; ++rp)
+                    *reinterpret_cast<h8 *>(rec + OFF_O + ((ct * 2 + rp) * 64 + lane) * 8) =
+                        join(to_h4(acc[2 * rp]), to_h4(acc[2 * rp + 1]));
             }
             // ---- (5) G[it, :] = Util^T V - Etil^T U -> HBM -------------------
             {
@@ -405,163 +417,182 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                         acc = mfma32(kb ? ne1 : ne0, up, acc);
                     }
                     big |= out_of_range(acc);
-                    *reinterpret_cast<h4 *>(rec + OFF_G + ((c2 * 8 + it) * 64 + lane) * 4) = to_h4(acc);
+                    *reinterpret_cast<h4 *>(rec + OFF_G + ((c2 * 4 + (it >> 1)) * 64 + lane) * 8 + 4 * (it & 1)) = to_h4(acc);
                 }
             }
             if (big) S.wide = 1;
-            if (tid < D) w.gam[task * D + tid] = S.gce[tid];
         } else if (next < ntask) {
             load_part<2, TIED>(R, a, pn, tid);
         }
         if (next < ntask) load_part<3, TIED>(R, a, pn, tid);
         __syncthreads();
-        if (tid == 0) {
-            w.flag[task] = (wide || S.wide) ? 1 : 0;
-            S.wide = 0;
-        }
+        // e^gC per key channel; a chunk to be run exactly is marked by -1 in
+        // channel 0 (e^gC is never negative)
+        const bool exact = wide || S.wide;  // reset after the next task's first barrier
+        if (tid < D) w.gam[task * D + tid] = (tid == 0 && exact) ? -1.f : S.gce[tid];
     }
 }
 
 // ----------------------------------------------------------------------------
-// Pass 2: the scan over chunks.  One wave = one chain x NB value tiles.
-// The per-chunk operands a wave of NB value tiles needs besides W, Qe, EtT.
-template <int NB>
-struct ScanSmall {
-    h4 g[NB][8], o[NB][4];
-    f4 gam[8];
-    int flag;
-};
+// Pass 2: the scan over chunks.  A workgroup of SCAN_W waves owns one chain
+// and SCAN_W value tiles (16 columns each, one per wave); each wave keeps its
+// 128 x 16 fp32 state slice in accumulators.  Everything a chunk needs -- W,
+// Qe, EtT (48 KiB, shared by the waves), the workgroup's slices of G and Oe
+// and e^gC -- is copied by the memory unit straight into LDS
+// (global_load_lds) one chunk ahead, into one of two slots, by SCAN_P copy
+// waves of the same workgroup, so the compute waves never wait behind
+// memory instructions; one barrier per chunk hands a slot over.
+constexpr int SCAN_W = 4;                 // compute waves (one value tile each)
+constexpr int SCAN_P = 4;                 // copy waves
+constexpr int SCAN_NTH = 64 * (SCAN_W + SCAN_P);
+constexpr int SLOT_F = 3 * 8192;          // halves of W | Qe | EtT
+constexpr int SLOT_G = SCAN_W * 4 * 512;  // halves of G for my tiles (4 pair rows of 512)
+constexpr int SLOT_O = SCAN_W * 2 * 512;  // halves of Oe^T for my tiles
+constexpr int SLOT_H = SLOT_F + SLOT_G + SLOT_O;
+constexpr int SLOT_PIECES = SLOT_H * 2 / 16 / (64 * SCAN_P);  // 1 KiB copies per copy wave (18)
+static_assert(SLOT_H * 2 % (1024 * SCAN_P) == 0, "slot copies must tile the copy waves");
 
-__device__ __forceinline__ void load_wq(h8 (&x)[4][4], const _Float16 *p, int lane) {
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) x[rt][kb] = *reinterpret_cast<const h8 *>(p + ((rt * 4 + kb) * 64 + lane) * 8);
-}
-__device__ __forceinline__ void load_e(h8 (&x)[8][2], const _Float16 *p, int lane) {
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (other counters untouched)
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <bool TIED, bool KEYG>
+__global__ void __launch_bounds__(SCAN_NTH) chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, int xcd_map) {
+    // two distinct slots (distinct objects, so the compiler can tell the slot
+    // being filled from the one being read)
+    __shared__ __attribute__((aligned(16))) _Float16 fr0[SLOT_H], fr1[SLOT_H];
+    __shared__ __attribute__((aligned(16))) float gm0[2 * D], gm1[2 * D];
+    const int G = blockIdx.x;
+    int chain, half;
+    if (xcd_map) {  // a chain's two workgroups on one XCD, so its records are read into one L2
+        half = (G / 8) & 1;
+        chain = (G / 16) * 8 + (G % 8);
+    } else {
+        half = G & 1;
+        chain = G / 2;
+    }
+    const int64_t b = chain / a.H, h = chain % a.H;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool copier = wv >= SCAN_W;
+    const int ct = SCAN_W * half + (copier ? 0 : wv);  // my value tile (compute waves)
+    const int64_t sbase = (b * a.H + h) * static_cast<int64_t>(D) * D;
+    const int64_t task0 = static_cast<int64_t>(chain) * nc;
+
+    // state slice: tile it holds S[16it+4lg+e][16ct+lr]
+    f4 sacc[8];
 #pragma unroll
     for (int it = 0; it < 8; ++it)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) x[it][kb] = *reinterpret_cast<const h8 *>(p + ((it * 2 + kb) * 64 + lane) * 8);
-}
-
-template <int NB, bool TIED, bool KEYG>
-__global__ void __launch_bounds__(64) chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, int ngrp, int xcd_map) {
-    const int L = blockIdx.x;
-    int chain, grp;
-    if (xcd_map) {  // a chain's waves on one XCD, so its records are read into one L2
-        grp = (L / 8) % ngrp;
-        chain = (L / (8 * ngrp)) * 8 + (L % 8);
-    } else {
-        grp = L % ngrp;
-        chain = L / ngrp;
-    }
-    const int64_t b = chain / a.H, h = chain % a.H;
-    const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
-    const int ct0 = grp * NB;
-    const int64_t sbase = (b * a.H + h) * static_cast<int64_t>(D) * D;
-
-    // state slice: tile (n, it) holds S[16it+4lg+e][16(ct0+n)+lr]
-    f4 sacc[NB][8];
-#pragma unroll
-    for (int n = 0; n < NB; ++n)
-#pragma unroll
-        for (int it = 0; it < 8; ++it)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t c = 16 * it + 4 * lg + e, v = 16 * (ct0 + n) + lr;
-                sacc[n][it][e] = a.s0 ? a.s0[sbase + c * D + v] : 0.f;
-            }
-
-    // Every operand of chunk n+1 is requested while chunk n is computed (each
-    // right after its last use in chunk n), so the scan waits on memory only
-    // when a chunk's compute is shorter than the load latency.
-    const int64_t task0 = static_cast<int64_t>(chain) * nc;
-    h8 wf[4][4], qf[4][4], ef[8][2];
-    ScanSmall<NB> cur, nx;
-    auto load_small = [&](ScanSmall<NB> &x, int64_t task) {
-        const _Float16 *rec = w.frag + task * REC;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-#pragma unroll
-            for (int it = 0; it < 8; ++it)
-                x.g[j][it] = *reinterpret_cast<const h4 *>(rec + OFF_G + (((ct0 + j) * 8 + it) * 64 + lane) * 4);
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-                x.o[j][rt] = *reinterpret_cast<const h4 *>(rec + OFF_O + (((ct0 + j) * 4 + rt) * 64 + lane) * 4);
+        for (int e = 0; e < 4; ++e) {
+            const int64_t c = 16 * it + 4 * lg + e, v = 16 * ct + lr;
+            sacc[it][e] = (a.s0 && !copier) ? a.s0[sbase + c * D + v] : 0.f;
         }
+
+    // Copy chunk `task` into a slot: W | Qe | EtT (record offset 0), then my
+    // workgroup's G and Oe^T tiles (contiguous in the record), then e^gC.
+    // Each wave moves 1 KiB per instruction (lane l -> bytes 16l..16l+15).
+    auto fill = [&](_Float16 *fr, float *gm, int64_t task, int pw) __attribute__((always_inline)) {
+        const char *rec = reinterpret_cast<const char *>(w.frag + task * REC);
+        const char *srcg = rec + 2 * (OFF_G + static_cast<int64_t>(SCAN_W * half) * 4 * 512);
+        const char *srco = rec + 2 * (OFF_O + static_cast<int64_t>(SCAN_W * half) * 2 * 512);
 #pragma unroll
-        for (int it = 0; it < 8; ++it) x.gam[it] = *reinterpret_cast<const f4 *>(&w.gam[task * D + 16 * it + 4 * lg]);
-        x.flag = w.flag[task];
+        for (int i = 0; i < SLOT_PIECES; ++i) {
+            const int byte = 1024 * (SCAN_P * i + pw);  // my 1 KiB block of the slot
+            const char *src = byte < 2 * SLOT_F ? rec + byte
+                            : byte < 2 * (SLOT_F + SLOT_G) ? srcg + (byte - 2 * SLOT_F)
+                                                           : srco + (byte - 2 * (SLOT_F + SLOT_G));
+            __builtin_amdgcn_global_load_lds(src + 16 * lane, reinterpret_cast<char *>(fr) + byte, 16, 0, 0);
+        }
+        // e^gC: copy waves 0,1 bring channels 0..127
+        if (pw < 2) __builtin_amdgcn_global_load_lds(w.gam + task * D + 64 * pw + lane, gm + 64 * pw, 4, 0, 0);
     };
-    load_wq(wf, w.frag + task0 * REC + OFF_W, lane);
-    load_wq(qf, w.frag + task0 * REC + OFF_Q, lane);
-    load_e(ef, w.frag + task0 * REC + OFF_E, lane);
-    load_small(cur, task0);
 
-    for (int n = 0; n < nc; ++n) {
+    // One chunk n on this wave, from slot (fr, gm).
+    auto compute = [&](int n, const _Float16 *fr, const float *gm) __attribute__((always_inline)) {
+        const _Float16 *fg = fr + SLOT_F + wv * 4 * 512;            // my G pairs
+        const _Float16 *fo = fr + SLOT_F + SLOT_G + wv * 2 * 512;   // my Oe^T pairs
         const int64_t t0 = static_cast<int64_t>(n) * C;
-        const int64_t nxt = task0 + (n + 1 < nc ? n + 1 : n);
-        load_small(nx, nxt);
-
         // the fp16 copies of the state and of the erase read must stay finite
         bool big = false;
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-#pragma unroll
-            for (int it = 0; it < 8; ++it) big |= !(fmaxf(fmaxf(fabsf(sacc[j][it][0]), fabsf(sacc[j][it][1])),
-                                                          fmaxf(fabsf(sacc[j][it][2]), fabsf(sacc[j][it][3]))) <= 16384.f);
-        bool bad = cur.flag != 0 || __ballot(big) != 0;
-        f4 p1[NB][4], oacc[NB][4];
+        for (int it = 0; it < 8; ++it)
+            big |= !(fmaxf(fmaxf(fabsf(sacc[it][0]), fabsf(sacc[it][1])), fmaxf(fabsf(sacc[it][2]), fabsf(sacc[it][3]))) <= 16384.f);
+        bool bad = gm[0] < 0.f || __ballot(big) != 0;  // chunk marked for the exact path
+        f4 p1[4], oacc[4];
+        h8 ef[8][2];
         big = false;
         if (!bad) {
-            // P1 = W S and O = Qe S + Oe; the state tiles 2kb, 2kb+1 form the
-            // B operand of key block kb in the permuted slot order
+            // Fragments are read from LDS ahead of use (W/Qe of the next row
+            // tile while the current one is multiplied, EtT at the start),
+            // each group fenced so the scheduler keeps reads early.
+            auto read_wq = [&](h8 (&x)[2][4], int rt) __attribute__((always_inline)) {
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                h8 sb[4];
-#pragma unroll
-                for (int kb = 0; kb < 4; ++kb) sb[kb] = join(to_h4(sacc[j][2 * kb]), to_h4(sacc[j][2 * kb + 1]));
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    f4 p = splat(0.f), o = to_f4(cur.o[j][rt]);
-#pragma unroll
-                    for (int kb = 0; kb < 4; ++kb) {
-                        p = mfma32(wf[rt][kb], sb[kb], p);
-                        o = mfma32(qf[rt][kb], sb[kb], o);
-                    }
-                    p1[j][rt] = p;
-                    oacc[j][rt] = o;
-                    big |= out_of_range(p);
+                for (int kb = 0; kb < 4; ++kb) {
+                    const int off = ((rt * 4 + kb) * 64 + lane) * 8;
+                    x[0][kb] = *reinterpret_cast<const h8 *>(fr + OFF_W + off);
+                    x[1][kb] = *reinterpret_cast<const h8 *>(fr + OFF_Q + off);
                 }
+            };
+            h8 wq[2][2][4];
+            read_wq(wq[0], 0);
+#pragma unroll
+            for (int it = 0; it < 8; ++it)
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) ef[it][k2] = *reinterpret_cast<const h8 *>(fr + OFF_E + ((it * 2 + k2) * 64 + lane) * 8);
+            // P1 = W S and O^T = S^T Qe^T + Oe^T.  State tiles 2kb, 2kb+1 in
+            // the record's permuted slot order are both the B operand of key
+            // block kb (for W S) and the A operand of S^T (for O^T).
+            h8 sb[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) sb[kb] = join(to_h4(sacc[2 * kb]), to_h4(sacc[2 * kb + 1]));
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                if (rt < 3) read_wq(wq[(rt + 1) & 1], rt + 1);
+                const h8 oe = *reinterpret_cast<const h8 *>(fo + ((rt >> 1) * 64 + lane) * 8);
+                __builtin_amdgcn_sched_barrier(0);
+                f4 p = splat(0.f);
+                f4 o = (rt & 1) ? f4{(float)oe[4], (float)oe[5], (float)oe[6], (float)oe[7]}
+                                : f4{(float)oe[0], (float)oe[1], (float)oe[2], (float)oe[3]};
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    p = mfma32(wq[rt & 1][0][kb], sb[kb], p);
+                    o = mfma32(sb[kb], wq[rt & 1][1][kb], o);
+                }
+                p1[rt] = p;
+                oacc[rt] = o;
+                big |= out_of_range(p);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // W and Qe of this chunk are consumed: fetch the next chunk's
-        load_wq(wf, w.frag + nxt * REC + OFF_W, lane);
-        load_wq(qf, w.frag + nxt * REC + OFF_Q, lane);
-
         bad = bad || __ballot(big) != 0;
         if (!bad) {
+            f4 gam[8];
+            h8 gp[4];
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
-                const int64_t col = 16 * (ct0 + j) + lr;
+            for (int it = 0; it < 8; ++it) gam[it] = *reinterpret_cast<const f4 *>(&gm[16 * it + 4 * lg]);
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
+            for (int ip = 0; ip < 4; ++ip) gp[ip] = *reinterpret_cast<const h8 *>(fg + (ip * 64 + lane) * 8);
+            __builtin_amdgcn_sched_barrier(0);
+            // O^T tile: lane t+16m holds token 16rt+t, value columns
+            // 16ct+4m..+3 -> one 16-byte store per lane and tile
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int64_t t = t0 + 16 * rt + 4 * lg + e;
-                        if (t < a.T) a.o[((b * a.T + t) * a.H + h) * D + col] = oacc[j][rt][e];
-                    }
-                // S <- Diag(e^gC) S + G - Etil^T P1, tokens in permuted slots
-                const h8 pb0 = join(to_h4(-p1[j][0]), to_h4(-p1[j][1]));
-                const h8 pb1 = join(to_h4(-p1[j][2]), to_h4(-p1[j][3]));
+            for (int rt = 0; rt < 4; ++rt) {
+                const int64_t t = t0 + 16 * rt + lr;
+                if (t < a.T) *reinterpret_cast<f4 *>(&a.o[((b * a.T + t) * a.H + h) * D + 16 * ct + 4 * lg]) = oacc[rt];
+            }
+            // S <- Diag(e^gC) S + G - Etil^T P1, tokens in permuted slots
+            const h8 pb0 = join(to_h4(-p1[0]), to_h4(-p1[1]));
+            const h8 pb1 = join(to_h4(-p1[2]), to_h4(-p1[3]));
 #pragma unroll
-                for (int it = 0; it < 8; ++it) {
-                    f4 s = cur.gam[it] * sacc[j][it] + to_f4(cur.g[j][it]);
-                    s = mfma32(ef[it][0], pb0, s);
-                    s = mfma32(ef[it][1], pb1, s);
-                    sacc[j][it] = s;
-                }
+            for (int it = 0; it < 8; ++it) {
+                const h8 g2 = gp[it >> 1];
+                const f4 gv = (it & 1) ? f4{(float)g2[4], (float)g2[5], (float)g2[6], (float)g2[7]}
+                                       : f4{(float)g2[0], (float)g2[1], (float)g2[2], (float)g2[3]};
+                f4 sv = gam[it] * sacc[it] + gv;
+                sv = mfma32(ef[it][0], pb0, sv);
+                sv = mfma32(ef[it][1], pb1, sv);
+                sacc[it] = sv;
             }
         } else {
             // exact fp32 token recurrence on the raw inputs of this chunk
@@ -573,30 +604,19 @@ __global__ void __launch_bounds__(64) chunk_scan_kernel(ChunkArgs a, SplitWs w, 
                 const int64_t row = (b * a.T + t0 + r) * a.H + h;
                 // gates of key channel c of this token (per channel or per head)
                 auto gate = [&](const float *g, int c) { return g[row * gw + (KEYG ? c : 0)]; };
-                float m[NB], o[NB];
-#pragma unroll
-                for (int j = 0; j < NB; ++j) m[j] = o[j] = 0.f;
+                float m = 0.f, o = 0.f;
                 // decay, then the erase read m = k^T S_bar
 #pragma unroll
                 for (int it = 0; it < 8; ++it)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int c = 16 * it + 4 * lg + e;
-                        const float ac = expf(gate(a.la, c)), kc = bf16_to_f32(kp[row * D + c]);
-#pragma unroll
-                        for (int j = 0; j < NB; ++j) {
-                            sacc[j][it][e] *= ac;
-                            m[j] += kc * sacc[j][it][e];
-                        }
+                        sacc[it][e] *= expf(gate(a.la, c));
+                        m += bf16_to_f32(kp[row * D + c]) * sacc[it][e];
                     }
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    m[j] += __shfl_xor(m[j], 16);
-                    m[j] += __shfl_xor(m[j], 32);
-                }
-                float vv[NB];
-#pragma unroll
-                for (int j = 0; j < NB; ++j) vv[j] = bf16_to_f32(vp[row * D + 16 * (ct0 + j) + lr]);
+                m += __shfl_xor(m, 16);
+                m += __shfl_xor(m, 32);
+                const float vv = bf16_to_f32(vp[row * D + 16 * ct + lr]);
                 // erase and write, then the read o = S^T q
 #pragma unroll
                 for (int it = 0; it < 8; ++it)
@@ -606,35 +626,55 @@ __global__ void __launch_bounds__(64) chunk_scan_kernel(ChunkArgs a, SplitWs w, 
                         const float kc = bf16_to_f32(kp[row * D + c]);
                         const float bb = gate(a.eb, c);
                         const float ec = bb * kc, uc = (TIED ? bb : gate(a.wr, c)) * kc;
-                        const float qc = a.q_scale * bf16_to_f32(qp[row * D + c]);
-#pragma unroll
-                        for (int j = 0; j < NB; ++j) {
-                            sacc[j][it][e] = sacc[j][it][e] - ec * m[j] + uc * vv[j];
-                            o[j] += qc * sacc[j][it][e];
-                        }
+                        sacc[it][e] = sacc[it][e] - ec * m + uc * vv;
+                        o += a.q_scale * bf16_to_f32(qp[row * D + c]) * sacc[it][e];
                     }
-#pragma unroll
-                for (int j = 0; j < NB; ++j) {
-                    o[j] += __shfl_xor(o[j], 16);
-                    o[j] += __shfl_xor(o[j], 32);
-                    if (lg == 0) a.o[row * D + 16 * (ct0 + j) + lr] = o[j];
-                }
+                o += __shfl_xor(o, 16);
+                o += __shfl_xor(o, 32);
+                if (lg == 0) a.o[row * D + 16 * ct + lr] = o;
             }
+            // leave nothing of this (rare) path outstanding, so that the fast
+            // path's precise waits for the prefetched slices survive the merge
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         }
-        load_e(ef, w.frag + nxt * REC + OFF_E, lane);
-        cur = nx;
-    }
+    };
 
-    if (a.s_out) {
+    // Chunk n: the barrier finds slot n & 1 complete (its copy waves waited
+    // for their copies before arriving) and every compute wave past chunk
+    // n-1; then the copy waves refill the other slot (last read in chunk n-1)
+    // with chunk n+1 and wait for it, while the compute waves compute chunk n.
+    // Unrolled by two so both slots are named statically.
+#define GDN2_SCAN_STEP(N, FR, GM, FRN, GMN)                                        \
+    do {                                                                          \
+        __builtin_amdgcn_s_barrier();                                             \
+        if (copier) {                                                             \
+            if ((N) + 1 < nc) fill(FRN, GMN, task0 + (N) + 1, wv - SCAN_W);       \
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                             \
+        } else {                                                                  \
+            compute((N), FR, GM);                                                 \
+        }                                                                         \
+    } while (0)
+
+    if (copier) {
+        fill(fr0, gm0, task0, wv - SCAN_W);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    }
+    int n = 0;
+    for (; n + 1 < nc; n += 2) {
+        GDN2_SCAN_STEP(n, fr0, gm0, fr1, gm1);
+        GDN2_SCAN_STEP(n + 1, fr1, gm1, fr0, gm0);
+    }
+    if (n < nc) GDN2_SCAN_STEP(n, fr0, gm0, fr1, gm1);
+#undef GDN2_SCAN_STEP
+
+    if (a.s_out && !copier) {
 #pragma unroll
-        for (int n = 0; n < NB; ++n)
+        for (int it = 0; it < 8; ++it)
 #pragma unroll
-            for (int it = 0; it < 8; ++it)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int64_t c = 16 * it + 4 * lg + e, v = 16 * (ct0 + n) + lr;
-                    a.s_out[sbase + c * D + v] = sacc[n][it][e];
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int64_t c = 16 * it + 4 * lg + e, v = 16 * ct + lr;
+                a.s_out[sbase + c * D + v] = sacc[it][e];
+            }
     }
 }
 
@@ -647,8 +687,6 @@ SplitWs carve(const ChunkArgs &a, void *ws) {
     w.frag = reinterpret_cast<_Float16 *>(p);
     p += align256(ntask * REC * 2);
     w.gam = reinterpret_cast<float *>(p);
-    p += align256(ntask * D * 4);
-    w.flag = reinterpret_cast<int *>(p);
     return w;
 }
 
@@ -669,8 +707,8 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int xcd_map = (chains % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((chunk_scan_kernel<1, TIED, KEYG>), dim3(static_cast<unsigned>(chains * 8)), dim3(64), 0, s,
-                       a, w, nc, 8, xcd_map);
+    hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG>), dim3(static_cast<unsigned>(chains * (8 / SCAN_W))),
+                       dim3(SCAN_NTH), 0, s, a, w, nc, xcd_map);
     return hipGetLastError();
 }
 
@@ -684,7 +722,7 @@ bool chunk_split_supported(const ChunkArgs &a) {
 
 size_t chunk_split_workspace(int64_t B, int64_t H, int64_t T) {
     const int64_t ntask = B * H * ((T + C - 1) / C);
-    return static_cast<size_t>(align256(ntask * REC * 2) + align256(ntask * D * 4) + align256(ntask * 4));
+    return static_cast<size_t>(align256(ntask * REC * 2) + align256(ntask * D * 4));
 }
 
 hipError_t launch_chunk_split(const ChunkArgs &a, void *ws, hipStream_t s) {

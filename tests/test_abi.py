@@ -128,11 +128,11 @@ def test_decode_needs_one_token(lib):
 
 
 def split_bytes(B, H, T):
-    """Two-pass workspace: per (chain, chunk) a 96 KiB fp16 record, 128 fp32
-    chunk-end decays and one int flag, each region 256-byte aligned."""
+    """Two-pass workspace: per (chain, chunk) a 96 KiB fp16 record and 128
+    fp32 chunk-end decays, each region 256-byte aligned."""
     a = lambda x: (x + 255) // 256 * 256
     n = B * H * ((T + 63) // 64)
-    return a(n * 98304) + a(n * 512) + a(n * 4)
+    return a(n * 98304) + a(n * 512)
 
 
 def query(lib, d):

@@ -205,7 +205,10 @@ def main():
                                f"dk=dv={w.dk} C={w.chunk}, per-channel decay/erase/write",
                    "global_batch": w.B, "seq_len": w.T, "heads": w.H, "dk": w.dk, "dv": w.dv,
                    "chunk": w.chunk, "parallelism": "single GPU"},
+        # the roofline unit is one gdn2_chunk_fwd call (its two kernels):
+        # the operation's algorithmic bytes over the HIP-event time of the call
         "roofline": roofline_hbm(bytes_alg, ms_kernel, traffic),
+        "roofline_unit": "one gdn2_chunk_fwd call: chunk_prep_kernel + chunk_scan_kernel",
         "kernel_ms": round(ms_kernel, 4),
         "algorithmic_bytes_per_launch": bytes_alg,
         "algorithmic_flops_per_launch": flops_alg,

@@ -128,17 +128,19 @@ def time_chunk(w, wid, steps, warmup, torch, chunk_fwd, one_pass=False, inp=None
     for _ in range(warmup):
         chunk_fwd(*args, chunk=w.chunk, out=o, state_out=st, workspace=ws)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     log(f"[bench] timing {steps} steps of {w.name}" + (" (one pass)" if one_pass else ""))
     t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         chunk_fwd(*args, chunk=w.chunk, out=o, state_out=st, workspace=ws)
-    ev1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / steps
-    ms_kernel = ev0.elapsed_time(ev1) / steps
+    per_call = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    ms_kernel = ev[0].elapsed_time(ev[steps]) / steps
+    time_chunk.last = {"kernel_ms_median": round(per_call[steps // 2], 4), "kernel_ms_min": round(per_call[0], 4)}
     return inp, ms_step, ms_kernel
 
 
@@ -210,6 +212,7 @@ def main():
         "roofline": roofline_hbm(bytes_alg, ms_kernel, traffic),
         "roofline_unit": "one gdn2_chunk_fwd call: chunk_prep_kernel + chunk_scan_kernel",
         "kernel_ms": round(ms_kernel, 4),
+        **time_chunk.last,
         "algorithmic_bytes_per_launch": bytes_alg,
         "algorithmic_flops_per_launch": flops_alg,
         "mfma_frac_of_algorithmic_flops": round(flops_alg / (ms_kernel * 1e-3) / 1e12

@@ -434,62 +434,113 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
 }
 
 // ----------------------------------------------------------------------------
-// Pass 2: the scan over chunks.  A workgroup of SCAN_W waves owns one chain
-// and SCAN_W value tiles (16 columns each, one per wave); each wave keeps its
-// 128 x 16 fp32 state slice in accumulators.  Everything a chunk needs -- W,
-// Qe, EtT (48 KiB, shared by the waves), the workgroup's slices of G and Oe
-// and e^gC -- is copied by the memory unit straight into LDS
-// (global_load_lds) one chunk ahead, into one of two slots, by SCAN_P copy
-// waves of the same workgroup, so the compute waves never wait behind
-// memory instructions; one barrier per chunk hands a slot over.
-constexpr int SCAN_W = 4;                 // compute waves (one value tile each)
+// Pass 2: the scan over chunks.  A workgroup of SCAN_W compute waves owns one
+// chain (or one segment of it, below) and SCAN_W value tiles (16 columns
+// each, one per wave); each wave keeps its 128 x 16 fp32 state slice in
+// accumulators.  Everything a chunk needs -- W, Qe, EtT (48 KiB, shared by
+// the waves), the workgroup's slices of G and Oe and e^gC -- is copied by the
+// memory unit straight into LDS (global_load_lds) one chunk ahead, into one
+// of two slots, by SCAN_P copy waves of the same workgroup, so the compute
+// waves never wait behind memory instructions; one barrier per chunk hands a
+// slot over.
+//
+// Long sequences on few chains use the affine view of a chunk (the Gated
+// DeltaNet page, "What makes the architecture more than a recurrence": each
+// gated transition is still affine, S -> F S + G, and such maps compose): a
+// chain's chunks are cut into segments, and
+//   A (MODE 1)  every segment j but the last is scanned from S = 0, giving
+//               its end state X[j+1], and its columns are also scanned from
+//               S = I without the write terms, giving its transition F[j];
+//               segment 0 starts from the chain's initial state instead (and
+//               copies it to X[0]), so X[1] is already the state entering
+//               segment 1;
+//   B           X[j+1] <- F[j] X[j] + X[j+1] for j = 1, 2, ... in order
+//               (segment_combine_kernel), so X[j] becomes the state entering
+//               segment j;
+//   C (MODE 0)  every segment j is scanned from X[j], writing O, and the
+//               last one the final state.
+// With one segment only C runs, as the plain scan, from the initial state.
+// (Phase C never reads the initial state, so the final state may overwrite
+// it in place.)
+constexpr int SCAN_W = 4;                 // compute waves per value half (one tile each)
 constexpr int SCAN_P = 4;                 // copy waves
-constexpr int SCAN_NTH = 64 * (SCAN_W + SCAN_P);
 constexpr int SLOT_F = 3 * 8192;          // halves of W | Qe | EtT
 constexpr int SLOT_G = SCAN_W * 4 * 512;  // halves of G for my tiles (4 pair rows of 512)
 constexpr int SLOT_O = SCAN_W * 2 * 512;  // halves of Oe^T for my tiles
-constexpr int SLOT_H = SLOT_F + SLOT_G + SLOT_O;
-constexpr int SLOT_PIECES = SLOT_H * 2 / 16 / (64 * SCAN_P);  // 1 KiB copies per copy wave (18)
-static_assert(SLOT_H * 2 % (1024 * SCAN_P) == 0, "slot copies must tile the copy waves");
+constexpr int SLOT_H = SLOT_F + SLOT_G + SLOT_O;  // MODE 0 slot
+constexpr int SLOT_A = 2 * 8192 + SLOT_G;         // MODE 1 slot: W | EtT | G
+static_assert(SLOT_H * 2 % (1024 * SCAN_P) == 0 && SLOT_A * 2 % (1024 * SCAN_P) == 0,
+              "slot copies must tile the copy waves");
+constexpr int SEG_MIN = 16;   // fewest chunks per segment
+constexpr int SEG_WG = 256;   // scan workgroups aimed at when chains are few
+
+constexpr int scan_threads(int mode) { return 64 * (SCAN_P + (mode ? 2 : 1) * SCAN_W); }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (other counters untouched)
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <bool TIED, bool KEYG>
-__global__ void __launch_bounds__(SCAN_NTH) chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, int xcd_map) {
+struct ScanPlan {
+    int nseg;     // segments per chain (1: plain scan)
+    int seg_len;  // chunks per segment; the last one may be shorter
+    float *xs;    // [chain][nseg][D][D] segment entry states X
+    float *fs;    // [chain][nseg][D][D] segment transitions F (0 and nseg-1 unused)
+};
+
+// MODE 0: the scan proper (O and, for the last segment, the final state).
+// MODE 1: segment summaries; SCAN_W more compute waves carry the columns of
+// F (the first SCAN_W carry the state), no Qe / Oe / O.
+template <bool TIED, bool KEYG, int MODE>
+__global__ void __launch_bounds__(scan_threads(MODE))
+chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
+    constexpr bool WITH_O = MODE == 0;
+    constexpr int NCOMP = (MODE ? 2 : 1) * SCAN_W;
+    constexpr int SH = MODE ? SLOT_A : SLOT_H;
+    constexpr int S_Q = 8192, S_E = MODE ? 8192 : 16384, S_G = MODE ? 16384 : SLOT_F, S_O = SLOT_F + SLOT_G;
+    constexpr int PIECES = SH * 2 / 1024 / SCAN_P;  // 1 KiB copies per copy wave
     // two distinct slots (distinct objects, so the compiler can tell the slot
     // being filled from the one being read)
-    __shared__ __attribute__((aligned(16))) _Float16 fr0[SLOT_H], fr1[SLOT_H];
+    __shared__ __attribute__((aligned(16))) _Float16 fr0[SH], fr1[SH];
     __shared__ __attribute__((aligned(16))) float gm0[2 * D], gm1[2 * D];
     const int G = blockIdx.x;
-    int chain, half;
-    if (xcd_map) {  // a chain's two workgroups on one XCD, so its records are read into one L2
+    int unit, half;
+    if (xcd_map) {  // a unit's two workgroups on one XCD, so its records are read into one L2
         half = (G / 8) & 1;
-        chain = (G / 16) * 8 + (G % 8);
+        unit = (G / 16) * 8 + (G % 8);
     } else {
         half = G & 1;
-        chain = G / 2;
+        unit = G / 2;
     }
+    const int nsl = MODE ? sp.nseg - 1 : sp.nseg;  // segments per chain in this launch
+    const int chain = unit / nsl, seg = unit % nsl;
+    const int n0 = seg * sp.seg_len, n1 = min(nc, n0 + sp.seg_len);
     const int64_t b = chain / a.H, h = chain % a.H;
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool copier = wv >= SCAN_W;
-    const int ct = SCAN_W * half + (copier ? 0 : wv);  // my value tile (compute waves)
-    const int64_t sbase = (b * a.H + h) * static_cast<int64_t>(D) * D;
+    const bool copier = wv >= NCOMP;
+    const bool frun = MODE && !copier && wv >= SCAN_W;  // this wave carries columns of F
+    const bool idle = frun && seg == 0;                 // the first segment's F is never used
+    const int wt = wv % SCAN_W;                          // my tile within the slot's slices
+    const int ct = SCAN_W * half + (copier ? 0 : wt);   // my value (or key) tile
+    const int64_t sbase = static_cast<int64_t>(chain) * D * D;
     const int64_t task0 = static_cast<int64_t>(chain) * nc;
+    const int64_t xbase = (static_cast<int64_t>(chain) * sp.nseg + seg) * D * D;  // slot seg
 
     // state slice: tile it holds S[16it+4lg+e][16ct+lr]
+    const float *init = nullptr;
+    if (MODE == 0) init = sp.nseg == 1 ? (a.s0 ? a.s0 + sbase : nullptr) : sp.xs + xbase;
+    else if (!frun && seg == 0 && a.s0) init = a.s0 + sbase;
     f4 sacc[8];
 #pragma unroll
     for (int it = 0; it < 8; ++it)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int64_t c = 16 * it + 4 * lg + e, v = 16 * ct + lr;
-            sacc[it][e] = (a.s0 && !copier) ? a.s0[sbase + c * D + v] : 0.f;
+            const int c = 16 * it + 4 * lg + e, v = 16 * ct + lr;
+            sacc[it][e] = copier ? 0.f : init ? init[c * D + v] : (frun && c == v) ? 1.f : 0.f;
+            if (MODE == 1 && !copier && !frun && seg == 0) sp.xs[xbase + c * D + v] = sacc[it][e];
         }
 
-    // Copy chunk `task` into a slot: W | Qe | EtT (record offset 0), then my
+    // Copy chunk `task` into a slot: W | Qe | EtT (MODE 1: W | EtT), then my
     // workgroup's G and Oe^T tiles (contiguous in the record), then e^gC.
     // Each wave moves 1 KiB per instruction (lane l -> bytes 16l..16l+15).
     auto fill = [&](_Float16 *fr, float *gm, int64_t task, int pw) __attribute__((always_inline)) {
@@ -497,11 +548,17 @@ __global__ void __launch_bounds__(SCAN_NTH) chunk_scan_kernel(ChunkArgs a, Split
         const char *srcg = rec + 2 * (OFF_G + static_cast<int64_t>(SCAN_W * half) * 4 * 512);
         const char *srco = rec + 2 * (OFF_O + static_cast<int64_t>(SCAN_W * half) * 2 * 512);
 #pragma unroll
-        for (int i = 0; i < SLOT_PIECES; ++i) {
+        for (int i = 0; i < PIECES; ++i) {
             const int byte = 1024 * (SCAN_P * i + pw);  // my 1 KiB block of the slot
-            const char *src = byte < 2 * SLOT_F ? rec + byte
-                            : byte < 2 * (SLOT_F + SLOT_G) ? srcg + (byte - 2 * SLOT_F)
-                                                           : srco + (byte - 2 * (SLOT_F + SLOT_G));
+            const char *src;
+            if (MODE == 0)
+                src = byte < 2 * SLOT_F ? rec + byte
+                    : byte < 2 * (SLOT_F + SLOT_G) ? srcg + (byte - 2 * SLOT_F)
+                                                   : srco + (byte - 2 * (SLOT_F + SLOT_G));
+            else
+                src = byte < 2 * 8192 ? rec + byte
+                    : byte < 4 * 8192 ? rec + 2 * OFF_E + (byte - 2 * 8192)
+                                      : srcg + (byte - 4 * 8192);
             __builtin_amdgcn_global_load_lds(src + 16 * lane, reinterpret_cast<char *>(fr) + byte, 16, 0, 0);
         }
         // e^gC: copy waves 0,1 bring channels 0..127
@@ -510,8 +567,8 @@ __global__ void __launch_bounds__(SCAN_NTH) chunk_scan_kernel(ChunkArgs a, Split
 
     // One chunk n on this wave, from slot (fr, gm).
     auto compute = [&](int n, const _Float16 *fr, const float *gm) __attribute__((always_inline)) {
-        const _Float16 *fg = fr + SLOT_F + wv * 4 * 512;            // my G pairs
-        const _Float16 *fo = fr + SLOT_F + SLOT_G + wv * 2 * 512;   // my Oe^T pairs
+        const _Float16 *fg = fr + S_G + wt * 4 * 512;  // my G pairs
+        const _Float16 *fo = fr + S_O + wt * 2 * 512;  // my Oe^T pairs (MODE 0)
         const int64_t t0 = static_cast<int64_t>(n) * C;
         // the fp16 copies of the state and of the erase read must stay finite
         bool big = false;
@@ -531,15 +588,17 @@ __global__ void __launch_bounds__(SCAN_NTH) chunk_scan_kernel(ChunkArgs a, Split
                 for (int kb = 0; kb < 4; ++kb) {
                     const int off = ((rt * 4 + kb) * 64 + lane) * 8;
                     x[0][kb] = *reinterpret_cast<const h8 *>(fr + OFF_W + off);
-                    x[1][kb] = *reinterpret_cast<const h8 *>(fr + OFF_Q + off);
+                    if (WITH_O) x[1][kb] = *reinterpret_cast<const h8 *>(fr + S_Q + off);
                 }
             };
             h8 wq[2][2][4];
             read_wq(wq[0], 0);
+            if (MODE == 0) {  // MODE 1 reads EtT where it is used (register budget of 12 waves)
 #pragma unroll
-            for (int it = 0; it < 8; ++it)
+                for (int it = 0; it < 8; ++it)
 #pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) ef[it][k2] = *reinterpret_cast<const h8 *>(fr + OFF_E + ((it * 2 + k2) * 64 + lane) * 8);
+                    for (int k2 = 0; k2 < 2; ++k2) ef[it][k2] = *reinterpret_cast<const h8 *>(fr + S_E + ((it * 2 + k2) * 64 + lane) * 8);
+            }
             // P1 = W S and O^T = S^T Qe^T + Oe^T.  State tiles 2kb, 2kb+1 in
             // the record's permuted slot order are both the B operand of key
             // block kb (for W S) and the A operand of S^T (for O^T).
@@ -549,18 +608,20 @@ __global__ void __launch_bounds__(SCAN_NTH) chunk_scan_kernel(ChunkArgs a, Split
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 if (rt < 3) read_wq(wq[(rt + 1) & 1], rt + 1);
-                const h8 oe = *reinterpret_cast<const h8 *>(fo + ((rt >> 1) * 64 + lane) * 8);
+                h8 oe;
+                if (WITH_O) oe = *reinterpret_cast<const h8 *>(fo + ((rt >> 1) * 64 + lane) * 8);
                 __builtin_amdgcn_sched_barrier(0);
                 f4 p = splat(0.f);
-                f4 o = (rt & 1) ? f4{(float)oe[4], (float)oe[5], (float)oe[6], (float)oe[7]}
-                                : f4{(float)oe[0], (float)oe[1], (float)oe[2], (float)oe[3]};
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb) {
-                    p = mfma32(wq[rt & 1][0][kb], sb[kb], p);
-                    o = mfma32(sb[kb], wq[rt & 1][1][kb], o);
+                for (int kb = 0; kb < 4; ++kb) p = mfma32(wq[rt & 1][0][kb], sb[kb], p);
+                if (WITH_O) {
+                    f4 o = (rt & 1) ? f4{(float)oe[4], (float)oe[5], (float)oe[6], (float)oe[7]}
+                                    : f4{(float)oe[0], (float)oe[1], (float)oe[2], (float)oe[3]};
+#pragma unroll
+                    for (int kb = 0; kb < 4; ++kb) o = mfma32(sb[kb], wq[rt & 1][1][kb], o);
+                    oacc[rt] = o;
                 }
                 p1[rt] = p;
-                oacc[rt] = o;
                 big |= out_of_range(p);
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -569,33 +630,46 @@ __global__ void __launch_bounds__(SCAN_NTH) chunk_scan_kernel(ChunkArgs a, Split
         if (!bad) {
             f4 gam[8];
             h8 gp[4];
+            if (MODE == 0) {
 #pragma unroll
-            for (int it = 0; it < 8; ++it) gam[it] = *reinterpret_cast<const f4 *>(&gm[16 * it + 4 * lg]);
+                for (int it = 0; it < 8; ++it) gam[it] = *reinterpret_cast<const f4 *>(&gm[16 * it + 4 * lg]);
 #pragma unroll
-            for (int ip = 0; ip < 4; ++ip) gp[ip] = *reinterpret_cast<const h8 *>(fg + (ip * 64 + lane) * 8);
-            __builtin_amdgcn_sched_barrier(0);
-            // O^T tile: lane t+16m holds token 16rt+t, value columns
-            // 16ct+4m..+3 -> one 16-byte store per lane and tile
+                for (int ip = 0; ip < 4; ++ip) gp[ip] = *reinterpret_cast<const h8 *>(fg + (ip * 64 + lane) * 8);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if (WITH_O) {
+                // O^T tile: lane t+16m holds token 16rt+t, value columns
+                // 16ct+4m..+3 -> one 16-byte store per lane and tile
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                const int64_t t = t0 + 16 * rt + lr;
-                if (t < a.T) *reinterpret_cast<f4 *>(&a.o[((b * a.T + t) * a.H + h) * D + 16 * ct + 4 * lg]) = oacc[rt];
+                for (int rt = 0; rt < 4; ++rt) {
+                    const int64_t t = t0 + 16 * rt + lr;
+                    if (t < a.T) *reinterpret_cast<f4 *>(&a.o[((b * a.T + t) * a.H + h) * D + 16 * ct + 4 * lg]) = oacc[rt];
+                }
             }
             // S <- Diag(e^gC) S + G - Etil^T P1, tokens in permuted slots
+            // (the columns of F take no G)
             const h8 pb0 = join(to_h4(-p1[0]), to_h4(-p1[1]));
             const h8 pb1 = join(to_h4(-p1[2]), to_h4(-p1[3]));
+            const float gsel = frun ? 0.f : 1.f;
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
+                if (MODE) {
+#pragma unroll
+                    for (int k2 = 0; k2 < 2; ++k2) ef[it][k2] = *reinterpret_cast<const h8 *>(fr + S_E + ((it * 2 + k2) * 64 + lane) * 8);
+                    gam[it] = *reinterpret_cast<const f4 *>(&gm[16 * it + 4 * lg]);
+                    if ((it & 1) == 0) gp[it >> 1] = *reinterpret_cast<const h8 *>(fg + ((it >> 1) * 64 + lane) * 8);
+                }
                 const h8 g2 = gp[it >> 1];
                 const f4 gv = (it & 1) ? f4{(float)g2[4], (float)g2[5], (float)g2[6], (float)g2[7]}
                                        : f4{(float)g2[0], (float)g2[1], (float)g2[2], (float)g2[3]};
-                f4 sv = gam[it] * sacc[it] + gv;
+                f4 sv = gam[it] * sacc[it] + (MODE ? gsel * gv : gv);
                 sv = mfma32(ef[it][0], pb0, sv);
                 sv = mfma32(ef[it][1], pb1, sv);
                 sacc[it] = sv;
             }
         } else {
             // exact fp32 token recurrence on the raw inputs of this chunk
+            // (the columns of F drop the write term)
             const uint16_t *kp = static_cast<const uint16_t *>(a.k);
             const uint16_t *qp = static_cast<const uint16_t *>(a.q);
             const uint16_t *vp = static_cast<const uint16_t *>(a.v);
@@ -616,7 +690,7 @@ __global__ void __launch_bounds__(SCAN_NTH) chunk_scan_kernel(ChunkArgs a, Split
                     }
                 m += __shfl_xor(m, 16);
                 m += __shfl_xor(m, 32);
-                const float vv = bf16_to_f32(vp[row * D + 16 * ct + lr]);
+                const float vv = frun ? 0.f : bf16_to_f32(vp[row * D + 16 * ct + lr]);
                 // erase and write, then the read o = S^T q
 #pragma unroll
                 for (int it = 0; it < 8; ++it)
@@ -627,11 +701,13 @@ __global__ void __launch_bounds__(SCAN_NTH) chunk_scan_kernel(ChunkArgs a, Split
                         const float bb = gate(a.eb, c);
                         const float ec = bb * kc, uc = (TIED ? bb : gate(a.wr, c)) * kc;
                         sacc[it][e] = sacc[it][e] - ec * m + uc * vv;
-                        o += a.q_scale * bf16_to_f32(qp[row * D + c]) * sacc[it][e];
+                        if (WITH_O) o += a.q_scale * bf16_to_f32(qp[row * D + c]) * sacc[it][e];
                     }
-                o += __shfl_xor(o, 16);
-                o += __shfl_xor(o, 32);
-                if (lg == 0) a.o[row * D + 16 * ct + lr] = o;
+                if (WITH_O) {
+                    o += __shfl_xor(o, 16);
+                    o += __shfl_xor(o, 32);
+                    if (lg == 0) a.o[row * D + 16 * ct + lr] = o;
+                }
             }
             // leave nothing of this (rare) path outstanding, so that the fast
             // path's precise waits for the prefetched slices survive the merge
@@ -648,46 +724,120 @@ __global__ void __launch_bounds__(SCAN_NTH) chunk_scan_kernel(ChunkArgs a, Split
     do {                                                                          \
         __builtin_amdgcn_s_barrier();                                             \
         if (copier) {                                                             \
-            if ((N) + 1 < nc) fill(FRN, GMN, task0 + (N) + 1, wv - SCAN_W);       \
+            if ((N) + 1 < n1) fill(FRN, GMN, task0 + (N) + 1, wv - NCOMP);        \
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                             \
-        } else {                                                                  \
+        } else if (!idle) {                                                       \
             compute((N), FR, GM);                                                 \
         }                                                                         \
     } while (0)
 
     if (copier) {
-        fill(fr0, gm0, task0, wv - SCAN_W);
+        fill(fr0, gm0, task0 + n0, wv - NCOMP);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-    int n = 0;
-    for (; n + 1 < nc; n += 2) {
+    int n = n0;
+    for (; n + 1 < n1; n += 2) {
         GDN2_SCAN_STEP(n, fr0, gm0, fr1, gm1);
         GDN2_SCAN_STEP(n + 1, fr1, gm1, fr0, gm0);
     }
-    if (n < nc) GDN2_SCAN_STEP(n, fr0, gm0, fr1, gm1);
+    if (n < n1) GDN2_SCAN_STEP(n, fr0, gm0, fr1, gm1);
 #undef GDN2_SCAN_STEP
 
-    if (a.s_out && !copier) {
+    float *dst = nullptr;
+    if (copier || idle) dst = nullptr;
+    else if (MODE == 0) dst = (seg == sp.nseg - 1 && a.s_out) ? a.s_out + sbase : nullptr;
+    else dst = frun ? sp.fs + xbase : sp.xs + xbase + D * D;  // F[seg], X[seg+1]
+    if (dst) {
 #pragma unroll
         for (int it = 0; it < 8; ++it)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int64_t c = 16 * it + 4 * lg + e, v = 16 * ct + lr;
-                a.s_out[sbase + c * D + v] = sacc[it][e];
+                const int c = 16 * it + 4 * lg + e, v = 16 * ct + lr;
+                dst[c * D + v] = sacc[it][e];
             }
+    }
+}
+
+// Phase B of the segmented scan: X[j+1] <- F[j] X[j] + X[j+1] for j = 1 ..
+// nseg-2, in order.  One workgroup per (chain, 16 columns); lane l owns row
+// l % 128 and 8 of the 16 columns.  F[j+1] is fetched into registers while
+// step j runs.
+constexpr int CMB_NTH = 256;
+constexpr int CMB_COLS = 16;
+constexpr int CMB_FST = D + 1;  // odd row stride: lanes on distinct rows hit distinct banks
+
+__global__ void __launch_bounds__(CMB_NTH) segment_combine_kernel(float *xs, const float *fs, int nseg) {
+    __shared__ float fl[D * CMB_FST];
+    __shared__ float sx[D * CMB_COLS];
+    const int chain = blockIdx.x / (D / CMB_COLS), cb = (blockIdx.x % (D / CMB_COLS)) * CMB_COLS;
+    const int tid = threadIdx.x, i = tid % D, c0 = 8 * (tid / D);
+    const int64_t base = static_cast<int64_t>(chain) * nseg * D * D;
+    for (int e = tid; e < D * CMB_COLS; e += CMB_NTH) sx[e] = xs[base + D * D + (e / CMB_COLS) * D + cb + e % CMB_COLS];
+    f4 pf[16];
+    auto load_f = [&](int j) __attribute__((always_inline)) {
+        const f4 *src = reinterpret_cast<const f4 *>(fs + base + static_cast<int64_t>(j) * D * D);
+#pragma unroll
+        for (int q = 0; q < 16; ++q) pf[q] = src[tid + CMB_NTH * q];
+    };
+    if (nseg > 2) load_f(1);
+    for (int j = 1; j <= nseg - 2; ++j) {
+        __syncthreads();  // step j-1 is done with fl and has written sx
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int f = 4 * (tid + CMB_NTH * q), r = f / D, c = f % D;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) fl[r * CMB_FST + c + e] = pf[q][e];
+        }
+        __syncthreads();
+        if (j + 1 <= nseg - 2) load_f(j + 1);
+        float *xj = xs + base + static_cast<int64_t>(j + 1) * D * D + static_cast<int64_t>(i) * D + cb + c0;
+        f4 acc0 = *reinterpret_cast<const f4 *>(xj), acc1 = *reinterpret_cast<const f4 *>(xj + 4);
+        for (int k = 0; k < D; ++k) {
+            const float f = fl[i * CMB_FST + k];
+            const f4 s0 = *reinterpret_cast<const f4 *>(&sx[k * CMB_COLS + c0]);
+            const f4 s1 = *reinterpret_cast<const f4 *>(&sx[k * CMB_COLS + c0 + 4]);
+            acc0 += f * s0;
+            acc1 += f * s1;
+        }
+        __syncthreads();  // every lane has read sx
+        *reinterpret_cast<f4 *>(&sx[i * CMB_COLS + c0]) = acc0;
+        *reinterpret_cast<f4 *>(&sx[i * CMB_COLS + c0 + 4]) = acc1;
+        *reinterpret_cast<f4 *>(xj) = acc0;
+        *reinterpret_cast<f4 *>(xj + 4) = acc1;
     }
 }
 
 int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
-SplitWs carve(const ChunkArgs &a, void *ws) {
-    const int64_t ntask = a.B * a.H * ((a.T + C - 1) / C);
-    char *p = static_cast<char *>(ws);
-    SplitWs w;
-    w.frag = reinterpret_cast<_Float16 *>(p);
-    p += align256(ntask * REC * 2);
-    w.gam = reinterpret_cast<float *>(p);
-    return w;
+// Segments per chain: one, unless the chains cannot fill SEG_WG scan
+// workgroups; then as many as fill them, each of at least SEG_MIN chunks.
+int scan_segments(int64_t chains, int64_t nc) {
+    if (chains * 2 * 2 > SEG_WG) return 1;
+    int64_t n = SEG_WG / (2 * chains);
+    if (n > nc / SEG_MIN) n = nc / SEG_MIN;
+    if (n < 2) return 1;
+    const int64_t len = (nc + n - 1) / n;
+    return static_cast<int>((nc + len - 1) / len);  // no empty segment
+}
+
+struct Layout {
+    int64_t nc, chains, ntask, nseg, seg_len;
+    int64_t off_gam, off_xs, off_fs, bytes;
+};
+
+Layout layout(int64_t B, int64_t H, int64_t T) {
+    Layout l;
+    l.nc = (T + C - 1) / C;
+    l.chains = B * H;
+    l.ntask = l.chains * l.nc;
+    l.nseg = scan_segments(l.chains, l.nc);
+    l.seg_len = (l.nc + l.nseg - 1) / l.nseg;
+    const int64_t sts = l.nseg > 1 ? align256(l.chains * l.nseg * D * D * 4) : 0;
+    l.off_gam = align256(l.ntask * REC * 2);
+    l.off_xs = l.off_gam + align256(l.ntask * D * 4);
+    l.off_fs = l.off_xs + sts;
+    l.bytes = l.off_fs + sts;
+    return l;
 }
 
 int cu_count() {
@@ -699,16 +849,35 @@ int cu_count() {
 
 template <bool TIED, bool KEYG>
 hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
-    const int nc = static_cast<int>((a.T + C - 1) / C);
-    const int64_t chains = a.B * a.H, ntask = chains * nc;
-    const SplitWs w = carve(a, ws);
-    const int64_t g1 = ntask < cu_count() ? ntask : cu_count();
+    const Layout l = layout(a.B, a.H, a.T);
+    char *p = static_cast<char *>(ws);
+    SplitWs w;
+    w.frag = reinterpret_cast<_Float16 *>(p);
+    w.gam = reinterpret_cast<float *>(p + l.off_gam);
+    ScanPlan sp;
+    sp.nseg = static_cast<int>(l.nseg);
+    sp.seg_len = static_cast<int>(l.seg_len);
+    sp.xs = l.nseg > 1 ? reinterpret_cast<float *>(p + l.off_xs) : nullptr;
+    sp.fs = l.nseg > 1 ? reinterpret_cast<float *>(p + l.off_fs) : nullptr;
+    const int nc = static_cast<int>(l.nc);
+    const int64_t g1 = l.ntask < cu_count() ? l.ntask : cu_count();
     hipLaunchKernelGGL((chunk_prep_kernel<TIED, KEYG>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s, a, w, nc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int xcd_map = (chains % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG>), dim3(static_cast<unsigned>(chains * (8 / SCAN_W))),
-                       dim3(SCAN_NTH), 0, s, a, w, nc, xcd_map);
+    if (l.nseg > 1) {
+        const int64_t units = l.chains * (l.nseg - 1);
+        hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG, 1>), dim3(static_cast<unsigned>(units * 2)),
+                           dim3(scan_threads(1)), 0, s, a, w, nc, sp, units % 8 == 0 ? 1 : 0);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (l.nseg > 2) {
+            hipLaunchKernelGGL(segment_combine_kernel, dim3(static_cast<unsigned>(l.chains * (D / CMB_COLS))),
+                               dim3(CMB_NTH), 0, s, sp.xs, sp.fs, sp.nseg);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+    }
+    const int64_t units = l.chains * l.nseg;
+    hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG, 0>), dim3(static_cast<unsigned>(units * 2)),
+                       dim3(scan_threads(0)), 0, s, a, w, nc, sp, units % 8 == 0 ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -720,10 +889,7 @@ bool chunk_split_supported(const ChunkArgs &a) {
     return chunk_mfma_supported(a) && ntask > 0 && ntask < (int64_t(1) << 31);
 }
 
-size_t chunk_split_workspace(int64_t B, int64_t H, int64_t T) {
-    const int64_t ntask = B * H * ((T + C - 1) / C);
-    return static_cast<size_t>(align256(ntask * REC * 2) + align256(ntask * D * 4));
-}
+size_t chunk_split_workspace(int64_t B, int64_t H, int64_t T) { return static_cast<size_t>(layout(B, H, T).bytes); }
 
 hipError_t launch_chunk_split(const ChunkArgs &a, void *ws, hipStream_t s) {
     const bool tied = a.wr == nullptr, keyg = a.la_key != 0;

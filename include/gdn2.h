@@ -100,7 +100,9 @@ const char *gdn2_status_str(int status);
  * `desc`; 0 when the request has no two-pass kernel (it then always runs in
  * one pass).  The two-pass form covers bf16 q/k/v, dk = dv = 128, chunk 64
  * and gates all of one kind; it needs B*H*ceil(T/64) records of about
- * 97 KiB.  Same validation as gdn2_chunk_fwd. */
+ * 97 KiB, and, when B*H is small against T (long sequences on few chains,
+ * scanned in parallel segments), two 64 KiB states per (chain, segment).
+ * Same validation as gdn2_chunk_fwd. */
 gdn2_status gdn2_chunk_fwd_workspace(const gdn2_desc *desc, size_t *bytes);
 
 /*

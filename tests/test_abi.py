@@ -127,12 +127,38 @@ def test_decode_needs_one_token(lib):
     assert step(lib, good(seqlen=0)) == 2
 
 
+def segments(chains, nc):
+    """Segments per chain of the two-level scan: one unless the chains
+    cannot fill 256 scan workgroups (two per chain and segment); then as
+    many as fill them, each of at least 16 chunks, none empty."""
+    if chains * 4 > 256:
+        return 1
+    n = min(256 // (2 * chains), nc // 16)
+    if n < 2:
+        return 1
+    ln = -(-nc // n)
+    return -(-nc // ln)
+
+
 def split_bytes(B, H, T):
     """Two-pass workspace: per (chain, chunk) a 96 KiB fp16 record and 128
-    fp32 chunk-end decays, each region 256-byte aligned."""
+    fp32 chunk-end decays; with several segments per chain, two fp32 states
+    per (chain, segment); each region 256-byte aligned."""
     a = lambda x: (x + 255) // 256 * 256
-    n = B * H * ((T + 63) // 64)
-    return a(n * 98304) + a(n * 512)
+    nc = (T + 63) // 64
+    n = B * H * nc
+    ns = segments(B * H, nc)
+    extra = 2 * a(B * H * ns * 128 * 128 * 4) if ns > 1 else 0
+    return a(n * 98304) + a(n * 512) + extra
+
+
+def test_segment_rule():
+    assert segments(128, 64) == 1          # 8 x 16 heads, 4096 tokens: chip already full
+    assert segments(16, 1024) == 8         # 1 x 16 heads, 65536 tokens
+    assert segments(64, 64) == 2
+    assert segments(2, 64) == 4            # capped by 16 chunks per segment
+    assert segments(2, 31) == 1
+    assert segments(1, 100) == 6           # 17-chunk segments, the last one 15
 
 
 def query(lib, d):
@@ -146,6 +172,9 @@ def test_workspace_query(lib):
     assert query(lib, good()) == split_bytes(2, 4, 128)
     assert query(lib, good(seqlen=100)) == split_bytes(2, 4, 100)
     assert query(lib, good(tied=True, decay_kind=0, erase_kind=0)) == split_bytes(2, 4, 128)
+    # long sequences on few chains add the segment states of the two-level scan
+    assert query(lib, good(batch=1, seqlen=4096)) == split_bytes(1, 4, 4096) > split_bytes(1, 4, 64) * 64
+    assert query(lib, good(batch=1, heads=16, seqlen=65536)) == split_bytes(1, 16, 65536)
     # everything else runs single-pass and needs none
     for d in (good(qkv_dtype=0, dk=32, dv=32, chunk=16), good(tied=True, decay_kind=0),
               good(dk=64), good(chunk=32), good(seqlen=0), good(batch=0)):

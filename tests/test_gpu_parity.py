@@ -330,3 +330,34 @@ def test_large_grams_run_exactly():
     inp["q_bf16"] = (inp["q_bf16"].astype(np.uint32) + (10 << 7)).astype(np.uint16)
     inp["write"] = inp["write"] * 1000.0
     _check(w, inp, 64, ws=True)
+
+
+# ---- the two-level scan: long sequences on few chains ----------------------
+# Few (batch, head) chains with many chunks are cut into segments (see
+# tests/test_abi.py::segments): 33 chunks -> 2 segments, 48 -> 3, 100 -> 6,
+# 64 on two chains -> 4.
+
+@pytest.mark.parametrize("B,H,T,tied,gates", [
+    (1, 1, 64 * 33 - 5, False, "key"),
+    (1, 2, 64 * 48, False, "key"),
+    (1, 1, 64 * 100 - 17, False, "key"),
+    (1, 2, 64 * 64, True, "head"),
+    (2, 1, 64 * 64 - 1, True, "key"),
+])
+def test_segmented_scan(B, H, T, tied, gates):
+    w = W[2].scaled(B=B, T=T, H=H, tied=tied, gates=gates)
+    _check(w, synth.make_inputs(w, seed=50 + T % 97 + H), 64, ws=True)
+
+
+def test_segmented_scan_exact_chunks():
+    # every chunk flagged for the exact recurrence (query Grams out of range,
+    # as in test_large_grams_run_exactly) and a state beyond the fp16 range:
+    # the exact path also serves the segment summaries (F without the writes)
+    w, inp = _bf16_case(51, T=64 * 48, H=1)
+    inp["q"] = inp["q"] * 1024.0
+    inp["q_bf16"] = (inp["q_bf16"].astype(np.uint32) + (10 << 7)).astype(np.uint16)
+    inp["write"] = inp["write"] * 1000.0
+    _check(w, inp, 64, ws=True)
+    w, inp = _bf16_case(52, T=64 * 48, H=1)
+    inp["S0"] = inp["S0"] * 3.0e5
+    _check(w, inp, 64, ws=True)

@@ -2,11 +2,14 @@
 
 The compute path is a HIP library for gfx950 (``libgdn2.so``, C ABI declared
 in ``include/gdn2.h``): a chunkwise-parallel forward and an O(1)-memory
-recurrent decode step.  ``chunk_fwd`` and ``recurrent_step`` below only
+recurrent decode step, plus the chunkwise backward.  ``chunk_fwd``,
+``chunk_bwd`` and ``recurrent_step`` below only
 marshal torch tensors into that ABI; importing this package does not load
 the library, calling either function does (and fails loudly if it is not
 built).
 """
-from .binding import chunk_fwd, recurrent_step, chunk_fwd_workspace, library_path, abi_version  # noqa: F401
+from .binding import (chunk_fwd, chunk_bwd, recurrent_step, chunk_fwd_workspace,  # noqa: F401
+                      chunk_bwd_workspace, library_path, abi_version)
 
-__all__ = ["chunk_fwd", "recurrent_step", "chunk_fwd_workspace", "library_path", "abi_version"]
+__all__ = ["chunk_fwd", "chunk_bwd", "recurrent_step", "chunk_fwd_workspace", "chunk_bwd_workspace",
+           "library_path", "abi_version"]

@@ -1,6 +1,6 @@
 """Thin Python binding of the C ABI in include/gdn2.h (argument marshalling only).
 
-``chunk_fwd`` and ``recurrent_step`` take torch CUDA (HIP) tensors, check
+``chunk_fwd``, ``chunk_bwd`` and ``recurrent_step`` take torch CUDA (HIP) tensors, check
 dtype / shape / device / contiguity, and pass raw device pointers plus
 torch's current stream to ``libgdn2.so``.  Every step of the computation runs
 in the library's gfx950 kernels; there is no CPU or torch fallback: if the
@@ -22,7 +22,7 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_UNSUPP
 
 # Every entry point include/gdn2.h declares.
 EXPORTS = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace",
-           "gdn2_chunk_fwd", "gdn2_recurrent_step")
+           "gdn2_chunk_fwd", "gdn2_chunk_bwd_workspace", "gdn2_chunk_bwd", "gdn2_recurrent_step")
 
 
 class Gdn2Desc(ctypes.Structure):
@@ -70,6 +70,11 @@ def load_library():
             lib.gdn2_chunk_fwd.restype = ctypes.c_int
             lib.gdn2_chunk_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp,
                                            ctypes.c_size_t, vp]
+            lib.gdn2_chunk_bwd_workspace.restype = ctypes.c_int
+            lib.gdn2_chunk_bwd_workspace.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
+            lib.gdn2_chunk_bwd.restype = ctypes.c_int
+            lib.gdn2_chunk_bwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
+                                           fp, fp, fp, vp, ctypes.c_size_t, vp]
             lib.gdn2_recurrent_step.restype = ctypes.c_int
             lib.gdn2_recurrent_step.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp]
             _lib = lib
@@ -194,6 +199,55 @@ def chunk_fwd(q, k, v, log_decay, erase, write=None, state0=None, chunk=64, q_sc
     if st != 0:
         raise Gdn2Error(st, "gdn2_chunk_fwd")
     return out, state_out
+
+
+def chunk_bwd_workspace(desc: Gdn2Desc) -> int:
+    n = ctypes.c_size_t(0)
+    st = load_library().gdn2_chunk_bwd_workspace(ctypes.byref(desc), ctypes.byref(n))
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_chunk_bwd_workspace")
+    return int(n.value)
+
+
+def chunk_bwd(q, k, v, log_decay, erase, write, state0, d_o, d_state=None, chunk=64,
+              q_scale=1.0, want_state0=True, workspace=None):
+    """Gradients of <d_o, o> + <d_state, S_T> for the chunkwise forward.
+
+    Inputs as for ``chunk_fwd``; d_o [B,T,H,dv] fp32; d_state [B,H,dk,dv]
+    fp32 or None (zeros).  Returns a dict of fp32 tensors: dq, dk, dv,
+    d_log_decay, d_erase, d_write (None when tied) shaped like their inputs,
+    and d_state0 (None unless ``want_state0``).  ``workspace``: None
+    allocates it, or a uint8 device tensor of at least chunk_bwd_workspace()
+    bytes.
+    """
+    import torch
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    desc = _desc_for(q, k, v, log_decay, erase, write, (B, T, H), B, T, H, chunk, q_scale)
+    dev = k.device
+    f32 = (torch.float32,)
+    if state0 is not None:
+        _check(state0, "state0", (B, H, dk, dv), f32, dev)
+    _check(d_o, "d_o", (B, T, H, dv), f32, dev)
+    if d_state is not None:
+        _check(d_state, "d_state", (B, H, dk, dv), f32, dev)
+    new = lambda t: torch.empty(tuple(t.shape), dtype=torch.float32, device=dev)
+    g = dict(dq=new(q), dk=new(k), dv=new(v), d_log_decay=new(log_decay), d_erase=new(erase),
+             d_write=None if write is None else new(write),
+             d_state0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_state0 else None)
+    if workspace is None:
+        n = chunk_bwd_workspace(desc)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    else:
+        _check(workspace, "workspace", tuple(workspace.shape), (torch.uint8,), dev)
+    st = load_library().gdn2_chunk_bwd(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(erase), _ptr(write),
+        _ptr(state0), _ptr(d_o), _ptr(d_state), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+        _ptr(g["d_log_decay"]), _ptr(g["d_erase"]), _ptr(g["d_write"]), _ptr(g["d_state0"]),
+        _ptr(workspace), workspace.numel(), _stream())
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_chunk_bwd")
+    return g
 
 
 def recurrent_step(q, k, v, log_decay, erase, write, state, q_scale=1.0, out=None):

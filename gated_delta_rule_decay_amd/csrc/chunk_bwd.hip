@@ -1,0 +1,618 @@
+// chunk_bwd.hip -- backward of the chunkwise GDN-2 forward, fp32 on the vector ALU.
+//
+// The gradients of L = <dO, o> + <dS_T, S_T> with respect to q, k, v, the
+// three gates and S0.  The forward is the chunk form of the recurrence
+// ("Gated DeltaNet-2" blog summary, "Core Mechanism"; gist.science summary,
+// "Technische Samenvatting" section 3): inside a chunk entered with state S,
+// with g the running sum of log a, e = b k, u = w k (w := b when tied),
+//   A, Bm = strictly lower Grams of (k, e) and (k, u), R, P = lower Grams of
+//   (q, e) and (q, u), each pair weighted by exp(g_r - g_s) per channel,
+//   Tm = (I + A)^-1, Kbar = k e^g, Qbar = q e^g, BV = Bm V,
+//   W = Tm Kbar, M = W S + Tm BV,
+//   O = Qbar S + P V - R M,
+//   S_out = Diag(e^gC) S + Util^T V - Etil^T M,  Util = u e^(gC-g), Etil = e e^(gC-g).
+// Reverse mode through these, chunk by chunk, given the gradient dSo of the
+// chunk's exit state:
+//   dM = -Etil dSo - R^T dO,     Y = Tm^T dM,
+//   dS = Diag(e^gC) dSo + Qbar^T dO + Kbar^T Y          (gradient of the entry state)
+//   dV = Util dSo + P^T dO + Bm^T Y
+//   dW = dM S^T, dQbar = dO S^T, dEtil = -M dSo^T, dUtil = V dSo^T
+//   dTm = dW Kbar^T + dM BV^T,  dKbar = Tm^T dW,  dA = -Tm^T dTm Tm^T (below the diagonal)
+//   dBm = Y V^T (r > s), dR = -dO M^T (r >= s), dP = dO V^T (r >= s)
+// and each Gram X_rs = sum_c L_r[c] F_s[c] exp(g_r[c] - g_s[c]) passes dX to
+// L, to F and to g (d g_r += L_r dL_r, d g_s -= F_s dF_s).  The decayed
+// operands pass their gradient to the raw ones and to g; the exit decay gC
+// collects its own terms; d log a is the reverse running sum of dg; and
+// e = b k, u = w k split their gradients between the gates and k.
+//
+// Three launches:
+//   1. the general forward records the state entering every chunk (hist);
+//   2. bwd_dstate_kernel walks the chunks backwards per (chain, value slice)
+//      carrying dS (value columns are independent) and records the gradient
+//      of every chunk's exit state (dhist), and dS0;
+//   3. bwd_grads_kernel takes every (chain, chunk) in parallel, recomputes
+//      the chunk's forward quantities from hist and forms all gradients.
+// Every pairwise decay exp(g_r - g_s) with r >= s is formed directly, so no
+// factor exceeds 1.
+#include "common.h"
+#include "kernels.h"
+
+namespace gdn2 {
+namespace {
+
+constexpr int kRevThreads = 256;
+constexpr int kRevBudget = 64 * 1024;
+constexpr int kGradThreads = 512;
+constexpr int kGradBudget = 160 * 1024;
+constexpr int RB = 4;  // rows per work item in the state products
+
+// ---------------------------------------------------------------------------
+// 2. reverse scan of the state gradient
+
+struct RevLayout {
+    int kf, qf, g, ee, dO, dM, Z, A, R, Tm, dS, gC, total;
+};
+
+__host__ __device__ inline RevLayout rev_layout(int Cg, int DVT, int dk) {
+    RevLayout L;
+    int off = 0;
+    auto take = [&](int n) { int o = off; off += n; return o; };
+    L.kf = take(Cg * dk);
+    L.qf = take(Cg * dk);
+    L.g = take(Cg * dk);
+    L.ee = take(Cg * dk);
+    L.dO = take(Cg * DVT);
+    L.dM = take(Cg * DVT);
+    L.Z = take(Cg * DVT);
+    L.A = take(Cg * Cg);
+    L.R = take(Cg * Cg);
+    L.Tm = take(Cg * Cg);
+    L.dS = take(dk * DVT);
+    L.gC = take(dk);
+    L.total = off;
+    return L;
+}
+
+__global__ void __launch_bounds__(kRevThreads) bwd_dstate_kernel(BwdArgs a, int Cg, int DVT, float *dhist) {
+    extern __shared__ float lds[];
+    const ChunkArgs &f = a.f;
+    const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
+    const int64_t T = f.T, H = f.H;
+    const RevLayout L = rev_layout(Cg, DVT, dk);
+    float *Kf = lds + L.kf, *Qf = lds + L.qf, *G = lds + L.g, *Ee = lds + L.ee;
+    float *dO = lds + L.dO, *dM = lds + L.dM, *Z = lds + L.Z;
+    float *A = lds + L.A, *R = lds + L.R, *Tm = lds + L.Tm, *dS = lds + L.dS, *gC = lds + L.gC;
+
+    const int64_t bh = blockIdx.x, b = bh / H, h = bh % H;
+    const int col0 = blockIdx.y * DVT, ncol = min(DVT, dv - col0);
+    const int tid = threadIdx.x;
+    const int64_t sbase = bh * static_cast<int64_t>(dk) * dv;
+    const int64_t nch = (T + Cg - 1) / Cg;
+
+    for (int idx = tid; idx < dk * DVT; idx += kRevThreads) {
+        const int c = idx / DVT, j = idx % DVT;
+        dS[idx] = (a.d_sT && j < ncol) ? a.d_sT[sbase + static_cast<int64_t>(c) * dv + col0 + j] : 0.f;
+    }
+    for (int64_t n = nch - 1; n >= 0; --n) {
+        const int64_t t0 = n * Cg;
+        __syncthreads();
+        // the gradient of this chunk's exit state, for the gradient pass
+        float *hs = dhist + (bh * nch + n) * static_cast<int64_t>(dk) * dv;
+        for (int idx = tid; idx < dk * DVT; idx += kRevThreads) {
+            const int c = idx / DVT, j = idx % DVT;
+            if (j < ncol) hs[static_cast<int64_t>(c) * dv + col0 + j] = dS[idx];
+        }
+        for (int idx = tid; idx < Cg * dk; idx += kRevThreads) {
+            const int r = idx / dk, c = idx % dk;
+            const int64_t t = t0 + r;
+            float kv = 0.f, qv = 0.f, la = 0.f, e = 0.f;
+            if (t < T) {
+                const int64_t row = (b * T + t) * H + h;
+                kv = load_qkv(f.k, row * dk + c, f.bf16);
+                qv = f.q_scale * load_qkv(f.q, row * dk + c, f.bf16);
+                la = load_gate(f.la, f.la_key, row, dk, c);
+                e = load_gate(f.eb, f.eb_key, row, dk, c) * kv;
+            }
+            Kf[idx] = kv;
+            Qf[idx] = qv;
+            G[idx] = la;
+            Ee[idx] = e;
+        }
+        for (int idx = tid; idx < Cg * DVT; idx += kRevThreads) {
+            const int r = idx / DVT, j = idx % DVT;
+            const int64_t t = t0 + r;
+            dO[idx] = (t < T && j < ncol) ? a.d_o[((b * T + t) * H + h) * dv + col0 + j] : 0.f;
+        }
+        __syncthreads();
+        for (int c = tid; c < dk; c += kRevThreads) {
+            float acc = 0.f;
+            for (int r = 0; r < Cg; ++r) {
+                acc += G[r * dk + c];
+                G[r * dk + c] = acc;
+            }
+            gC[c] = acc;
+        }
+        __syncthreads();
+        // erase Gram A (r > s) and query Gram R (r >= s)
+        for (int idx = tid; idx < Cg * Cg; idx += kRevThreads) {
+            const int r = idx / Cg, s = idx % Cg;
+            float sa = 0.f, sr = 0.f;
+            if (s <= r) {
+                for (int c = 0; c < dk; ++c) {
+                    const float d = expf(G[r * dk + c] - G[s * dk + c]);
+                    const float e = Ee[s * dk + c];
+                    sa += Kf[r * dk + c] * d * e;
+                    sr += Qf[r * dk + c] * d * e;
+                }
+            }
+            A[idx] = s < r ? sa : 0.f;
+            R[idx] = sr;
+        }
+        __syncthreads();
+        if (tid < Cg) {
+            const int j = tid;
+            for (int r = 0; r < Cg; ++r) {
+                float val = r < j ? 0.f : 1.f;
+                if (r > j) {
+                    float acc = 0.f;
+                    for (int s = j; s < r; ++s) acc += A[r * Cg + s] * Tm[s * Cg + j];
+                    val = -acc;
+                }
+                Tm[r * Cg + j] = val;
+            }
+        }
+        for (int idx = tid; idx < Cg * dk; idx += kRevThreads) {
+            const int c = idx % dk;
+            const float eg = expf(G[idx]);
+            Kf[idx] *= eg;                        // Kbar
+            Qf[idx] *= eg;                        // Qbar
+            Ee[idx] *= expf(gC[c] - G[idx]);      // Etil
+        }
+        __syncthreads();
+        // dM = -Etil dSo - R^T dO
+        for (int idx = tid; idx < Cg * DVT; idx += kRevThreads) {
+            const int r = idx / DVT, j = idx % DVT;
+            float acc = 0.f;
+            for (int c = 0; c < dk; ++c) acc += Ee[r * dk + c] * dS[c * DVT + j];
+            for (int s = r; s < Cg; ++s) acc += R[s * Cg + r] * dO[s * DVT + j];
+            dM[idx] = -acc;
+        }
+        __syncthreads();
+        // Y = Tm^T dM
+        for (int idx = tid; idx < Cg * DVT; idx += kRevThreads) {
+            const int s = idx / DVT, j = idx % DVT;
+            float acc = 0.f;
+            for (int r = s; r < Cg; ++r) acc += Tm[r * Cg + s] * dM[r * DVT + j];
+            Z[idx] = acc;
+        }
+        __syncthreads();
+        // dS <- Diag(e^gC) dS + Qbar^T dO + Kbar^T Y (each thread owns its elements)
+        for (int idx = tid; idx < dk * DVT; idx += kRevThreads) {
+            const int c = idx / DVT, j = idx % DVT;
+            float acc = expf(gC[c]) * dS[idx];
+            for (int r = 0; r < Cg; ++r) acc += Qf[r * dk + c] * dO[r * DVT + j] + Kf[r * dk + c] * Z[r * DVT + j];
+            dS[idx] = acc;
+        }
+    }
+    __syncthreads();
+    if (a.ds0) {
+        for (int idx = tid; idx < dk * DVT; idx += kRevThreads) {
+            const int c = idx / DVT, j = idx % DVT;
+            if (j < ncol) a.ds0[sbase + static_cast<int64_t>(c) * dv + col0 + j] = dS[idx];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 3. per-chunk gradients
+
+struct GradLayout {
+    int K, Q, G, E, U, EG, EC, W, dW, dQ, dE, dU;  // Cg x dk
+    int V, dO, BV, M, dM, Y;                        // Cg x dv
+    int A, Bm, R, P, Tm, dT, X1, dA, dBm, dR, dP;   // Cg x Cg
+    int gC, dgC;                                    // dk
+    int total;
+};
+
+__host__ __device__ inline GradLayout grad_layout(int Cg, int dk, int dv) {
+    GradLayout L;
+    int off = 0;
+    auto take = [&](int n) { int o = off; off += n; return o; };
+    L.K = take(Cg * dk); L.Q = take(Cg * dk); L.G = take(Cg * dk); L.E = take(Cg * dk);
+    L.U = take(Cg * dk); L.EG = take(Cg * dk); L.EC = take(Cg * dk); L.W = take(Cg * dk);
+    L.dW = take(Cg * dk); L.dQ = take(Cg * dk); L.dE = take(Cg * dk); L.dU = take(Cg * dk);
+    L.V = take(Cg * dv); L.dO = take(Cg * dv); L.BV = take(Cg * dv); L.M = take(Cg * dv);
+    L.dM = take(Cg * dv); L.Y = take(Cg * dv);
+    L.A = take(Cg * Cg); L.Bm = take(Cg * Cg); L.R = take(Cg * Cg); L.P = take(Cg * Cg);
+    L.Tm = take(Cg * Cg); L.dT = take(Cg * Cg); L.X1 = take(Cg * Cg); L.dA = take(Cg * Cg);
+    L.dBm = take(Cg * Cg); L.dR = take(Cg * Cg); L.dP = take(Cg * Cg);
+    L.gC = take(dk); L.dgC = take(dk);
+    L.total = off;
+    return L;
+}
+
+__global__ void __launch_bounds__(kGradThreads)
+bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
+    extern __shared__ float lds[];
+    const ChunkArgs &f = a.f;
+    const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
+    const int64_t T = f.T, H = f.H;
+    const GradLayout L = grad_layout(Cg, dk, dv);
+    float *K = lds + L.K, *Q = lds + L.Q, *G = lds + L.G, *E = lds + L.E, *U = lds + L.U;
+    float *EG = lds + L.EG, *EC = lds + L.EC, *W = lds + L.W, *dW = lds + L.dW, *dQ = lds + L.dQ;
+    float *dE = lds + L.dE, *dU = lds + L.dU;
+    float *V = lds + L.V, *dO = lds + L.dO, *BV = lds + L.BV, *M = lds + L.M, *dM = lds + L.dM, *Y = lds + L.Y;
+    float *A = lds + L.A, *Bm = lds + L.Bm, *R = lds + L.R, *P = lds + L.P, *Tm = lds + L.Tm;
+    float *dT = lds + L.dT, *X1 = lds + L.X1, *dA = lds + L.dA, *dBm = lds + L.dBm, *dR = lds + L.dR, *dP = lds + L.dP;
+    float *gC = lds + L.gC, *dgC = lds + L.dgC;
+
+    const int64_t nch = (T + Cg - 1) / Cg;
+    const int64_t bh = blockIdx.x / nch, n = blockIdx.x % nch;
+    const int64_t b = bh / H, h = bh % H, t0 = n * Cg;
+    const int tid = threadIdx.x;
+    const float *Sg = hist + (bh * nch + n) * static_cast<int64_t>(dk) * dv;    // entry state
+    const float *dSg = dhist + (bh * nch + n) * static_cast<int64_t>(dk) * dv;  // exit gradient
+    auto row_of = [&](int r) { return (b * T + t0 + r) * H + h; };
+    auto live = [&](int r) { return t0 + r < T; };
+
+    // P0: the chunk's inputs (rows past T are zero and contribute nothing)
+    for (int idx = tid; idx < Cg * dk; idx += kGradThreads) {
+        const int r = idx / dk, c = idx % dk;
+        float kv = 0.f, qv = 0.f, la = 0.f, e = 0.f, u = 0.f;
+        if (live(r)) {
+            const int64_t row = row_of(r);
+            kv = load_qkv(f.k, row * dk + c, f.bf16);
+            qv = f.q_scale * load_qkv(f.q, row * dk + c, f.bf16);
+            la = load_gate(f.la, f.la_key, row, dk, c);
+            const float bb = load_gate(f.eb, f.eb_key, row, dk, c);
+            const float ww = f.wr ? load_gate(f.wr, f.wr_key, row, dk, c) : bb;
+            e = bb * kv;
+            u = ww * kv;
+        }
+        K[idx] = kv; Q[idx] = qv; G[idx] = la; E[idx] = e; U[idx] = u;
+    }
+    for (int idx = tid; idx < Cg * dv; idx += kGradThreads) {
+        const int r = idx / dv, j = idx % dv;
+        const bool ok = live(r);
+        V[idx] = ok ? load_qkv(f.v, row_of(r) * dv + j, f.bf16) : 0.f;
+        dO[idx] = ok ? a.d_o[row_of(r) * dv + j] : 0.f;
+    }
+    __syncthreads();
+    // P1: running log-decay, e^g and e^(gC - g)
+    for (int c = tid; c < dk; c += kGradThreads) {
+        float acc = 0.f;
+        for (int r = 0; r < Cg; ++r) {
+            acc += G[r * dk + c];
+            G[r * dk + c] = acc;
+        }
+        gC[c] = acc;
+        dgC[c] = 0.f;
+        for (int r = 0; r < Cg; ++r) {
+            EG[r * dk + c] = expf(G[r * dk + c]);
+            EC[r * dk + c] = expf(acc - G[r * dk + c]);
+        }
+    }
+    __syncthreads();
+    // P2: the four Grams
+    for (int idx = tid; idx < Cg * Cg; idx += kGradThreads) {
+        const int r = idx / Cg, s = idx % Cg;
+        float sa = 0.f, sb = 0.f, sr = 0.f, sp = 0.f;
+        if (s <= r) {
+            for (int c = 0; c < dk; ++c) {
+                const float d = expf(G[r * dk + c] - G[s * dk + c]);
+                const float kd = K[r * dk + c] * d, qd = Q[r * dk + c] * d;
+                const float e = E[s * dk + c], u = U[s * dk + c];
+                sa += kd * e; sb += kd * u; sr += qd * e; sp += qd * u;
+            }
+        }
+        A[idx] = s < r ? sa : 0.f;
+        Bm[idx] = s < r ? sb : 0.f;
+        R[idx] = sr;
+        P[idx] = sp;
+    }
+    __syncthreads();
+    // P3: Tm = (I + A)^-1, a column per thread
+    if (tid < Cg) {
+        const int j = tid;
+        for (int r = 0; r < Cg; ++r) {
+            float val = r < j ? 0.f : 1.f;
+            if (r > j) {
+                float acc = 0.f;
+                for (int s = j; s < r; ++s) acc += A[r * Cg + s] * Tm[s * Cg + j];
+                val = -acc;
+            }
+            Tm[r * Cg + j] = val;
+        }
+    }
+    __syncthreads();
+    // P4: W = Tm Kbar, BV = Bm V
+    for (int idx = tid; idx < Cg * dk; idx += kGradThreads) {
+        const int r = idx / dk, c = idx % dk;
+        float acc = 0.f;
+        for (int s = 0; s <= r; ++s) acc += Tm[r * Cg + s] * K[s * dk + c] * EG[s * dk + c];
+        W[idx] = acc;
+    }
+    for (int idx = tid; idx < Cg * dv; idx += kGradThreads) {
+        const int r = idx / dv, j = idx % dv;
+        float acc = 0.f;
+        for (int s = 0; s < r; ++s) acc += Bm[r * Cg + s] * V[s * dv + j];
+        BV[idx] = acc;
+    }
+    __syncthreads();
+    // P5: M = W S + Tm BV and dM = -Etil dSo - R^T dO; work item = one value
+    // column j and RB rows, S and dSo streamed from memory along c
+    for (int item = tid; item < dv * (Cg / RB); item += kGradThreads) {
+        const int j = item % dv, r0 = (item / dv) * RB;
+        float am[RB], ad[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) am[i] = ad[i] = 0.f;
+        for (int c = 0; c < dk; ++c) {
+            const float sv = Sg[static_cast<int64_t>(c) * dv + j], dsv = dSg[static_cast<int64_t>(c) * dv + j];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const int r = r0 + i;
+                am[i] += W[r * dk + c] * sv;
+                ad[i] += E[r * dk + c] * EC[r * dk + c] * dsv;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int r = r0 + i;
+            float mu = am[i], dm = ad[i];
+            for (int s = 0; s <= r; ++s) mu += Tm[r * Cg + s] * BV[s * dv + j];
+            for (int s = r; s < Cg; ++s) dm += R[s * Cg + r] * dO[s * dv + j];
+            M[r * dv + j] = mu;
+            dM[r * dv + j] = -dm;
+        }
+    }
+    __syncthreads();
+    // P6: Y = Tm^T dM; the exit decay's own term dgC = e^gC (dSo . S) per channel
+    for (int idx = tid; idx < Cg * dv; idx += kGradThreads) {
+        const int s = idx / dv, j = idx % dv;
+        float acc = 0.f;
+        for (int r = s; r < Cg; ++r) acc += Tm[r * Cg + s] * dM[r * dv + j];
+        Y[idx] = acc;
+    }
+    for (int c = tid; c < dk; c += kGradThreads) {
+        float acc = 0.f;
+        for (int j = 0; j < dv; ++j) acc += dSg[static_cast<int64_t>(c) * dv + j] * Sg[static_cast<int64_t>(c) * dv + j];
+        dgC[c] = expf(gC[c]) * acc;
+    }
+    __syncthreads();
+    // P7: dV -> memory; dW, dQbar, dEtil, dUtil; dBm, dR, dP
+    for (int item = tid; item < dv * (Cg / RB); item += kGradThreads) {
+        const int j = item % dv, s0 = (item / dv) * RB;
+        float acc[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) acc[i] = 0.f;
+        for (int c = 0; c < dk; ++c) {
+            const float dsv = dSg[static_cast<int64_t>(c) * dv + j];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) acc[i] += U[(s0 + i) * dk + c] * EC[(s0 + i) * dk + c] * dsv;
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int s = s0 + i;
+            float x = acc[i];
+            for (int r = s; r < Cg; ++r) x += P[r * Cg + s] * dO[r * dv + j];
+            for (int r = s + 1; r < Cg; ++r) x += Bm[r * Cg + s] * Y[r * dv + j];
+            if (live(s)) a.dv[row_of(s) * dv + j] = x;
+        }
+    }
+    for (int item = tid; item < dk * (Cg / RB); item += kGradThreads) {
+        const int c = item % dk, r0 = (item / dk) * RB;
+        float aw[RB], aq[RB], ae[RB], au[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) aw[i] = aq[i] = ae[i] = au[i] = 0.f;
+        for (int j = 0; j < dv; ++j) {
+            const float sv = Sg[static_cast<int64_t>(c) * dv + j], dsv = dSg[static_cast<int64_t>(c) * dv + j];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const int r = r0 + i;
+                aw[i] += dM[r * dv + j] * sv;
+                aq[i] += dO[r * dv + j] * sv;
+                ae[i] -= M[r * dv + j] * dsv;
+                au[i] += V[r * dv + j] * dsv;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            const int r = r0 + i;
+            dW[r * dk + c] = aw[i];
+            dQ[r * dk + c] = aq[i];
+            dE[r * dk + c] = ae[i];
+            dU[r * dk + c] = au[i];
+        }
+    }
+    for (int idx = tid; idx < Cg * Cg; idx += kGradThreads) {
+        const int r = idx / Cg, s = idx % Cg;
+        float xb = 0.f, xr = 0.f, xp = 0.f;
+        if (s <= r) {
+            for (int j = 0; j < dv; ++j) {
+                const float o = dO[r * dv + j], vs = V[s * dv + j];
+                xb += Y[r * dv + j] * vs;
+                xr -= o * M[s * dv + j];
+                xp += o * vs;
+            }
+        }
+        dBm[idx] = s < r ? xb : 0.f;
+        dR[idx] = xr;
+        dP[idx] = xp;
+    }
+    __syncthreads();
+    // P8: dTm (lower part) = dW Kbar^T + dM BV^T; dKbar = Tm^T dW (into W)
+    for (int idx = tid; idx < Cg * Cg; idx += kGradThreads) {
+        const int r = idx / Cg, s = idx % Cg;
+        float acc = 0.f;
+        if (s <= r) {
+            for (int c = 0; c < dk; ++c) acc += dW[r * dk + c] * K[s * dk + c] * EG[s * dk + c];
+            for (int j = 0; j < dv; ++j) acc += dM[r * dv + j] * BV[s * dv + j];
+        }
+        dT[idx] = acc;
+    }
+    for (int idx = tid; idx < Cg * dk; idx += kGradThreads) {
+        const int s = idx / dk, c = idx % dk;
+        float acc = 0.f;
+        for (int r = s; r < Cg; ++r) acc += Tm[r * Cg + s] * dW[r * dk + c];
+        W[idx] = acc;
+    }
+    __syncthreads();
+    // P9: dA = -(Tm^T dTm) Tm^T, strictly below the diagonal
+    for (int idx = tid; idx < Cg * Cg; idx += kGradThreads) {
+        const int i = idx / Cg, j = idx % Cg;
+        float acc = 0.f;
+        for (int r = (i > j ? i : j); r < Cg; ++r) acc += Tm[r * Cg + i] * dT[r * Cg + j];
+        X1[idx] = acc;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < Cg * Cg; idx += kGradThreads) {
+        const int r = idx / Cg, s = idx % Cg;
+        float acc = 0.f;
+        if (s < r)
+            for (int j = 0; j <= s; ++j) acc += X1[r * Cg + j] * Tm[s * Cg + j];
+        dA[idx] = -acc;
+    }
+    __syncthreads();
+    // P10: per (token x, channel c): the Grams' gradients with x as row and as
+    // column, the decayed operands', then k, q and the gates
+    const bool la_key = f.la_key, eb_key = f.eb_key, wr_key = f.wr_key, tied = f.wr == nullptr;
+    for (int idx = tid; idx < Cg * dk; idx += kGradThreads) {
+        const int x = idx / dk, c = idx % dk;
+        const float gx = G[idx];
+        float glk = 0.f, glq = 0.f, gre = 0.f, gru = 0.f;
+        for (int y = 0; y < x; ++y) {  // x as the row of a Gram
+            const float d = expf(gx - G[y * dk + c]);
+            const float ey = E[y * dk + c], uy = U[y * dk + c];
+            glk += (dA[x * Cg + y] * ey + dBm[x * Cg + y] * uy) * d;
+            glq += (dR[x * Cg + y] * ey + dP[x * Cg + y] * uy) * d;
+        }
+        glq += dR[x * Cg + x] * E[idx] + dP[x * Cg + x] * U[idx];
+        gre += dR[x * Cg + x] * Q[idx];
+        gru += dP[x * Cg + x] * Q[idx];
+        for (int y = x + 1; y < Cg; ++y) {  // x as the column
+            const float d = expf(G[y * dk + c] - gx);
+            const float ky = K[y * dk + c], qy = Q[y * dk + c];
+            gre += (dA[y * Cg + x] * ky + dR[y * Cg + x] * qy) * d;
+            gru += (dBm[y * Cg + x] * ky + dP[y * Cg + x] * qy) * d;
+        }
+        const float kx = K[idx], qx = Q[idx], ex = E[idx], ux = U[idx], eg = EG[idx], ec = EC[idx];
+        const float dkb = W[idx], dqb = dQ[idx], det = dE[idx], dut = dU[idx];
+        const float de = gre + det * ec, du = gru + dut * ec;
+        const float dg = kx * glk + qx * glq - ex * gre - ux * gru + (dkb * kx + dqb * qx) * eg -
+                         (det * ex + dut * ux) * ec;
+        float dkk = glk + dkb * eg;
+        float dbv, dwv = 0.f;
+        if (live(x)) {
+            const int64_t row = row_of(x);
+            const float bb = load_gate(f.eb, eb_key, row, dk, c);
+            if (tied) {
+                dkk += (de + du) * bb;
+                dbv = (de + du) * kx;
+            } else {
+                const float ww = load_gate(f.wr, wr_key, row, dk, c);
+                dkk += de * bb + du * ww;
+                dbv = de * kx;
+                dwv = du * kx;
+            }
+            a.dq[row * dk + c] = f.q_scale * (glq + dqb * eg);
+            a.dk[row * dk + c] = dkk;
+            if (eb_key) a.deb[row * dk + c] = dbv;
+            if (!tied && wr_key) a.dwr[row * dk + c] = dwv;
+        } else {
+            dbv = 0.f;
+        }
+        dE[idx] = (det * ex + dut * ux) * ec;  // this token's share of d gC
+        dQ[idx] = dg;
+        dU[idx] = dbv;
+        dW[idx] = dwv;
+    }
+    __syncthreads();
+    // P11: d log a = reverse running sum of dg, d gC entering at the last row
+    for (int c = tid; c < dk; c += kGradThreads) {
+        float run = dgC[c];
+        for (int x = 0; x < Cg; ++x) run += dE[x * dk + c];
+        for (int x = Cg - 1; x >= 0; --x) {
+            run += dQ[x * dk + c];
+            if (la_key) {
+                if (live(x)) a.dla[row_of(x) * dk + c] = run;
+            } else {
+                dQ[x * dk + c] = run;
+            }
+        }
+    }
+    __syncthreads();
+    // P12: gates with one value per token-head sum their channels
+    if (tid < Cg && live(tid) && (!la_key || !eb_key || (!tied && !wr_key))) {
+        const int x = tid;
+        float sl = 0.f, sb = 0.f, sw = 0.f;
+        for (int c = 0; c < dk; ++c) {
+            sl += dQ[x * dk + c];
+            sb += dU[x * dk + c];
+            sw += dW[x * dk + c];
+        }
+        const int64_t row = row_of(x);
+        if (!la_key) a.dla[row] = sl;
+        if (!eb_key) a.deb[row] = sb;
+        if (!tied && !wr_key) a.dwr[row] = sw;
+    }
+}
+
+}  // namespace
+
+int chunk_bwd_chunk(int64_t dk, int64_t dv, int C) {
+    for (int c = C; c >= 8; c /= 2) {
+        if (grad_layout(c, static_cast<int>(dk), static_cast<int>(dv)).total * 4 > kGradBudget) continue;
+        if (rev_layout(c, dv < 8 ? static_cast<int>(dv) : 8, static_cast<int>(dk)).total * 4 > kRevBudget) continue;
+        return c;
+    }
+    return 0;
+}
+
+size_t chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int C) {
+    const int Cg = chunk_bwd_chunk(dk, dv, C);
+    if (!Cg || B * H * T == 0) return 0;
+    const int64_t one = B * H * ((T + Cg - 1) / Cg) * dk * dv * 4;
+    return static_cast<size_t>(2 * ((one + 255) & ~int64_t(255)));
+}
+
+hipError_t launch_chunk_bwd(const BwdArgs &a, void *ws, hipStream_t s) {
+    const ChunkArgs &f = a.f;
+    const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
+    const int Cg = chunk_bwd_chunk(dk, dv, f.C);
+    if (!Cg) return hipErrorInvalidValue;
+    const int64_t nch = (f.T + Cg - 1) / Cg;
+    const int64_t one = f.B * f.H * nch * dk * dv * 4;
+    float *hist = static_cast<float *>(ws);
+    float *dhist = reinterpret_cast<float *>(static_cast<char *>(ws) + ((one + 255) & ~int64_t(255)));
+    if (f.B * f.H * nch > 0x7fffffffLL) return hipErrorInvalidValue;
+
+    ChunkArgs fwd = f;
+    fwd.o = nullptr;
+    fwd.s_out = nullptr;
+    hipError_t e = launch_chunk_general_hist(fwd, Cg, hist, s);
+    if (e != hipSuccess) return e;
+
+    int DVT = 0;
+    for (int w = 32; w >= 8 && !DVT; w /= 2) {
+        const int wv = dv < w ? dv : w;
+        if (rev_layout(Cg, wv, dk).total * 4 <= kRevBudget) DVT = wv;
+    }
+    if (!DVT) return hipErrorInvalidValue;
+    size_t lds = static_cast<size_t>(rev_layout(Cg, DVT, dk).total) * 4;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_dstate_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds))) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(bwd_dstate_kernel, dim3(static_cast<unsigned>(f.B * f.H), static_cast<unsigned>((dv + DVT - 1) / DVT)),
+                       dim3(kRevThreads), lds, s, a, Cg, DVT, dhist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    lds = static_cast<size_t>(grad_layout(Cg, dk, dv).total) * 4;
+    if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_grads_kernel),
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds))) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(bwd_grads_kernel, dim3(static_cast<unsigned>(f.B * f.H * nch)), dim3(kGradThreads), lds, s, a,
+                       Cg, static_cast<const float *>(hist), static_cast<const float *>(dhist));
+    return hipGetLastError();
+}
+
+}  // namespace gdn2

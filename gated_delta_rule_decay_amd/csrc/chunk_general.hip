@@ -19,6 +19,10 @@
 // a DVT-wide slice of the value channels (value columns evolve independently
 // given the chunk's Grams) and walks the chunks in order; the state slice
 // stays in LDS for the whole sequence.
+//
+// With `hist` set (the backward's first step), the kernel instead records
+// the state entering every chunk, hist[chain][chunk][dk][dv], and writes
+// no output.
 #include "common.h"
 #include "kernels.h"
 
@@ -55,7 +59,7 @@ __host__ __device__ inline GenLayout gen_layout(int Cg, int DVT, int dk) {
     return L;
 }
 
-__global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, int Cg, int DVT) {
+__global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, int Cg, int DVT, float *hist) {
     extern __shared__ float lds[];
     const int dk = static_cast<int>(a.dk), dv = static_cast<int>(a.dv);
     const int64_t T = a.T, H = a.H;
@@ -77,8 +81,16 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
         S[idx] = (a.s0 && j < ncol) ? a.s0[sbase + static_cast<int64_t>(c) * dv + col0 + j] : 0.f;
     }
 
+    const int64_t nch = (T + Cg - 1) / Cg;
     for (int64_t t0 = 0; t0 < T; t0 += Cg) {
         __syncthreads();
+        if (hist) {
+            float *hs = hist + ((b * H + h) * nch + t0 / Cg) * static_cast<int64_t>(dk) * dv;
+            for (int idx = tid; idx < dk * DVT; idx += kThreads) {
+                const int c = idx / DVT, j = idx % DVT;
+                if (j < ncol) hs[static_cast<int64_t>(c) * dv + col0 + j] = S[idx];
+            }
+        }
         // 1. stage the chunk: keys, queries, raw log-decay, e = b*k, u = w*k, values
         for (int idx = tid; idx < Cg * dk; idx += kThreads) {
             const int r = idx / dk, c = idx % dk;
@@ -185,7 +197,7 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
         }
         __syncthreads();
         // 7. O = Qbar S + P V - R M
-        for (int idx = tid; idx < Cg * DVT; idx += kThreads) {
+        for (int idx = tid; idx < (hist ? 0 : Cg * DVT); idx += kThreads) {
             const int r = idx / DVT, j = idx % DVT;
             const int64_t t = t0 + r;
             if (t >= T || j >= ncol) continue;
@@ -235,7 +247,25 @@ hipError_t launch_chunk_general(const ChunkArgs &a, hipStream_t s) {
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
     dim3 grid(static_cast<unsigned>(a.B * a.H), static_cast<unsigned>((dv + DVT - 1) / DVT));
-    hipLaunchKernelGGL(chunk_general_kernel, grid, dim3(kThreads), lds, s, a, Cg, DVT);
+    hipLaunchKernelGGL(chunk_general_kernel, grid, dim3(kThreads), lds, s, a, Cg, DVT, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_general_hist(const ChunkArgs &a, int Cg, float *hist, hipStream_t s) {
+    const int dk = static_cast<int>(a.dk), dv = static_cast<int>(a.dv);
+    int DVT = 0;
+    for (int w = 32; w >= 8 && !DVT; w /= 2) {
+        const int wv = dv < w ? dv : w;
+        if (gen_layout(Cg, wv, dk).total * 4 <= kLdsBudget) DVT = wv;
+    }
+    if (!DVT) return hipErrorInvalidValue;
+    const size_t lds = static_cast<size_t>(gen_layout(Cg, DVT, dk).total) * 4;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(chunk_general_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+    dim3 grid(static_cast<unsigned>(a.B * a.H), static_cast<unsigned>((dv + DVT - 1) / DVT));
+    hipLaunchKernelGGL(chunk_general_kernel, grid, dim3(kThreads), lds, s, a, Cg, DVT, hist);
     return hipGetLastError();
 }
 

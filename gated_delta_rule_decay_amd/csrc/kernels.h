@@ -47,6 +47,23 @@ bool chunk_split_supported(const ChunkArgs &a);
 size_t chunk_split_workspace(int64_t B, int64_t H, int64_t T);
 hipError_t launch_chunk_split(const ChunkArgs &a, void *ws, hipStream_t s);
 
+// The general forward recording the state that enters every chunk of Cg
+// tokens, hist[B*H][ceil(T/Cg)][dk][dv]; writes neither o nor the final state.
+hipError_t launch_chunk_general_hist(const ChunkArgs &a, int Cg, float *hist, hipStream_t s);
+
+// Backward of the chunked forward: gradients of <d_o, o> + <d_sT, S_T>.
+struct BwdArgs {
+    ChunkArgs f;            // the forward's inputs (f.o and f.s_out unused)
+    const float *d_o;       // [B,T,H,dv]
+    const float *d_sT;      // [B,H,dk,dv] or nullptr (zeros)
+    float *dq, *dk, *dv;    // [B,T,H,dk] / [B,T,H,dv]
+    float *dla, *deb, *dwr; // shaped like the gates; dwr nullptr when tied
+    float *ds0;             // [B,H,dk,dv] or nullptr
+};
+int chunk_bwd_chunk(int64_t dk, int64_t dv, int C);  // internal chunk length (0: none fits)
+size_t chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int C);
+hipError_t launch_chunk_bwd(const BwdArgs &a, void *ws, hipStream_t s);
+
 // Recurrent decode step.
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
 

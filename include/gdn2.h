@@ -144,6 +144,51 @@ gdn2_status gdn2_chunk_fwd(const gdn2_desc *desc,
                            const float *state0, float *o, float *state_out,
                            void *workspace, size_t ws_bytes, void *stream);
 
+/* Device workspace, in bytes, for gdn2_chunk_bwd on `desc`: two fp32 state
+ * histories, B*H*ceil(T/Cb)*dk*dv*4 bytes each (Cb = 16 for dk = dv = 128,
+ * larger for small heads; each region 256-byte aligned).  Same validation
+ * as gdn2_chunk_fwd; GDN2_ERR_UNSUPPORTED if no internal chunk fits. */
+gdn2_status gdn2_chunk_bwd_workspace(const gdn2_desc *desc, size_t *bytes);
+
+/*
+ * Backward of gdn2_chunk_fwd: the gradients of
+ *     L = <d_o, o> + <d_state_out, S_T>
+ * with respect to q, k, v, the three gates and state0.  Training is why the
+ * chunk form exists ("Gated DeltaNet-2" blog summary, "Core Mechanism": the
+ * chunkwise algorithm and its kernels serve training; gist.science summary,
+ * "Technische Samenvatting" section 3).  The result equals reverse-mode
+ * differentiation of the token recurrence (up to rounding).  It is computed
+ * chunk by chunk in fp32 on the vector ALU: the forward recomputes and
+ * records the state entering every internal chunk, a reverse scan carries
+ * the state gradient back through the chunks, then every chunk forms its
+ * gradients in parallel from the two records.
+ *
+ *   q .. state0  the forward's inputs (same layouts and rules as
+ *                gdn2_chunk_fwd; state0 NULL means zeros).
+ *   d_o          gradient of o, [B,T,H,dv] fp32 (required).
+ *   d_state_out  gradient of the final state [B,H,dk,dv] fp32, or NULL for
+ *                zeros.
+ *   dq, dk, dv   fp32, [B,T,H,dk] / [B,T,H,dv] (fp32 whatever qkv_dtype).
+ *   d_log_decay, d_erase, d_write   fp32, shaped like their gate (per key
+ *                channel or per token-head); d_write ignored (may be NULL)
+ *                when tied, and then d_erase holds the gradient of the one
+ *                shared gate.
+ *   d_state0     gradient of state0 [B,H,dk,dv] fp32, or NULL to skip.
+ *   workspace    device scratch of ws_bytes >= gdn2_chunk_bwd_workspace(),
+ *                256-byte aligned, else GDN2_ERR_WORKSPACE; contents need no
+ *                initialisation and are undefined afterwards.
+ * Outputs must not overlap each other, any input or the workspace
+ * (GDN2_ERR_ALIAS).  Every output is written in full.  With T == 0,
+ * d_state0 receives d_state_out (or zeros) and nothing else is touched.
+ */
+gdn2_status gdn2_chunk_bwd(const gdn2_desc *desc,
+                           const void *q, const void *k, const void *v,
+                           const float *log_decay, const float *erase, const float *write,
+                           const float *state0, const float *d_o, const float *d_state_out,
+                           float *dq, float *dk, float *dv,
+                           float *d_log_decay, float *d_erase, float *d_write,
+                           float *d_state0, void *workspace, size_t ws_bytes, void *stream);
+
 /*
  * One recurrent decode step for N = desc->batch sequences (desc->seqlen must
  * be 1): the O(1)-memory inference form ("Gated DeltaNet-2" blog summary,

@@ -189,3 +189,51 @@ def test_workspace_checks(lib):
     assert fwd(lib, d, ws=Q, wsb=need) == 5            # on top of q
     assert fwd(lib, d, ws=O - 256, wsb=need) == 5      # runs into o
     assert fwd(lib, d, ws=SO - need + 256, wsb=need) == 5  # runs into state_out
+
+
+# ---- the backward ---------------------------------------------------------
+
+DO, DST, DQ, DK, DV, DLA, DEB, DWR, DS0, BWS = (BASE + (20 + i) * SLOT for i in range(10))
+
+
+def bwd(lib, desc, d_o=DO, dst=DST, dq=DQ, dk=DK, dv=DV, dla=DLA, deb=DEB, dwr=DWR, ds0=DS0,
+        ws=BWS, wsb=None, q=Q, s0=S0):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    if wsb is None:
+        wsb = bwd_bytes(desc) if desc is not None else 0
+    return lib.gdn2_chunk_bwd(None if desc is None else ctypes.byref(desc), vp(q), vp(K), vp(V), vp(LA),
+                              vp(EB), vp(WR), vp(s0), vp(d_o), vp(dst), vp(dq), vp(dk), vp(dv), vp(dla),
+                              vp(deb), vp(dwr), vp(ds0), vp(ws), wsb, None)
+
+
+def bwd_bytes(desc):
+    """Two fp32 state records per (chain, internal chunk): 16 tokens for
+    d = 128, 32 for d <= 32 at chunk 64 (whatever fits LDS)."""
+    n = ctypes.c_size_t(0)
+    assert bd.load_library().gdn2_chunk_bwd_workspace(ctypes.byref(desc), ctypes.byref(n)) == 0
+    return n.value
+
+
+def test_bwd_workspace_query(lib):
+    a = lambda x: (x + 255) // 256 * 256
+    assert bwd_bytes(good()) == 2 * a(2 * 4 * (128 // 16) * 128 * 128 * 4)
+    assert bwd_bytes(good(seqlen=100)) == 2 * a(2 * 4 * 7 * 128 * 128 * 4)
+    assert bwd_bytes(good(dk=32, dv=32, chunk=64)) == 2 * a(2 * 4 * (128 // 32) * 32 * 32 * 4)
+    assert bwd_bytes(good(seqlen=0)) == 0
+
+
+def test_bwd_checks(lib):
+    d = good()
+    assert bwd(lib, None) == 1
+    assert bwd(lib, d, d_o=None) == 1
+    assert bwd(lib, d, dq=None) == 1
+    assert bwd(lib, d, dwr=None) == 1
+    assert bwd(lib, d, ws=None) == 6
+    assert bwd(lib, d, wsb=bwd_bytes(d) - 1) == 6
+    assert bwd(lib, d, ws=BWS + 16) == 6
+    assert bwd(lib, d, dq=Q) == 5                    # gradient on top of an input
+    assert bwd(lib, d, dk=DQ + 64) == 5              # two gradients overlap
+    assert bwd(lib, d, ds0=BWS + 4096) == 5          # gradient inside the workspace
+    assert bwd(lib, d, dv=DO) == 5                   # gradient on top of d_o
+    assert bwd(lib, good(dk=129), wsb=0) == 4
+    assert bwd(lib, good(chunk=8), wsb=0) == 4

@@ -46,6 +46,10 @@ constexpr int kGradThreads = 512;
 constexpr int kGradBudget = 160 * 1024;
 constexpr int RB = 4;  // rows per work item in the state products
 
+// Row stride of the token-by-channel arrays in LDS: odd, so that lanes
+// reading one channel of different rows (the Gram loops) hit different banks.
+__host__ __device__ inline int row_stride(int d) { return d | 1; }
+
 // ---------------------------------------------------------------------------
 // 2. reverse scan of the state gradient
 
@@ -57,10 +61,11 @@ __host__ __device__ inline RevLayout rev_layout(int Cg, int DVT, int dk) {
     RevLayout L;
     int off = 0;
     auto take = [&](int n) { int o = off; off += n; return o; };
-    L.kf = take(Cg * dk);
-    L.qf = take(Cg * dk);
-    L.g = take(Cg * dk);
-    L.ee = take(Cg * dk);
+    const int KS = row_stride(dk);
+    L.kf = take(Cg * KS);
+    L.qf = take(Cg * KS);
+    L.g = take(Cg * KS);
+    L.ee = take(Cg * KS);
     L.dO = take(Cg * DVT);
     L.dM = take(Cg * DVT);
     L.Z = take(Cg * DVT);
@@ -79,6 +84,7 @@ __global__ void __launch_bounds__(kRevThreads) bwd_dstate_kernel(BwdArgs a, int 
     const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
     const int64_t T = f.T, H = f.H;
     const RevLayout L = rev_layout(Cg, DVT, dk);
+    const int KS = row_stride(dk);
     float *Kf = lds + L.kf, *Qf = lds + L.qf, *G = lds + L.g, *Ee = lds + L.ee;
     float *dO = lds + L.dO, *dM = lds + L.dM, *Z = lds + L.Z;
     float *A = lds + L.A, *R = lds + L.R, *Tm = lds + L.Tm, *dS = lds + L.dS, *gC = lds + L.gC;
@@ -113,10 +119,11 @@ __global__ void __launch_bounds__(kRevThreads) bwd_dstate_kernel(BwdArgs a, int 
                 la = load_gate(f.la, f.la_key, row, dk, c);
                 e = load_gate(f.eb, f.eb_key, row, dk, c) * kv;
             }
-            Kf[idx] = kv;
-            Qf[idx] = qv;
-            G[idx] = la;
-            Ee[idx] = e;
+            const int li = r * KS + c;
+            Kf[li] = kv;
+            Qf[li] = qv;
+            G[li] = la;
+            Ee[li] = e;
         }
         for (int idx = tid; idx < Cg * DVT; idx += kRevThreads) {
             const int r = idx / DVT, j = idx % DVT;
@@ -127,8 +134,8 @@ __global__ void __launch_bounds__(kRevThreads) bwd_dstate_kernel(BwdArgs a, int 
         for (int c = tid; c < dk; c += kRevThreads) {
             float acc = 0.f;
             for (int r = 0; r < Cg; ++r) {
-                acc += G[r * dk + c];
-                G[r * dk + c] = acc;
+                acc += G[r * KS + c];
+                G[r * KS + c] = acc;
             }
             gC[c] = acc;
         }
@@ -139,10 +146,10 @@ __global__ void __launch_bounds__(kRevThreads) bwd_dstate_kernel(BwdArgs a, int 
             float sa = 0.f, sr = 0.f;
             if (s <= r) {
                 for (int c = 0; c < dk; ++c) {
-                    const float d = expf(G[r * dk + c] - G[s * dk + c]);
-                    const float e = Ee[s * dk + c];
-                    sa += Kf[r * dk + c] * d * e;
-                    sr += Qf[r * dk + c] * d * e;
+                    const float d = expf(G[r * KS + c] - G[s * KS + c]);
+                    const float e = Ee[s * KS + c];
+                    sa += Kf[r * KS + c] * d * e;
+                    sr += Qf[r * KS + c] * d * e;
                 }
             }
             A[idx] = s < r ? sa : 0.f;
@@ -163,17 +170,18 @@ __global__ void __launch_bounds__(kRevThreads) bwd_dstate_kernel(BwdArgs a, int 
         }
         for (int idx = tid; idx < Cg * dk; idx += kRevThreads) {
             const int c = idx % dk;
-            const float eg = expf(G[idx]);
-            Kf[idx] *= eg;                        // Kbar
-            Qf[idx] *= eg;                        // Qbar
-            Ee[idx] *= expf(gC[c] - G[idx]);      // Etil
+            const int li = (idx / dk) * KS + c;
+            const float eg = expf(G[li]);
+            Kf[li] *= eg;                        // Kbar
+            Qf[li] *= eg;                        // Qbar
+            Ee[li] *= expf(gC[c] - G[li]);       // Etil
         }
         __syncthreads();
         // dM = -Etil dSo - R^T dO
         for (int idx = tid; idx < Cg * DVT; idx += kRevThreads) {
             const int r = idx / DVT, j = idx % DVT;
             float acc = 0.f;
-            for (int c = 0; c < dk; ++c) acc += Ee[r * dk + c] * dS[c * DVT + j];
+            for (int c = 0; c < dk; ++c) acc += Ee[r * KS + c] * dS[c * DVT + j];
             for (int s = r; s < Cg; ++s) acc += R[s * Cg + r] * dO[s * DVT + j];
             dM[idx] = -acc;
         }
@@ -190,7 +198,7 @@ __global__ void __launch_bounds__(kRevThreads) bwd_dstate_kernel(BwdArgs a, int 
         for (int idx = tid; idx < dk * DVT; idx += kRevThreads) {
             const int c = idx / DVT, j = idx % DVT;
             float acc = expf(gC[c]) * dS[idx];
-            for (int r = 0; r < Cg; ++r) acc += Qf[r * dk + c] * dO[r * DVT + j] + Kf[r * dk + c] * Z[r * DVT + j];
+            for (int r = 0; r < Cg; ++r) acc += Qf[r * KS + c] * dO[r * DVT + j] + Kf[r * KS + c] * Z[r * DVT + j];
             dS[idx] = acc;
         }
     }
@@ -218,11 +226,12 @@ __host__ __device__ inline GradLayout grad_layout(int Cg, int dk, int dv) {
     GradLayout L;
     int off = 0;
     auto take = [&](int n) { int o = off; off += n; return o; };
-    L.K = take(Cg * dk); L.Q = take(Cg * dk); L.G = take(Cg * dk); L.E = take(Cg * dk);
-    L.U = take(Cg * dk); L.EG = take(Cg * dk); L.EC = take(Cg * dk); L.W = take(Cg * dk);
-    L.dW = take(Cg * dk); L.dQ = take(Cg * dk); L.dE = take(Cg * dk); L.dU = take(Cg * dk);
-    L.V = take(Cg * dv); L.dO = take(Cg * dv); L.BV = take(Cg * dv); L.M = take(Cg * dv);
-    L.dM = take(Cg * dv); L.Y = take(Cg * dv);
+    const int KS = row_stride(dk), VS = row_stride(dv);
+    L.K = take(Cg * KS); L.Q = take(Cg * KS); L.G = take(Cg * KS); L.E = take(Cg * KS);
+    L.U = take(Cg * KS); L.EG = take(Cg * KS); L.EC = take(Cg * KS); L.W = take(Cg * KS);
+    L.dW = take(Cg * KS); L.dQ = take(Cg * KS); L.dE = take(Cg * KS); L.dU = take(Cg * KS);
+    L.V = take(Cg * VS); L.dO = take(Cg * VS); L.BV = take(Cg * VS); L.M = take(Cg * VS);
+    L.dM = take(Cg * VS); L.Y = take(Cg * VS);
     L.A = take(Cg * Cg); L.Bm = take(Cg * Cg); L.R = take(Cg * Cg); L.P = take(Cg * Cg);
     L.Tm = take(Cg * Cg); L.dT = take(Cg * Cg); L.X1 = take(Cg * Cg); L.dA = take(Cg * Cg);
     L.dBm = take(Cg * Cg); L.dR = take(Cg * Cg); L.dP = take(Cg * Cg);
@@ -238,6 +247,7 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
     const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
     const int64_t T = f.T, H = f.H;
     const GradLayout L = grad_layout(Cg, dk, dv);
+    const int KS = row_stride(dk), VS = row_stride(dv);
     float *K = lds + L.K, *Q = lds + L.Q, *G = lds + L.G, *E = lds + L.E, *U = lds + L.U;
     float *EG = lds + L.EG, *EC = lds + L.EC, *W = lds + L.W, *dW = lds + L.dW, *dQ = lds + L.dQ;
     float *dE = lds + L.dE, *dU = lds + L.dU;
@@ -269,27 +279,28 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
             e = bb * kv;
             u = ww * kv;
         }
-        K[idx] = kv; Q[idx] = qv; G[idx] = la; E[idx] = e; U[idx] = u;
+        const int li = r * KS + c;
+        K[li] = kv; Q[li] = qv; G[li] = la; E[li] = e; U[li] = u;
     }
     for (int idx = tid; idx < Cg * dv; idx += kGradThreads) {
         const int r = idx / dv, j = idx % dv;
         const bool ok = live(r);
-        V[idx] = ok ? load_qkv(f.v, row_of(r) * dv + j, f.bf16) : 0.f;
-        dO[idx] = ok ? a.d_o[row_of(r) * dv + j] : 0.f;
+        V[r * VS + j] = ok ? load_qkv(f.v, row_of(r) * dv + j, f.bf16) : 0.f;
+        dO[r * VS + j] = ok ? a.d_o[row_of(r) * dv + j] : 0.f;
     }
     __syncthreads();
     // P1: running log-decay, e^g and e^(gC - g)
     for (int c = tid; c < dk; c += kGradThreads) {
         float acc = 0.f;
         for (int r = 0; r < Cg; ++r) {
-            acc += G[r * dk + c];
-            G[r * dk + c] = acc;
+            acc += G[r * KS + c];
+            G[r * KS + c] = acc;
         }
         gC[c] = acc;
         dgC[c] = 0.f;
         for (int r = 0; r < Cg; ++r) {
-            EG[r * dk + c] = expf(G[r * dk + c]);
-            EC[r * dk + c] = expf(acc - G[r * dk + c]);
+            EG[r * KS + c] = expf(G[r * KS + c]);
+            EC[r * KS + c] = expf(acc - G[r * KS + c]);
         }
     }
     __syncthreads();
@@ -299,9 +310,9 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
         float sa = 0.f, sb = 0.f, sr = 0.f, sp = 0.f;
         if (s <= r) {
             for (int c = 0; c < dk; ++c) {
-                const float d = expf(G[r * dk + c] - G[s * dk + c]);
-                const float kd = K[r * dk + c] * d, qd = Q[r * dk + c] * d;
-                const float e = E[s * dk + c], u = U[s * dk + c];
+                const float d = expf(G[r * KS + c] - G[s * KS + c]);
+                const float kd = K[r * KS + c] * d, qd = Q[r * KS + c] * d;
+                const float e = E[s * KS + c], u = U[s * KS + c];
                 sa += kd * e; sb += kd * u; sr += qd * e; sp += qd * u;
             }
         }
@@ -329,14 +340,14 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
     for (int idx = tid; idx < Cg * dk; idx += kGradThreads) {
         const int r = idx / dk, c = idx % dk;
         float acc = 0.f;
-        for (int s = 0; s <= r; ++s) acc += Tm[r * Cg + s] * K[s * dk + c] * EG[s * dk + c];
-        W[idx] = acc;
+        for (int s = 0; s <= r; ++s) acc += Tm[r * Cg + s] * K[s * KS + c] * EG[s * KS + c];
+        W[r * KS + c] = acc;
     }
     for (int idx = tid; idx < Cg * dv; idx += kGradThreads) {
         const int r = idx / dv, j = idx % dv;
         float acc = 0.f;
-        for (int s = 0; s < r; ++s) acc += Bm[r * Cg + s] * V[s * dv + j];
-        BV[idx] = acc;
+        for (int s = 0; s < r; ++s) acc += Bm[r * Cg + s] * V[s * VS + j];
+        BV[r * VS + j] = acc;
     }
     __syncthreads();
     // P5: M = W S + Tm BV and dM = -Etil dSo - R^T dO; work item = one value
@@ -351,18 +362,18 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
                 const int r = r0 + i;
-                am[i] += W[r * dk + c] * sv;
-                ad[i] += E[r * dk + c] * EC[r * dk + c] * dsv;
+                am[i] += W[r * KS + c] * sv;
+                ad[i] += E[r * KS + c] * EC[r * KS + c] * dsv;
             }
         }
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
             const int r = r0 + i;
             float mu = am[i], dm = ad[i];
-            for (int s = 0; s <= r; ++s) mu += Tm[r * Cg + s] * BV[s * dv + j];
-            for (int s = r; s < Cg; ++s) dm += R[s * Cg + r] * dO[s * dv + j];
-            M[r * dv + j] = mu;
-            dM[r * dv + j] = -dm;
+            for (int s = 0; s <= r; ++s) mu += Tm[r * Cg + s] * BV[s * VS + j];
+            for (int s = r; s < Cg; ++s) dm += R[s * Cg + r] * dO[s * VS + j];
+            M[r * VS + j] = mu;
+            dM[r * VS + j] = -dm;
         }
     }
     __syncthreads();
@@ -370,8 +381,8 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
     for (int idx = tid; idx < Cg * dv; idx += kGradThreads) {
         const int s = idx / dv, j = idx % dv;
         float acc = 0.f;
-        for (int r = s; r < Cg; ++r) acc += Tm[r * Cg + s] * dM[r * dv + j];
-        Y[idx] = acc;
+        for (int r = s; r < Cg; ++r) acc += Tm[r * Cg + s] * dM[r * VS + j];
+        Y[s * VS + j] = acc;
     }
     for (int c = tid; c < dk; c += kGradThreads) {
         float acc = 0.f;
@@ -388,14 +399,14 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
         for (int c = 0; c < dk; ++c) {
             const float dsv = dSg[static_cast<int64_t>(c) * dv + j];
 #pragma unroll
-            for (int i = 0; i < RB; ++i) acc[i] += U[(s0 + i) * dk + c] * EC[(s0 + i) * dk + c] * dsv;
+            for (int i = 0; i < RB; ++i) acc[i] += U[(s0 + i) * KS + c] * EC[(s0 + i) * KS + c] * dsv;
         }
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
             const int s = s0 + i;
             float x = acc[i];
-            for (int r = s; r < Cg; ++r) x += P[r * Cg + s] * dO[r * dv + j];
-            for (int r = s + 1; r < Cg; ++r) x += Bm[r * Cg + s] * Y[r * dv + j];
+            for (int r = s; r < Cg; ++r) x += P[r * Cg + s] * dO[r * VS + j];
+            for (int r = s + 1; r < Cg; ++r) x += Bm[r * Cg + s] * Y[r * VS + j];
             if (live(s)) a.dv[row_of(s) * dv + j] = x;
         }
     }
@@ -409,19 +420,19 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
                 const int r = r0 + i;
-                aw[i] += dM[r * dv + j] * sv;
-                aq[i] += dO[r * dv + j] * sv;
-                ae[i] -= M[r * dv + j] * dsv;
-                au[i] += V[r * dv + j] * dsv;
+                aw[i] += dM[r * VS + j] * sv;
+                aq[i] += dO[r * VS + j] * sv;
+                ae[i] -= M[r * VS + j] * dsv;
+                au[i] += V[r * VS + j] * dsv;
             }
         }
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
             const int r = r0 + i;
-            dW[r * dk + c] = aw[i];
-            dQ[r * dk + c] = aq[i];
-            dE[r * dk + c] = ae[i];
-            dU[r * dk + c] = au[i];
+            dW[r * KS + c] = aw[i];
+            dQ[r * KS + c] = aq[i];
+            dE[r * KS + c] = ae[i];
+            dU[r * KS + c] = au[i];
         }
     }
     for (int idx = tid; idx < Cg * Cg; idx += kGradThreads) {
@@ -429,9 +440,9 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
         float xb = 0.f, xr = 0.f, xp = 0.f;
         if (s <= r) {
             for (int j = 0; j < dv; ++j) {
-                const float o = dO[r * dv + j], vs = V[s * dv + j];
-                xb += Y[r * dv + j] * vs;
-                xr -= o * M[s * dv + j];
+                const float o = dO[r * VS + j], vs = V[s * VS + j];
+                xb += Y[r * VS + j] * vs;
+                xr -= o * M[s * VS + j];
                 xp += o * vs;
             }
         }
@@ -445,16 +456,16 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
         const int r = idx / Cg, s = idx % Cg;
         float acc = 0.f;
         if (s <= r) {
-            for (int c = 0; c < dk; ++c) acc += dW[r * dk + c] * K[s * dk + c] * EG[s * dk + c];
-            for (int j = 0; j < dv; ++j) acc += dM[r * dv + j] * BV[s * dv + j];
+            for (int c = 0; c < dk; ++c) acc += dW[r * KS + c] * K[s * KS + c] * EG[s * KS + c];
+            for (int j = 0; j < dv; ++j) acc += dM[r * VS + j] * BV[s * VS + j];
         }
         dT[idx] = acc;
     }
     for (int idx = tid; idx < Cg * dk; idx += kGradThreads) {
         const int s = idx / dk, c = idx % dk;
         float acc = 0.f;
-        for (int r = s; r < Cg; ++r) acc += Tm[r * Cg + s] * dW[r * dk + c];
-        W[idx] = acc;
+        for (int r = s; r < Cg; ++r) acc += Tm[r * Cg + s] * dW[r * KS + c];
+        W[s * KS + c] = acc;
     }
     __syncthreads();
     // P9: dA = -(Tm^T dTm) Tm^T, strictly below the diagonal
@@ -477,26 +488,26 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
     // column, the decayed operands', then k, q and the gates
     const bool la_key = f.la_key, eb_key = f.eb_key, wr_key = f.wr_key, tied = f.wr == nullptr;
     for (int idx = tid; idx < Cg * dk; idx += kGradThreads) {
-        const int x = idx / dk, c = idx % dk;
-        const float gx = G[idx];
+        const int x = idx / dk, c = idx % dk, li = x * KS + c;
+        const float gx = G[li];
         float glk = 0.f, glq = 0.f, gre = 0.f, gru = 0.f;
         for (int y = 0; y < x; ++y) {  // x as the row of a Gram
-            const float d = expf(gx - G[y * dk + c]);
-            const float ey = E[y * dk + c], uy = U[y * dk + c];
+            const float d = expf(gx - G[y * KS + c]);
+            const float ey = E[y * KS + c], uy = U[y * KS + c];
             glk += (dA[x * Cg + y] * ey + dBm[x * Cg + y] * uy) * d;
             glq += (dR[x * Cg + y] * ey + dP[x * Cg + y] * uy) * d;
         }
-        glq += dR[x * Cg + x] * E[idx] + dP[x * Cg + x] * U[idx];
-        gre += dR[x * Cg + x] * Q[idx];
-        gru += dP[x * Cg + x] * Q[idx];
+        glq += dR[x * Cg + x] * E[li] + dP[x * Cg + x] * U[li];
+        gre += dR[x * Cg + x] * Q[li];
+        gru += dP[x * Cg + x] * Q[li];
         for (int y = x + 1; y < Cg; ++y) {  // x as the column
-            const float d = expf(G[y * dk + c] - gx);
-            const float ky = K[y * dk + c], qy = Q[y * dk + c];
+            const float d = expf(G[y * KS + c] - gx);
+            const float ky = K[y * KS + c], qy = Q[y * KS + c];
             gre += (dA[y * Cg + x] * ky + dR[y * Cg + x] * qy) * d;
             gru += (dBm[y * Cg + x] * ky + dP[y * Cg + x] * qy) * d;
         }
-        const float kx = K[idx], qx = Q[idx], ex = E[idx], ux = U[idx], eg = EG[idx], ec = EC[idx];
-        const float dkb = W[idx], dqb = dQ[idx], det = dE[idx], dut = dU[idx];
+        const float kx = K[li], qx = Q[li], ex = E[li], ux = U[li], eg = EG[li], ec = EC[li];
+        const float dkb = W[li], dqb = dQ[li], det = dE[li], dut = dU[li];
         const float de = gre + det * ec, du = gru + dut * ec;
         const float dg = kx * glk + qx * glq - ex * gre - ux * gru + (dkb * kx + dqb * qx) * eg -
                          (det * ex + dut * ux) * ec;
@@ -521,22 +532,22 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
         } else {
             dbv = 0.f;
         }
-        dE[idx] = (det * ex + dut * ux) * ec;  // this token's share of d gC
-        dQ[idx] = dg;
-        dU[idx] = dbv;
-        dW[idx] = dwv;
+        dE[li] = (det * ex + dut * ux) * ec;  // this token's share of d gC
+        dQ[li] = dg;
+        dU[li] = dbv;
+        dW[li] = dwv;
     }
     __syncthreads();
     // P11: d log a = reverse running sum of dg, d gC entering at the last row
     for (int c = tid; c < dk; c += kGradThreads) {
         float run = dgC[c];
-        for (int x = 0; x < Cg; ++x) run += dE[x * dk + c];
+        for (int x = 0; x < Cg; ++x) run += dE[x * KS + c];
         for (int x = Cg - 1; x >= 0; --x) {
-            run += dQ[x * dk + c];
+            run += dQ[x * KS + c];
             if (la_key) {
                 if (live(x)) a.dla[row_of(x) * dk + c] = run;
             } else {
-                dQ[x * dk + c] = run;
+                dQ[x * KS + c] = run;
             }
         }
     }
@@ -546,9 +557,9 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
         const int x = tid;
         float sl = 0.f, sb = 0.f, sw = 0.f;
         for (int c = 0; c < dk; ++c) {
-            sl += dQ[x * dk + c];
-            sb += dU[x * dk + c];
-            sw += dW[x * dk + c];
+            sl += dQ[x * KS + c];
+            sb += dU[x * KS + c];
+            sw += dW[x * KS + c];
         }
         const int64_t row = row_of(x);
         if (!la_key) a.dla[row] = sl;

@@ -36,15 +36,20 @@ struct GenLayout {
     int kf, qf, g, eb, uw, vv, xx, mm, A, Bm, R, P, Tm, S, gC, total;
 };
 
+// Row stride of the Cg x dk arrays: odd, so that lanes reading one channel
+// of different rows (the Gram loops) hit different LDS banks.
+__host__ __device__ inline int row_stride(int dk) { return dk | 1; }
+
 __host__ __device__ inline GenLayout gen_layout(int Cg, int DVT, int dk) {
     GenLayout L;
     int off = 0;
+    const int KS = row_stride(dk);
     auto take = [&](int n) { int o = off; off += n; return o; };
-    L.kf = take(Cg * dk);
-    L.qf = take(Cg * dk);
-    L.g = take(Cg * dk);
-    L.eb = take(Cg * dk);
-    L.uw = take(Cg * dk);
+    L.kf = take(Cg * KS);
+    L.qf = take(Cg * KS);
+    L.g = take(Cg * KS);
+    L.eb = take(Cg * KS);
+    L.uw = take(Cg * KS);
     L.vv = take(Cg * DVT);
     L.xx = take(Cg * DVT);
     L.mm = take(Cg * DVT);
@@ -64,6 +69,7 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
     const int dk = static_cast<int>(a.dk), dv = static_cast<int>(a.dv);
     const int64_t T = a.T, H = a.H;
     const GenLayout L = gen_layout(Cg, DVT, dk);
+    const int KS = row_stride(dk);
     float *Kf = lds + L.kf, *Qf = lds + L.qf, *G = lds + L.g, *Eb = lds + L.eb, *Uw = lds + L.uw;
     float *V = lds + L.vv, *X = lds + L.xx, *M = lds + L.mm;
     float *A = lds + L.A, *Bm = lds + L.Bm, *R = lds + L.R, *P = lds + L.P, *Tm = lds + L.Tm;
@@ -106,11 +112,12 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
                 e = bb * kv;
                 u = ww * kv;
             }
-            Kf[idx] = kv;
-            Qf[idx] = qv;
-            G[idx] = la;
-            Eb[idx] = e;
-            Uw[idx] = u;
+            const int li = r * KS + c;
+            Kf[li] = kv;
+            Qf[li] = qv;
+            G[li] = la;
+            Eb[li] = e;
+            Uw[li] = u;
         }
         for (int idx = tid; idx < Cg * DVT; idx += kThreads) {
             const int r = idx / DVT, j = idx % DVT;
@@ -124,8 +131,8 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
         for (int c = tid; c < dk; c += kThreads) {
             float acc = 0.f;
             for (int r = 0; r < Cg; ++r) {
-                acc += G[r * dk + c];
-                G[r * dk + c] = acc;
+                acc += G[r * KS + c];
+                G[r * KS + c] = acc;
             }
             gC[c] = acc;
         }
@@ -136,9 +143,9 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
             float sa = 0.f, sb = 0.f, sr = 0.f, sp = 0.f;
             if (s <= r) {
                 for (int c = 0; c < dk; ++c) {
-                    const float d = expf(G[r * dk + c] - G[s * dk + c]);
-                    const float kd = Kf[r * dk + c] * d, qd = Qf[r * dk + c] * d;
-                    const float e = Eb[s * dk + c], u = Uw[s * dk + c];
+                    const float d = expf(G[r * KS + c] - G[s * KS + c]);
+                    const float kd = Kf[r * KS + c] * d, qd = Qf[r * KS + c] * d;
+                    const float e = Eb[s * KS + c], u = Uw[s * KS + c];
                     sa += kd * e;
                     sb += kd * u;
                     sr += qd * e;
@@ -170,20 +177,20 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
             }
         }
         for (int idx = tid; idx < Cg * dk; idx += kThreads) {
-            const int c = idx % dk;
-            const float eg = expf(G[idx]);
-            const float ec = expf(gC[c] - G[idx]);
-            Kf[idx] *= eg;  // Kbar
-            Qf[idx] *= eg;  // Qbar
-            Eb[idx] *= ec;  // Etil
-            Uw[idx] *= ec;  // Util
+            const int c = idx % dk, li = (idx / dk) * KS + c;
+            const float eg = expf(G[li]);
+            const float ec = expf(gC[c] - G[li]);
+            Kf[li] *= eg;  // Kbar
+            Qf[li] *= eg;  // Qbar
+            Eb[li] *= ec;  // Etil
+            Uw[li] *= ec;  // Util
         }
         __syncthreads();
         // 5. X = Kbar S + Bm V
         for (int idx = tid; idx < Cg * DVT; idx += kThreads) {
             const int r = idx / DVT, j = idx % DVT;
             float acc = 0.f;
-            for (int c = 0; c < dk; ++c) acc += Kf[r * dk + c] * S[c * DVT + j];
+            for (int c = 0; c < dk; ++c) acc += Kf[r * KS + c] * S[c * DVT + j];
             for (int s = 0; s < r; ++s) acc += Bm[r * Cg + s] * V[s * DVT + j];
             X[idx] = acc;
         }
@@ -202,7 +209,7 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
             const int64_t t = t0 + r;
             if (t >= T || j >= ncol) continue;
             float acc = 0.f;
-            for (int c = 0; c < dk; ++c) acc += Qf[r * dk + c] * S[c * DVT + j];
+            for (int c = 0; c < dk; ++c) acc += Qf[r * KS + c] * S[c * DVT + j];
             for (int s = 0; s <= r; ++s) acc += P[r * Cg + s] * V[s * DVT + j] - R[r * Cg + s] * M[s * DVT + j];
             a.o[((b * T + t) * H + h) * dv + col0 + j] = acc;
         }
@@ -211,7 +218,7 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
         for (int idx = tid; idx < dk * DVT; idx += kThreads) {
             const int c = idx / DVT, j = idx % DVT;
             float acc = expf(gC[c]) * S[idx];
-            for (int s = 0; s < Cg; ++s) acc += Uw[s * dk + c] * V[s * DVT + j] - Eb[s * dk + c] * M[s * DVT + j];
+            for (int s = 0; s < Cg; ++s) acc += Uw[s * KS + c] * V[s * DVT + j] - Eb[s * KS + c] * M[s * DVT + j];
             S[idx] = acc;
         }
     }

@@ -31,10 +31,18 @@
  * tied scalar beta gives KDA; a = 1 gives the plain delta rule (gist.science
  * summary, "Technische Samenvatting", section 1).
  *
+ * value_write_form != 0 selects the update as the gist.science summary
+ * writes it ("Methodologie", 1. "Gated Delta-regel-2"): the write gate has
+ * one factor per VALUE channel and the erase gate weights the read,
+ *         m_t = Sbar^T (b_t .* k_t),   S_t = Sbar - k_t m_t^T + k_t (w_t .* v_t)^T
+ * i.e. S_t = (I - k_t (b_t .* k_t)^T) Sbar + k_t (w_t .* v_t)^T; the write
+ * gate is then [B, T, H, dv] (per channel) or [B, T, H], and must be given.
+ *
  * Layouts (all row-major, contiguous, fp64):
  *   q, k        [B, T, H, dk]
  *   v, o        [B, T, H, dv]
  *   gates       [B, T, H, dk] when *_per_key != 0, else [B, T, H]
+ *               (the write gate of the value-write form: [B, T, H, dv])
  *   S0, S_T     [B, H, dk, dv]   (S0 may be NULL: zero initial state;
  *                                  S_T may be NULL: not written)
  *   w           may be NULL: tied to b.
@@ -57,10 +65,11 @@ int gdn2_oracle_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                     const double *erase, int erase_per_key,
                     const double *write, int write_per_key,
                     const double *S0, double q_scale,
-                    double *o, double *S_T, int nthreads)
+                    double *o, double *S_T, int value_write_form, int nthreads)
 {
     if (B < 0 || T < 0 || H < 1 || dk < 1 || dv < 1) return -1;
     if (B * T > 0 && (!q || !k || !v || !log_decay || !erase || !o)) return -1;
+    if (value_write_form && B * T > 0 && !write) return -1;
     if (nthreads < 1) nthreads = 1;
     int bad = 0;
 
@@ -98,6 +107,21 @@ int gdn2_oracle_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
             for (int64_t j = 0; j < dv; ++j) m[j] = 0.0;
             for (int64_t i = 0; i < dk; ++i)
                 for (int64_t j = 0; j < dv; ++j) m[j] += S[i * dv + j] * kt[i];
+            if (value_write_form) {
+                /* 2'. read along the erase-weighted key instead: m = Sbar^T (b .* k) */
+                for (int64_t j = 0; j < dv; ++j) m[j] = 0.0;
+                for (int64_t i = 0; i < dk; ++i) {
+                    const double bi = erase_per_key ? erase[row * dk + i] : erase[row];
+                    for (int64_t j = 0; j < dv; ++j) m[j] += S[i * dv + j] * bi * kt[i];
+                }
+                /* 3'. erase k m^T, write k (w .* v)^T */
+                for (int64_t i = 0; i < dk; ++i)
+                    for (int64_t j = 0; j < dv; ++j) {
+                        const double wj = write_per_key ? write[row * dv + j] : write[row];
+                        S[i * dv + j] = S[i * dv + j] - kt[i] * m[j] + kt[i] * wj * vt[j];
+                    }
+                goto query_read;
+            }
             /* 3. erase (b .* k) m^T, write (w .* k) v^T */
             for (int64_t i = 0; i < dk; ++i) {
                 const double bi = erase_per_key ? erase[row * dk + i] : erase[row];
@@ -111,6 +135,7 @@ int gdn2_oracle_fwd(int64_t B, int64_t T, int64_t H, int64_t dk, int64_t dv,
                 for (int64_t j = 0; j < dv; ++j)
                     S[i * dv + j] = S[i * dv + j] - ei * m[j] + ui * vt[j];
             }
+        query_read:;
             /* 4. read the updated state with the query */
             for (int64_t j = 0; j < dv; ++j) ot[j] = 0.0;
             for (int64_t i = 0; i < dk; ++i) {

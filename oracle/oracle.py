@@ -58,7 +58,7 @@ def _load():
                 dp, ctypes.c_int,
                 dp, ctypes.c_int,
                 dp, ctypes.c_double,
-                dp, dp, ctypes.c_int,
+                dp, dp, ctypes.c_int, ctypes.c_int,
             ]
             lib.gdn2_oracle_max_threads.restype = ctypes.c_int
             lib.gdn2_oracle_max_threads.argtypes = []
@@ -86,12 +86,14 @@ def _ptr(x):
 
 
 def gdn2_forward(q, k, v, log_decay, erase, write=None, S0=None, q_scale=1.0,
-                 threads: int | None = None):
+                 threads: int | None = None, value_write=False):
     """Run the recurrence token by token in fp64.
 
     Shapes: q, k [B,T,H,dk]; v [B,T,H,dv]; each gate either [B,T,H,dk]
     (one value per key channel) or [B,T,H] (one per token-head); S0
     [B,H,dk,dv] or None (zeros); write None ties it to erase.
+    ``value_write``: the gist.science form (write gate per value channel,
+    [B,T,H,dv] or [B,T,H], required; the erase gate weights the read).
     Returns (o [B,T,H,dv], S_T [B,H,dk,dv]) as float64 arrays.
     """
     q, k, v = _f64(q), _f64(k), _f64(v)
@@ -100,15 +102,17 @@ def gdn2_forward(q, k, v, log_decay, erase, write=None, S0=None, q_scale=1.0,
     assert q.shape == k.shape and v.shape[:3] == (B, T, H)
     la, b, w, s0 = _f64(log_decay), _f64(erase), _f64(write), _f64(S0)
 
-    def kind(g):
-        if g.shape == (B, T, H, dk):
+    def kind(g, d=dk):
+        if g.shape == (B, T, H, d):
             return 1
         if g.shape == (B, T, H):
             return 0
-        raise ValueError(f"gate shape {g.shape} is neither [B,T,H,dk] nor [B,T,H]")
+        raise ValueError(f"gate shape {g.shape} is neither [B,T,H,{d}] nor [B,T,H]")
 
     la_k, b_k = kind(la), kind(b)
-    w_k = kind(w) if w is not None else 0
+    if value_write and w is None:
+        raise ValueError("the value-write form needs a write gate")
+    w_k = kind(w, dv if value_write else dk) if w is not None else 0
     if s0 is not None:
         assert s0.shape == (B, H, dk, dv)
     o = np.zeros((B, T, H, dv), dtype=np.float64)
@@ -117,7 +121,7 @@ def gdn2_forward(q, k, v, log_decay, erase, write=None, S0=None, q_scale=1.0,
     rc = _load().gdn2_oracle_fwd(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(la), la_k, _ptr(b), b_k, _ptr(w), w_k,
                                  _ptr(s0), float(q_scale), _ptr(o), _ptr(S_T),
-                                 int(nthreads))
+                                 1 if value_write else 0, int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle failed with code {rc}")
     return o, S_T

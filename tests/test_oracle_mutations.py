@@ -53,6 +53,10 @@ MUTANTS = {
     "output_read_before_update": [(OUT_BLOCK, ""), (ERASE_START, OUT_BLOCK + ERASE_START)],
     "decay_after_write": [(DECAY_BLOCK + READ_BLOCK, READ_BLOCK),
                           (OUT_START, DECAY_BLOCK + OUT_START)],
+    # the value-write form (gist.science summary's equation)
+    "value_write_read_not_gated": [("m[j] += S[i * dv + j] * bi * kt[i];", "m[j] += S[i * dv + j] * kt[i];")],
+    "value_write_gate_on_key": [("const double wj = write_per_key ? write[row * dv + j] : write[row];",
+                                 "const double wj = write_per_key ? write[row * dv + (i % dv)] : write[row];")],
 }
 
 
@@ -71,11 +75,11 @@ def _build(tmp, name, edits):
     L.gdn2_oracle_fwd.restype = ctypes.c_int
     L.gdn2_oracle_fwd.argtypes = [i64, i64, i64, i64, i64, dp, dp, dp, dp, ctypes.c_int,
                                   dp, ctypes.c_int, dp, ctypes.c_int, dp, ctypes.c_double,
-                                  dp, dp, ctypes.c_int]
+                                  dp, dp, ctypes.c_int, ctypes.c_int]
     return L
 
 
-def _run(L, q, k, v, la, b, w, S0):
+def _run(L, q, k, v, la, b, w, S0, form=0):
     arrs = [np.ascontiguousarray(x, dtype=np.float64) if x is not None else None
             for x in (q, k, v, la, b, w, S0)]
     q, k, v, la, b, w, S0 = arrs
@@ -86,7 +90,7 @@ def _run(L, q, k, v, la, b, w, S0):
     p = lambda x: None if x is None else x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
     kind = lambda g: 1 if g.ndim == 4 else 0
     rc = L.gdn2_oracle_fwd(B, T, H, dk, dv, p(q), p(k), p(v), p(la), kind(la), p(b), kind(b),
-                           p(w), 0 if w is None else kind(w), p(S0), 1.0, p(o), p(S), 1)
+                           p(w), 0 if w is None else kind(w), p(S0), 1.0, p(o), p(S), form, 1)
     assert rc == 0
     return o, S
 
@@ -125,6 +129,12 @@ def _pins_pass(L):
     o, S = _run(L, kk, kk, v, la, np.ones((1, T, 1, dk)), w, r.normal(size=(1, 1, dk, dv)))
     gain = np.sum(w * kk ** 2, axis=-1)
     ok.append(np.allclose(o, gain[..., None] * v, atol=1e-11))
+    # the value-write form, worked by hand (tests/test_oracle_value_write.py)
+    o, S = _run(L, np.array([1.0, 0]).reshape(1, 1, 1, 2), np.array([0.6, 0.8]).reshape(1, 1, 1, 2),
+                np.array([9.0, 9]).reshape(1, 1, 1, 2), np.full((1, 1, 1), math.log(0.8)),
+                np.array([0.5, 1.0]).reshape(1, 1, 1, 2), np.array([1.0, 0.5]).reshape(1, 1, 1, 2),
+                np.array([[2.0, 3], [5, 1]]).reshape(1, 1, 2, 2), form=1)
+    ok.append(np.allclose(S[0, 0], [[4.792, 4.284], [8.256, 3.312]], atol=1e-12))
     return all(ok)
 
 

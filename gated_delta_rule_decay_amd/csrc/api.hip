@@ -49,6 +49,8 @@ gdn2_status check_common(const gdn2_desc *d) {
     if (!kind_ok(d->decay_kind) || !kind_ok(d->erase_kind) ||
         (!d->tie_write_to_erase && !kind_ok(d->write_kind)))
         return GDN2_ERR_SHAPE;
+    if (d->form != GDN2_FORM_KEY && d->form != GDN2_FORM_VALUE_WRITE) return GDN2_ERR_SHAPE;
+    if (d->form == GDN2_FORM_VALUE_WRITE && d->tie_write_to_erase) return GDN2_ERR_SHAPE;
     if (d->dk > 128 || d->dv > 128) return GDN2_ERR_UNSUPPORTED;
     // every tensor's byte size must fit in int64
     int64_t x;
@@ -77,7 +79,8 @@ Sizes sizes_of(const gdn2_desc *d, int64_t T) {
     s.v = s.tok * d->dv * esz;
     s.la = s.tok * (d->decay_kind == GDN2_GATE_KEY ? d->dk : 1) * 4;
     s.eb = s.tok * (d->erase_kind == GDN2_GATE_KEY ? d->dk : 1) * 4;
-    s.wr = d->tie_write_to_erase ? 0 : s.tok * (d->write_kind == GDN2_GATE_KEY ? d->dk : 1) * 4;
+    const int64_t wch = d->form == GDN2_FORM_VALUE_WRITE ? d->dv : d->dk;  // channels of the write gate
+    s.wr = d->tie_write_to_erase ? 0 : s.tok * (d->write_kind == GDN2_GATE_KEY ? wch : 1) * 4;
     s.o = s.tok * d->dv * 4;
     s.st = d->batch * d->heads * d->dk * d->dv * 4;
     return s;
@@ -100,6 +103,7 @@ ChunkArgs args_of(const gdn2_desc *d, const void *q, const void *k, const void *
     a.eb_key = d->erase_kind == GDN2_GATE_KEY;
     a.wr_key = d->tie_write_to_erase ? a.eb_key : d->write_kind == GDN2_GATE_KEY;
     a.q_scale = d->q_scale;
+    a.value_write = d->form == GDN2_FORM_VALUE_WRITE;
     return a;
 }
 
@@ -195,6 +199,7 @@ gdn2_status gdn2_chunk_bwd_workspace(const gdn2_desc *desc, size_t *bytes) {
     if (st != GDN2_OK) return st;
     if (desc->chunk != 16 && desc->chunk != 32 && desc->chunk != 64) return GDN2_ERR_UNSUPPORTED;
     if (!gdn2::chunk_bwd_chunk(desc->dk, desc->dv, static_cast<int>(desc->chunk))) return GDN2_ERR_UNSUPPORTED;
+    if (desc->form != GDN2_FORM_KEY) return GDN2_ERR_UNSUPPORTED;  // no backward of the value-write form
     *bytes = gdn2::chunk_bwd_workspace(desc->batch, desc->heads, desc->seqlen, desc->dk, desc->dv,
                                        static_cast<int>(desc->chunk));
     return GDN2_OK;
@@ -281,6 +286,7 @@ gdn2_status gdn2_recurrent_step(const gdn2_desc *d, const void *q, const void *k
     a.eb_key = d->erase_kind == GDN2_GATE_KEY;
     a.wr_key = d->tie_write_to_erase ? a.eb_key : d->write_kind == GDN2_GATE_KEY;
     a.q_scale = d->q_scale;
+    a.value_write = d->form == GDN2_FORM_VALUE_WRITE;
     return hip_status(gdn2::launch_step(a, static_cast<hipStream_t>(stream)));
 }
 

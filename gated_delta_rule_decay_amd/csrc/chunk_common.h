@@ -245,10 +245,13 @@ __device__ __forceinline__ void chunk_tables(SM &S, int c) {
 // eh = e 2^(gm-g), uh = u 2^(gm-g); keeps k 2^(g-gm), q 2^(g-gm) (fp32) and
 // 2^gm for the later Kbar/Qbar rewrite.  Raises S.wide when a factor or
 // operand leaves the fast range.
-template <typename SM, bool TIED, bool KEYG, int NV>
+// With VW (the value-write form: erase gate on the read, erase and write
+// along k; TIED holds) the row operand is b k and the column operand k.
+template <typename SM, bool TIED, bool KEYG, int NV, bool VW = false>
 __device__ __forceinline__ void factored_operands(SM &S, const Raw<KEYG, NV> &R, f4 (&g)[RPS],
                                                   f4 (&khf)[RPS], f4 (&qhf)[RPS], f4 &egm, int seg,
                                                   int cq, float qs) {
+    static_assert(!VW || TIED, "the value-write form erases and writes along the same vector");
     const int blk = seg / 4;  // 16-row block of my rows
     const f4 base = *reinterpret_cast<const f4 *>(&S.segtot[seg][4 * cq]);
     const f4 gmv = *reinterpret_cast<const f4 *>(&S.segtot[4 * blk + 2][4 * cq]);
@@ -266,11 +269,12 @@ __device__ __forceinline__ void factored_operands(SM &S, const Raw<KEYG, NV> &R,
             e1[j] = __builtin_amdgcn_exp2f(x[j]);
             e2[j] = __builtin_amdgcn_exp2f(-x[j]);
         }
-        const f4 kf = bf16x4_to_f4(R.k[i]);
+        const f4 kraw = bf16x4_to_f4(R.k[i]);
+        const f4 kf = VW ? gate4(R.eb, i) * kraw : kraw;  // the read key
         const f4 qf = bf16x4_to_f4(R.q[i]) * qs;
         khf[i] = kf * e1;
         qhf[i] = qf * e1;
-        const f4 ev = gate4(R.eb, i) * kf * e2;
+        const f4 ev = VW ? kraw * e2 : gate4(R.eb, i) * kraw * e2;
         const f4 uv = TIED ? ev : gate4(R.wr, i) * kf * e2;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

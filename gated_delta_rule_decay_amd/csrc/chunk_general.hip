@@ -20,6 +20,10 @@
 // given the chunk's Grams) and walks the chunks in order; the state slice
 // stays in LDS for the whole sequence.
 //
+// The value-write form (erase gate on the read, write gate per value
+// channel) is the same algebra with the read key b .* k in place of k,
+// erase and write vectors k, and values w .* v.
+//
 // With `hist` set (the backward's first step), the kernel instead records
 // the state entering every chunk, hist[chain][chunk][dk][dv], and writes
 // no output.
@@ -108,9 +112,15 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
                 qv = a.q_scale * load_qkv(a.q, row * dk + c, a.bf16);
                 la = load_gate(a.la, a.la_key, row, dk, c);
                 const float bb = load_gate(a.eb, a.eb_key, row, dk, c);
-                const float ww = a.wr ? load_gate(a.wr, a.wr_key, row, dk, c) : bb;
-                e = bb * kv;
-                u = ww * kv;
+                if (a.value_write) {
+                    // the read key is b .* k; erase and write run along k
+                    e = u = kv;
+                    kv *= bb;
+                } else {
+                    const float ww = a.wr ? load_gate(a.wr, a.wr_key, row, dk, c) : bb;
+                    e = bb * kv;
+                    u = ww * kv;
+                }
             }
             const int li = r * KS + c;
             Kf[li] = kv;
@@ -122,9 +132,13 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
         for (int idx = tid; idx < Cg * DVT; idx += kThreads) {
             const int r = idx / DVT, j = idx % DVT;
             const int64_t t = t0 + r;
-            V[idx] = (t < T && j < ncol)
-                         ? load_qkv(a.v, ((b * T + t) * H + h) * dv + col0 + j, a.bf16)
-                         : 0.f;
+            float vv = 0.f;
+            if (t < T && j < ncol) {
+                const int64_t row = (b * T + t) * H + h;
+                vv = load_qkv(a.v, row * dv + col0 + j, a.bf16);
+                if (a.value_write) vv *= load_gate(a.wr, a.wr_key, row, dv, col0 + j);  // w .* v
+            }
+            V[idx] = vv;
         }
         __syncthreads();
         // 2. inclusive cumulative log-decay per key channel (padded rows add 0)

@@ -115,7 +115,7 @@ __device__ __forceinline__ TaskPos task_pos(int64_t task, int nc, int H) {
     return p;
 }
 
-template <int PART, bool TIED, bool KEYG>
+template <int PART, bool TIED, bool KEYG, bool VW = false>
 __device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, const TaskPos &tp0, int tid) {
     const int64_t b = tp0.b, h = tp0.h, t0 = tp0.t0;
     const int seg = tid >> 5, cq = tid & 31;
@@ -141,6 +141,22 @@ __device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, c
 #pragma unroll
         for (int i = 0; i < 2; ++i)
             R.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, ((2 * tp + i) * rowk + 8 * piece) * 2, 0, 0));
+        if constexpr (VW) {
+            // write gate of my two tokens' 8 value columns (per channel) or
+            // of my two tokens (per head), into the unused wr registers
+            const auto rw = chain_rsrc(a.wr, a, b, h, t0, gw, 4, 0);
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                if constexpr (KEYG) {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+                        R.wr.x[2 * i + hh] = __builtin_bit_cast(
+                            f4, __builtin_amdgcn_raw_buffer_load_b128(rw, ((2 * tp + i) * rowg + 8 * piece + 4 * hh) * 4, 0, 0));
+                } else {
+                    R.wr.x[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, (2 * tp + i) * rowg * 4, 0, 0));
+                }
+            }
+        }
     }
     if constexpr (PART == 3) {
         const auto rk = chain_rsrc(a.k, a, b, h, t0, D, 2, 0);
@@ -214,7 +230,7 @@ __device__ __forceinline__ bool wq_tiles(const PrepSmem &S, _Float16 *rec, int k
     return big;
 }
 
-template <bool TIED, bool KEYG>
+template <bool TIED, bool KEYG, bool VW>
 __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w, int nc) {
     __shared__ PrepSmem S;
     const int tid = threadIdx.x;
@@ -234,10 +250,10 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
     int64_t task = blockIdx.x;
     if (task < ntask) {
         const TaskPos p0 = task_pos(task, nc, static_cast<int>(a.H));
-        load_part<0, TIED>(R, a, p0, tid);
-        load_part<1, TIED>(R, a, p0, tid);
-        load_part<2, TIED>(R, a, p0, tid);
-        load_part<3, TIED>(R, a, p0, tid);
+        load_part<0, TIED, KEYG, VW>(R, a, p0, tid);
+        load_part<1, TIED, KEYG, VW>(R, a, p0, tid);
+        load_part<2, TIED, KEYG, VW>(R, a, p0, tid);
+        load_part<3, TIED, KEYG, VW>(R, a, p0, tid);
     }
 
     for (; task < ntask; task += gridDim.x) {
@@ -257,11 +273,18 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             const int tp = tl & 31, piece = tl >> 5;
             const uint32_t r0[4] = {R.v[0].x, R.v[0].y, R.v[0].z, R.v[0].w};
             const uint32_t r1[4] = {R.v[1].x, R.v[1].y, R.v[1].z, R.v[1].w};
+            // the value-write form writes w .* v: gate of token i, column 2e + s
+            auto wg = [&](int i, int e, int s) -> float {
+                if constexpr (!VW) return 1.f;
+                else if constexpr (KEYG) return R.wr.x[2 * i + (2 * e + s) / 4][(2 * e + s) % 4];
+                else return R.wr.x[i];
+            };
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const _Float16 a0 = (_Float16)__uint_as_float(r0[e] << 16), a1 = (_Float16)__uint_as_float(r1[e] << 16);
-                const _Float16 b0 = (_Float16)__uint_as_float(r0[e] & 0xffff0000u);
-                const _Float16 b1 = (_Float16)__uint_as_float(r1[e] & 0xffff0000u);
+                const _Float16 a0 = (_Float16)(__uint_as_float(r0[e] << 16) * wg(0, e, 0));
+                const _Float16 a1 = (_Float16)(__uint_as_float(r1[e] << 16) * wg(1, e, 0));
+                const _Float16 b0 = (_Float16)(__uint_as_float(r0[e] & 0xffff0000u) * wg(0, e, 1));
+                const _Float16 b1 = (_Float16)(__uint_as_float(r1[e] & 0xffff0000u) * wg(1, e, 1));
                 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
                 *reinterpret_cast<h2 *>(&S.v16[(8 * piece + 2 * e) * SP + 2 * tp]) = h2{a0, a1};
                 *reinterpret_cast<h2 *>(&S.v16[(8 * piece + 2 * e + 1) * SP + 2 * tp]) = h2{b0, b1};
@@ -275,10 +298,10 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
 
         // ---- factored fp16 Gram operands -------------------------------------
         f4 khf[RPS], qhf[RPS], egm;
-        factored_operands<PrepSmem, TIED>(S, R, g, khf, qhf, egm, seg, cq, a.q_scale);
+        factored_operands<PrepSmem, TIED, KEYG, 2, VW>(S, R, g, khf, qhf, egm, seg, cq, a.q_scale);
         const int64_t next = task + gridDim.x;  // prefetched in four parts below
         const TaskPos pn = task_pos(next < ntask ? next : task, nc, static_cast<int>(a.H));
-        if (next < ntask) load_part<0, TIED>(R, a, pn, tid);
+        if (next < ntask) load_part<0, TIED, KEYG, VW>(R, a, pn, tid);
         __syncthreads();
 
         const bool wide = S.wide != 0;  // read by all before any later write
@@ -306,7 +329,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 *reinterpret_cast<h4 *>(&S.qh[r * KP + 4 * cq]) = to_h4(qhf[i] * egm);
             }
         }
-        if (next < ntask) load_part<1, TIED>(R, a, pn, tid);
+        if (next < ntask) load_part<1, TIED, KEYG, VW>(R, a, pn, tid);
 
         _Float16 *rec = w.frag + task * REC;
         if (!wide) {
@@ -378,7 +401,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 *reinterpret_cast<h4 *>(&S.u16[(16 * ct + lr) * SP + 16 * rt + 4 * lg]) = to_h4(uacc[rt]);
             if (big) S.wide = 1;
             __syncthreads();  // U complete in u16
-            if (next < ntask) load_part<2, TIED>(R, a, pn, tid);
+            if (next < ntask) load_part<2, TIED, KEYG, VW>(R, a, pn, tid);
 
             // ---- (4) Oe^T[ct, :] = V^T P^T - U^T R^T -> HBM (transposed, so
             //      the scan's output tiles hold adjacent columns per lane)
@@ -422,9 +445,9 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             }
             if (big) S.wide = 1;
         } else if (next < ntask) {
-            load_part<2, TIED>(R, a, pn, tid);
+            load_part<2, TIED, KEYG, VW>(R, a, pn, tid);
         }
-        if (next < ntask) load_part<3, TIED>(R, a, pn, tid);
+        if (next < ntask) load_part<3, TIED, KEYG, VW>(R, a, pn, tid);
         __syncthreads();
         // e^gC per key channel; a chunk to be run exactly is marked by -1 in
         // channel 0 (e^gC is never negative)
@@ -490,7 +513,7 @@ struct ScanPlan {
 // MODE 0: the scan proper (O and, for the last segment, the final state).
 // MODE 1: segment summaries; SCAN_W more compute waves carry the columns of
 // F (the first SCAN_W carry the state), no Qe / Oe / O.
-template <bool TIED, bool KEYG, int MODE>
+template <bool TIED, bool KEYG, bool VW, int MODE>
 __global__ void __launch_bounds__(scan_threads(MODE))
 chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     constexpr bool WITH_O = MODE == 0;
@@ -679,18 +702,21 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
                 // gates of key channel c of this token (per channel or per head)
                 auto gate = [&](const float *g, int c) { return g[row * gw + (KEYG ? c : 0)]; };
                 float m = 0.f, o = 0.f;
-                // decay, then the erase read m = k^T S_bar
+                // decay, then the erase read m = k^T S_bar (the value-write
+                // form reads along b .* k)
 #pragma unroll
                 for (int it = 0; it < 8; ++it)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int c = 16 * it + 4 * lg + e;
                         sacc[it][e] *= expf(gate(a.la, c));
-                        m += bf16_to_f32(kp[row * D + c]) * sacc[it][e];
+                        const float kc = bf16_to_f32(kp[row * D + c]);
+                        m += (VW ? gate(a.eb, c) * kc : kc) * sacc[it][e];
                     }
                 m += __shfl_xor(m, 16);
                 m += __shfl_xor(m, 32);
-                const float vv = frun ? 0.f : bf16_to_f32(vp[row * D + 16 * ct + lr]);
+                float vv = frun ? 0.f : bf16_to_f32(vp[row * D + 16 * ct + lr]);
+                if (VW) vv *= a.wr[row * gw + (KEYG ? 16 * ct + lr : 0)];
                 // erase and write, then the read o = S^T q
 #pragma unroll
                 for (int it = 0; it < 8; ++it)
@@ -699,7 +725,8 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
                         const int c = 16 * it + 4 * lg + e;
                         const float kc = bf16_to_f32(kp[row * D + c]);
                         const float bb = gate(a.eb, c);
-                        const float ec = bb * kc, uc = (TIED ? bb : gate(a.wr, c)) * kc;
+                        const float ec = VW ? kc : bb * kc;
+                        const float uc = VW ? kc : (TIED ? bb : gate(a.wr, c)) * kc;
                         sacc[it][e] = sacc[it][e] - ec * m + uc * vv;
                         if (WITH_O) o += a.q_scale * bf16_to_f32(qp[row * D + c]) * sacc[it][e];
                     }
@@ -847,7 +874,7 @@ int cu_count() {
     return n;
 }
 
-template <bool TIED, bool KEYG>
+template <bool TIED, bool KEYG, bool VW = false>
 hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
     const Layout l = layout(a.B, a.H, a.T);
     char *p = static_cast<char *>(ws);
@@ -861,12 +888,12 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
     sp.fs = l.nseg > 1 ? reinterpret_cast<float *>(p + l.off_fs) : nullptr;
     const int nc = static_cast<int>(l.nc);
     const int64_t g1 = l.ntask < cu_count() ? l.ntask : cu_count();
-    hipLaunchKernelGGL((chunk_prep_kernel<TIED, KEYG>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s, a, w, nc);
+    hipLaunchKernelGGL((chunk_prep_kernel<TIED, KEYG, VW>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s, a, w, nc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (l.nseg > 1) {
         const int64_t units = l.chains * (l.nseg - 1);
-        hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG, 1>), dim3(static_cast<unsigned>(units * 2)),
+        hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG, VW, 1>), dim3(static_cast<unsigned>(units * 2)),
                            dim3(scan_threads(1)), 0, s, a, w, nc, sp, units % 8 == 0 ? 1 : 0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (l.nseg > 2) {
@@ -876,7 +903,7 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
         }
     }
     const int64_t units = l.chains * l.nseg;
-    hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG, 0>), dim3(static_cast<unsigned>(units * 2)),
+    hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG, VW, 0>), dim3(static_cast<unsigned>(units * 2)),
                        dim3(scan_threads(0)), 0, s, a, w, nc, sp, units % 8 == 0 ? 1 : 0);
     return hipGetLastError();
 }
@@ -884,15 +911,20 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
 }  // namespace
 
 bool chunk_split_supported(const ChunkArgs &a) {
-    // the kernels index tasks (chain * chunks + chunk) with 32-bit arithmetic
+    // every present gate of one kind (all per channel or all per head); the
+    // kernels index tasks (chain * chunks + chunk) with 32-bit arithmetic
+    const bool tied = a.wr == nullptr;
+    const bool same = a.la_key == a.eb_key && (tied || a.wr_key == a.eb_key);
     const int64_t ntask = a.B * a.H * ((a.T + C - 1) / C);
-    return chunk_mfma_supported(a) && ntask > 0 && ntask < (int64_t(1) << 31);
+    return a.bf16 && a.dk == D && a.dv == D && a.C == C && same && (!a.value_write || !tied) &&
+           a.H * D * 4 * C < (int64_t(1) << 31) && ntask > 0 && ntask < (int64_t(1) << 31);
 }
 
 size_t chunk_split_workspace(int64_t B, int64_t H, int64_t T) { return static_cast<size_t>(layout(B, H, T).bytes); }
 
 hipError_t launch_chunk_split(const ChunkArgs &a, void *ws, hipStream_t s) {
     const bool tied = a.wr == nullptr, keyg = a.la_key != 0;
+    if (a.value_write) return keyg ? launch_kinds<true, true, true>(a, ws, s) : launch_kinds<true, false, true>(a, ws, s);
     if (tied) return keyg ? launch_kinds<true, true>(a, ws, s) : launch_kinds<true, false>(a, ws, s);
     return keyg ? launch_kinds<false, true>(a, ws, s) : launch_kinds<false, false>(a, ws, s);
 }

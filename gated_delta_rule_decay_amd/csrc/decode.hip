@@ -2,7 +2,8 @@
 //
 // The O(1)-memory inference form ("Gated DeltaNet-2" blog summary, "Core
 // Mechanism"): for each head, with the fp32 state S (dk x dv) in HBM,
-//   Sbar = Diag(a) S,  m = Sbar^T k,  S = Sbar - (b*k) m^T + (w*k) v^T,  o = S^T q.
+//   Sbar = Diag(a) S,  m = Sbar^T k,  S = Sbar - (b*k) m^T + (w*k) v^T,  o = S^T q
+// (value-write form: m = Sbar^T (b*k), S = Sbar - k m^T + k (w*v)^T).
 // Decay comes first and the read sees the decayed state ("Gated DeltaNet"
 // page, "Decay first, then compute the write error").
 //
@@ -43,18 +44,30 @@ __global__ void __launch_bounds__(256) step128_kernel(StepArgs a) {
         const float qv = a.q_scale * load_qkv(a.q, head * kD + c, a.bf16);
         const float la = load_gate(a.la, a.la_key, head, kD, c);
         const float bb = load_gate(a.eb, a.eb_key, head, kD, c);
-        const float ww = a.wr ? load_gate(a.wr, a.wr_key, head, kD, c) : bb;
-        s_k[c] = kv;
         s_q[c] = qv;
         s_a[c] = __expf(la);
-        s_e[c] = bb * kv;
-        s_u[c] = ww * kv;
+        if (a.value_write) {  // read along b .* k, erase and write along k
+            s_k[c] = bb * kv;
+            s_e[c] = kv;
+            s_u[c] = kv;
+        } else {
+            const float ww = a.wr ? load_gate(a.wr, a.wr_key, head, kD, c) : bb;
+            s_k[c] = kv;
+            s_e[c] = bb * kv;
+            s_u[c] = ww * kv;
+        }
     }
     float4 v;
     v.x = load_qkv(a.v, head * kD + 4 * cg + 0, a.bf16);
     v.y = load_qkv(a.v, head * kD + 4 * cg + 1, a.bf16);
     v.z = load_qkv(a.v, head * kD + 4 * cg + 2, a.bf16);
     v.w = load_qkv(a.v, head * kD + 4 * cg + 3, a.bf16);
+    if (a.value_write) {  // w .* v, one factor per value channel (or per head)
+        v.x *= load_gate(a.wr, a.wr_key, head, kD, 4 * cg + 0);
+        v.y *= load_gate(a.wr, a.wr_key, head, kD, 4 * cg + 1);
+        v.z *= load_gate(a.wr, a.wr_key, head, kD, 4 * cg + 2);
+        v.w *= load_gate(a.wr, a.wr_key, head, kD, 4 * cg + 3);
+    }
     __syncthreads();
 
     // decay, then the key read of the decayed state
@@ -118,19 +131,26 @@ __global__ void __launch_bounds__(128) step_general_kernel(StepArgs a) {
     if (j < dk) {
         const float kv = load_qkv(a.k, head * dk + j, a.bf16);
         const float bb = load_gate(a.eb, a.eb_key, head, dk, j);
-        const float ww = a.wr ? load_gate(a.wr, a.wr_key, head, dk, j) : bb;
-        s_k[j] = kv;
         s_q[j] = a.q_scale * load_qkv(a.q, head * dk + j, a.bf16);
         s_a[j] = expf(load_gate(a.la, a.la_key, head, dk, j));
-        s_e[j] = bb * kv;
-        s_u[j] = ww * kv;
+        if (a.value_write) {
+            s_k[j] = bb * kv;
+            s_e[j] = kv;
+            s_u[j] = kv;
+        } else {
+            const float ww = a.wr ? load_gate(a.wr, a.wr_key, head, dk, j) : bb;
+            s_k[j] = kv;
+            s_e[j] = bb * kv;
+            s_u[j] = ww * kv;
+        }
     }
     __syncthreads();
     if (j >= dv) return;
     float *col = a.state + head * static_cast<int64_t>(dk) * dv + j;
     float m = 0.f;
     for (int c = 0; c < dk; ++c) m += s_k[c] * (s_a[c] * col[static_cast<int64_t>(c) * dv]);
-    const float vj = load_qkv(a.v, head * dv + j, a.bf16);
+    float vj = load_qkv(a.v, head * dv + j, a.bf16);
+    if (a.value_write) vj *= load_gate(a.wr, a.wr_key, head, dv, j);
     float o = 0.f;
     for (int c = 0; c < dk; ++c) {
         const float sn = s_a[c] * col[static_cast<int64_t>(c) * dv] - s_e[c] * m + s_u[c] * vj;

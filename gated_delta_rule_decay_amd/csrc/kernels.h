@@ -19,6 +19,8 @@ struct ChunkArgs {
     int bf16;                       // q/k/v element type
     int la_key, eb_key, wr_key;     // 1: per key channel, 0: per token-head
     float q_scale;
+    int value_write;                // 1: erase gate on the read, write gate per value
+                                    //    channel ([B,T,H,dv] when wr_key)
 };
 
 struct StepArgs {
@@ -30,6 +32,7 @@ struct StepArgs {
     int bf16;
     int la_key, eb_key, wr_key;
     float q_scale;
+    int value_write;                // as in ChunkArgs
 };
 
 // General chunked forward: fp32 arithmetic on the vector ALU, any dk, dv in

@@ -19,6 +19,15 @@
  * DeltaNet, per-channel decay with tied scalar beta gives KDA, a = 1 gives
  * the delta rule (gist.science summary, "Technische Samenvatting", sec. 1).
  *
+ * desc->form = GDN2_FORM_VALUE_WRITE selects the update as the gist.science
+ * summary writes it ("Methodologie", 1. "Gated Delta-regel-2"):
+ *
+ *     S    = (I - k_t (b_t .* k_t)^T) Sbar + k_t (w_t .* v_t)^T
+ *
+ * i.e. the erase gate weights the read (m = Sbar^T (b_t .* k_t)), the erase
+ * and the write run along k_t, and the write gate has one factor per VALUE
+ * channel.  With scalar gates both forms are the same operation.
+ *
  * Conventions shared by every call:
  *  - Every data pointer is DEVICE memory (hipMalloc'd or torch CUDA
  *    tensors) owned by the caller; the library allocates nothing, keeps no
@@ -29,7 +38,9 @@
  *        o              [B, T, H, dv]    fp32
  *        log_decay      [B, T, H, dk] fp32 if decay_kind == GDN2_GATE_KEY,
  *                       [B, T, H]     fp32 if GDN2_GATE_HEAD
- *        erase, write   same rule with erase_kind / write_kind
+ *        erase, write   same rule with erase_kind / write_kind (the write
+ *                       gate of GDN2_FORM_VALUE_WRITE: [B, T, H, dv] per
+ *                       channel)
  *        state tensors  [B, H, dk, dv]   fp32
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *    and the call returns without synchronising.  Device faults surface at
@@ -53,7 +64,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 1
+#define GDN2_ABI_VERSION 2
 
 typedef enum gdn2_status {
     GDN2_OK = 0,
@@ -73,6 +84,12 @@ typedef enum gdn2_gate_kind {
     GDN2_GATE_KEY = 1   /* one value per key channel                            */
 } gdn2_gate_kind;
 
+typedef enum gdn2_form {
+    GDN2_FORM_KEY = 0,         /* erase (b.*k)(k^T Sbar), write (w.*k) v^T  */
+    GDN2_FORM_VALUE_WRITE = 1  /* erase k((b.*k)^T Sbar), write k (w.*v)^T;
+                                  needs an untied write gate               */
+} gdn2_form;
+
 /* Problem description.  For gdn2_recurrent_step `batch` is the number of
  * sequences N and `seqlen` must be 1. */
 typedef struct gdn2_desc {
@@ -88,6 +105,8 @@ typedef struct gdn2_desc {
     int32_t write_kind; /* gdn2_gate_kind of write (ignored when tied) */
     int32_t tie_write_to_erase; /* nonzero: w := b and `write` is ignored */
     float q_scale;      /* multiplies q; 1.0 for the plain read */
+    int32_t form;       /* gdn2_form; a tied write gate with
+                           GDN2_FORM_VALUE_WRITE is GDN2_ERR_SHAPE */
 } gdn2_desc;
 
 /* GDN2_ABI_VERSION of the loaded library. */

@@ -36,16 +36,17 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn2_abi_version() == 1
+    assert lib.gdn2_abi_version() == 2
     for s in range(8):
         assert lib.gdn2_status_str(s)
     assert lib.gdn2_status_str(0) == b"ok"
 
 
 def test_desc_layout_matches_header():
-    # six int64, five int32, one float: 72 bytes, no padding surprises
-    assert ctypes.sizeof(bd.Gdn2Desc) == 72
+    # six int64, five int32, one float, one int32: 76 bytes, padded to 80
+    assert ctypes.sizeof(bd.Gdn2Desc) == 80
     assert bd.Gdn2Desc.q_scale.offset == 68
+    assert bd.Gdn2Desc.form.offset == 72
 
 
 # Fake, well-separated device addresses for the inputs and outputs.
@@ -237,3 +238,18 @@ def test_bwd_checks(lib):
     assert bwd(lib, d, dv=DO) == 5                   # gradient on top of d_o
     assert bwd(lib, good(dk=129), wsb=0) == 4
     assert bwd(lib, good(chunk=8), wsb=0) == 4
+
+
+def test_value_write_form_checks(lib):
+    vw = dict(form=bd.GDN2_FORM_VALUE_WRITE)
+    assert fwd(lib, good(form=2)) == 2                       # unknown form
+    assert fwd(lib, good(tied=True, **vw)) == 2              # needs its own write gate
+    assert fwd(lib, good(**vw), wr=None) == 1
+    # the write gate has dv channels: its span is sized by dv, not dk
+    d = good(dk=64, dv=128, **vw)
+    wbytes = 2 * 128 * 4 * 128 * 4
+    assert fwd(lib, d, wr=O - wbytes + 256) == 5             # runs into o
+    # the two-pass kernels cover it; the backward does not
+    assert query(lib, good(**vw)) == split_bytes(2, 4, 128)
+    n = ctypes.c_size_t(0)
+    assert lib.gdn2_chunk_bwd_workspace(ctypes.byref(good(**vw)), ctypes.byref(n)) == 4

@@ -5,10 +5,12 @@
 One step is one chunked forward over the whole batch of the full GDN-2
 workload (B=8, H=16, T=4096, dk=dv=128, C=64, bf16 q/k/v, fp32 per-channel
 decay/erase/write gates and state, S0 ~ N(0, 0.1)), inputs resident in HBM.
-``value`` is tokens/s (B*T per step).  The same run also times the recurrent
-decode step (256 sequences x 16 heads, fp32 state in HBM, in place) and the
-Gated DeltaNet mode (scalar gates, B=4), each reported beside ``value`` with
-its own roofline, and times the fp64 CPU oracle on the full workload.
+``value`` is tokens/s (B*T per step).  The same run also times, each beside
+``value`` with its own roofline: the single-pass kernel and the value-write
+form on the same inputs, the backward, the long-context workload (B=1,
+T=65536, two-level scan), the Gated DeltaNet mode (scalar gates, B=4) and
+the recurrent decode step (256 sequences x 16 heads, fp32 state in HBM, in
+place); and the fp64 CPU oracle on the full workload.
 
 Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits.
 """
@@ -104,7 +106,7 @@ def to_dev(inp, torch):
     return out
 
 
-def time_chunk(w, wid, steps, warmup, torch, chunk_fwd, one_pass=False, inp=None):
+def time_chunk(w, wid, steps, warmup, torch, chunk_fwd, one_pass=False, inp=None, value_write=False):
     """Time `steps` chunked forwards of workload w with inputs, outputs and
     the two-pass workspace resident in HBM.  Returns (inputs, wall ms per
     step, HIP-event ms per step on the launch stream)."""
@@ -121,19 +123,21 @@ def time_chunk(w, wid, steps, warmup, torch, chunk_fwd, one_pass=False, inp=None
         desc = binding.make_desc(w.B, w.T, w.H, w.dk, w.dv, w.chunk,
                                  binding.GDN2_BF16 if w.qkv_dtype == "bf16" else binding.GDN2_F32,
                                  int(w.gates == "key"), int(w.gates == "key"), int(w.gates == "key"),
-                                 w.tied)
+                                 w.tied, form=int(value_write))
         n = binding.chunk_fwd_workspace(desc)
         ws = torch.empty(n, dtype=torch.uint8, device="cuda") if n else False
     args = (d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"])
+    kw = dict(chunk=w.chunk, out=o, state_out=st, workspace=ws, value_write=value_write)
     for _ in range(warmup):
-        chunk_fwd(*args, chunk=w.chunk, out=o, state_out=st, workspace=ws)
+        chunk_fwd(*args, **kw)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-    log(f"[bench] timing {steps} steps of {w.name}" + (" (one pass)" if one_pass else ""))
+    log(f"[bench] timing {steps} steps of {w.name}" + (" (one pass)" if one_pass else "")
+        + (" (value-write form)" if value_write else ""))
     t0 = time.perf_counter()
     ev[0].record()
     for i in range(steps):
-        chunk_fwd(*args, chunk=w.chunk, out=o, state_out=st, workspace=ws)
+        chunk_fwd(*args, **kw)
         ev[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -142,6 +146,49 @@ def time_chunk(w, wid, steps, warmup, torch, chunk_fwd, one_pass=False, inp=None
     ms_kernel = ev[0].elapsed_time(ev[steps]) / steps
     time_chunk.last = {"kernel_ms_median": round(per_call[steps // 2], 4), "kernel_ms_min": round(per_call[0], 4)}
     return inp, ms_step, ms_kernel
+
+
+def bwd_bytes(w) -> int:
+    """Algorithmic HBM bytes of one backward call: the forward's inputs, d_o
+    and d_S_T read once; dq, dk, dv, the gate gradients and d_S0 written once
+    (fp32)."""
+    e = 2 if w.qkv_dtype == "bf16" else 4
+    gate = w.dk * 4 if w.gates == "key" else 4
+    n_gates = 2 if w.tied else 3
+    per_tok = (2 * w.dk + w.dv) * e + n_gates * gate + w.dv * 4 + (2 * w.dk + w.dv) * 4 + n_gates * gate
+    state = w.B * w.H * w.dk * w.dv * 4
+    return w.B * w.T * w.H * per_tok + 3 * state
+
+
+def time_backward(w, inp, torch, steps):
+    """Time gdn2_chunk_bwd on workload w (random cotangents, workspace
+    resident)."""
+    from gated_delta_rule_decay_amd import binding, chunk_bwd
+
+    d = to_dev(inp, torch)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    d_o = torch.randn((w.B, w.T, w.H, w.dv), device="cuda", generator=g)
+    d_st = torch.randn((w.B, w.H, w.dk, w.dv), device="cuda", generator=g)
+    desc = binding.make_desc(w.B, w.T, w.H, w.dk, w.dv, w.chunk, binding.GDN2_BF16,
+                             int(w.gates == "key"), int(w.gates == "key"), int(w.gates == "key"), w.tied)
+    ws = torch.empty(binding.chunk_bwd_workspace(desc), dtype=torch.uint8, device="cuda")
+    args = (d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"], d_o, d_st)
+    chunk_bwd(*args, chunk=w.chunk, workspace=ws)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {steps} backward calls of {w.name}")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        chunk_bwd(*args, chunk=w.chunk, workspace=ws)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    k = ev0.elapsed_time(ev1) / steps
+    return {"workload": f"{w.name}: gradients of q, k, v, gates and S0 (general fp32 kernels)",
+            "ms_per_step": round(ms, 3), "kernel_ms": round(k, 3),
+            "value": round(w.B * w.T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "roofline": roofline_hbm(bwd_bytes(w), k), "algorithmic_bytes_per_launch": bwd_bytes(w)}
 
 
 def synth_make(w, wid):
@@ -226,9 +273,26 @@ def main():
                                   inp=inp)
         result["one_pass"] = {"ms_per_step": round(ms1p, 4), "kernel_ms": round(k1p, 4),
                               "value": round(tokens / (ms1p * 1e-3), 1), "unit": "tokens/s"}
+        # the value-write form on the same inputs (dk = dv: the write gate
+        # reads as one factor per value channel)
+        _, msvw, kvw = time_chunk(w, 2, max(2, args.steps // 4), 1, torch, chunk_fwd, inp=inp,
+                                  value_write=True)
+        result["value_write"] = {"workload": f"{w.name}, value-write form (tied-structure kernels)",
+                                 "ms_per_step": round(msvw, 4), "kernel_ms": round(kvw, 4),
+                                 "value": round(tokens / (msvw * 1e-3), 1), "unit": "tokens/s",
+                                 "roofline": roofline_hbm(chunk_bytes(w), kvw)}
+        result["backward"] = time_backward(w, inp, torch, max(2, args.steps // 8))
     del inp
 
     if not args.no_extra:
+        # long context: one sequence per head, T = 65536 (two-level scan)
+        w3 = W[3]
+        _, ms3, k3 = time_chunk(w3, 3, max(2, args.steps // 4), 1, torch, chunk_fwd)
+        result["long_context"] = {"workload": f"{w3.name}: B={w3.B} H={w3.H} T={w3.T}, decay spikes",
+                                  "value": round(w3.B * w3.T / (ms3 * 1e-3), 1), "unit": "tokens/s",
+                                  "ms_per_step": round(ms3, 4), "kernel_ms": round(k3, 4),
+                                  "roofline": roofline_hbm(chunk_bytes(w3), k3,
+                                                           read_traffic("chunk_fwd", w3.name, chunk_hash))}
         # Gated DeltaNet mode: scalar gates tied, zero initial state, B=4
         w1 = W[1]
         _, ms1, k1 = time_chunk(w1, 1, args.steps, args.warmup, torch, chunk_fwd)

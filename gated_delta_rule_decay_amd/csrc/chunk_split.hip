@@ -499,6 +499,15 @@ constexpr int SEG_WG = 256;   // scan workgroups aimed at when chains are few
 
 constexpr int scan_threads(int mode) { return 64 * (SCAN_P + (mode ? 2 : 1) * SCAN_W); }
 
+// The workgroup barrier that hands a slot over.  The empty asm statements
+// keep the compiler from moving LDS accesses across it (the barrier
+// intrinsic alone does not order memory), without the waits a fence adds.
+__device__ __forceinline__ void slot_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (other counters untouched)
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -549,47 +558,56 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     const int64_t task0 = static_cast<int64_t>(chain) * nc;
     const int64_t xbase = (static_cast<int64_t>(chain) * sp.nseg + seg) * D * D;  // slot seg
 
-    // state slice: tile it holds S[16it+4lg+e][16ct+lr]
-    const float *init = nullptr;
-    if (MODE == 0) init = sp.nseg == 1 ? (a.s0 ? a.s0 + sbase : nullptr) : sp.xs + xbase;
-    else if (!frun && seg == 0 && a.s0) init = a.s0 + sbase;
-    f4 sacc[8];
-#pragma unroll
-    for (int it = 0; it < 8; ++it)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c = 16 * it + 4 * lg + e, v = 16 * ct + lr;
-            sacc[it][e] = copier ? 0.f : init ? init[c * D + v] : (frun && c == v) ? 1.f : 0.f;
-            if (MODE == 1 && !copier && !frun && seg == 0) sp.xs[xbase + c * D + v] = sacc[it][e];
-        }
+    f4 sacc[8];  // state slice (compute waves): tile it holds S[16it+4lg+e][16ct+lr]
 
-    // Copy chunk `task` into a slot: W | Qe | EtT (MODE 1: W | EtT), then my
+    // Chunks travel memory -> copy-wave registers -> LDS slot.  While the
+    // compute waves work on chunk n (one slot), the copy waves write chunk
+    // n+1 from their registers into the other slot and issue the loads of
+    // chunk n+2 into their registers, so two chunks' memory latency is always
+    // in flight.  A slot holds W | Qe | EtT (MODE 1: W | EtT), then my
     // workgroup's G and Oe^T tiles (contiguous in the record), then e^gC.
     // Each wave moves 1 KiB per instruction (lane l -> bytes 16l..16l+15).
-    auto fill = [&](_Float16 *fr, float *gm, int64_t task, int pw) __attribute__((always_inline)) {
-        const char *rec = reinterpret_cast<const char *>(w.frag + task * REC);
-        const char *srcg = rec + 2 * (OFF_G + static_cast<int64_t>(SCAN_W * half) * 4 * 512);
-        const char *srco = rec + 2 * (OFF_O + static_cast<int64_t>(SCAN_W * half) * 2 * 512);
+    typedef uint32_t u4v __attribute__((ext_vector_type(4)));
+    u4v cr[PIECES];
+    float cgam = 0.f;
+    auto load_regs = [&](int64_t task, int pw) __attribute__((always_inline)) {
+        // one buffer resource per record: every piece is the same lane offset
+        // plus a uniform byte offset, so no per-piece address registers
+        const auto rs = __builtin_amdgcn_make_buffer_rsrc(w.frag + task * REC, (short)0, static_cast<int>(REC * 2),
+                                                          0x00020000);
+        const int og = 2 * (static_cast<int>(OFF_G) + SCAN_W * half * 4 * 512);
+        const int oo = 2 * (static_cast<int>(OFF_O) + SCAN_W * half * 2 * 512);
 #pragma unroll
         for (int i = 0; i < PIECES; ++i) {
             const int byte = 1024 * (SCAN_P * i + pw);  // my 1 KiB block of the slot
-            const char *src;
+            int src;
             if (MODE == 0)
-                src = byte < 2 * SLOT_F ? rec + byte
-                    : byte < 2 * (SLOT_F + SLOT_G) ? srcg + (byte - 2 * SLOT_F)
-                                                   : srco + (byte - 2 * (SLOT_F + SLOT_G));
+                src = byte < 2 * SLOT_F ? byte
+                    : byte < 2 * (SLOT_F + SLOT_G) ? og + (byte - 2 * SLOT_F)
+                                                   : oo + (byte - 2 * (SLOT_F + SLOT_G));
             else
-                src = byte < 2 * 8192 ? rec + byte
-                    : byte < 4 * 8192 ? rec + 2 * OFF_E + (byte - 2 * 8192)
-                                      : srcg + (byte - 4 * 8192);
-            __builtin_amdgcn_global_load_lds(src + 16 * lane, reinterpret_cast<char *>(fr) + byte, 16, 0, 0);
+                src = byte < 2 * 8192 ? byte
+                    : byte < 4 * 8192 ? 2 * static_cast<int>(OFF_E) + (byte - 2 * 8192)
+                                      : og + (byte - 4 * 8192);
+            cr[i] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, src, 0));
         }
         // e^gC: copy waves 0,1 bring channels 0..127
-        if (pw < 2) __builtin_amdgcn_global_load_lds(w.gam + task * D + 64 * pw + lane, gm + 64 * pw, 4, 0, 0);
+        if (pw < 2) cgam = w.gam[task * D + 64 * pw + lane];
+    };
+    auto store_regs = [&](_Float16 *fr, float *gm, int pw) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < PIECES; ++i)
+            *reinterpret_cast<u4v *>(reinterpret_cast<char *>(fr) + 1024 * (SCAN_P * i + pw) + 16 * lane) = cr[i];
+        if (pw < 2) gm[64 * pw + lane] = cgam;
     };
 
     // One chunk n on this wave, from slot (fr, gm).
     auto compute = [&](int n, const _Float16 *fr, const float *gm) __attribute__((always_inline)) {
+        // lane coordinates re-derived per chunk, so that the LDS addresses
+        // built from them are not hoisted out of the loop (and spilled)
+        int lane_ = lane;
+        asm volatile("" : "+v"(lane_));
+        const int lane = lane_, lr = lane & 15, lg = lane >> 4;
         const _Float16 *fg = fr + S_G + wt * 4 * 512;  // my G pairs
         const _Float16 *fo = fr + S_O + wt * 2 * 512;  // my Oe^T pairs (MODE 0)
         const int64_t t0 = static_cast<int64_t>(n) * C;
@@ -743,45 +761,69 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     };
 
     // Chunk n: the barrier finds slot n & 1 complete (its copy waves waited
-    // for their copies before arriving) and every compute wave past chunk
-    // n-1; then the copy waves refill the other slot (last read in chunk n-1)
-    // with chunk n+1 and wait for it, while the compute waves compute chunk n.
-    // Unrolled by two so both slots are named statically.
-#define GDN2_SCAN_STEP(N, FR, GM, FRN, GMN)                                        \
-    do {                                                                          \
-        __builtin_amdgcn_s_barrier();                                             \
-        if (copier) {                                                             \
-            if ((N) + 1 < n1) fill(FRN, GMN, task0 + (N) + 1, wv - NCOMP);        \
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                             \
-        } else if (!idle) {                                                       \
-            compute((N), FR, GM);                                                 \
-        }                                                                         \
-    } while (0)
-
+    // for their LDS writes before arriving) and every compute wave past chunk
+    // n-1; then the copy waves write chunk n+1 into the other slot (last read
+    // in chunk n-1) and start the loads of chunk n+2, while the compute waves
+    // compute chunk n.  The two roles run separate loops with one barrier per
+    // chunk each (so the copy registers and the compute registers are never
+    // live at once), unrolled by two so both slots are named statically.
+    constexpr int LGKM0 = 15 | (7 << 4) | (3 << 14);  // s_waitcnt lgkmcnt(0), other counters untouched
     if (copier) {
-        fill(fr0, gm0, task0 + n0, wv - NCOMP);
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    }
-    int n = n0;
-    for (; n + 1 < n1; n += 2) {
-        GDN2_SCAN_STEP(n, fr0, gm0, fr1, gm1);
-        GDN2_SCAN_STEP(n + 1, fr1, gm1, fr0, gm0);
-    }
-    if (n < n1) GDN2_SCAN_STEP(n, fr0, gm0, fr1, gm1);
-#undef GDN2_SCAN_STEP
-
-    float *dst = nullptr;
-    if (copier || idle) dst = nullptr;
-    else if (MODE == 0) dst = (seg == sp.nseg - 1 && a.s_out) ? a.s_out + sbase : nullptr;
-    else dst = frun ? sp.fs + xbase : sp.xs + xbase + D * D;  // F[seg], X[seg+1]
-    if (dst) {
+        const int pw = wv - NCOMP;
+        load_regs(task0 + n0, pw);
+        store_regs(fr0, gm0, pw);
+        if (n0 + 1 < n1) load_regs(task0 + n0 + 1, pw);
+        __builtin_amdgcn_s_waitcnt(LGKM0);
+#define GDN2_COPY_STEP(N, FRN, GMN)                                                \
+        do {                                                                      \
+            slot_barrier();                                         \
+            if ((N) + 1 < n1) store_regs(FRN, GMN, pw);                           \
+            if ((N) + 2 < n1) load_regs(task0 + (N) + 2, pw);                     \
+            __builtin_amdgcn_s_waitcnt(LGKM0);                                    \
+        } while (0)
+        int n = n0;
+        for (; n + 1 < n1; n += 2) {
+            GDN2_COPY_STEP(n, fr1, gm1);
+            GDN2_COPY_STEP(n + 1, fr0, gm0);
+        }
+        if (n < n1) GDN2_COPY_STEP(n, fr1, gm1);
+#undef GDN2_COPY_STEP
+    } else {
+        const float *init = nullptr;
+        if (MODE == 0) init = sp.nseg == 1 ? (a.s0 ? a.s0 + sbase : nullptr) : sp.xs + xbase;
+        else if (!frun && seg == 0 && a.s0) init = a.s0 + sbase;
 #pragma unroll
         for (int it = 0; it < 8; ++it)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int c = 16 * it + 4 * lg + e, v = 16 * ct + lr;
-                dst[c * D + v] = sacc[it][e];
+                sacc[it][e] = init ? init[c * D + v] : (frun && c == v) ? 1.f : 0.f;
+                if (MODE == 1 && !frun && seg == 0) sp.xs[xbase + c * D + v] = sacc[it][e];
             }
+        int n = n0;
+        for (; n + 1 < n1; n += 2) {
+            slot_barrier();
+            if (!idle) compute(n, fr0, gm0);
+            slot_barrier();
+            if (!idle) compute(n + 1, fr1, gm1);
+        }
+        if (n < n1) {
+            slot_barrier();
+            if (!idle) compute(n, fr0, gm0);
+        }
+        float *dst = nullptr;
+        if (idle) dst = nullptr;
+        else if (MODE == 0) dst = (seg == sp.nseg - 1 && a.s_out) ? a.s_out + sbase : nullptr;
+        else dst = frun ? sp.fs + xbase : sp.xs + xbase + D * D;  // F[seg], X[seg+1]
+        if (dst) {
+#pragma unroll
+            for (int it = 0; it < 8; ++it)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 16 * it + 4 * lg + e, v = 16 * ct + lr;
+                    dst[c * D + v] = sacc[it][e];
+                }
+        }
     }
 }
 

@@ -166,6 +166,40 @@ def make_inputs(w: Workload, seed: int | None = None, wid: int | None = None) ->
     return out
 
 
+def make_raw_inputs(w: Workload, seed: int | None = None, wid: int | None = None) -> dict:
+    """The same draws as ``make_inputs`` before any input preparation: q, k
+    ~ N(0, 1) NOT normalised, and the gate logits x_a, x_b, x_w themselves,
+    rounded to bf16 (bits in ``*_bf16``, exact values as fp32 arrays).
+
+    Returns q, k, v (+ ``_bf16`` bits), ``x_decay``, ``x_erase``, ``x_write``
+    (None when tied) shaped [B,T,H,dk] or [B,T,H] (+ ``_bf16`` bits), and S0.
+    """
+    if seed is None:
+        seed = BASE_SEED + (wid if wid is not None else 0)
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    q64 = rng.normal(0.0, 1.0, size=(B, T, H, dk))
+    k64 = rng.normal(0.0, 1.0, size=(B, T, H, dk))
+    v64 = rng.normal(0.0, 1.0, size=(B, T, H, dv))
+    x_a, x_b, x_w = _gates(rng, (B, T, H), dk, w.gates)
+    s0 = None
+    if w.s0_std > 0.0:
+        s0 = rng.normal(0.0, w.s0_std, size=(B, H, dk, dv)).astype(np.float32)
+    out = {}
+    for name, x in (("q", q64), ("k", k64), ("v", v64)):
+        c = _cast_qkv(x, w.qkv_dtype)
+        out[name] = c["values"]
+        out[name + "_bf16"] = c["bf16_bits"]
+    for name, x in (("x_decay", x_a), ("x_erase", x_b), ("x_write", None if w.tied else x_w)):
+        if x is None:
+            out[name], out[name + "_bf16"] = None, None
+            continue
+        vals, bits = round_to_bf16(x.astype(np.float32))
+        out[name], out[name + "_bf16"] = vals, bits
+    out["S0"] = s0
+    return out
+
+
 def make_decode_state(w: Workload, seed: int | None = None) -> np.ndarray:
     """Initial fp32 state [N,H,dk,dv] ~ N(0, s0_std) for a decode workload."""
     if seed is None:

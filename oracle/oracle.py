@@ -127,6 +127,32 @@ def gdn2_forward(q, k, v, log_decay, erase, write=None, S0=None, q_scale=1.0,
     return o, S_T
 
 
+def prepare_inputs(q, k, x_decay, x_erase, x_write=None, qk_l2norm=True):
+    """The input preparation that precedes the mixer, in fp64: the decay gate
+    a = exp(-softplus(x_a)) in (0, 1) (log a = -log(1 + e^x_a)), the erase
+    and write gates b = sigmoid(x_b), w = sigmoid(x_w) in (0, 1), and q, k
+    divided by their L2 norm over the key channels of each token-head (a
+    zero vector stays zero).  Returns (q, k, log_decay, erase, write)."""
+    def l2(x):
+        x = np.asarray(x, dtype=np.float64)
+        n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+        return np.where(n > 0, x / np.where(n > 0, n, 1.0), 0.0)
+
+    sig = lambda x: None if x is None else 1.0 / (1.0 + np.exp(-np.asarray(x, dtype=np.float64)))
+    la = -np.logaddexp(0.0, np.asarray(x_decay, dtype=np.float64))
+    if qk_l2norm:
+        q, k = l2(q), l2(k)
+    return q, k, la, sig(x_erase), sig(x_write)
+
+
+def gdn2_forward_raw(q, k, v, x_decay, x_erase, x_write=None, S0=None, q_scale=1.0, qk_l2norm=True,
+                     threads: int | None = None, value_write=False):
+    """``gdn2_forward`` on raw inputs: gate logits and (with qk_l2norm)
+    unnormalised q, k, prepared by ``prepare_inputs`` first."""
+    q, k, la, b, w = prepare_inputs(q, k, x_decay, x_erase, x_write, qk_l2norm)
+    return gdn2_forward(q, k, v, la, b, w, S0, q_scale=q_scale, threads=threads, value_write=value_write)
+
+
 def gdn2_step(q, k, v, log_decay, erase, write, state):
     """One recurrent step for N sequences: inputs [N,H,d], gates [N,H,dk] or
     [N,H]; state [N,H,dk,dv].  Returns (o [N,H,dv], new state)."""

@@ -33,7 +33,7 @@ class Gdn2Desc(ctypes.Structure):
         ("qkv_dtype", ctypes.c_int32), ("decay_kind", ctypes.c_int32),
         ("erase_kind", ctypes.c_int32), ("write_kind", ctypes.c_int32),
         ("tie_write_to_erase", ctypes.c_int32), ("q_scale", ctypes.c_float),
-        ("form", ctypes.c_int32),
+        ("form", ctypes.c_int32), ("gate_logits", ctypes.c_int32), ("qk_l2norm", ctypes.c_int32),
     ]
 
 
@@ -96,9 +96,11 @@ def abi_version() -> int:
 
 def make_desc(batch, seqlen, heads, dk, dv, chunk=64, qkv_dtype=GDN2_BF16,
               decay_kind=GDN2_GATE_KEY, erase_kind=GDN2_GATE_KEY, write_kind=GDN2_GATE_KEY,
-              tied=False, q_scale=1.0, form=GDN2_FORM_KEY) -> Gdn2Desc:
+              tied=False, q_scale=1.0, form=GDN2_FORM_KEY, gate_logits=False,
+              qk_l2norm=False) -> Gdn2Desc:
     return Gdn2Desc(batch, seqlen, heads, dk, dv, chunk, qkv_dtype, decay_kind, erase_kind,
-                    write_kind, 1 if tied else 0, q_scale, form)
+                    write_kind, 1 if tied else 0, q_scale, form, int(bool(gate_logits)),
+                    int(bool(qk_l2norm)))
 
 
 def _ptr(t):
@@ -134,7 +136,7 @@ def _gate_kind(g, tok_shape, dk, name):
 
 
 def _desc_for(q, k, v, log_decay, erase, write, tok_shape, batch, seqlen, heads, chunk, q_scale,
-              value_write=False):
+              value_write=False, qk_l2norm=False):
     import torch
     dk, dv = k.shape[-1], v.shape[-1]
     dev = k.device
@@ -144,19 +146,22 @@ def _desc_for(q, k, v, log_decay, erase, write, tok_shape, batch, seqlen, heads,
         _check(t, n, tuple(tok_shape) + (d,), (k.dtype,), dev)
     la_kind, la_shape = _gate_kind(log_decay, tok_shape, dk, "log_decay")
     eb_kind, eb_shape = _gate_kind(erase, tok_shape, dk, "erase")
-    _check(log_decay, "log_decay", la_shape, (torch.float32,), dev)
-    _check(erase, "erase", eb_shape, (torch.float32,), dev)
+    # fp32 gates, or bf16 logits that the kernels activate
+    gate_logits = log_decay.dtype == torch.bfloat16
+    gdt = (torch.bfloat16,) if gate_logits else (torch.float32,)
+    _check(log_decay, "log_decay", la_shape, gdt, dev)
+    _check(erase, "erase", eb_shape, gdt, dev)
     wr_kind = eb_kind
     if value_write and write is None:
         raise ValueError("the value-write form needs a write gate")
     if write is not None:
         # the value-write form gates the value channels
         wr_kind, wr_shape = _gate_kind(write, tok_shape, dv if value_write else dk, "write")
-        _check(write, "write", wr_shape, (torch.float32,), dev)
+        _check(write, "write", wr_shape, gdt, dev)
     return make_desc(batch, seqlen, heads, dk, dv, chunk,
                      GDN2_BF16 if k.dtype == torch.bfloat16 else GDN2_F32,
                      la_kind, eb_kind, wr_kind, write is None, q_scale,
-                     GDN2_FORM_VALUE_WRITE if value_write else GDN2_FORM_KEY)
+                     GDN2_FORM_VALUE_WRITE if value_write else GDN2_FORM_KEY, gate_logits, qk_l2norm)
 
 
 def chunk_fwd_workspace(desc: Gdn2Desc) -> int:
@@ -168,7 +173,8 @@ def chunk_fwd_workspace(desc: Gdn2Desc) -> int:
 
 
 def chunk_fwd(q, k, v, log_decay, erase, write=None, state0=None, chunk=64, q_scale=1.0,
-              out=None, state_out=None, return_state=True, workspace=True, value_write=False):
+              out=None, state_out=None, return_state=True, workspace=True, value_write=False,
+              qk_l2norm=False):
     """Chunkwise GDN-2 forward on the GPU.
 
     q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32, one dtype); gates fp32
@@ -177,13 +183,16 @@ def chunk_fwd(q, k, v, log_decay, erase, write=None, state0=None, chunk=64, q_sc
     the request has a two-pass kernel, False runs in one pass, or a uint8
     device tensor of at least chunk_fwd_workspace() bytes to use.
     ``value_write``: the gist.science form of the update (write gate
-    [B,T,H,dv] or [B,T,H], required).
+    [B,T,H,dv] or [B,T,H], required).  Gates given as bfloat16 tensors are
+    raw logits (log a = -softplus, b and w = sigmoid, applied in-kernel);
+    ``qk_l2norm`` normalises q and k per token-head in-kernel.
     Returns (o [B,T,H,dv] fp32, final state or None).
     """
     import torch
     B, T, H, dk = k.shape
     dv = v.shape[-1]
-    desc = _desc_for(q, k, v, log_decay, erase, write, (B, T, H), B, T, H, chunk, q_scale, value_write)
+    desc = _desc_for(q, k, v, log_decay, erase, write, (B, T, H), B, T, H, chunk, q_scale, value_write,
+                     qk_l2norm)
     dev = k.device
     if state0 is not None:
         _check(state0, "state0", (B, H, dk, dv), (torch.float32,), dev)
@@ -259,7 +268,8 @@ def chunk_bwd(q, k, v, log_decay, erase, write, state0, d_o, d_state=None, chunk
     return g
 
 
-def recurrent_step(q, k, v, log_decay, erase, write, state, q_scale=1.0, out=None, value_write=False):
+def recurrent_step(q, k, v, log_decay, erase, write, state, q_scale=1.0, out=None, value_write=False,
+                   qk_l2norm=False):
     """One decode step for N sequences; updates ``state`` [N,H,dk,dv] in place.
 
     q, k [N,H,dk], v [N,H,dv]; gates [N,H,dk] or [N,H]; write None = tied.
@@ -268,7 +278,7 @@ def recurrent_step(q, k, v, log_decay, erase, write, state, q_scale=1.0, out=Non
     import torch
     N, H, dk = k.shape
     dv = v.shape[-1]
-    desc = _desc_for(q, k, v, log_decay, erase, write, (N, H), N, 1, H, 64, q_scale, value_write)
+    desc = _desc_for(q, k, v, log_decay, erase, write, (N, H), N, 1, H, 64, q_scale, value_write, qk_l2norm)
     _check(state, "state", (N, H, dk, dv), (torch.float32,), k.device)
     if out is None:
         out = torch.empty((N, H, dv), dtype=torch.float32, device=k.device)

@@ -77,10 +77,11 @@ Sizes sizes_of(const gdn2_desc *d, int64_t T) {
     s.tok = d->batch * T * d->heads;
     s.qk = s.tok * d->dk * esz;
     s.v = s.tok * d->dv * esz;
-    s.la = s.tok * (d->decay_kind == GDN2_GATE_KEY ? d->dk : 1) * 4;
-    s.eb = s.tok * (d->erase_kind == GDN2_GATE_KEY ? d->dk : 1) * 4;
+    const int64_t gsz = d->gate_logits ? 2 : 4;  // bf16 logits or fp32 gates
+    s.la = s.tok * (d->decay_kind == GDN2_GATE_KEY ? d->dk : 1) * gsz;
+    s.eb = s.tok * (d->erase_kind == GDN2_GATE_KEY ? d->dk : 1) * gsz;
     const int64_t wch = d->form == GDN2_FORM_VALUE_WRITE ? d->dv : d->dk;  // channels of the write gate
-    s.wr = d->tie_write_to_erase ? 0 : s.tok * (d->write_kind == GDN2_GATE_KEY ? wch : 1) * 4;
+    s.wr = d->tie_write_to_erase ? 0 : s.tok * (d->write_kind == GDN2_GATE_KEY ? wch : 1) * gsz;
     s.o = s.tok * d->dv * 4;
     s.st = d->batch * d->heads * d->dk * d->dv * 4;
     return s;
@@ -104,6 +105,8 @@ ChunkArgs args_of(const gdn2_desc *d, const void *q, const void *k, const void *
     a.wr_key = d->tie_write_to_erase ? a.eb_key : d->write_kind == GDN2_GATE_KEY;
     a.q_scale = d->q_scale;
     a.value_write = d->form == GDN2_FORM_VALUE_WRITE;
+    a.gate_logits = d->gate_logits != 0;
+    a.qk_norm = d->qk_l2norm != 0;
     return a;
 }
 
@@ -199,7 +202,8 @@ gdn2_status gdn2_chunk_bwd_workspace(const gdn2_desc *desc, size_t *bytes) {
     if (st != GDN2_OK) return st;
     if (desc->chunk != 16 && desc->chunk != 32 && desc->chunk != 64) return GDN2_ERR_UNSUPPORTED;
     if (!gdn2::chunk_bwd_chunk(desc->dk, desc->dv, static_cast<int>(desc->chunk))) return GDN2_ERR_UNSUPPORTED;
-    if (desc->form != GDN2_FORM_KEY) return GDN2_ERR_UNSUPPORTED;  // no backward of the value-write form
+    // no backward of the value-write form or of fused input preparation
+    if (desc->form != GDN2_FORM_KEY || desc->gate_logits || desc->qk_l2norm) return GDN2_ERR_UNSUPPORTED;
     *bytes = gdn2::chunk_bwd_workspace(desc->batch, desc->heads, desc->seqlen, desc->dk, desc->dv,
                                        static_cast<int>(desc->chunk));
     return GDN2_OK;
@@ -287,6 +291,8 @@ gdn2_status gdn2_recurrent_step(const gdn2_desc *d, const void *q, const void *k
     a.wr_key = d->tie_write_to_erase ? a.eb_key : d->write_kind == GDN2_GATE_KEY;
     a.q_scale = d->q_scale;
     a.value_write = d->form == GDN2_FORM_VALUE_WRITE;
+    a.gate_logits = d->gate_logits != 0;
+    a.qk_norm = d->qk_l2norm != 0;
     return hip_status(gdn2::launch_step(a, static_cast<hipStream_t>(stream)));
 }
 

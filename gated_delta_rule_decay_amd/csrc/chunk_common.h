@@ -77,6 +77,24 @@ __device__ __forceinline__ f4 gate4(const GateRow<false> &g, int i) {
     return f4{g.x[i], g.x[i], g.x[i], g.x[i]};
 }
 
+
+// With bf16 gate logits, a gate row holds the raw bits (per channel: four
+// logits in the first two words; per head: the logit in the low half) and
+// is activated where it is used (act 0: -softplus, the log-decay; act 1:
+// sigmoid).
+__device__ __forceinline__ float act_gate(float x, int act) { return act == 0 ? neg_softplus(x) : sigmoid_gate(x); }
+__device__ __forceinline__ f4 gate4a(const GateRow<true> &g, int i, int logits, int act) {
+    if (!logits) return g.x[i];
+    const uint32_t lo = __float_as_uint(g.x[i][0]), hi = __float_as_uint(g.x[i][1]);
+    return f4{act_gate(__uint_as_float(lo << 16), act), act_gate(__uint_as_float(lo & 0xffff0000u), act),
+              act_gate(__uint_as_float(hi << 16), act), act_gate(__uint_as_float(hi & 0xffff0000u), act)};
+}
+__device__ __forceinline__ f4 gate4a(const GateRow<false> &g, int i, int logits, int act) {
+    if (!logits) return gate4(g, i);
+    const float x = act_gate(__uint_as_float(__float_as_uint(g.x[i]) << 16), act);
+    return f4{x, x, x, x};
+}
+
 __device__ __forceinline__ f4 bf16x4_to_f4(uint2 p) {
     f4 r;
     r[0] = __uint_as_float(p.x << 16);
@@ -205,13 +223,15 @@ __device__ __forceinline__ void load_kqg(Raw<KEYG, NV> &R, const ChunkArgs &a, i
 
 // Running log2-decay of my RPS rows (relative to the start of my segment);
 // the segment total goes to segtot[seg].
+// With logits, rows past the end of the sequence (which load as zero
+// logits, i.e. a real decay of 1/2) are given no decay: nvalid = T - t0.
 template <typename SM, bool KEYG, int NV>
 __device__ __forceinline__ void segment_cumsum(SM &S, const Raw<KEYG, NV> &R, f4 (&g)[RPS], int seg,
-                                               int cq) {
+                                               int cq, int logits = 0, int64_t nvalid = C) {
     f4 run = splat(0.f);
 #pragma unroll
     for (int i = 0; i < RPS; ++i) {
-        run += gate4(R.la, i) * LOG2E;
+        if (!logits || seg * RPS + i < nvalid) run += gate4a(R.la, i, logits, 0) * LOG2E;
         g[i] = run;
     }
     *reinterpret_cast<f4 *>(&S.segtot[seg][4 * cq]) = run;
@@ -247,10 +267,12 @@ __device__ __forceinline__ void chunk_tables(SM &S, int c) {
 // operand leaves the fast range.
 // With VW (the value-write form: erase gate on the read, erase and write
 // along k; TIED holds) the row operand is b k and the column operand k.
+// With `logits` the gates are activated here; with `qknorm` every row of k
+// and q is divided by its L2 norm (the 32 lanes of a segment hold a row).
 template <typename SM, bool TIED, bool KEYG, int NV, bool VW = false>
 __device__ __forceinline__ void factored_operands(SM &S, const Raw<KEYG, NV> &R, f4 (&g)[RPS],
                                                   f4 (&khf)[RPS], f4 (&qhf)[RPS], f4 &egm, int seg,
-                                                  int cq, float qs) {
+                                                  int cq, float qs, int logits = 0, int qknorm = 0) {
     static_assert(!VW || TIED, "the value-write form erases and writes along the same vector");
     const int blk = seg / 4;  // 16-row block of my rows
     const f4 base = *reinterpret_cast<const f4 *>(&S.segtot[seg][4 * cq]);
@@ -269,13 +291,26 @@ __device__ __forceinline__ void factored_operands(SM &S, const Raw<KEYG, NV> &R,
             e1[j] = __builtin_amdgcn_exp2f(x[j]);
             e2[j] = __builtin_amdgcn_exp2f(-x[j]);
         }
-        const f4 kraw = bf16x4_to_f4(R.k[i]);
-        const f4 kf = VW ? gate4(R.eb, i) * kraw : kraw;  // the read key
-        const f4 qf = bf16x4_to_f4(R.q[i]) * qs;
+        f4 kraw = bf16x4_to_f4(R.k[i]);
+        f4 qraw = bf16x4_to_f4(R.q[i]);
+        if (qknorm) {
+            float sk = kraw[0] * kraw[0] + kraw[1] * kraw[1] + kraw[2] * kraw[2] + kraw[3] * kraw[3];
+            float sq = qraw[0] * qraw[0] + qraw[1] * qraw[1] + qraw[2] * qraw[2] + qraw[3] * qraw[3];
+#pragma unroll
+            for (int o = 16; o >= 1; o >>= 1) {
+                sk += __shfl_xor(sk, o);
+                sq += __shfl_xor(sq, o);
+            }
+            kraw = kraw * (sk > 0.f ? rsqrtf(sk) : 0.f);
+            qraw = qraw * (sq > 0.f ? rsqrtf(sq) : 0.f);
+        }
+        const f4 eb = gate4a(R.eb, i, logits, 1);
+        const f4 kf = VW ? eb * kraw : kraw;  // the read key
+        const f4 qf = qraw * qs;
         khf[i] = kf * e1;
         qhf[i] = qf * e1;
-        const f4 ev = VW ? kraw * e2 : gate4(R.eb, i) * kraw * e2;
-        const f4 uv = TIED ? ev : gate4(R.wr, i) * kf * e2;
+        const f4 ev = VW ? kraw * e2 : eb * kraw * e2;
+        const f4 uv = TIED ? ev : gate4a(R.wr, i, logits, 1) * kf * e2;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const float m = fmaxf(fmaxf(fabsf(khf[i][j]), fabsf(qhf[i][j])), fmaxf(fabsf(ev[j]), fabsf(uv[j])));

@@ -101,33 +101,40 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
                 if (j < ncol) hs[static_cast<int64_t>(c) * dv + col0 + j] = S[idx];
             }
         }
-        // 1. stage the chunk: keys, queries, raw log-decay, e = b*k, u = w*k, values
+        // 1. stage the chunk: keys, queries, raw log-decay, e = b*k, u = w*k, values.
+        //    With in-kernel q/k normalisation the raw rows and the gates are
+        //    staged first and combined once the row norms are known.
+        const bool norm = a.qk_norm;
         for (int idx = tid; idx < Cg * dk; idx += kThreads) {
             const int r = idx / dk, c = idx % dk;
             const int64_t t = t0 + r;
-            float kv = 0.f, qv = 0.f, la = 0.f, e = 0.f, u = 0.f;
+            float kv = 0.f, qv = 0.f, la = 0.f, bb = 0.f, ww = 0.f;
             if (t < T) {
                 const int64_t row = (b * T + t) * H + h;
                 kv = load_qkv(a.k, row * dk + c, a.bf16);
-                qv = a.q_scale * load_qkv(a.q, row * dk + c, a.bf16);
-                la = load_gate(a.la, a.la_key, row, dk, c);
-                const float bb = load_gate(a.eb, a.eb_key, row, dk, c);
-                if (a.value_write) {
-                    // the read key is b .* k; erase and write run along k
-                    e = u = kv;
-                    kv *= bb;
-                } else {
-                    const float ww = a.wr ? load_gate(a.wr, a.wr_key, row, dk, c) : bb;
-                    e = bb * kv;
-                    u = ww * kv;
-                }
+                qv = load_qkv(a.q, row * dk + c, a.bf16);
+                la = load_gate_x(a.la, a.la_key, row, dk, c, a.gate_logits, 0);
+                bb = load_gate_x(a.eb, a.eb_key, row, dk, c, a.gate_logits, 1);
+                ww = a.value_write ? 0.f : a.wr ? load_gate_x(a.wr, a.wr_key, row, dk, c, a.gate_logits, 1) : bb;
             }
             const int li = r * KS + c;
-            Kf[li] = kv;
-            Qf[li] = qv;
             G[li] = la;
-            Eb[li] = e;
-            Uw[li] = u;
+            if (norm) {
+                Kf[li] = kv;
+                Qf[li] = qv;
+                Eb[li] = bb;
+                Uw[li] = ww;
+            } else {
+                Qf[li] = a.q_scale * qv;
+                if (a.value_write) {  // the read key is b .* k; erase and write run along k
+                    Kf[li] = bb * kv;
+                    Eb[li] = Uw[li] = kv;
+                } else {
+                    Kf[li] = kv;
+                    Eb[li] = bb * kv;
+                    Uw[li] = ww * kv;
+                }
+            }
         }
         for (int idx = tid; idx < Cg * DVT; idx += kThreads) {
             const int r = idx / DVT, j = idx % DVT;
@@ -136,9 +143,33 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
             if (t < T && j < ncol) {
                 const int64_t row = (b * T + t) * H + h;
                 vv = load_qkv(a.v, row * dv + col0 + j, a.bf16);
-                if (a.value_write) vv *= load_gate(a.wr, a.wr_key, row, dv, col0 + j);  // w .* v
+                if (a.value_write) vv *= load_gate_x(a.wr, a.wr_key, row, dv, col0 + j, a.gate_logits, 1);  // w .* v
             }
             V[idx] = vv;
+        }
+        if (norm) {
+            __syncthreads();
+            float *inv = A;  // 1 / ||k_r||, then 1 / ||q_r|| (A is written later)
+            for (int i = tid; i < 2 * Cg; i += kThreads) {
+                const float *x = (i < Cg ? Kf : Qf) + (i % Cg) * KS;
+                float ss = 0.f;
+                for (int c = 0; c < dk; ++c) ss += x[c] * x[c];
+                inv[i] = ss > 0.f ? rsqrtf(ss) : 0.f;
+            }
+            __syncthreads();
+            for (int idx = tid; idx < Cg * dk; idx += kThreads) {
+                const int r = idx / dk, li = r * KS + idx % dk;
+                const float kv = Kf[li] * inv[r], bb = Eb[li], ww = Uw[li];
+                Qf[li] = a.q_scale * Qf[li] * inv[Cg + r];
+                if (a.value_write) {
+                    Kf[li] = bb * kv;
+                    Eb[li] = Uw[li] = kv;
+                } else {
+                    Kf[li] = kv;
+                    Eb[li] = bb * kv;
+                    Uw[li] = ww * kv;
+                }
+            }
         }
         __syncthreads();
         // 2. inclusive cumulative log-decay per key channel (padded rows add 0)

@@ -421,7 +421,7 @@ bool chunk_mfma_supported(const ChunkArgs &a) {
     // every present gate of one kind (all per key channel or all per head)
     const bool tied = a.wr == nullptr;
     const bool same = a.la_key == a.eb_key && (tied || a.wr_key == a.eb_key);
-    return a.bf16 && a.dk == D && a.dv == D && a.C == C && same && !a.value_write &&
+    return a.bf16 && a.dk == D && a.dv == D && a.C == C && same && !a.value_write && !a.gate_logits && !a.qk_norm &&
            a.H * D * 4 * C < (int64_t(1) << 31);
 }
 

@@ -122,6 +122,20 @@ __device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, c
     const int gw = KEYG ? D : 1;
     const int rowk = static_cast<int>(a.H) * D, rowg = static_cast<int>(a.H) * gw;
     auto gates = [&](GateRow<KEYG> &x, const float *src) {
+        if (a.gate_logits) {  // bf16 logits: raw bits, activated where used
+            const auto rs = chain_rsrc(src, a, b, h, t0, gw, 2, 0);
+#pragma unroll
+            for (int i = 0; i < RPS; ++i) {
+                const int r = seg * RPS + i;
+                if constexpr (KEYG) {
+                    const uint2 u = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs, (r * rowg + 4 * cq) * 2, 0, 0));
+                    x.x[i] = f4{__uint_as_float(u.x), __uint_as_float(u.y), 0.f, 0.f};
+                } else {
+                    x.x[i] = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, r * rowg * 2, 0, 0)));
+                }
+            }
+            return;
+        }
         const auto rs = chain_rsrc(src, a, b, h, t0, gw, 4, 0);
 #pragma unroll
         for (int i = 0; i < RPS; ++i) {
@@ -144,14 +158,23 @@ __device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, c
         if constexpr (VW) {
             // write gate of my two tokens' 8 value columns (per channel) or
             // of my two tokens (per head), into the unused wr registers
-            const auto rw = chain_rsrc(a.wr, a, b, h, t0, gw, 4, 0);
+            // (bf16 logits: the 8 columns of token i in wr.x[2i])
+            const int es = a.gate_logits ? 2 : 4;
+            const auto rw = chain_rsrc(a.wr, a, b, h, t0, gw, es, 0);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 if constexpr (KEYG) {
+                    if (a.gate_logits) {
+                        R.wr.x[2 * i] = __builtin_bit_cast(
+                            f4, __builtin_amdgcn_raw_buffer_load_b128(rw, ((2 * tp + i) * rowg + 8 * piece) * 2, 0, 0));
+                    } else {
 #pragma unroll
-                    for (int hh = 0; hh < 2; ++hh)
-                        R.wr.x[2 * i + hh] = __builtin_bit_cast(
-                            f4, __builtin_amdgcn_raw_buffer_load_b128(rw, ((2 * tp + i) * rowg + 8 * piece + 4 * hh) * 4, 0, 0));
+                        for (int hh = 0; hh < 2; ++hh)
+                            R.wr.x[2 * i + hh] = __builtin_bit_cast(
+                                f4, __builtin_amdgcn_raw_buffer_load_b128(rw, ((2 * tp + i) * rowg + 8 * piece + 4 * hh) * 4, 0, 0));
+                    }
+                } else if (a.gate_logits) {
+                    R.wr.x[i] = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rw, (2 * tp + i) * rowg * 2, 0, 0)));
                 } else {
                     R.wr.x[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, (2 * tp + i) * rowg * 4, 0, 0));
                 }
@@ -275,9 +298,17 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             const uint32_t r1[4] = {R.v[1].x, R.v[1].y, R.v[1].z, R.v[1].w};
             // the value-write form writes w .* v: gate of token i, column 2e + s
             auto wg = [&](int i, int e, int s) -> float {
-                if constexpr (!VW) return 1.f;
-                else if constexpr (KEYG) return R.wr.x[2 * i + (2 * e + s) / 4][(2 * e + s) % 4];
-                else return R.wr.x[i];
+                if constexpr (!VW) {
+                    return 1.f;
+                } else if constexpr (KEYG) {
+                    if (a.gate_logits) {  // column 2e+s of token i: half s of word e
+                        const uint32_t u = __float_as_uint(R.wr.x[2 * i][e]);
+                        return sigmoid_gate(__uint_as_float(s ? (u & 0xffff0000u) : (u << 16)));
+                    }
+                    return R.wr.x[2 * i + (2 * e + s) / 4][(2 * e + s) % 4];
+                } else {
+                    return a.gate_logits ? sigmoid_gate(__uint_as_float(__float_as_uint(R.wr.x[i]) << 16)) : R.wr.x[i];
+                }
             };
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -291,14 +322,15 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             }
         }
         f4 g[RPS];
-        segment_cumsum(S, R, g, seg, cq);
+        segment_cumsum(S, R, g, seg, cq, a.gate_logits, a.T - task_pos(task, nc, static_cast<int>(a.H)).t0);
         __syncthreads();
         if (tid < D) chunk_tables(S, tid);
         __syncthreads();
 
         // ---- factored fp16 Gram operands -------------------------------------
         f4 khf[RPS], qhf[RPS], egm;
-        factored_operands<PrepSmem, TIED, KEYG, 2, VW>(S, R, g, khf, qhf, egm, seg, cq, a.q_scale);
+        factored_operands<PrepSmem, TIED, KEYG, 2, VW>(S, R, g, khf, qhf, egm, seg, cq, a.q_scale, a.gate_logits,
+                                                       a.qk_norm);
         const int64_t next = task + gridDim.x;  // prefetched in four parts below
         const TaskPos pn = task_pos(next < ntask ? next : task, nc, static_cast<int>(a.H));
         if (next < ntask) load_part<0, TIED, KEYG, VW>(R, a, pn, tid);
@@ -498,6 +530,80 @@ constexpr int SEG_MIN = 16;   // fewest chunks per segment
 constexpr int SEG_WG = 256;   // scan workgroups aimed at when chains are few
 
 constexpr int scan_threads(int mode) { return 64 * (SCAN_P + (mode ? 2 : 1) * SCAN_W); }
+
+// The exact fp32 token recurrence of one chunk on one wave's 16 state
+// columns, from the raw inputs (the fallback when a chunk leaves the fp16
+// range; the columns of F drop the write term).  Kept out of line: its
+// registers do not burden the scan's fast path.
+template <bool TIED, bool KEYG, bool VW, bool WITH_O>
+__device__ __noinline__ void exact_chunk(ChunkArgs a, f4 *sacc, int64_t b, int64_t h, int64_t t0, int ct, int lr,
+                                         int lg, bool frun) {
+    const uint16_t *kp = static_cast<const uint16_t *>(a.k);
+    const uint16_t *qp = static_cast<const uint16_t *>(a.q);
+    const uint16_t *vp = static_cast<const uint16_t *>(a.v);
+    for (int r = 0; r < C && t0 + r < a.T; ++r) {
+        const int64_t row = (b * a.T + t0 + r) * a.H + h;
+        // gates of channel c of this token (per channel or per head;
+        // bf16 logits activated here)
+        auto gate = [&](const float *g, int c, int act) {
+            return load_gate_x(g, KEYG, row, D, c, a.gate_logits, act);
+        };
+        // 1 / ||k||, 1 / ||q|| of this token when normalised in the kernel
+        float ik = 1.f, iq = 1.f;
+        if (a.qk_norm) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int it = 0; it < 8; ++it)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = 16 * it + 4 * lg + e;
+                    const float kc = bf16_to_f32(kp[row * D + c]), qc = bf16_to_f32(qp[row * D + c]);
+                    sk += kc * kc;
+                    sq += qc * qc;
+                }
+            sk += __shfl_xor(sk, 16);
+            sk += __shfl_xor(sk, 32);
+            sq += __shfl_xor(sq, 16);
+            sq += __shfl_xor(sq, 32);
+            ik = sk > 0.f ? rsqrtf(sk) : 0.f;
+            iq = sq > 0.f ? rsqrtf(sq) : 0.f;
+        }
+        float m = 0.f, o = 0.f;
+        // decay, then the erase read m = k^T S_bar (the value-write
+        // form reads along b .* k)
+#pragma unroll
+        for (int it = 0; it < 8; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 16 * it + 4 * lg + e;
+                sacc[it][e] *= expf(gate(a.la, c, 0));
+                const float kc = ik * bf16_to_f32(kp[row * D + c]);
+                m += (VW ? gate(a.eb, c, 1) * kc : kc) * sacc[it][e];
+            }
+        m += __shfl_xor(m, 16);
+        m += __shfl_xor(m, 32);
+        float vv = frun ? 0.f : bf16_to_f32(vp[row * D + 16 * ct + lr]);
+        if (VW) vv *= gate(a.wr, 16 * ct + lr, 1);
+        // erase and write, then the read o = S^T q
+#pragma unroll
+        for (int it = 0; it < 8; ++it)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = 16 * it + 4 * lg + e;
+                const float kc = ik * bf16_to_f32(kp[row * D + c]);
+                const float bb = gate(a.eb, c, 1);
+                const float ec = VW ? kc : bb * kc;
+                const float uc = VW ? kc : (TIED ? bb : gate(a.wr, c, 1)) * kc;
+                sacc[it][e] = sacc[it][e] - ec * m + uc * vv;
+                if (WITH_O) o += a.q_scale * iq * bf16_to_f32(qp[row * D + c]) * sacc[it][e];
+            }
+        if (WITH_O) {
+            o += __shfl_xor(o, 16);
+            o += __shfl_xor(o, 32);
+            if (lg == 0) a.o[row * D + 16 * ct + lr] = o;
+        }
+    }
+}
 
 // The workgroup barrier that hands a slot over.  The empty asm statements
 // keep the compiler from moving LDS accesses across it (the barrier
@@ -710,50 +816,13 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
             }
         } else {
             // exact fp32 token recurrence on the raw inputs of this chunk
-            // (the columns of F drop the write term)
-            const uint16_t *kp = static_cast<const uint16_t *>(a.k);
-            const uint16_t *qp = static_cast<const uint16_t *>(a.q);
-            const uint16_t *vp = static_cast<const uint16_t *>(a.v);
-            const int gw = KEYG ? D : 1;
-            for (int r = 0; r < C && t0 + r < a.T; ++r) {
-                const int64_t row = (b * a.T + t0 + r) * a.H + h;
-                // gates of key channel c of this token (per channel or per head)
-                auto gate = [&](const float *g, int c) { return g[row * gw + (KEYG ? c : 0)]; };
-                float m = 0.f, o = 0.f;
-                // decay, then the erase read m = k^T S_bar (the value-write
-                // form reads along b .* k)
+            // (a separate function: its registers do not burden the fast path)
+            f4 st[8];
 #pragma unroll
-                for (int it = 0; it < 8; ++it)
+            for (int it = 0; it < 8; ++it) st[it] = sacc[it];
+            exact_chunk<TIED, KEYG, VW, WITH_O>(a, st, b, h, t0, ct, lr, lg, frun);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int c = 16 * it + 4 * lg + e;
-                        sacc[it][e] *= expf(gate(a.la, c));
-                        const float kc = bf16_to_f32(kp[row * D + c]);
-                        m += (VW ? gate(a.eb, c) * kc : kc) * sacc[it][e];
-                    }
-                m += __shfl_xor(m, 16);
-                m += __shfl_xor(m, 32);
-                float vv = frun ? 0.f : bf16_to_f32(vp[row * D + 16 * ct + lr]);
-                if (VW) vv *= a.wr[row * gw + (KEYG ? 16 * ct + lr : 0)];
-                // erase and write, then the read o = S^T q
-#pragma unroll
-                for (int it = 0; it < 8; ++it)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int c = 16 * it + 4 * lg + e;
-                        const float kc = bf16_to_f32(kp[row * D + c]);
-                        const float bb = gate(a.eb, c);
-                        const float ec = VW ? kc : bb * kc;
-                        const float uc = VW ? kc : (TIED ? bb : gate(a.wr, c)) * kc;
-                        sacc[it][e] = sacc[it][e] - ec * m + uc * vv;
-                        if (WITH_O) o += a.q_scale * bf16_to_f32(qp[row * D + c]) * sacc[it][e];
-                    }
-                if (WITH_O) {
-                    o += __shfl_xor(o, 16);
-                    o += __shfl_xor(o, 32);
-                    if (lg == 0) a.o[row * D + 16 * ct + lr] = o;
-                }
-            }
+            for (int it = 0; it < 8; ++it) sacc[it] = st[it];
             // leave nothing of this (rare) path outstanding, so that the fast
             // path's precise waits for the prefetched slices survive the merge
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));

@@ -24,4 +24,24 @@ __device__ __forceinline__ float load_gate(const float *g, int per_key, int64_t 
     return per_key ? g[row * dk + c] : g[row];
 }
 
+// Gate activations of the fused input preparation: log a = -softplus(x)
+// (so a = exp(log a) in (0, 1)) and sigmoid(x) for the erase / write gates,
+// with the hardware exp2 / log2 (a few ulp; log(1 + y) for tiny y rounds to
+// 0, an absolute error below 1e-7 in log a).
+__device__ __forceinline__ float neg_softplus(float x) {
+    return -(fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x))));
+}
+__device__ __forceinline__ float sigmoid_gate(float x) { return __fdividef(1.f, 1.f + __expf(-x)); }
+
+// Gate value of token-head `row` at channel c: the fp32 value as stored, or,
+// with `logits`, the activation of the bf16 logit there (act 0: decay,
+// -softplus; act 1: sigmoid).
+__device__ __forceinline__ float load_gate_x(const float *g, int per_key, int64_t row, int64_t width,
+                                             int64_t c, int logits, int act) {
+    if (!logits) return load_gate(g, per_key, row, width, c);
+    const uint16_t *p = reinterpret_cast<const uint16_t *>(g);
+    const float x = bf16_to_f32(per_key ? p[row * width + c] : p[row]);
+    return act == 0 ? neg_softplus(x) : sigmoid_gate(x);
+}
+
 }  // namespace gdn2

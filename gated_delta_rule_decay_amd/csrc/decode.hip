@@ -38,24 +38,14 @@ __global__ void __launch_bounds__(256) step128_kernel(StepArgs a) {
     for (int i = 0; i < kRowsPerLane; ++i)
         S[i] = *reinterpret_cast<const float4 *>(state + (rg + 8 * i) * kD + 4 * cg);
 
+    float kv = 0.f, qv = 0.f, bb = 0.f, ww = 0.f;
     if (tid < kD) {
         const int c = tid;
-        const float kv = load_qkv(a.k, head * kD + c, a.bf16);
-        const float qv = a.q_scale * load_qkv(a.q, head * kD + c, a.bf16);
-        const float la = load_gate(a.la, a.la_key, head, kD, c);
-        const float bb = load_gate(a.eb, a.eb_key, head, kD, c);
-        s_q[c] = qv;
-        s_a[c] = __expf(la);
-        if (a.value_write) {  // read along b .* k, erase and write along k
-            s_k[c] = bb * kv;
-            s_e[c] = kv;
-            s_u[c] = kv;
-        } else {
-            const float ww = a.wr ? load_gate(a.wr, a.wr_key, head, kD, c) : bb;
-            s_k[c] = kv;
-            s_e[c] = bb * kv;
-            s_u[c] = ww * kv;
-        }
+        kv = load_qkv(a.k, head * kD + c, a.bf16);
+        qv = load_qkv(a.q, head * kD + c, a.bf16);
+        s_a[c] = __expf(load_gate_x(a.la, a.la_key, head, kD, c, a.gate_logits, 0));
+        bb = load_gate_x(a.eb, a.eb_key, head, kD, c, a.gate_logits, 1);
+        ww = a.value_write ? 0.f : a.wr ? load_gate_x(a.wr, a.wr_key, head, kD, c, a.gate_logits, 1) : bb;
     }
     float4 v;
     v.x = load_qkv(a.v, head * kD + 4 * cg + 0, a.bf16);
@@ -63,10 +53,41 @@ __global__ void __launch_bounds__(256) step128_kernel(StepArgs a) {
     v.z = load_qkv(a.v, head * kD + 4 * cg + 2, a.bf16);
     v.w = load_qkv(a.v, head * kD + 4 * cg + 3, a.bf16);
     if (a.value_write) {  // w .* v, one factor per value channel (or per head)
-        v.x *= load_gate(a.wr, a.wr_key, head, kD, 4 * cg + 0);
-        v.y *= load_gate(a.wr, a.wr_key, head, kD, 4 * cg + 1);
-        v.z *= load_gate(a.wr, a.wr_key, head, kD, 4 * cg + 2);
-        v.w *= load_gate(a.wr, a.wr_key, head, kD, 4 * cg + 3);
+        v.x *= load_gate_x(a.wr, a.wr_key, head, kD, 4 * cg + 0, a.gate_logits, 1);
+        v.y *= load_gate_x(a.wr, a.wr_key, head, kD, 4 * cg + 1, a.gate_logits, 1);
+        v.z *= load_gate_x(a.wr, a.wr_key, head, kD, 4 * cg + 2, a.gate_logits, 1);
+        v.w *= load_gate_x(a.wr, a.wr_key, head, kD, 4 * cg + 3, a.gate_logits, 1);
+    }
+    if (a.qk_norm) {
+        // waves 0 and 1 hold the 128 channels: squared norms of k and q
+        float sk = kv * kv, sq = qv * qv;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            sk += __shfl_xor(sk, o);
+            sq += __shfl_xor(sq, o);
+        }
+        if (tid < kD && (tid & 63) == 0) {
+            s_red[0][wave][0].x = sk;
+            s_red[0][wave][0].y = sq;
+        }
+        __syncthreads();
+        const float nk = s_red[0][0][0].x + s_red[0][1][0].x, nq = s_red[0][0][0].y + s_red[0][1][0].y;
+        kv *= nk > 0.f ? rsqrtf(nk) : 0.f;
+        qv *= nq > 0.f ? rsqrtf(nq) : 0.f;
+        __syncthreads();  // s_red is reused below
+    }
+    if (tid < kD) {
+        const int c = tid;
+        s_q[c] = a.q_scale * qv;
+        if (a.value_write) {  // read along b .* k, erase and write along k
+            s_k[c] = bb * kv;
+            s_e[c] = kv;
+            s_u[c] = kv;
+        } else {
+            s_k[c] = kv;
+            s_e[c] = bb * kv;
+            s_u[c] = ww * kv;
+        }
     }
     __syncthreads();
 
@@ -128,17 +149,34 @@ __global__ void __launch_bounds__(128) step_general_kernel(StepArgs a) {
     const int64_t head = blockIdx.x;
     const int dk = static_cast<int>(a.dk), dv = static_cast<int>(a.dv);
     const int j = threadIdx.x;
+    float kv = 0.f, qv = 0.f, bb = 0.f, ww = 0.f;
     if (j < dk) {
-        const float kv = load_qkv(a.k, head * dk + j, a.bf16);
-        const float bb = load_gate(a.eb, a.eb_key, head, dk, j);
-        s_q[j] = a.q_scale * load_qkv(a.q, head * dk + j, a.bf16);
-        s_a[j] = expf(load_gate(a.la, a.la_key, head, dk, j));
+        kv = load_qkv(a.k, head * dk + j, a.bf16);
+        qv = load_qkv(a.q, head * dk + j, a.bf16);
+        bb = load_gate_x(a.eb, a.eb_key, head, dk, j, a.gate_logits, 1);
+        ww = a.value_write ? 0.f : a.wr ? load_gate_x(a.wr, a.wr_key, head, dk, j, a.gate_logits, 1) : bb;
+        s_a[j] = expf(load_gate_x(a.la, a.la_key, head, dk, j, a.gate_logits, 0));
+    }
+    if (a.qk_norm) {  // squared norms over the dk channels (lanes past dk hold 0)
+        s_k[j] = kv * kv;
+        s_q[j] = qv * qv;
+        __syncthreads();
+        float nk = 0.f, nq = 0.f;
+        for (int c = 0; c < dk; ++c) {
+            nk += s_k[c];
+            nq += s_q[c];
+        }
+        kv *= nk > 0.f ? rsqrtf(nk) : 0.f;
+        qv *= nq > 0.f ? rsqrtf(nq) : 0.f;
+        __syncthreads();
+    }
+    if (j < dk) {
+        s_q[j] = a.q_scale * qv;
         if (a.value_write) {
             s_k[j] = bb * kv;
             s_e[j] = kv;
             s_u[j] = kv;
         } else {
-            const float ww = a.wr ? load_gate(a.wr, a.wr_key, head, dk, j) : bb;
             s_k[j] = kv;
             s_e[j] = bb * kv;
             s_u[j] = ww * kv;
@@ -150,7 +188,7 @@ __global__ void __launch_bounds__(128) step_general_kernel(StepArgs a) {
     float m = 0.f;
     for (int c = 0; c < dk; ++c) m += s_k[c] * (s_a[c] * col[static_cast<int64_t>(c) * dv]);
     float vj = load_qkv(a.v, head * dv + j, a.bf16);
-    if (a.value_write) vj *= load_gate(a.wr, a.wr_key, head, dv, j);
+    if (a.value_write) vj *= load_gate_x(a.wr, a.wr_key, head, dv, j, a.gate_logits, 1);
     float o = 0.f;
     for (int c = 0; c < dk; ++c) {
         const float sn = s_a[c] * col[static_cast<int64_t>(c) * dv] - s_e[c] * m + s_u[c] * vj;

@@ -21,6 +21,8 @@ struct ChunkArgs {
     float q_scale;
     int value_write;                // 1: erase gate on the read, write gate per value
                                     //    channel ([B,T,H,dv] when wr_key)
+    int gate_logits;                // 1: gates are bf16 logits (-softplus / sigmoid in-kernel)
+    int qk_norm;                    // 1: q, k L2-normalised per token-head in-kernel
 };
 
 struct StepArgs {
@@ -33,6 +35,7 @@ struct StepArgs {
     int la_key, eb_key, wr_key;
     float q_scale;
     int value_write;                // as in ChunkArgs
+    int gate_logits, qk_norm;       // as in ChunkArgs
 };
 
 // General chunked forward: fp32 arithmetic on the vector ALU, any dk, dv in

@@ -48,6 +48,10 @@
  *  - Host-side validation runs before any HIP call: on any status other
  *    than GDN2_OK nothing has been enqueued and no output was touched
  *    (GDN2_ERR_HIP aside, which reports a failed launch).
+ *  - Input preparation may be fused (desc->gate_logits, desc->qk_l2norm):
+ *    the gates then arrive as bf16 logits and q, k unnormalised, and the
+ *    kernels apply the activations and the normalisation as they load them
+ *    (2048 instead of 2816 bytes per token-head for the full GDN-2 forward).
  *  - Preconditions not checked (they would need a device pass): log_decay
  *    finite and <= 0 (decay gate in (0, 1], course slides "Stability"),
  *    erase/write in [0, 1], all values finite.  On the bf16 path derived
@@ -64,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 2
+#define GDN2_ABI_VERSION 3
 
 typedef enum gdn2_status {
     GDN2_OK = 0,
@@ -107,6 +111,14 @@ typedef struct gdn2_desc {
     float q_scale;      /* multiplies q; 1.0 for the plain read */
     int32_t form;       /* gdn2_form; a tied write gate with
                            GDN2_FORM_VALUE_WRITE is GDN2_ERR_SHAPE */
+    int32_t gate_logits; /* nonzero: log_decay, erase and write point at bf16
+                            LOGITS x (same shapes, 2 bytes per element; the
+                            float* parameters are reinterpreted); the kernels
+                            use log a = -softplus(x), b = sigmoid(x),
+                            w = sigmoid(x) */
+    int32_t qk_l2norm;  /* nonzero: q and k are divided by their L2 norm over
+                           the dk channels of each token-head inside the
+                           kernels (a zero vector stays zero), before q_scale */
 } gdn2_desc;
 
 /* GDN2_ABI_VERSION of the loaded library. */

@@ -36,17 +36,18 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn2_abi_version() == 2
+    assert lib.gdn2_abi_version() == 3
     for s in range(8):
         assert lib.gdn2_status_str(s)
     assert lib.gdn2_status_str(0) == b"ok"
 
 
 def test_desc_layout_matches_header():
-    # six int64, five int32, one float, one int32: 76 bytes, padded to 80
-    assert ctypes.sizeof(bd.Gdn2Desc) == 80
+    # six int64, five int32, one float, three int32: 84 bytes, padded to 88
+    assert ctypes.sizeof(bd.Gdn2Desc) == 88
     assert bd.Gdn2Desc.q_scale.offset == 68
     assert bd.Gdn2Desc.form.offset == 72
+    assert bd.Gdn2Desc.gate_logits.offset == 76 and bd.Gdn2Desc.qk_l2norm.offset == 80
 
 
 # Fake, well-separated device addresses for the inputs and outputs.
@@ -253,3 +254,16 @@ def test_value_write_form_checks(lib):
     assert query(lib, good(**vw)) == split_bytes(2, 4, 128)
     n = ctypes.c_size_t(0)
     assert lib.gdn2_chunk_bwd_workspace(ctypes.byref(good(**vw)), ctypes.byref(n)) == 4
+
+
+def test_fused_input_checks(lib):
+    # bf16 logits take 2 bytes per gate element
+    d = good(gate_logits=True)
+    gbytes = 2 * 128 * 4 * 128 * 2
+    assert fwd(lib, d, la=O - gbytes + 256) == 5        # a bf16 gate running into o
+    assert fwd(lib, good(), la=O - gbytes + 256) == 5   # twice as long as fp32: also overlaps
+    # the two-pass kernels cover it; the backward does not
+    assert query(lib, good(gate_logits=True, qk_l2norm=True)) == split_bytes(2, 4, 128)
+    n = ctypes.c_size_t(0)
+    assert lib.gdn2_chunk_bwd_workspace(ctypes.byref(good(qk_l2norm=True)), ctypes.byref(n)) == 4
+    assert lib.gdn2_chunk_bwd_workspace(ctypes.byref(good(gate_logits=True)), ctypes.byref(n)) == 4

@@ -7,7 +7,8 @@ workload (B=8, H=16, T=4096, dk=dv=128, C=64, bf16 q/k/v, fp32 per-channel
 decay/erase/write gates and state, S0 ~ N(0, 0.1)), inputs resident in HBM.
 ``value`` is tokens/s (B*T per step).  The same run also times, each beside
 ``value`` with its own roofline: the single-pass kernel and the value-write
-form on the same inputs, the backward, the long-context workload (B=1,
+form on the same inputs, the forward on raw inputs (bf16 gate logits, q/k
+normalised in-kernel), the backward, the long-context workload (B=1,
 T=65536, two-level scan), the Gated DeltaNet mode (scalar gates, B=4) and
 the recurrent decode step (256 sequences x 16 heads, fp32 state in HBM, in
 place); and the fp64 CPU oracle on the full workload.
@@ -148,6 +149,54 @@ def time_chunk(w, wid, steps, warmup, torch, chunk_fwd, one_pass=False, inp=None
     return inp, ms_step, ms_kernel
 
 
+def fused_bytes(w) -> int:
+    """Algorithmic HBM bytes of one forward with fused input preparation:
+    q, k, v bf16, the gate logits bf16, o fp32, S0 and S_T."""
+    n_gates = 2 if w.tied else 3
+    per_tok = (2 * w.dk + w.dv) * 2 + n_gates * w.dk * 2 + w.dv * 4
+    state = w.B * w.H * w.dk * w.dv * 4
+    return w.B * w.T * w.H * per_tok + (state if w.s0_std > 0 else 0) + state
+
+
+def time_fused(w, torch, chunk_fwd, steps):
+    """Time the forward on raw inputs: bf16 gate logits activated and q, k
+    L2-normalised inside the kernels (same draws as the main workload)."""
+    from gated_delta_rule_decay_amd import binding, synth
+
+    log(f"[bench] generating raw {w.name} inputs")
+    raw = synth.make_raw_inputs(w, wid=2)
+    bf = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = bf(raw["q_bf16"]), bf(raw["k_bf16"]), bf(raw["v_bf16"])
+    xa, xb, xw = bf(raw["x_decay_bf16"]), bf(raw["x_erase_bf16"]), bf(raw["x_write_bf16"])
+    s0 = torch.from_numpy(raw["S0"]).cuda()
+    del raw
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
+    st = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    desc = binding.make_desc(w.B, w.T, w.H, w.dk, w.dv, w.chunk, binding.GDN2_BF16, 1, 1, 1, False,
+                             gate_logits=True, qk_l2norm=True)
+    ws = torch.empty(binding.chunk_fwd_workspace(desc), dtype=torch.uint8, device="cuda")
+    kw = dict(chunk=w.chunk, out=o, state_out=st, workspace=ws, qk_l2norm=True)
+    chunk_fwd(q, k, v, xa, xb, xw, s0, **kw)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {steps} steps of {w.name} with fused input preparation")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        chunk_fwd(q, k, v, xa, xb, xw, s0, **kw)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    kms = ev0.elapsed_time(ev1) / steps
+    return {"workload": f"{w.name} on raw inputs: bf16 gate logits (-softplus / sigmoid in-kernel), "
+                        f"q and k L2-normalised in-kernel",
+            "ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
+            "value": round(w.B * w.T / (ms * 1e-3), 1), "unit": "tokens/s",
+            "roofline": roofline_hbm(fused_bytes(w), kms,
+                                     read_traffic("chunk_fwd_raw_inputs", w.name, source_hash(CHUNK_SOURCES))),
+            "algorithmic_bytes_per_launch": fused_bytes(w)}
+
+
 def bwd_bytes(w) -> int:
     """Algorithmic HBM bytes of one backward call: the forward's inputs, d_o
     and d_S_T read once; dq, dk, dv, the gate gradients and d_S0 written once
@@ -283,6 +332,8 @@ def main():
                                  "roofline": roofline_hbm(chunk_bytes(w), kvw)}
         result["backward"] = time_backward(w, inp, torch, max(2, args.steps // 8))
     del inp
+    if not args.no_extra:
+        result["fused_inputs"] = time_fused(w, torch, chunk_fwd, max(2, args.steps // 4))
 
     if not args.no_extra:
         # long context: one sequence per head, T = 65536 (two-level scan)

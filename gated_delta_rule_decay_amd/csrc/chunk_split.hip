@@ -115,14 +115,15 @@ __device__ __forceinline__ TaskPos task_pos(int64_t task, int nc, int H) {
     return p;
 }
 
-template <int PART, bool TIED, bool KEYG, bool VW = false>
+template <int PART, bool TIED, bool KEYG, bool VW = false, bool RAW = false>
 __device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, const TaskPos &tp0, int tid) {
+    const bool logits = RAW && a.gate_logits;  // bf16 gate logits (fused input preparation)
     const int64_t b = tp0.b, h = tp0.h, t0 = tp0.t0;
     const int seg = tid >> 5, cq = tid & 31;
     const int gw = KEYG ? D : 1;
     const int rowk = static_cast<int>(a.H) * D, rowg = static_cast<int>(a.H) * gw;
     auto gates = [&](GateRow<KEYG> &x, const float *src) {
-        if (a.gate_logits) {  // bf16 logits: raw bits, activated where used
+        if (logits) {  // bf16 logits: raw bits, activated where used
             const auto rs = chain_rsrc(src, a, b, h, t0, gw, 2, 0);
 #pragma unroll
             for (int i = 0; i < RPS; ++i) {
@@ -159,12 +160,12 @@ __device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, c
             // write gate of my two tokens' 8 value columns (per channel) or
             // of my two tokens (per head), into the unused wr registers
             // (bf16 logits: the 8 columns of token i in wr.x[2i])
-            const int es = a.gate_logits ? 2 : 4;
+            const int es = logits ? 2 : 4;
             const auto rw = chain_rsrc(a.wr, a, b, h, t0, gw, es, 0);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 if constexpr (KEYG) {
-                    if (a.gate_logits) {
+                    if (logits) {
                         R.wr.x[2 * i] = __builtin_bit_cast(
                             f4, __builtin_amdgcn_raw_buffer_load_b128(rw, ((2 * tp + i) * rowg + 8 * piece) * 2, 0, 0));
                     } else {
@@ -173,7 +174,7 @@ __device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, c
                             R.wr.x[2 * i + hh] = __builtin_bit_cast(
                                 f4, __builtin_amdgcn_raw_buffer_load_b128(rw, ((2 * tp + i) * rowg + 8 * piece + 4 * hh) * 4, 0, 0));
                     }
-                } else if (a.gate_logits) {
+                } else if (logits) {
                     R.wr.x[i] = __uint_as_float(static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rw, (2 * tp + i) * rowg * 2, 0, 0)));
                 } else {
                     R.wr.x[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rw, (2 * tp + i) * rowg * 4, 0, 0));
@@ -253,8 +254,10 @@ __device__ __forceinline__ bool wq_tiles(const PrepSmem &S, _Float16 *rec, int k
     return big;
 }
 
-template <bool TIED, bool KEYG, bool VW>
+template <bool TIED, bool KEYG, bool VW, bool RAW>
 __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w, int nc) {
+    // RAW: fused input preparation (bf16 gate logits and / or q, k normalised here)
+    const int logits = RAW ? a.gate_logits : 0, qknorm = RAW ? a.qk_norm : 0;
     __shared__ PrepSmem S;
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -273,10 +276,10 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
     int64_t task = blockIdx.x;
     if (task < ntask) {
         const TaskPos p0 = task_pos(task, nc, static_cast<int>(a.H));
-        load_part<0, TIED, KEYG, VW>(R, a, p0, tid);
-        load_part<1, TIED, KEYG, VW>(R, a, p0, tid);
-        load_part<2, TIED, KEYG, VW>(R, a, p0, tid);
-        load_part<3, TIED, KEYG, VW>(R, a, p0, tid);
+        load_part<0, TIED, KEYG, VW, RAW>(R, a, p0, tid);
+        load_part<1, TIED, KEYG, VW, RAW>(R, a, p0, tid);
+        load_part<2, TIED, KEYG, VW, RAW>(R, a, p0, tid);
+        load_part<3, TIED, KEYG, VW, RAW>(R, a, p0, tid);
     }
 
     for (; task < ntask; task += gridDim.x) {
@@ -301,13 +304,13 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 if constexpr (!VW) {
                     return 1.f;
                 } else if constexpr (KEYG) {
-                    if (a.gate_logits) {  // column 2e+s of token i: half s of word e
+                    if (logits) {  // column 2e+s of token i: half s of word e
                         const uint32_t u = __float_as_uint(R.wr.x[2 * i][e]);
                         return sigmoid_gate(__uint_as_float(s ? (u & 0xffff0000u) : (u << 16)));
                     }
                     return R.wr.x[2 * i + (2 * e + s) / 4][(2 * e + s) % 4];
                 } else {
-                    return a.gate_logits ? sigmoid_gate(__uint_as_float(__float_as_uint(R.wr.x[i]) << 16)) : R.wr.x[i];
+                    return logits ? sigmoid_gate(__uint_as_float(__float_as_uint(R.wr.x[i]) << 16)) : R.wr.x[i];
                 }
             };
 #pragma unroll
@@ -322,18 +325,17 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             }
         }
         f4 g[RPS];
-        segment_cumsum(S, R, g, seg, cq, a.gate_logits, a.T - task_pos(task, nc, static_cast<int>(a.H)).t0);
+        segment_cumsum(S, R, g, seg, cq, logits, RAW ? a.T - task_pos(task, nc, static_cast<int>(a.H)).t0 : C);
         __syncthreads();
         if (tid < D) chunk_tables(S, tid);
         __syncthreads();
 
         // ---- factored fp16 Gram operands -------------------------------------
         f4 khf[RPS], qhf[RPS], egm;
-        factored_operands<PrepSmem, TIED, KEYG, 2, VW>(S, R, g, khf, qhf, egm, seg, cq, a.q_scale, a.gate_logits,
-                                                       a.qk_norm);
+        factored_operands<PrepSmem, TIED, KEYG, 2, VW>(S, R, g, khf, qhf, egm, seg, cq, a.q_scale, logits, qknorm);
         const int64_t next = task + gridDim.x;  // prefetched in four parts below
         const TaskPos pn = task_pos(next < ntask ? next : task, nc, static_cast<int>(a.H));
-        if (next < ntask) load_part<0, TIED, KEYG, VW>(R, a, pn, tid);
+        if (next < ntask) load_part<0, TIED, KEYG, VW, RAW>(R, a, pn, tid);
         __syncthreads();
 
         const bool wide = S.wide != 0;  // read by all before any later write
@@ -361,7 +363,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 *reinterpret_cast<h4 *>(&S.qh[r * KP + 4 * cq]) = to_h4(qhf[i] * egm);
             }
         }
-        if (next < ntask) load_part<1, TIED, KEYG, VW>(R, a, pn, tid);
+        if (next < ntask) load_part<1, TIED, KEYG, VW, RAW>(R, a, pn, tid);
 
         _Float16 *rec = w.frag + task * REC;
         if (!wide) {
@@ -433,7 +435,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 *reinterpret_cast<h4 *>(&S.u16[(16 * ct + lr) * SP + 16 * rt + 4 * lg]) = to_h4(uacc[rt]);
             if (big) S.wide = 1;
             __syncthreads();  // U complete in u16
-            if (next < ntask) load_part<2, TIED, KEYG, VW>(R, a, pn, tid);
+            if (next < ntask) load_part<2, TIED, KEYG, VW, RAW>(R, a, pn, tid);
 
             // ---- (4) Oe^T[ct, :] = V^T P^T - U^T R^T -> HBM (transposed, so
             //      the scan's output tiles hold adjacent columns per lane)
@@ -477,9 +479,9 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             }
             if (big) S.wide = 1;
         } else if (next < ntask) {
-            load_part<2, TIED, KEYG, VW>(R, a, pn, tid);
+            load_part<2, TIED, KEYG, VW, RAW>(R, a, pn, tid);
         }
-        if (next < ntask) load_part<3, TIED, KEYG, VW>(R, a, pn, tid);
+        if (next < ntask) load_part<3, TIED, KEYG, VW, RAW>(R, a, pn, tid);
         __syncthreads();
         // e^gC per key channel; a chunk to be run exactly is marked by -1 in
         // channel 0 (e^gC is never negative)
@@ -999,7 +1001,10 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
     sp.fs = l.nseg > 1 ? reinterpret_cast<float *>(p + l.off_fs) : nullptr;
     const int nc = static_cast<int>(l.nc);
     const int64_t g1 = l.ntask < cu_count() ? l.ntask : cu_count();
-    hipLaunchKernelGGL((chunk_prep_kernel<TIED, KEYG, VW>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s, a, w, nc);
+    if (a.gate_logits || a.qk_norm)
+        hipLaunchKernelGGL((chunk_prep_kernel<TIED, KEYG, VW, true>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s, a, w, nc);
+    else
+        hipLaunchKernelGGL((chunk_prep_kernel<TIED, KEYG, VW, false>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s, a, w, nc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (l.nseg > 1) {

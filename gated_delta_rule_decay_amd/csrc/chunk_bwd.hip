@@ -45,6 +45,7 @@ constexpr int kRevBudget = 64 * 1024;
 constexpr int kGradThreads = 512;
 constexpr int kGradBudget = 160 * 1024;
 constexpr int RB = 4;  // rows per work item in the state products
+typedef float f4v __attribute__((ext_vector_type(4)));
 
 // Row stride of the token-by-channel arrays in LDS: odd, so that lanes
 // reading one channel of different rows (the Gram loops) hit different banks.
@@ -385,8 +386,16 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
         Y[s * VS + j] = acc;
     }
     for (int c = tid; c < dk; c += kGradThreads) {
+        const float *sr = Sg + static_cast<int64_t>(c) * dv, *dr = dSg + static_cast<int64_t>(c) * dv;
         float acc = 0.f;
-        for (int j = 0; j < dv; ++j) acc += dSg[static_cast<int64_t>(c) * dv + j] * Sg[static_cast<int64_t>(c) * dv + j];
+        if ((dv & 3) == 0) {  // 16-byte row loads: each lane walks its own row
+            for (int j4 = 0; j4 < dv / 4; ++j4) {
+                const f4v sv = reinterpret_cast<const f4v *>(sr)[j4], dsv = reinterpret_cast<const f4v *>(dr)[j4];
+                acc += sv[0] * dsv[0] + sv[1] * dsv[1] + sv[2] * dsv[2] + sv[3] * dsv[3];
+            }
+        } else {
+            for (int j = 0; j < dv; ++j) acc += dr[j] * sr[j];
+        }
         dgC[c] = expf(gC[c]) * acc;
     }
     __syncthreads();
@@ -415,8 +424,8 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
         float aw[RB], aq[RB], ae[RB], au[RB];
 #pragma unroll
         for (int i = 0; i < RB; ++i) aw[i] = aq[i] = ae[i] = au[i] = 0.f;
-        for (int j = 0; j < dv; ++j) {
-            const float sv = Sg[static_cast<int64_t>(c) * dv + j], dsv = dSg[static_cast<int64_t>(c) * dv + j];
+        const float *sr = Sg + static_cast<int64_t>(c) * dv, *dr = dSg + static_cast<int64_t>(c) * dv;
+        auto term = [&](int j, float sv, float dsv) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
                 const int r = r0 + i;
@@ -425,6 +434,15 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
                 ae[i] -= M[r * VS + j] * dsv;
                 au[i] += V[r * VS + j] * dsv;
             }
+        };
+        if ((dv & 3) == 0) {  // 16-byte row loads: each lane walks its own row of S and dSo
+            for (int j4 = 0; j4 < dv / 4; ++j4) {
+                const f4v sv = reinterpret_cast<const f4v *>(sr)[j4], dsv = reinterpret_cast<const f4v *>(dr)[j4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) term(4 * j4 + e, sv[e], dsv[e]);
+            }
+        } else {
+            for (int j = 0; j < dv; ++j) term(j, sr[j], dr[j]);
         }
 #pragma unroll
         for (int i = 0; i < RB; ++i) {

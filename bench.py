@@ -11,7 +11,8 @@ form on the same inputs, the forward on raw inputs (bf16 gate logits, q/k
 normalised in-kernel), the backward, the long-context workload (B=1,
 T=65536, two-level scan), the Gated DeltaNet mode (scalar gates, B=4) and
 the recurrent decode step (256 sequences x 16 heads, fp32 state in HBM, in
-place); and the fp64 CPU oracle on the full workload.
+place), and the same tokens packed as sequences of mixed lengths; and the
+fp64 CPU oracle on the full workload.
 
 Prints ONE JSON line.  Only one GPU is used; --gpus above 1 exits.
 """
@@ -240,6 +241,45 @@ def time_backward(w, inp, torch, steps):
             "roofline": roofline_hbm(bwd_bytes(w), k), "algorithmic_bytes_per_launch": bwd_bytes(w)}
 
 
+def time_packed(w, inp, torch, steps, n_seq=12):
+    """Time gdn2_chunk_fwd_varlen on the workload's B*T tokens of every head
+    packed as n_seq sequences of drawn lengths (the same q/k/v/gate values,
+    one N(0, 0.1) initial state per sequence)."""
+    from gated_delta_rule_decay_amd import binding, chunk_fwd_varlen, synth
+
+    tot = w.B * w.T
+    lengths = synth.draw_lengths(tot, n_seq, seed=950)
+    d = to_dev(inp, torch)
+    flat = lambda x: None if x is None else x.reshape((tot,) + tuple(x.shape[2:]))
+    args = [flat(d[n]) for n in ("q", "k", "v", "log_decay", "erase", "write")]
+    cu = torch.from_numpy(synth.packed_offsets(lengths)).cuda()
+    s0 = torch.from_numpy(synth.make_inputs(w.scaled(B=n_seq, T=1), seed=951)["S0"]).cuda()
+    o = torch.empty((tot, w.H, w.dv), dtype=torch.float32, device="cuda")
+    st = torch.empty((n_seq, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    desc = binding.make_desc(n_seq, tot, w.H, w.dk, w.dv, w.chunk, binding.GDN2_BF16, 1, 1, 1, False)
+    ws = torch.empty(binding.chunk_fwd_varlen_workspace(desc), dtype=torch.uint8, device="cuda")
+    kw = dict(chunk=w.chunk, out=o, state_out=st, workspace=ws)
+    chunk_fwd_varlen(*args, cu, s0, **kw)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {steps} packed forwards ({n_seq} sequences)")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        chunk_fwd_varlen(*args, cu, s0, **kw)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    k = ev0.elapsed_time(ev1) / steps
+    nbytes = chunk_bytes(w.scaled(B=1, T=tot)) + 2 * (n_seq - 1) * w.H * w.dk * w.dv * 4
+    return {"workload": f"{w.name} tokens packed as {n_seq} sequences of lengths {lengths} "
+                        f"(H={w.H}), two-pass kernels",
+            "ms_per_step": round(ms, 4), "kernel_ms": round(k, 4),
+            "value": round(tot / (ms * 1e-3), 1), "unit": "tokens/s",
+            "roofline": roofline_hbm(nbytes, k, read_traffic("chunk_fwd_packed", w.name, source_hash(CHUNK_SOURCES))),
+            "algorithmic_bytes_per_launch": nbytes}
+
+
 def synth_make(w, wid):
     from gated_delta_rule_decay_amd import synth
     return synth.make_inputs(w, wid=wid)
@@ -331,6 +371,7 @@ def main():
                                  "value": round(tokens / (msvw * 1e-3), 1), "unit": "tokens/s",
                                  "roofline": roofline_hbm(chunk_bytes(w), kvw)}
         result["backward"] = time_backward(w, inp, torch, max(2, args.steps // 8))
+        result["packed"] = time_packed(w, inp, torch, max(2, args.steps // 4))
     del inp
     if not args.no_extra:
         result["fused_inputs"] = time_fused(w, torch, chunk_fwd, max(2, args.steps // 4))

@@ -23,7 +23,8 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_UNSUPP
 
 # Every entry point include/gdn2.h declares.
 EXPORTS = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace",
-           "gdn2_chunk_fwd", "gdn2_chunk_bwd_workspace", "gdn2_chunk_bwd", "gdn2_recurrent_step")
+           "gdn2_chunk_fwd", "gdn2_chunk_fwd_varlen_workspace", "gdn2_chunk_fwd_varlen",
+           "gdn2_chunk_bwd_workspace", "gdn2_chunk_bwd", "gdn2_recurrent_step")
 
 
 class Gdn2Desc(ctypes.Structure):
@@ -72,6 +73,11 @@ def load_library():
             lib.gdn2_chunk_fwd.restype = ctypes.c_int
             lib.gdn2_chunk_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp,
                                            ctypes.c_size_t, vp]
+            lib.gdn2_chunk_fwd_varlen_workspace.restype = ctypes.c_int
+            lib.gdn2_chunk_fwd_varlen_workspace.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
+            lib.gdn2_chunk_fwd_varlen.restype = ctypes.c_int
+            lib.gdn2_chunk_fwd_varlen.argtypes = [dp, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp,
+                                                  ctypes.c_size_t, vp]
             lib.gdn2_chunk_bwd_workspace.restype = ctypes.c_int
             lib.gdn2_chunk_bwd_workspace.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
             lib.gdn2_chunk_bwd.restype = ctypes.c_int
@@ -216,6 +222,65 @@ def chunk_fwd(q, k, v, log_decay, erase, write=None, state0=None, chunk=64, q_sc
         _ptr(write), _ptr(state0), _ptr(out), _ptr(state_out), _ptr(ws), ws_bytes, _stream())
     if st != 0:
         raise Gdn2Error(st, "gdn2_chunk_fwd")
+    return out, state_out
+
+
+def chunk_fwd_varlen_workspace(desc: Gdn2Desc) -> int:
+    n = ctypes.c_size_t(0)
+    st = load_library().gdn2_chunk_fwd_varlen_workspace(ctypes.byref(desc), ctypes.byref(n))
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_chunk_fwd_varlen_workspace")
+    return int(n.value)
+
+
+def chunk_fwd_varlen(q, k, v, log_decay, erase, write, cu_seqlens, state0=None, chunk=64,
+                     q_scale=1.0, out=None, state_out=None, return_state=True, workspace=True,
+                     value_write=False, qk_l2norm=False):
+    """Chunkwise GDN-2 forward over N sequences packed along one token axis.
+
+    q, k [T,H,dk], v [T,H,dv], gates [T,H,dk] / [T,H] (or the same with a
+    leading 1); cu_seqlens int32 [N+1] on the device (sequence i is tokens
+    cu_seqlens[i] .. cu_seqlens[i+1]-1); state0 [N,H,dk,dv] fp32 or None.
+    Other arguments as for chunk_fwd.  Returns (o shaped like v but fp32,
+    final states [N,H,dk,dv] or None).
+    """
+    import torch
+    lead = k.shape[:-3]
+    if len(lead) > 1 or (len(lead) == 1 and lead[0] != 1):
+        raise ValueError("packed tensors are [T,H,d] or [1,T,H,d]")
+    T, H, dk = k.shape[-3:]
+    dv = v.shape[-1]
+    dev = k.device
+    _check(cu_seqlens, "cu_seqlens", tuple(cu_seqlens.shape), (torch.int32,), dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of N+1 offsets")
+    N = cu_seqlens.numel() - 1
+    desc = _desc_for(q, k, v, log_decay, erase, write, tuple(lead) + (T, H), N, T, H, chunk, q_scale,
+                     value_write, qk_l2norm)
+    if state0 is not None:
+        _check(state0, "state0", (N, H, dk, dv), (torch.float32,), dev)
+    oshape = tuple(lead) + (T, H, dv)
+    if out is None:
+        out = torch.empty(oshape, dtype=torch.float32, device=dev)
+    else:
+        _check(out, "out", oshape, (torch.float32,), dev)
+    if state_out is None and return_state:
+        state_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif state_out is not None:
+        _check(state_out, "state_out", (N, H, dk, dv), (torch.float32,), dev)
+    ws, ws_bytes = None, 0
+    if workspace is True:
+        ws_bytes = chunk_fwd_varlen_workspace(desc)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+    elif workspace is not False and workspace is not None:
+        _check(workspace, "workspace", tuple(workspace.shape), (torch.uint8,), dev)
+        ws, ws_bytes = workspace, workspace.numel()
+    st = load_library().gdn2_chunk_fwd_varlen(
+        ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay),
+        _ptr(erase), _ptr(write), _ptr(state0), _ptr(out), _ptr(state_out), _ptr(ws), ws_bytes,
+        _stream())
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_chunk_fwd_varlen")
     return out, state_out
 
 

@@ -119,6 +119,32 @@ bool split_path(const gdn2_desc *d) {
     return d->batch * d->seqlen > 0 && gdn2::chunk_split_supported(a);
 }
 
+// Packed sequences: batch = N sequences along one axis of seqlen = T
+// tokens.  The token tensors are the B = 1 layouts; the states have N rows.
+gdn2_status check_varlen(const gdn2_desc *d, gdn2_desc *one) {
+    if (!d) return GDN2_ERR_NULL;
+    if (d->batch < 0 || d->seqlen < 0) return GDN2_ERR_SHAPE;
+    if (d->seqlen > INT32_MAX || d->batch >= INT32_MAX) return GDN2_ERR_SHAPE;  // int32 offsets
+    *one = *d;
+    one->batch = 1;
+    gdn2_status st = check_common(one);
+    if (st != GDN2_OK) return st;
+    int64_t x;
+    if (!mul_ok(d->batch, d->heads, &x) || !mul_ok(x, d->dk, &x) || !mul_ok(x, d->dv, &x) || !mul_ok(x, 8, &x))
+        return GDN2_ERR_SHAPE;
+    if (d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return GDN2_ERR_UNSUPPORTED;
+    return GDN2_OK;
+}
+
+bool split_path_varlen(const gdn2_desc *d) {
+    static const float placeholder = 0.f;  // stands for an untied write gate
+    static const int32_t cu_placeholder = 0;
+    ChunkArgs a = args_of(d, nullptr, nullptr, nullptr, nullptr, nullptr, &placeholder, nullptr, nullptr,
+                          nullptr);
+    a.cu = &cu_placeholder;
+    return d->batch > 0 && d->seqlen > 0 && gdn2::chunk_split_supported(a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -193,6 +219,66 @@ gdn2_status gdn2_chunk_fwd(const gdn2_desc *d, const void *q, const void *k, con
     if (a.B * a.H > 0x7fffffffLL) return GDN2_ERR_UNSUPPORTED;
     if (use_ws && need > 0) return hip_status(gdn2::launch_chunk_split(a, workspace, s));
     if (gdn2::chunk_mfma_supported(a)) return hip_status(gdn2::launch_chunk_mfma(a, s));
+    return hip_status(gdn2::launch_chunk_general(a, s));
+}
+
+gdn2_status gdn2_chunk_fwd_varlen_workspace(const gdn2_desc *desc, size_t *bytes) {
+    if (!bytes) return GDN2_ERR_NULL;
+    gdn2_desc one;
+    gdn2_status st = check_varlen(desc, &one);
+    if (st != GDN2_OK) return st;
+    *bytes = split_path_varlen(desc) ? gdn2::chunk_split_workspace_varlen(desc->batch, desc->heads, desc->seqlen) : 0;
+    return GDN2_OK;
+}
+
+gdn2_status gdn2_chunk_fwd_varlen(const gdn2_desc *d, const int32_t *cu_seqlens, const void *q, const void *k,
+                                  const void *v, const float *log_decay, const float *erase, const float *write,
+                                  const float *state0, float *o, float *state_out, void *workspace,
+                                  size_t ws_bytes, void *stream) {
+    size_t need = 0;
+    gdn2_status st = gdn2_chunk_fwd_varlen_workspace(d, &need);
+    if (st != GDN2_OK) return st;
+    const bool use_ws = workspace != nullptr && ws_bytes > 0;
+    if (use_ws && (ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0))
+        return GDN2_ERR_WORKSPACE;
+    const int64_t N = d->batch, T = d->seqlen;
+    if (N == 0) return GDN2_OK;  // no sequence: nothing to read or write
+    if (!cu_seqlens) return GDN2_ERR_NULL;
+    const bool work = T > 0;
+    if (work && (!q || !k || !v || !log_decay || !erase || !o)) return GDN2_ERR_NULL;
+    if (work && !d->tie_write_to_erase && !write) return GDN2_ERR_NULL;
+    gdn2_desc one = *d;
+    one.batch = 1;
+    const Sizes sz = sizes_of(&one, T);
+    const int64_t stb = N * d->heads * d->dk * d->dv * 4;
+    const Span in[] = {span_of(q, sz.qk), span_of(k, sz.qk), span_of(v, sz.v),
+                       span_of(log_decay, sz.la), span_of(erase, sz.eb),
+                       span_of(d->tie_write_to_erase ? nullptr : write, sz.wr),
+                       span_of(cu_seqlens, (N + 1) * 4)};
+    const Span s_in = span_of(state0, stb), s_out = span_of(state_out, stb);
+    const Span o_sp = span_of(o, sz.o);
+    for (const Span &x : in) {
+        if (overlap(o_sp, x) || overlap(s_out, x)) return GDN2_ERR_ALIAS;
+    }
+    if (overlap(o_sp, s_in) || overlap(o_sp, s_out)) return GDN2_ERR_ALIAS;
+    if (overlap(s_out, s_in) && s_out.lo != s_in.lo) return GDN2_ERR_ALIAS;
+    if (use_ws) {
+        const Span ws = span_of(workspace, static_cast<int64_t>(ws_bytes));
+        for (const Span &x : in)
+            if (overlap(ws, x)) return GDN2_ERR_ALIAS;
+        if (overlap(ws, o_sp) || overlap(ws, s_in) || overlap(ws, s_out)) return GDN2_ERR_ALIAS;
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!work) {  // every sequence empty
+        if (state_out && state_out != state0)
+            return hip_status(gdn2::launch_state_copy(state0, state_out, stb / 4, s));
+        return GDN2_OK;
+    }
+    ChunkArgs a = args_of(d, q, k, v, log_decay, erase, write, state0, o, state_out);
+    a.cu = cu_seqlens;
+    if (a.B * a.H > 0x7fffffffLL) return GDN2_ERR_UNSUPPORTED;
+    if (use_ws && need > 0) return hip_status(gdn2::launch_chunk_split(a, workspace, s));
     return hip_status(gdn2::launch_chunk_general(a, s));
 }
 

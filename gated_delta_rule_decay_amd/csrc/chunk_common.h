@@ -180,8 +180,11 @@ __device__ __forceinline__ void invert_unit_lower16(float *na, _Float16 *th, flo
 // hardware returns zeros for them and the loads need no branch.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void *base, const ChunkArgs &a,
                                                             int64_t b, int64_t h, int64_t t0,
-                                                            int width, int esize, int col0) {
-    const int64_t nvalid = a.T - t0 < C ? (a.T - t0 > 0 ? a.T - t0 : 0) : C;
+                                                            int width, int esize, int col0,
+                                                            int64_t tlim = -1) {
+    // rows at or past tlim (default: the sequence length T) read as zero
+    const int64_t lim = tlim < 0 ? a.T : tlim;
+    const int64_t nvalid = lim - t0 < C ? (lim - t0 > 0 ? lim - t0 : 0) : C;
     const char *p = static_cast<const char *>(base) +
                     (((b * a.T + t0) * a.H + h) * width + col0) * static_cast<int64_t>(esize);
     const int64_t bytes = nvalid > 0 ? ((nvalid - 1) * a.H * width + width - col0) * esize : 0;

@@ -81,6 +81,14 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
 
     const int64_t bh = blockIdx.x;
     const int64_t b = bh / H, h = bh % H;
+    // tokens [lo, hi) of the flattened [B*T] token axis: sequence b of T
+    // tokens, or, packed, offsets cu[b], cu[b+1] clamped into [0, T] and
+    // [lo, T] (no access leaves the tensors whatever they hold)
+    int64_t lo = b * T, hi = lo + T;
+    if (a.cu) {
+        lo = min(max(static_cast<int64_t>(a.cu[b]), int64_t(0)), T);
+        hi = min(max(static_cast<int64_t>(a.cu[b + 1]), lo), T);
+    }
     const int col0 = blockIdx.y * DVT;
     const int ncol = min(DVT, dv - col0);
     const int tid = threadIdx.x;
@@ -91,11 +99,11 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
         S[idx] = (a.s0 && j < ncol) ? a.s0[sbase + static_cast<int64_t>(c) * dv + col0 + j] : 0.f;
     }
 
-    const int64_t nch = (T + Cg - 1) / Cg;
-    for (int64_t t0 = 0; t0 < T; t0 += Cg) {
+    const int64_t nch = (T + Cg - 1) / Cg;  // (hist: B sequences of T tokens)
+    for (int64_t t0 = lo; t0 < hi; t0 += Cg) {
         __syncthreads();
         if (hist) {
-            float *hs = hist + ((b * H + h) * nch + t0 / Cg) * static_cast<int64_t>(dk) * dv;
+            float *hs = hist + ((b * H + h) * nch + (t0 - lo) / Cg) * static_cast<int64_t>(dk) * dv;
             for (int idx = tid; idx < dk * DVT; idx += kThreads) {
                 const int c = idx / DVT, j = idx % DVT;
                 if (j < ncol) hs[static_cast<int64_t>(c) * dv + col0 + j] = S[idx];
@@ -109,8 +117,8 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
             const int r = idx / dk, c = idx % dk;
             const int64_t t = t0 + r;
             float kv = 0.f, qv = 0.f, la = 0.f, bb = 0.f, ww = 0.f;
-            if (t < T) {
-                const int64_t row = (b * T + t) * H + h;
+            if (t < hi) {
+                const int64_t row = t * H + h;
                 kv = load_qkv(a.k, row * dk + c, a.bf16);
                 qv = load_qkv(a.q, row * dk + c, a.bf16);
                 la = load_gate_x(a.la, a.la_key, row, dk, c, a.gate_logits, 0);
@@ -140,8 +148,8 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
             const int r = idx / DVT, j = idx % DVT;
             const int64_t t = t0 + r;
             float vv = 0.f;
-            if (t < T && j < ncol) {
-                const int64_t row = (b * T + t) * H + h;
+            if (t < hi && j < ncol) {
+                const int64_t row = t * H + h;
                 vv = load_qkv(a.v, row * dv + col0 + j, a.bf16);
                 if (a.value_write) vv *= load_gate_x(a.wr, a.wr_key, row, dv, col0 + j, a.gate_logits, 1);  // w .* v
             }
@@ -252,11 +260,11 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
         for (int idx = tid; idx < (hist ? 0 : Cg * DVT); idx += kThreads) {
             const int r = idx / DVT, j = idx % DVT;
             const int64_t t = t0 + r;
-            if (t >= T || j >= ncol) continue;
+            if (t >= hi || j >= ncol) continue;
             float acc = 0.f;
             for (int c = 0; c < dk; ++c) acc += Qf[r * KS + c] * S[c * DVT + j];
             for (int s = 0; s <= r; ++s) acc += P[r * Cg + s] * V[s * DVT + j] - R[r * Cg + s] * M[s * DVT + j];
-            a.o[((b * T + t) * H + h) * dv + col0 + j] = acc;
+            a.o[(t * H + h) * dv + col0 + j] = acc;
         }
         __syncthreads();
         // 8. S <- exp(g_C) S + Util^T V - Etil^T M (each thread owns its elements)

@@ -422,6 +422,7 @@ bool chunk_mfma_supported(const ChunkArgs &a) {
     const bool tied = a.wr == nullptr;
     const bool same = a.la_key == a.eb_key && (tied || a.wr_key == a.eb_key);
     return a.bf16 && a.dk == D && a.dv == D && a.C == C && same && !a.value_write && !a.gate_logits && !a.qk_norm &&
+           !a.cu &&
            a.H * D * 4 * C < (int64_t(1) << 31);
 }
 

@@ -65,6 +65,10 @@ struct SplitWs {
     _Float16 *frag;  // [task][REC]
     float *gam;      // [task][D]   e^gC per key channel; -1 in channel 0 marks
                      //             a chunk to be run as the exact recurrence
+    // packed sequences only (built on the device from the offsets):
+    const int2 *vseq;  // [N]    token range [lo, hi) of each sequence
+    const int *vpfx;   // [N+1]  chunks before each sequence; vpfx[N]: all chunks
+    const int2 *vtab;  // [chunk] first token of each chunk, end of its sequence
 };
 
 struct PrepSmem {
@@ -100,31 +104,43 @@ __device__ __forceinline__ bool out_of_range(f4 x) {
 // are spread over the previous task instead of arriving at HBM in one burst:
 // part 0 the decay, 1 the erase gate, 2 the write gate and the values
 // (thread = token pair tid%32, 8-column piece tid/32), 3 keys and queries.
+// Token positions count over the flattened [B*T] token axis.
 struct TaskPos {
-    int64_t b, h, t0;
+    int64_t h, t0, tlim;  // head, first token, end of the chunk's sequence
 };
 
-// (batch, head, first token) of task `task` = chain * nc + chunk; 32-bit
-// division (the task count is checked to fit on the host).
-__device__ __forceinline__ TaskPos task_pos(int64_t task, int nc, int H) {
-    const uint32_t t = static_cast<uint32_t>(task), chain = t / static_cast<uint32_t>(nc);
+// Position of task `task`: chain * nc + chunk for B sequences of T tokens;
+// for packed sequences chunk-major (task = chunk * H + head, chunks of all
+// sequences in order), placed by the chunk table.  32-bit division (the task
+// count is checked to fit on the host).
+__device__ __forceinline__ TaskPos task_pos(const ChunkArgs &a, const SplitWs &w, int64_t task, int nc) {
+    const uint32_t t = static_cast<uint32_t>(task), H = static_cast<uint32_t>(a.H);
     TaskPos p;
-    p.b = chain / static_cast<uint32_t>(H);
-    p.h = chain % static_cast<uint32_t>(H);
-    p.t0 = static_cast<int64_t>(t - chain * static_cast<uint32_t>(nc)) * C;
+    if (a.cu) {
+        const uint32_t gc = t / H;
+        const int2 e = w.vtab[gc];
+        p.h = t - gc * H;
+        p.t0 = e.x;
+        p.tlim = e.y;
+    } else {
+        const uint32_t chain = t / static_cast<uint32_t>(nc), b = chain / H;
+        p.h = chain - b * H;
+        p.t0 = static_cast<int64_t>(b) * a.T + static_cast<int64_t>(t - chain * static_cast<uint32_t>(nc)) * C;
+        p.tlim = static_cast<int64_t>(b) * a.T + a.T;
+    }
     return p;
 }
 
 template <int PART, bool TIED, bool KEYG, bool VW = false, bool RAW = false>
 __device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, const TaskPos &tp0, int tid) {
     const bool logits = RAW && a.gate_logits;  // bf16 gate logits (fused input preparation)
-    const int64_t b = tp0.b, h = tp0.h, t0 = tp0.t0;
+    const int64_t b = 0, h = tp0.h, t0 = tp0.t0, tl = tp0.tlim;
     const int seg = tid >> 5, cq = tid & 31;
     const int gw = KEYG ? D : 1;
     const int rowk = static_cast<int>(a.H) * D, rowg = static_cast<int>(a.H) * gw;
     auto gates = [&](GateRow<KEYG> &x, const float *src) {
         if (logits) {  // bf16 logits: raw bits, activated where used
-            const auto rs = chain_rsrc(src, a, b, h, t0, gw, 2, 0);
+            const auto rs = chain_rsrc(src, a, b, h, t0, gw, 2, 0, tl);
 #pragma unroll
             for (int i = 0; i < RPS; ++i) {
                 const int r = seg * RPS + i;
@@ -137,7 +153,7 @@ __device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, c
             }
             return;
         }
-        const auto rs = chain_rsrc(src, a, b, h, t0, gw, 4, 0);
+        const auto rs = chain_rsrc(src, a, b, h, t0, gw, 4, 0, tl);
 #pragma unroll
         for (int i = 0; i < RPS; ++i) {
             const int r = seg * RPS + i;
@@ -151,7 +167,7 @@ __device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, c
     if constexpr (PART == 1) gates(R.eb, a.eb);
     if constexpr (PART == 2) {
         if (!TIED) gates(R.wr, a.wr);
-        const auto rv = chain_rsrc(a.v, a, b, h, t0, D, 2, 0);
+        const auto rv = chain_rsrc(a.v, a, b, h, t0, D, 2, 0, tl);
         const int tp = tid & 31, piece = tid >> 5;
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -161,7 +177,7 @@ __device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, c
             // of my two tokens (per head), into the unused wr registers
             // (bf16 logits: the 8 columns of token i in wr.x[2i])
             const int es = logits ? 2 : 4;
-            const auto rw = chain_rsrc(a.wr, a, b, h, t0, gw, es, 0);
+            const auto rw = chain_rsrc(a.wr, a, b, h, t0, gw, es, 0, tl);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 if constexpr (KEYG) {
@@ -183,8 +199,8 @@ __device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, c
         }
     }
     if constexpr (PART == 3) {
-        const auto rk = chain_rsrc(a.k, a, b, h, t0, D, 2, 0);
-        const auto rq = chain_rsrc(a.q, a, b, h, t0, D, 2, 0);
+        const auto rk = chain_rsrc(a.k, a, b, h, t0, D, 2, 0, tl);
+        const auto rq = chain_rsrc(a.q, a, b, h, t0, D, 2, 0, tl);
 #pragma unroll
         for (int i = 0; i < RPS; ++i) {
             const int ok = ((seg * RPS + i) * rowk + 4 * cq) * 2;
@@ -261,7 +277,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
     __shared__ PrepSmem S;
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t ntask = a.B * a.H * nc;
+    const int64_t ntask = a.cu ? a.H * w.vpfx[a.B] : a.B * a.H * nc;
 
     // zero the upper blocks of the C x C operands once; they are never written
     for (int idx = tid; idx < C * SP; idx += NTH) {
@@ -274,8 +290,10 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
 
     Raw<KEYG, 2> R;
     int64_t task = blockIdx.x;
+    TaskPos cur{0, 0, 0};
     if (task < ntask) {
-        const TaskPos p0 = task_pos(task, nc, static_cast<int>(a.H));
+        const TaskPos p0 = task_pos(a, w, task, nc);
+        cur = p0;
         load_part<0, TIED, KEYG, VW, RAW>(R, a, p0, tid);
         load_part<1, TIED, KEYG, VW, RAW>(R, a, p0, tid);
         load_part<2, TIED, KEYG, VW, RAW>(R, a, p0, tid);
@@ -325,7 +343,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             }
         }
         f4 g[RPS];
-        segment_cumsum(S, R, g, seg, cq, logits, RAW ? a.T - task_pos(task, nc, static_cast<int>(a.H)).t0 : C);
+        segment_cumsum(S, R, g, seg, cq, logits, RAW ? cur.tlim - cur.t0 : C);
         __syncthreads();
         if (tid < D) chunk_tables(S, tid);
         __syncthreads();
@@ -334,7 +352,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         f4 khf[RPS], qhf[RPS], egm;
         factored_operands<PrepSmem, TIED, KEYG, 2, VW>(S, R, g, khf, qhf, egm, seg, cq, a.q_scale, logits, qknorm);
         const int64_t next = task + gridDim.x;  // prefetched in four parts below
-        const TaskPos pn = task_pos(next < ntask ? next : task, nc, static_cast<int>(a.H));
+        const TaskPos pn = task_pos(a, w, next < ntask ? next : task, nc);
         if (next < ntask) load_part<0, TIED, KEYG, VW, RAW>(R, a, pn, tid);
         __syncthreads();
 
@@ -487,6 +505,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         // channel 0 (e^gC is never negative)
         const bool exact = wide || S.wide;  // reset after the next task's first barrier
         if (tid < D) w.gam[task * D + tid] = (tid == 0 && exact) ? -1.f : S.gce[tid];
+        cur = pn;
     }
 }
 
@@ -538,13 +557,13 @@ constexpr int scan_threads(int mode) { return 64 * (SCAN_P + (mode ? 2 : 1) * SC
 // range; the columns of F drop the write term).  Kept out of line: its
 // registers do not burden the scan's fast path.
 template <bool TIED, bool KEYG, bool VW, bool WITH_O>
-__device__ __noinline__ void exact_chunk(ChunkArgs a, f4 *sacc, int64_t b, int64_t h, int64_t t0, int ct, int lr,
-                                         int lg, bool frun) {
+__device__ __noinline__ void exact_chunk(ChunkArgs a, f4 *sacc, int64_t h, int64_t t0, int64_t tlim, int ct,
+                                         int lr, int lg, bool frun) {
     const uint16_t *kp = static_cast<const uint16_t *>(a.k);
     const uint16_t *qp = static_cast<const uint16_t *>(a.q);
     const uint16_t *vp = static_cast<const uint16_t *>(a.v);
-    for (int r = 0; r < C && t0 + r < a.T; ++r) {
-        const int64_t row = (b * a.T + t0 + r) * a.H + h;
+    for (int r = 0; r < C && t0 + r < tlim; ++r) {
+        const int64_t row = (t0 + r) * a.H + h;
         // gates of channel c of this token (per channel or per head;
         // bf16 logits activated here)
         auto gate = [&](const float *g, int c, int act) {
@@ -653,8 +672,31 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     }
     const int nsl = MODE ? sp.nseg - 1 : sp.nseg;  // segments per chain in this launch
     const int chain = unit / nsl, seg = unit % nsl;
-    const int n0 = seg * sp.seg_len, n1 = min(nc, n0 + sp.seg_len);
-    const int64_t b = chain / a.H, h = chain % a.H;
+    // chunks [n0, n1) of this unit; chunk n is task task0 + n * tstr and
+    // starts at token tbase + n * C of the flattened token axis; the
+    // sequence ends at tlim
+    int n0, n1;
+    int64_t h, task0, tstr, tbase, tlim;
+    if (a.cu) {  // packed sequences (one segment per chain)
+        const int i = chain / static_cast<int>(a.H), p0 = w.vpfx[i];
+        const int2 e = w.vseq[i];
+        h = chain - static_cast<int64_t>(i) * a.H;
+        n0 = 0;
+        n1 = w.vpfx[i + 1] - p0;
+        task0 = static_cast<int64_t>(p0) * a.H + h;
+        tstr = a.H;
+        tbase = e.x;
+        tlim = e.y;
+    } else {
+        const int64_t b = chain / a.H;
+        h = chain % a.H;
+        n0 = seg * sp.seg_len;
+        n1 = min(nc, n0 + sp.seg_len);
+        task0 = static_cast<int64_t>(chain) * nc;
+        tstr = 1;
+        tbase = b * a.T;
+        tlim = tbase + a.T;
+    }
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool copier = wv >= NCOMP;
@@ -663,7 +705,6 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     const int wt = wv % SCAN_W;                          // my tile within the slot's slices
     const int ct = SCAN_W * half + (copier ? 0 : wt);   // my value (or key) tile
     const int64_t sbase = static_cast<int64_t>(chain) * D * D;
-    const int64_t task0 = static_cast<int64_t>(chain) * nc;
     const int64_t xbase = (static_cast<int64_t>(chain) * sp.nseg + seg) * D * D;  // slot seg
 
     f4 sacc[8];  // state slice (compute waves): tile it holds S[16it+4lg+e][16ct+lr]
@@ -718,7 +759,7 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         const int lane = lane_, lr = lane & 15, lg = lane >> 4;
         const _Float16 *fg = fr + S_G + wt * 4 * 512;  // my G pairs
         const _Float16 *fo = fr + S_O + wt * 2 * 512;  // my Oe^T pairs (MODE 0)
-        const int64_t t0 = static_cast<int64_t>(n) * C;
+        const int64_t t0 = tbase + static_cast<int64_t>(n) * C;
         // the fp16 copies of the state and of the erase read must stay finite
         bool big = false;
 #pragma unroll
@@ -792,7 +833,7 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     const int64_t t = t0 + 16 * rt + lr;
-                    if (t < a.T) *reinterpret_cast<f4 *>(&a.o[((b * a.T + t) * a.H + h) * D + 16 * ct + 4 * lg]) = oacc[rt];
+                    if (t < tlim) *reinterpret_cast<f4 *>(&a.o[(t * a.H + h) * D + 16 * ct + 4 * lg]) = oacc[rt];
                 }
             }
             // S <- Diag(e^gC) S + G - Etil^T P1, tokens in permuted slots
@@ -822,7 +863,7 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
             f4 st[8];
 #pragma unroll
             for (int it = 0; it < 8; ++it) st[it] = sacc[it];
-            exact_chunk<TIED, KEYG, VW, WITH_O>(a, st, b, h, t0, ct, lr, lg, frun);
+            exact_chunk<TIED, KEYG, VW, WITH_O>(a, st, h, t0, tlim, ct, lr, lg, frun);
 #pragma unroll
             for (int it = 0; it < 8; ++it) sacc[it] = st[it];
             // leave nothing of this (rare) path outstanding, so that the fast
@@ -841,15 +882,17 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     constexpr int LGKM0 = 15 | (7 << 4) | (3 << 14);  // s_waitcnt lgkmcnt(0), other counters untouched
     if (copier) {
         const int pw = wv - NCOMP;
-        load_regs(task0 + n0, pw);
-        store_regs(fr0, gm0, pw);
-        if (n0 + 1 < n1) load_regs(task0 + n0 + 1, pw);
+        if (n0 < n1) {
+            load_regs(task0 + n0 * tstr, pw);
+            store_regs(fr0, gm0, pw);
+        }
+        if (n0 + 1 < n1) load_regs(task0 + (n0 + 1) * tstr, pw);
         __builtin_amdgcn_s_waitcnt(LGKM0);
 #define GDN2_COPY_STEP(N, FRN, GMN)                                                \
         do {                                                                      \
-            slot_barrier();                                         \
+            slot_barrier();                                                       \
             if ((N) + 1 < n1) store_regs(FRN, GMN, pw);                           \
-            if ((N) + 2 < n1) load_regs(task0 + (N) + 2, pw);                     \
+            if ((N) + 2 < n1) load_regs(task0 + ((N) + 2) * tstr, pw);            \
             __builtin_amdgcn_s_waitcnt(LGKM0);                                    \
         } while (0)
         int n = n0;
@@ -960,9 +1003,67 @@ int scan_segments(int64_t chains, int64_t nc) {
     return static_cast<int>((nc + len - 1) / len);  // no empty segment
 }
 
+// ----------------------------------------------------------------------------
+// Packed sequences: the plan.  Sequence i covers tokens [lo_i, hi_i) of the
+// flattened token axis, lo_i = cu[i] and hi_i = cu[i+1] clamped into
+// [0, T] and [lo_i, T]; its chunks start at lo_i, lo_i + C, ...  (the last
+// one ragged).  Chunk counts are capped at `cap` chunks in all, the number
+// the workspace holds: offsets that break 0 = cu[0] <= ... <= cu[N] = T give
+// unspecified results but never an access outside the tensors or the
+// workspace.
+constexpr int PLAN_NTH = 1024;
+
+// Ranges and chunk prefix counts (one workgroup, blocks of PLAN_NTH
+// sequences, an LDS scan per block).
+__global__ void __launch_bounds__(PLAN_NTH) varlen_plan_kernel(const int32_t *cu, int n, int64_t T, int cap,
+                                                               int2 *seq, int *pfx) {
+    __shared__ int64_t part[PLAN_NTH];  // 64-bit: overlapping ranges may sum past 2^31 chunks
+    const int tid = threadIdx.x;
+    int64_t carry = 0;
+    for (int base = 0; base < n; base += PLAN_NTH) {
+        const int i = base + tid;
+        int64_t cnt = 0;
+        if (i < n) {
+            const int64_t lo = min(max(static_cast<int64_t>(cu[i]), int64_t(0)), T);
+            const int64_t hi = min(max(static_cast<int64_t>(cu[i + 1]), lo), T);
+            seq[i] = make_int2(static_cast<int>(lo), static_cast<int>(hi));
+            cnt = (hi - lo + C - 1) / C;
+        }
+        part[tid] = cnt;
+        __syncthreads();
+        for (int off = 1; off < PLAN_NTH; off <<= 1) {
+            const int64_t x = tid >= off ? part[tid - off] : 0;
+            __syncthreads();
+            part[tid] += x;
+            __syncthreads();
+        }
+        if (i < n) pfx[i] = static_cast<int>(min(carry + part[tid] - cnt, static_cast<int64_t>(cap)));
+        const int64_t tot = part[PLAN_NTH - 1];
+        __syncthreads();  // every read of this block's scan before the next block's writes
+        carry = min(carry + tot, static_cast<int64_t>(cap));
+    }
+    if (tid == 0) pfx[n] = static_cast<int>(carry);
+}
+
+// The chunk table: first token of each chunk and the end of its sequence.
+__global__ void __launch_bounds__(256) varlen_table_kernel(const int2 *seq, const int *pfx, int n, int2 *tab) {
+    const int total = pfx[n];
+    for (int gc = blockIdx.x * 256 + threadIdx.x; gc < total; gc += gridDim.x * 256) {
+        int lo = 0, hi = n - 1;  // the last sequence that starts at or before chunk gc
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pfx[mid] <= gc) lo = mid;
+            else hi = mid - 1;
+        }
+        const int2 e = seq[lo];
+        tab[gc] = make_int2(e.x + C * (gc - pfx[lo]), e.y);
+    }
+}
+
 struct Layout {
     int64_t nc, chains, ntask, nseg, seg_len;
     int64_t off_gam, off_xs, off_fs, bytes;
+    int64_t off_seq, off_pfx, off_tab;  // packed sequences
 };
 
 Layout layout(int64_t B, int64_t H, int64_t T) {
@@ -980,6 +1081,24 @@ Layout layout(int64_t B, int64_t H, int64_t T) {
     return l;
 }
 
+// Packed sequences: N sequences, T tokens in all, at most ceil(T/C) + N
+// chunks per head (each sequence's last chunk the only partial one).
+Layout layout_varlen(int64_t N, int64_t H, int64_t T) {
+    Layout l;
+    l.nc = (T + C - 1) / C + N;  // chunk bound per head
+    l.chains = N * H;
+    l.ntask = l.nc * H;
+    l.nseg = 1;
+    l.seg_len = 0;
+    l.off_gam = align256(l.ntask * REC * 2);
+    l.off_seq = l.off_gam + align256(l.ntask * D * 4);
+    l.off_pfx = l.off_seq + align256(N * 8);
+    l.off_tab = l.off_pfx + align256((N + 1) * 4);
+    l.off_xs = l.off_fs = 0;
+    l.bytes = l.off_tab + align256(l.nc * 8);
+    return l;
+}
+
 int cu_count() {
     int dev = 0, n = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
@@ -989,11 +1108,30 @@ int cu_count() {
 
 template <bool TIED, bool KEYG, bool VW = false>
 hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
-    const Layout l = layout(a.B, a.H, a.T);
+    const Layout l = a.cu ? layout_varlen(a.B, a.H, a.T) : layout(a.B, a.H, a.T);
     char *p = static_cast<char *>(ws);
     SplitWs w;
     w.frag = reinterpret_cast<_Float16 *>(p);
     w.gam = reinterpret_cast<float *>(p + l.off_gam);
+    w.vseq = nullptr;
+    w.vpfx = nullptr;
+    w.vtab = nullptr;
+    if (a.cu) {
+        int2 *seq = reinterpret_cast<int2 *>(p + l.off_seq);
+        int *pfx = reinterpret_cast<int *>(p + l.off_pfx);
+        int2 *tab = reinterpret_cast<int2 *>(p + l.off_tab);
+        hipLaunchKernelGGL(varlen_plan_kernel, dim3(1), dim3(PLAN_NTH), 0, s, a.cu, static_cast<int>(a.B), a.T,
+                           static_cast<int>(l.nc), seq, pfx);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t tb = (l.nc + 255) / 256;
+        hipLaunchKernelGGL(varlen_table_kernel, dim3(static_cast<unsigned>(tb < 1024 ? tb : 1024)), dim3(256), 0, s,
+                           seq, pfx, static_cast<int>(a.B), tab);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        w.vseq = seq;
+        w.vpfx = pfx;
+        w.vtab = tab;
+    }
     ScanPlan sp;
     sp.nseg = static_cast<int>(l.nseg);
     sp.seg_len = static_cast<int>(l.seg_len);
@@ -1031,12 +1169,16 @@ bool chunk_split_supported(const ChunkArgs &a) {
     // kernels index tasks (chain * chunks + chunk) with 32-bit arithmetic
     const bool tied = a.wr == nullptr;
     const bool same = a.la_key == a.eb_key && (tied || a.wr_key == a.eb_key);
-    const int64_t ntask = a.B * a.H * ((a.T + C - 1) / C);
+    const int64_t ntask = a.cu ? a.H * ((a.T + C - 1) / C + a.B) : a.B * a.H * ((a.T + C - 1) / C);
     return a.bf16 && a.dk == D && a.dv == D && a.C == C && same && (!a.value_write || !tied) &&
            a.H * D * 4 * C < (int64_t(1) << 31) && ntask > 0 && ntask < (int64_t(1) << 31);
 }
 
 size_t chunk_split_workspace(int64_t B, int64_t H, int64_t T) { return static_cast<size_t>(layout(B, H, T).bytes); }
+
+size_t chunk_split_workspace_varlen(int64_t N, int64_t H, int64_t T) {
+    return static_cast<size_t>(layout_varlen(N, H, T).bytes);
+}
 
 hipError_t launch_chunk_split(const ChunkArgs &a, void *ws, hipStream_t s) {
     const bool tied = a.wr == nullptr, keyg = a.la_key != 0;

@@ -23,6 +23,8 @@ struct ChunkArgs {
                                     //    channel ([B,T,H,dv] when wr_key)
     int gate_logits;                // 1: gates are bf16 logits (-softplus / sigmoid in-kernel)
     int qk_norm;                    // 1: q, k L2-normalised per token-head in-kernel
+    const int32_t *cu = nullptr;    // packed sequences: [B+1] token offsets (device), B sequences
+                                    // along T of batch-1 tensors; nullptr: B fixed-length ones
 };
 
 struct StepArgs {
@@ -52,6 +54,9 @@ hipError_t launch_chunk_mfma(const ChunkArgs &a, hipStream_t s);
 bool chunk_split_supported(const ChunkArgs &a);
 size_t chunk_split_workspace(int64_t B, int64_t H, int64_t T);
 hipError_t launch_chunk_split(const ChunkArgs &a, void *ws, hipStream_t s);
+// The same for packed sequences (a.cu set): the workspace bound uses at most
+// ceil(T/64) + B chunks per head.
+size_t chunk_split_workspace_varlen(int64_t N, int64_t H, int64_t T);
 
 // The general forward recording the state that enters every chunk of Cg
 // tokens, hist[B*H][ceil(T/Cg)][dk][dv]; writes neither o nor the final state.

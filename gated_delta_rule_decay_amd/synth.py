@@ -200,6 +200,36 @@ def make_raw_inputs(w: Workload, seed: int | None = None, wid: int | None = None
     return out
 
 
+def packed_offsets(lengths) -> np.ndarray:
+    """int32 offsets [N+1] of sequences of the given lengths packed in order."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def draw_lengths(total: int, n: int, seed: int) -> list[int]:
+    """A length mix for packed sequences: ``n`` lengths summing to ``total``,
+    the shares drawn as Exp(1) weights (a uniform Dirichlet split: a few long
+    documents and many short ones, zeros possible), cut points rounded down."""
+    r = np.random.Generator(np.random.PCG64(seed))
+    wts = r.exponential(1.0, size=n)
+    cuts = np.floor(total * np.cumsum(wts) / wts.sum()).astype(np.int64)
+    cuts[-1] = total
+    return np.diff(np.concatenate([[0], cuts])).tolist()
+
+
+def make_packed_inputs(w: Workload, lengths, seed: int, raw: bool = False) -> dict:
+    """Inputs for N = len(lengths) sequences packed along one token axis:
+    the workload recipe drawn for B = 1 and T = sum(lengths) (``raw``: before
+    input preparation, as ``make_raw_inputs``), one initial state per
+    sequence from the recipe's S0 draw with B = N (seed + 1), and the
+    offsets ``cu_seqlens``."""
+    T = int(sum(lengths))
+    gen = make_raw_inputs if raw else make_inputs
+    out = gen(w.scaled(B=1, T=T), seed=seed)
+    out["S0"] = gen(w.scaled(B=len(lengths), T=1), seed=seed + 1)["S0"]
+    out["cu_seqlens"] = packed_offsets(lengths)
+    return out
+
+
 def make_decode_state(w: Workload, seed: int | None = None) -> np.ndarray:
     """Initial fp32 state [N,H,dk,dv] ~ N(0, s0_std) for a decode workload."""
     if seed is None:

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 3
+#define GDN2_ABI_VERSION 4
 
 typedef enum gdn2_status {
     GDN2_OK = 0,
@@ -174,6 +174,48 @@ gdn2_status gdn2_chunk_fwd(const gdn2_desc *desc,
                            const float *log_decay, const float *erase, const float *write,
                            const float *state0, float *o, float *state_out,
                            void *workspace, size_t ws_bytes, void *stream);
+
+/* Device workspace, in bytes, for the two-pass form of gdn2_chunk_fwd_varlen
+ * on `desc` (batch = N sequences, seqlen = T packed tokens); 0 when the
+ * request has no two-pass kernel.  It holds records for ceil(T/64) + N
+ * chunks per head (every sequence may end in a partial chunk) and the
+ * sequence plan.  Same validation as gdn2_chunk_fwd_varlen. */
+gdn2_status gdn2_chunk_fwd_varlen_workspace(const gdn2_desc *desc, size_t *bytes);
+
+/*
+ * The chunkwise forward over N sequences of different lengths packed along
+ * one token axis (training on packed documents, prefill of a batch of
+ * prompts).  The sequences are independent recurrences, each from its own
+ * initial state: the result for sequence i equals gdn2_chunk_fwd on its
+ * tokens alone.  Chunks never straddle two sequences; each sequence's
+ * chunks start at its first token ("Gated DeltaNet" page, "What makes the
+ * architecture more than a recurrence": chunkwise training over long
+ * sequences, each transition an affine map of the state).
+ *
+ *   desc         batch = N >= 0 sequences, seqlen = T >= 0 packed tokens
+ *                (T <= INT32_MAX), other fields as for gdn2_chunk_fwd.
+ *   cu_seqlens   DEVICE int32 [N+1]: sequence i covers packed tokens
+ *                cu_seqlens[i] .. cu_seqlens[i+1]-1; required
+ *                0 = cu_seqlens[0] <= cu_seqlens[1] <= ... <= cu_seqlens[N]
+ *                = T.  Not checked (it would need a device pass): other
+ *                offsets give unspecified results, but every offset is
+ *                clamped into [0, T] and every range made non-negative, so
+ *                no access leaves the tensors or the workspace.
+ *   q, k, v, gates, o   [T, H, ...]: the [B, T, H, ...] layouts with B = 1.
+ *   state0, state_out   [N, H, dk, dv] fp32, one state per sequence
+ *                (state0 NULL: zeros; state_out NULL: skipped; in place as
+ *                for gdn2_chunk_fwd).
+ *   workspace    as for gdn2_chunk_fwd with gdn2_chunk_fwd_varlen_workspace()
+ *                bytes; NULL runs the single-kernel path.
+ * Outputs must not overlap cu_seqlens, any other input or the workspace
+ * (GDN2_ERR_ALIAS).  Rows of o outside every sequence are untouched; an
+ * empty sequence passes its initial state through.
+ */
+gdn2_status gdn2_chunk_fwd_varlen(const gdn2_desc *desc, const int32_t *cu_seqlens,
+                                  const void *q, const void *k, const void *v,
+                                  const float *log_decay, const float *erase, const float *write,
+                                  const float *state0, float *o, float *state_out,
+                                  void *workspace, size_t ws_bytes, void *stream);
 
 /* Device workspace, in bytes, for gdn2_chunk_bwd on `desc`: two fp32 state
  * histories, B*H*ceil(T/Cb)*dk*dv*4 bytes each (Cb = 16 for dk = dv = 128,

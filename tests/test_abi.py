@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn2_abi_version() == 3
+    assert lib.gdn2_abi_version() == 4
     for s in range(8):
         assert lib.gdn2_status_str(s)
     assert lib.gdn2_status_str(0) == b"ok"
@@ -267,3 +267,68 @@ def test_fused_input_checks(lib):
     n = ctypes.c_size_t(0)
     assert lib.gdn2_chunk_bwd_workspace(ctypes.byref(good(qk_l2norm=True)), ctypes.byref(n)) == 4
     assert lib.gdn2_chunk_bwd_workspace(ctypes.byref(good(gate_logits=True)), ctypes.byref(n)) == 4
+
+
+# ---- packed sequences -----------------------------------------------------
+
+CU = BASE + 40 * SLOT
+
+
+def fwd_varlen(lib, desc, cu=CU, q=Q, k=K, v=V, la=LA, eb=EB, wr=WR, s0=S0, o=O, so=SO, ws=None, wsb=0):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gdn2_chunk_fwd_varlen(None if desc is None else ctypes.byref(desc), vp(cu), vp(q), vp(k),
+                                     vp(v), vp(la), vp(eb), vp(wr), vp(s0), vp(o), vp(so), vp(ws), wsb,
+                                     None)
+
+
+def varlen_bytes(N, H, T):
+    """Records and chunk-end decays for ceil(T/64) + N chunks per head (each
+    sequence may end in a partial chunk), then the plan: N token ranges
+    (int32 pairs), N+1 chunk prefix counts, one int32 pair per chunk."""
+    a = lambda x: (x + 255) // 256 * 256
+    nc = (T + 63) // 64 + N
+    n = H * nc
+    return a(n * 98304) + a(n * 512) + a(N * 8) + a((N + 1) * 4) + a(nc * 8)
+
+
+def query_varlen(lib, d):
+    n = ctypes.c_size_t(123)
+    assert lib.gdn2_chunk_fwd_varlen_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
+    return n.value
+
+
+def test_varlen_workspace_query(lib):
+    # batch = N sequences, seqlen = T packed tokens
+    assert query_varlen(lib, good(batch=6, seqlen=430)) == varlen_bytes(6, 4, 430)
+    assert query_varlen(lib, good(batch=1, seqlen=65536, heads=16)) == varlen_bytes(1, 16, 65536)
+    vw = dict(form=bd.GDN2_FORM_VALUE_WRITE)
+    assert query_varlen(lib, good(batch=3, seqlen=100, **vw)) == varlen_bytes(3, 4, 100)
+    for d in (good(qkv_dtype=0), good(dk=64), good(chunk=32), good(seqlen=0), good(batch=0),
+              good(tied=True, decay_kind=0)):
+        assert query_varlen(lib, d) == 0
+
+
+def test_varlen_checks(lib):
+    d = good(batch=3, seqlen=200)
+    n = ctypes.c_size_t(0)
+    assert lib.gdn2_chunk_fwd_varlen_workspace(None, ctypes.byref(n)) == 1
+    assert lib.gdn2_chunk_fwd_varlen_workspace(ctypes.byref(d), None) == 1
+    assert fwd_varlen(lib, None) == 1
+    assert fwd_varlen(lib, d, cu=None) == 1
+    assert fwd_varlen(lib, d, q=None) == 1
+    assert fwd_varlen(lib, d, wr=None) == 1
+    assert fwd_varlen(lib, good(batch=0), cu=None, q=None) == 0   # no sequence: nothing to do
+    assert fwd_varlen(lib, good(batch=3, seqlen=2 ** 31)) == 2    # offsets are int32
+    assert fwd_varlen(lib, good(batch=-1)) == 2
+    assert fwd_varlen(lib, good(chunk=8)) == 4
+    assert fwd_varlen(lib, good(dk=129)) == 4
+    # the offsets are an input; states are [N, H, dk, dv]
+    assert fwd_varlen(lib, d, o=CU - 256) == 5
+    assert fwd_varlen(lib, d, so=CU) == 5
+    st = 3 * 4 * 128 * 128 * 4
+    assert fwd_varlen(lib, d, so=S0 + st - 256) == 5
+    need = varlen_bytes(3, 4, 200)
+    assert fwd_varlen(lib, d, ws=WS, wsb=need - 1) == 6
+    assert fwd_varlen(lib, d, ws=WS + 16, wsb=need) == 6
+    assert fwd_varlen(lib, d, ws=CU - 256, wsb=need) == 5
+    assert fwd_varlen(lib, d, ws=O - 256, wsb=need) == 5

@@ -25,11 +25,14 @@
 // collects its own terms; d log a is the reverse running sum of dg; and
 // e = b k, u = w k split their gradients between the gates and k.
 //
-// Three launches:
-//   1. the general forward records the state entering every chunk (hist);
-//   2. bwd_dstate_kernel walks the chunks backwards per (chain, value slice)
-//      carrying dS (value columns are independent) and records the gradient
-//      of every chunk's exit state (dhist), and dS0;
+// Three steps:
+//   1. the state entering every chunk is recorded (hist): by the general
+//      forward, or for dk = dv = 128 by the matrix-core scan of
+//      chunk_bwd_scan.hip;
+//   2. the chunks are walked backwards per (chain, value slice) carrying dS
+//      (value columns are independent), recording the gradient of every
+//      chunk's exit state (dhist), and dS0: bwd_dstate_kernel, or for
+//      dk = dv = 128 the matrix-core reverse scan;
 //   3. bwd_grads_kernel takes every (chain, chunk) in parallel, recomputes
 //      the chunk's forward quantities from hist and forms all gradients.
 // Every pairwise decay exp(g_r - g_s) with r >= s is formed directly, so no
@@ -597,24 +600,24 @@ int chunk_bwd_chunk(int64_t dk, int64_t dv, int C) {
     return 0;
 }
 
+// dk = dv = 128 takes the scans on the matrix cores (chunk_bwd_scan.hip),
+// which add a per-chunk record region after the two state records.
+static bool matrix_scans(int64_t dk, int64_t dv, int Cg) { return dk == 128 && dv == 128 && Cg == 16; }
+
 size_t chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int C) {
     const int Cg = chunk_bwd_chunk(dk, dv, C);
     if (!Cg || B * H * T == 0) return 0;
-    const int64_t one = B * H * ((T + Cg - 1) / Cg) * dk * dv * 4;
-    return static_cast<size_t>(2 * ((one + 255) & ~int64_t(255)));
+    const int64_t nch = (T + Cg - 1) / Cg;
+    const int64_t one = B * H * nch * dk * dv * 4;
+    const int64_t rec = matrix_scans(dk, dv, Cg) ? static_cast<int64_t>(bwd_record_bytes(B * H * nch)) : 0;
+    return static_cast<size_t>(2 * ((one + 255) & ~int64_t(255)) + ((rec + 255) & ~int64_t(255)));
 }
 
-hipError_t launch_chunk_bwd(const BwdArgs &a, void *ws, hipStream_t s) {
+// The two scans on the vector ALU (any head size): the general forward records
+// the states, bwd_dstate_kernel the state gradients.
+static hipError_t launch_bwd_scans_general(const BwdArgs &a, int Cg, float *hist, float *dhist, hipStream_t s) {
     const ChunkArgs &f = a.f;
     const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
-    const int Cg = chunk_bwd_chunk(dk, dv, f.C);
-    if (!Cg) return hipErrorInvalidValue;
-    const int64_t nch = (f.T + Cg - 1) / Cg;
-    const int64_t one = f.B * f.H * nch * dk * dv * 4;
-    float *hist = static_cast<float *>(ws);
-    float *dhist = reinterpret_cast<float *>(static_cast<char *>(ws) + ((one + 255) & ~int64_t(255)));
-    if (f.B * f.H * nch > 0x7fffffffLL) return hipErrorInvalidValue;
-
     ChunkArgs fwd = f;
     fwd.o = nullptr;
     fwd.s_out = nullptr;
@@ -633,9 +636,27 @@ hipError_t launch_chunk_bwd(const BwdArgs &a, void *ws, hipStream_t s) {
         return e;
     hipLaunchKernelGGL(bwd_dstate_kernel, dim3(static_cast<unsigned>(f.B * f.H), static_cast<unsigned>((dv + DVT - 1) / DVT)),
                        dim3(kRevThreads), lds, s, a, Cg, DVT, dhist);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return hipGetLastError();
+}
 
-    lds = static_cast<size_t>(grad_layout(Cg, dk, dv).total) * 4;
+hipError_t launch_chunk_bwd(const BwdArgs &a, void *ws, hipStream_t s) {
+    const ChunkArgs &f = a.f;
+    const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
+    const int Cg = chunk_bwd_chunk(dk, dv, f.C);
+    if (!Cg) return hipErrorInvalidValue;
+    const int64_t nch = (f.T + Cg - 1) / Cg;
+    const int64_t one = f.B * f.H * nch * dk * dv * 4;
+    float *hist = static_cast<float *>(ws);
+    float *dhist = reinterpret_cast<float *>(static_cast<char *>(ws) + ((one + 255) & ~int64_t(255)));
+    if (f.B * f.H * nch > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipError_t e;
+    if (matrix_scans(dk, dv, Cg)) {
+        float *rec = reinterpret_cast<float *>(static_cast<char *>(ws) + 2 * ((one + 255) & ~int64_t(255)));
+        if ((e = launch_bwd_scans_d128(a, rec, hist, dhist, static_cast<int>(nch), s)) != hipSuccess) return e;
+    } else {
+        if ((e = launch_bwd_scans_general(a, Cg, hist, dhist, s)) != hipSuccess) return e;
+    }
+    const size_t lds = static_cast<size_t>(grad_layout(Cg, dk, dv).total) * 4;
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_grads_kernel),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds))) != hipSuccess)
         return e;

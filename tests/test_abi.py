@@ -218,8 +218,12 @@ def bwd_bytes(desc):
 
 def test_bwd_workspace_query(lib):
     a = lambda x: (x + 255) // 256 * 256
-    assert bwd_bytes(good()) == 2 * a(2 * 4 * (128 // 16) * 128 * 128 * 4)
-    assert bwd_bytes(good(seqlen=100)) == 2 * a(2 * 4 * 7 * 128 * 128 * 4)
+    # d = 128: two state records per 16-token chunk, then a per-chunk record of
+    # the scans on the matrix cores (4 x 16x128 operands, 4 x 16x16 Grams/Tm,
+    # 128 exit decays, fp32)
+    rec = (4 * 16 * 128 + 4 * 16 * 16 + 128) * 4
+    assert bwd_bytes(good()) == 2 * a(2 * 4 * (128 // 16) * 128 * 128 * 4) + a(2 * 4 * 8 * rec)
+    assert bwd_bytes(good(seqlen=100)) == 2 * a(2 * 4 * 7 * 128 * 128 * 4) + a(2 * 4 * 7 * rec)
     assert bwd_bytes(good(dk=32, dv=32, chunk=64)) == 2 * a(2 * 4 * (128 // 32) * 32 * 32 * 4)
     assert bwd_bytes(good(seqlen=0)) == 0
 

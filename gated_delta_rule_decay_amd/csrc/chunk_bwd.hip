@@ -28,7 +28,7 @@
 // Three steps:
 //   1. the state entering every chunk is recorded (hist): by the general
 //      forward, or for dk = dv = 128 by the matrix-core scan of
-//      chunk_bwd_scan.hip;
+//      chunk_bwd_mfma.hip;
 //   2. the chunks are walked backwards per (chain, value slice) carrying dS
 //      (value columns are independent), recording the gradient of every
 //      chunk's exit state (dhist), and dS0: bwd_dstate_kernel, or for
@@ -600,7 +600,7 @@ int chunk_bwd_chunk(int64_t dk, int64_t dv, int C) {
     return 0;
 }
 
-// dk = dv = 128 takes the scans on the matrix cores (chunk_bwd_scan.hip),
+// dk = dv = 128 takes the scans on the matrix cores (chunk_bwd_mfma.hip),
 // which add a per-chunk record region after the two state records.
 static bool matrix_scans(int64_t dk, int64_t dv, int Cg) { return dk == 128 && dv == 128 && Cg == 16; }
 
@@ -649,13 +649,12 @@ hipError_t launch_chunk_bwd(const BwdArgs &a, void *ws, hipStream_t s) {
     float *hist = static_cast<float *>(ws);
     float *dhist = reinterpret_cast<float *>(static_cast<char *>(ws) + ((one + 255) & ~int64_t(255)));
     if (f.B * f.H * nch > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipError_t e;
     if (matrix_scans(dk, dv, Cg)) {
         float *rec = reinterpret_cast<float *>(static_cast<char *>(ws) + 2 * ((one + 255) & ~int64_t(255)));
-        if ((e = launch_bwd_scans_d128(a, rec, hist, dhist, static_cast<int>(nch), s)) != hipSuccess) return e;
-    } else {
-        if ((e = launch_bwd_scans_general(a, Cg, hist, dhist, s)) != hipSuccess) return e;
+        return launch_bwd_d128(a, rec, hist, dhist, static_cast<int>(nch), s);
     }
+    hipError_t e = launch_bwd_scans_general(a, Cg, hist, dhist, s);
+    if (e != hipSuccess) return e;
     const size_t lds = static_cast<size_t>(grad_layout(Cg, dk, dv).total) * 4;
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_grads_kernel),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds))) != hipSuccess)

@@ -1,0 +1,726 @@
+// chunk_bwd_mfma.hip -- the backward on the matrix cores (fp32 MFMA), for
+// dk = dv = 128 and the backward's 16-token chunks.
+//
+// The backward (chunk_bwd.hip has the general path and the adjoint formulas)
+// needs, for every chunk, the state S entering it and the gradient dSo of the
+// state leaving it; both come from scans over the chunks of a chain.  In the
+// chunk form of the recurrence ("Gated DeltaNet-2" blog summary, "Core
+// Mechanism"; gist.science summary, "Technische Samenvatting" section 3),
+// with Kbar, Qbar, Etil, Util the decayed key, query, erase and write operands
+// of a chunk, Tm = (I + A)^-1 and Bm, R, P its Grams:
+//   forward:  X = Kbar S + Bm V,  M = Tm X,  S <- Diag(e^gC) S + Util^T V - Etil^T M
+//   reverse:  dM = -Etil dSo - R^T dO,  Y = Tm^T dM,
+//             dS = Diag(e^gC) dSo + Qbar^T dO + Kbar^T Y
+// Four launches:
+//   bwd_record_kernel   every chunk in parallel: the Grams (pairwise decays
+//                       formed directly, never above 1), Tm by forward
+//                       substitution, the decayed operands -> a record;
+//   bwd_state_kernel    per (chain, 64 value columns), chunks in order: S in
+//                       accumulator registers, recorded on entry to each chunk;
+//   bwd_dgrad_kernel    per (chain, 64 value columns), chunks in reverse: dS in
+//                       registers, recorded on entry (= each chunk's dSo), dS0;
+//   bwd_grads128_kernel every chunk in parallel: all input gradients from the
+//                       record, S and dSo.
+// All arithmetic is fp32 (v_mfma_f32_16x16x4f32, fp32 accumulate), so the
+// gradients keep the fp32 tolerance.
+//
+// Register layout.  A wave owns 16 value columns; its state slice (128 key
+// channels x 16 columns) sits in 8 accumulator tiles: lane l = 16 kq + n holds
+// S[16 it + 4 kq + i][n] in register i of tile it.  The k-sum of a product
+// may run in any order, so each product is arranged so that the lane's own
+// accumulator registers are its B operand: in Kbar S the k-step (it, i) takes
+// key channel 16 it + 4 kq + i for lane group kq; in the token contractions
+// (Tm X, Etil^T M, ...) k-step j takes token 4 kq + j, which is where the
+// token-row accumulators of X, M, dM, Y hold their values.  Only the A
+// operands (the chunk's record, shared by the workgroup) come from LDS.
+#include "common.h"
+#include "kernels.h"
+
+namespace gdn2 {
+namespace {
+
+constexpr int BD = 128;   // dk = dv
+constexpr int BC = 16;    // tokens per chunk
+constexpr int BNT = 256;  // threads per workgroup (4 waves x 16 value columns)
+constexpr int RS = 132;   // LDS row stride of the 16 x 128 operands (2-way banked for the reads below)
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// record of one (chain, chunk), fp32, in this order
+constexpr int R_KB = 0;                 // Kbar = k e^g         [16][128]
+constexpr int R_QB = R_KB + BC * BD;    // Qbar = q_scale q e^g [16][128]
+constexpr int R_ET = R_QB + BC * BD;    // Etil = e e^(gC-g)    [16][128]
+constexpr int R_UT = R_ET + BC * BD;    // Util = u e^(gC-g)    [16][128]
+constexpr int R_TM = R_UT + BC * BD;    // Tm                   [16][16]
+constexpr int R_BM = R_TM + BC * BC;    // Bm (strictly lower)  [16][16]
+constexpr int R_RR = R_BM + BC * BC;    // R (lower)            [16][16]
+constexpr int R_PP = R_RR + BC * BC;    // P (lower)            [16][16]
+constexpr int R_GM = R_PP + BC * BC;    // e^gC                 [128]
+constexpr int REC_BWD = R_GM + BD;
+
+__device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// the record pass
+
+constexpr int KS = BD + 1;  // odd row stride: the Gram loops read one channel of different rows
+
+__global__ void __launch_bounds__(BNT) bwd_record_kernel(BwdArgs a, float *rec, int nch) {
+    __shared__ float K[BC * KS], Q[BC * KS], G[BC * KS], E[BC * KS], U[BC * KS];
+    __shared__ float A[BC * BC], Tm[BC * BC], gC[BD];
+    const ChunkArgs &f = a.f;
+    const int64_t T = f.T, H = f.H;
+    const int64_t ntask = f.B * H * nch;
+    const int tid = threadIdx.x;
+    for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
+        const int64_t bh = task / nch, n = task % nch, b = bh / H, h = bh % H, t0 = n * BC;
+        float *out = rec + task * REC_BWD;
+        __syncthreads();  // the previous task is done with LDS
+        for (int idx = tid; idx < BC * BD; idx += BNT) {
+            const int r = idx / BD, c = idx % BD;
+            float kv = 0.f, qv = 0.f, la = 0.f, e = 0.f, u = 0.f;
+            if (t0 + r < T) {
+                const int64_t row = (b * T + t0 + r) * H + h;
+                kv = load_qkv(f.k, row * BD + c, f.bf16);
+                qv = f.q_scale * load_qkv(f.q, row * BD + c, f.bf16);
+                la = load_gate(f.la, f.la_key, row, BD, c);
+                const float bb = load_gate(f.eb, f.eb_key, row, BD, c);
+                const float ww = f.wr ? load_gate(f.wr, f.wr_key, row, BD, c) : bb;
+                e = bb * kv;
+                u = ww * kv;
+            }
+            const int li = r * KS + c;
+            K[li] = kv; Q[li] = qv; G[li] = la; E[li] = e; U[li] = u;
+        }
+        __syncthreads();
+        if (tid < BD) {  // running log-decay per channel (padded rows add 0)
+            float run = 0.f;
+            for (int r = 0; r < BC; ++r) {
+                run += G[r * KS + tid];
+                G[r * KS + tid] = run;
+            }
+            gC[tid] = run;
+            out[R_GM + tid] = expf(run);
+        }
+        __syncthreads();
+        {  // the four Grams, one (r, s) pair per thread, pairwise decays formed directly
+            const int r = tid / BC, s = tid % BC;
+            float sa = 0.f, sb = 0.f, sr = 0.f, sp = 0.f;
+            if (s <= r) {
+                for (int c = 0; c < BD; ++c) {
+                    const float d = expf(G[r * KS + c] - G[s * KS + c]);
+                    const float kd = K[r * KS + c] * d, qd = Q[r * KS + c] * d;
+                    const float e = E[s * KS + c], u = U[s * KS + c];
+                    sa += kd * e;
+                    sb += kd * u;
+                    sr += qd * e;
+                    sp += qd * u;
+                }
+            }
+            A[tid] = s < r ? sa : 0.f;
+            out[R_BM + tid] = s < r ? sb : 0.f;
+            out[R_RR + tid] = sr;
+            out[R_PP + tid] = sp;
+        }
+        __syncthreads();
+        // Tm = (I + A)^-1 by forward substitution, a column per thread; the
+        // others fold the decays into the operands meanwhile
+        if (tid < BC) {
+            const int j = tid;
+            for (int r = 0; r < BC; ++r) {
+                float val = r < j ? 0.f : 1.f;
+                if (r > j) {
+                    float acc = 0.f;
+                    for (int s = j; s < r; ++s) acc += A[r * BC + s] * Tm[s * BC + j];
+                    val = -acc;
+                }
+                Tm[r * BC + j] = val;
+            }
+        }
+        for (int idx = tid; idx < BC * BD; idx += BNT) {
+            const int r = idx / BD, c = idx % BD, li = r * KS + c;
+            const float eg = expf(G[li]), ec = expf(gC[c] - G[li]);
+            out[R_KB + idx] = K[li] * eg;
+            out[R_QB + idx] = Q[li] * eg;
+            out[R_ET + idx] = E[li] * ec;
+            out[R_UT + idx] = U[li] * ec;
+        }
+        __syncthreads();
+        out[R_TM + tid] = Tm[tid];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// the two scans
+
+// LDS copy of the record parts a scan reads (row stride RS for the 16 x 128
+// operands)
+struct ScanLds {
+    float m0[BC * RS], m1[BC * RS], m2[BC * RS];
+    float t0[BC * BC], t1[BC * BC];
+    float gm[BD];
+};
+
+// Copy the parts [(src0, m0), (src1, m1), (src2, m2), (srcT0, t0), (srcT1, t1), gm]
+// of record `r`: every thread moves 8 + 8 + 8 + 1 + 1 (+ gm) floats as float4s.
+struct Staged {
+    f4 x[6];
+    f4 tt[2];
+    float g;
+};
+
+__device__ __forceinline__ void stage_load(Staged &st, const float *r, int o0, int o1, int o2, int oT0, int oT1,
+                                           int tid) {
+#pragma unroll
+    for (int p = 0; p < 6; ++p) {
+        const int part = p / 2, q = tid + BNT * (p % 2);  // float4 index 0..511 within a 16 x 128 part
+        const int off = part == 0 ? o0 : part == 1 ? o1 : o2;
+        st.x[p] = *reinterpret_cast<const f4 *>(r + off + 4 * q);
+    }
+    // the two 16 x 16 parts: 64 float4s each, threads 0..63 and 64..127
+    const int q = tid & 63;
+    st.tt[0] = *reinterpret_cast<const f4 *>(r + (tid < 64 ? oT0 : oT1) + 4 * q);
+    st.g = tid < BD ? r[R_GM + tid] : 0.f;
+}
+
+__device__ __forceinline__ void stage_store(const Staged &st, ScanLds &L, int tid) {
+#pragma unroll
+    for (int p = 0; p < 6; ++p) {
+        const int part = p / 2, q = tid + BNT * (p % 2);
+        const int row = q / 32, col = 4 * (q % 32);
+        float *m = part == 0 ? L.m0 : part == 1 ? L.m1 : L.m2;
+        *reinterpret_cast<f4 *>(&m[row * RS + col]) = st.x[p];
+    }
+    if (tid < 128) *reinterpret_cast<f4 *>(&(tid < 64 ? L.t0 : L.t1)[4 * (tid & 63)]) = st.tt[0];
+    if (tid < BD) L.gm[tid] = st.g;
+}
+
+// Four values of a [B*T*H, 128] row-major tensor for lane (kq, n): rows
+// (tokens) 4 kq + j of the chunk, column col; zero past T.
+__device__ __forceinline__ void load_rows4(float (&x)[4], const void *p, int bf16, int64_t b, int64_t h, int64_t t0,
+                                           int kq, int col, const ChunkArgs &f) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t t = t0 + 4 * kq + j;
+        x[j] = t < f.T ? load_qkv(p, ((b * f.T + t) * f.H + h) * BD + col, bf16) : 0.f;
+    }
+}
+
+// Store (or read) a wave's 128 x 16 state slice to/from a [128][128] matrix.
+__device__ __forceinline__ void put_state(float *dst, const f4 (&s)[8], int kq, int col) {
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(16 * it + 4 * kq + i) * BD + col] = s[it][i];
+}
+
+// The state entering every chunk, hist[chain][chunk][128][128].
+__global__ void __launch_bounds__(BNT) bwd_state_kernel(BwdArgs a, const float *rec, float *hist, int nch) {
+    __shared__ __attribute__((aligned(16))) ScanLds L;
+    const ChunkArgs &f = a.f;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int m = lane & 15, kq = lane >> 4;
+    const int64_t bh = blockIdx.x >> 1, b = bh / f.H, h = bh % f.H;
+    const int col = 64 * (blockIdx.x & 1) + 16 * wv + m;  // this lane's value column (as n)
+    const float *rc = rec + bh * nch * static_cast<int64_t>(REC_BWD);
+    float *hs = hist + bh * nch * static_cast<int64_t>(BD * BD);
+
+    f4 S[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[it][i] = f.s0 ? f.s0[bh * BD * BD + (16 * it + 4 * kq + i) * BD + col] : 0.f;
+
+    // m0 = Kbar, m1 = Etil, m2 = Util; t0 = Tm, t1 = Bm
+    Staged st;
+    float vn[4];
+    stage_load(st, rc, R_KB, R_ET, R_UT, R_TM, R_BM, tid);
+    load_rows4(vn, f.v, f.bf16, b, h, 0, kq, col, f);
+    for (int n = 0; n < nch; ++n) {
+        __syncthreads();  // every wave done with the previous chunk's LDS copy
+        stage_store(st, L, tid);
+        float v[4] = {vn[0], vn[1], vn[2], vn[3]};
+        if (n + 1 < nch) {
+            stage_load(st, rc + (n + 1) * static_cast<int64_t>(REC_BWD), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
+            load_rows4(vn, f.v, f.bf16, b, h, (n + 1) * BC, kq, col, f);
+        }
+        put_state(hs + n * static_cast<int64_t>(BD * BD), S, kq, col);
+        __syncthreads();
+        // X = Kbar S + Bm V (token rows)
+        f4 X = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const f4 k4 = *reinterpret_cast<const f4 *>(&L.m0[m * RS + 16 * it + 4 * kq]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) X = mfma4(k4[i], S[it][i], X);
+        }
+        {
+            const f4 b4 = *reinterpret_cast<const f4 *>(&L.t1[m * BC + 4 * kq]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) X = mfma4(b4[j], v[j], X);
+        }
+        // M = Tm X
+        f4 M = {0.f, 0.f, 0.f, 0.f};
+        {
+            const f4 t4 = *reinterpret_cast<const f4 *>(&L.t0[m * BC + 4 * kq]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) M = mfma4(t4[j], X[j], M);
+        }
+        // S <- Diag(e^gC) S + Util^T V - Etil^T M
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const f4 g4 = *reinterpret_cast<const f4 *>(&L.gm[16 * it + 4 * kq]);
+            f4 s = g4 * S[it];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s = mfma4(L.m2[(4 * kq + j) * RS + 16 * it + m], v[j], s);
+                s = mfma4(-L.m1[(4 * kq + j) * RS + 16 * it + m], M[j], s);
+            }
+            S[it] = s;
+        }
+    }
+}
+
+// The gradient of every chunk's exit state, dhist[chain][chunk][128][128],
+// carried backwards from d_sT; the gradient of S0 at the end.
+__global__ void __launch_bounds__(BNT) bwd_dgrad_kernel(BwdArgs a, const float *rec, float *dhist, int nch) {
+    __shared__ __attribute__((aligned(16))) ScanLds L;
+    const ChunkArgs &f = a.f;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int m = lane & 15, kq = lane >> 4;
+    const int64_t bh = blockIdx.x >> 1, b = bh / f.H, h = bh % f.H;
+    const int col = 64 * (blockIdx.x & 1) + 16 * wv + m;
+    const float *rc = rec + bh * nch * static_cast<int64_t>(REC_BWD);
+    float *hs = dhist + bh * nch * static_cast<int64_t>(BD * BD);
+
+    f4 dS[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dS[it][i] = a.d_sT ? a.d_sT[bh * BD * BD + (16 * it + 4 * kq + i) * BD + col] : 0.f;
+
+    // m0 = Etil, m1 = Qbar, m2 = Kbar; t0 = Tm, t1 = R
+    Staged st;
+    float on[4];
+    const int nl = nch - 1;
+    stage_load(st, rc + nl * static_cast<int64_t>(REC_BWD), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
+    load_rows4(on, a.d_o, 0, b, h, static_cast<int64_t>(nl) * BC, kq, col, f);
+    for (int n = nl; n >= 0; --n) {
+        __syncthreads();
+        stage_store(st, L, tid);
+        float o[4] = {on[0], on[1], on[2], on[3]};
+        if (n > 0) {
+            stage_load(st, rc + (n - 1) * static_cast<int64_t>(REC_BWD), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
+            load_rows4(on, a.d_o, 0, b, h, static_cast<int64_t>(n - 1) * BC, kq, col, f);
+        }
+        put_state(hs + n * static_cast<int64_t>(BD * BD), dS, kq, col);
+        __syncthreads();
+        // dM = -(Etil dSo + R^T dO)  (token rows)
+        f4 dM = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const f4 e4 = *reinterpret_cast<const f4 *>(&L.m0[m * RS + 16 * it + 4 * kq]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dM = mfma4(e4[i], dS[it][i], dM);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dM = mfma4(L.t1[(4 * kq + j) * BC + m], o[j], dM);
+        dM = -dM;
+        // Y = Tm^T dM
+        f4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Y = mfma4(L.t0[(4 * kq + j) * BC + m], dM[j], Y);
+        // dS <- Diag(e^gC) dSo + Qbar^T dO + Kbar^T Y
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const f4 g4 = *reinterpret_cast<const f4 *>(&L.gm[16 * it + 4 * kq]);
+            f4 s = g4 * dS[it];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                s = mfma4(L.m1[(4 * kq + j) * RS + 16 * it + m], o[j], s);
+                s = mfma4(L.m2[(4 * kq + j) * RS + 16 * it + m], Y[j], s);
+            }
+            dS[it] = s;
+        }
+    }
+    if (a.ds0) put_state(a.ds0 + bh * BD * BD, dS, kq, col);
+}
+
+// ---------------------------------------------------------------------------
+// the per-chunk gradients
+//
+// One workgroup of 8 waves per chunk.  Wave w first owns value columns
+// 16w..16w+15 (the products whose columns are value columns: X, M, dM, Y,
+// dV, Bm V), then key channels 16w..16w+15 (the products whose columns are key
+// channels, contracting over the value columns: dW = dM S^T, dQbar = dO S^T,
+// dEtil = -M dSo^T, dUtil = V dSo^T, then dKbar = Tm^T dW), and finally the
+// gradients of its channels' inputs: the Grams pass dA, dBm, dR, dP to their
+// operands with every pairwise decay formed directly.
+
+constexpr int GNT = 512;
+
+struct GradLds {
+    float kb[BC * RS], et[BC * RS], ut[BC * RS];       // record: Kbar, Etil, Util
+    float tm[BC * BC], bm[BC * BC], rr[BC * BC], pp[BC * BC];
+    float gm[BD];                                        // e^gC, later d gC's exit term
+    float k[BC * KS], q[BC * KS], e[BC * KS], u[BC * KS], g[BC * KS];  // raw operands; running log-decay
+    float gc[BD];
+    float v[BC * RS], o[BC * RS];                        // V, dO
+    float mm[BC * RS], dm[BC * RS], y[BC * RS], bv[BC * RS];  // M, dM, Y, Bm V; later the per-(x, c) results
+    float dw[BC * RS];
+    float dt[BC * BC], x1[BC * BC], da[BC * BC], dbm[BC * BC], dr[BC * BC], dp[BC * BC];
+};
+
+// 16 x 16 product over 128 columns of two [16][RS] LDS matrices, X Z^T
+// (lane (kq, n) gets rows 4 kq + r, column n)
+__device__ __forceinline__ f4 gram16(const float *X, const float *Z, int m, int kq) {
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+        const f4 xa = *reinterpret_cast<const f4 *>(&X[m * RS + 16 * jt + 4 * kq]);
+        const f4 zb = *reinterpret_cast<const f4 *>(&Z[m * RS + 16 * jt + 4 * kq]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = mfma4(xa[i], zb[i], acc);
+    }
+    return acc;
+}
+
+__global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const float *rec, const float *hist,
+                                                           const float *dhist, int nch) {
+    __shared__ __attribute__((aligned(16))) GradLds L;
+    const ChunkArgs &f = a.f;
+    const int64_t T = f.T, H = f.H;
+    const int64_t ntask = f.B * H * nch;
+    const bool la_key = f.la_key, eb_key = f.eb_key, wr_key = f.wr_key, tied = f.wr == nullptr;
+    for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
+        // lane coordinates, re-derived every task so that the addresses built
+        // from them are not hoisted out of the loop (and spilled)
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int m = lane & 15, kq = lane >> 4;
+        const int64_t bh = task / nch, n = task % nch, b = bh / H, h = bh % H, t0 = n * BC;
+        const float *rc = rec + task * REC_BWD;
+        const float *Sg = hist + task * (BD * BD), *dSg = dhist + task * (BD * BD);
+        auto row_of = [&](int r) { return (b * T + t0 + r) * H + h; };
+        auto live = [&](int r) { return t0 + r < T; };
+        __syncthreads();  // the previous task is done with LDS
+
+        // ---- the chunk's record, raw operands, V and dO
+        for (int qi = tid; qi < 3 * 512; qi += GNT) {
+            const int part = qi / 512, qq = qi % 512, row = qq / 32, col = 4 * (qq % 32);
+            const f4 x = *reinterpret_cast<const f4 *>(rc + (part == 0 ? R_KB : part == 1 ? R_ET : R_UT) + 4 * qq);
+            *reinterpret_cast<f4 *>(&(part == 0 ? L.kb : part == 1 ? L.et : L.ut)[row * RS + col]) = x;
+        }
+        if (tid < 256) {  // Tm, Bm, R, P: consecutive in the record
+            const int part = tid / 64, qq = tid % 64;
+            const f4 x = *reinterpret_cast<const f4 *>(rc + R_TM + 256 * part + 4 * qq);
+            float *dst = part == 0 ? L.tm : part == 1 ? L.bm : part == 2 ? L.rr : L.pp;
+            *reinterpret_cast<f4 *>(&dst[4 * qq]) = x;
+        } else if (tid < 256 + BD) {
+            L.gm[tid - 256] = rc[R_GM + tid - 256];
+        }
+        for (int idx = tid; idx < BC * BD; idx += GNT) {
+            const int r = idx / BD, c = idx % BD;
+            float kv = 0.f, qv = 0.f, la = 0.f, e = 0.f, u = 0.f, vv = 0.f, ov = 0.f;
+            if (live(r)) {
+                const int64_t row = row_of(r);
+                kv = load_qkv(f.k, row * BD + c, f.bf16);
+                qv = f.q_scale * load_qkv(f.q, row * BD + c, f.bf16);
+                la = load_gate(f.la, la_key, row, BD, c);
+                const float bb = load_gate(f.eb, eb_key, row, BD, c);
+                const float ww = tied ? bb : load_gate(f.wr, wr_key, row, BD, c);
+                e = bb * kv;
+                u = ww * kv;
+                vv = load_qkv(f.v, row * BD + c, f.bf16);
+                ov = a.d_o[row * BD + c];
+            }
+            const int li = r * KS + c;
+            L.k[li] = kv; L.q[li] = qv; L.g[li] = la; L.e[li] = e; L.u[li] = u;
+            L.v[r * RS + c] = vv;
+            L.o[r * RS + c] = ov;
+        }
+        __syncthreads();
+        if (tid < BD) {  // running log-decay (read only by the last phase)
+            float run = 0.f;
+            for (int r = 0; r < BC; ++r) {
+                run += L.g[r * KS + tid];
+                L.g[r * KS + tid] = run;
+            }
+            L.gc[tid] = run;
+        }
+
+        // ---- value columns 16 wv + m: Bm V, X, M, dM, Y, dV
+        {
+            const int col = 16 * wv + m;
+            // S first (X, M), then dSo (dM, Y, dV): never both in registers
+            f4 S[8];
+#pragma unroll
+            for (int it = 0; it < 8; ++it)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[it][i] = Sg[(16 * it + 4 * kq + i) * BD + col];
+            float v4[4], o4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v4[j] = L.v[(4 * kq + j) * RS + col];
+                o4[j] = L.o[(4 * kq + j) * RS + col];
+            }
+            f4 BV = {0.f, 0.f, 0.f, 0.f};
+            {
+                const f4 b4 = *reinterpret_cast<const f4 *>(&L.bm[m * BC + 4 * kq]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) BV = mfma4(b4[j], v4[j], BV);
+            }
+            f4 X = BV;
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const f4 k4 = *reinterpret_cast<const f4 *>(&L.kb[m * RS + 16 * it + 4 * kq]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) X = mfma4(k4[i], S[it][i], X);
+            }
+            f4 M = {0.f, 0.f, 0.f, 0.f};
+            {
+                const f4 t4 = *reinterpret_cast<const f4 *>(&L.tm[m * BC + 4 * kq]);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) M = mfma4(t4[j], X[j], M);
+            }
+            asm volatile("" ::: "memory");  // keep the dSo loads below the S products
+            f4 dS[8];
+#pragma unroll
+            for (int it = 0; it < 8; ++it)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dS[it][i] = dSg[(16 * it + 4 * kq + i) * BD + col];
+            f4 dM = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const f4 e4 = *reinterpret_cast<const f4 *>(&L.et[m * RS + 16 * it + 4 * kq]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dM = mfma4(e4[i], dS[it][i], dM);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dM = mfma4(L.rr[(4 * kq + j) * BC + m], o4[j], dM);
+            dM = -dM;
+            f4 Y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Y = mfma4(L.tm[(4 * kq + j) * BC + m], dM[j], Y);
+            f4 dV = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int it = 0; it < 8; ++it) {
+                const f4 u4 = *reinterpret_cast<const f4 *>(&L.ut[m * RS + 16 * it + 4 * kq]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dV = mfma4(u4[i], dS[it][i], dV);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                dV = mfma4(L.pp[(4 * kq + j) * BC + m], o4[j], dV);
+                dV = mfma4(L.bm[(4 * kq + j) * BC + m], Y[j], dV);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = 4 * kq + r;
+                if (live(tok)) a.dv[row_of(tok) * BD + col] = dV[r];
+                L.mm[tok * RS + col] = M[r];
+                L.dm[tok * RS + col] = dM[r];
+                L.y[tok * RS + col] = Y[r];
+                L.bv[tok * RS + col] = BV[r];
+            }
+        }
+        __syncthreads();
+
+        // ---- key channels c = 16 wv + m: dW, dQbar, dEtil, dUtil (over the
+        //      value columns, S and dSo read as rows), the exit decay's term
+        const int c = 16 * wv + m;
+        f4 dW = {0.f, 0.f, 0.f, 0.f}, dQb = dW, dEt = dW, dUt = dW;
+        {
+            const float *srow = Sg + c * BD, *drow = dSg + c * BD;
+            float dot = 0.f;
+#pragma unroll 2
+            for (int jt = 0; jt < 8; ++jt) {
+                const f4 s4 = *reinterpret_cast<const f4 *>(srow + 16 * jt + 4 * kq);
+                const f4 d4 = *reinterpret_cast<const f4 *>(drow + 16 * jt + 4 * kq);
+                const int lo = m * RS + 16 * jt + 4 * kq;
+                const f4 am = *reinterpret_cast<const f4 *>(&L.dm[lo]), ao = *reinterpret_cast<const f4 *>(&L.o[lo]);
+                const f4 ax = *reinterpret_cast<const f4 *>(&L.mm[lo]), av = *reinterpret_cast<const f4 *>(&L.v[lo]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    dW = mfma4(am[i], s4[i], dW);
+                    dQb = mfma4(ao[i], s4[i], dQb);
+                    dEt = mfma4(ax[i], d4[i], dEt);
+                    dUt = mfma4(av[i], d4[i], dUt);
+                    dot += s4[i] * d4[i];
+                }
+            }
+            dEt = -dEt;
+            dot += __shfl_xor(dot, 16);
+            dot += __shfl_xor(dot, 32);
+            const float dgc = L.gm[c] * dot;  // e^gC (dSo . S) for channel c
+            __builtin_amdgcn_wave_barrier();
+            if (kq == 0) L.gm[c] = dgc;  // only this wave reads channel c's entry
+#pragma unroll
+            for (int r = 0; r < 4; ++r) L.dw[(4 * kq + r) * RS + c] = dW[r];
+        }
+        __syncthreads();
+
+        // ---- dKbar = Tm^T dW (registers); the 16 x 16 gradients
+        f4 dKb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dKb = mfma4(L.tm[(4 * kq + j) * BC + m], dW[j], dKb);
+        if (wv < 4) {
+            f4 x;
+            float *dst;
+            int strict = 0;
+            if (wv == 0) {         // dBm = Y V^T, strictly lower
+                x = gram16(L.y, L.v, m, kq);
+                dst = L.dbm;
+                strict = 1;
+            } else if (wv == 1) {  // dR = -dO M^T
+                x = -gram16(L.o, L.mm, m, kq);
+                dst = L.dr;
+            } else if (wv == 2) {  // dP = dO V^T
+                x = gram16(L.o, L.v, m, kq);
+                dst = L.dp;
+            } else {               // dT = dW Kbar^T + dM (Bm V)^T
+                x = gram16(L.dw, L.kb, m, kq) + gram16(L.dm, L.bv, m, kq);
+                dst = L.dt;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * kq + r;
+                dst[row * BC + m] = (m < row || (!strict && m == row)) ? x[r] : 0.f;
+            }
+        }
+        __syncthreads();
+        if (wv == 0) {  // X1 = Tm^T dT
+            f4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x = mfma4(L.tm[(4 * kq + j) * BC + m], L.dt[(4 * kq + j) * BC + m], x);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) L.x1[(4 * kq + r) * BC + m] = x[r];
+        }
+        __syncthreads();
+        if (wv == 0) {  // dA = -X1 Tm^T, strictly lower
+            f4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x = mfma4(L.x1[m * BC + 4 * kq + j], L.tm[m * BC + 4 * kq + j], x);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * kq + r;
+                L.da[row * BC + m] = m < row ? -x[r] : 0.f;
+            }
+        }
+        __syncthreads();
+
+        // ---- per (token x, channel c): the Grams' gradients with x as row and
+        //      as column, the decayed operands', then q, k and the gates
+        float *dgv = L.mm, *shr = L.dm, *dbs = L.y, *dws = L.bv;  // [16][RS] each, free now
+        const float gcc = L.gc[c];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int x = 4 * kq + r, li = x * KS + c;
+            const float gx = L.g[li];
+            float glk = 0.f, glq = 0.f, gre = 0.f, gru = 0.f;
+            for (int yy = 0; yy < x; ++yy) {  // x as the row of a Gram
+                const float d = __expf(gx - L.g[yy * KS + c]);
+                const float ey = L.e[yy * KS + c], uy = L.u[yy * KS + c];
+                glk += (L.da[x * BC + yy] * ey + L.dbm[x * BC + yy] * uy) * d;
+                glq += (L.dr[x * BC + yy] * ey + L.dp[x * BC + yy] * uy) * d;
+            }
+            const float kx = L.k[li], qx = L.q[li], ex = L.e[li], ux = L.u[li];
+            glq += L.dr[x * BC + x] * ex + L.dp[x * BC + x] * ux;
+            gre += L.dr[x * BC + x] * qx;
+            gru += L.dp[x * BC + x] * qx;
+            for (int yy = x + 1; yy < BC; ++yy) {  // x as the column
+                const float d = __expf(L.g[yy * KS + c] - gx);
+                const float ky = L.k[yy * KS + c], qy = L.q[yy * KS + c];
+                gre += (L.da[yy * BC + x] * ky + L.dr[yy * BC + x] * qy) * d;
+                gru += (L.dbm[yy * BC + x] * ky + L.dp[yy * BC + x] * qy) * d;
+            }
+            const float eg = __expf(gx), ec = __expf(gcc - gx);
+            const float dkb = dKb[r], dqb = dQb[r], det = dEt[r], dut = dUt[r];
+            const float de = gre + det * ec, du = gru + dut * ec;
+            const float dg = kx * glk + qx * glq - ex * gre - ux * gru + (dkb * kx + dqb * qx) * eg -
+                             (det * ex + dut * ux) * ec;
+            float dkk = glk + dkb * eg, dbv = 0.f, dwv = 0.f;
+            if (live(x)) {
+                const int64_t row = row_of(x);
+                const float bb = load_gate(f.eb, eb_key, row, BD, c);
+                if (tied) {
+                    dkk += (de + du) * bb;
+                    dbv = (de + du) * kx;
+                } else {
+                    const float ww = load_gate(f.wr, wr_key, row, BD, c);
+                    dkk += de * bb + du * ww;
+                    dbv = de * kx;
+                    dwv = du * kx;
+                }
+                a.dq[row * BD + c] = f.q_scale * (glq + dqb * eg);
+                a.dk[row * BD + c] = dkk;
+                if (eb_key) a.deb[row * BD + c] = dbv;
+                if (!tied && wr_key) a.dwr[row * BD + c] = dwv;
+            }
+            dgv[x * RS + c] = dg;
+            shr[x * RS + c] = (det * ex + dut * ux) * ec;  // this token's share of d gC
+            dbs[x * RS + c] = dbv;
+            dws[x * RS + c] = dwv;
+        }
+        __syncthreads();
+        // ---- d log a: the reverse running sum of dg, d gC entering at the last row
+        if (tid < BD) {
+            float run = L.gm[tid];
+            for (int x = 0; x < BC; ++x) run += shr[x * RS + tid];
+            for (int x = BC - 1; x >= 0; --x) {
+                run += dgv[x * RS + tid];
+                if (la_key) {
+                    if (live(x)) a.dla[row_of(x) * BD + tid] = run;
+                } else {
+                    dgv[x * RS + tid] = run;
+                }
+            }
+        }
+        // ---- gates with one value per token-head sum their channels
+        if (!la_key || !eb_key || (!tied && !wr_key)) {
+            __syncthreads();
+            if (tid < BC && live(tid)) {
+                const int x = tid;
+                float sl = 0.f, sb = 0.f, sw = 0.f;
+                for (int cc = 0; cc < BD; ++cc) {
+                    sl += dgv[x * RS + cc];
+                    sb += dbs[x * RS + cc];
+                    sw += dws[x * RS + cc];
+                }
+                const int64_t row = row_of(x);
+                if (!la_key) a.dla[row] = sl;
+                if (!eb_key) a.deb[row] = sb;
+                if (!tied && !wr_key) a.dwr[row] = sw;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+size_t bwd_record_bytes(int64_t chunks) { return static_cast<size_t>(chunks * REC_BWD * 4); }
+
+hipError_t launch_bwd_d128(const BwdArgs &a, float *rec, float *hist, float *dhist, int nch, hipStream_t s) {
+    const ChunkArgs &f = a.f;
+    const int64_t tasks = f.B * f.H * nch;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int64_t g1 = tasks < 8 * cus ? tasks : 8 * cus;
+    hipLaunchKernelGGL(bwd_record_kernel, dim3(static_cast<unsigned>(g1)), dim3(BNT), 0, s, a, rec, nch);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned g2 = static_cast<unsigned>(f.B * f.H * 2);
+    hipLaunchKernelGGL(bwd_state_kernel, dim3(g2), dim3(BNT), 0, s, a, static_cast<const float *>(rec), hist, nch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dgrad_kernel, dim3(g2), dim3(BNT), 0, s, a, static_cast<const float *>(rec), dhist, nch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t g3 = tasks < cus ? tasks : cus;  // one 137 KiB workgroup per CU
+    hipLaunchKernelGGL(bwd_grads128_kernel, dim3(static_cast<unsigned>(g3)), dim3(GNT), 0, s, a,
+                       static_cast<const float *>(rec), static_cast<const float *>(hist),
+                       static_cast<const float *>(dhist), nch);
+    return hipGetLastError();
+}
+
+}  // namespace gdn2

@@ -74,11 +74,11 @@ struct BwdArgs {
 int chunk_bwd_chunk(int64_t dk, int64_t dv, int C);  // internal chunk length (0: none fits)
 size_t chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int C);
 hipError_t launch_chunk_bwd(const BwdArgs &a, void *ws, hipStream_t s);
-// dk = dv = 128 (16-token chunks): the state records and the state-gradient
-// records from scans on the matrix cores, through per-chunk records of
-// bwd_record_bytes(B*H*chunks) bytes.
+// dk = dv = 128 (16-token chunks): the whole backward on the matrix cores
+// (state and state-gradient scans, per-chunk gradients), through per-chunk
+// records of bwd_record_bytes(B*H*chunks) bytes.
 size_t bwd_record_bytes(int64_t chunks);
-hipError_t launch_bwd_scans_d128(const BwdArgs &a, float *rec, float *hist, float *dhist, int nch, hipStream_t s);
+hipError_t launch_bwd_d128(const BwdArgs &a, float *rec, float *hist, float *dhist, int nch, hipStream_t s);
 
 // Recurrent decode step.
 hipError_t launch_step(const StepArgs &a, hipStream_t s);

@@ -360,6 +360,23 @@ __global__ void __launch_bounds__(BNT) bwd_dgrad_kernel(BwdArgs a, const float *
 
 constexpr int GNT = 512;
 
+// Four consecutive elements (16-byte or 8-byte aligned) of q/k/v, bf16 or fp32.
+__device__ __forceinline__ f4 load4_qkv(const void *p, int64_t i, int bf16) {
+    if (bf16) {
+        const uint2 w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + i);
+        return f4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                  __uint_as_float(w.y & 0xffff0000u)};
+    }
+    return *reinterpret_cast<const f4 *>(static_cast<const float *>(p) + i);
+}
+
+// Gate of token-head `row` at channels c4 .. c4 + 3 (one value per head broadcast).
+__device__ __forceinline__ f4 load4_gate(const float *g, int per_key, int64_t row, int c4) {
+    if (per_key) return *reinterpret_cast<const f4 *>(g + row * BD + c4);
+    const float x = g[row];
+    return f4{x, x, x, x};
+}
+
 struct GradLds {
     float kb[BC * RS], et[BC * RS], ut[BC * RS];       // record: Kbar, Etil, Util
     float tm[BC * BC], bm[BC * BC], rr[BC * BC], pp[BC * BC];
@@ -370,6 +387,7 @@ struct GradLds {
     float mm[BC * RS], dm[BC * RS], y[BC * RS], bv[BC * RS];  // M, dM, Y, Bm V; later the per-(x, c) results
     float dw[BC * RS];
     float dt[BC * BC], x1[BC * BC], da[BC * BC], dbm[BC * BC], dr[BC * BC], dp[BC * BC];
+    float daT[BC * BC], dbmT[BC * BC], drT[BC * BC], dpT[BC * BC];  // transposes (columns as rows)
 };
 
 // 16 x 16 product over 128 columns of two [16][RS] LDS matrices, X Z^T
@@ -386,6 +404,17 @@ __device__ __forceinline__ f4 gram16(const float *X, const float *Z, int m, int 
     return acc;
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses,
+// not for its global loads (so that prefetches stay in flight across it).
+// The waves share data through LDS alone; global memory is read-only input
+// or write-only output here.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const float *rec, const float *hist,
                                                            const float *dhist, int nch) {
     __shared__ __attribute__((aligned(16))) GradLds L;
@@ -393,6 +422,21 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
     const int64_t T = f.T, H = f.H;
     const int64_t ntask = f.B * H * nch;
     const bool la_key = f.la_key, eb_key = f.eb_key, wr_key = f.wr_key, tied = f.wr == nullptr;
+    // this wave's value columns of S and dSo, consumed by the value products;
+    // the next task's are loaded while this one finishes
+    f4 S[8], dS[8];
+    auto load_sd = [&](int64_t t) __attribute__((always_inline)) {
+        const int vc = 16 * (threadIdx.x >> 6) + (threadIdx.x & 15), kk = (threadIdx.x >> 4) & 3;
+        const float *sg = hist + t * (BD * BD), *dsg = dhist + t * (BD * BD);
+#pragma unroll
+        for (int it = 0; it < 8; ++it)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                S[it][i] = sg[(16 * it + 4 * kk + i) * BD + vc];
+                dS[it][i] = dsg[(16 * it + 4 * kk + i) * BD + vc];
+            }
+    };
+    if (static_cast<int64_t>(blockIdx.x) < ntask) load_sd(blockIdx.x);
     for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
         // lane coordinates, re-derived every task so that the addresses built
         // from them are not hoisted out of the loop (and spilled)
@@ -405,7 +449,9 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
         const float *Sg = hist + task * (BD * BD), *dSg = dhist + task * (BD * BD);
         auto row_of = [&](int r) { return (b * T + t0 + r) * H + h; };
         auto live = [&](int r) { return t0 + r < T; };
-        __syncthreads();  // the previous task is done with LDS
+        lds_barrier();  // the previous task is done with LDS
+
+        const int vcol = 16 * wv + m;
 
         // ---- the chunk's record, raw operands, V and dO
         for (int qi = tid; qi < 3 * 512; qi += GNT) {
@@ -421,27 +467,34 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
         } else if (tid < 256 + BD) {
             L.gm[tid - 256] = rc[R_GM + tid - 256];
         }
-        for (int idx = tid; idx < BC * BD; idx += GNT) {
-            const int r = idx / BD, c = idx % BD;
-            float kv = 0.f, qv = 0.f, la = 0.f, e = 0.f, u = 0.f, vv = 0.f, ov = 0.f;
+        f4 bb, ww;  // erase / write gates of token tid / 32, channels c4 .. c4 + 3 (for the last phase)
+        {  // token r = tid / 32, channels c4 .. c4 + 3
+            const int r = tid >> 5, c4 = 4 * (tid & 31);
+            const f4 z = {0.f, 0.f, 0.f, 0.f};
+            f4 kv = z, qv = z, la = z, vv = z, ov = z;
+            bb = z;
+            ww = z;
             if (live(r)) {
                 const int64_t row = row_of(r);
-                kv = load_qkv(f.k, row * BD + c, f.bf16);
-                qv = f.q_scale * load_qkv(f.q, row * BD + c, f.bf16);
-                la = load_gate(f.la, la_key, row, BD, c);
-                const float bb = load_gate(f.eb, eb_key, row, BD, c);
-                const float ww = tied ? bb : load_gate(f.wr, wr_key, row, BD, c);
-                e = bb * kv;
-                u = ww * kv;
-                vv = load_qkv(f.v, row * BD + c, f.bf16);
-                ov = a.d_o[row * BD + c];
+                kv = load4_qkv(f.k, row * BD + c4, f.bf16);
+                qv = f.q_scale * load4_qkv(f.q, row * BD + c4, f.bf16);
+                la = load4_gate(f.la, la_key, row, c4);
+                bb = load4_gate(f.eb, eb_key, row, c4);
+                ww = tied ? bb : load4_gate(f.wr, wr_key, row, c4);
+                vv = load4_qkv(f.v, row * BD + c4, f.bf16);
+                ov = *reinterpret_cast<const f4 *>(a.d_o + row * BD + c4);
             }
-            const int li = r * KS + c;
-            L.k[li] = kv; L.q[li] = qv; L.g[li] = la; L.e[li] = e; L.u[li] = u;
-            L.v[r * RS + c] = vv;
-            L.o[r * RS + c] = ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int li = r * KS + c4 + i;
+                L.k[li] = kv[i]; L.q[li] = qv[i]; L.g[li] = la[i];
+                L.e[li] = bb[i] * kv[i];
+                L.u[li] = ww[i] * kv[i];
+            }
+            *reinterpret_cast<f4 *>(&L.v[r * RS + c4]) = vv;
+            *reinterpret_cast<f4 *>(&L.o[r * RS + c4]) = ov;
         }
-        __syncthreads();
+        lds_barrier();
         if (tid < BD) {  // running log-decay (read only by the last phase)
             float run = 0.f;
             for (int r = 0; r < BC; ++r) {
@@ -453,13 +506,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
 
         // ---- value columns 16 wv + m: Bm V, X, M, dM, Y, dV
         {
-            const int col = 16 * wv + m;
-            // S first (X, M), then dSo (dM, Y, dV): never both in registers
-            f4 S[8];
-#pragma unroll
-            for (int it = 0; it < 8; ++it)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) S[it][i] = Sg[(16 * it + 4 * kq + i) * BD + col];
+            const int col = vcol;
             float v4[4], o4[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -485,12 +532,6 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
 #pragma unroll
                 for (int j = 0; j < 4; ++j) M = mfma4(t4[j], X[j], M);
             }
-            asm volatile("" ::: "memory");  // keep the dSo loads below the S products
-            f4 dS[8];
-#pragma unroll
-            for (int it = 0; it < 8; ++it)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dS[it][i] = dSg[(16 * it + 4 * kq + i) * BD + col];
             f4 dM = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
@@ -526,7 +567,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
                 L.bv[tok * RS + col] = BV[r];
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- key channels c = 16 wv + m: dW, dQbar, dEtil, dUtil (over the
         //      value columns, S and dSo read as rows), the exit decay's term
@@ -560,7 +601,8 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
 #pragma unroll
             for (int r = 0; r < 4; ++r) L.dw[(4 * kq + r) * RS + c] = dW[r];
         }
-        __syncthreads();
+        if (task + gridDim.x < ntask) load_sd(task + gridDim.x);  // in flight until the next task
+        lds_barrier();
 
         // ---- dKbar = Tm^T dW (registers); the 16 x 16 gradients
         f4 dKb = {0.f, 0.f, 0.f, 0.f};
@@ -568,29 +610,50 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
         for (int j = 0; j < 4; ++j) dKb = mfma4(L.tm[(4 * kq + j) * BC + m], dW[j], dKb);
         if (wv < 4) {
             f4 x;
-            float *dst;
+            float *dst, *dstT;
             int strict = 0;
             if (wv == 0) {         // dBm = Y V^T, strictly lower
                 x = gram16(L.y, L.v, m, kq);
                 dst = L.dbm;
+                dstT = L.dbmT;
                 strict = 1;
             } else if (wv == 1) {  // dR = -dO M^T
                 x = -gram16(L.o, L.mm, m, kq);
                 dst = L.dr;
+                dstT = L.drT;
             } else if (wv == 2) {  // dP = dO V^T
                 x = gram16(L.o, L.v, m, kq);
                 dst = L.dp;
+                dstT = L.dpT;
             } else {               // dT = dW Kbar^T + dM (Bm V)^T
                 x = gram16(L.dw, L.kb, m, kq) + gram16(L.dm, L.bv, m, kq);
                 dst = L.dt;
+                dstT = L.x1;       // (not read)
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 4 * kq + r;
-                dst[row * BC + m] = (m < row || (!strict && m == row)) ? x[r] : 0.f;
+                const float val = (m < row || (!strict && m == row)) ? x[r] : 0.f;
+                dst[row * BC + m] = val;
+                dstT[m * BC + row] = val;
             }
         }
-        __syncthreads();
+        lds_barrier();
+        // the channel gradients, for the (token, channel) phase below: lane =
+        // channel there (V, dO, Kbar, Etil, Util and dW are no longer read)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int li = (4 * kq + r) * RS + c;
+            L.kb[li] = dKb[r];
+            L.et[li] = dQb[r];
+            L.ut[li] = dEt[r];
+            L.v[li] = dUt[r];
+        }
+        {  // the gates, into the regions of dO and dW (no longer read)
+            const int r = tid >> 5, c4 = 4 * (tid & 31);
+            *reinterpret_cast<f4 *>(&L.o[r * RS + c4]) = bb;
+            *reinterpret_cast<f4 *>(&L.dw[r * RS + c4]) = ww;
+        }
         if (wv == 0) {  // X1 = Tm^T dT
             f4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -598,7 +661,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
 #pragma unroll
             for (int r = 0; r < 4; ++r) L.x1[(4 * kq + r) * BC + m] = x[r];
         }
-        __syncthreads();
+        lds_barrier();
         if (wv == 0) {  // dA = -X1 Tm^T, strictly lower
             f4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -606,65 +669,86 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 4 * kq + r;
-                L.da[row * BC + m] = m < row ? -x[r] : 0.f;
+                const float val = m < row ? -x[r] : 0.f;
+                L.da[row * BC + m] = val;
+                L.daT[m * BC + row] = val;
             }
         }
-        __syncthreads();
+        lds_barrier();
 
         // ---- per (token x, channel c): the Grams' gradients with x as row and
-        //      as column, the decayed operands', then q, k and the gates
-        float *dgv = L.mm, *shr = L.dm, *dbs = L.y, *dws = L.bv;  // [16][RS] each, free now
-        const float gcc = L.gc[c];
+        //      as column, the decayed operands', then q, k and the gates.  Wave
+        //      w takes tokens 4 (w / 2) .. +3 of channels 64 (w % 2) + lane, so
+        //      a token is uniform across the wave and the rows (and, through the
+        //      transposes, the columns) of dA, dBm, dR, dP are broadcast reads.
+        {
+            float *dgv = L.mm, *shr = L.dm, *dbs = L.y, *dws = L.bv;  // [16][RS] each, free now
+            const int cc = 64 * (wv & 1) + lane, x0 = 4 * (wv >> 1);
+            const float gcc = L.gc[cc];
+            float gy[BC], ey[BC], uy[BC], ky[BC], qy[BC];  // channel cc of every token
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int x = 4 * kq + r, li = x * KS + c;
-            const float gx = L.g[li];
-            float glk = 0.f, glq = 0.f, gre = 0.f, gru = 0.f;
-            for (int yy = 0; yy < x; ++yy) {  // x as the row of a Gram
-                const float d = __expf(gx - L.g[yy * KS + c]);
-                const float ey = L.e[yy * KS + c], uy = L.u[yy * KS + c];
-                glk += (L.da[x * BC + yy] * ey + L.dbm[x * BC + yy] * uy) * d;
-                glq += (L.dr[x * BC + yy] * ey + L.dp[x * BC + yy] * uy) * d;
+            for (int yy = 0; yy < BC; ++yy) {
+                const int ly = yy * KS + cc;
+                gy[yy] = L.g[ly]; ey[yy] = L.e[ly]; uy[yy] = L.u[ly]; ky[yy] = L.k[ly]; qy[yy] = L.q[ly];
             }
-            const float kx = L.k[li], qx = L.q[li], ex = L.e[li], ux = L.u[li];
-            glq += L.dr[x * BC + x] * ex + L.dp[x * BC + x] * ux;
-            gre += L.dr[x * BC + x] * qx;
-            gru += L.dp[x * BC + x] * qx;
-            for (int yy = x + 1; yy < BC; ++yy) {  // x as the column
-                const float d = __expf(L.g[yy * KS + c] - gx);
-                const float ky = L.k[yy * KS + c], qy = L.q[yy * KS + c];
-                gre += (L.da[yy * BC + x] * ky + L.dr[yy * BC + x] * qy) * d;
-                gru += (L.dbm[yy * BC + x] * ky + L.dp[yy * BC + x] * qy) * d;
-            }
-            const float eg = __expf(gx), ec = __expf(gcc - gx);
-            const float dkb = dKb[r], dqb = dQb[r], det = dEt[r], dut = dUt[r];
-            const float de = gre + det * ec, du = gru + dut * ec;
-            const float dg = kx * glk + qx * glq - ex * gre - ux * gru + (dkb * kx + dqb * qx) * eg -
-                             (det * ex + dut * ux) * ec;
-            float dkk = glk + dkb * eg, dbv = 0.f, dwv = 0.f;
-            if (live(x)) {
-                const int64_t row = row_of(x);
-                const float bb = load_gate(f.eb, eb_key, row, BD, c);
-                if (tied) {
-                    dkk += (de + du) * bb;
-                    dbv = (de + du) * kx;
-                } else {
-                    const float ww = load_gate(f.wr, wr_key, row, BD, c);
-                    dkk += de * bb + du * ww;
-                    dbv = de * kx;
-                    dwv = du * kx;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int x = x0 + r;
+                const float gx = L.g[x * KS + cc];
+                // x as the row (dA[x][y] ...: zero for y >= x, dR/dP also at y = x)
+                // and as the column (dA[y][x] ... via the transposes), with the
+                // pairwise decay e^(g_x - g_y) for y before x, e^(g_y - g_x) after
+                float glk = 0.f, glq = 0.f, gre = 0.f, gru = 0.f;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int o4 = x * BC + 4 * jj;
+                    const f4 ra = *reinterpret_cast<const f4 *>(&L.da[o4]), rb = *reinterpret_cast<const f4 *>(&L.dbm[o4]);
+                    const f4 rr = *reinterpret_cast<const f4 *>(&L.dr[o4]), rp = *reinterpret_cast<const f4 *>(&L.dp[o4]);
+                    const f4 ca = *reinterpret_cast<const f4 *>(&L.daT[o4]), cb = *reinterpret_cast<const f4 *>(&L.dbmT[o4]);
+                    const f4 cr = *reinterpret_cast<const f4 *>(&L.drT[o4]), cp = *reinterpret_cast<const f4 *>(&L.dpT[o4]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int yy = 4 * jj + e;
+                        const float d = __expf(yy < x ? gx - gy[yy] : gy[yy] - gx);
+                        glk += (ra[e] * ey[yy] + rb[e] * uy[yy]) * d;
+                        glq += (rr[e] * ey[yy] + rp[e] * uy[yy]) * d;
+                        gre += (ca[e] * ky[yy] + cr[e] * qy[yy]) * d;
+                        gru += (cb[e] * ky[yy] + cp[e] * qy[yy]) * d;
+                    }
                 }
-                a.dq[row * BD + c] = f.q_scale * (glq + dqb * eg);
-                a.dk[row * BD + c] = dkk;
-                if (eb_key) a.deb[row * BD + c] = dbv;
-                if (!tied && wr_key) a.dwr[row * BD + c] = dwv;
+                const int li = x * KS + cc, lr = x * RS + cc;
+                const float kx = L.k[li], qx = L.q[li], ex = L.e[li], ux = L.u[li];
+                const float eg = __expf(gx), ec = __expf(gcc - gx);
+                const float dkb = L.kb[lr], dqb = L.et[lr], det = L.ut[lr], dut = L.v[lr];
+                const float de = gre + det * ec, du = gru + dut * ec;
+                const float dg = kx * glk + qx * glq - ex * gre - ux * gru + (dkb * kx + dqb * qx) * eg -
+                                 (det * ex + dut * ux) * ec;
+                float dkk = glk + dkb * eg, dbv = 0.f, dwv = 0.f;
+                if (live(x)) {
+                    const int64_t row = row_of(x);
+                    const float bx = L.o[lr];
+                    if (tied) {
+                        dkk += (de + du) * bx;
+                        dbv = (de + du) * kx;
+                    } else {
+                        const float wx = L.dw[lr];
+                        dkk += de * bx + du * wx;
+                        dbv = de * kx;
+                        dwv = du * kx;
+                    }
+                    a.dq[row * BD + cc] = f.q_scale * (glq + dqb * eg);
+                    a.dk[row * BD + cc] = dkk;
+                    if (eb_key) a.deb[row * BD + cc] = dbv;
+                    if (!tied && wr_key) a.dwr[row * BD + cc] = dwv;
+                }
+                dgv[lr] = dg;
+                shr[lr] = (det * ex + dut * ux) * ec;  // this token's share of d gC
+                dbs[lr] = dbv;
+                dws[lr] = dwv;
             }
-            dgv[x * RS + c] = dg;
-            shr[x * RS + c] = (det * ex + dut * ux) * ec;  // this token's share of d gC
-            dbs[x * RS + c] = dbv;
-            dws[x * RS + c] = dwv;
         }
-        __syncthreads();
+        float *dgv = L.mm, *shr = L.dm, *dbs = L.y, *dws = L.bv;
+        lds_barrier();
         // ---- d log a: the reverse running sum of dg, d gC entering at the last row
         if (tid < BD) {
             float run = L.gm[tid];
@@ -680,7 +764,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
         }
         // ---- gates with one value per token-head sum their channels
         if (!la_key || !eb_key || (!tied && !wr_key)) {
-            __syncthreads();
+            lds_barrier();
             if (tid < BC && live(tid)) {
                 const int x = tid;
                 float sl = 0.f, sb = 0.f, sw = 0.f;

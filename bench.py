@@ -36,6 +36,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 CHUNK_SOURCES = ("chunk_split.hip", "chunk_common.h", "chunk_mfma.hip", "chunk_general.hip",
                  "kernels.h", "common.h")
 DECODE_SOURCES = ("decode.hip", "kernels.h", "common.h")
+BWD_SOURCES = ("chunk_bwd.hip", "chunk_bwd_mfma.hip", "kernels.h", "common.h")
 
 
 def log(msg):
@@ -235,10 +236,12 @@ def time_backward(w, inp, torch, steps):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     k = ev0.elapsed_time(ev1) / steps
-    return {"workload": f"{w.name}: gradients of q, k, v, gates and S0 (general fp32 kernels)",
+    return {"workload": f"{w.name}: gradients of q, k, v, gates and S0 (fp32 matrix-core kernels: chunk "
+                        f"records, state and state-gradient scans, per-chunk gradients)",
             "ms_per_step": round(ms, 3), "kernel_ms": round(k, 3),
             "value": round(w.B * w.T / (ms * 1e-3), 1), "unit": "tokens/s",
-            "roofline": roofline_hbm(bwd_bytes(w), k), "algorithmic_bytes_per_launch": bwd_bytes(w)}
+            "roofline": roofline_hbm(bwd_bytes(w), k, read_traffic("chunk_bwd", w.name, source_hash(BWD_SOURCES))),
+            "algorithmic_bytes_per_launch": bwd_bytes(w)}
 
 
 def time_packed(w, inp, torch, steps, n_seq=12):

@@ -19,6 +19,14 @@ special cases that follow from the recurrence by hand:
   dv = (s q . u) dO + dS_1^T u.
 A dropped term, a wrong sign, a transposed operand or a gradient taken
 against the stale state fails one of these.
+
+The value-write form and the raw-input preparation are pinned the same way
+(finite differences), and further: the value-write forward to the C oracle's;
+with one erase and one write gate per head the two forms are the same
+operation, so their gradients must agree; the torch input preparation to the
+numpy one (itself pinned to scipy); and the raw-input gradients to the
+prepared-input gradients through the chain rule of -softplus, sigmoid and the
+L2 normalisation written out by hand.
 """
 import json
 import math
@@ -28,8 +36,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.oracle import gdn2_forward
-from oracle.oracle_bwd import gdn2_backward, recurrence
+from oracle.oracle import gdn2_forward, prepare_inputs
+from oracle.oracle_bwd import gdn2_backward, prepare, recurrence
 
 
 def _rand(shape, r, lo=None):
@@ -47,12 +55,35 @@ def _case(r, B=1, T=4, H=2, dk=3, dv=2, gates="key", tied=False, s0=True):
         S0=r.standard_normal((B, H, dk, dv)) * 0.5 if s0 else None)
 
 
-def _loss(inp, d_o, d_state, q_scale):
-    """L = <d_o, o> + <d_state, S_T> evaluated with the differentiable forward."""
+def _loss(inp, d_o, d_state, q_scale, value_write=False, raw=False):
+    """L = <d_o, o> + <d_state, S_T> evaluated with the differentiable forward
+    (``raw``: the gate entries are logits and q, k are normalised first)."""
     t = lambda x: None if x is None else torch.as_tensor(np.asarray(x, dtype=np.float64))
-    o, S = recurrence(t(inp["q"]), t(inp["k"]), t(inp["v"]), t(inp["log_decay"]), t(inp["erase"]),
-                      t(inp["write"]), t(inp["S0"]), q_scale)
+    q, k, la, b, w = t(inp["q"]), t(inp["k"]), t(inp["log_decay"]), t(inp["erase"]), t(inp["write"])
+    if raw:
+        q, k, la, b, w = prepare(q, k, la, b, w)
+    o, S = recurrence(q, k, t(inp["v"]), la, b, w, t(inp["S0"]), q_scale, value_write)
     return float((o.numpy() * d_o).sum() + (S.numpy() * d_state).sum())
+
+
+def _fd_check(inp, g, d_o, d_state, qs, names, **kw):
+    h = 1e-6
+    for key, gkey in names:
+        x = inp[key]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _loss(inp, d_o, d_state, qs, **kw)
+            x[idx] = old - h
+            lm = _loss(inp, d_o, d_state, qs, **kw)
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g[gkey], fd, rtol=1e-6, atol=1e-8, err_msg=key)
+
+
+NAMES = [("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_decay", "d_log_decay"), ("erase", "d_erase"),
+         ("S0", "d_state0"), ("write", "d_write")]
 
 
 def test_forward_matches_page_examples(golden_dir):
@@ -96,21 +127,7 @@ def test_gradients_match_finite_differences(gates, tied, s0):
     d_o = r.standard_normal(inp["v"].shape)
     d_state = r.standard_normal(inp["S0"].shape)
     g = gdn2_backward(**inp, d_o=d_o, d_state=d_state, q_scale=qs)
-    names = [("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_decay", "d_log_decay"),
-             ("erase", "d_erase"), ("S0", "d_state0")] + ([] if tied else [("write", "d_write")])
-    h = 1e-6
-    for key, gkey in names:
-        x = inp[key]
-        fd = np.zeros_like(x)
-        for idx in np.ndindex(x.shape):
-            old = x[idx]
-            x[idx] = old + h
-            lp = _loss(inp, d_o, d_state, qs)
-            x[idx] = old - h
-            lm = _loss(inp, d_o, d_state, qs)
-            x[idx] = old
-            fd[idx] = (lp - lm) / (2 * h)
-        np.testing.assert_allclose(g[gkey], fd, rtol=1e-6, atol=1e-8, err_msg=key)
+    _fd_check(inp, g, d_o, d_state, qs, NAMES[:6] + ([] if tied else NAMES[6:]))
 
 
 def test_hold_closed_form():
@@ -168,3 +185,98 @@ def test_no_cotangent_gives_zero_gradients():
     g = gdn2_backward(**inp)
     for key in ("dq", "dk", "dv", "d_log_decay", "d_erase", "d_write", "d_state0"):
         assert np.abs(g[key]).max() == 0
+
+
+def _vw_case(r, gates, B=1, T=4, H=2, dk=3, dv=2):
+    """A value-write case: the write gate per value channel (or per head)."""
+    inp = _case(r, B, T, H, dk, dv, gates=gates)
+    ws = (B, T, H, dv) if gates == "key" else (B, T, H)
+    inp["write"] = 1 / (1 + np.exp(-r.standard_normal(ws)))
+    return inp
+
+
+def test_value_write_forward_matches_c_oracle():
+    r = np.random.default_rng(21)
+    inp = _vw_case(r, "key", B=2, T=7, H=2, dk=5, dv=4)
+    t = lambda x: torch.as_tensor(np.asarray(x, dtype=np.float64))
+    o_t, S_t = recurrence(*[t(inp[n]) for n in ("q", "k", "v", "log_decay", "erase", "write", "S0")],
+                          q_scale=1.0, value_write=True)
+    o_c, S_c = gdn2_forward(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"],
+                            inp["S0"], value_write=True)
+    np.testing.assert_allclose(o_t.numpy(), o_c, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(S_t.numpy(), S_c, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("gates", ["key", "head"])
+def test_value_write_gradients_match_finite_differences(gates):
+    r = np.random.default_rng(22)
+    inp = _vw_case(r, gates)
+    qs = 0.8
+    d_o, d_state = r.standard_normal(inp["v"].shape), r.standard_normal(inp["S0"].shape)
+    g = gdn2_backward(**inp, d_o=d_o, d_state=d_state, q_scale=qs, value_write=True)
+    _fd_check(inp, g, d_o, d_state, qs, NAMES, value_write=True)
+
+
+def test_forms_agree_with_scalar_gates():
+    # one erase and one write gate per head: (I - k (b k)^T) Sbar + k (w v)^T
+    # is Sbar - (b k)(k^T Sbar) + (w k) v^T, so every gradient is the same
+    r = np.random.default_rng(23)
+    inp = _case(r, B=2, T=6, H=2, dk=4, dv=3, gates="head")
+    d_o, d_state = r.standard_normal(inp["v"].shape), r.standard_normal(inp["S0"].shape)
+    gk = gdn2_backward(**inp, d_o=d_o, d_state=d_state, q_scale=1.1)
+    gv = gdn2_backward(**inp, d_o=d_o, d_state=d_state, q_scale=1.1, value_write=True)
+    for key in ("dq", "dk", "dv", "d_log_decay", "d_erase", "d_write", "d_state0"):
+        np.testing.assert_allclose(gv[key], gk[key], rtol=1e-11, atol=1e-12, err_msg=key)
+
+
+def _raw_case(r, gates="key", B=1, T=4, H=2, dk=3, dv=2):
+    gs = (B, T, H, dk) if gates == "key" else (B, T, H)
+    return dict(q=r.standard_normal((B, T, H, dk)) * 2, k=r.standard_normal((B, T, H, dk)) * 0.7,
+                v=r.standard_normal((B, T, H, dv)), log_decay=r.standard_normal(gs) - 1.0,
+                erase=r.standard_normal(gs), write=r.standard_normal(gs),
+                S0=r.standard_normal((B, H, dk, dv)) * 0.5)
+
+
+def test_torch_preparation_matches_numpy():
+    r = np.random.default_rng(24)
+    inp = _raw_case(r, B=2, T=5, H=2, dk=6)
+    inp["q"][0, 1, 1] = 0.0  # a zero row stays zero
+    t = lambda x: torch.as_tensor(np.asarray(x, dtype=np.float64))
+    got = prepare(t(inp["q"]), t(inp["k"]), t(inp["log_decay"]), t(inp["erase"]), t(inp["write"]))
+    want = prepare_inputs(inp["q"], inp["k"], inp["log_decay"], inp["erase"], inp["write"])
+    for a, b in zip(got, want):
+        np.testing.assert_allclose(a.numpy(), b, rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("gates,vw", [("key", False), ("head", False), ("key", True)])
+def test_raw_input_gradients_match_finite_differences(gates, vw):
+    r = np.random.default_rng(25)
+    inp = _raw_case(r, gates)
+    if vw:
+        inp["write"] = r.standard_normal(inp["v"].shape if gates == "key" else inp["v"].shape[:3])
+    qs = 0.9
+    d_o, d_state = r.standard_normal(inp["v"].shape), r.standard_normal(inp["S0"].shape)
+    g = gdn2_backward(**inp, d_o=d_o, d_state=d_state, q_scale=qs, raw=True, value_write=vw)
+    _fd_check(inp, g, d_o, d_state, qs, NAMES, raw=True, value_write=vw)
+
+
+def test_raw_gradients_by_the_chain_rule():
+    # d/dx (-softplus x) = -sigmoid x, d/dx sigmoid x = s (1 - s), and for
+    # n = x / |x|: dx = (dn - n (n . dn)) / |x|
+    r = np.random.default_rng(26)
+    raw = _raw_case(r, "key", B=2, T=5, H=2, dk=4, dv=3)
+    d_o, d_state = r.standard_normal(raw["v"].shape), r.standard_normal(raw["S0"].shape)
+    g_raw = gdn2_backward(**raw, d_o=d_o, d_state=d_state, raw=True)
+    q, k, la, b, w = prepare_inputs(raw["q"], raw["k"], raw["log_decay"], raw["erase"], raw["write"])
+    g = gdn2_backward(q, k, raw["v"], la, b, w, raw["S0"], d_o=d_o, d_state=d_state)
+    sig = lambda x: 1 / (1 + np.exp(-x))
+    np.testing.assert_allclose(g_raw["d_log_decay"], -sig(raw["log_decay"]) * g["d_log_decay"], rtol=1e-10,
+                               atol=1e-12)
+    for key, x in (("d_erase", raw["erase"]), ("d_write", raw["write"])):
+        np.testing.assert_allclose(g_raw[key], sig(x) * (1 - sig(x)) * g[key], rtol=1e-10, atol=1e-12)
+    for key, x, n in (("dq", raw["q"], q), ("dk", raw["k"], k)):
+        dn = g[key]
+        want = (dn - n * (n * dn).sum(-1, keepdims=True)) / np.linalg.norm(x, axis=-1, keepdims=True)
+        np.testing.assert_allclose(g_raw[key], want, rtol=1e-10, atol=1e-12)
+    for key in ("dv", "d_state0"):
+        np.testing.assert_allclose(g_raw[key], g[key], rtol=1e-12, atol=1e-12)

@@ -293,20 +293,22 @@ def chunk_bwd_workspace(desc: Gdn2Desc) -> int:
 
 
 def chunk_bwd(q, k, v, log_decay, erase, write, state0, d_o, d_state=None, chunk=64,
-              q_scale=1.0, want_state0=True, workspace=None):
+              q_scale=1.0, want_state0=True, workspace=None, value_write=False, qk_l2norm=False):
     """Gradients of <d_o, o> + <d_state, S_T> for the chunkwise forward.
 
-    Inputs as for ``chunk_fwd``; d_o [B,T,H,dv] fp32; d_state [B,H,dk,dv]
-    fp32 or None (zeros).  Returns a dict of fp32 tensors: dq, dk, dv,
-    d_log_decay, d_erase, d_write (None when tied) shaped like their inputs,
-    and d_state0 (None unless ``want_state0``).  ``workspace``: None
-    allocates it, or a uint8 device tensor of at least chunk_bwd_workspace()
-    bytes.
+    Inputs as for ``chunk_fwd`` (``value_write``, bf16 gate logits and
+    ``qk_l2norm`` included: the gradients are then those of the logits and
+    of the raw q, k); d_o [B,T,H,dv] fp32; d_state [B,H,dk,dv] fp32 or None
+    (zeros).  Returns a dict of fp32 tensors: dq, dk, dv, d_log_decay,
+    d_erase, d_write (None when tied) shaped like their inputs, and d_state0
+    (None unless ``want_state0``).  ``workspace``: None allocates it, or a
+    uint8 device tensor of at least chunk_bwd_workspace() bytes.
     """
     import torch
     B, T, H, dk = k.shape
     dv = v.shape[-1]
-    desc = _desc_for(q, k, v, log_decay, erase, write, (B, T, H), B, T, H, chunk, q_scale)
+    desc = _desc_for(q, k, v, log_decay, erase, write, (B, T, H), B, T, H, chunk, q_scale, value_write,
+                     qk_l2norm)
     dev = k.device
     f32 = (torch.float32,)
     if state0 is not None:
@@ -314,7 +316,7 @@ def chunk_bwd(q, k, v, log_decay, erase, write, state0, d_o, d_state=None, chunk
     _check(d_o, "d_o", (B, T, H, dv), f32, dev)
     if d_state is not None:
         _check(d_state, "d_state", (B, H, dk, dv), f32, dev)
-    new = lambda t: torch.empty(tuple(t.shape), dtype=torch.float32, device=dev)
+    new = lambda t: torch.empty(tuple(t.shape), dtype=torch.float32, device=dev)  # fp32 whatever t's dtype
     g = dict(dq=new(q), dk=new(k), dv=new(v), d_log_decay=new(log_decay), d_erase=new(erase),
              d_write=None if write is None else new(write),
              d_state0=torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev) if want_state0 else None)

@@ -288,10 +288,10 @@ gdn2_status gdn2_chunk_bwd_workspace(const gdn2_desc *desc, size_t *bytes) {
     if (st != GDN2_OK) return st;
     if (desc->chunk != 16 && desc->chunk != 32 && desc->chunk != 64) return GDN2_ERR_UNSUPPORTED;
     if (!gdn2::chunk_bwd_chunk(desc->dk, desc->dv, static_cast<int>(desc->chunk))) return GDN2_ERR_UNSUPPORTED;
-    // no backward of the value-write form or of fused input preparation
-    if (desc->form != GDN2_FORM_KEY || desc->gate_logits || desc->qk_l2norm) return GDN2_ERR_UNSUPPORTED;
-    *bytes = gdn2::chunk_bwd_workspace(desc->batch, desc->heads, desc->seqlen, desc->dk, desc->dv,
-                                       static_cast<int>(desc->chunk));
+    static const float placeholder = 0.f;  // stands for an untied write gate
+    const ChunkArgs a = args_of(desc, nullptr, nullptr, nullptr, nullptr, nullptr, &placeholder, nullptr,
+                                nullptr, nullptr);
+    *bytes = gdn2::chunk_bwd_workspace(a);
     return GDN2_OK;
 }
 
@@ -317,11 +317,15 @@ gdn2_status gdn2_chunk_bwd(const gdn2_desc *d, const void *q, const void *k, con
                        span_of(log_decay, sz.la), span_of(erase, sz.eb),
                        span_of(tied ? nullptr : write, sz.wr), span_of(state0, sz.st),
                        span_of(d_o, sz.o), span_of(d_state_out, sz.st)};
-    // gradients are fp32 and shaped like their inputs
+    // gradients are fp32 and shaped like their inputs (those of bf16 gate
+    // logits too)
     const int64_t f32 = d->qkv_dtype == GDN2_BF16 ? 2 : 1;
+    gdn2_desc d4 = *d;
+    d4.gate_logits = 0;
+    const Sizes sg = sizes_of(&d4, T);
     const Span out[] = {span_of(dq, sz.qk * f32), span_of(dk, sz.qk * f32), span_of(dv, sz.v * f32),
-                        span_of(d_log_decay, sz.la), span_of(d_erase, sz.eb),
-                        span_of(tied ? nullptr : d_write, sz.wr), span_of(d_state0, sz.st),
+                        span_of(d_log_decay, sg.la), span_of(d_erase, sg.eb),
+                        span_of(tied ? nullptr : d_write, sg.wr), span_of(d_state0, sz.st),
                         span_of(workspace, need > 0 ? static_cast<int64_t>(ws_bytes) : 0)};
     const int nout = sizeof(out) / sizeof(out[0]);
     for (int i = 0; i < nout; ++i) {

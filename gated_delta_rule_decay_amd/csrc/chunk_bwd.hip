@@ -121,7 +121,9 @@ __global__ void __launch_bounds__(kRevThreads) bwd_dstate_kernel(BwdArgs a, int 
                 kv = load_qkv(f.k, row * dk + c, f.bf16);
                 qv = f.q_scale * load_qkv(f.q, row * dk + c, f.bf16);
                 la = load_gate(f.la, f.la_key, row, dk, c);
-                e = load_gate(f.eb, f.eb_key, row, dk, c) * kv;
+                const float bb = load_gate(f.eb, f.eb_key, row, dk, c);
+                e = f.value_write ? kv : bb * kv;
+                if (f.value_write) kv *= bb;  // the read key
             }
             const int li = r * KS + c;
             Kf[li] = kv;
@@ -223,6 +225,7 @@ struct GradLayout {
     int V, dO, BV, M, dM, Y;                        // Cg x dv
     int A, Bm, R, P, Tm, dT, X1, dA, dBm, dR, dP;   // Cg x Cg
     int gC, dgC;                                    // dk
+    int WH;                                         // Cg: value-write form, per-head dw
     int total;
 };
 
@@ -240,6 +243,7 @@ __host__ __device__ inline GradLayout grad_layout(int Cg, int dk, int dv) {
     L.Tm = take(Cg * Cg); L.dT = take(Cg * Cg); L.X1 = take(Cg * Cg); L.dA = take(Cg * Cg);
     L.dBm = take(Cg * Cg); L.dR = take(Cg * Cg); L.dP = take(Cg * Cg);
     L.gC = take(dk); L.dgC = take(dk);
+    L.WH = take(Cg);
     L.total = off;
     return L;
 }
@@ -258,7 +262,7 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
     float *V = lds + L.V, *dO = lds + L.dO, *BV = lds + L.BV, *M = lds + L.M, *dM = lds + L.dM, *Y = lds + L.Y;
     float *A = lds + L.A, *Bm = lds + L.Bm, *R = lds + L.R, *P = lds + L.P, *Tm = lds + L.Tm;
     float *dT = lds + L.dT, *X1 = lds + L.X1, *dA = lds + L.dA, *dBm = lds + L.dBm, *dR = lds + L.dR, *dP = lds + L.dP;
-    float *gC = lds + L.gC, *dgC = lds + L.dgC;
+    float *gC = lds + L.gC, *dgC = lds + L.dgC, *WH = lds + L.WH;
 
     const int64_t nch = (T + Cg - 1) / Cg;
     const int64_t bh = blockIdx.x / nch, n = blockIdx.x % nch;
@@ -279,17 +283,25 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
             qv = f.q_scale * load_qkv(f.q, row * dk + c, f.bf16);
             la = load_gate(f.la, f.la_key, row, dk, c);
             const float bb = load_gate(f.eb, f.eb_key, row, dk, c);
-            const float ww = f.wr ? load_gate(f.wr, f.wr_key, row, dk, c) : bb;
-            e = bb * kv;
-            u = ww * kv;
+            if (f.value_write) {  // read along b k, erase and write along k
+                e = u = kv;
+                kv *= bb;
+            } else {
+                const float ww = f.wr ? load_gate(f.wr, f.wr_key, row, dk, c) : bb;
+                e = bb * kv;
+                u = ww * kv;
+            }
         }
         const int li = r * KS + c;
         K[li] = kv; Q[li] = qv; G[li] = la; E[li] = e; U[li] = u;
     }
+    if (tid < Cg) WH[tid] = 0.f;
     for (int idx = tid; idx < Cg * dv; idx += kGradThreads) {
         const int r = idx / dv, j = idx % dv;
         const bool ok = live(r);
-        V[r * VS + j] = ok ? load_qkv(f.v, row_of(r) * dv + j, f.bf16) : 0.f;
+        float vv = ok ? load_qkv(f.v, row_of(r) * dv + j, f.bf16) : 0.f;
+        if (ok && f.value_write) vv *= load_gate(f.wr, f.wr_key, row_of(r), dv, j);  // values w .* v
+        V[r * VS + j] = vv;
         dO[r * VS + j] = ok ? a.d_o[row_of(r) * dv + j] : 0.f;
     }
     __syncthreads();
@@ -419,7 +431,17 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
             float x = acc[i];
             for (int r = s; r < Cg; ++r) x += P[r * Cg + s] * dO[r * VS + j];
             for (int r = s + 1; r < Cg; ++r) x += Bm[r * Cg + s] * Y[r * VS + j];
-            if (live(s)) a.dv[row_of(s) * dv + j] = x;
+            if (live(s)) {
+                if (f.value_write) {  // x is the gradient of w .* v
+                    const float vr = load_qkv(f.v, row_of(s) * dv + j, f.bf16);
+                    const float wr = load_gate(f.wr, f.wr_key, row_of(s), dv, j);
+                    a.dv[row_of(s) * dv + j] = x * wr;
+                    if (f.wr_key) a.dwr[row_of(s) * dv + j] = x * vr;
+                    else atomicAdd(&WH[s], x * vr);
+                } else {
+                    a.dv[row_of(s) * dv + j] = x;
+                }
+            }
         }
     }
     for (int item = tid; item < dk * (Cg / RB); item += kGradThreads) {
@@ -537,7 +559,10 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
         if (live(x)) {
             const int64_t row = row_of(x);
             const float bb = load_gate(f.eb, eb_key, row, dk, c);
-            if (tied) {
+            if (f.value_write) {  // dkk is the gradient of the read key b k; e = u = k
+                dbv = dkk * ex;
+                dkk = dkk * bb + de + du;
+            } else if (tied) {
                 dkk += (de + du) * bb;
                 dbv = (de + du) * kx;
             } else {
@@ -549,7 +574,7 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
             a.dq[row * dk + c] = f.q_scale * (glq + dqb * eg);
             a.dk[row * dk + c] = dkk;
             if (eb_key) a.deb[row * dk + c] = dbv;
-            if (!tied && wr_key) a.dwr[row * dk + c] = dwv;
+            if (!tied && wr_key && !f.value_write) a.dwr[row * dk + c] = dwv;
         } else {
             dbv = 0.f;
         }
@@ -585,8 +610,139 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
         const int64_t row = row_of(x);
         if (!la_key) a.dla[row] = sl;
         if (!eb_key) a.deb[row] = sb;
-        if (!tied && !wr_key) a.dwr[row] = sw;
+        if (!tied && !wr_key) a.dwr[row] = f.value_write ? WH[x] : sw;
     }
+}
+
+// ---------------------------------------------------------------------------
+// fused input preparation: the backward runs on the prepared inputs, then the
+// chain rule of the preparation maps their gradients to the raw ones
+
+// Per token-head row of the prepared copy: q, k divided by their L2 norm (a
+// zero row stays zero) and v, all fp32, and 1/|q|, 1/|k|; the gates
+// activated from their bf16 logits, fp32: log a = -softplus(x), b = w =
+// sigmoid(x).  Same activations as the forward kernels.
+struct PrepBufs {
+    float *q, *k, *v, *iq, *ik;  // [rows][dk], [rows][dk], [rows][dv], [rows], [rows] (q/k normalised)
+    float *la, *eb, *wr;         // shaped like the gates (gate logits)
+};
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Elements of one row's gate: dk (per key channel), dv (the value-write
+// form's write gate per value channel) or 1 (per head).
+__device__ __forceinline__ int gate_width(int per_key, int width) { return per_key ? width : 1; }
+
+__global__ void __launch_bounds__(256) bwd_prepare_kernel(ChunkArgs f, PrepBufs p, int64_t rows) {
+    const int lane = threadIdx.x & 63;
+    const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
+    const int wch = f.value_write ? dv : dk;
+    for (int64_t row = blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += gridDim.x * 4) {
+        if (f.qk_norm) {
+            float sq = 0.f, sk = 0.f;
+            for (int c = lane; c < dk; c += 64) {
+                const float qv = load_qkv(f.q, row * dk + c, f.bf16), kv = load_qkv(f.k, row * dk + c, f.bf16);
+                sq += qv * qv;
+                sk += kv * kv;
+            }
+            sq = wave_sum(sq);
+            sk = wave_sum(sk);
+            const float iq = sq > 0.f ? rsqrtf(sq) : 0.f, ik = sk > 0.f ? rsqrtf(sk) : 0.f;
+            for (int c = lane; c < dk; c += 64) {
+                p.q[row * dk + c] = load_qkv(f.q, row * dk + c, f.bf16) * iq;
+                p.k[row * dk + c] = load_qkv(f.k, row * dk + c, f.bf16) * ik;
+            }
+            for (int c = lane; c < dv; c += 64) p.v[row * dv + c] = load_qkv(f.v, row * dv + c, f.bf16);
+            if (lane == 0) {
+                p.iq[row] = iq;
+                p.ik[row] = ik;
+            }
+        }
+        if (f.gate_logits) {
+            const uint16_t *xa = reinterpret_cast<const uint16_t *>(f.la);
+            const uint16_t *xb = reinterpret_cast<const uint16_t *>(f.eb);
+            const uint16_t *xw = reinterpret_cast<const uint16_t *>(f.wr);
+            const int na = gate_width(f.la_key, dk), nb = gate_width(f.eb_key, dk), nw = gate_width(f.wr_key, wch);
+            for (int c = lane; c < na; c += 64) p.la[row * na + c] = neg_softplus(bf16_to_f32(xa[row * na + c]));
+            for (int c = lane; c < nb; c += 64) p.eb[row * nb + c] = sigmoid_gate(bf16_to_f32(xb[row * nb + c]));
+            if (f.wr)
+                for (int c = lane; c < nw; c += 64) p.wr[row * nw + c] = sigmoid_gate(bf16_to_f32(xw[row * nw + c]));
+        }
+    }
+}
+
+// In place on the gradients: logits get the derivative of their activation
+// (-sigmoid for the decay, s (1 - s) for the sigmoid gates); raw q, k get
+// (dn - n (n . dn)) / |x| from the gradient dn of their normalised copy n.
+__global__ void __launch_bounds__(256) bwd_chain_kernel(BwdArgs a, PrepBufs p, int64_t rows) {
+    const ChunkArgs &f = a.f;
+    const int lane = threadIdx.x & 63;
+    const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
+    const int wch = f.value_write ? dv : dk;
+    for (int64_t row = blockIdx.x * 4 + (threadIdx.x >> 6); row < rows; row += gridDim.x * 4) {
+        if (f.qk_norm) {
+            float dotq = 0.f, dotk = 0.f;
+            for (int c = lane; c < dk; c += 64) {
+                dotq += p.q[row * dk + c] * a.dq[row * dk + c];
+                dotk += p.k[row * dk + c] * a.dk[row * dk + c];
+            }
+            dotq = wave_sum(dotq);
+            dotk = wave_sum(dotk);
+            const float iq = p.iq[row], ik = p.ik[row];
+            for (int c = lane; c < dk; c += 64) {
+                a.dq[row * dk + c] = (a.dq[row * dk + c] - p.q[row * dk + c] * dotq) * iq;
+                a.dk[row * dk + c] = (a.dk[row * dk + c] - p.k[row * dk + c] * dotk) * ik;
+            }
+        }
+        if (f.gate_logits) {
+            const uint16_t *xa = reinterpret_cast<const uint16_t *>(f.la);
+            const uint16_t *xb = reinterpret_cast<const uint16_t *>(f.eb);
+            const uint16_t *xw = reinterpret_cast<const uint16_t *>(f.wr);
+            const int na = gate_width(f.la_key, dk), nb = gate_width(f.eb_key, dk), nw = gate_width(f.wr_key, wch);
+            for (int c = lane; c < na; c += 64)
+                a.dla[row * na + c] *= -sigmoid_gate(bf16_to_f32(xa[row * na + c]));
+            for (int c = lane; c < nb; c += 64) {
+                const float sgm = sigmoid_gate(bf16_to_f32(xb[row * nb + c]));
+                a.deb[row * nb + c] *= sgm * (1.f - sgm);
+            }
+            if (f.wr && a.dwr)
+                for (int c = lane; c < nw; c += 64) {
+                    const float sgm = sigmoid_gate(bf16_to_f32(xw[row * nw + c]));
+                    a.dwr[row * nw + c] *= sgm * (1.f - sgm);
+                }
+        }
+    }
+}
+
+// Layout of the prepared copy after the backward's own workspace.
+struct PrepLayout {
+    int64_t q, k, v, iq, ik, la, eb, wr, bytes;
+};
+
+PrepLayout prep_layout(const ChunkArgs &f) {
+    const int64_t rows = f.B * f.T * f.H, dk = f.dk, dv = f.dv;
+    const int64_t wch = f.value_write ? dv : dk;
+    PrepLayout l{};
+    int64_t off = 0;
+    auto take = [&](int64_t floats) { const int64_t o = off; off += (floats * 4 + 255) & ~int64_t(255); return o; };
+    if (f.qk_norm) {
+        l.q = take(rows * dk);
+        l.k = take(rows * dk);
+        l.v = take(rows * dv);
+        l.iq = take(rows);
+        l.ik = take(rows);
+    }
+    if (f.gate_logits) {
+        l.la = take(rows * (f.la_key ? dk : 1));
+        l.eb = take(rows * (f.eb_key ? dk : 1));
+        if (f.wr) l.wr = take(rows * (f.wr_key ? wch : 1));
+    }
+    l.bytes = off;
+    return l;
 }
 
 }  // namespace
@@ -604,7 +760,7 @@ int chunk_bwd_chunk(int64_t dk, int64_t dv, int C) {
 // which add a per-chunk record region after the two state records.
 static bool matrix_scans(int64_t dk, int64_t dv, int Cg) { return dk == 128 && dv == 128 && Cg == 16; }
 
-size_t chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int C) {
+static size_t core_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int C) {
     const int Cg = chunk_bwd_chunk(dk, dv, C);
     if (!Cg || B * H * T == 0) return 0;
     const int64_t nch = (T + Cg - 1) / Cg;
@@ -639,7 +795,59 @@ static hipError_t launch_bwd_scans_general(const BwdArgs &a, int Cg, float *hist
     return hipGetLastError();
 }
 
+size_t chunk_bwd_workspace(const ChunkArgs &f) {
+    const size_t core = core_workspace(f.B, f.H, f.T, f.dk, f.dv, f.C);
+    if (!core) return 0;
+    return core + static_cast<size_t>(prep_layout(f).bytes);
+}
+
+static hipError_t launch_core(const BwdArgs &a, void *ws, hipStream_t s);
+
 hipError_t launch_chunk_bwd(const BwdArgs &a, void *ws, hipStream_t s) {
+    const ChunkArgs &f = a.f;
+    if (!f.gate_logits && !f.qk_norm) return launch_core(a, ws, s);
+    // fused input preparation: prepare, run the backward on the prepared
+    // copy, then the chain rule of the preparation in place on the gradients
+    char *base = static_cast<char *>(ws) + core_workspace(f.B, f.H, f.T, f.dk, f.dv, f.C);
+    const PrepLayout l = prep_layout(f);
+    PrepBufs p{};
+    if (f.qk_norm) {
+        p.q = reinterpret_cast<float *>(base + l.q);
+        p.k = reinterpret_cast<float *>(base + l.k);
+        p.v = reinterpret_cast<float *>(base + l.v);
+        p.iq = reinterpret_cast<float *>(base + l.iq);
+        p.ik = reinterpret_cast<float *>(base + l.ik);
+    }
+    if (f.gate_logits) {
+        p.la = reinterpret_cast<float *>(base + l.la);
+        p.eb = reinterpret_cast<float *>(base + l.eb);
+        if (f.wr) p.wr = reinterpret_cast<float *>(base + l.wr);
+    }
+    const int64_t rows = f.B * f.T * f.H;
+    const int64_t blocks = (rows + 3) / 4 < 65536 ? (rows + 3) / 4 : 65536;
+    hipLaunchKernelGGL(bwd_prepare_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, f, p, rows);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    BwdArgs core = a;
+    if (f.qk_norm) {
+        core.f.q = p.q;
+        core.f.k = p.k;
+        core.f.v = p.v;
+        core.f.bf16 = 0;
+        core.f.qk_norm = 0;
+    }
+    if (f.gate_logits) {
+        core.f.la = p.la;
+        core.f.eb = p.eb;
+        core.f.wr = p.wr;
+        core.f.gate_logits = 0;
+    }
+    if ((e = launch_core(core, ws, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_chain_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, a, p, rows);
+    return hipGetLastError();
+}
+
+static hipError_t launch_core(const BwdArgs &a, void *ws, hipStream_t s) {
     const ChunkArgs &f = a.f;
     const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
     const int Cg = chunk_bwd_chunk(dk, dv, f.C);

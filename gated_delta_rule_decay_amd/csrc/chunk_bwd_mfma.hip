@@ -86,9 +86,14 @@ __global__ void __launch_bounds__(BNT) bwd_record_kernel(BwdArgs a, float *rec, 
                 qv = f.q_scale * load_qkv(f.q, row * BD + c, f.bf16);
                 la = load_gate(f.la, f.la_key, row, BD, c);
                 const float bb = load_gate(f.eb, f.eb_key, row, BD, c);
-                const float ww = f.wr ? load_gate(f.wr, f.wr_key, row, BD, c) : bb;
-                e = bb * kv;
-                u = ww * kv;
+                if (f.value_write) {  // read along b k, erase and write along k
+                    e = u = kv;
+                    kv *= bb;
+                } else {
+                    const float ww = f.wr ? load_gate(f.wr, f.wr_key, row, BD, c) : bb;
+                    e = bb * kv;
+                    u = ww * kv;
+                }
             }
             const int li = r * KS + c;
             K[li] = kv; Q[li] = qv; G[li] = la; E[li] = e; U[li] = u;
@@ -207,6 +212,19 @@ __device__ __forceinline__ void load_rows4(float (&x)[4], const void *p, int bf1
     }
 }
 
+// The values of lane (kq, n)'s rows, times the write gate in the value-write form.
+__device__ __forceinline__ void load_vals4(float (&x)[4], int64_t b, int64_t h, int64_t t0, int kq, int col,
+                                           const ChunkArgs &f) {
+    load_rows4(x, f.v, f.bf16, b, h, t0, kq, col, f);
+    if (f.value_write) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t t = t0 + 4 * kq + j;
+            if (t < f.T) x[j] *= load_gate(f.wr, f.wr_key, (b * f.T + t) * f.H + h, BD, col);
+        }
+    }
+}
+
 // Store (or read) a wave's 128 x 16 state slice to/from a [128][128] matrix.
 __device__ __forceinline__ void put_state(float *dst, const f4 (&s)[8], int kq, int col) {
 #pragma unroll
@@ -236,14 +254,14 @@ __global__ void __launch_bounds__(BNT) bwd_state_kernel(BwdArgs a, const float *
     Staged st;
     float vn[4];
     stage_load(st, rc, R_KB, R_ET, R_UT, R_TM, R_BM, tid);
-    load_rows4(vn, f.v, f.bf16, b, h, 0, kq, col, f);
+    load_vals4(vn, b, h, 0, kq, col, f);
     for (int n = 0; n < nch; ++n) {
         __syncthreads();  // every wave done with the previous chunk's LDS copy
         stage_store(st, L, tid);
         float v[4] = {vn[0], vn[1], vn[2], vn[3]};
         if (n + 1 < nch) {
             stage_load(st, rc + (n + 1) * static_cast<int64_t>(REC_BWD), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
-            load_rows4(vn, f.v, f.bf16, b, h, (n + 1) * BC, kq, col, f);
+            load_vals4(vn, b, h, (n + 1) * BC, kq, col, f);
         }
         put_state(hs + n * static_cast<int64_t>(BD * BD), S, kq, col);
         __syncthreads();
@@ -388,6 +406,7 @@ struct GradLds {
     float dw[BC * RS];
     float dt[BC * BC], x1[BC * BC], da[BC * BC], dbm[BC * BC], dr[BC * BC], dp[BC * BC];
     float daT[BC * BC], dbmT[BC * BC], drT[BC * BC], dpT[BC * BC];  // transposes (columns as rows)
+    float wpart[8 * BC];  // value-write form, one write gate per head: per-wave partial sums of dw
 };
 
 // 16 x 16 product over 128 columns of two [16][RS] LDS matrices, X Z^T
@@ -422,6 +441,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
     const int64_t T = f.T, H = f.H;
     const int64_t ntask = f.B * H * nch;
     const bool la_key = f.la_key, eb_key = f.eb_key, wr_key = f.wr_key, tied = f.wr == nullptr;
+    const bool vw = f.value_write;  // read along b k, erase / write along k, values w .* v
     // this wave's value columns of S and dSo, consumed by the value products;
     // the next task's are loaded while this one finishes
     f4 S[8], dS[8];
@@ -480,16 +500,22 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
                 qv = f.q_scale * load4_qkv(f.q, row * BD + c4, f.bf16);
                 la = load4_gate(f.la, la_key, row, c4);
                 bb = load4_gate(f.eb, eb_key, row, c4);
-                ww = tied ? bb : load4_gate(f.wr, wr_key, row, c4);
+                ww = tied ? bb : load4_gate(f.wr, wr_key, row, c4);  // value-write: per value column
                 vv = load4_qkv(f.v, row * BD + c4, f.bf16);
                 ov = *reinterpret_cast<const f4 *>(a.d_o + row * BD + c4);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int li = r * KS + c4 + i;
-                L.k[li] = kv[i]; L.q[li] = qv[i]; L.g[li] = la[i];
-                L.e[li] = bb[i] * kv[i];
-                L.u[li] = ww[i] * kv[i];
+                L.q[li] = qv[i]; L.g[li] = la[i];
+                L.k[li] = vw ? bb[i] * kv[i] : kv[i];
+                L.e[li] = vw ? kv[i] : bb[i] * kv[i];
+                L.u[li] = vw ? kv[i] : ww[i] * kv[i];
+            }
+            if (vw) {  // the raw values and write gates, for dv and dw after the value products
+                *reinterpret_cast<f4 *>(&L.mm[r * RS + c4]) = vv;
+                *reinterpret_cast<f4 *>(&L.dm[r * RS + c4]) = ww;
+                vv = vv * ww;
             }
             *reinterpret_cast<f4 *>(&L.v[r * RS + c4]) = vv;
             *reinterpret_cast<f4 *>(&L.o[r * RS + c4]) = ov;
@@ -557,14 +583,35 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
                 dV = mfma4(L.pp[(4 * kq + j) * BC + m], o4[j], dV);
                 dV = mfma4(L.bm[(4 * kq + j) * BC + m], Y[j], dV);
             }
+            float wsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tok = 4 * kq + r;
-                if (live(tok)) a.dv[row_of(tok) * BD + col] = dV[r];
+                if (vw) {  // dV is the gradient of w .* v
+                    const float vr = L.mm[tok * RS + col], wr = L.dm[tok * RS + col];
+                    if (live(tok)) {
+                        a.dv[row_of(tok) * BD + col] = dV[r] * wr;
+                        if (wr_key) a.dwr[row_of(tok) * BD + col] = dV[r] * vr;
+                    }
+                    wsum[r] = dV[r] * vr;
+                } else if (live(tok)) {
+                    a.dv[row_of(tok) * BD + col] = dV[r];
+                }
                 L.mm[tok * RS + col] = M[r];
                 L.dm[tok * RS + col] = dM[r];
                 L.y[tok * RS + col] = Y[r];
                 L.bv[tok * RS + col] = BV[r];
+            }
+            if (vw && !wr_key) {  // one write gate per head: partial sums over this wave's 16 columns
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float x = wsum[r];
+                    x += __shfl_xor(x, 1);
+                    x += __shfl_xor(x, 2);
+                    x += __shfl_xor(x, 4);
+                    x += __shfl_xor(x, 8);
+                    if (m == 0) L.wpart[wv * BC + 4 * kq + r] = x;
+                }
             }
         }
         lds_barrier();
@@ -727,7 +774,10 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
                 if (live(x)) {
                     const int64_t row = row_of(x);
                     const float bx = L.o[lr];
-                    if (tied) {
+                    if (vw) {  // dkk is the gradient of the read key b k; e = u = k
+                        dbv = dkk * ex;
+                        dkk = dkk * bx + de + du;
+                    } else if (tied) {
                         dkk += (de + du) * bx;
                         dbv = (de + du) * kx;
                     } else {
@@ -739,7 +789,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
                     a.dq[row * BD + cc] = f.q_scale * (glq + dqb * eg);
                     a.dk[row * BD + cc] = dkk;
                     if (eb_key) a.deb[row * BD + cc] = dbv;
-                    if (!tied && wr_key) a.dwr[row * BD + cc] = dwv;
+                    if (!tied && wr_key && !vw) a.dwr[row * BD + cc] = dwv;
                 }
                 dgv[lr] = dg;
                 shr[lr] = (det * ex + dut * ux) * ec;  // this token's share of d gC
@@ -776,6 +826,10 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
                 const int64_t row = row_of(x);
                 if (!la_key) a.dla[row] = sl;
                 if (!eb_key) a.deb[row] = sb;
+                if (vw && !wr_key) {
+                    sw = 0.f;
+                    for (int w8 = 0; w8 < 8; ++w8) sw += L.wpart[w8 * BC + x];
+                }
                 if (!tied && !wr_key) a.dwr[row] = sw;
             }
         }

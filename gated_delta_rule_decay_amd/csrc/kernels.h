@@ -72,7 +72,9 @@ struct BwdArgs {
     float *ds0;             // [B,H,dk,dv] or nullptr
 };
 int chunk_bwd_chunk(int64_t dk, int64_t dv, int C);  // internal chunk length (0: none fits)
-size_t chunk_bwd_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int C);
+// workspace of launch_chunk_bwd for these arguments (the state records, and
+// the prepared inputs when the preparation is fused)
+size_t chunk_bwd_workspace(const ChunkArgs &f);
 hipError_t launch_chunk_bwd(const BwdArgs &a, void *ws, hipStream_t s);
 // dk = dv = 128 (16-token chunks): the whole backward on the matrix cores
 // (state and state-gradient scans, per-chunk gradients), through per-chunk

@@ -219,8 +219,12 @@ gdn2_status gdn2_chunk_fwd_varlen(const gdn2_desc *desc, const int32_t *cu_seqle
 
 /* Device workspace, in bytes, for gdn2_chunk_bwd on `desc`: two fp32 state
  * histories, B*H*ceil(T/Cb)*dk*dv*4 bytes each (Cb = 16 for dk = dv = 128,
- * larger for small heads; each region 256-byte aligned).  Same validation
- * as gdn2_chunk_fwd; GDN2_ERR_UNSUPPORTED if no internal chunk fits. */
+ * larger for small heads); for dk = dv = 128 a 37 KiB fp32 record per
+ * (chain, internal chunk); with fused input preparation an fp32 copy of the
+ * prepared inputs (q, k, v and two norms per token-head when qk_l2norm, the
+ * activated gates when gate_logits).  Each region 256-byte aligned.  Same
+ * validation as gdn2_chunk_fwd; GDN2_ERR_UNSUPPORTED if no internal chunk
+ * fits. */
 gdn2_status gdn2_chunk_bwd_workspace(const gdn2_desc *desc, size_t *bytes);
 
 /*
@@ -231,10 +235,14 @@ gdn2_status gdn2_chunk_bwd_workspace(const gdn2_desc *desc, size_t *bytes);
  * chunkwise algorithm and its kernels serve training; gist.science summary,
  * "Technische Samenvatting" section 3).  The result equals reverse-mode
  * differentiation of the token recurrence (up to rounding).  It is computed
- * chunk by chunk in fp32 on the vector ALU: the forward recomputes and
- * records the state entering every internal chunk, a reverse scan carries
- * the state gradient back through the chunks, then every chunk forms its
- * gradients in parallel from the two records.
+ * chunk by chunk in fp32 (on the matrix cores for dk = dv = 128): a forward
+ * scan records the state entering every internal chunk, a reverse scan
+ * carries the state gradient back through the chunks, then every chunk
+ * forms its gradients in parallel from the two records.  Both forms
+ * (desc->form) are covered.  With fused input preparation (desc->gate_logits,
+ * desc->qk_l2norm) the gradients are those of the raw inputs: of the gate
+ * logits (through -softplus and sigmoid) and of unnormalised q, k (through
+ * the L2 normalisation; a zero row gets zero).
  *
  *   q .. state0  the forward's inputs (same layouts and rules as
  *                gdn2_chunk_fwd; state0 NULL means zeros).
@@ -243,9 +251,10 @@ gdn2_status gdn2_chunk_bwd_workspace(const gdn2_desc *desc, size_t *bytes);
  *                zeros.
  *   dq, dk, dv   fp32, [B,T,H,dk] / [B,T,H,dv] (fp32 whatever qkv_dtype).
  *   d_log_decay, d_erase, d_write   fp32, shaped like their gate (per key
- *                channel or per token-head); d_write ignored (may be NULL)
- *                when tied, and then d_erase holds the gradient of the one
- *                shared gate.
+ *                channel or per token-head; the value-write form's write gate
+ *                per value channel), also for bf16 logits; d_write ignored
+ *                (may be NULL) when tied, and then d_erase holds the gradient
+ *                of the one shared gate.
  *   d_state0     gradient of state0 [B,H,dk,dv] fp32, or NULL to skip.
  *   workspace    device scratch of ws_bytes >= gdn2_chunk_bwd_workspace(),
  *                256-byte aligned, else GDN2_ERR_WORKSPACE; contents need no

@@ -254,10 +254,9 @@ def test_value_write_form_checks(lib):
     d = good(dk=64, dv=128, **vw)
     wbytes = 2 * 128 * 4 * 128 * 4
     assert fwd(lib, d, wr=O - wbytes + 256) == 5             # runs into o
-    # the two-pass kernels cover it; the backward does not
+    # the two-pass kernels cover it, and the backward (same workspace as the key form)
     assert query(lib, good(**vw)) == split_bytes(2, 4, 128)
-    n = ctypes.c_size_t(0)
-    assert lib.gdn2_chunk_bwd_workspace(ctypes.byref(good(**vw)), ctypes.byref(n)) == 4
+    assert bwd_bytes(good(**vw)) == bwd_bytes(good())
 
 
 def test_fused_input_checks(lib):
@@ -266,11 +265,18 @@ def test_fused_input_checks(lib):
     gbytes = 2 * 128 * 4 * 128 * 2
     assert fwd(lib, d, la=O - gbytes + 256) == 5        # a bf16 gate running into o
     assert fwd(lib, good(), la=O - gbytes + 256) == 5   # twice as long as fp32: also overlaps
-    # the two-pass kernels cover it; the backward does not
+    # the two-pass kernels cover it; the backward adds an fp32 copy of the
+    # prepared inputs: q, k, v and two norms per token-head, the activated gates
     assert query(lib, good(gate_logits=True, qk_l2norm=True)) == split_bytes(2, 4, 128)
-    n = ctypes.c_size_t(0)
-    assert lib.gdn2_chunk_bwd_workspace(ctypes.byref(good(qk_l2norm=True)), ctypes.byref(n)) == 4
-    assert lib.gdn2_chunk_bwd_workspace(ctypes.byref(good(gate_logits=True)), ctypes.byref(n)) == 4
+    a = lambda x: (x + 255) // 256 * 256
+    rows = 2 * 128 * 4
+    base = bwd_bytes(good())
+    assert bwd_bytes(good(qk_l2norm=True)) == base + 3 * a(rows * 128 * 4) + 2 * a(rows * 4)
+    assert bwd_bytes(good(gate_logits=True)) == base + 3 * a(rows * 128 * 4)
+    assert bwd_bytes(good(gate_logits=True, tied=True, decay_kind=0, erase_kind=0)) == base + 2 * a(rows * 4)
+    # gradients of bf16 logits are fp32: their spans are twice the logits'
+    d = good(gate_logits=True)
+    assert bwd(lib, d, dla=DO - gbytes - 256) == 5   # an fp32 d_log_decay running into d_o
 
 
 # ---- packed sequences -----------------------------------------------------

@@ -24,7 +24,8 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_UNSUPP
 # Every entry point include/gdn2.h declares.
 EXPORTS = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace",
            "gdn2_chunk_fwd", "gdn2_chunk_fwd_varlen_workspace", "gdn2_chunk_fwd_varlen",
-           "gdn2_chunk_bwd_workspace", "gdn2_chunk_bwd", "gdn2_recurrent_step")
+           "gdn2_chunk_bwd_workspace", "gdn2_chunk_bwd", "gdn2_chunk_bwd_varlen_workspace",
+           "gdn2_chunk_bwd_varlen", "gdn2_recurrent_step")
 
 
 class Gdn2Desc(ctypes.Structure):
@@ -83,6 +84,11 @@ def load_library():
             lib.gdn2_chunk_bwd.restype = ctypes.c_int
             lib.gdn2_chunk_bwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                                            fp, fp, fp, vp, ctypes.c_size_t, vp]
+            lib.gdn2_chunk_bwd_varlen_workspace.restype = ctypes.c_int
+            lib.gdn2_chunk_bwd_varlen_workspace.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
+            lib.gdn2_chunk_bwd_varlen.restype = ctypes.c_int
+            lib.gdn2_chunk_bwd_varlen.argtypes = [dp, vp, vp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
+                                                  fp, fp, fp, vp, ctypes.c_size_t, vp]
             lib.gdn2_recurrent_step.restype = ctypes.c_int
             lib.gdn2_recurrent_step.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, vp]
             _lib = lib
@@ -332,6 +338,61 @@ def chunk_bwd(q, k, v, log_decay, erase, write, state0, d_o, d_state=None, chunk
         _ptr(workspace), workspace.numel(), _stream())
     if st != 0:
         raise Gdn2Error(st, "gdn2_chunk_bwd")
+    return g
+
+
+def chunk_bwd_varlen_workspace(desc: Gdn2Desc) -> int:
+    n = ctypes.c_size_t(0)
+    st = load_library().gdn2_chunk_bwd_varlen_workspace(ctypes.byref(desc), ctypes.byref(n))
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_chunk_bwd_varlen_workspace")
+    return int(n.value)
+
+
+def chunk_bwd_varlen(q, k, v, log_decay, erase, write, cu_seqlens, state0, d_o, d_state=None, chunk=64,
+                     q_scale=1.0, want_state0=True, workspace=None, value_write=False, qk_l2norm=False):
+    """Gradients of the packed-sequence forward (``chunk_fwd_varlen``).
+
+    Packed tensors [T,H,d] (or [1,T,H,d]) as for ``chunk_fwd_varlen``;
+    cu_seqlens int32 [N+1] on the device; state0, d_state [N,H,dk,dv] fp32
+    (or None); d_o shaped like v, fp32.  Returns the dict of ``chunk_bwd``
+    (gradients shaped like their inputs, d_state0 [N,H,dk,dv]).
+    """
+    import torch
+    lead = k.shape[:-3]
+    if len(lead) > 1 or (len(lead) == 1 and lead[0] != 1):
+        raise ValueError("packed tensors are [T,H,d] or [1,T,H,d]")
+    T, H, dk = k.shape[-3:]
+    dv = v.shape[-1]
+    dev = k.device
+    _check(cu_seqlens, "cu_seqlens", tuple(cu_seqlens.shape), (torch.int32,), dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of N+1 offsets")
+    N = cu_seqlens.numel() - 1
+    desc = _desc_for(q, k, v, log_decay, erase, write, tuple(lead) + (T, H), N, T, H, chunk, q_scale,
+                     value_write, qk_l2norm)
+    f32 = (torch.float32,)
+    if state0 is not None:
+        _check(state0, "state0", (N, H, dk, dv), f32, dev)
+    _check(d_o, "d_o", tuple(lead) + (T, H, dv), f32, dev)
+    if d_state is not None:
+        _check(d_state, "d_state", (N, H, dk, dv), f32, dev)
+    new = lambda t: torch.empty(tuple(t.shape), dtype=torch.float32, device=dev)  # fp32 whatever t's dtype
+    g = dict(dq=new(q), dk=new(k), dv=new(v), d_log_decay=new(log_decay), d_erase=new(erase),
+             d_write=None if write is None else new(write),
+             d_state0=torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_state0 else None)
+    if workspace is None:
+        n = chunk_bwd_varlen_workspace(desc)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+    else:
+        _check(workspace, "workspace", tuple(workspace.shape), (torch.uint8,), dev)
+    st = load_library().gdn2_chunk_bwd_varlen(
+        ctypes.byref(desc), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(erase),
+        _ptr(write), _ptr(state0), _ptr(d_o), _ptr(d_state), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+        _ptr(g["d_log_decay"]), _ptr(g["d_erase"]), _ptr(g["d_write"]), _ptr(g["d_state0"]),
+        _ptr(workspace), workspace.numel(), _stream())
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_chunk_bwd_varlen")
     return g
 
 

@@ -351,6 +351,78 @@ gdn2_status gdn2_chunk_bwd(const gdn2_desc *d, const void *q, const void *k, con
     return hip_status(gdn2::launch_chunk_bwd(a, workspace, s));
 }
 
+gdn2_status gdn2_chunk_bwd_varlen_workspace(const gdn2_desc *desc, size_t *bytes) {
+    if (!bytes) return GDN2_ERR_NULL;
+    gdn2_desc one;
+    gdn2_status st = check_varlen(desc, &one);
+    if (st != GDN2_OK) return st;
+    if (!gdn2::chunk_bwd_chunk(desc->dk, desc->dv, static_cast<int>(desc->chunk))) return GDN2_ERR_UNSUPPORTED;
+    static const float placeholder = 0.f;  // stands for an untied write gate
+    static const int32_t cu_placeholder = 0;
+    ChunkArgs a = args_of(desc, nullptr, nullptr, nullptr, nullptr, nullptr, &placeholder, nullptr, nullptr, nullptr);
+    a.cu = &cu_placeholder;
+    *bytes = gdn2::chunk_bwd_workspace(a);
+    return GDN2_OK;
+}
+
+gdn2_status gdn2_chunk_bwd_varlen(const gdn2_desc *d, const int32_t *cu_seqlens, const void *q, const void *k,
+                                  const void *v, const float *log_decay, const float *erase, const float *write,
+                                  const float *state0, const float *d_o, const float *d_state_out, float *dq,
+                                  float *dk, float *dv, float *d_log_decay, float *d_erase, float *d_write,
+                                  float *d_state0, void *workspace, size_t ws_bytes, void *stream) {
+    size_t need = 0;
+    gdn2_status st = gdn2_chunk_bwd_varlen_workspace(d, &need);
+    if (st != GDN2_OK) return st;
+    const int64_t N = d->batch, T = d->seqlen;
+    if (N == 0) return GDN2_OK;  // no sequence: nothing to read or write
+    if (!cu_seqlens) return GDN2_ERR_NULL;
+    if (need > 0 && (!workspace || ws_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0))
+        return GDN2_ERR_WORKSPACE;
+    const bool work = T > 0;
+    const bool tied = d->tie_write_to_erase != 0;
+    if (work && (!q || !k || !v || !log_decay || !erase || !d_o || !dq || !dk || !dv || !d_log_decay || !d_erase))
+        return GDN2_ERR_NULL;
+    if (work && !tied && (!write || !d_write)) return GDN2_ERR_NULL;
+    gdn2_desc one = *d;
+    one.batch = 1;
+    const Sizes sz = sizes_of(&one, T);
+    const int64_t stb = N * d->heads * d->dk * d->dv * 4;
+    const Span in[] = {span_of(q, sz.qk), span_of(k, sz.qk), span_of(v, sz.v),
+                       span_of(log_decay, sz.la), span_of(erase, sz.eb),
+                       span_of(tied ? nullptr : write, sz.wr), span_of(state0, stb),
+                       span_of(d_o, sz.o), span_of(d_state_out, stb), span_of(cu_seqlens, (N + 1) * 4)};
+    const int64_t f32 = d->qkv_dtype == GDN2_BF16 ? 2 : 1;
+    gdn2_desc d4 = one;
+    d4.gate_logits = 0;
+    const Sizes sg = sizes_of(&d4, T);
+    const Span out[] = {span_of(dq, sz.qk * f32), span_of(dk, sz.qk * f32), span_of(dv, sz.v * f32),
+                        span_of(d_log_decay, sg.la), span_of(d_erase, sg.eb),
+                        span_of(tied ? nullptr : d_write, sg.wr), span_of(d_state0, stb),
+                        span_of(workspace, need > 0 ? static_cast<int64_t>(ws_bytes) : 0)};
+    const int nout = sizeof(out) / sizeof(out[0]);
+    for (int i = 0; i < nout; ++i) {
+        for (const Span &x : in)
+            if (overlap(out[i], x)) return GDN2_ERR_ALIAS;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(out[i], out[j])) return GDN2_ERR_ALIAS;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!work) {  // every sequence empty: the state gradients pass through
+        if (d_state0) return hip_status(gdn2::launch_state_copy(d_state_out, d_state0, stb / 4, s));
+        return GDN2_OK;
+    }
+    if (N * d->heads > 0x7fffffffLL) return GDN2_ERR_UNSUPPORTED;
+    gdn2::BwdArgs a;
+    a.f = args_of(d, q, k, v, log_decay, erase, write, state0, nullptr, nullptr);
+    a.f.cu = cu_seqlens;
+    a.d_o = d_o;
+    a.d_sT = d_state_out;
+    a.dq = dq; a.dk = dk; a.dv = dv;
+    a.dla = d_log_decay; a.deb = d_erase; a.dwr = tied ? nullptr : d_write;
+    a.ds0 = d_state0;
+    return hip_status(gdn2::launch_chunk_bwd(a, workspace, s));
+}
+
 gdn2_status gdn2_recurrent_step(const gdn2_desc *d, const void *q, const void *k, const void *v,
                                 const float *log_decay, const float *erase, const float *write,
                                 float *state, float *o, void *stream) {

@@ -82,7 +82,8 @@ __host__ __device__ inline RevLayout rev_layout(int Cg, int DVT, int dk) {
     return L;
 }
 
-__global__ void __launch_bounds__(kRevThreads) bwd_dstate_kernel(BwdArgs a, int Cg, int DVT, float *dhist) {
+__global__ void __launch_bounds__(kRevThreads) bwd_dstate_kernel(BwdArgs a, int Cg, int DVT, float *dhist,
+                                                                 VarPlan vp) {
     extern __shared__ float lds[];
     const ChunkArgs &f = a.f;
     const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
@@ -97,17 +98,27 @@ __global__ void __launch_bounds__(kRevThreads) bwd_dstate_kernel(BwdArgs a, int 
     const int col0 = blockIdx.y * DVT, ncol = min(DVT, dv - col0);
     const int tid = threadIdx.x;
     const int64_t sbase = bh * static_cast<int64_t>(dk) * dv;
-    const int64_t nch = (T + Cg - 1) / Cg;
+    // this chain's chunks: n < nch from token tbase (packed: the plan's), record
+    // index rec0 + n rstr, rows before tlim
+    int64_t nch = (T + Cg - 1) / Cg, tbase = b * T, tlim = b * T + T, rec0 = bh * nch, rstr = 1;
+    if (f.cu) {
+        const int2 e = vp.seq[b];
+        nch = vp.pfx[b + 1] - vp.pfx[b];
+        tbase = e.x;
+        tlim = e.y;
+        rec0 = static_cast<int64_t>(vp.pfx[b]) * H + h;
+        rstr = H;
+    }
 
     for (int idx = tid; idx < dk * DVT; idx += kRevThreads) {
         const int c = idx / DVT, j = idx % DVT;
         dS[idx] = (a.d_sT && j < ncol) ? a.d_sT[sbase + static_cast<int64_t>(c) * dv + col0 + j] : 0.f;
     }
     for (int64_t n = nch - 1; n >= 0; --n) {
-        const int64_t t0 = n * Cg;
+        const int64_t t0 = tbase + n * Cg;
         __syncthreads();
         // the gradient of this chunk's exit state, for the gradient pass
-        float *hs = dhist + (bh * nch + n) * static_cast<int64_t>(dk) * dv;
+        float *hs = dhist + (rec0 + n * rstr) * static_cast<int64_t>(dk) * dv;
         for (int idx = tid; idx < dk * DVT; idx += kRevThreads) {
             const int c = idx / DVT, j = idx % DVT;
             if (j < ncol) hs[static_cast<int64_t>(c) * dv + col0 + j] = dS[idx];
@@ -116,8 +127,8 @@ __global__ void __launch_bounds__(kRevThreads) bwd_dstate_kernel(BwdArgs a, int 
             const int r = idx / dk, c = idx % dk;
             const int64_t t = t0 + r;
             float kv = 0.f, qv = 0.f, la = 0.f, e = 0.f;
-            if (t < T) {
-                const int64_t row = (b * T + t) * H + h;
+            if (t < tlim) {
+                const int64_t row = t * H + h;
                 kv = load_qkv(f.k, row * dk + c, f.bf16);
                 qv = f.q_scale * load_qkv(f.q, row * dk + c, f.bf16);
                 la = load_gate(f.la, f.la_key, row, dk, c);
@@ -134,7 +145,7 @@ __global__ void __launch_bounds__(kRevThreads) bwd_dstate_kernel(BwdArgs a, int 
         for (int idx = tid; idx < Cg * DVT; idx += kRevThreads) {
             const int r = idx / DVT, j = idx % DVT;
             const int64_t t = t0 + r;
-            dO[idx] = (t < T && j < ncol) ? a.d_o[((b * T + t) * H + h) * dv + col0 + j] : 0.f;
+            dO[idx] = (t < tlim && j < ncol) ? a.d_o[(t * H + h) * dv + col0 + j] : 0.f;
         }
         __syncthreads();
         for (int c = tid; c < dk; c += kRevThreads) {
@@ -249,7 +260,7 @@ __host__ __device__ inline GradLayout grad_layout(int Cg, int dk, int dv) {
 }
 
 __global__ void __launch_bounds__(kGradThreads)
-bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
+bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist, VarPlan vp) {
     extern __shared__ float lds[];
     const ChunkArgs &f = a.f;
     const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
@@ -264,14 +275,28 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist) {
     float *dT = lds + L.dT, *X1 = lds + L.X1, *dA = lds + L.dA, *dBm = lds + L.dBm, *dR = lds + L.dR, *dP = lds + L.dP;
     float *gC = lds + L.gC, *dgC = lds + L.dgC, *WH = lds + L.WH;
 
-    const int64_t nch = (T + Cg - 1) / Cg;
-    const int64_t bh = blockIdx.x / nch, n = blockIdx.x % nch;
-    const int64_t b = bh / H, h = bh % H, t0 = n * Cg;
+    // the task's head, first token and sequence end (packed: chunk-major
+    // tasks placed by the plan's chunk table)
+    const int64_t task = blockIdx.x;
+    int64_t h, t0, tlim;
+    if (f.cu) {
+        if (task >= H * vp.pfx[f.B]) return;  // launched for the bound on the chunk count
+        const int64_t gc = task / H;
+        const int2 e = vp.tab[gc];
+        h = task - gc * H;
+        t0 = e.x;
+        tlim = e.y;
+    } else {
+        const int64_t nch = (T + Cg - 1) / Cg, bh = task / nch, b = bh / H;
+        h = bh - b * H;
+        t0 = b * T + (task - bh * nch) * Cg;
+        tlim = b * T + T;
+    }
     const int tid = threadIdx.x;
-    const float *Sg = hist + (bh * nch + n) * static_cast<int64_t>(dk) * dv;    // entry state
-    const float *dSg = dhist + (bh * nch + n) * static_cast<int64_t>(dk) * dv;  // exit gradient
-    auto row_of = [&](int r) { return (b * T + t0 + r) * H + h; };
-    auto live = [&](int r) { return t0 + r < T; };
+    const float *Sg = hist + task * static_cast<int64_t>(dk) * dv;    // entry state
+    const float *dSg = dhist + task * static_cast<int64_t>(dk) * dv;  // exit gradient
+    auto row_of = [&](int r) { return (t0 + r) * H + h; };
+    auto live = [&](int r) { return t0 + r < tlim; };
 
     // P0: the chunk's inputs (rows past T are zero and contribute nothing)
     for (int idx = tid; idx < Cg * dk; idx += kGradThreads) {
@@ -723,8 +748,11 @@ struct PrepLayout {
     int64_t q, k, v, iq, ik, la, eb, wr, bytes;
 };
 
+// Token-head rows of the token tensors ([T,H,...] for packed sequences).
+int64_t token_rows(const ChunkArgs &f) { return (f.cu ? 1 : f.B) * f.T * f.H; }
+
 PrepLayout prep_layout(const ChunkArgs &f) {
-    const int64_t rows = f.B * f.T * f.H, dk = f.dk, dv = f.dv;
+    const int64_t rows = token_rows(f), dk = f.dk, dv = f.dv;
     const int64_t wch = f.value_write ? dv : dk;
     PrepLayout l{};
     int64_t off = 0;
@@ -760,24 +788,47 @@ int chunk_bwd_chunk(int64_t dk, int64_t dv, int C) {
 // which add a per-chunk record region after the two state records.
 static bool matrix_scans(int64_t dk, int64_t dv, int Cg) { return dk == 128 && dv == 128 && Cg == 16; }
 
-static size_t core_workspace(int64_t B, int64_t H, int64_t T, int64_t dk, int64_t dv, int C) {
-    const int Cg = chunk_bwd_chunk(dk, dv, C);
-    if (!Cg || B * H * T == 0) return 0;
-    const int64_t nch = (T + Cg - 1) / Cg;
-    const int64_t one = B * H * nch * dk * dv * 4;
-    const int64_t rec = matrix_scans(dk, dv, Cg) ? static_cast<int64_t>(bwd_record_bytes(B * H * nch)) : 0;
-    return static_cast<size_t>(2 * ((one + 255) & ~int64_t(255)) + ((rec + 255) & ~int64_t(255)));
+// Chunks the records hold: B H ceil(T/Cg), or for packed sequences the
+// bound H (ceil(T/Cg) + N).
+static int64_t record_chunks(const ChunkArgs &f, int Cg) {
+    return f.cu ? f.H * varlen_chunk_bound(f.B, f.T, Cg) : f.B * f.H * ((f.T + Cg - 1) / Cg);
+}
+
+// Regions of the backward's own workspace: the state records, the
+// gradient records, the per-chunk records (dk = dv = 128), the plan (packed).
+struct CoreLayout {
+    int64_t hist, dhist, rec, plan, bytes;
+};
+
+static CoreLayout core_layout(const ChunkArgs &f, int Cg) {
+    const int64_t chunks = record_chunks(f, Cg);
+    const int64_t one = (chunks * f.dk * f.dv * 4 + 255) & ~int64_t(255);
+    const int64_t rec = matrix_scans(f.dk, f.dv, Cg) ? static_cast<int64_t>(bwd_record_bytes(chunks)) : 0;
+    CoreLayout l;
+    l.hist = 0;
+    l.dhist = one;
+    l.rec = 2 * one;
+    l.plan = l.rec + ((rec + 255) & ~int64_t(255));
+    l.bytes = l.plan + (f.cu ? static_cast<int64_t>(varlen_plan_bytes(f.B, f.T, Cg)) : 0);
+    return l;
+}
+
+static size_t core_workspace(const ChunkArgs &f) {
+    const int Cg = chunk_bwd_chunk(f.dk, f.dv, f.C);
+    if (!Cg || f.B * f.H * f.T == 0) return 0;
+    return static_cast<size_t>(core_layout(f, Cg).bytes);
 }
 
 // The two scans on the vector ALU (any head size): the general forward records
 // the states, bwd_dstate_kernel the state gradients.
-static hipError_t launch_bwd_scans_general(const BwdArgs &a, int Cg, float *hist, float *dhist, hipStream_t s) {
+static hipError_t launch_bwd_scans_general(const BwdArgs &a, const VarPlan &vp, int Cg, float *hist, float *dhist,
+                                           hipStream_t s) {
     const ChunkArgs &f = a.f;
     const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
     ChunkArgs fwd = f;
     fwd.o = nullptr;
     fwd.s_out = nullptr;
-    hipError_t e = launch_chunk_general_hist(fwd, Cg, hist, s);
+    hipError_t e = launch_chunk_general_hist(fwd, Cg, hist, vp, s);
     if (e != hipSuccess) return e;
 
     int DVT = 0;
@@ -791,12 +842,12 @@ static hipError_t launch_bwd_scans_general(const BwdArgs &a, int Cg, float *hist
                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds))) != hipSuccess)
         return e;
     hipLaunchKernelGGL(bwd_dstate_kernel, dim3(static_cast<unsigned>(f.B * f.H), static_cast<unsigned>((dv + DVT - 1) / DVT)),
-                       dim3(kRevThreads), lds, s, a, Cg, DVT, dhist);
+                       dim3(kRevThreads), lds, s, a, Cg, DVT, dhist, vp);
     return hipGetLastError();
 }
 
 size_t chunk_bwd_workspace(const ChunkArgs &f) {
-    const size_t core = core_workspace(f.B, f.H, f.T, f.dk, f.dv, f.C);
+    const size_t core = core_workspace(f);
     if (!core) return 0;
     return core + static_cast<size_t>(prep_layout(f).bytes);
 }
@@ -808,7 +859,7 @@ hipError_t launch_chunk_bwd(const BwdArgs &a, void *ws, hipStream_t s) {
     if (!f.gate_logits && !f.qk_norm) return launch_core(a, ws, s);
     // fused input preparation: prepare, run the backward on the prepared
     // copy, then the chain rule of the preparation in place on the gradients
-    char *base = static_cast<char *>(ws) + core_workspace(f.B, f.H, f.T, f.dk, f.dv, f.C);
+    char *base = static_cast<char *>(ws) + core_workspace(f);
     const PrepLayout l = prep_layout(f);
     PrepBufs p{};
     if (f.qk_norm) {
@@ -823,7 +874,7 @@ hipError_t launch_chunk_bwd(const BwdArgs &a, void *ws, hipStream_t s) {
         p.eb = reinterpret_cast<float *>(base + l.eb);
         if (f.wr) p.wr = reinterpret_cast<float *>(base + l.wr);
     }
-    const int64_t rows = f.B * f.T * f.H;
+    const int64_t rows = token_rows(f);
     const int64_t blocks = (rows + 3) / 4 < 65536 ? (rows + 3) / 4 : 65536;
     hipLaunchKernelGGL(bwd_prepare_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, f, p, rows);
     hipError_t e = hipGetLastError();
@@ -852,23 +903,25 @@ static hipError_t launch_core(const BwdArgs &a, void *ws, hipStream_t s) {
     const int dk = static_cast<int>(f.dk), dv = static_cast<int>(f.dv);
     const int Cg = chunk_bwd_chunk(dk, dv, f.C);
     if (!Cg) return hipErrorInvalidValue;
-    const int64_t nch = (f.T + Cg - 1) / Cg;
-    const int64_t one = f.B * f.H * nch * dk * dv * 4;
-    float *hist = static_cast<float *>(ws);
-    float *dhist = reinterpret_cast<float *>(static_cast<char *>(ws) + ((one + 255) & ~int64_t(255)));
-    if (f.B * f.H * nch > 0x7fffffffLL) return hipErrorInvalidValue;
-    if (matrix_scans(dk, dv, Cg)) {
-        float *rec = reinterpret_cast<float *>(static_cast<char *>(ws) + 2 * ((one + 255) & ~int64_t(255)));
-        return launch_bwd_d128(a, rec, hist, dhist, static_cast<int>(nch), s);
-    }
-    hipError_t e = launch_bwd_scans_general(a, Cg, hist, dhist, s);
-    if (e != hipSuccess) return e;
+    const int64_t chunks = record_chunks(f, Cg);
+    if (chunks > 0x7fffffffLL) return hipErrorInvalidValue;
+    const CoreLayout l = core_layout(f, Cg);
+    char *w = static_cast<char *>(ws);
+    float *hist = reinterpret_cast<float *>(w + l.hist);
+    float *dhist = reinterpret_cast<float *>(w + l.dhist);
+    VarPlan vp{};
+    hipError_t e;
+    if (f.cu && (e = launch_varlen_plan(f.cu, f.B, f.T, Cg, w + l.plan, &vp, s)) != hipSuccess) return e;
+    const int nch = static_cast<int>((f.T + Cg - 1) / Cg);
+    if (matrix_scans(dk, dv, Cg)) return launch_bwd_d128(a, vp, reinterpret_cast<float *>(w + l.rec), hist, dhist, nch, s);
+    if ((e = launch_bwd_scans_general(a, vp, Cg, hist, dhist, s)) != hipSuccess) return e;
     const size_t lds = static_cast<size_t>(grad_layout(Cg, dk, dv).total) * 4;
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_grads_kernel),
                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds))) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(bwd_grads_kernel, dim3(static_cast<unsigned>(f.B * f.H * nch)), dim3(kGradThreads), lds, s, a,
-                       Cg, static_cast<const float *>(hist), static_cast<const float *>(dhist));
+    // (packed sequences: launched for the bound; the kernel reads the count)
+    hipLaunchKernelGGL(bwd_grads_kernel, dim3(static_cast<unsigned>(chunks)), dim3(kGradThreads), lds, s, a, Cg,
+                       static_cast<const float *>(hist), static_cast<const float *>(dhist), vp);
     return hipGetLastError();
 }
 

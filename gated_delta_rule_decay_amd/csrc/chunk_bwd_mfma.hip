@@ -61,27 +61,88 @@ __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Where a task (one chunk of one head) sits: head h, first token tok0 on the
+// flattened [B*T] token axis, end tlim of its sequence.  B sequences of T
+// tokens: task = (b H + h) nch + n; packed sequences (f.cu): chunk-major,
+// task = chunk H + h, placed by the plan's chunk table.
+struct BTask {
+    int64_t h, tok0, tlim;
+};
+
+__device__ __forceinline__ BTask btask(const ChunkArgs &f, const VarPlan &vp, int64_t task, int nch) {
+    BTask t;
+    if (f.cu) {
+        const int64_t gc = task / f.H;
+        const int2 e = vp.tab[gc];
+        t.h = task - gc * f.H;
+        t.tok0 = e.x;
+        t.tlim = e.y;
+    } else {
+        const int64_t bh = task / nch, n = task - bh * nch, b = bh / f.H;
+        t.h = bh - b * f.H;
+        t.tok0 = b * f.T + n * BC;
+        t.tlim = b * f.T + f.T;
+    }
+    return t;
+}
+
+// The tasks a chain (one sequence, one head; chain = sequence H + head)
+// walks: task0 + n tstr for n < nc, tokens from tbase, sequence end tlim.
+struct BChain {
+    int64_t h, task0, tstr, tbase, tlim;
+    int nc;
+};
+
+__device__ __forceinline__ BChain bchain(const ChunkArgs &f, const VarPlan &vp, int64_t chain, int nch) {
+    BChain c;
+    const int64_t i = chain / f.H;
+    c.h = chain - i * f.H;
+    if (f.cu) {
+        const int p0 = vp.pfx[i];
+        const int2 e = vp.seq[i];
+        c.nc = vp.pfx[i + 1] - p0;
+        c.task0 = static_cast<int64_t>(p0) * f.H + c.h;
+        c.tstr = f.H;
+        c.tbase = e.x;
+        c.tlim = e.y;
+    } else {
+        c.nc = nch;
+        c.task0 = chain * nch;
+        c.tstr = 1;
+        c.tbase = i * f.T;
+        c.tlim = c.tbase + f.T;
+    }
+    return c;
+}
+
+// Tasks of a launch: every chunk of every head (read from the plan for
+// packed sequences).
+__device__ __forceinline__ int64_t btask_count(const ChunkArgs &f, const VarPlan &vp, int nch) {
+    return f.cu ? f.H * vp.pfx[f.B] : f.B * f.H * nch;
+}
+
 // ---------------------------------------------------------------------------
 // the record pass
 
 constexpr int KS = BD + 1;  // odd row stride: the Gram loops read one channel of different rows
 
-__global__ void __launch_bounds__(BNT) bwd_record_kernel(BwdArgs a, float *rec, int nch) {
+__global__ void __launch_bounds__(BNT) bwd_record_kernel(BwdArgs a, VarPlan vp, float *rec, int nch) {
     __shared__ float K[BC * KS], Q[BC * KS], G[BC * KS], E[BC * KS], U[BC * KS];
     __shared__ float A[BC * BC], Tm[BC * BC], gC[BD];
     const ChunkArgs &f = a.f;
     const int64_t T = f.T, H = f.H;
-    const int64_t ntask = f.B * H * nch;
+    const int64_t ntask = btask_count(f, vp, nch);
     const int tid = threadIdx.x;
     for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
-        const int64_t bh = task / nch, n = task % nch, b = bh / H, h = bh % H, t0 = n * BC;
+        const BTask tp = btask(f, vp, task, nch);
+        const int64_t h = tp.h;
         float *out = rec + task * REC_BWD;
         __syncthreads();  // the previous task is done with LDS
         for (int idx = tid; idx < BC * BD; idx += BNT) {
             const int r = idx / BD, c = idx % BD;
             float kv = 0.f, qv = 0.f, la = 0.f, e = 0.f, u = 0.f;
-            if (t0 + r < T) {
-                const int64_t row = (b * T + t0 + r) * H + h;
+            if (tp.tok0 + r < tp.tlim) {
+                const int64_t row = (tp.tok0 + r) * H + h;
                 kv = load_qkv(f.k, row * BD + c, f.bf16);
                 qv = f.q_scale * load_qkv(f.q, row * BD + c, f.bf16);
                 la = load_gate(f.la, f.la_key, row, BD, c);
@@ -203,24 +264,24 @@ __device__ __forceinline__ void stage_store(const Staged &st, ScanLds &L, int ti
 
 // Four values of a [B*T*H, 128] row-major tensor for lane (kq, n): rows
 // (tokens) 4 kq + j of the chunk, column col; zero past T.
-__device__ __forceinline__ void load_rows4(float (&x)[4], const void *p, int bf16, int64_t b, int64_t h, int64_t t0,
-                                           int kq, int col, const ChunkArgs &f) {
+__device__ __forceinline__ void load_rows4(float (&x)[4], const void *p, int bf16, int64_t h, int64_t tok0,
+                                           int64_t tlim, int kq, int col, const ChunkArgs &f) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int64_t t = t0 + 4 * kq + j;
-        x[j] = t < f.T ? load_qkv(p, ((b * f.T + t) * f.H + h) * BD + col, bf16) : 0.f;
+        const int64_t t = tok0 + 4 * kq + j;
+        x[j] = t < tlim ? load_qkv(p, (t * f.H + h) * BD + col, bf16) : 0.f;
     }
 }
 
 // The values of lane (kq, n)'s rows, times the write gate in the value-write form.
-__device__ __forceinline__ void load_vals4(float (&x)[4], int64_t b, int64_t h, int64_t t0, int kq, int col,
+__device__ __forceinline__ void load_vals4(float (&x)[4], int64_t h, int64_t tok0, int64_t tlim, int kq, int col,
                                            const ChunkArgs &f) {
-    load_rows4(x, f.v, f.bf16, b, h, t0, kq, col, f);
+    load_rows4(x, f.v, f.bf16, h, tok0, tlim, kq, col, f);
     if (f.value_write) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int64_t t = t0 + 4 * kq + j;
-            if (t < f.T) x[j] *= load_gate(f.wr, f.wr_key, (b * f.T + t) * f.H + h, BD, col);
+            const int64_t t = tok0 + 4 * kq + j;
+            if (t < tlim) x[j] *= load_gate(f.wr, f.wr_key, t * f.H + h, BD, col);
         }
     }
 }
@@ -234,15 +295,18 @@ __device__ __forceinline__ void put_state(float *dst, const f4 (&s)[8], int kq, 
 }
 
 // The state entering every chunk, hist[chain][chunk][128][128].
-__global__ void __launch_bounds__(BNT) bwd_state_kernel(BwdArgs a, const float *rec, float *hist, int nch) {
+__global__ void __launch_bounds__(BNT) bwd_state_kernel(BwdArgs a, VarPlan vp, const float *rec, float *hist,
+                                                        int nch) {
     __shared__ __attribute__((aligned(16))) ScanLds L;
     const ChunkArgs &f = a.f;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int m = lane & 15, kq = lane >> 4;
-    const int64_t bh = blockIdx.x >> 1, b = bh / f.H, h = bh % f.H;
+    const int64_t bh = blockIdx.x >> 1;
+    const BChain ch = bchain(f, vp, bh, nch);
+    const int64_t h = ch.h;
     const int col = 64 * (blockIdx.x & 1) + 16 * wv + m;  // this lane's value column (as n)
-    const float *rc = rec + bh * nch * static_cast<int64_t>(REC_BWD);
-    float *hs = hist + bh * nch * static_cast<int64_t>(BD * BD);
+    auto rc = [&](int n) { return rec + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(REC_BWD); };
+    auto hs = [&](int n) { return hist + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(BD * BD); };
 
     f4 S[8];
 #pragma unroll
@@ -253,17 +317,19 @@ __global__ void __launch_bounds__(BNT) bwd_state_kernel(BwdArgs a, const float *
     // m0 = Kbar, m1 = Etil, m2 = Util; t0 = Tm, t1 = Bm
     Staged st;
     float vn[4];
-    stage_load(st, rc, R_KB, R_ET, R_UT, R_TM, R_BM, tid);
-    load_vals4(vn, b, h, 0, kq, col, f);
-    for (int n = 0; n < nch; ++n) {
+    if (ch.nc > 0) {
+        stage_load(st, rc(0), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
+        load_vals4(vn, h, ch.tbase, ch.tlim, kq, col, f);
+    }
+    for (int n = 0; n < ch.nc; ++n) {
         __syncthreads();  // every wave done with the previous chunk's LDS copy
         stage_store(st, L, tid);
         float v[4] = {vn[0], vn[1], vn[2], vn[3]};
-        if (n + 1 < nch) {
-            stage_load(st, rc + (n + 1) * static_cast<int64_t>(REC_BWD), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
-            load_vals4(vn, b, h, (n + 1) * BC, kq, col, f);
+        if (n + 1 < ch.nc) {
+            stage_load(st, rc(n + 1), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
+            load_vals4(vn, h, ch.tbase + (n + 1) * BC, ch.tlim, kq, col, f);
         }
-        put_state(hs + n * static_cast<int64_t>(BD * BD), S, kq, col);
+        put_state(hs(n), S, kq, col);
         __syncthreads();
         // X = Kbar S + Bm V (token rows)
         f4 X = {0.f, 0.f, 0.f, 0.f};
@@ -302,15 +368,18 @@ __global__ void __launch_bounds__(BNT) bwd_state_kernel(BwdArgs a, const float *
 
 // The gradient of every chunk's exit state, dhist[chain][chunk][128][128],
 // carried backwards from d_sT; the gradient of S0 at the end.
-__global__ void __launch_bounds__(BNT) bwd_dgrad_kernel(BwdArgs a, const float *rec, float *dhist, int nch) {
+__global__ void __launch_bounds__(BNT) bwd_dgrad_kernel(BwdArgs a, VarPlan vp, const float *rec, float *dhist,
+                                                        int nch) {
     __shared__ __attribute__((aligned(16))) ScanLds L;
     const ChunkArgs &f = a.f;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int m = lane & 15, kq = lane >> 4;
-    const int64_t bh = blockIdx.x >> 1, b = bh / f.H, h = bh % f.H;
+    const int64_t bh = blockIdx.x >> 1;
+    const BChain ch = bchain(f, vp, bh, nch);
+    const int64_t h = ch.h;
     const int col = 64 * (blockIdx.x & 1) + 16 * wv + m;
-    const float *rc = rec + bh * nch * static_cast<int64_t>(REC_BWD);
-    float *hs = dhist + bh * nch * static_cast<int64_t>(BD * BD);
+    auto rc = [&](int n) { return rec + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(REC_BWD); };
+    auto hs = [&](int n) { return dhist + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(BD * BD); };
 
     f4 dS[8];
 #pragma unroll
@@ -321,18 +390,20 @@ __global__ void __launch_bounds__(BNT) bwd_dgrad_kernel(BwdArgs a, const float *
     // m0 = Etil, m1 = Qbar, m2 = Kbar; t0 = Tm, t1 = R
     Staged st;
     float on[4];
-    const int nl = nch - 1;
-    stage_load(st, rc + nl * static_cast<int64_t>(REC_BWD), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
-    load_rows4(on, a.d_o, 0, b, h, static_cast<int64_t>(nl) * BC, kq, col, f);
+    const int nl = ch.nc - 1;
+    if (nl >= 0) {
+        stage_load(st, rc(nl), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
+        load_rows4(on, a.d_o, 0, h, ch.tbase + static_cast<int64_t>(nl) * BC, ch.tlim, kq, col, f);
+    }
     for (int n = nl; n >= 0; --n) {
         __syncthreads();
         stage_store(st, L, tid);
         float o[4] = {on[0], on[1], on[2], on[3]};
         if (n > 0) {
-            stage_load(st, rc + (n - 1) * static_cast<int64_t>(REC_BWD), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
-            load_rows4(on, a.d_o, 0, b, h, static_cast<int64_t>(n - 1) * BC, kq, col, f);
+            stage_load(st, rc(n - 1), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
+            load_rows4(on, a.d_o, 0, h, ch.tbase + static_cast<int64_t>(n - 1) * BC, ch.tlim, kq, col, f);
         }
-        put_state(hs + n * static_cast<int64_t>(BD * BD), dS, kq, col);
+        put_state(hs(n), dS, kq, col);
         __syncthreads();
         // dM = -(Etil dSo + R^T dO)  (token rows)
         f4 dM = {0.f, 0.f, 0.f, 0.f};
@@ -434,12 +505,12 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-__global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const float *rec, const float *hist,
-                                                           const float *dhist, int nch) {
+__global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp, const float *rec,
+                                                           const float *hist, const float *dhist, int nch) {
     __shared__ __attribute__((aligned(16))) GradLds L;
     const ChunkArgs &f = a.f;
-    const int64_t T = f.T, H = f.H;
-    const int64_t ntask = f.B * H * nch;
+    const int64_t H = f.H;
+    const int64_t ntask = btask_count(f, vp, nch);
     const bool la_key = f.la_key, eb_key = f.eb_key, wr_key = f.wr_key, tied = f.wr == nullptr;
     const bool vw = f.value_write;  // read along b k, erase / write along k, values w .* v
     // this wave's value columns of S and dSo, consumed by the value products;
@@ -464,11 +535,12 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
         asm volatile("" : "+v"(tid));
         const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int m = lane & 15, kq = lane >> 4;
-        const int64_t bh = task / nch, n = task % nch, b = bh / H, h = bh % H, t0 = n * BC;
+        const BTask tp = btask(f, vp, task, nch);
+        const int64_t h = tp.h;
         const float *rc = rec + task * REC_BWD;
         const float *Sg = hist + task * (BD * BD), *dSg = dhist + task * (BD * BD);
-        auto row_of = [&](int r) { return (b * T + t0 + r) * H + h; };
-        auto live = [&](int r) { return t0 + r < T; };
+        auto row_of = [&](int r) { return (tp.tok0 + r) * H + h; };
+        auto live = [&](int r) { return tp.tok0 + r < tp.tlim; };
         lds_barrier();  // the previous task is done with LDS
 
         const int vcol = 16 * wv + m;
@@ -840,22 +912,25 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, const floa
 
 size_t bwd_record_bytes(int64_t chunks) { return static_cast<size_t>(chunks * REC_BWD * 4); }
 
-hipError_t launch_bwd_d128(const BwdArgs &a, float *rec, float *hist, float *dhist, int nch, hipStream_t s) {
+hipError_t launch_bwd_d128(const BwdArgs &a, const VarPlan &vp, float *rec, float *hist, float *dhist, int nch,
+                           hipStream_t s) {
     const ChunkArgs &f = a.f;
-    const int64_t tasks = f.B * f.H * nch;
+    // (packed sequences: the bound on the task count; the kernels read the count)
+    const int64_t tasks = f.cu ? f.H * varlen_chunk_bound(f.B, f.T, BC) : f.B * f.H * nch;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int64_t g1 = tasks < 8 * cus ? tasks : 8 * cus;
-    hipLaunchKernelGGL(bwd_record_kernel, dim3(static_cast<unsigned>(g1)), dim3(BNT), 0, s, a, rec, nch);
+    hipLaunchKernelGGL(bwd_record_kernel, dim3(static_cast<unsigned>(g1)), dim3(BNT), 0, s, a, vp, rec, nch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned g2 = static_cast<unsigned>(f.B * f.H * 2);
-    hipLaunchKernelGGL(bwd_state_kernel, dim3(g2), dim3(BNT), 0, s, a, static_cast<const float *>(rec), hist, nch);
+    hipLaunchKernelGGL(bwd_state_kernel, dim3(g2), dim3(BNT), 0, s, a, vp, static_cast<const float *>(rec), hist, nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dgrad_kernel, dim3(g2), dim3(BNT), 0, s, a, static_cast<const float *>(rec), dhist, nch);
+    hipLaunchKernelGGL(bwd_dgrad_kernel, dim3(g2), dim3(BNT), 0, s, a, vp, static_cast<const float *>(rec), dhist,
+                       nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t g3 = tasks < cus ? tasks : cus;  // one 137 KiB workgroup per CU
-    hipLaunchKernelGGL(bwd_grads128_kernel, dim3(static_cast<unsigned>(g3)), dim3(GNT), 0, s, a,
+    hipLaunchKernelGGL(bwd_grads128_kernel, dim3(static_cast<unsigned>(g3)), dim3(GNT), 0, s, a, vp,
                        static_cast<const float *>(rec), static_cast<const float *>(hist),
                        static_cast<const float *>(dhist), nch);
     return hipGetLastError();

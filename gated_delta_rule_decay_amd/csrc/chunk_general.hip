@@ -25,7 +25,8 @@
 // erase and write vectors k, and values w .* v.
 //
 // With `hist` set (the backward's first step), the kernel instead records
-// the state entering every chunk, hist[chain][chunk][dk][dv], and writes
+// the state entering every chunk, hist[chain][chunk][dk][dv] (packed
+// sequences: hist[chunk][head][dk][dv], the chunks of the plan), and writes
 // no output.
 #include "common.h"
 #include "kernels.h"
@@ -68,7 +69,8 @@ __host__ __device__ inline GenLayout gen_layout(int Cg, int DVT, int dk) {
     return L;
 }
 
-__global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, int Cg, int DVT, float *hist) {
+__global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, int Cg, int DVT, float *hist,
+                                                                 VarPlan vp) {
     extern __shared__ float lds[];
     const int dk = static_cast<int>(a.dk), dv = static_cast<int>(a.dv);
     const int64_t T = a.T, H = a.H;
@@ -85,9 +87,16 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
     // tokens, or, packed, offsets cu[b], cu[b+1] clamped into [0, T] and
     // [lo, T] (no access leaves the tensors whatever they hold)
     int64_t lo = b * T, hi = lo + T;
-    if (a.cu) {
+    int64_t nmax = (T + Cg - 1) / Cg;  // chunks this chain walks
+    if (a.cu && vp.seq) {               // the plan's ranges and chunk counts (the backward's records)
+        const int2 e = vp.seq[b];
+        lo = e.x;
+        hi = e.y;
+        nmax = vp.pfx[b + 1] - vp.pfx[b];
+    } else if (a.cu) {
         lo = min(max(static_cast<int64_t>(a.cu[b]), int64_t(0)), T);
         hi = min(max(static_cast<int64_t>(a.cu[b + 1]), lo), T);
+        nmax = (hi - lo + Cg - 1) / Cg;
     }
     const int col0 = blockIdx.y * DVT;
     const int ncol = min(DVT, dv - col0);
@@ -100,10 +109,11 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
     }
 
     const int64_t nch = (T + Cg - 1) / Cg;  // (hist: B sequences of T tokens)
-    for (int64_t t0 = lo; t0 < hi; t0 += Cg) {
+    for (int64_t t0 = lo, n = 0; t0 < hi && n < nmax; t0 += Cg, ++n) {
         __syncthreads();
         if (hist) {
-            float *hs = hist + ((b * H + h) * nch + (t0 - lo) / Cg) * static_cast<int64_t>(dk) * dv;
+            const int64_t rec_i = a.cu ? (vp.pfx[b] + n) * H + h : (b * H + h) * nch + n;
+            float *hs = hist + rec_i * static_cast<int64_t>(dk) * dv;
             for (int idx = tid; idx < dk * DVT; idx += kThreads) {
                 const int c = idx / DVT, j = idx % DVT;
                 if (j < ncol) hs[static_cast<int64_t>(c) * dv + col0 + j] = S[idx];
@@ -307,11 +317,11 @@ hipError_t launch_chunk_general(const ChunkArgs &a, hipStream_t s) {
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
     dim3 grid(static_cast<unsigned>(a.B * a.H), static_cast<unsigned>((dv + DVT - 1) / DVT));
-    hipLaunchKernelGGL(chunk_general_kernel, grid, dim3(kThreads), lds, s, a, Cg, DVT, nullptr);
+    hipLaunchKernelGGL(chunk_general_kernel, grid, dim3(kThreads), lds, s, a, Cg, DVT, nullptr, VarPlan{});
     return hipGetLastError();
 }
 
-hipError_t launch_chunk_general_hist(const ChunkArgs &a, int Cg, float *hist, hipStream_t s) {
+hipError_t launch_chunk_general_hist(const ChunkArgs &a, int Cg, float *hist, const VarPlan &vp, hipStream_t s) {
     const int dk = static_cast<int>(a.dk), dv = static_cast<int>(a.dv);
     int DVT = 0;
     for (int w = 32; w >= 8 && !DVT; w /= 2) {
@@ -325,7 +335,7 @@ hipError_t launch_chunk_general_hist(const ChunkArgs &a, int Cg, float *hist, hi
                                        static_cast<int>(lds));
     if (e != hipSuccess) return e;
     dim3 grid(static_cast<unsigned>(a.B * a.H), static_cast<unsigned>((dv + DVT - 1) / DVT));
-    hipLaunchKernelGGL(chunk_general_kernel, grid, dim3(kThreads), lds, s, a, Cg, DVT, hist);
+    hipLaunchKernelGGL(chunk_general_kernel, grid, dim3(kThreads), lds, s, a, Cg, DVT, hist, vp);
     return hipGetLastError();
 }
 

@@ -1003,67 +1003,10 @@ int scan_segments(int64_t chains, int64_t nc) {
     return static_cast<int>((nc + len - 1) / len);  // no empty segment
 }
 
-// ----------------------------------------------------------------------------
-// Packed sequences: the plan.  Sequence i covers tokens [lo_i, hi_i) of the
-// flattened token axis, lo_i = cu[i] and hi_i = cu[i+1] clamped into
-// [0, T] and [lo_i, T]; its chunks start at lo_i, lo_i + C, ...  (the last
-// one ragged).  Chunk counts are capped at `cap` chunks in all, the number
-// the workspace holds: offsets that break 0 = cu[0] <= ... <= cu[N] = T give
-// unspecified results but never an access outside the tensors or the
-// workspace.
-constexpr int PLAN_NTH = 1024;
-
-// Ranges and chunk prefix counts (one workgroup, blocks of PLAN_NTH
-// sequences, an LDS scan per block).
-__global__ void __launch_bounds__(PLAN_NTH) varlen_plan_kernel(const int32_t *cu, int n, int64_t T, int cap,
-                                                               int2 *seq, int *pfx) {
-    __shared__ int64_t part[PLAN_NTH];  // 64-bit: overlapping ranges may sum past 2^31 chunks
-    const int tid = threadIdx.x;
-    int64_t carry = 0;
-    for (int base = 0; base < n; base += PLAN_NTH) {
-        const int i = base + tid;
-        int64_t cnt = 0;
-        if (i < n) {
-            const int64_t lo = min(max(static_cast<int64_t>(cu[i]), int64_t(0)), T);
-            const int64_t hi = min(max(static_cast<int64_t>(cu[i + 1]), lo), T);
-            seq[i] = make_int2(static_cast<int>(lo), static_cast<int>(hi));
-            cnt = (hi - lo + C - 1) / C;
-        }
-        part[tid] = cnt;
-        __syncthreads();
-        for (int off = 1; off < PLAN_NTH; off <<= 1) {
-            const int64_t x = tid >= off ? part[tid - off] : 0;
-            __syncthreads();
-            part[tid] += x;
-            __syncthreads();
-        }
-        if (i < n) pfx[i] = static_cast<int>(min(carry + part[tid] - cnt, static_cast<int64_t>(cap)));
-        const int64_t tot = part[PLAN_NTH - 1];
-        __syncthreads();  // every read of this block's scan before the next block's writes
-        carry = min(carry + tot, static_cast<int64_t>(cap));
-    }
-    if (tid == 0) pfx[n] = static_cast<int>(carry);
-}
-
-// The chunk table: first token of each chunk and the end of its sequence.
-__global__ void __launch_bounds__(256) varlen_table_kernel(const int2 *seq, const int *pfx, int n, int2 *tab) {
-    const int total = pfx[n];
-    for (int gc = blockIdx.x * 256 + threadIdx.x; gc < total; gc += gridDim.x * 256) {
-        int lo = 0, hi = n - 1;  // the last sequence that starts at or before chunk gc
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (pfx[mid] <= gc) lo = mid;
-            else hi = mid - 1;
-        }
-        const int2 e = seq[lo];
-        tab[gc] = make_int2(e.x + C * (gc - pfx[lo]), e.y);
-    }
-}
-
 struct Layout {
     int64_t nc, chains, ntask, nseg, seg_len;
     int64_t off_gam, off_xs, off_fs, bytes;
-    int64_t off_seq, off_pfx, off_tab;  // packed sequences
+    int64_t off_plan;  // packed sequences: the plan (varlen.hip)
 };
 
 Layout layout(int64_t B, int64_t H, int64_t T) {
@@ -1091,11 +1034,9 @@ Layout layout_varlen(int64_t N, int64_t H, int64_t T) {
     l.nseg = 1;
     l.seg_len = 0;
     l.off_gam = align256(l.ntask * REC * 2);
-    l.off_seq = l.off_gam + align256(l.ntask * D * 4);
-    l.off_pfx = l.off_seq + align256(N * 8);
-    l.off_tab = l.off_pfx + align256((N + 1) * 4);
+    l.off_plan = l.off_gam + align256(l.ntask * D * 4);
     l.off_xs = l.off_fs = 0;
-    l.bytes = l.off_tab + align256(l.nc * 8);
+    l.bytes = l.off_plan + static_cast<int64_t>(varlen_plan_bytes(N, T, C));
     return l;
 }
 
@@ -1117,20 +1058,12 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
     w.vpfx = nullptr;
     w.vtab = nullptr;
     if (a.cu) {
-        int2 *seq = reinterpret_cast<int2 *>(p + l.off_seq);
-        int *pfx = reinterpret_cast<int *>(p + l.off_pfx);
-        int2 *tab = reinterpret_cast<int2 *>(p + l.off_tab);
-        hipLaunchKernelGGL(varlen_plan_kernel, dim3(1), dim3(PLAN_NTH), 0, s, a.cu, static_cast<int>(a.B), a.T,
-                           static_cast<int>(l.nc), seq, pfx);
-        hipError_t e = hipGetLastError();
+        VarPlan vp;
+        hipError_t e = launch_varlen_plan(a.cu, a.B, a.T, C, p + l.off_plan, &vp, s);
         if (e != hipSuccess) return e;
-        const int64_t tb = (l.nc + 255) / 256;
-        hipLaunchKernelGGL(varlen_table_kernel, dim3(static_cast<unsigned>(tb < 1024 ? tb : 1024)), dim3(256), 0, s,
-                           seq, pfx, static_cast<int>(a.B), tab);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        w.vseq = seq;
-        w.vpfx = pfx;
-        w.vtab = tab;
+        w.vseq = vp.seq;
+        w.vpfx = vp.pfx;
+        w.vtab = vp.tab;
     }
     ScanPlan sp;
     sp.nseg = static_cast<int>(l.nseg);

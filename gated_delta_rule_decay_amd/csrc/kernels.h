@@ -58,9 +58,22 @@ hipError_t launch_chunk_split(const ChunkArgs &a, void *ws, hipStream_t s);
 // ceil(T/64) + B chunks per head.
 size_t chunk_split_workspace_varlen(int64_t N, int64_t H, int64_t T);
 
+// Packed sequences: the plan built on the device from the offsets
+// (varlen.hip), for chunks of C tokens.
+struct VarPlan {
+    const int2 *seq;  // [N]    token range [lo, hi) of each sequence
+    const int *pfx;   // [N+1]  chunks before each sequence; pfx[N]: all chunks
+    const int2 *tab;  // [chunk] first token of each chunk, end of its sequence
+};
+int64_t varlen_chunk_bound(int64_t N, int64_t T, int C);  // ceil(T/C) + N
+size_t varlen_plan_bytes(int64_t N, int64_t T, int C);
+hipError_t launch_varlen_plan(const int32_t *cu, int64_t N, int64_t T, int C, void *buf, VarPlan *plan,
+                              hipStream_t s);
+
 // The general forward recording the state that enters every chunk of Cg
-// tokens, hist[B*H][ceil(T/Cg)][dk][dv]; writes neither o nor the final state.
-hipError_t launch_chunk_general_hist(const ChunkArgs &a, int Cg, float *hist, hipStream_t s);
+// tokens, hist[B*H][ceil(T/Cg)][dk][dv] (packed sequences: the plan's chunks,
+// hist[chunk][H]); writes neither o nor the final state.
+hipError_t launch_chunk_general_hist(const ChunkArgs &a, int Cg, float *hist, const VarPlan &vp, hipStream_t s);
 
 // Backward of the chunked forward: gradients of <d_o, o> + <d_sT, S_T>.
 struct BwdArgs {
@@ -80,7 +93,8 @@ hipError_t launch_chunk_bwd(const BwdArgs &a, void *ws, hipStream_t s);
 // (state and state-gradient scans, per-chunk gradients), through per-chunk
 // records of bwd_record_bytes(B*H*chunks) bytes.
 size_t bwd_record_bytes(int64_t chunks);
-hipError_t launch_bwd_d128(const BwdArgs &a, float *rec, float *hist, float *dhist, int nch, hipStream_t s);
+hipError_t launch_bwd_d128(const BwdArgs &a, const VarPlan &vp, float *rec, float *hist, float *dhist, int nch,
+                           hipStream_t s);
 
 // Recurrent decode step.
 hipError_t launch_step(const StepArgs &a, hipStream_t s);

@@ -271,6 +271,37 @@ gdn2_status gdn2_chunk_bwd(const gdn2_desc *desc,
                            float *d_log_decay, float *d_erase, float *d_write,
                            float *d_state0, void *workspace, size_t ws_bytes, void *stream);
 
+/* Device workspace, in bytes, for gdn2_chunk_bwd_varlen on `desc` (batch =
+ * N sequences, seqlen = T packed tokens): the regions of
+ * gdn2_chunk_bwd_workspace sized for ceil(T/Cb) + N internal chunks per head,
+ * and the sequence plan.  Same validation as gdn2_chunk_bwd_varlen. */
+gdn2_status gdn2_chunk_bwd_varlen_workspace(const gdn2_desc *desc, size_t *bytes);
+
+/*
+ * Backward of gdn2_chunk_fwd_varlen: the gradients of
+ *     L = <d_o, o> + <d_state_out, S_T(i) for every sequence i>
+ * for N sequences packed along one token axis, each its own recurrence
+ * (training on packed documents).  The result for sequence i equals
+ * gdn2_chunk_bwd on its tokens alone.
+ *
+ *   desc, cu_seqlens   as for gdn2_chunk_fwd_varlen (offsets unchecked, but
+ *                clamped so that no access leaves the buffers).
+ *   q .. write, d_o, the gradients of q .. write   [T, H, ...] (the B = 1
+ *                layouts), rules as for gdn2_chunk_bwd.
+ *   state0, d_state_out, d_state0   [N, H, dk, dv] fp32.
+ *   workspace    as for gdn2_chunk_bwd, gdn2_chunk_bwd_varlen_workspace() bytes.
+ * Outputs must not overlap each other, cu_seqlens, any other input or the
+ * workspace (GDN2_ERR_ALIAS).  Rows outside every sequence are untouched; an
+ * empty sequence passes its state gradient through to d_state0.
+ */
+gdn2_status gdn2_chunk_bwd_varlen(const gdn2_desc *desc, const int32_t *cu_seqlens,
+                                  const void *q, const void *k, const void *v,
+                                  const float *log_decay, const float *erase, const float *write,
+                                  const float *state0, const float *d_o, const float *d_state_out,
+                                  float *dq, float *dk, float *dv,
+                                  float *d_log_decay, float *d_erase, float *d_write,
+                                  float *d_state0, void *workspace, size_t ws_bytes, void *stream);
+
 /*
  * One recurrent decode step for N = desc->batch sequences (desc->seqlen must
  * be 1): the O(1)-memory inference form ("Gated DeltaNet-2" blog summary,

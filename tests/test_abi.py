@@ -342,3 +342,36 @@ def test_varlen_checks(lib):
     assert fwd_varlen(lib, d, ws=WS + 16, wsb=need) == 6
     assert fwd_varlen(lib, d, ws=CU - 256, wsb=need) == 5
     assert fwd_varlen(lib, d, ws=O - 256, wsb=need) == 5
+
+
+def bwd_varlen(lib, desc, cu=CU, ws=BWS, wsb=None, d_o=DO, dq=DQ, ds0=DS0):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    if wsb is None:  # the size the library asks for (0 for a rejected descriptor)
+        n = ctypes.c_size_t(0)
+        if desc is not None:
+            lib.gdn2_chunk_bwd_varlen_workspace(ctypes.byref(desc), ctypes.byref(n))
+        wsb = n.value
+    return lib.gdn2_chunk_bwd_varlen(None if desc is None else ctypes.byref(desc), vp(cu), vp(Q), vp(K), vp(V),
+                                     vp(LA), vp(EB), vp(WR), vp(S0), vp(d_o), vp(DST), vp(dq), vp(DK), vp(DV),
+                                     vp(DLA), vp(DEB), vp(DWR), vp(ds0), vp(ws), wsb, None)
+
+
+def test_bwd_varlen_workspace_and_checks(lib):
+    a = lambda x: (x + 255) // 256 * 256
+    N, H, T = 3, 4, 200
+    nc = (T + 15) // 16 + N  # 16-token chunks per head, bounded
+    rec = (4 * 16 * 128 + 4 * 16 * 16 + 128) * 4
+    plan = a(N * 8) + a((N + 1) * 4) + a(nc * 8)
+    n = ctypes.c_size_t(0)
+    d = good(batch=N, seqlen=T)
+    assert lib.gdn2_chunk_bwd_varlen_workspace(ctypes.byref(d), ctypes.byref(n)) == 0
+    assert n.value == 2 * a(H * nc * 128 * 128 * 4) + a(H * nc * rec) + plan
+    assert lib.gdn2_chunk_bwd_varlen_workspace(None, ctypes.byref(n)) == 1
+    assert lib.gdn2_chunk_bwd_varlen_workspace(ctypes.byref(good(batch=3, seqlen=2 ** 31)), ctypes.byref(n)) == 2
+    assert bwd_varlen(lib, None) == 1
+    assert bwd_varlen(lib, d, cu=None) == 1
+    assert bwd_varlen(lib, d, d_o=None) == 1
+    assert bwd_varlen(lib, good(batch=0), cu=None) == 0        # no sequence: nothing to do
+    assert bwd_varlen(lib, d, ws=None) == 6
+    assert bwd_varlen(lib, d, dq=CU - 256) == 5                # a gradient over the offsets
+    assert bwd_varlen(lib, d, ds0=S0 + 3 * 4 * 128 * 128 * 4 - 256) == 5  # d_state0 over state0 ([N,H,dk,dv])

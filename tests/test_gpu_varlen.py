@@ -8,7 +8,11 @@ sequence start at its first token; the last one is ragged), the general fp32
 kernel, empty sequences, the value-write form and fused input preparation,
 the exact path, and at the full GDN-2 size: equal lengths against the
 batched forward (bit-exact: the same chunks through the same kernels) and a
-drawn length mix on sampled (sequence, head) pairs.
+drawn length mix on sampled (sequence, head) pairs.  The backward over packed
+sequences (gdn2_chunk_bwd_varlen) likewise: every sequence's gradients against
+the gradient oracle on that sequence alone (both paths, the value-write form
+and fused input preparation), and bit-exact against the batched backward at
+equal lengths.
 """
 import numpy as np
 import pytest
@@ -179,3 +183,91 @@ def test_full_size_length_mix_sampled():
     ln = np.array(lengths)
     pairs = [(int(ln.argmax()), 3), (int(ln.argmin()), 11), (5, 0), (9, 15)]
     _check(inp, TOL_BF16, pairs=pairs)
+
+
+# ---- the backward over packed sequences ------------------------------------
+
+def _bwd_check(inp, seed, raw=False, vw=False, chunk=64, pairs=None):
+    """Gradients of every sequence (or of the (sequence, head) pairs given)
+    against the gradient oracle run on that sequence alone."""
+    import torch
+    from gated_delta_rule_decay_amd import chunk_bwd_varlen
+    from oracle.oracle_bwd import gdn2_backward
+
+    r = np.random.Generator(np.random.PCG64(seed))
+    cu = inp["cu_seqlens"]
+    n = len(cu) - 1
+    d_o = r.standard_normal(inp["v"].shape).astype(np.float32)
+    d_st = r.standard_normal(inp["S0"].shape).astype(np.float32)
+    d = _dev(inp)
+    gn = _gates(inp, raw)
+    sq = lambda x: None if x is None else x[0]
+    g = chunk_bwd_varlen(sq(d["q"]), sq(d["k"]), sq(d["v"]), *[sq(d.get(x)) for x in gn], d["cu"], d["S0"],
+                         torch.from_numpy(d_o[0]).cuda(), torch.from_numpy(d_st).cuda(), chunk=chunk,
+                         value_write=vw, qk_l2norm=raw)
+    torch.cuda.synchronize()
+    got = {k: (None if x is None else x.cpu().numpy()) for k, x in g.items()}
+    names = ("dq", "dk", "dv", "d_log_decay", "d_erase", "d_write", "d_state0")
+    acc = {k: ([], []) for k in names}
+    for i, h in pairs or [(i, None) for i in range(n)]:
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        hs = slice(None) if h is None else slice(h, h + 1)
+        if hi > lo:
+            sl = lambda x: None if x is None else x[:, lo:hi, hs]
+            ref = gdn2_backward(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), *[sl(inp.get(x)) for x in gn],
+                                inp["S0"][i:i + 1, hs], sl(d_o), d_st[i:i + 1, hs], value_write=vw, raw=raw)
+        for key in names:
+            if got[key] is None:
+                continue
+            if key == "d_state0":
+                want = ref[key][0] if hi > lo else d_st[i, hs]
+                acc[key][0].append(got[key][i, hs].ravel())
+                acc[key][1].append(np.asarray(want).ravel())
+            elif hi > lo:
+                acc[key][0].append(got[key][lo:hi, hs].ravel())
+                acc[key][1].append(ref[key][0].ravel())
+    errs = {k: rel_l2(np.concatenate(a), np.concatenate(b)) for k, (a, b) in acc.items() if a}
+    print("  " + " ".join(f"{k}={e:.1e}" for k, e in errs.items()), flush=True)
+    for k, e in errs.items():
+        assert e <= TOL_F32, (k, e)
+
+
+@pytest.mark.parametrize("gates,tied", [("key", False), ("head", True)])
+def test_backward_bf16_d128(gates, tied):
+    w = W[2].scaled(H=2, gates=gates, tied=tied)
+    _bwd_check(synth.make_packed_inputs(w, LENGTHS, seed=960), seed=961)
+
+
+def test_backward_general_shapes():
+    w = W[2].scaled(H=2, dk=48, dv=80, qkv_dtype="f32")
+    _bwd_check(synth.make_packed_inputs(w, [5, 0, 33, 17, 64], seed=970), seed=971, chunk=16)
+
+
+def test_backward_raw_inputs_value_write():
+    w = W[2].scaled(H=2)
+    inp = synth.make_packed_inputs(w, [70, 3, 130, 0, 64], seed=980, raw=True)
+    r = np.random.Generator(np.random.PCG64(981))
+    inp["x_write"], inp["x_write_bf16"] = synth.round_to_bf16(r.standard_normal(inp["v"].shape).astype(np.float32))
+    _bwd_check(inp, seed=982, raw=True, vw=True)
+
+
+def test_backward_full_size_equal_lengths_match_batched():
+    # 8 x 4096 tokens, 16 heads: the same chunks through the same kernels as
+    # the batched backward (bit-exact)
+    import torch
+    from gated_delta_rule_decay_amd import chunk_bwd, chunk_bwd_varlen
+
+    w = W[2]
+    inp = synth.make_inputs(w, seed=990)
+    d = _dev({**inp, "cu_seqlens": synth.packed_offsets([w.T] * w.B)})
+    gen = torch.Generator(device="cuda").manual_seed(991)
+    d_o = torch.randn((w.B, w.T, w.H, w.dv), device="cuda", generator=gen)
+    d_st = torch.randn((w.B, w.H, w.dk, w.dv), device="cuda", generator=gen)
+    args = [d[n] for n in ("q", "k", "v", "log_decay", "erase", "write")]
+    gb = chunk_bwd(*args, d["S0"], d_o, d_st)
+    flat = lambda x: x.reshape((w.B * w.T,) + tuple(x.shape[2:]))
+    gp = chunk_bwd_varlen(*[flat(x) for x in args], d["cu"], d["S0"], flat(d_o), d_st)
+    torch.cuda.synchronize()
+    for key in ("dq", "dk", "dv", "d_log_decay", "d_erase", "d_write"):
+        assert torch.equal(flat(gb[key]), gp[key]), key
+    assert torch.equal(gb["d_state0"], gp["d_state0"])

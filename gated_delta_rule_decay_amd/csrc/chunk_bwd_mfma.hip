@@ -115,6 +115,22 @@ __device__ __forceinline__ BChain bchain(const ChunkArgs &f, const VarPlan &vp, 
     return c;
 }
 
+// sum_c A[m][c] B[c][n] over the 128 key channels, A row m from LDS (row
+// stride RS) in the channel order of the state registers B; four independent
+// accumulation chains (channel 16 it + 4 kq + i goes to chain i), so that the
+// matrix unit never waits on its own previous result for long.
+__device__ __forceinline__ f4 chan_product(const float *A, const f4 (&B)[8], int m, int kq, f4 init) {
+    const f4 z = {0.f, 0.f, 0.f, 0.f};
+    f4 acc[4] = {init, z, z, z};
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const f4 a4 = *reinterpret_cast<const f4 *>(&A[m * RS + 16 * it + 4 * kq]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = mfma4(a4[i], B[it][i], acc[i]);
+    }
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
 // Tasks of a launch: every chunk of every head (read from the plan for
 // packed sequences).
 __device__ __forceinline__ int64_t btask_count(const ChunkArgs &f, const VarPlan &vp, int nch) {
@@ -332,13 +348,7 @@ __global__ void __launch_bounds__(BNT) bwd_state_kernel(BwdArgs a, VarPlan vp, c
         put_state(hs(n), S, kq, col);
         __syncthreads();
         // X = Kbar S + Bm V (token rows)
-        f4 X = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const f4 k4 = *reinterpret_cast<const f4 *>(&L.m0[m * RS + 16 * it + 4 * kq]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) X = mfma4(k4[i], S[it][i], X);
-        }
+        f4 X = chan_product(L.m0, S, m, kq, f4{0.f, 0.f, 0.f, 0.f});
         {
             const f4 b4 = *reinterpret_cast<const f4 *>(&L.t1[m * BC + 4 * kq]);
 #pragma unroll
@@ -406,13 +416,7 @@ __global__ void __launch_bounds__(BNT) bwd_dgrad_kernel(BwdArgs a, VarPlan vp, c
         put_state(hs(n), dS, kq, col);
         __syncthreads();
         // dM = -(Etil dSo + R^T dO)  (token rows)
-        f4 dM = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const f4 e4 = *reinterpret_cast<const f4 *>(&L.m0[m * RS + 16 * it + 4 * kq]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dM = mfma4(e4[i], dS[it][i], dM);
-        }
+        f4 dM = chan_product(L.m0, dS, m, kq, f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int j = 0; j < 4; ++j) dM = mfma4(L.t1[(4 * kq + j) * BC + m], o[j], dM);
         dM = -dM;
@@ -617,39 +621,21 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
 #pragma unroll
                 for (int j = 0; j < 4; ++j) BV = mfma4(b4[j], v4[j], BV);
             }
-            f4 X = BV;
-#pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const f4 k4 = *reinterpret_cast<const f4 *>(&L.kb[m * RS + 16 * it + 4 * kq]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) X = mfma4(k4[i], S[it][i], X);
-            }
+            f4 X = chan_product(L.kb, S, m, kq, BV);
             f4 M = {0.f, 0.f, 0.f, 0.f};
             {
                 const f4 t4 = *reinterpret_cast<const f4 *>(&L.tm[m * BC + 4 * kq]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) M = mfma4(t4[j], X[j], M);
             }
-            f4 dM = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const f4 e4 = *reinterpret_cast<const f4 *>(&L.et[m * RS + 16 * it + 4 * kq]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dM = mfma4(e4[i], dS[it][i], dM);
-            }
+            f4 dM = chan_product(L.et, dS, m, kq, f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int j = 0; j < 4; ++j) dM = mfma4(L.rr[(4 * kq + j) * BC + m], o4[j], dM);
             dM = -dM;
             f4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < 4; ++j) Y = mfma4(L.tm[(4 * kq + j) * BC + m], dM[j], Y);
-            f4 dV = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const f4 u4 = *reinterpret_cast<const f4 *>(&L.ut[m * RS + 16 * it + 4 * kq]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) dV = mfma4(u4[i], dS[it][i], dV);
-            }
+            f4 dV = chan_product(L.ut, dS, m, kq, f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 dV = mfma4(L.pp[(4 * kq + j) * BC + m], o4[j], dV);

@@ -244,14 +244,17 @@ def time_backward(w, inp, torch, steps):
             "algorithmic_bytes_per_launch": bwd_bytes(w)}
 
 
-def time_packed(w, inp, torch, steps, n_seq=12):
+def time_packed(w, inp, torch, steps, n_seq=12, lengths=None):
     """Time gdn2_chunk_fwd_varlen on the workload's B*T tokens of every head
-    packed as n_seq sequences of drawn lengths (the same q/k/v/gate values,
-    one N(0, 0.1) initial state per sequence)."""
+    packed as n_seq sequences of drawn lengths (or the lengths given: the
+    same number of tokens), the same q/k/v/gate values, one N(0, 0.1)
+    initial state per sequence."""
     from gated_delta_rule_decay_amd import binding, chunk_fwd_varlen, synth
 
     tot = w.B * w.T
-    lengths = synth.draw_lengths(tot, n_seq, seed=950)
+    if lengths is None:
+        lengths = synth.draw_lengths(tot, n_seq, seed=950)
+    n_seq = len(lengths)
     d = to_dev(inp, torch)
     flat = lambda x: None if x is None else x.reshape((tot,) + tuple(x.shape[2:]))
     args = [flat(d[n]) for n in ("q", "k", "v", "log_decay", "erase", "write")]
@@ -375,6 +378,10 @@ def main():
                                  "roofline": roofline_hbm(chunk_bytes(w), kvw)}
         result["backward"] = time_backward(w, inp, torch, max(2, args.steps // 8))
         result["packed"] = time_packed(w, inp, torch, max(2, args.steps // 4))
+        # one sequence holding most of the tokens: cut into segments of the
+        # two-level scan (without them its chain alone would bound the scan)
+        result["packed_long"] = time_packed(w, inp, torch, max(2, args.steps // 4),
+                                            lengths=[28000, 2000, 1500, 1268])
     del inp
     if not args.no_extra:
         result["fused_inputs"] = time_fused(w, torch, chunk_fwd, max(2, args.steps // 4))

@@ -640,11 +640,28 @@ __device__ __forceinline__ void slot_barrier() {
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 struct ScanPlan {
-    int nseg;     // segments per chain (1: plain scan)
+    int nseg;     // segments per chain (1: plain scan); packed: unused
     int seg_len;  // chunks per segment; the last one may be shorter
-    float *xs;    // [chain][nseg][D][D] segment entry states X
+    float *xs;    // [chain][nseg][D][D] segment entry states X (packed: [slot][H][D][D])
     float *fs;    // [chain][nseg][D][D] segment transitions F (0 and nseg-1 unused)
+    // packed sequences, [N+1] exclusive prefix counts over the sequences of:
+    const int *qs;  // segments (the units of the scan proper)
+    const int *q1;  // segments but each sequence's last (the units of the summaries)
+    const int *zs;  // X / F slots (the segments of sequences cut in two or more)
+    const int *c2;  // sequences cut in three or more (the units of the combine)
 };
+
+// Packed sequences: the last sequence i in [0, n) with pre[i] <= q (for q
+// below pre[n], the one whose range of units holds q).
+__device__ __forceinline__ int seq_of(const int *pre, int n, int q) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= q) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
 
 // MODE 0: the scan proper (O and, for the last segment, the final state).
 // MODE 1: segment summaries; SCAN_W more compute waves carry the columns of
@@ -670,24 +687,36 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         half = G & 1;
         unit = G / 2;
     }
-    const int nsl = MODE ? sp.nseg - 1 : sp.nseg;  // segments per chain in this launch
-    const int chain = unit / nsl, seg = unit % nsl;
     // chunks [n0, n1) of this unit; chunk n is task task0 + n * tstr and
     // starts at token tbase + n * C of the flattened token axis; the
-    // sequence ends at tlim
-    int n0, n1;
-    int64_t h, task0, tstr, tbase, tlim;
-    if (a.cu) {  // packed sequences (one segment per chain)
-        const int i = chain / static_cast<int>(a.H), p0 = w.vpfx[i];
+    // sequence ends at tlim.  The chain has nsegc segments; its segment slots
+    // (X, F) are xbase + j xstep.
+    int chain, seg, nsegc, n0, n1;
+    int64_t h, task0, tstr, tbase, tlim, xbase, xstep;
+    if (a.cu) {  // packed sequences: units are (segment, head), segment-major
+        const int H = static_cast<int>(a.H), N = static_cast<int>(a.B);
+        const int q = unit / H;
+        const int *pre = MODE ? sp.q1 : sp.qs;  // the summaries skip each sequence's last segment
+        if (q >= pre[N]) return;                 // launched for the bound (the whole workgroup)
+        const int i = seq_of(pre, N, q), p0 = w.vpfx[i], nci = w.vpfx[i + 1] - p0;
         const int2 e = w.vseq[i];
-        h = chain - static_cast<int64_t>(i) * a.H;
-        n0 = 0;
-        n1 = w.vpfx[i + 1] - p0;
+        h = unit - q * H;
+        seg = q - pre[i];
+        nsegc = sp.qs[i + 1] - sp.qs[i];
+        chain = i * H + static_cast<int>(h);
+        n0 = seg * sp.seg_len;
+        n1 = nsegc == 1 ? nci : min(nci, n0 + sp.seg_len);
         task0 = static_cast<int64_t>(p0) * a.H + h;
         tstr = a.H;
         tbase = e.x;
         tlim = e.y;
+        xbase = ((static_cast<int64_t>(sp.zs[i]) + seg) * a.H + h) * D * D;
+        xstep = a.H * D * D;
     } else {
+        const int nsl = MODE ? sp.nseg - 1 : sp.nseg;  // segments per chain in this launch
+        chain = unit / nsl;
+        seg = unit % nsl;
+        nsegc = sp.nseg;
         const int64_t b = chain / a.H;
         h = chain % a.H;
         n0 = seg * sp.seg_len;
@@ -696,6 +725,8 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         tstr = 1;
         tbase = b * a.T;
         tlim = tbase + a.T;
+        xbase = (static_cast<int64_t>(chain) * sp.nseg + seg) * D * D;  // slot seg
+        xstep = D * D;
     }
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -705,7 +736,6 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     const int wt = wv % SCAN_W;                          // my tile within the slot's slices
     const int ct = SCAN_W * half + (copier ? 0 : wt);   // my value (or key) tile
     const int64_t sbase = static_cast<int64_t>(chain) * D * D;
-    const int64_t xbase = (static_cast<int64_t>(chain) * sp.nseg + seg) * D * D;  // slot seg
 
     f4 sacc[8];  // state slice (compute waves): tile it holds S[16it+4lg+e][16ct+lr]
 
@@ -904,7 +934,7 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
 #undef GDN2_COPY_STEP
     } else {
         const float *init = nullptr;
-        if (MODE == 0) init = sp.nseg == 1 ? (a.s0 ? a.s0 + sbase : nullptr) : sp.xs + xbase;
+        if (MODE == 0) init = nsegc == 1 ? (a.s0 ? a.s0 + sbase : nullptr) : sp.xs + xbase;
         else if (!frun && seg == 0 && a.s0) init = a.s0 + sbase;
 #pragma unroll
         for (int it = 0; it < 8; ++it)
@@ -927,8 +957,8 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         }
         float *dst = nullptr;
         if (idle) dst = nullptr;
-        else if (MODE == 0) dst = (seg == sp.nseg - 1 && a.s_out) ? a.s_out + sbase : nullptr;
-        else dst = frun ? sp.fs + xbase : sp.xs + xbase + D * D;  // F[seg], X[seg+1]
+        else if (MODE == 0) dst = (seg == nsegc - 1 && a.s_out) ? a.s_out + sbase : nullptr;
+        else dst = frun ? sp.fs + xbase : sp.xs + xbase + xstep;  // F[seg], X[seg+1]
         if (dst) {
 #pragma unroll
             for (int it = 0; it < 8; ++it)
@@ -949,16 +979,27 @@ constexpr int CMB_NTH = 256;
 constexpr int CMB_COLS = 16;
 constexpr int CMB_FST = D + 1;  // odd row stride: lanes on distinct rows hit distinct banks
 
-__global__ void __launch_bounds__(CMB_NTH) segment_combine_kernel(float *xs, const float *fs, int nseg) {
+__global__ void __launch_bounds__(CMB_NTH) segment_combine_kernel(float *xs, const float *fs, int nseg, ScanPlan sp,
+                                                                  int N, int H) {
     __shared__ float fl[D * CMB_FST];
     __shared__ float sx[D * CMB_COLS];
     const int chain = blockIdx.x / (D / CMB_COLS), cb = (blockIdx.x % (D / CMB_COLS)) * CMB_COLS;
     const int tid = threadIdx.x, i = tid % D, c0 = 8 * (tid / D);
-    const int64_t base = static_cast<int64_t>(chain) * nseg * D * D;
-    for (int e = tid; e < D * CMB_COLS; e += CMB_NTH) sx[e] = xs[base + D * D + (e / CMB_COLS) * D + cb + e % CMB_COLS];
+    // slot j of this chain at base + j step: [chain][nseg] for B sequences of
+    // T tokens; packed, the chains cut in three or more, slots (zs[s] + j) H + h
+    int64_t base = static_cast<int64_t>(chain) * nseg * D * D, step = static_cast<int64_t>(D) * D;
+    if (sp.qs) {
+        const int k = chain / H, h = chain - k * H;
+        if (k >= sp.c2[N]) return;  // launched for the bound
+        const int sq = seq_of(sp.c2, N, k);
+        nseg = sp.qs[sq + 1] - sp.qs[sq];
+        base = (static_cast<int64_t>(sp.zs[sq]) * H + h) * D * D;
+        step = static_cast<int64_t>(H) * D * D;
+    }
+    for (int e = tid; e < D * CMB_COLS; e += CMB_NTH) sx[e] = xs[base + step + (e / CMB_COLS) * D + cb + e % CMB_COLS];
     f4 pf[16];
     auto load_f = [&](int j) __attribute__((always_inline)) {
-        const f4 *src = reinterpret_cast<const f4 *>(fs + base + static_cast<int64_t>(j) * D * D);
+        const f4 *src = reinterpret_cast<const f4 *>(fs + base + static_cast<int64_t>(j) * step);
 #pragma unroll
         for (int q = 0; q < 16; ++q) pf[q] = src[tid + CMB_NTH * q];
     };
@@ -973,7 +1014,7 @@ __global__ void __launch_bounds__(CMB_NTH) segment_combine_kernel(float *xs, con
         }
         __syncthreads();
         if (j + 1 <= nseg - 2) load_f(j + 1);
-        float *xj = xs + base + static_cast<int64_t>(j + 1) * D * D + static_cast<int64_t>(i) * D + cb + c0;
+        float *xj = xs + base + static_cast<int64_t>(j + 1) * step + static_cast<int64_t>(i) * D + cb + c0;
         f4 acc0 = *reinterpret_cast<const f4 *>(xj), acc1 = *reinterpret_cast<const f4 *>(xj + 4);
         for (int k = 0; k < D; ++k) {
             const float f = fl[i * CMB_FST + k];
@@ -1003,10 +1044,82 @@ int scan_segments(int64_t chains, int64_t nc) {
     return static_cast<int>((nc + len - 1) / len);  // no empty segment
 }
 
+// Packed sequences: the segments of the two-level scan.  Sequence i of nc_i
+// chunks is cut into ceil(nc_i / L) segments when nc_i > 2 L, else scanned in
+// one: the summaries of all but the last segment run before the scan proper,
+// so two segments would cost as many sequential steps as none, three or more
+// cut the chain's sequential length to 2 L.  The host sizes the units and slots for valid offsets (bounds that
+// depend on T alone); a sequence that would exceed one is scanned in one
+// segment instead (which only offsets that break the contract can cause), so
+// every count stays within its bound and every result is still exact.
+constexpr int SP_NTH = 1024;
+
+__device__ __forceinline__ void block_scan4(int4 *part, int tid) {
+    for (int off = 1; off < SP_NTH; off <<= 1) {
+        const int4 x = tid >= off ? part[tid - off] : make_int4(0, 0, 0, 0);
+        __syncthreads();
+        part[tid].x += x.x;
+        part[tid].y += x.y;
+        part[tid].z += x.z;
+        part[tid].w += x.w;
+        __syncthreads();
+    }
+}
+
+__global__ void __launch_bounds__(SP_NTH) varlen_segment_kernel(const int *pfx, int n, int L, int q1b, int zb, int c2b,
+                                                                int *qs, int *q1, int *zs, int *c2) {
+    __shared__ int4 part[SP_NTH];
+    const int tid = threadIdx.x;
+    int4 c_orig = make_int4(0, 0, 0, 0), c_fin = make_int4(0, 0, 0, 0);  // carries
+    auto counts = [](int ns) { return make_int4(ns, ns - 1, ns > 1 ? ns : 0, ns > 2 ? 1 : 0); };
+    for (int base = 0; base < n; base += SP_NTH) {
+        const int i = base + tid;
+        int ns = 0;
+        if (i < n) {
+            const int nc = pfx[i + 1] - pfx[i];
+            ns = nc > 2 * L ? (nc + L - 1) / L : 1;
+        }
+        // the requested cuts' prefix decides which sequences stay cut
+        const int4 want = i < n ? counts(ns) : make_int4(0, 0, 0, 0);
+        part[tid] = want;
+        __syncthreads();
+        block_scan4(part, tid);
+        const int4 incl = part[tid];
+        const int4 tot = part[SP_NTH - 1];
+        if (i < n && ns > 1 &&
+            (c_orig.y + incl.y > q1b || c_orig.z + incl.z > zb || c_orig.w + incl.w > c2b))
+            ns = 1;
+        c_orig.x += tot.x; c_orig.y += tot.y; c_orig.z += tot.z; c_orig.w += tot.w;
+        __syncthreads();
+        // the final counts' prefix
+        const int4 have = i < n ? counts(ns) : make_int4(0, 0, 0, 0);
+        part[tid] = have;
+        __syncthreads();
+        block_scan4(part, tid);
+        const int4 in2 = part[tid], tot2 = part[SP_NTH - 1];
+        if (i < n) {
+            qs[i] = c_fin.x + in2.x - have.x;
+            q1[i] = c_fin.y + in2.y - have.y;
+            zs[i] = c_fin.z + in2.z - have.z;
+            c2[i] = c_fin.w + in2.w - have.w;
+        }
+        c_fin.x += tot2.x; c_fin.y += tot2.y; c_fin.z += tot2.z; c_fin.w += tot2.w;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        qs[n] = c_fin.x;
+        q1[n] = c_fin.y;
+        zs[n] = c_fin.z;
+        c2[n] = c_fin.w;
+    }
+}
+
 struct Layout {
     int64_t nc, chains, ntask, nseg, seg_len;
     int64_t off_gam, off_xs, off_fs, bytes;
-    int64_t off_plan;  // packed sequences: the plan (varlen.hip)
+    // packed sequences: the plan (varlen.hip), the segment prefix counts, and
+    // the bounds on the summary units, slots and combined sequences
+    int64_t off_plan, off_seg, q1b, zb, c2b;
 };
 
 Layout layout(int64_t B, int64_t H, int64_t T) {
@@ -1026,17 +1139,30 @@ Layout layout(int64_t B, int64_t H, int64_t T) {
 
 // Packed sequences: N sequences, T tokens in all, at most ceil(T/C) + N
 // chunks per head (each sequence's last chunk the only partial one).
+// Packed sequences: segments of L chunks, L chosen (from T and H, the host
+// knows no lengths) so that the longest chain is cut to about as many chunks
+// as SEG_WG / 2 scan units share evenly.  A sequence cut has more than 2 L
+// chunks, so more than 64 L tokens: at most long_max = ceil(T / 64 L) are cut,
+// and the units and slots are bounded by T alone (not by the sequence count).
 Layout layout_varlen(int64_t N, int64_t H, int64_t T) {
     Layout l;
-    l.nc = (T + C - 1) / C + N;  // chunk bound per head
+    const int64_t ct = (T + C - 1) / C;
+    l.nc = ct + N;  // chunk bound per head
     l.chains = N * H;
     l.ntask = l.nc * H;
     l.nseg = 1;
-    l.seg_len = 0;
+    const int64_t want = (H * ct + SEG_WG / 2 - 1) / (SEG_WG / 2);
+    l.seg_len = want > SEG_MIN ? want : SEG_MIN;
+    const int64_t long_max = (T + C * l.seg_len - 1) / (C * l.seg_len);
+    l.q1b = (ct + long_max) / l.seg_len + 1;  // > sum over sequences of (segments - 1)
+    l.zb = l.q1b + long_max;                   // >= segments of the sequences cut
+    l.c2b = long_max;                          // >= sequences cut in three or more
     l.off_gam = align256(l.ntask * REC * 2);
     l.off_plan = l.off_gam + align256(l.ntask * D * 4);
-    l.off_xs = l.off_fs = 0;
-    l.bytes = l.off_plan + static_cast<int64_t>(varlen_plan_bytes(N, T, C));
+    l.off_seg = l.off_plan + static_cast<int64_t>(varlen_plan_bytes(N, T, C));
+    l.off_xs = l.off_seg + 4 * align256((N + 1) * 4);
+    l.off_fs = l.off_xs + align256(l.zb * H * D * D * 4);
+    l.bytes = l.off_fs + align256(l.zb * H * D * D * 4);
     return l;
 }
 
@@ -1057,6 +1183,12 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
     w.vseq = nullptr;
     w.vpfx = nullptr;
     w.vtab = nullptr;
+    ScanPlan sp;
+    sp.nseg = static_cast<int>(l.nseg);
+    sp.seg_len = static_cast<int>(l.seg_len);
+    sp.xs = l.nseg > 1 ? reinterpret_cast<float *>(p + l.off_xs) : nullptr;
+    sp.fs = l.nseg > 1 ? reinterpret_cast<float *>(p + l.off_fs) : nullptr;
+    sp.qs = sp.q1 = sp.zs = sp.c2 = nullptr;
     if (a.cu) {
         VarPlan vp;
         hipError_t e = launch_varlen_plan(a.cu, a.B, a.T, C, p + l.off_plan, &vp, s);
@@ -1064,12 +1196,20 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
         w.vseq = vp.seq;
         w.vpfx = vp.pfx;
         w.vtab = vp.tab;
+        const int64_t stride = align256((a.B + 1) * 4);
+        int *qs = reinterpret_cast<int *>(p + l.off_seg), *q1 = reinterpret_cast<int *>(p + l.off_seg + stride);
+        int *zs = reinterpret_cast<int *>(p + l.off_seg + 2 * stride), *c2 = reinterpret_cast<int *>(p + l.off_seg + 3 * stride);
+        hipLaunchKernelGGL(varlen_segment_kernel, dim3(1), dim3(SP_NTH), 0, s, vp.pfx, static_cast<int>(a.B),
+                           static_cast<int>(l.seg_len), static_cast<int>(l.q1b), static_cast<int>(l.zb),
+                           static_cast<int>(l.c2b), qs, q1, zs, c2);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        sp.qs = qs;
+        sp.q1 = q1;
+        sp.zs = zs;
+        sp.c2 = c2;
+        sp.xs = reinterpret_cast<float *>(p + l.off_xs);
+        sp.fs = reinterpret_cast<float *>(p + l.off_fs);
     }
-    ScanPlan sp;
-    sp.nseg = static_cast<int>(l.nseg);
-    sp.seg_len = static_cast<int>(l.seg_len);
-    sp.xs = l.nseg > 1 ? reinterpret_cast<float *>(p + l.off_xs) : nullptr;
-    sp.fs = l.nseg > 1 ? reinterpret_cast<float *>(p + l.off_fs) : nullptr;
     const int nc = static_cast<int>(l.nc);
     const int64_t g1 = l.ntask < cu_count() ? l.ntask : cu_count();
     if (a.gate_logits || a.qk_norm)
@@ -1078,6 +1218,20 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
         hipLaunchKernelGGL((chunk_prep_kernel<TIED, KEYG, VW, false>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s, a, w, nc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.cu) {  // packed: the units are bounded on the host, counted on the device
+        const int64_t u1 = a.H * l.q1b, uc = a.H * l.c2b, u0 = a.H * (a.B + l.q1b);
+        hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG, VW, 1>), dim3(static_cast<unsigned>(u1 * 2)),
+                           dim3(scan_threads(1)), 0, s, a, w, nc, sp, u1 % 8 == 0 ? 1 : 0);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (uc > 0) {
+            hipLaunchKernelGGL(segment_combine_kernel, dim3(static_cast<unsigned>(uc * (D / CMB_COLS))), dim3(CMB_NTH), 0,
+                               s, sp.xs, sp.fs, 0, sp, static_cast<int>(a.B), static_cast<int>(a.H));
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG, VW, 0>), dim3(static_cast<unsigned>(u0 * 2)),
+                           dim3(scan_threads(0)), 0, s, a, w, nc, sp, u0 % 8 == 0 ? 1 : 0);
+        return hipGetLastError();
+    }
     if (l.nseg > 1) {
         const int64_t units = l.chains * (l.nseg - 1);
         hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG, VW, 1>), dim3(static_cast<unsigned>(units * 2)),
@@ -1085,7 +1239,7 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (l.nseg > 2) {
             hipLaunchKernelGGL(segment_combine_kernel, dim3(static_cast<unsigned>(l.chains * (D / CMB_COLS))),
-                               dim3(CMB_NTH), 0, s, sp.xs, sp.fs, sp.nseg);
+                               dim3(CMB_NTH), 0, s, sp.xs, sp.fs, sp.nseg, sp, 0, static_cast<int>(a.H));
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
     }

@@ -293,12 +293,20 @@ def fwd_varlen(lib, desc, cu=CU, q=Q, k=K, v=V, la=LA, eb=EB, wr=WR, s0=S0, o=O,
 
 def varlen_bytes(N, H, T):
     """Records and chunk-end decays for ceil(T/64) + N chunks per head (each
-    sequence may end in a partial chunk), then the plan: N token ranges
-    (int32 pairs), N+1 chunk prefix counts, one int32 pair per chunk."""
+    sequence may end in a partial chunk); the plan: N token ranges (int32
+    pairs), N+1 chunk prefix counts, one int32 pair per chunk; four N+1
+    segment prefix counts; X and F slots for the segments of the sequences
+    cut (segments of L chunks, L = max(16, ceil(H ceil(T/64) / 128)), at most
+    ceil(T / 64 L) sequences cut), each a fp32 state per head."""
     a = lambda x: (x + 255) // 256 * 256
-    nc = (T + 63) // 64 + N
+    ct = (T + 63) // 64
+    nc = ct + N
     n = H * nc
-    return a(n * 98304) + a(n * 512) + a(N * 8) + a((N + 1) * 4) + a(nc * 8)
+    L = max(16, -(-H * ct // 128))
+    long_max = -(-T // (64 * L))
+    zb = (ct + long_max) // L + 1 + long_max
+    return (a(n * 98304) + a(n * 512) + a(N * 8) + a((N + 1) * 4) + a(nc * 8) + 4 * a((N + 1) * 4)
+            + 2 * a(zb * H * 128 * 128 * 4))
 
 
 def query_varlen(lib, d):

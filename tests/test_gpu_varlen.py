@@ -156,6 +156,26 @@ def test_exact_chunks():
     _check(inp, TOL_BF16, pairs=[(0, None), (2, None)])
 
 
+@pytest.mark.parametrize("lengths", [[20000, 300, 1000], [1000, 9000, 0, 6000]])
+def test_long_sequences_segmented(lengths):
+    # sequences of more than L chunks (L = 16 here) are scanned in segments
+    # (summaries, then the combine for three or more, then the scan from each
+    # segment's entry state); the others in one piece
+    w = W[2].scaled(H=2)
+    inp = synth.make_packed_inputs(w, lengths, seed=sum(lengths) % 1000)
+    _check(inp, TOL_BF16)
+
+
+def test_segmented_exact_chunks():
+    # a long sequence entering with a state beyond the fp16 range: its first
+    # segment's chunks run as the exact fp32 recurrence
+    w = W[2].scaled(H=1)
+    inp = synth.make_packed_inputs(w, [200, 3000, 64], seed=995)
+    inp["S0"][1] *= 3.0e5
+    _check(inp, (1e-4, TOL_BF16), pairs=[(1, None)])
+    _check(inp, TOL_BF16, pairs=[(0, None), (2, None)])
+
+
 def test_full_size_equal_lengths_match_batched():
     # 8 sequences of 4096 tokens, 16 heads: the packed call runs the same
     # chunks as the batched one through the same kernels (bit-exact)

@@ -300,8 +300,10 @@ def roofline_hbm(bytes_alg, ms, traffic=None):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    # the first dozen calls after an idle period run up to a quarter slower
+    # while the GPU's clocks settle; the default warmup covers that
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-extra", action="store_true", help="time only the main workload")

@@ -352,8 +352,13 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         f4 khf[RPS], qhf[RPS], egm;
         factored_operands<PrepSmem, TIED, KEYG, 2, VW>(S, R, g, khf, qhf, egm, seg, cq, a.q_scale, logits, qknorm);
         const int64_t next = task + gridDim.x;  // prefetched in four parts below
-        const TaskPos pn = task_pos(a, w, next < ntask ? next : task, nc);
-        if (next < ntask) load_part<0, TIED, KEYG, VW, RAW>(R, a, pn, tid);
+        TaskPos pn = task_pos(a, w, next < ntask ? next : task, nc);
+        // Without a next task the loads still issue, over an empty range (they
+        // read zeros and touch no memory): every path through the loop then
+        // has the same memory operations in flight, so the waits before the
+        // first use of each part count only what was issued after it.
+        if (next >= ntask) pn.tlim = pn.t0;
+        load_part<0, TIED, KEYG, VW, RAW>(R, a, pn, tid);
         __syncthreads();
 
         const bool wide = S.wide != 0;  // read by all before any later write
@@ -381,9 +386,13 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 *reinterpret_cast<h4 *>(&S.qh[r * KP + 4 * cq]) = to_h4(qhf[i] * egm);
             }
         }
-        if (next < ntask) load_part<1, TIED, KEYG, VW, RAW>(R, a, pn, tid);
+        load_part<1, TIED, KEYG, VW, RAW>(R, a, pn, tid);
 
         _Float16 *rec = w.frag + task * REC;
+        bool big = false;
+        const int ct = wv, it = wv;  // value tile, key channel tile of this wave
+        h8 vb[2], ef[2], uf[2];
+        f4 uacc[4];
         if (!wide) {
             // ---- Tm = (I + A)^-1 (diagonal blocks were inverted with the Grams)
             solve_offdiag(S, wv, lr, lg);
@@ -391,11 +400,9 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             // entry that overflowed is inf and turns every product it enters
             // into inf or NaN.  All LDS reads of this phase come before its
             // LDS writes, so the compiler may issue them early.
-            bool big = false;
 
             // ---- (1) value tile ct = wv: Y = Bm V, U = Tm Y ------------------
-            const int ct = wv;
-            h8 vb[2];  // V[:, ct] as a B operand, natural token order
+            // vb: V[:, ct] as a B operand, natural token order
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) vb[ks] = *reinterpret_cast<const h8 *>(&S.v16[(16 * ct + lr) * SP + 32 * ks + 8 * lg]);
             f4 y[4];
@@ -407,7 +414,6 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                     y[rt] = mfma32(*reinterpret_cast<const h8 *>(&S.b16[(16 * rt + lr) * SP + 32 * ks + 8 * lg]), vb[ks], y[rt]);
                 big |= out_of_range(y[rt]);
             }
-            f4 uacc[4];
             {
                 const h8 yb0 = join(to_h4(y[0]), to_h4(y[1])), yb1 = join(to_h4(y[2]), to_h4(y[3]));
 #pragma unroll
@@ -426,8 +432,6 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
 
             // ---- (3) key channel tile it = wv: Etil^T, Util^T fragments
             //      (chunk-end reference: column operand times 2^(gC - gm_j))
-            const int it = wv;
-            h8 ef[2], uf[2];
             {
                 const int c = 16 * it + lr;
 #pragma unroll
@@ -452,9 +456,10 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             for (int rt = 0; rt < 4; ++rt)
                 *reinterpret_cast<h4 *>(&S.u16[(16 * ct + lr) * SP + 16 * rt + 4 * lg]) = to_h4(uacc[rt]);
             if (big) S.wide = 1;
-            __syncthreads();  // U complete in u16
-            if (next < ntask) load_part<2, TIED, KEYG, VW, RAW>(R, a, pn, tid);
-
+        }
+        __syncthreads();  // U complete in u16
+        load_part<2, TIED, KEYG, VW, RAW>(R, a, pn, tid);
+        if (!wide) {
             // ---- (4) Oe^T[ct, :] = V^T P^T - U^T R^T -> HBM (transposed, so
             //      the scan's output tiles hold adjacent columns per lane)
             {
@@ -496,10 +501,8 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 }
             }
             if (big) S.wide = 1;
-        } else if (next < ntask) {
-            load_part<2, TIED, KEYG, VW, RAW>(R, a, pn, tid);
         }
-        if (next < ntask) load_part<3, TIED, KEYG, VW, RAW>(R, a, pn, tid);
+        load_part<3, TIED, KEYG, VW, RAW>(R, a, pn, tid);
         __syncthreads();
         // e^gC per key channel; a chunk to be run exactly is marked by -1 in
         // channel 0 (e^gC is never negative)

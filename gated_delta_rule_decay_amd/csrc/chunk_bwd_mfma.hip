@@ -140,13 +140,46 @@ __device__ __forceinline__ int64_t btask_count(const ChunkArgs &f, const VarPlan
 // ---------------------------------------------------------------------------
 // the record pass
 
-constexpr int KS = BD + 1;  // odd row stride: the Gram loops read one channel of different rows
+constexpr int KS = BD + 1;  // odd row stride: loops that read one channel of different rows
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr int QP = BC + 1;  // quads per channel-quad column in LDS (one pad: the quad writes hit distinct banks)
+
+// Four consecutive channels c0..c0+3 of a q/k/v row (bf16 or fp32), one load.
+__device__ __forceinline__ f4 load_qkv4(const void *p, int64_t i, int bf16) {
+    if (bf16) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + i);
+        return f4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                  __uint_as_float(u.y & 0xffff0000u)};
+    }
+    return *reinterpret_cast<const f4 *>(static_cast<const float *>(p) + i);
+}
+
+// The gate of channels c0..c0+3 of token-head `row` (one value per token-head
+// broadcast when the gate is not per channel).
+__device__ __forceinline__ f4 load_gate4(const float *g, int per_key, int64_t row, int c0) {
+    if (per_key) return *reinterpret_cast<const f4 *>(g + row * BD + c0);
+    const float x = g[row];
+    return f4{x, x, x, x};
+}
+
+__device__ __forceinline__ f4 exp2_4(f4 x) {
+    return f4{__builtin_amdgcn_exp2f(x[0]), __builtin_amdgcn_exp2f(x[1]), __builtin_amdgcn_exp2f(x[2]),
+              __builtin_amdgcn_exp2f(x[3])};
+}
+
+// LDS of the record pass: the chunk's operands channel-quad-major,
+// [channel / 4][row][4 channels] (row BC is padding), so that a Gram thread
+// reads four channels of a row in one 16-byte access; the running log2-decay
+// in G.
+struct RecLds {
+    f4 K[32 * QP], Q[32 * QP], G[32 * QP], E[32 * QP], U[32 * QP];
+    float A[BC * BC];
+};
 
 __global__ void __launch_bounds__(BNT) bwd_record_kernel(BwdArgs a, VarPlan vp, float *rec, int nch) {
-    __shared__ float K[BC * KS], Q[BC * KS], G[BC * KS], E[BC * KS], U[BC * KS];
-    __shared__ float A[BC * BC], Tm[BC * BC], gC[BD];
+    __shared__ RecLds L;
     const ChunkArgs &f = a.f;
-    const int64_t T = f.T, H = f.H;
+    const int64_t H = f.H;
     const int64_t ntask = btask_count(f, vp, nch);
     const int tid = threadIdx.x;
     for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
@@ -154,82 +187,93 @@ __global__ void __launch_bounds__(BNT) bwd_record_kernel(BwdArgs a, VarPlan vp, 
         const int64_t h = tp.h;
         float *out = rec + task * REC_BWD;
         __syncthreads();  // the previous task is done with LDS
-        for (int idx = tid; idx < BC * BD; idx += BNT) {
-            const int r = idx / BD, c = idx % BD;
-            float kv = 0.f, qv = 0.f, la = 0.f, e = 0.f, u = 0.f;
+        // ---- operands: thread = channel quad c4 of rows r (two quads each)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int qd = tid + BNT * p, r = qd / 32, c4 = qd % 32;
+            f4 kv = {0.f, 0.f, 0.f, 0.f}, qv = kv, la = kv, e = kv, u = kv;
             if (tp.tok0 + r < tp.tlim) {
                 const int64_t row = (tp.tok0 + r) * H + h;
-                kv = load_qkv(f.k, row * BD + c, f.bf16);
-                qv = f.q_scale * load_qkv(f.q, row * BD + c, f.bf16);
-                la = load_gate(f.la, f.la_key, row, BD, c);
-                const float bb = load_gate(f.eb, f.eb_key, row, BD, c);
+                kv = load_qkv4(f.k, row * BD + 4 * c4, f.bf16);
+                qv = f.q_scale * load_qkv4(f.q, row * BD + 4 * c4, f.bf16);
+                la = LOG2E * load_gate4(f.la, f.la_key, row, 4 * c4);
+                const f4 bb = load_gate4(f.eb, f.eb_key, row, 4 * c4);
                 if (f.value_write) {  // read along b k, erase and write along k
                     e = u = kv;
                     kv *= bb;
                 } else {
-                    const float ww = f.wr ? load_gate(f.wr, f.wr_key, row, BD, c) : bb;
+                    const f4 ww = f.wr ? load_gate4(f.wr, f.wr_key, row, 4 * c4) : bb;
                     e = bb * kv;
                     u = ww * kv;
                 }
             }
-            const int li = r * KS + c;
-            K[li] = kv; Q[li] = qv; G[li] = la; E[li] = e; U[li] = u;
+            const int li = c4 * QP + r;
+            L.K[li] = kv; L.Q[li] = qv; L.G[li] = la; L.E[li] = e; L.U[li] = u;
         }
         __syncthreads();
-        if (tid < BD) {  // running log-decay per channel (padded rows add 0)
+        if (tid < BD) {  // running log2-decay per channel (padded rows add 0)
+            float *g = reinterpret_cast<float *>(L.G) + (tid / 4) * QP * 4 + (tid % 4);
             float run = 0.f;
+#pragma unroll
             for (int r = 0; r < BC; ++r) {
-                run += G[r * KS + tid];
-                G[r * KS + tid] = run;
+                run += g[4 * r];
+                g[4 * r] = run;
             }
-            gC[tid] = run;
-            out[R_GM + tid] = expf(run);
+            out[R_GM + tid] = __builtin_amdgcn_exp2f(run);
         }
         __syncthreads();
-        {  // the four Grams, one (r, s) pair per thread, pairwise decays formed directly
+        {  // the four Grams, one (r, s) pair per thread, pairwise decays
+           // 2^(g_r - g_s) <= 1 formed directly
             const int r = tid / BC, s = tid % BC;
             float sa = 0.f, sb = 0.f, sr = 0.f, sp = 0.f;
             if (s <= r) {
-                for (int c = 0; c < BD; ++c) {
-                    const float d = expf(G[r * KS + c] - G[s * KS + c]);
-                    const float kd = K[r * KS + c] * d, qd = Q[r * KS + c] * d;
-                    const float e = E[s * KS + c], u = U[s * KS + c];
-                    sa += kd * e;
-                    sb += kd * u;
-                    sr += qd * e;
-                    sp += qd * u;
+#pragma unroll 4
+                for (int c4 = 0; c4 < 32; ++c4) {
+                    const int lr = c4 * QP + r, ls = c4 * QP + s;
+                    const f4 d = exp2_4(L.G[lr] - L.G[ls]);
+                    const f4 kd = L.K[lr] * d, qd = L.Q[lr] * d;
+                    const f4 e = L.E[ls], u = L.U[ls];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        sa += kd[i] * e[i];
+                        sb += kd[i] * u[i];
+                        sr += qd[i] * e[i];
+                        sp += qd[i] * u[i];
+                    }
                 }
             }
-            A[tid] = s < r ? sa : 0.f;
+            L.A[tid] = s < r ? sa : 0.f;
             out[R_BM + tid] = s < r ? sb : 0.f;
             out[R_RR + tid] = sr;
             out[R_PP + tid] = sp;
         }
         __syncthreads();
-        // Tm = (I + A)^-1 by forward substitution, a column per thread; the
-        // others fold the decays into the operands meanwhile
         if (tid < BC) {
+            // Tm = (I + A)^-1 by forward substitution, column j = tid in
+            // registers: Tm[r][j] = -sum_{j <= s < r} A[r][s] Tm[s][j]
             const int j = tid;
+            float t[BC];
+#pragma unroll
             for (int r = 0; r < BC; ++r) {
-                float val = r < j ? 0.f : 1.f;
-                if (r > j) {
-                    float acc = 0.f;
-                    for (int s = j; s < r; ++s) acc += A[r * BC + s] * Tm[s * BC + j];
-                    val = -acc;
-                }
-                Tm[r * BC + j] = val;
+                float acc = 0.f;
+#pragma unroll
+                for (int s2 = 0; s2 < r; ++s2) acc += L.A[r * BC + s2] * t[s2];
+                t[r] = r < j ? 0.f : (r == j ? 1.f : -acc);
+                out[R_TM + r * BC + j] = t[r];
             }
         }
-        for (int idx = tid; idx < BC * BD; idx += BNT) {
-            const int r = idx / BD, c = idx % BD, li = r * KS + c;
-            const float eg = expf(G[li]), ec = expf(gC[c] - G[li]);
-            out[R_KB + idx] = K[li] * eg;
-            out[R_QB + idx] = Q[li] * eg;
-            out[R_ET + idx] = E[li] * ec;
-            out[R_UT + idx] = U[li] * ec;
+        // the decays folded into the operands (two quads per thread)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int qd = tid + BNT * p, r = qd / 32, c4 = qd % 32, li = c4 * QP + r;
+            const f4 g = L.G[li], gc = L.G[c4 * QP + BC - 1];
+            const f4 eg = exp2_4(g), ec = exp2_4(gc - g);
+            const int o = r * BD + 4 * c4;
+            *reinterpret_cast<f4 *>(out + R_KB + o) = L.K[li] * eg;
+            *reinterpret_cast<f4 *>(out + R_QB + o) = L.Q[li] * eg;
+            *reinterpret_cast<f4 *>(out + R_ET + o) = L.E[li] * ec;
+            *reinterpret_cast<f4 *>(out + R_UT + o) = L.U[li] * ec;
         }
-        __syncthreads();
-        out[R_TM + tid] = Tm[tid];
     }
 }
 
@@ -278,27 +322,56 @@ __device__ __forceinline__ void stage_store(const Staged &st, ScanLds &L, int ti
     if (tid < BD) L.gm[tid] = st.g;
 }
 
-// Four values of a [B*T*H, 128] row-major tensor for lane (kq, n): rows
-// (tokens) 4 kq + j of the chunk, column col; zero past T.
-__device__ __forceinline__ void load_rows4(float (&x)[4], const void *p, int bf16, int64_t h, int64_t tok0,
-                                           int64_t tlim, int kq, int col, const ChunkArgs &f) {
+// Buffer resource over rows tok0 .. tlim-1 (at most one chunk) of head h of
+// a [tokens, H, width] tensor with elements of es bytes: the hardware returns
+// zero for rows past tlim, so loads through it need no select (and no wait).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void *p, int64_t H, int64_t h, int64_t tok0,
+                                                           int64_t tlim, int width, int es) {
+    const int64_t n = tlim - tok0 < BC ? (tlim - tok0 > 0 ? tlim - tok0 : 0) : BC;
+    const char *base = static_cast<const char *>(p) + (tok0 * H + h) * width * es;
+    const int bytes = n > 0 ? static_cast<int>(((n - 1) * H * width + width) * es) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, bytes, 0x00020000);
+}
+
+// The raw words of lane (kq, n)'s rows 4 kq + j of a chunk at column col of a
+// [tokens, H, 128] tensor (bf16 bits in the low half, or fp32 bits), zero
+// past tlim; with the value-write form also the write gate of those rows
+// (fp32 bits).  Nothing is converted here, so prefetched loads stay in flight
+// until raw_rows4 uses them.
+struct RawRows {
+    uint32_t x[4], w[4];
+};
+
+__device__ __forceinline__ void load_rows_raw(uint32_t (&x)[4], const void *p, int bf16, int64_t H, int64_t h,
+                                              int64_t tok0, int64_t tlim, int kq, int col) {
+    const int es = bf16 ? 2 : 4;
+    const auto rs = rows_rsrc(p, H, h, tok0, tlim, BD, es);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const int64_t t = tok0 + 4 * kq + j;
-        x[j] = t < tlim ? load_qkv(p, (t * f.H + h) * BD + col, bf16) : 0.f;
+        const int off = static_cast<int>(((4 * kq + j) * H * BD + col) * es);
+        x[j] = bf16 ? static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0))
+                    : __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
     }
 }
 
-// The values of lane (kq, n)'s rows, times the write gate in the value-write form.
-__device__ __forceinline__ void load_vals4(float (&x)[4], int64_t h, int64_t tok0, int64_t tlim, int kq, int col,
-                                           const ChunkArgs &f) {
-    load_rows4(x, f.v, f.bf16, h, tok0, tlim, kq, col, f);
+__device__ __forceinline__ void load_vals_raw(RawRows &r, int64_t tok0, int64_t tlim, int64_t h, int kq, int col,
+                                              const ChunkArgs &f) {
+    load_rows_raw(r.x, f.v, f.bf16, f.H, h, tok0, tlim, kq, col);
     if (f.value_write) {
+        const int gw = f.wr_key ? BD : 1;
+        const auto rs = rows_rsrc(f.wr, f.H, h, tok0, tlim, gw, 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t t = tok0 + 4 * kq + j;
-            if (t < tlim) x[j] *= load_gate(f.wr, f.wr_key, t * f.H + h, BD, col);
-        }
+        for (int j = 0; j < 4; ++j)
+            r.w[j] = __builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<int>(((4 * kq + j) * f.H * gw + (f.wr_key ? col : 0)) * 4), 0, 0);
+    }
+}
+
+// The four values of raw rows, times the write gate in the value-write form.
+__device__ __forceinline__ void raw_rows4(float (&v)[4], const RawRows &r, int bf16, int vw) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[j] = bf16 ? __uint_as_float(r.x[j] << 16) : __uint_as_float(r.x[j]);
+        if (vw) v[j] *= __uint_as_float(r.w[j]);
     }
 }
 
@@ -332,21 +405,24 @@ __global__ void __launch_bounds__(BNT) bwd_state_kernel(BwdArgs a, VarPlan vp, c
 
     // m0 = Kbar, m1 = Etil, m2 = Util; t0 = Tm, t1 = Bm
     Staged st;
-    float vn[4];
+    RawRows vn;
+    float v[4];
     if (ch.nc > 0) {
         stage_load(st, rc(0), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
-        load_vals4(vn, h, ch.tbase, ch.tlim, kq, col, f);
+        load_vals_raw(vn, ch.tbase, ch.tlim, h, kq, col, f);
+        stage_store(st, L, tid);
+        raw_rows4(v, vn, f.bf16, f.value_write);
     }
     for (int n = 0; n < ch.nc; ++n) {
-        __syncthreads();  // every wave done with the previous chunk's LDS copy
-        stage_store(st, L, tid);
-        float v[4] = {vn[0], vn[1], vn[2], vn[3]};
+        // the next chunk's loads go out before this chunk's state stores, so
+        // that waiting for them (after this chunk's products) never waits
+        // for the stores
         if (n + 1 < ch.nc) {
             stage_load(st, rc(n + 1), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
-            load_vals4(vn, h, ch.tbase + (n + 1) * BC, ch.tlim, kq, col, f);
+            load_vals_raw(vn, ch.tbase + (n + 1) * BC, ch.tlim, h, kq, col, f);
         }
         put_state(hs(n), S, kq, col);
-        __syncthreads();
+        __syncthreads();  // chunk n's LDS copy complete
         // X = Kbar S + Bm V (token rows)
         f4 X = chan_product(L.m0, S, m, kq, f4{0.f, 0.f, 0.f, 0.f});
         {
@@ -372,6 +448,11 @@ __global__ void __launch_bounds__(BNT) bwd_state_kernel(BwdArgs a, VarPlan vp, c
                 s = mfma4(-L.m1[(4 * kq + j) * RS + 16 * it + m], M[j], s);
             }
             S[it] = s;
+        }
+        __syncthreads();  // every wave done with chunk n's LDS copy
+        if (n + 1 < ch.nc) {
+            stage_store(st, L, tid);
+            raw_rows4(v, vn, f.bf16, f.value_write);
         }
     }
 }
@@ -399,22 +480,23 @@ __global__ void __launch_bounds__(BNT) bwd_dgrad_kernel(BwdArgs a, VarPlan vp, c
 
     // m0 = Etil, m1 = Qbar, m2 = Kbar; t0 = Tm, t1 = R
     Staged st;
-    float on[4];
+    RawRows on;
+    float o[4];
     const int nl = ch.nc - 1;
     if (nl >= 0) {
         stage_load(st, rc(nl), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
-        load_rows4(on, a.d_o, 0, h, ch.tbase + static_cast<int64_t>(nl) * BC, ch.tlim, kq, col, f);
+        load_rows_raw(on.x, a.d_o, 0, f.H, h, ch.tbase + static_cast<int64_t>(nl) * BC, ch.tlim, kq, col);
+        stage_store(st, L, tid);
+        raw_rows4(o, on, 0, 0);
     }
     for (int n = nl; n >= 0; --n) {
-        __syncthreads();
-        stage_store(st, L, tid);
-        float o[4] = {on[0], on[1], on[2], on[3]};
+        // loads of the chunk before go out ahead of this chunk's stores
         if (n > 0) {
             stage_load(st, rc(n - 1), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
-            load_rows4(on, a.d_o, 0, h, ch.tbase + static_cast<int64_t>(n - 1) * BC, ch.tlim, kq, col, f);
+            load_rows_raw(on.x, a.d_o, 0, f.H, h, ch.tbase + static_cast<int64_t>(n - 1) * BC, ch.tlim, kq, col);
         }
         put_state(hs(n), dS, kq, col);
-        __syncthreads();
+        __syncthreads();  // chunk n's LDS copy complete
         // dM = -(Etil dSo + R^T dO)  (token rows)
         f4 dM = chan_product(L.m0, dS, m, kq, f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -435,6 +517,11 @@ __global__ void __launch_bounds__(BNT) bwd_dgrad_kernel(BwdArgs a, VarPlan vp, c
                 s = mfma4(L.m2[(4 * kq + j) * RS + 16 * it + m], Y[j], s);
             }
             dS[it] = s;
+        }
+        __syncthreads();  // every wave done with chunk n's LDS copy
+        if (n > 0) {
+            stage_store(st, L, tid);
+            raw_rows4(o, on, 0, 0);
         }
     }
     if (a.ds0) put_state(a.ds0 + bh * BD * BD, dS, kq, col);
@@ -549,37 +636,68 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
 
         const int vcol = 16 * wv + m;
 
-        // ---- the chunk's record, raw operands, V and dO
-        for (int qi = tid; qi < 3 * 512; qi += GNT) {
-            const int part = qi / 512, qq = qi % 512, row = qq / 32, col = 4 * (qq % 32);
-            const f4 x = *reinterpret_cast<const f4 *>(rc + (part == 0 ? R_KB : part == 1 ? R_ET : R_UT) + 4 * qq);
-            *reinterpret_cast<f4 *>(&(part == 0 ? L.kb : part == 1 ? L.et : L.ut)[row * RS + col]) = x;
-        }
-        if (tid < 256) {  // Tm, Bm, R, P: consecutive in the record
-            const int part = tid / 64, qq = tid % 64;
-            const f4 x = *reinterpret_cast<const f4 *>(rc + R_TM + 256 * part + 4 * qq);
-            float *dst = part == 0 ? L.tm : part == 1 ? L.bm : part == 2 ? L.rr : L.pp;
-            *reinterpret_cast<f4 *>(&dst[4 * qq]) = x;
-        } else if (tid < 256 + BD) {
-            L.gm[tid - 256] = rc[R_GM + tid - 256];
-        }
+        // ---- the chunk's record, raw operands, V and dO.  Every load is issued
+        //      before any is used (rows past the sequence end read as zero
+        //      through the buffer range; bf16 / fp32 and per-channel / per-head
+        //      operands differ only in offsets), then converted into LDS.
+        f4 xr[3], xt;
+        float xg;
+#pragma unroll
+        for (int p = 0; p < 3; ++p)  // Kbar, Etil, Util: quad tid of each
+            xr[p] = *reinterpret_cast<const f4 *>(rc + (p == 0 ? R_KB : p == 1 ? R_ET : R_UT) + 4 * tid);
+        if (tid < 256)  // Tm, Bm, R, P: consecutive in the record
+            xt = *reinterpret_cast<const f4 *>(rc + R_TM + 4 * tid);
+        else if (tid < 256 + BD)
+            xg = rc[R_GM + tid - 256];
         f4 bb, ww;  // erase / write gates of token tid / 32, channels c4 .. c4 + 3 (for the last phase)
-        {  // token r = tid / 32, channels c4 .. c4 + 3
-            const int r = tid >> 5, c4 = 4 * (tid & 31);
-            const f4 z = {0.f, 0.f, 0.f, 0.f};
-            f4 kv = z, qv = z, la = z, vv = z, ov = z;
-            bb = z;
-            ww = z;
-            if (live(r)) {
-                const int64_t row = row_of(r);
-                kv = load4_qkv(f.k, row * BD + c4, f.bf16);
-                qv = f.q_scale * load4_qkv(f.q, row * BD + c4, f.bf16);
-                la = load4_gate(f.la, la_key, row, c4);
-                bb = load4_gate(f.eb, eb_key, row, c4);
-                ww = tied ? bb : load4_gate(f.wr, wr_key, row, c4);  // value-write: per value column
-                vv = load4_qkv(f.v, row * BD + c4, f.bf16);
-                ov = *reinterpret_cast<const f4 *>(a.d_o + row * BD + c4);
+        const int r = tid >> 5, c4 = 4 * (tid & 31);
+        {
+            const int es = f.bf16 ? 2 : 4;
+            // dword j of my four channels: bf16 takes two words, fp32 four
+            auto qoff = [&](int j) { return static_cast<int>((r * H * BD + c4) * es + 4 * (f.bf16 ? (j < 1 ? j : 1) : j)); };
+            auto goff = [&](int key, int j) { return static_cast<int>(key ? (r * H * BD + c4 + j) * 4 : r * H * 4); };
+            const auto rk = rows_rsrc(f.k, H, h, tp.tok0, tp.tlim, BD, es);
+            const auto rq = rows_rsrc(f.q, H, h, tp.tok0, tp.tlim, BD, es);
+            const auto rv = rows_rsrc(f.v, H, h, tp.tok0, tp.tlim, BD, es);
+            const auto ro = rows_rsrc(a.d_o, H, h, tp.tok0, tp.tlim, BD, 4);
+            const auto rla = rows_rsrc(f.la, H, h, tp.tok0, tp.tlim, la_key ? BD : 1, 4);
+            const auto reb = rows_rsrc(f.eb, H, h, tp.tok0, tp.tlim, eb_key ? BD : 1, 4);
+            const auto rwr = rows_rsrc(tied ? f.eb : f.wr, H, h, tp.tok0, tp.tlim, (tied ? eb_key : wr_key) ? BD : 1, 4);
+            const int wkey = tied ? eb_key : wr_key;
+            uint32_t kw[4], qw[4], vw4[4], lw[4], bw[4], ww4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                kw[j] = __builtin_amdgcn_raw_buffer_load_b32(rk, qoff(j), 0, 0);
+                qw[j] = __builtin_amdgcn_raw_buffer_load_b32(rq, qoff(j), 0, 0);
+                lw[j] = __builtin_amdgcn_raw_buffer_load_b32(rla, goff(la_key, j), 0, 0);
+                bw[j] = __builtin_amdgcn_raw_buffer_load_b32(reb, goff(eb_key, j), 0, 0);
+                ww4[j] = __builtin_amdgcn_raw_buffer_load_b32(rwr, goff(wkey, j), 0, 0);
+                vw4[j] = __builtin_amdgcn_raw_buffer_load_b32(rv, qoff(j), 0, 0);
             }
+            const f4 ov = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(ro, (r * H * BD + c4) * 4, 0, 0));
+            auto qkv = [&](const uint32_t (&w)[4]) {
+                return f.bf16 ? f4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                                   __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)}
+                              : f4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
+                                   __uint_as_float(w[3])};
+            };
+            auto gate = [&](const uint32_t (&w)[4]) {
+                return f4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3])};
+            };
+            // the record parts into LDS
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+                *reinterpret_cast<f4 *>(&(p == 0 ? L.kb : p == 1 ? L.et : L.ut)[(tid / 32) * RS + 4 * (tid % 32)]) = xr[p];
+            if (tid < 256) {
+                float *dst = tid < 64 ? L.tm : tid < 128 ? L.bm : tid < 192 ? L.rr : L.pp;
+                *reinterpret_cast<f4 *>(&dst[4 * (tid & 63)]) = xt;
+            } else if (tid < 256 + BD) {
+                L.gm[tid - 256] = xg;
+            }
+            const f4 kv = qkv(kw), qv = f.q_scale * qkv(qw), la = gate(lw);
+            f4 vv = qkv(vw4);
+            bb = gate(bw);
+            ww = gate(ww4);  // value-write: per value column
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int li = r * KS + c4 + i;
@@ -905,7 +1023,11 @@ hipError_t launch_bwd_d128(const BwdArgs &a, const VarPlan &vp, float *rec, floa
     const int64_t tasks = f.cu ? f.H * varlen_chunk_bound(f.B, f.T, BC) : f.B * f.H * nch;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    const int64_t g1 = tasks < 8 * cus ? tasks : 8 * cus;
+    // the record pass loops over tasks: as many workgroups as can be resident
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_record_kernel, BNT, 0) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    const int64_t g1 = tasks < int64_t(per_cu) * cus ? tasks : int64_t(per_cu) * cus;
     hipLaunchKernelGGL(bwd_record_kernel, dim3(static_cast<unsigned>(g1)), dim3(BNT), 0, s, a, vp, rec, nch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -799,10 +799,16 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
         {
             const float *srow = Sg + c * BD, *drow = dSg + c * BD;
             float dot = 0.f;
-#pragma unroll 2
+            // every row load goes out before the first product needs one
+            f4 sr[8], dr[8];
+#pragma unroll
             for (int jt = 0; jt < 8; ++jt) {
-                const f4 s4 = *reinterpret_cast<const f4 *>(srow + 16 * jt + 4 * kq);
-                const f4 d4 = *reinterpret_cast<const f4 *>(drow + 16 * jt + 4 * kq);
+                sr[jt] = *reinterpret_cast<const f4 *>(srow + 16 * jt + 4 * kq);
+                dr[jt] = *reinterpret_cast<const f4 *>(drow + 16 * jt + 4 * kq);
+            }
+#pragma unroll
+            for (int jt = 0; jt < 8; ++jt) {
+                const f4 s4 = sr[jt], d4 = dr[jt];
                 const int lo = m * RS + 16 * jt + 4 * kq;
                 const f4 am = *reinterpret_cast<const f4 *>(&L.dm[lo]), ao = *reinterpret_cast<const f4 *>(&L.o[lo]);
                 const f4 ax = *reinterpret_cast<const f4 *>(&L.mm[lo]), av = *reinterpret_cast<const f4 *>(&L.v[lo]);

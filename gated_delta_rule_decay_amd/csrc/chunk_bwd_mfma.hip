@@ -288,40 +288,6 @@ struct ScanLds {
     float gm[BD];
 };
 
-// Copy the parts [(src0, m0), (src1, m1), (src2, m2), (srcT0, t0), (srcT1, t1), gm]
-// of record `r`: every thread moves 8 + 8 + 8 + 1 + 1 (+ gm) floats as float4s.
-struct Staged {
-    f4 x[6];
-    f4 tt[2];
-    float g;
-};
-
-__device__ __forceinline__ void stage_load(Staged &st, const float *r, int o0, int o1, int o2, int oT0, int oT1,
-                                           int tid) {
-#pragma unroll
-    for (int p = 0; p < 6; ++p) {
-        const int part = p / 2, q = tid + BNT * (p % 2);  // float4 index 0..511 within a 16 x 128 part
-        const int off = part == 0 ? o0 : part == 1 ? o1 : o2;
-        st.x[p] = *reinterpret_cast<const f4 *>(r + off + 4 * q);
-    }
-    // the two 16 x 16 parts: 64 float4s each, threads 0..63 and 64..127
-    const int q = tid & 63;
-    st.tt[0] = *reinterpret_cast<const f4 *>(r + (tid < 64 ? oT0 : oT1) + 4 * q);
-    st.g = tid < BD ? r[R_GM + tid] : 0.f;
-}
-
-__device__ __forceinline__ void stage_store(const Staged &st, ScanLds &L, int tid) {
-#pragma unroll
-    for (int p = 0; p < 6; ++p) {
-        const int part = p / 2, q = tid + BNT * (p % 2);
-        const int row = q / 32, col = 4 * (q % 32);
-        float *m = part == 0 ? L.m0 : part == 1 ? L.m1 : L.m2;
-        *reinterpret_cast<f4 *>(&m[row * RS + col]) = st.x[p];
-    }
-    if (tid < 128) *reinterpret_cast<f4 *>(&(tid < 64 ? L.t0 : L.t1)[4 * (tid & 63)]) = st.tt[0];
-    if (tid < BD) L.gm[tid] = st.g;
-}
-
 // Buffer resource over rows tok0 .. tlim-1 (at most one chunk) of head h of
 // a [tokens, H, width] tensor with elements of es bytes: the hardware returns
 // zero for rows past tlim, so loads through it need no select (and no wait).
@@ -375,42 +341,112 @@ __device__ __forceinline__ void raw_rows4(float (&v)[4], const RawRows &r, int b
     }
 }
 
-// Store (or read) a wave's 128 x 16 state slice to/from a [128][128] matrix.
-__device__ __forceinline__ void put_state(float *dst, const f4 (&s)[8], int kq, int col) {
-#pragma unroll
-    for (int it = 0; it < 8; ++it)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dst[(16 * it + 4 * kq + i) * BD + col] = s[it][i];
-}
 
 // The state entering every chunk, hist[chain][chunk][128][128].
-__global__ void __launch_bounds__(BNT) bwd_state_kernel(BwdArgs a, VarPlan vp, const float *rec, float *hist,
+// The scans run 8 waves per workgroup: waves w and w + 4 share value tile
+// w % 4 (16 columns) and split the key channels, tiles 0..3 and 4..7, so two
+// waves per SIMD hide each other's latency.  A token-row product over the
+// channels (Kbar S, Etil dS) is summed from the two halves through LDS; the
+// small token products after it (Tm X, Tm^T dM) run in both waves of a pair.
+constexpr int SNT = 512;
+constexpr int VMCNT0 = (7 << 4) | (15 << 8);  // s_waitcnt: vector memory count 0, the others untouched
+
+// The record parts a scan reads, staged through registers (512 threads: one
+// float4 of each 16 x 128 part, one of the two 16 x 16 parts, one of e^gC).
+// Every thread loads (duplicates stay in bounds), so no loaded value passes
+// through a select and the loads can stay in flight.
+struct Staged8 {
+    f4 x[3];
+    f4 tt;
+    float g;
+};
+
+__device__ __forceinline__ void stage_load8(Staged8 &st, const float *r, int o0, int o1, int o2, int oT0, int oT1,
+                                            int tid) {
+#pragma unroll
+    for (int p = 0; p < 3; ++p) st.x[p] = *reinterpret_cast<const f4 *>(r + (p == 0 ? o0 : p == 1 ? o1 : o2) + 4 * tid);
+    st.tt = *reinterpret_cast<const f4 *>(r + ((tid & 64) ? oT1 : oT0) + 4 * (tid & 63));
+    st.g = r[R_GM + (tid & (BD - 1))];
+}
+
+__device__ __forceinline__ void stage_store8(const Staged8 &st, ScanLds &L, int tid) {
+    const int row = tid / 32, col = 4 * (tid % 32);
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+        *reinterpret_cast<f4 *>(&(p == 0 ? L.m0 : p == 1 ? L.m1 : L.m2)[row * RS + col]) = st.x[p];
+    if (tid < 128) *reinterpret_cast<f4 *>(&((tid & 64) ? L.t1 : L.t0)[4 * (tid & 63)]) = st.tt;
+    else if (tid < 128 + BD) L.gm[tid - 128] = st.g;
+}
+
+// sum_c A[m][c] B[c][n] over this wave's 64 key channels (tiles 4 kh + t),
+// A row m from LDS, B the state registers; four accumulation chains.
+__device__ __forceinline__ f4 chan_half(const float *A, const f4 (&B)[4], int m, int kq, int kh) {
+    const f4 z = {0.f, 0.f, 0.f, 0.f};
+    f4 acc[4] = {z, z, z, z};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const f4 a4 = *reinterpret_cast<const f4 *>(&A[m * RS + 16 * (4 * kh + t) + 4 * kq]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = mfma4(a4[i], B[t][i], acc[i]);
+    }
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+// Store a wave's half state slice (tiles 4 kh + t, 64 x 16) into a [128][128] matrix.
+__device__ __forceinline__ void put_half(float *dst, const f4 (&s)[4], int kq, int kh, int col) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(16 * (4 * kh + t) + 4 * kq + i) * BD + col] = s[t][i];
+}
+
+// Both halves of a token-row product: write mine, wait, add my partner's
+// (low half first in both waves, so the pair holds identical sums).
+__device__ __forceinline__ f4 pair_sum(f4 *xp, f4 mine, int wv, int lane, int kh) {
+    xp[wv * 64 + lane] = mine;
+    __syncthreads();
+    const f4 other = xp[(wv ^ 4) * 64 + lane];
+    return kh ? other + mine : mine + other;
+}
+
+struct ScanLds8 {
+    ScanLds r;
+    f4 xp[8 * 64];  // the waves' half products
+};
+
+// The state entering every chunk, hist[chain][chunk][128][128], from S0.
+__global__ void __launch_bounds__(SNT) bwd_state_kernel(BwdArgs a, VarPlan vp, const float *rec, float *hist,
                                                         int nch) {
-    __shared__ __attribute__((aligned(16))) ScanLds L;
+    __shared__ __attribute__((aligned(16))) ScanLds8 LL;
+    ScanLds &L = LL.r;
     const ChunkArgs &f = a.f;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int m = lane & 15, kq = lane >> 4;
+    const int m = lane & 15, kq = lane >> 4, kh = wv >> 2;
     const int64_t bh = blockIdx.x >> 1;
     const BChain ch = bchain(f, vp, bh, nch);
     const int64_t h = ch.h;
-    const int col = 64 * (blockIdx.x & 1) + 16 * wv + m;  // this lane's value column (as n)
+    const int col = 64 * (blockIdx.x & 1) + 16 * (wv & 3) + m;  // this lane's value column (as n)
     auto rc = [&](int n) { return rec + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(REC_BWD); };
     auto hs = [&](int n) { return hist + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(BD * BD); };
 
-    f4 S[8];
+    f4 S[4];  // key channel tiles 4 kh + t
 #pragma unroll
-    for (int it = 0; it < 8; ++it)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[it][i] = f.s0 ? f.s0[bh * BD * BD + (16 * it + 4 * kq + i) * BD + col] : 0.f;
+        for (int i = 0; i < 4; ++i)
+            S[t][i] = f.s0 ? f.s0[bh * BD * BD + (16 * (4 * kh + t) + 4 * kq + i) * BD + col] : 0.f;
+    // the initial state is complete before the loop: no wait inside the loop
+    // has to allow for its loads
+    __builtin_amdgcn_s_waitcnt(VMCNT0);
 
     // m0 = Kbar, m1 = Etil, m2 = Util; t0 = Tm, t1 = Bm
-    Staged st;
+    Staged8 st;
     RawRows vn;
     float v[4];
     if (ch.nc > 0) {
-        stage_load(st, rc(0), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
+        stage_load8(st, rc(0), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
         load_vals_raw(vn, ch.tbase, ch.tlim, h, kq, col, f);
-        stage_store(st, L, tid);
+        stage_store8(st, L, tid);
         raw_rows4(v, vn, f.bf16, f.value_write);
     }
     for (int n = 0; n < ch.nc; ++n) {
@@ -418,13 +454,13 @@ __global__ void __launch_bounds__(BNT) bwd_state_kernel(BwdArgs a, VarPlan vp, c
         // that waiting for them (after this chunk's products) never waits
         // for the stores
         if (n + 1 < ch.nc) {
-            stage_load(st, rc(n + 1), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
+            stage_load8(st, rc(n + 1), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
             load_vals_raw(vn, ch.tbase + (n + 1) * BC, ch.tlim, h, kq, col, f);
         }
-        put_state(hs(n), S, kq, col);
+        put_half(hs(n), S, kq, kh, col);
         __syncthreads();  // chunk n's LDS copy complete
         // X = Kbar S + Bm V (token rows)
-        f4 X = chan_product(L.m0, S, m, kq, f4{0.f, 0.f, 0.f, 0.f});
+        f4 X = pair_sum(LL.xp, chan_half(L.m0, S, m, kq, kh), wv, lane, kh);
         {
             const f4 b4 = *reinterpret_cast<const f4 *>(&L.t1[m * BC + 4 * kq]);
 #pragma unroll
@@ -439,19 +475,20 @@ __global__ void __launch_bounds__(BNT) bwd_state_kernel(BwdArgs a, VarPlan vp, c
         }
         // S <- Diag(e^gC) S + Util^T V - Etil^T M
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
+        for (int t = 0; t < 4; ++t) {
+            const int it = 4 * kh + t;
             const f4 g4 = *reinterpret_cast<const f4 *>(&L.gm[16 * it + 4 * kq]);
-            f4 s = g4 * S[it];
+            f4 s = g4 * S[t];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 s = mfma4(L.m2[(4 * kq + j) * RS + 16 * it + m], v[j], s);
                 s = mfma4(-L.m1[(4 * kq + j) * RS + 16 * it + m], M[j], s);
             }
-            S[it] = s;
+            S[t] = s;
         }
         __syncthreads();  // every wave done with chunk n's LDS copy
         if (n + 1 < ch.nc) {
-            stage_store(st, L, tid);
+            stage_store8(st, L, tid);
             raw_rows4(v, vn, f.bf16, f.value_write);
         }
     }
@@ -459,46 +496,49 @@ __global__ void __launch_bounds__(BNT) bwd_state_kernel(BwdArgs a, VarPlan vp, c
 
 // The gradient of every chunk's exit state, dhist[chain][chunk][128][128],
 // carried backwards from d_sT; the gradient of S0 at the end.
-__global__ void __launch_bounds__(BNT) bwd_dgrad_kernel(BwdArgs a, VarPlan vp, const float *rec, float *dhist,
+__global__ void __launch_bounds__(SNT) bwd_dgrad_kernel(BwdArgs a, VarPlan vp, const float *rec, float *dhist,
                                                         int nch) {
-    __shared__ __attribute__((aligned(16))) ScanLds L;
+    __shared__ __attribute__((aligned(16))) ScanLds8 LL;
+    ScanLds &L = LL.r;
     const ChunkArgs &f = a.f;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int m = lane & 15, kq = lane >> 4;
+    const int m = lane & 15, kq = lane >> 4, kh = wv >> 2;
     const int64_t bh = blockIdx.x >> 1;
     const BChain ch = bchain(f, vp, bh, nch);
     const int64_t h = ch.h;
-    const int col = 64 * (blockIdx.x & 1) + 16 * wv + m;
+    const int col = 64 * (blockIdx.x & 1) + 16 * (wv & 3) + m;
     auto rc = [&](int n) { return rec + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(REC_BWD); };
     auto hs = [&](int n) { return dhist + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(BD * BD); };
 
-    f4 dS[8];
+    f4 dS[4];
 #pragma unroll
-    for (int it = 0; it < 8; ++it)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dS[it][i] = a.d_sT ? a.d_sT[bh * BD * BD + (16 * it + 4 * kq + i) * BD + col] : 0.f;
+        for (int i = 0; i < 4; ++i)
+            dS[t][i] = a.d_sT ? a.d_sT[bh * BD * BD + (16 * (4 * kh + t) + 4 * kq + i) * BD + col] : 0.f;
+    __builtin_amdgcn_s_waitcnt(VMCNT0);
 
     // m0 = Etil, m1 = Qbar, m2 = Kbar; t0 = Tm, t1 = R
-    Staged st;
+    Staged8 st;
     RawRows on;
     float o[4];
     const int nl = ch.nc - 1;
     if (nl >= 0) {
-        stage_load(st, rc(nl), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
+        stage_load8(st, rc(nl), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
         load_rows_raw(on.x, a.d_o, 0, f.H, h, ch.tbase + static_cast<int64_t>(nl) * BC, ch.tlim, kq, col);
-        stage_store(st, L, tid);
+        stage_store8(st, L, tid);
         raw_rows4(o, on, 0, 0);
     }
     for (int n = nl; n >= 0; --n) {
         // loads of the chunk before go out ahead of this chunk's stores
         if (n > 0) {
-            stage_load(st, rc(n - 1), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
+            stage_load8(st, rc(n - 1), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
             load_rows_raw(on.x, a.d_o, 0, f.H, h, ch.tbase + static_cast<int64_t>(n - 1) * BC, ch.tlim, kq, col);
         }
-        put_state(hs(n), dS, kq, col);
+        put_half(hs(n), dS, kq, kh, col);
         __syncthreads();  // chunk n's LDS copy complete
         // dM = -(Etil dSo + R^T dO)  (token rows)
-        f4 dM = chan_product(L.m0, dS, m, kq, f4{0.f, 0.f, 0.f, 0.f});
+        f4 dM = pair_sum(LL.xp, chan_half(L.m0, dS, m, kq, kh), wv, lane, kh);
 #pragma unroll
         for (int j = 0; j < 4; ++j) dM = mfma4(L.t1[(4 * kq + j) * BC + m], o[j], dM);
         dM = -dM;
@@ -508,23 +548,24 @@ __global__ void __launch_bounds__(BNT) bwd_dgrad_kernel(BwdArgs a, VarPlan vp, c
         for (int j = 0; j < 4; ++j) Y = mfma4(L.t0[(4 * kq + j) * BC + m], dM[j], Y);
         // dS <- Diag(e^gC) dSo + Qbar^T dO + Kbar^T Y
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
+        for (int t = 0; t < 4; ++t) {
+            const int it = 4 * kh + t;
             const f4 g4 = *reinterpret_cast<const f4 *>(&L.gm[16 * it + 4 * kq]);
-            f4 s = g4 * dS[it];
+            f4 s = g4 * dS[t];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 s = mfma4(L.m1[(4 * kq + j) * RS + 16 * it + m], o[j], s);
                 s = mfma4(L.m2[(4 * kq + j) * RS + 16 * it + m], Y[j], s);
             }
-            dS[it] = s;
+            dS[t] = s;
         }
         __syncthreads();  // every wave done with chunk n's LDS copy
         if (n > 0) {
-            stage_store(st, L, tid);
+            stage_store8(st, L, tid);
             raw_rows4(o, on, 0, 0);
         }
     }
-    if (a.ds0) put_state(a.ds0 + bh * BD * BD, dS, kq, col);
+    if (a.ds0) put_half(a.ds0 + bh * BD * BD, dS, kq, kh, col);
 }
 
 // ---------------------------------------------------------------------------
@@ -1038,9 +1079,9 @@ hipError_t launch_bwd_d128(const BwdArgs &a, const VarPlan &vp, float *rec, floa
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned g2 = static_cast<unsigned>(f.B * f.H * 2);
-    hipLaunchKernelGGL(bwd_state_kernel, dim3(g2), dim3(BNT), 0, s, a, vp, static_cast<const float *>(rec), hist, nch);
+    hipLaunchKernelGGL(bwd_state_kernel, dim3(g2), dim3(SNT), 0, s, a, vp, static_cast<const float *>(rec), hist, nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dgrad_kernel, dim3(g2), dim3(BNT), 0, s, a, vp, static_cast<const float *>(rec), dhist,
+    hipLaunchKernelGGL(bwd_dgrad_kernel, dim3(g2), dim3(SNT), 0, s, a, vp, static_cast<const float *>(rec), dhist,
                        nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t g3 = tasks < cus ? tasks : cus;  // one 137 KiB workgroup per CU

@@ -25,7 +25,8 @@
 // gradients keep the fp32 tolerance.
 //
 // Register layout.  A wave owns 16 value columns; its state slice (128 key
-// channels x 16 columns) sits in 8 accumulator tiles: lane l = 16 kq + n holds
+// channels x 16 columns, or half of them in the scans, where two waves split
+// the channels) sits in accumulator tiles: lane l = 16 kq + n holds
 // S[16 it + 4 kq + i][n] in register i of tile it.  The k-sum of a product
 // may run in any order, so each product is arranged so that the lane's own
 // accumulator registers are its B operand: in Kbar S the k-step (it, i) takes

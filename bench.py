@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -44,10 +45,14 @@ def log(msg):
 
 
 def source_hash(names) -> str:
+    """Hash of the kernel sources' code: comments and blank lines do not count,
+    so a stored counter profile stays valid across comment-only edits."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "gated_delta_rule_decay_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "gated_delta_rule_decay_amd", "csrc", n)) as f:
+            code = re.sub(r"/\*.*?\*/", "", f.read(), flags=re.S)
+        lines = (re.sub(r"//.*", "", ln).rstrip() for ln in code.splitlines())
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 

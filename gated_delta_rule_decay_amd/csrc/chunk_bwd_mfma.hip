@@ -611,7 +611,13 @@ struct GradLds {
     float dt[BC * BC], x1[BC * BC], da[BC * BC], dbm[BC * BC], dr[BC * BC], dp[BC * BC];
     float daT[BC * BC], dbmT[BC * BC], drT[BC * BC], dpT[BC * BC];  // transposes (columns as rows)
     float wpart[8 * BC];  // value-write form, one write gate per head: per-wave partial sums of dw
+    int steep;            // some channel decays by more than STEEP within the chunk
 };
+
+// Largest decay (nats) of a channel over one chunk for which the Gram
+// gradients take the factored form below: its factors e^(+-(g - g_ref)) then
+// stay within fp32's normal range.
+constexpr float STEEP = 80.f;
 
 // 16 x 16 product over 128 columns of two [16][RS] LDS matrices, X Z^T
 // (lane (kq, n) gets rows 4 kq + r, column n)
@@ -693,6 +699,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
             xg = rc[R_GM + tid - 256];
         f4 bb, ww;  // erase / write gates of token tid / 32, channels c4 .. c4 + 3 (for the last phase)
         const int r = tid >> 5, c4 = 4 * (tid & 31);
+        if (tid == 0) L.steep = 0;
         {
             const int es = f.bf16 ? 2 : 4;
             // dword j of my four channels: bf16 takes two words, fp32 four
@@ -764,6 +771,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
                 L.g[r * KS + tid] = run;
             }
             L.gc[tid] = run;
+            if (L.g[tid] - run > STEEP) L.steep = 1;
         }
 
         // ---- value columns 16 wv + m: Bm V, X, M, dM, Y, dV
@@ -872,7 +880,6 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
 #pragma unroll
             for (int r = 0; r < 4; ++r) L.dw[(4 * kq + r) * RS + c] = dW[r];
         }
-        if (task + gridDim.x < ntask) load_sd(task + gridDim.x);  // in flight until the next task
         lds_barrier();
 
         // ---- dKbar = Tm^T dW (registers); the 16 x 16 gradients
@@ -948,53 +955,93 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
         lds_barrier();
 
         // ---- per (token x, channel c): the Grams' gradients with x as row and
-        //      as column, the decayed operands', then q, k and the gates.  Wave
-        //      w takes tokens 4 (w / 2) .. +3 of channels 64 (w % 2) + lane, so
-        //      a token is uniform across the wave and the rows (and, through the
-        //      transposes, the columns) of dA, dBm, dR, dP are broadcast reads.
+        //      as column, the decayed operands', then q, k and the gates.  Lane
+        //      (kq, m) of wave w takes channel c = 16 w + m and tokens 4 kq .. +3.
+        //        glk[x] = sum_y d_xy (dA[x][y] e_y + dBm[x][y] u_y)   (y < x)
+        //        glq[x] = sum_y d_xy (dR[x][y] e_y + dP[x][y] u_y)    (y <= x)
+        //        gre[x] = sum_y d_xy (dA[y][x] k_y + dR[y][x] q_y)    (y >= x)
+        //        gru[x] = sum_y d_xy (dBm[y][x] k_y + dP[y][x] q_y)   (y >= x)
+        //      with the pairwise decay d_xy = e^-|g_x - g_y| of channel c.
         {
             float *dgv = L.mm, *shr = L.dm, *dbs = L.y, *dws = L.bv;  // [16][RS] each, free now
-            const int cc = 64 * (wv & 1) + lane, x0 = 4 * (wv >> 1);
+            const int cc = 16 * wv + m, x0 = 4 * kq;
             const float gcc = L.gc[cc];
-            float gy[BC], ey[BC], uy[BC], ky[BC], qy[BC];  // channel cc of every token
+            float glk[4], glq[4], gre[4], gru[4];
+            if (!L.steep) {
+                // factored around g_ref = g at token 7: d_xy = e^(g_x - g_ref) e^(g_ref - g_y)
+                // for y <= x (the other way round for y >= x), so the four sums are
+                // 16 x 16 by 16 x 128 products on the matrix cores; every factor is
+                // below e^STEEP.  The B operand of lane (kq, m) is token 4 s + kq of
+                // channel c, the A operand row m of the 16 x 16 gradients.
+                const float gref = L.g[7 * KS + cc];
+                const f4 z = {0.f, 0.f, 0.f, 0.f};
+                f4 GLK = z, GLQ = z, GRE = z, GRU = z;
 #pragma unroll
-            for (int yy = 0; yy < BC; ++yy) {
-                const int ly = yy * KS + cc;
-                gy[yy] = L.g[ly]; ey[yy] = L.e[ly]; uy[yy] = L.u[ly]; ky[yy] = L.k[ly]; qy[yy] = L.q[ly];
+                for (int s4 = 0; s4 < 4; ++s4) {
+                    const int y = 4 * s4 + kq, ly = y * KS + cc, ay = m * BC + y;
+                    const float gy = L.g[ly];
+                    const float fe = __expf(gref - gy), fk = __expf(gy - gref);
+                    const float ey = L.e[ly] * fe, uy = L.u[ly] * fe, ky = L.k[ly] * fk, qy = L.q[ly] * fk;
+                    GLK = mfma4(L.da[ay], ey, GLK);
+                    GLQ = mfma4(L.dr[ay], ey, GLQ);
+                    GRE = mfma4(L.daT[ay], ky, GRE);
+                    GRU = mfma4(L.dbmT[ay], ky, GRU);
+                    GLK = mfma4(L.dbm[ay], uy, GLK);
+                    GLQ = mfma4(L.dp[ay], uy, GLQ);
+                    GRE = mfma4(L.drT[ay], qy, GRE);
+                    GRU = mfma4(L.dpT[ay], qy, GRU);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float gx = L.g[(x0 + r) * KS + cc];
+                    const float fr = __expf(gx - gref), fc = __expf(gref - gx);
+                    glk[r] = fr * GLK[r];
+                    glq[r] = fr * GLQ[r];
+                    gre[r] = fc * GRE[r];
+                    gru[r] = fc * GRU[r];
+                }
+            } else {
+                // a steep chunk: every pairwise decay formed directly (never above 1);
+                // the operands are read where used (this path is rare)
+                for (int r = 0; r < 4; ++r) {
+                    const int x = x0 + r;
+                    const float gx = L.g[x * KS + cc];
+                    float sk = 0.f, sq = 0.f, se = 0.f, su = 0.f;
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int o4 = x * BC + 4 * jj;
+                        const f4 ra = *reinterpret_cast<const f4 *>(&L.da[o4]), rb = *reinterpret_cast<const f4 *>(&L.dbm[o4]);
+                        const f4 rr = *reinterpret_cast<const f4 *>(&L.dr[o4]), rp = *reinterpret_cast<const f4 *>(&L.dp[o4]);
+                        const f4 ca = *reinterpret_cast<const f4 *>(&L.daT[o4]), cb = *reinterpret_cast<const f4 *>(&L.dbmT[o4]);
+                        const f4 cr = *reinterpret_cast<const f4 *>(&L.drT[o4]), cp = *reinterpret_cast<const f4 *>(&L.dpT[o4]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int yy = 4 * jj + e, ly = yy * KS + cc;
+                            const float gy = L.g[ly], ey = L.e[ly], uy = L.u[ly], ky = L.k[ly], qy = L.q[ly];
+                            const float d = __expf(yy < x ? gx - gy : gy - gx);
+                            sk += (ra[e] * ey + rb[e] * uy) * d;
+                            sq += (rr[e] * ey + rp[e] * uy) * d;
+                            se += (ca[e] * ky + cr[e] * qy) * d;
+                            su += (cb[e] * ky + cp[e] * qy) * d;
+                        }
+                    }
+                    glk[r] = sk;
+                    glq[r] = sq;
+                    gre[r] = se;
+                    gru[r] = su;
+                }
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int x = x0 + r;
                 const float gx = L.g[x * KS + cc];
-                // x as the row (dA[x][y] ...: zero for y >= x, dR/dP also at y = x)
-                // and as the column (dA[y][x] ... via the transposes), with the
-                // pairwise decay e^(g_x - g_y) for y before x, e^(g_y - g_x) after
-                float glk = 0.f, glq = 0.f, gre = 0.f, gru = 0.f;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int o4 = x * BC + 4 * jj;
-                    const f4 ra = *reinterpret_cast<const f4 *>(&L.da[o4]), rb = *reinterpret_cast<const f4 *>(&L.dbm[o4]);
-                    const f4 rr = *reinterpret_cast<const f4 *>(&L.dr[o4]), rp = *reinterpret_cast<const f4 *>(&L.dp[o4]);
-                    const f4 ca = *reinterpret_cast<const f4 *>(&L.daT[o4]), cb = *reinterpret_cast<const f4 *>(&L.dbmT[o4]);
-                    const f4 cr = *reinterpret_cast<const f4 *>(&L.drT[o4]), cp = *reinterpret_cast<const f4 *>(&L.dpT[o4]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int yy = 4 * jj + e;
-                        const float d = __expf(yy < x ? gx - gy[yy] : gy[yy] - gx);
-                        glk += (ra[e] * ey[yy] + rb[e] * uy[yy]) * d;
-                        glq += (rr[e] * ey[yy] + rp[e] * uy[yy]) * d;
-                        gre += (ca[e] * ky[yy] + cr[e] * qy[yy]) * d;
-                        gru += (cb[e] * ky[yy] + cp[e] * qy[yy]) * d;
-                    }
-                }
                 const int li = x * KS + cc, lr = x * RS + cc;
                 const float kx = L.k[li], qx = L.q[li], ex = L.e[li], ux = L.u[li];
                 const float eg = __expf(gx), ec = __expf(gcc - gx);
                 const float dkb = L.kb[lr], dqb = L.et[lr], det = L.ut[lr], dut = L.v[lr];
-                const float de = gre + det * ec, du = gru + dut * ec;
-                const float dg = kx * glk + qx * glq - ex * gre - ux * gru + (dkb * kx + dqb * qx) * eg -
+                const float de = gre[r] + det * ec, du = gru[r] + dut * ec;
+                const float dg = kx * glk[r] + qx * glq[r] - ex * gre[r] - ux * gru[r] + (dkb * kx + dqb * qx) * eg -
                                  (det * ex + dut * ux) * ec;
-                float dkk = glk + dkb * eg, dbv = 0.f, dwv = 0.f;
+                float dkk = glk[r] + dkb * eg, dbv = 0.f, dwv = 0.f;
                 if (live(x)) {
                     const int64_t row = row_of(x);
                     const float bx = L.o[lr];
@@ -1010,7 +1057,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
                         dbv = de * kx;
                         dwv = du * kx;
                     }
-                    a.dq[row * BD + cc] = f.q_scale * (glq + dqb * eg);
+                    a.dq[row * BD + cc] = f.q_scale * (glq[r] + dqb * eg);
                     a.dk[row * BD + cc] = dkk;
                     if (eb_key) a.deb[row * BD + cc] = dbv;
                     if (!tied && wr_key && !vw) a.dwr[row * BD + cc] = dwv;
@@ -1057,6 +1104,8 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
                 if (!tied && !wr_key) a.dwr[row] = sw;
             }
         }
+        // the next task's S and dSo columns, in flight across its staging
+        if (task + gridDim.x < ntask) load_sd(task + gridDim.x);
     }
 }
 

@@ -111,6 +111,18 @@ def test_zero_initial_state_and_strong_decay():
     _compare(*_run(w, inp, 64, seed=511))
 
 
+def test_steep_decay_chunks():
+    # channels decaying by 12 nats a token over two 16-token chunks (180 nats
+    # within a chunk, where factors around the chunk's middle would pass
+    # e^88 and overflow): those chunks' Gram gradients take the direct path
+    # (pairwise decays formed one by one), the others the factored
+    # matrix-core path
+    w = W[2].scaled(B=1, T=80, H=2)
+    inp = synth.make_inputs(w, seed=540)
+    inp["log_decay"][:, 16:48, :, :8] = -12.0
+    _compare(*_run(w, inp, 64, seed=541))
+
+
 def test_empty_sequence_passes_the_state_gradient():
     import torch
     from gated_delta_rule_decay_amd import chunk_bwd

@@ -36,6 +36,7 @@ class Gdn2Desc(ctypes.Structure):
         ("erase_kind", ctypes.c_int32), ("write_kind", ctypes.c_int32),
         ("tie_write_to_erase", ctypes.c_int32), ("q_scale", ctypes.c_float),
         ("form", ctypes.c_int32), ("gate_logits", ctypes.c_int32), ("qk_l2norm", ctypes.c_int32),
+        ("o_dtype", ctypes.c_int32),
     ]
 
 
@@ -109,10 +110,10 @@ def abi_version() -> int:
 def make_desc(batch, seqlen, heads, dk, dv, chunk=64, qkv_dtype=GDN2_BF16,
               decay_kind=GDN2_GATE_KEY, erase_kind=GDN2_GATE_KEY, write_kind=GDN2_GATE_KEY,
               tied=False, q_scale=1.0, form=GDN2_FORM_KEY, gate_logits=False,
-              qk_l2norm=False) -> Gdn2Desc:
+              qk_l2norm=False, o_dtype=GDN2_F32) -> Gdn2Desc:
     return Gdn2Desc(batch, seqlen, heads, dk, dv, chunk, qkv_dtype, decay_kind, erase_kind,
                     write_kind, 1 if tied else 0, q_scale, form, int(bool(gate_logits)),
-                    int(bool(qk_l2norm)))
+                    int(bool(qk_l2norm)), o_dtype)
 
 
 def _ptr(t):
@@ -147,8 +148,18 @@ def _gate_kind(g, tok_shape, dk, name):
                      f"nor {tuple(tok_shape)}")
 
 
+def _out_dtype(out, out_dtype):
+    """The output's torch dtype and its gdn2_dtype: that of `out` when given,
+    else `out_dtype` (default float32)."""
+    import torch
+    dt = out.dtype if out is not None else (out_dtype or torch.float32)
+    if dt not in (torch.float32, torch.bfloat16):
+        raise TypeError(f"o must be float32 or bfloat16, not {dt}")
+    return dt, (GDN2_BF16 if dt == torch.bfloat16 else GDN2_F32)
+
+
 def _desc_for(q, k, v, log_decay, erase, write, tok_shape, batch, seqlen, heads, chunk, q_scale,
-              value_write=False, qk_l2norm=False):
+              value_write=False, qk_l2norm=False, o_dtype=GDN2_F32):
     import torch
     dk, dv = k.shape[-1], v.shape[-1]
     dev = k.device
@@ -173,7 +184,7 @@ def _desc_for(q, k, v, log_decay, erase, write, tok_shape, batch, seqlen, heads,
     return make_desc(batch, seqlen, heads, dk, dv, chunk,
                      GDN2_BF16 if k.dtype == torch.bfloat16 else GDN2_F32,
                      la_kind, eb_kind, wr_kind, write is None, q_scale,
-                     GDN2_FORM_VALUE_WRITE if value_write else GDN2_FORM_KEY, gate_logits, qk_l2norm)
+                     GDN2_FORM_VALUE_WRITE if value_write else GDN2_FORM_KEY, gate_logits, qk_l2norm, o_dtype)
 
 
 def chunk_fwd_workspace(desc: Gdn2Desc) -> int:
@@ -186,7 +197,7 @@ def chunk_fwd_workspace(desc: Gdn2Desc) -> int:
 
 def chunk_fwd(q, k, v, log_decay, erase, write=None, state0=None, chunk=64, q_scale=1.0,
               out=None, state_out=None, return_state=True, workspace=True, value_write=False,
-              qk_l2norm=False):
+              qk_l2norm=False, out_dtype=None):
     """Chunkwise GDN-2 forward on the GPU.
 
     q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32, one dtype); gates fp32
@@ -197,21 +208,24 @@ def chunk_fwd(q, k, v, log_decay, erase, write=None, state0=None, chunk=64, q_sc
     ``value_write``: the gist.science form of the update (write gate
     [B,T,H,dv] or [B,T,H], required).  Gates given as bfloat16 tensors are
     raw logits (log a = -softplus, b and w = sigmoid, applied in-kernel);
-    ``qk_l2norm`` normalises q and k per token-head in-kernel.
-    Returns (o [B,T,H,dv] fp32, final state or None).
+    ``qk_l2norm`` normalises q and k per token-head in-kernel.  The output is
+    fp32, or bf16 (the fp32 result rounded to nearest even) when ``out`` is a
+    bfloat16 tensor or ``out_dtype`` is torch.bfloat16.
+    Returns (o [B,T,H,dv], final state or None).
     """
     import torch
     B, T, H, dk = k.shape
     dv = v.shape[-1]
+    odt, o_code = _out_dtype(out, out_dtype)
     desc = _desc_for(q, k, v, log_decay, erase, write, (B, T, H), B, T, H, chunk, q_scale, value_write,
-                     qk_l2norm)
+                     qk_l2norm, o_code)
     dev = k.device
     if state0 is not None:
         _check(state0, "state0", (B, H, dk, dv), (torch.float32,), dev)
     if out is None:
-        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+        out = torch.empty((B, T, H, dv), dtype=odt, device=dev)
     else:
-        _check(out, "out", (B, T, H, dv), (torch.float32,), dev)
+        _check(out, "out", (B, T, H, dv), (odt,), dev)
     if state_out is None and return_state:
         state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
     elif state_out is not None:
@@ -241,7 +255,7 @@ def chunk_fwd_varlen_workspace(desc: Gdn2Desc) -> int:
 
 def chunk_fwd_varlen(q, k, v, log_decay, erase, write, cu_seqlens, state0=None, chunk=64,
                      q_scale=1.0, out=None, state_out=None, return_state=True, workspace=True,
-                     value_write=False, qk_l2norm=False):
+                     value_write=False, qk_l2norm=False, out_dtype=None):
     """Chunkwise GDN-2 forward over N sequences packed along one token axis.
 
     q, k [T,H,dk], v [T,H,dv], gates [T,H,dk] / [T,H] (or the same with a
@@ -261,15 +275,16 @@ def chunk_fwd_varlen(q, k, v, log_decay, erase, write, cu_seqlens, state0=None, 
     if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
         raise ValueError("cu_seqlens must be a 1-D tensor of N+1 offsets")
     N = cu_seqlens.numel() - 1
+    odt, o_code = _out_dtype(out, out_dtype)
     desc = _desc_for(q, k, v, log_decay, erase, write, tuple(lead) + (T, H), N, T, H, chunk, q_scale,
-                     value_write, qk_l2norm)
+                     value_write, qk_l2norm, o_code)
     if state0 is not None:
         _check(state0, "state0", (N, H, dk, dv), (torch.float32,), dev)
     oshape = tuple(lead) + (T, H, dv)
     if out is None:
-        out = torch.empty(oshape, dtype=torch.float32, device=dev)
+        out = torch.empty(oshape, dtype=odt, device=dev)
     else:
-        _check(out, "out", oshape, (torch.float32,), dev)
+        _check(out, "out", oshape, (odt,), dev)
     if state_out is None and return_state:
         state_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     elif state_out is not None:
@@ -397,21 +412,23 @@ def chunk_bwd_varlen(q, k, v, log_decay, erase, write, cu_seqlens, state0, d_o, 
 
 
 def recurrent_step(q, k, v, log_decay, erase, write, state, q_scale=1.0, out=None, value_write=False,
-                   qk_l2norm=False):
+                   qk_l2norm=False, out_dtype=None):
     """One decode step for N sequences; updates ``state`` [N,H,dk,dv] in place.
 
     q, k [N,H,dk], v [N,H,dv]; gates [N,H,dk] or [N,H]; write None = tied.
-    Returns o [N,H,dv] fp32.
+    Returns o [N,H,dv], fp32 or (``out`` / ``out_dtype`` bfloat16) bf16.
     """
     import torch
     N, H, dk = k.shape
     dv = v.shape[-1]
-    desc = _desc_for(q, k, v, log_decay, erase, write, (N, H), N, 1, H, 64, q_scale, value_write, qk_l2norm)
+    odt, o_code = _out_dtype(out, out_dtype)
+    desc = _desc_for(q, k, v, log_decay, erase, write, (N, H), N, 1, H, 64, q_scale, value_write, qk_l2norm,
+                     o_code)
     _check(state, "state", (N, H, dk, dv), (torch.float32,), k.device)
     if out is None:
-        out = torch.empty((N, H, dv), dtype=torch.float32, device=k.device)
+        out = torch.empty((N, H, dv), dtype=odt, device=k.device)
     else:
-        _check(out, "out", (N, H, dv), (torch.float32,), k.device)
+        _check(out, "out", (N, H, dv), (odt,), k.device)
     st = load_library().gdn2_recurrent_step(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(erase),
         _ptr(write), _ptr(state), _ptr(out), _stream())

@@ -45,6 +45,7 @@ gdn2_status check_common(const gdn2_desc *d) {
     if (d->batch < 0 || d->seqlen < 0 || d->heads < 1 || d->dk < 1 || d->dv < 1)
         return GDN2_ERR_SHAPE;
     if (d->qkv_dtype != GDN2_F32 && d->qkv_dtype != GDN2_BF16) return GDN2_ERR_DTYPE;
+    if (d->o_dtype != GDN2_F32 && d->o_dtype != GDN2_BF16) return GDN2_ERR_DTYPE;
     auto kind_ok = [](int32_t k) { return k == GDN2_GATE_HEAD || k == GDN2_GATE_KEY; };
     if (!kind_ok(d->decay_kind) || !kind_ok(d->erase_kind) ||
         (!d->tie_write_to_erase && !kind_ok(d->write_kind)))
@@ -82,7 +83,7 @@ Sizes sizes_of(const gdn2_desc *d, int64_t T) {
     s.eb = s.tok * (d->erase_kind == GDN2_GATE_KEY ? d->dk : 1) * gsz;
     const int64_t wch = d->form == GDN2_FORM_VALUE_WRITE ? d->dv : d->dk;  // channels of the write gate
     s.wr = d->tie_write_to_erase ? 0 : s.tok * (d->write_kind == GDN2_GATE_KEY ? wch : 1) * gsz;
-    s.o = s.tok * d->dv * 4;
+    s.o = s.tok * d->dv * (d->o_dtype == GDN2_BF16 ? 2 : 4);
     s.st = d->batch * d->heads * d->dk * d->dv * 4;
     return s;
 }
@@ -107,6 +108,7 @@ ChunkArgs args_of(const gdn2_desc *d, const void *q, const void *k, const void *
     a.value_write = d->form == GDN2_FORM_VALUE_WRITE;
     a.gate_logits = d->gate_logits != 0;
     a.qk_norm = d->qk_l2norm != 0;
+    a.o_bf16 = d->o_dtype == GDN2_BF16;
     return a;
 }
 
@@ -156,7 +158,7 @@ const char *gdn2_status_str(int status) {
         case GDN2_OK: return "ok";
         case GDN2_ERR_NULL: return "a required pointer is NULL";
         case GDN2_ERR_SHAPE: return "invalid sizes or gate kinds";
-        case GDN2_ERR_DTYPE: return "unknown q/k/v dtype";
+        case GDN2_ERR_DTYPE: return "unknown q/k/v or o dtype";
         case GDN2_ERR_UNSUPPORTED: return "valid request without a kernel in this build";
         case GDN2_ERR_ALIAS: return "an output overlaps an input";
         case GDN2_ERR_WORKSPACE: return "workspace too small";
@@ -455,6 +457,7 @@ gdn2_status gdn2_recurrent_step(const gdn2_desc *d, const void *q, const void *k
     a.value_write = d->form == GDN2_FORM_VALUE_WRITE;
     a.gate_logits = d->gate_logits != 0;
     a.qk_norm = d->qk_l2norm != 0;
+    a.o_bf16 = d->o_dtype == GDN2_BF16;
     return hip_status(gdn2::launch_step(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -274,7 +274,7 @@ __global__ void __launch_bounds__(kThreads) chunk_general_kernel(ChunkArgs a, in
             float acc = 0.f;
             for (int c = 0; c < dk; ++c) acc += Qf[r * KS + c] * S[c * DVT + j];
             for (int s = 0; s <= r; ++s) acc += P[r * Cg + s] * V[s * DVT + j] - R[r * Cg + s] * M[s * DVT + j];
-            a.o[(t * H + h) * dv + col0 + j] = acc;
+            store_out(a.o, (t * H + h) * dv + col0 + j, acc, a.o_bf16);
         }
         __syncthreads();
         // 8. S <- exp(g_C) S + Util^T V - Etil^T M (each thread owns its elements)

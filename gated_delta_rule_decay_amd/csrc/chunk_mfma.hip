@@ -269,7 +269,9 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int64_t t = t0 + 16 * rb + 4 * lg + e;
-                        if (t < a.T) a.o[((b * a.T + t) * a.H + h) * D + col0 + 16 * (ct0 + n) + lr] = acc[n][e];
+                        if (t < a.T)
+                            store_out(a.o, ((b * a.T + t) * a.H + h) * D + col0 + 16 * (ct0 + n) + lr, acc[n][e],
+                                      a.o_bf16);
                     }
             }
 
@@ -378,7 +380,7 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
                     float o = 0.f;
 #pragma unroll
                     for (int w = 0; w < NW; ++w) o += S.fb.red[1][w][tid];
-                    a.o[row * D + col0 + tid] = o;
+                    store_out(a.o, row * D + col0 + tid, o, a.o_bf16);
                 }
                 __syncthreads();  // tok and red reused by the next token
             }

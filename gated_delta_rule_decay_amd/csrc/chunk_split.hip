@@ -624,7 +624,7 @@ __device__ __noinline__ void exact_chunk(ChunkArgs a, f4 *sacc, int64_t h, int64
         if (WITH_O) {
             o += __shfl_xor(o, 16);
             o += __shfl_xor(o, 32);
-            if (lg == 0) a.o[row * D + 16 * ct + lr] = o;
+            if (lg == 0) store_out(a.o, row * D + 16 * ct + lr, o, a.o_bf16);
         }
     }
 }
@@ -866,7 +866,9 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     const int64_t t = t0 + 16 * rt + lr;
-                    if (t < tlim) *reinterpret_cast<f4 *>(&a.o[(t * a.H + h) * D + 16 * ct + 4 * lg]) = oacc[rt];
+                    if (t < tlim)
+                        store_out4(a.o, (t * a.H + h) * D + 16 * ct + 4 * lg, oacc[rt][0], oacc[rt][1], oacc[rt][2],
+                                   oacc[rt][3], a.o_bf16);
                 }
             }
             // S <- Diag(e^gC) S + G - Etil^T P1, tokens in permuted slots

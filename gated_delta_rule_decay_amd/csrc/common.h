@@ -17,6 +17,34 @@ __device__ __forceinline__ float load_qkv(const void *p, int64_t i, int bf16) {
                 : static_cast<const float *>(p)[i];
 }
 
+// fp32 -> bf16 bits, rounded to nearest even (the carry of the dropped half
+// into the kept one); a NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Output element i of o: fp32, or bf16 when o_bf16 (o then points at bf16).
+__device__ __forceinline__ void store_out(float *o, int64_t i, float x, int o_bf16) {
+    if (o_bf16)
+        reinterpret_cast<uint16_t *>(o)[i] = f32_to_bf16(x);
+    else
+        o[i] = x;
+}
+
+// Output elements i .. i+3 (i a multiple of 4): one 16-byte or 8-byte store.
+__device__ __forceinline__ void store_out4(float *o, int64_t i, float x0, float x1, float x2, float x3,
+                                           int o_bf16) {
+    if (o_bf16) {
+        const uint2 w = {f32_to_bf16(x0) | (static_cast<uint32_t>(f32_to_bf16(x1)) << 16),
+                         f32_to_bf16(x2) | (static_cast<uint32_t>(f32_to_bf16(x3)) << 16)};
+        *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(o) + i) = w;
+    } else {
+        *reinterpret_cast<float4 *>(o + i) = make_float4(x0, x1, x2, x3);
+    }
+}
+
 // Gate value of token-head `row` at key channel c: per key channel or one
 // value per token-head.
 __device__ __forceinline__ float load_gate(const float *g, int per_key, int64_t row, int64_t dk,

@@ -139,7 +139,7 @@ __global__ void __launch_bounds__(256) step128_kernel(StepArgs a) {
             const float4 p = s_red[1][w][cg];
             o.x += p.x; o.y += p.y; o.z += p.z; o.w += p.w;
         }
-        *reinterpret_cast<float4 *>(a.o + head * kD + 4 * cg) = o;
+        store_out4(a.o, head * kD + 4 * cg, o.x, o.y, o.z, o.w, a.o_bf16);
     }
 }
 
@@ -195,7 +195,7 @@ __global__ void __launch_bounds__(128) step_general_kernel(StepArgs a) {
         col[static_cast<int64_t>(c) * dv] = sn;
         o += s_q[c] * sn;
     }
-    a.o[head * dv + j] = o;
+    store_out(a.o, head * dv + j, o, a.o_bf16);
 }
 
 __global__ void state_copy_kernel(const float *src, float *dst, int64_t n) {

@@ -12,7 +12,7 @@ struct ChunkArgs {
     const void *q, *k, *v;          // [B,T,H,dk] / [B,T,H,dv], bf16 or fp32
     const float *la, *eb, *wr;      // gates; wr == nullptr when tied
     const float *s0;                // [B,H,dk,dv] or nullptr (zeros)
-    float *o;                       // [B,T,H,dv]
+    float *o;                       // [B,T,H,dv], fp32 (bf16 when o_bf16)
     float *s_out;                   // [B,H,dk,dv] or nullptr
     int64_t B, T, H, dk, dv;
     int C;                          // chunk length requested
@@ -25,19 +25,21 @@ struct ChunkArgs {
     int qk_norm;                    // 1: q, k L2-normalised per token-head in-kernel
     const int32_t *cu = nullptr;    // packed sequences: [B+1] token offsets (device), B sequences
                                     // along T of batch-1 tensors; nullptr: B fixed-length ones
+    int o_bf16 = 0;                 // 1: o holds bf16 (the fp32 result rounded to nearest even)
 };
 
 struct StepArgs {
     const void *q, *k, *v;          // [N,H,dk] / [N,H,dv]
     const float *la, *eb, *wr;      // [N,H,dk] or [N,H]; wr == nullptr when tied
     float *state;                   // [N,H,dk,dv], in place
-    float *o;                       // [N,H,dv]
+    float *o;                       // [N,H,dv], fp32 (bf16 when o_bf16)
     int64_t N, H, dk, dv;
     int bf16;
     int la_key, eb_key, wr_key;
     float q_scale;
     int value_write;                // as in ChunkArgs
     int gate_logits, qk_norm;       // as in ChunkArgs
+    int o_bf16 = 0;                 // as in ChunkArgs
 };
 
 // General chunked forward: fp32 arithmetic on the vector ALU, any dk, dv in

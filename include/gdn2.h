@@ -68,13 +68,13 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 4
+#define GDN2_ABI_VERSION 5
 
 typedef enum gdn2_status {
     GDN2_OK = 0,
     GDN2_ERR_NULL = 1,        /* a required pointer (or desc) is NULL            */
     GDN2_ERR_SHAPE = 2,       /* negative / zero / overflowing sizes            */
-    GDN2_ERR_DTYPE = 3,       /* unknown qkv_dtype                               */
+    GDN2_ERR_DTYPE = 3,       /* unknown qkv_dtype or o_dtype                    */
     GDN2_ERR_UNSUPPORTED = 4, /* valid request this build has no kernel for      */
     GDN2_ERR_ALIAS = 5,       /* an output overlaps an input (see each call)     */
     GDN2_ERR_WORKSPACE = 6,   /* workspace smaller than the query reported      */
@@ -119,6 +119,13 @@ typedef struct gdn2_desc {
     int32_t qk_l2norm;  /* nonzero: q and k are divided by their L2 norm over
                            the dk channels of each token-head inside the
                            kernels (a zero vector stays zero), before q_scale */
+    int32_t o_dtype;    /* gdn2_dtype of the output o of gdn2_chunk_fwd,
+                           gdn2_chunk_fwd_varlen and gdn2_recurrent_step:
+                           GDN2_F32 (0, the default) or GDN2_BF16, the fp32
+                           result rounded to nearest even (2 bytes per element;
+                           the float* o parameter is reinterpreted).  Anything
+                           else is GDN2_ERR_DTYPE.  The backward's d_o is fp32
+                           whatever this says. */
 } gdn2_desc;
 
 /* GDN2_ABI_VERSION of the loaded library. */

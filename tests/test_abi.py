@@ -36,18 +36,40 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn2_abi_version() == 4
+    assert lib.gdn2_abi_version() == 5
     for s in range(8):
         assert lib.gdn2_status_str(s)
     assert lib.gdn2_status_str(0) == b"ok"
 
 
 def test_desc_layout_matches_header():
-    # six int64, five int32, one float, three int32: 84 bytes, padded to 88
+    # six int64, five int32, one float, four int32: 88 bytes
     assert ctypes.sizeof(bd.Gdn2Desc) == 88
     assert bd.Gdn2Desc.q_scale.offset == 68
     assert bd.Gdn2Desc.form.offset == 72
     assert bd.Gdn2Desc.gate_logits.offset == 76 and bd.Gdn2Desc.qk_l2norm.offset == 80
+    assert bd.Gdn2Desc.o_dtype.offset == 84
+
+
+def test_desc_layout_as_a_c_compiler_sees_it(tmp_path):
+    # the header compiled by the host C compiler: size and every field offset
+    # equal to the binding's ctypes structure
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    names = [f[0] for f in bd.Gdn2Desc._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "gdn2.h"\nint main(void) {\n'
+                   '    printf("%zu\\n", sizeof(gdn2_desc));\n'
+                   + "".join(f'    printf("%zu\\n", offsetof(gdn2_desc, {n}));\n' for n in names)
+                   + "    return 0;\n}\n")
+    exe = tmp_path / "layout"
+    inc = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+    subprocess.run([cc, "-I", inc, str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got == [ctypes.sizeof(bd.Gdn2Desc)] + [getattr(bd.Gdn2Desc, n).offset for n in names]
 
 
 # Fake, well-separated device addresses for the inputs and outputs.
@@ -90,7 +112,8 @@ def test_null_arguments(lib):
 @pytest.mark.parametrize("kw,status", [
     (dict(batch=-1), 2), (dict(seqlen=-5), 2), (dict(heads=0), 2), (dict(dk=0), 2),
     (dict(dv=0), 2), (dict(dk=129), 4), (dict(dv=256), 4), (dict(chunk=8), 4),
-    (dict(chunk=128), 4), (dict(qkv_dtype=7), 3), (dict(decay_kind=2), 2),
+    (dict(chunk=128), 4), (dict(qkv_dtype=7), 3), (dict(o_dtype=2), 3), (dict(o_dtype=-1), 3),
+    (dict(decay_kind=2), 2),
     (dict(erase_kind=-1), 2), (dict(batch=1 << 40, seqlen=1 << 30), 2),
 ])
 def test_bad_descriptors(lib, kw, status):
@@ -114,6 +137,17 @@ def test_aliasing(lib):
     d1 = good(seqlen=1)
     assert step(lib, d1, o=S0 + 8) == 5        # decode output inside the state
     assert step(lib, d1, st=K) == 5            # state on k
+
+
+def test_bf16_output_span(lib):
+    # a bf16 o is half as long as an fp32 one (only error paths are called
+    # here: the addresses are not real)
+    obytes = 2 * 128 * 4 * 128 * 2   # the bf16 o of good()
+    assert fwd(lib, good(), q=O + obytes) == 5             # inside the fp32 o
+    assert fwd(lib, good(o_dtype=1), q=O + obytes - 2) == 5  # on the bf16 o's last element
+    assert step(lib, good(seqlen=1, o_dtype=3)) == 3
+    d1 = good(seqlen=1, o_dtype=1)
+    assert step(lib, d1, o=S0 - 2 * 4 * 128 * 2 + 2) == 5     # a bf16 decode output running into the state
 
 
 def test_empty_calls_touch_nothing(lib):

@@ -35,7 +35,7 @@
  *  - All tensors are contiguous, row-major, last index fastest:
  *        q, k           [B, T, H, dk]    bf16 or fp32 (desc->qkv_dtype)
  *        v              [B, T, H, dv]    same dtype as q, k
- *        o              [B, T, H, dv]    fp32
+ *        o              [B, T, H, dv]    fp32, or bf16 (desc->o_dtype)
  *        log_decay      [B, T, H, dk] fp32 if decay_kind == GDN2_GATE_KEY,
  *                       [B, T, H]     fp32 if GDN2_GATE_HEAD
  *        erase, write   same rule with erase_kind / write_kind (the write
@@ -160,7 +160,8 @@ gdn2_status gdn2_chunk_fwd_workspace(const gdn2_desc *desc, size_t *bytes);
  *   write        write gate w; ignored (may be NULL) when
  *                desc->tie_write_to_erase is set.
  *   state0       initial state [B,H,dk,dv] fp32, or NULL for zeros.
- *   o            output [B,T,H,dv] fp32 (must not overlap any input).
+ *   o            output [B,T,H,dv], fp32 or bf16 per desc->o_dtype (must not overlap
+ *                any input).
  *   state_out    final state [B,H,dk,dv] fp32, or NULL to skip.  It may be
  *                exactly state0 (updated in place); any other overlap with
  *                an input is GDN2_ERR_ALIAS.
@@ -316,7 +317,7 @@ gdn2_status gdn2_chunk_bwd_varlen(const gdn2_desc *desc, const int32_t *cu_seqle
  * 5).  The fp32 state [N,H,dk,dv] is read and rewritten in place.
  *
  *   q, k [N,H,dk], v [N,H,dv] (qkv_dtype); gates [N,H,dk] or [N,H] fp32;
- *   write ignored when tied; state in/out; o [N,H,dv] fp32, must not overlap
+ *   write ignored when tied; state in/out; o [N,H,dv] fp32 or bf16 (o_dtype), must not overlap
  *   the state or any input.
  */
 gdn2_status gdn2_recurrent_step(const gdn2_desc *desc,

@@ -264,6 +264,25 @@ __device__ __forceinline__ void chunk_tables(SM &S, int c) {
     S.dtab[5][c] = __builtin_amdgcn_exp2f(gmc[3] - gmc[2]);
 }
 
+// x moved across lanes by the DPP control CTRL (all rows and banks).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over each half-wave's 32 lanes (the 32 lanes that hold one token row),
+// the same total in every lane: within rows of 16 lanes the quad swaps
+// (lane ^ 1, lane ^ 2), then the half-row and row mirrors (lane i with 7 - i,
+// then with 15 - i), each pairing a lane with one from the other group; last
+// a swizzle that swaps the two rows of the half-wave (lane ^ 16).
+__device__ __forceinline__ float half_wave_sum(float x) {
+    x += dpp_f32<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+    x += dpp_f32<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    x += dpp_f32<0x141>(x);  // row_half_mirror
+    x += dpp_f32<0x140>(x);  // row_mirror
+    return x + __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));  // xor 16 in 32
+}
+
 // Factored fp16 Gram operands of my rows: kh = k 2^(g-gm), qh = q 2^(g-gm),
 // eh = e 2^(gm-g), uh = u 2^(gm-g); keeps k 2^(g-gm), q 2^(g-gm) (fp32) and
 // 2^gm for the later Kbar/Qbar rewrite.  Raises S.wide when a factor or
@@ -297,13 +316,8 @@ __device__ __forceinline__ void factored_operands(SM &S, const Raw<KEYG, NV> &R,
         f4 kraw = bf16x4_to_f4(R.k[i]);
         f4 qraw = bf16x4_to_f4(R.q[i]);
         if (qknorm) {
-            float sk = kraw[0] * kraw[0] + kraw[1] * kraw[1] + kraw[2] * kraw[2] + kraw[3] * kraw[3];
-            float sq = qraw[0] * qraw[0] + qraw[1] * qraw[1] + qraw[2] * qraw[2] + qraw[3] * qraw[3];
-#pragma unroll
-            for (int o = 16; o >= 1; o >>= 1) {
-                sk += __shfl_xor(sk, o);
-                sq += __shfl_xor(sq, o);
-            }
+            const float sk = half_wave_sum(kraw[0] * kraw[0] + kraw[1] * kraw[1] + kraw[2] * kraw[2] + kraw[3] * kraw[3]);
+            const float sq = half_wave_sum(qraw[0] * qraw[0] + qraw[1] * qraw[1] + qraw[2] * qraw[2] + qraw[3] * qraw[3]);
             kraw = kraw * (sk > 0.f ? rsqrtf(sk) : 0.f);
             qraw = qraw * (sq > 0.f ? rsqrtf(sq) : 0.f);
         }

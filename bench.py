@@ -114,7 +114,8 @@ def to_dev(inp, torch):
     return out
 
 
-def time_chunk(w, wid, steps, warmup, torch, chunk_fwd, one_pass=False, inp=None, value_write=False):
+def time_chunk(w, wid, steps, warmup, torch, chunk_fwd, one_pass=False, inp=None, value_write=False,
+               out_bf16=False):
     """Time `steps` chunked forwards of workload w with inputs, outputs and
     the two-pass workspace resident in HBM.  Returns (inputs, wall ms per
     step, HIP-event ms per step on the launch stream)."""
@@ -124,7 +125,7 @@ def time_chunk(w, wid, steps, warmup, torch, chunk_fwd, one_pass=False, inp=None
         log(f"[bench] generating {w.name} inputs")
         inp = synth_make(w, wid)
     d = to_dev(inp, torch)
-    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16 if out_bf16 else torch.float32, device="cuda")
     st = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
     ws = False
     if not one_pass:
@@ -379,6 +380,14 @@ def main():
         # reads as one factor per value channel)
         _, msvw, kvw = time_chunk(w, 2, max(2, args.steps // 4), 1, torch, chunk_fwd, inp=inp,
                                   value_write=True)
+        # the same call with o stored as bf16 (the fp32 result rounded): o's
+        # 512 B per token-head halve
+        _, msbo, kbo = time_chunk(w, 2, max(2, args.steps // 4), 1, torch, chunk_fwd, inp=inp, out_bf16=True)
+        bo_bytes = chunk_bytes(w) - w.B * w.T * w.H * w.dv * 2
+        result["bf16_output"] = {"workload": f"{w.name}, o stored as bf16", "ms_per_step": round(msbo, 4),
+                                 "kernel_ms": round(kbo, 4), "value": round(tokens / (msbo * 1e-3), 1),
+                                 "unit": "tokens/s", "roofline": roofline_hbm(bo_bytes, kbo),
+                                 "algorithmic_bytes_per_launch": bo_bytes}
         result["value_write"] = {"workload": f"{w.name}, value-write form (tied-structure kernels)",
                                  "ms_per_step": round(msvw, 4), "kernel_ms": round(kvw, 4),
                                  "value": round(tokens / (msvw * 1e-3), 1), "unit": "tokens/s",

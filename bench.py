@@ -166,7 +166,7 @@ def fused_bytes(w) -> int:
     return w.B * w.T * w.H * per_tok + (state if w.s0_std > 0 else 0) + state
 
 
-def time_fused(w, torch, chunk_fwd, steps):
+def time_fused(w, torch, chunk_fwd, steps, warmup=1):
     """Time the forward on raw inputs: bf16 gate logits activated and q, k
     L2-normalised inside the kernels (same draws as the main workload)."""
     from gated_delta_rule_decay_amd import binding, synth
@@ -184,7 +184,8 @@ def time_fused(w, torch, chunk_fwd, steps):
                              gate_logits=True, qk_l2norm=True)
     ws = torch.empty(binding.chunk_fwd_workspace(desc), dtype=torch.uint8, device="cuda")
     kw = dict(chunk=w.chunk, out=o, state_out=st, workspace=ws, qk_l2norm=True)
-    chunk_fwd(q, k, v, xa, xb, xw, s0, **kw)
+    for _ in range(warmup):
+        chunk_fwd(q, k, v, xa, xb, xw, s0, **kw)
     torch.cuda.synchronize()
     log(f"[bench] timing {steps} steps of {w.name} with fused input preparation")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -217,7 +218,7 @@ def bwd_bytes(w) -> int:
     return w.B * w.T * w.H * per_tok + 3 * state
 
 
-def time_backward(w, inp, torch, steps):
+def time_backward(w, inp, torch, steps, warmup=1):
     """Time gdn2_chunk_bwd on workload w (random cotangents, workspace
     resident)."""
     from gated_delta_rule_decay_amd import binding, chunk_bwd
@@ -230,7 +231,8 @@ def time_backward(w, inp, torch, steps):
                              int(w.gates == "key"), int(w.gates == "key"), int(w.gates == "key"), w.tied)
     ws = torch.empty(binding.chunk_bwd_workspace(desc), dtype=torch.uint8, device="cuda")
     args = (d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"], d_o, d_st)
-    chunk_bwd(*args, chunk=w.chunk, workspace=ws)
+    for _ in range(warmup):
+        chunk_bwd(*args, chunk=w.chunk, workspace=ws)
     torch.cuda.synchronize()
     log(f"[bench] timing {steps} backward calls of {w.name}")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -250,7 +252,7 @@ def time_backward(w, inp, torch, steps):
             "algorithmic_bytes_per_launch": bwd_bytes(w)}
 
 
-def time_packed(w, inp, torch, steps, n_seq=12, lengths=None):
+def time_packed(w, inp, torch, steps, n_seq=12, lengths=None, warmup=1):
     """Time gdn2_chunk_fwd_varlen on the workload's B*T tokens of every head
     packed as n_seq sequences of drawn lengths (or the lengths given: the
     same number of tokens), the same q/k/v/gate values, one N(0, 0.1)
@@ -271,7 +273,8 @@ def time_packed(w, inp, torch, steps, n_seq=12, lengths=None):
     desc = binding.make_desc(n_seq, tot, w.H, w.dk, w.dv, w.chunk, binding.GDN2_BF16, 1, 1, 1, False)
     ws = torch.empty(binding.chunk_fwd_varlen_workspace(desc), dtype=torch.uint8, device="cuda")
     kw = dict(chunk=w.chunk, out=o, state_out=st, workspace=ws)
-    chunk_fwd_varlen(*args, cu, s0, **kw)
+    for _ in range(warmup):
+        chunk_fwd_varlen(*args, cu, s0, **kw)
     torch.cuda.synchronize()
     log(f"[bench] timing {steps} packed forwards ({n_seq} sequences)")
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -371,18 +374,21 @@ def main():
         "chunk_path": "two-pass: chunk_prep_kernel (every chunk's state-independent products, "
                       "in parallel, into a workspace) then chunk_scan_kernel (the scan over chunks)",
     }
+    # the other lines warm up with a third of the main warmup each: the
+    # clocks are settled by then, but every line has buffers of its own
+    ew = max(1, args.warmup // 3)
     if not args.no_extra:
-        _, ms1p, k1p = time_chunk(w, 2, max(2, args.steps // 4), 1, torch, chunk_fwd, one_pass=True,
+        _, ms1p, k1p = time_chunk(w, 2, max(2, args.steps // 4), ew, torch, chunk_fwd, one_pass=True,
                                   inp=inp)
         result["one_pass"] = {"ms_per_step": round(ms1p, 4), "kernel_ms": round(k1p, 4),
                               "value": round(tokens / (ms1p * 1e-3), 1), "unit": "tokens/s"}
         # the value-write form on the same inputs (dk = dv: the write gate
         # reads as one factor per value channel)
-        _, msvw, kvw = time_chunk(w, 2, max(2, args.steps // 4), 1, torch, chunk_fwd, inp=inp,
+        _, msvw, kvw = time_chunk(w, 2, max(2, args.steps // 4), ew, torch, chunk_fwd, inp=inp,
                                   value_write=True)
         # the same call with o stored as bf16 (the fp32 result rounded): o's
         # 512 B per token-head halve
-        _, msbo, kbo = time_chunk(w, 2, max(2, args.steps // 4), 1, torch, chunk_fwd, inp=inp, out_bf16=True)
+        _, msbo, kbo = time_chunk(w, 2, max(2, args.steps // 4), ew, torch, chunk_fwd, inp=inp, out_bf16=True)
         bo_bytes = chunk_bytes(w) - w.B * w.T * w.H * w.dv * 2
         result["bf16_output"] = {"workload": f"{w.name}, o stored as bf16", "ms_per_step": round(msbo, 4),
                                  "kernel_ms": round(kbo, 4), "value": round(tokens / (msbo * 1e-3), 1),
@@ -392,20 +398,20 @@ def main():
                                  "ms_per_step": round(msvw, 4), "kernel_ms": round(kvw, 4),
                                  "value": round(tokens / (msvw * 1e-3), 1), "unit": "tokens/s",
                                  "roofline": roofline_hbm(chunk_bytes(w), kvw)}
-        result["backward"] = time_backward(w, inp, torch, max(2, args.steps // 8))
-        result["packed"] = time_packed(w, inp, torch, max(2, args.steps // 4))
+        result["backward"] = time_backward(w, inp, torch, max(2, args.steps // 8), ew)
+        result["packed"] = time_packed(w, inp, torch, max(2, args.steps // 4), warmup=ew)
         # one sequence holding most of the tokens: cut into segments of the
         # two-level scan (without them its chain alone would bound the scan)
         result["packed_long"] = time_packed(w, inp, torch, max(2, args.steps // 4),
-                                            lengths=[28000, 2000, 1500, 1268])
+                                            lengths=[28000, 2000, 1500, 1268], warmup=ew)
     del inp
     if not args.no_extra:
-        result["fused_inputs"] = time_fused(w, torch, chunk_fwd, max(2, args.steps // 4))
+        result["fused_inputs"] = time_fused(w, torch, chunk_fwd, max(2, args.steps // 4), ew)
 
     if not args.no_extra:
         # long context: one sequence per head, T = 65536 (two-level scan)
         w3 = W[3]
-        _, ms3, k3 = time_chunk(w3, 3, max(2, args.steps // 4), 1, torch, chunk_fwd)
+        _, ms3, k3 = time_chunk(w3, 3, max(2, args.steps // 4), ew, torch, chunk_fwd)
         result["long_context"] = {"workload": f"{w3.name}: B={w3.B} H={w3.H} T={w3.T}, decay spikes",
                                   "value": round(w3.B * w3.T / (ms3 * 1e-3), 1), "unit": "tokens/s",
                                   "ms_per_step": round(ms3, 4), "kernel_ms": round(k3, 4),

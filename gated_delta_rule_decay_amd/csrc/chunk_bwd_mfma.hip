@@ -410,6 +410,21 @@ __device__ __forceinline__ f4 pair_sum(f4 *xp, f4 mine, int wv, int lane, int kh
     return kh ? other + mine : mine + other;
 }
 
+// The chain and value half of a scan workgroup.  Workgroups are spread over
+// the 8 XCDs round robin; when the grid is a multiple of 16, the two halves
+// of a chain go to workgroups 8 apart, i.e. to one XCD, so the record parts
+// both read come into one L2.
+struct ScanUnit {
+    int64_t chain;
+    int half;
+};
+
+__device__ __forceinline__ ScanUnit scan_unit() {
+    const int64_t G = blockIdx.x;
+    if (gridDim.x % 16 == 0) return {(G / 16) * 8 + (G % 8), static_cast<int>((G / 8) & 1)};
+    return {G >> 1, static_cast<int>(G & 1)};
+}
+
 struct ScanLds8 {
     ScanLds r;
     f4 xp[8 * 64];  // the waves' half products
@@ -423,10 +438,11 @@ __global__ void __launch_bounds__(SNT) bwd_state_kernel(BwdArgs a, VarPlan vp, c
     const ChunkArgs &f = a.f;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int m = lane & 15, kq = lane >> 4, kh = wv >> 2;
-    const int64_t bh = blockIdx.x >> 1;
+    const ScanUnit su = scan_unit();
+    const int64_t bh = su.chain;
     const BChain ch = bchain(f, vp, bh, nch);
     const int64_t h = ch.h;
-    const int col = 64 * (blockIdx.x & 1) + 16 * (wv & 3) + m;  // this lane's value column (as n)
+    const int col = 64 * su.half + 16 * (wv & 3) + m;  // this lane's value column (as n)
     auto rc = [&](int n) { return rec + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(REC_BWD); };
     auto hs = [&](int n) { return hist + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(BD * BD); };
 
@@ -504,10 +520,11 @@ __global__ void __launch_bounds__(SNT) bwd_dgrad_kernel(BwdArgs a, VarPlan vp, c
     const ChunkArgs &f = a.f;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int m = lane & 15, kq = lane >> 4, kh = wv >> 2;
-    const int64_t bh = blockIdx.x >> 1;
+    const ScanUnit su = scan_unit();
+    const int64_t bh = su.chain;
     const BChain ch = bchain(f, vp, bh, nch);
     const int64_t h = ch.h;
-    const int col = 64 * (blockIdx.x & 1) + 16 * (wv & 3) + m;
+    const int col = 64 * su.half + 16 * (wv & 3) + m;
     auto rc = [&](int n) { return rec + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(REC_BWD); };
     auto hs = [&](int n) { return dhist + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(BD * BD); };
 

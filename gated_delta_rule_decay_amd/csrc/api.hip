@@ -159,7 +159,7 @@ const char *gdn2_status_str(int status) {
         case GDN2_ERR_NULL: return "a required pointer is NULL";
         case GDN2_ERR_SHAPE: return "invalid sizes or gate kinds";
         case GDN2_ERR_DTYPE: return "unknown q/k/v or o dtype";
-        case GDN2_ERR_UNSUPPORTED: return "valid request without a kernel in this build";
+        case GDN2_ERR_UNSUPPORTED: return "valid request that no kernel of the library covers";
         case GDN2_ERR_ALIAS: return "an output overlaps an input";
         case GDN2_ERR_WORKSPACE: return "workspace too small";
         case GDN2_ERR_HIP: return "a HIP launch failed";

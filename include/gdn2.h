@@ -75,7 +75,7 @@ typedef enum gdn2_status {
     GDN2_ERR_NULL = 1,        /* a required pointer (or desc) is NULL            */
     GDN2_ERR_SHAPE = 2,       /* negative / zero / overflowing sizes            */
     GDN2_ERR_DTYPE = 3,       /* unknown qkv_dtype or o_dtype                    */
-    GDN2_ERR_UNSUPPORTED = 4, /* valid request this build has no kernel for      */
+    GDN2_ERR_UNSUPPORTED = 4, /* valid request no kernel of the library covers  */
     GDN2_ERR_ALIAS = 5,       /* an output overlaps an input (see each call)     */
     GDN2_ERR_WORKSPACE = 6,   /* workspace smaller than the query reported      */
     GDN2_ERR_HIP = 7          /* a HIP launch or copy failed                     */

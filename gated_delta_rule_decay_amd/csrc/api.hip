@@ -315,10 +315,11 @@ gdn2_status gdn2_chunk_bwd(const gdn2_desc *d, const void *q, const void *k, con
         return GDN2_ERR_NULL;
     if (work && !tied && (!write || !d_write)) return GDN2_ERR_NULL;
     const Sizes sz = sizes_of(d, T);
+    // d_o is fp32 whatever desc->o_dtype says
     const Span in[] = {span_of(q, sz.qk), span_of(k, sz.qk), span_of(v, sz.v),
                        span_of(log_decay, sz.la), span_of(erase, sz.eb),
                        span_of(tied ? nullptr : write, sz.wr), span_of(state0, sz.st),
-                       span_of(d_o, sz.o), span_of(d_state_out, sz.st)};
+                       span_of(d_o, sz.tok * d->dv * 4), span_of(d_state_out, sz.st)};
     // gradients are fp32 and shaped like their inputs (those of bf16 gate
     // logits too)
     const int64_t f32 = d->qkv_dtype == GDN2_BF16 ? 2 : 1;
@@ -392,7 +393,8 @@ gdn2_status gdn2_chunk_bwd_varlen(const gdn2_desc *d, const int32_t *cu_seqlens,
     const Span in[] = {span_of(q, sz.qk), span_of(k, sz.qk), span_of(v, sz.v),
                        span_of(log_decay, sz.la), span_of(erase, sz.eb),
                        span_of(tied ? nullptr : write, sz.wr), span_of(state0, stb),
-                       span_of(d_o, sz.o), span_of(d_state_out, stb), span_of(cu_seqlens, (N + 1) * 4)};
+                       span_of(d_o, sz.tok * d->dv * 4), span_of(d_state_out, stb),
+                       span_of(cu_seqlens, (N + 1) * 4)};
     const int64_t f32 = d->qkv_dtype == GDN2_BF16 ? 2 : 1;
     gdn2_desc d4 = one;
     d4.gate_logits = 0;

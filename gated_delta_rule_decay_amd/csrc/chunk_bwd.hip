@@ -458,11 +458,16 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist, VarPl
             for (int r = s + 1; r < Cg; ++r) x += Bm[r * Cg + s] * Y[r * VS + j];
             if (live(s)) {
                 if (f.value_write) {  // x is the gradient of w .* v
-                    const float vr = load_qkv(f.v, row_of(s) * dv + j, f.bf16);
-                    const float wr = load_gate(f.wr, f.wr_key, row_of(s), dv, j);
-                    a.dv[row_of(s) * dv + j] = x * wr;
-                    if (f.wr_key) a.dwr[row_of(s) * dv + j] = x * vr;
-                    else atomicAdd(&WH[s], x * vr);
+                    if (f.wr_key) {
+                        const float vr = load_qkv(f.v, row_of(s) * dv + j, f.bf16);
+                        a.dv[row_of(s) * dv + j] = x * load_gate(f.wr, 1, row_of(s), dv, j);
+                        a.dwr[row_of(s) * dv + j] = x * vr;
+                    } else {
+                        // one write gate per token-head: x itself for now; the
+                        // row is summed against v and scaled by w after the
+                        // barrier, in a fixed order (no atomics)
+                        a.dv[row_of(s) * dv + j] = x;
+                    }
                 } else {
                     a.dv[row_of(s) * dv + j] = x;
                 }
@@ -520,6 +525,19 @@ bwd_grads_kernel(BwdArgs a, int Cg, const float *hist, const float *dhist, VarPl
     }
     __syncthreads();
     // P8: dTm (lower part) = dW Kbar^T + dM BV^T; dKbar = Tm^T dW (into W)
+    // (value-write form with one write gate per token-head: dw of token s is
+    // sum_j x_j v_j over the row x of P7, which becomes dv = x w)
+    if (f.value_write && !f.wr_key && tid < Cg && live(tid)) {
+        const int64_t row = row_of(tid);
+        const float wr = load_gate(f.wr, 0, row, dv, 0);
+        float acc = 0.f;
+        for (int j = 0; j < dv; ++j) {
+            const float x = a.dv[row * dv + j];
+            acc += x * load_qkv(f.v, row * dv + j, f.bf16);
+            a.dv[row * dv + j] = x * wr;
+        }
+        WH[tid] = acc;
+    }
     for (int idx = tid; idx < Cg * Cg; idx += kGradThreads) {
         const int r = idx / Cg, s = idx % Cg;
         float acc = 0.f;

@@ -40,6 +40,8 @@ constexpr int AP = C + 4;      // pitch (floats) of the fp32 C x C matrix
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float MAX_EXP2 = 14.f;        // largest |log2 factor| on the fast path
 constexpr float MAX_OPERAND = 16384.f;  // largest |fp16 operand| on the fast path
+constexpr float MAX_RESULT = 30000.f;   // largest |fp16 product| kept on the fast path
+constexpr float MAX_STATE = 16384.f;    // largest |state| whose fp16 copy feeds a product
 
 // (block row, block col) of the strictly-lower 16x16 tiles of a 64x64 chunk
 // matrix, and the index of each such pair in the cross-block factor table.
@@ -105,6 +107,12 @@ __device__ __forceinline__ f4 bf16x4_to_f4(uint2 p) {
 }
 
 __device__ __forceinline__ f4 splat(float x) { return f4{x, x, x, x}; }
+
+// Whether a product about to be rounded to fp16 leaves the fast range (or is
+// not finite).
+__device__ __forceinline__ bool out_of_range(f4 x) {
+    return !(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))) <= MAX_RESULT);
+}
 
 __device__ __forceinline__ h4 to_h4(f4 x) {
     return h4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
@@ -344,9 +352,10 @@ __device__ __forceinline__ void factored_operands(SM &S, const Raw<KEYG, NV> &R,
 
 // One 16x16 tile (block row i, block column j <= i) of the four Grams, A/Bm/R/P
 // sharing fragments; an off-diagonal tile folds the cross-block factor into
-// its column fragment.  Writes af (A, fp32), b16, r16 and p16.
+// its column fragment.  Writes af (A, fp32), b16, r16 and p16, and returns
+// whether an entry stored in fp16 (Bm, R, P) left the fast range.
 template <typename SM, bool TIED>
-__device__ __forceinline__ void gram_tile(SM &S, int i, int j, int lr, int lg) {
+__device__ __forceinline__ bool gram_tile(SM &S, int i, int j, int lr, int lg) {
     const float *dj = (i != j) ? S.dtab[kPair[i][j]] : nullptr;
     f4 aA = splat(0.f), aB = splat(0.f), aR = splat(0.f), aP = splat(0.f);
 #pragma unroll
@@ -385,14 +394,17 @@ __device__ __forceinline__ void gram_tile(SM &S, int i, int j, int lr, int lg) {
         S.r16[r * SP + s] = (_Float16)(incl ? aR[e] : 0.f);
         if (!TIED) S.p16[r * SP + s] = (_Float16)(incl ? aP[e] : 0.f);
     }
+    return out_of_range(aR) || (!TIED && (out_of_range(aB) || out_of_range(aP)));
 }
 
 // The four Grams with 8 waves: waves 0,1 take two diagonal tiles each (and
 // invert them right away), waves 2..7 one off-diagonal tile each.  Writes
 // af (A, fp32, diagonal blocks then inverted), b16, r16, p16 and the
-// diagonal blocks of t16.
+// diagonal blocks of t16; returns whether a Gram entry held in fp16 left the
+// fast range (A and Tm are checked through the products they enter).
 template <typename SM, bool TIED>
-__device__ __forceinline__ void gram_tiles(SM &S, int wv, int lr, int lg) {
+__device__ __forceinline__ bool gram_tiles(SM &S, int wv, int lr, int lg) {
+    bool big = false;
     for (int n = 0; n < 2; ++n) {
         int i, j;
         if (wv < 2) {
@@ -402,13 +414,14 @@ __device__ __forceinline__ void gram_tiles(SM &S, int wv, int lr, int lg) {
             i = kOffI[wv - 2];
             j = kOffJ[wv - 2];
         }
-        gram_tile<SM, TIED>(S, i, j, lr, lg);
+        big |= gram_tile<SM, TIED>(S, i, j, lr, lg);
         // scratch blocks 4..7 do not overlap the cross-block factor table
         // that the off-diagonal waves are still reading
         if (i == j)
             invert_unit_lower16(&S.af[(16 * i) * AP + 16 * i], &S.t16[(16 * i) * SP + 16 * i],
                                 S.scr[4 + 2 * wv], S.scr[5 + 2 * wv], lr, lg);
     }
+    return big;
 }
 
 // Off-diagonal blocks of Tm = (I + A)^-1 (diagonal blocks already inverted),

@@ -28,8 +28,11 @@
 // 16-token block: the row side carries exp(g_r - gm_i), the column side
 // exp(gm_j - g_s), and a cross-block factor exp(gm_i - gm_j) <= 1 is folded
 // into the column fragment.  The factors stay within fp16 unless about eight
-// consecutive tokens decay a channel by more than 2^14; such a chunk is
-// detected and run as the exact fp32 token recurrence instead.
+// consecutive tokens decay a channel by more than 2^14.  The fp16 copies
+// of the state, the Grams and the intermediates X and M are range-checked
+// before anything of the chunk is stored (|state| <= 16384, products <=
+// 30000, all finite); a chunk that fails any check is run as the exact fp32
+// token recurrence instead.
 #include "chunk_common.h"
 
 namespace gdn2 {
@@ -64,7 +67,8 @@ struct Smem {
     };
     float fsc[4][D];         // 2^(g_C - gm_j)
     float gce[D];            // 2^g_C
-    int wide;
+    int wide;    // the chunk's factors or operands leave the fast range
+    int wide2;   // its state copy, Grams, X or M do
 };
 
 // Issue every load of one chunk (no waits: the values are first used by the
@@ -114,7 +118,10 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
         S.r16[idx] = (_Float16)0.f;
         S.p16[idx] = (_Float16)0.f;
     }
-    if (tid == 0) S.wide = 0;
+    if (tid == 0) {
+        S.wide = 0;
+        S.wide2 = 0;
+    }
 
     // state slice: wave wv owns key rows 16wv..16wv+15, every value tile
     f4 sacc[NCT];
@@ -144,9 +151,14 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
         const int seg = tl >> 5, cq = tl & 31;
 
         // ---- prep 1: fp16 state copy, values, segment log2-decay totals ----
+        if (tid == 0) S.wide2 = 0;  // last read before this chunk's first barrier
+        bool sbig = false;
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
+        for (int ct = 0; ct < NCT; ++ct) {
+            sbig |= !(fmaxf(fmaxf(fabsf(sacc[ct][0]), fabsf(sacc[ct][1])), fmaxf(fabsf(sacc[ct][2]), fabsf(sacc[ct][3]))) <= MAX_STATE);
             *reinterpret_cast<h4 *>(&S.s16[(16 * ct + lr) * KP + 16 * wv + 4 * lg]) = to_h4(sacc[ct]);
+        }
+        if (__ballot(sbig) != 0 && lane == 0) S.wide = 1;
         if (tid < C * PPR) {
             const int s = tid / PPR, piece = tid % PPR;
             const uint32_t w4[4] = {R.v[0].x, R.v[0].y, R.v[0].z, R.v[0].w};
@@ -168,7 +180,7 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
         __syncthreads();
 
         const bool wide = S.wide != 0;
-        if (!wide) gram_tiles<Smem<VT>, TIED>(S, wv, lr, lg);
+        if (!wide && gram_tiles<Smem<VT>, TIED>(S, wv, lr, lg)) S.wide2 = 1;
         __syncthreads();
         if (tid == 0) S.wide = 0;
 
@@ -185,18 +197,21 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
         // end come back as zeros)
         load_raw<VT, TIED, KEYG>(R, a, b, h, t0 + C, col0, seg, cq, tid);
 
-        if (!wide) {
+        // Chunk-row outputs (X, M, O: C x VT): wave wv owns row block
+        // rb = wv/2 and NCTW value tiles, so its row-side fragment is read
+        // once per k-step for all of them.
+        const int rb = wv >> 1, ct0 = (wv & 1) * NCTW;
+        const bool rows_active = NCT >= 2 || (wv & 1) == 0;
+        f4 acc[NCTW];
+        // Nothing of the chunk is stored (o, the state) before X and M have
+        // passed their range checks, so a chunk that fails one can still
+        // take the exact path from the unchanged state.
+        bool fast = !wide;
+        if (fast) {
             // ---- Tm = (I + A)^-1 (diagonal blocks were inverted with the Grams)
             solve_offdiag(S, wv, lr, lg);  // Tm ready in fp16; af region free for X / -M
 
-            // Chunk-row outputs (X, M, O: C x VT): wave wv owns row block
-            // rb = wv/2 and NCTW value tiles, so its row-side fragment is read
-            // once per k-step for all of them.
-            const int rb = wv >> 1, ct0 = (wv & 1) * NCTW;
-            const bool rows_active = NCT >= 2 || (wv & 1) == 0;
-
             // ---- X = Kbar S + Bm V -------------------------------------------
-            f4 acc[NCTW];
             if (rows_active) {
 #pragma unroll
                 for (int n = 0; n < NCTW; ++n) acc[n] = splat(0.f);
@@ -215,12 +230,18 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
                     for (int n = 0; n < NCTW; ++n)
                         acc[n] = mfma32(xa, *reinterpret_cast<const h8 *>(&S.v16[(16 * (ct0 + n) + lr) * SP + sb]), acc[n]);
                 }
+                bool big = false;
 #pragma unroll
-                for (int n = 0; n < NCTW; ++n)
+                for (int n = 0; n < NCTW; ++n) {
+                    big |= out_of_range(acc[n]);
                     *reinterpret_cast<h4 *>(&S.xm16[(16 * (ct0 + n) + lr) * SP + 16 * rb + 4 * lg]) = to_h4(acc[n]);
+                }
+                if (__ballot(big) != 0 && lane == 0) S.wide2 = 1;
             }
-            __syncthreads();
-
+        }
+        __syncthreads();  // X complete; the flags of the Grams and of X visible
+        fast = fast && S.wide2 == 0;
+        if (fast) {
             // ---- M = Tm X ------------------------------------------------------
             if (rows_active) {
 #pragma unroll
@@ -232,8 +253,15 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
                     for (int n = 0; n < NCTW; ++n)
                         acc[n] = mfma32(xa, *reinterpret_cast<const h8 *>(&S.xm16[(16 * (ct0 + n) + lr) * SP + sb]), acc[n]);
                 }
+                bool big = false;
+#pragma unroll
+                for (int n = 0; n < NCTW; ++n) big |= out_of_range(acc[n]);
+                if (__ballot(big) != 0 && lane == 0) S.wide2 = 1;
             }
-            __syncthreads();
+        }
+        __syncthreads();  // every wave has read X; the flag of M visible
+        fast = fast && S.wide2 == 0;
+        if (fast) {
             if (rows_active) {
 #pragma unroll
                 for (int n = 0; n < NCTW; ++n)

@@ -59,7 +59,6 @@ constexpr int64_t OFF_E = 16384;
 constexpr int64_t OFF_G = 24576;
 constexpr int64_t OFF_O = 40960;
 constexpr int64_t REC = 49152;
-constexpr float MAX_RESULT = 30000.f;  // largest |fp16 value| a record may hold
 
 struct SplitWs {
     _Float16 *frag;  // [task][REC]
@@ -95,10 +94,6 @@ struct PrepSmem {
     float iscr[4][2][16 * 16];  // private scratch of the four diagonal inverses
     int wide;
 };
-
-__device__ __forceinline__ bool out_of_range(f4 x) {
-    return !(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))) <= MAX_RESULT);
-}
 
 // Loads of task `task` in four parts (no waits), so that a task's requests
 // are spread over the previous task instead of arriving at HBM in one burst:
@@ -797,7 +792,7 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         bool big = false;
 #pragma unroll
         for (int it = 0; it < 8; ++it)
-            big |= !(fmaxf(fmaxf(fabsf(sacc[it][0]), fabsf(sacc[it][1])), fmaxf(fabsf(sacc[it][2]), fabsf(sacc[it][3]))) <= 16384.f);
+            big |= !(fmaxf(fmaxf(fabsf(sacc[it][0]), fabsf(sacc[it][1])), fmaxf(fabsf(sacc[it][2]), fabsf(sacc[it][3]))) <= MAX_STATE);
         bool bad = gm[0] < 0.f || __ballot(big) != 0;  // chunk marked for the exact path
         f4 p1[4], oacc[4];
         h8 ef[8][2];

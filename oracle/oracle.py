@@ -60,6 +60,18 @@ def _load():
                 dp, ctypes.c_double,
                 dp, dp, ctypes.c_int, ctypes.c_int,
             ]
+            lib.gdn2_oracle_bwd.restype = ctypes.c_int
+            lib.gdn2_oracle_bwd.argtypes = [
+                i64, i64, i64, i64, i64,
+                dp, dp, dp,
+                dp, ctypes.c_int,
+                dp, ctypes.c_int,
+                dp, ctypes.c_int,
+                dp, ctypes.c_double,
+                dp, dp,
+                dp, dp, dp, dp, dp, dp, dp,
+                ctypes.c_int, ctypes.c_int,
+            ]
             lib.gdn2_oracle_max_threads.restype = ctypes.c_int
             lib.gdn2_oracle_max_threads.argtypes = []
             _lib = lib
@@ -125,6 +137,37 @@ def gdn2_forward(q, k, v, log_decay, erase, write=None, S0=None, q_scale=1.0,
     if rc != 0:
         raise RuntimeError(f"oracle failed with code {rc}")
     return o, S_T
+
+
+def gdn2_backward_c(q, k, v, log_decay, erase, write=None, S0=None, d_o=None, d_state=None,
+                    q_scale=1.0, threads: int | None = None):
+    """Gradients of L = <d_o, o> + <d_state, S_T> with respect to every input
+    of ``gdn2_forward`` (key form), by the reverse pass written out by hand in
+    ``gdn2_oracle.c`` (fp64, chains in parallel).  Same arguments and the
+    same result keys as ``oracle_bwd.gdn2_backward`` (dq, dk, dv,
+    d_log_decay, d_erase, d_write -- None when tied -- and d_state0); d_o or
+    d_state None means zeros.  Gate gradients are shaped like their gates.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, T, H, dk = k.shape
+    dv = v.shape[3]
+    la, b, w, s0 = _f64(log_decay), _f64(erase), _f64(write), _f64(S0)
+    kind = lambda g: 1 if g.shape == (B, T, H, dk) else 0
+    do, ds = _f64(d_o), _f64(d_state)
+    out = dict(dq=np.zeros((B, T, H, dk)), dk=np.zeros((B, T, H, dk)), dv=np.zeros((B, T, H, dv)),
+               d_log_decay=np.zeros(la.shape), d_erase=np.zeros(b.shape),
+               d_write=None if w is None else np.zeros(w.shape),
+               d_state0=np.zeros((B, H, dk, dv)))
+    nthreads = threads or available_cores()
+    rc = _load().gdn2_oracle_bwd(B, T, H, dk, dv, _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(la), kind(la), _ptr(b), kind(b), _ptr(w),
+                                 kind(w) if w is not None else 0, _ptr(s0), float(q_scale),
+                                 _ptr(do), _ptr(ds), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                 _ptr(out["d_log_decay"]), _ptr(out["d_erase"]), _ptr(out["d_write"]),
+                                 _ptr(out["d_state0"]), 0, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"gradient oracle failed with code {rc}")
+    return out
 
 
 def prepare_inputs(q, k, x_decay, x_erase, x_write=None, qk_l2norm=True):

@@ -71,3 +71,48 @@ def pick_chains(w: synth.Workload, n: int, seed: int = 0):
     pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
     idx = r.choice(len(pairs), size=min(n, len(pairs)), replace=False)
     return [pairs[i] for i in sorted(idx)]
+
+
+# An error confined to a few outputs hardly moves a relative L2 norm over a
+# whole chain.  Besides the rel-L2 bound, each chain's largest element error,
+# relative to the chain's RMS, is bounded by MAX_ELEM_FACTOR times the
+# tolerance (measured rel-L2 sits well below the tolerance, and the largest
+# of ~5e5 roughly Gaussian element errors is about 5 of their RMS), so a
+# single wholly wrong element -- an error of the order of the RMS itself --
+# fails the check.
+MAX_ELEM_FACTOR = 10.0
+
+
+def chain_errors(x, ref, chain_axes):
+    """Per-chain relative L2 error of ``x`` against ``ref`` and per-chain
+    largest |x - ref| relative to the chain's RMS of ``ref``; the chain is
+    what ``chain_axes`` (the within-chain axes) sum over."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    d = x - ref
+    num = np.sqrt((d * d).sum(axis=chain_axes))
+    den = np.sqrt((ref * ref).sum(axis=chain_axes))
+    count = int(np.prod([ref.shape[a] for a in chain_axes]))
+    safe = np.where(den > 0, den, 1.0)
+    rel = np.where(den > 0, num / safe, num)
+    mx = np.abs(d).max(axis=chain_axes) / np.where(den > 0, safe / np.sqrt(count), 1.0)
+    return rel, mx
+
+
+def check_every_chain(label, tensors, tol):
+    """Assert, for every (name, x, ref, chain_axes) in ``tensors``, that x is
+    finite, that the whole tensor and every chain meet the relative-L2
+    tolerance, and that no chain's largest element error exceeds
+    MAX_ELEM_FACTOR * tol times its RMS.  Prints the worst chain of each."""
+    for name, x, ref, axes in tensors:
+        assert np.isfinite(np.asarray(x)).all(), f"{label} {name}: non-finite values"
+        rel, mx = chain_errors(x, ref, axes)
+        overall = rel_l2(x, ref)
+        worst = tuple(int(i) for i in np.unravel_index(int(np.argmax(rel)), rel.shape))
+        print(f"  {label} {name}: {rel.size} chains, rel_l2 overall {overall:.3e}, worst chain "
+              f"{worst} {rel.max():.3e}, largest element error {mx.max():.3e} x chain RMS", flush=True)
+        assert overall <= tol, f"{label} {name}: overall rel_l2 {overall:.3e} > {tol:.0e}"
+        assert rel.max() <= tol, f"{label} {name}: chain {worst} rel_l2 {rel.max():.3e} > {tol:.0e}"
+        assert mx.max() <= MAX_ELEM_FACTOR * tol, (
+            f"{label} {name}: an element error of {mx.max():.3e} x chain RMS "
+            f"(bound {MAX_ELEM_FACTOR * tol:.0e})")

@@ -277,6 +277,10 @@ def test_bwd_checks(lib):
     assert bwd(lib, d, dv=DO) == 5                   # gradient on top of d_o
     assert bwd(lib, good(dk=129), wsb=0) == 4
     assert bwd(lib, good(chunk=8), wsb=0) == 4
+    # d_o is fp32 whatever o_dtype says (a forward's descriptor reused with a
+    # bf16 o): a gradient in the upper half of d_o still overlaps it
+    dobytes = 2 * 128 * 4 * 128 * 4
+    assert bwd(lib, good(o_dtype=1), dv=DO + dobytes // 2 + 256) == 5
 
 
 def test_value_write_form_checks(lib):
@@ -417,3 +421,5 @@ def test_bwd_varlen_workspace_and_checks(lib):
     assert bwd_varlen(lib, d, ws=None) == 6
     assert bwd_varlen(lib, d, dq=CU - 256) == 5                # a gradient over the offsets
     assert bwd_varlen(lib, d, ds0=S0 + 3 * 4 * 128 * 128 * 4 - 256) == 5  # d_state0 over state0 ([N,H,dk,dv])
+    # d_o [T,H,dv] is fp32 whatever o_dtype says
+    assert bwd_varlen(lib, good(batch=N, seqlen=T, o_dtype=1), dq=DO + T * H * 128 * 4 - 64) == 5

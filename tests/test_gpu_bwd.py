@@ -13,7 +13,7 @@ import pytest
 
 from gated_delta_rule_decay_amd import synth
 from oracle.oracle_bwd import gdn2_backward
-from tests.parity_util import rel_l2, to_device
+from tests.parity_util import check_every_chain, rel_l2, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -137,7 +137,35 @@ def test_empty_sequence_passes_the_state_gradient():
     assert torch.equal(g["d_state0"], d_st)
 
 
-def test_full_size_sampled_chains():
-    # the full GDN-2 workload (B8 H16 T4096, d128): every chain runs, two are checked
+def _bwd_full(w, inp, d_o, d_st):
+    import torch
+    from gated_delta_rule_decay_amd import chunk_bwd
+
+    d = to_device(inp)
+    g = chunk_bwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"],
+                  torch.from_numpy(d_o).cuda(), torch.from_numpy(d_st).cuda(), chunk=w.chunk)
+    torch.cuda.synchronize()
+    return {k: (None if v is None else v.cpu().numpy()) for k, v in g.items()}
+
+
+def test_full_size_every_chain():
+    # the full GDN-2 workload (B8 H16 T4096, d128), every one of its 128
+    # chains against the hand-written fp64 reverse pass of the C oracle
+    # (pinned to finite differences and to autograd), per chain; and the
+    # same call again, bit for bit
+    from oracle.oracle import gdn2_backward_c
+
     w = W[2]
-    _compare(*_run(w, synth.make_inputs(w, wid=2), 64, seed=530, chains=[(0, 3), (7, 12)]))
+    inp = synth.make_inputs(w, wid=2)
+    r = np.random.Generator(np.random.PCG64(530))
+    d_o = r.standard_normal((w.B, w.T, w.H, w.dv)).astype(np.float32)
+    d_st = r.standard_normal((w.B, w.H, w.dk, w.dv)).astype(np.float32)
+    got = _bwd_full(w, inp, d_o, d_st)
+    ref = gdn2_backward_c(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"],
+                          inp["S0"], d_o, d_st)
+    tok = (1, 3)   # [B,T,H,d]: a chain is (b, h)
+    check_every_chain("gdn2-bf16 backward", [(n, got[n], ref[n], (2, 3) if n == "d_state0" else tok)
+                                             for n in NAMES], TOL)
+    again = _bwd_full(w, inp, d_o, d_st)
+    for n in NAMES:
+        assert np.array_equal(got[n], again[n]), f"{n} differs between two identical calls"

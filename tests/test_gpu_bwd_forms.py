@@ -95,6 +95,28 @@ def test_value_write_general_shapes(gates):
     _run(w, inp, 16, seed=812, vw=True)
 
 
+def test_value_write_head_gate_run_to_run_bitwise():
+    # the general path's per-head write gradient of the value-write form is a
+    # sum over value channels: taken in a fixed order, two calls agree bit for bit
+    import torch
+    from gated_delta_rule_decay_amd import chunk_bwd
+
+    w = W[2].scaled(B=2, T=70, H=2, dk=48, dv=80, qkv_dtype="f32", gates="head")
+    inp = synth.make_inputs(w, seed=815)
+    _value_gate(inp, "write", w, 816, raw=False)
+    r = np.random.Generator(np.random.PCG64(817))
+    d_o = _dev(r.standard_normal((w.B, w.T, w.H, w.dv)))
+    d_st = _dev(r.standard_normal((w.B, w.H, w.dk, w.dv)))
+    args = [_dev(inp[n]) for n in ("q", "k", "v", "log_decay", "erase", "write", "S0")]
+    runs = []
+    for _ in range(3):
+        g = chunk_bwd(*args, d_o, d_st, chunk=16, value_write=True)
+        torch.cuda.synchronize()
+        runs.append({k: v.cpu().numpy() for k, v in g.items() if v is not None})
+    for n in runs[0]:
+        assert np.array_equal(runs[0][n], runs[1][n]) and np.array_equal(runs[0][n], runs[2][n]), n
+
+
 @pytest.mark.parametrize("gates,tied", [("key", False), ("head", True)])
 def test_raw_inputs_d128(gates, tied):
     w = W[2].scaled(B=1, T=90, H=2, gates=gates, tied=tied)

@@ -8,7 +8,7 @@ sequence start at its first token; the last one is ragged), the general fp32
 kernel, empty sequences, the value-write form and fused input preparation,
 the exact path, and at the full GDN-2 size: equal lengths against the
 batched forward (bit-exact: the same chunks through the same kernels) and a
-drawn length mix on sampled (sequence, head) pairs.  The backward over packed
+drawn length mix on every (sequence, head) chain.  The backward over packed
 sequences (gdn2_chunk_bwd_varlen) likewise: every sequence's gradients against
 the gradient oracle on that sequence alone (both paths, the value-write form
 and fused input preparation), and bit-exact against the batched backward at
@@ -19,7 +19,7 @@ import pytest
 
 from gated_delta_rule_decay_amd import synth
 from oracle.oracle import gdn2_forward, gdn2_forward_raw
-from tests.parity_util import TOL_BF16, TOL_F32, rel_l2
+from tests.parity_util import MAX_ELEM_FACTOR, TOL_BF16, TOL_F32, chain_errors, rel_l2
 
 pytestmark = pytest.mark.gpu
 W = synth.WORKLOADS
@@ -193,16 +193,30 @@ def test_full_size_equal_lengths_match_batched():
     assert torch.equal(flat(o_b), o_p) and torch.equal(S_b, S_p)
 
 
-def test_full_size_length_mix_sampled():
+def test_full_size_length_mix_every_sequence():
     # 32768 tokens (the GDN-2 workload's 8 x 4096) cut into 12 drawn lengths,
-    # 16 heads; (sequence, head) pairs sampled against the oracle, among them
-    # the longest and the shortest sequence
+    # 16 heads: every (sequence, head) chain against the oracle run on that
+    # sequence alone, per chain (and its largest element error)
     w = W[2]
     lengths = synth.draw_lengths(w.B * w.T, 12, seed=950)
     inp = synth.make_packed_inputs(w, lengths, seed=951)
-    ln = np.array(lengths)
-    pairs = [(int(ln.argmax()), 3), (int(ln.argmin()), 11), (5, 0), (9, 15)]
-    _check(inp, TOL_BF16, pairs=pairs)
+    o, S = _run(inp)
+    cu = inp["cu_seqlens"]
+    rel, big = [], []
+    for i in range(len(lengths)):
+        o_ref, S_ref = _oracle_seq(inp, i)
+        parts = [(S[i], S_ref, (1, 2))]
+        if o_ref is not None:
+            parts.append((o[cu[i]:cu[i + 1]], o_ref, (0, 2)))
+        for x, ref, axes in parts:
+            assert np.isfinite(x).all()
+            r_, m_ = chain_errors(x, ref, axes)
+            rel.append(r_)
+            big.append(m_)
+    rel, big = np.concatenate(rel), np.concatenate(big)
+    print(f"  lengths {lengths}: {rel.size} (sequence, head) checks of o and S, worst rel_l2 {rel.max():.3e}, "
+          f"largest element error {big.max():.3e} x chain RMS", flush=True)
+    assert rel.max() <= TOL_BF16 and big.max() <= MAX_ELEM_FACTOR * TOL_BF16
 
 
 # ---- the backward over packed sequences ------------------------------------

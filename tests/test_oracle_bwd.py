@@ -280,3 +280,67 @@ def test_raw_gradients_by_the_chain_rule():
         np.testing.assert_allclose(g_raw[key], want, rtol=1e-10, atol=1e-12)
     for key in ("dv", "d_state0"):
         np.testing.assert_allclose(g_raw[key], g[key], rtol=1e-12, atol=1e-12)
+
+
+# ---- the hand-written reverse pass of the C oracle (gdn2_backward_c) -------
+# It serves the full-size GPU gradient checks, where autograd's tape would be
+# too slow and too large.  It is pinned to central finite differences of the
+# C forward (a different program from the one it differentiates by hand) and
+# to the autograd gradients above, for every gate kind, tied and untied, with
+# segment boundaries of its checkpointed recomputation inside the sequence.
+
+def _c_loss(inp, d_o, d_state, qs):
+    o, S = gdn2_forward(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"],
+                        inp["S0"], q_scale=qs, threads=1)
+    return float((o * d_o).sum() + (S * d_state).sum())
+
+
+@pytest.mark.parametrize("gates,tied", [("key", False), ("head", False), ("key", True), ("head", True)])
+def test_c_reverse_pass_equals_finite_differences_of_the_c_forward(gates, tied):
+    from oracle.oracle import gdn2_backward_c
+
+    r = np.random.Generator(np.random.PCG64(900 + 2 * tied + (gates == "head")))
+    inp = _case(r, B=1, T=5, H=2, dk=3, dv=2, gates=gates, tied=tied)
+    d_o = r.standard_normal((1, 5, 2, 2))
+    d_state = r.standard_normal((1, 2, 3, 2))
+    qs = 0.8
+    g = gdn2_backward_c(**inp, d_o=d_o, d_state=d_state, q_scale=qs, threads=1)
+    names = [("q", "dq"), ("k", "dk"), ("v", "dv"), ("log_decay", "d_log_decay"), ("erase", "d_erase"),
+             ("S0", "d_state0")] + ([] if tied else [("write", "d_write")])
+    h = 1e-6
+    for key, gkey in names:
+        x = inp[key]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _c_loss(inp, d_o, d_state, qs)
+            x[idx] = old - h
+            lm = _c_loss(inp, d_o, d_state, qs)
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g[gkey], fd, rtol=1e-6, atol=1e-7, err_msg=gkey)
+
+
+@pytest.mark.parametrize("gates,tied,T", [("key", False, 150), ("head", False, 64), ("key", True, 129),
+                                          ("head", True, 1)])
+def test_c_reverse_pass_equals_autograd(gates, tied, T):
+    from oracle.oracle import gdn2_backward_c
+
+    r = np.random.Generator(np.random.PCG64(950 + T))
+    inp = _case(r, B=2, T=T, H=2, dk=6, dv=5, gates=gates, tied=tied)
+    d_o = r.standard_normal((2, T, 2, 5))
+    d_state = r.standard_normal((2, 2, 6, 5))
+    a = gdn2_backward(**inp, d_o=d_o, d_state=d_state, q_scale=0.6)
+    c = gdn2_backward_c(**inp, d_o=d_o, d_state=d_state, q_scale=0.6, threads=2)
+    for n in ("dq", "dk", "dv", "d_log_decay", "d_erase", "d_write", "d_state0"):
+        if a[n] is None:
+            assert c[n] is None
+            continue
+        np.testing.assert_allclose(c[n], a[n], rtol=1e-10, atol=1e-12, err_msg=n)
+    # no cotangent of o, no initial state: only the final state's gradient flows
+    inp["S0"] = None
+    a = gdn2_backward(**inp, d_o=None, d_state=d_state)
+    c = gdn2_backward_c(**inp, d_o=None, d_state=d_state)
+    for n in ("dq", "dk", "dv", "d_log_decay", "d_erase", "d_state0"):
+        np.testing.assert_allclose(c[n], a[n], rtol=1e-10, atol=1e-12, err_msg=n)

@@ -14,14 +14,18 @@ the definition that a plausible mistake would break:
 * with no erase the recurrence is decayed linear attention, checked by an
   O(T^2) sum over all token pairs;
 * with unit keys and b = 1 the key reads back (sum_c w_c k_c^2) v exactly;
-* reductions: tied scalar gates give the Gated DeltaNet step written in that
-  page's own form (decay, error against the decayed read, rank-one write);
+* reductions: tied scalar gates give the Gated DeltaNet step, written here
+  element by element from its defining property (decay, then a correction
+  along the key sized by the rate times the gap between the value and the
+  decayed state's prediction for the key);
   per-channel decay with a tied scalar rate gives KDA; a = 1 gives the delta
   rule (gist.science summary, "Technische Samenvatting", section 1);
 * splitting a sequence and resuming from the final state equals one call
   (affine composition, "Gated DeltaNet" page, "What makes the architecture
   more than a recurrence").
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -126,18 +130,35 @@ def test_full_erase_reads_back_the_written_value():
 
 
 def _gdn_reference(q, k, v, alpha_log, beta, S0):
-    """The Gated DeltaNet step as that page writes it: decay the state, take
-    the error against the decayed read, add a beta-scaled rank-one write.
-    ``alpha_log`` is [B,T,H] (scalar) or [B,T,H,dk] (KDA's per-channel decay)."""
+    """Gated DeltaNet / KDA / the delta rule from their defining property,
+    element by element: the new state is the decayed old one plus a
+    correction along the key, sized by beta times the gap between the value
+    and what the decayed state predicts for the key,
+        S'[c, j] = a_c S[c, j] + beta k_c (v_j - sum_i a_i k_i S[i, j]),
+    and the output reads the new state with the query, o_j = sum_c q_c S'[c, j].
+    ``alpha_log`` is [B,T,H] (one decay per head) or [B,T,H,dk] (one per key
+    channel).  Plain loops over every index: an independent spelling of the
+    update, not the oracle's operation order."""
     B, T, H, dk = k.shape
+    dv = v.shape[3]
     S = S0.copy()
     o = np.zeros(v.shape)
-    for t in range(T):
-        a = np.exp(alpha_log[:, t])
-        decayed = (a[..., :, None] if a.ndim == 3 else a[..., None, None]) * S
-        err = v[:, t] - np.einsum("bhcv,bhc->bhv", decayed, k[:, t])
-        S = decayed + beta[:, t][..., None, None] * k[:, t][..., :, None] * err[..., None, :]
-        o[:, t] = np.einsum("bhcv,bhc->bhv", S, q[:, t])
+    for b in range(B):
+        for h in range(H):
+            st = S[b, h]
+            for t in range(T):
+                a = [math.exp(alpha_log[b, t, h, c] if alpha_log.ndim == 4 else alpha_log[b, t, h])
+                     for c in range(dk)]
+                kk, qq, vv, bt = k[b, t, h], q[b, t, h], v[b, t, h], beta[b, t, h]
+                pred = [sum(a[i] * kk[i] * st[i, j] for i in range(dk)) for j in range(dv)]
+                new = np.empty((dk, dv))
+                for c in range(dk):
+                    for j in range(dv):
+                        new[c, j] = a[c] * st[c, j] + bt * kk[c] * (vv[j] - pred[j])
+                st = new
+                for j in range(dv):
+                    o[b, t, h, j] = sum(qq[c] * st[c, j] for c in range(dk))
+            S[b, h] = st
     return o, S
 
 

@@ -52,25 +52,35 @@ __constant__ int kOffJ[6] = {0, 0, 1, 0, 1, 2};
 __constant__ int kPair[4][4] = {{-1, -1, -1, -1}, {0, -1, -1, -1}, {1, 2, -1, -1}, {3, 4, 5, -1}};
 }  // namespace
 
-// Raw gate rows held in registers: 4 key channels per row when the gates are
-// per key channel (KEYG), one value per row when per head.
+// Gate kinds of a request, one compile-time code GK: 0 every gate one value
+// per token-head; 1 every gate per key channel; 2 the decay per key channel
+// and the erase / write rates per token-head (KDA's gates: per-channel decay,
+// one rate per head).
+constexpr bool decay_key(int GK) { return GK != 0; }
+constexpr bool rate_key(int GK) { return GK == 1; }
+
+// Raw gate rows held in registers: 4 key channels per row when a gate is
+// per key channel, one value per row when per head.
 template <bool KEYG>
 struct GateRow;
 template <>
 struct GateRow<true> {
+    static constexpr bool key = true;
     f4 x[RPS];
 };
 template <>
 struct GateRow<false> {
+    static constexpr bool key = false;
     float x[RPS];
 };
 
 // Raw inputs of one chunk held in registers: thread (seg, cq) owns rows
 // RPS*seg.. and key channels 4cq..4cq+3; NV 16-byte pieces of values.
-template <bool KEYG, int NV>
+template <int GK, int NV>
 struct Raw {
     uint2 k[RPS], q[RPS];
-    GateRow<KEYG> la, eb, wr;
+    GateRow<decay_key(GK)> la;
+    GateRow<rate_key(GK)> eb, wr;
     uint4 v[NV];
 };
 
@@ -201,43 +211,45 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chain_rsrc(const void *base, c
 }
 
 // Issue the key, query and gate loads of one chunk (no waits).
-template <bool TIED, bool KEYG, int NV>
-__device__ __forceinline__ void load_kqg(Raw<KEYG, NV> &R, const ChunkArgs &a, int64_t b, int64_t h,
-                                         int64_t t0, int seg, int cq) {
-    const auto rk = chain_rsrc(a.k, a, b, h, t0, D, 2, 0);
-    const auto rq = chain_rsrc(a.q, a, b, h, t0, D, 2, 0);
-    const int gw = KEYG ? D : 1;
-    const auto rla = chain_rsrc(a.la, a, b, h, t0, gw, 4, 0);
-    const auto reb = chain_rsrc(a.eb, a, b, h, t0, gw, 4, 0);
-    const auto rwr = chain_rsrc(TIED ? a.eb : a.wr, a, b, h, t0, gw, 4, 0);
-    const int rowk = static_cast<int>(a.H) * D;  // elements between consecutive tokens
-    const int rowg = static_cast<int>(a.H) * gw;
+// Row i of my segment of one fp32 gate (per key channel or per head) into
+// `x`, from the buffer resource `rs` over the chunk's rows (no wait).
+template <bool KEY>
+__device__ __forceinline__ void load_gate_row(GateRow<KEY> &x, __amdgpu_buffer_rsrc_t rs, int row_elems,
+                                              int seg, int cq) {
 #pragma unroll
     for (int i = 0; i < RPS; ++i) {
         const int r = seg * RPS + i;
-        const int ok = (r * rowk + 4 * cq) * 2;
+        if constexpr (KEY)
+            x.x[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rs, (r * row_elems + 4 * cq) * 4, 0, 0));
+        else
+            x.x[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, r * row_elems * 4, 0, 0));
+    }
+}
+
+template <bool TIED, int GK, int NV>
+__device__ __forceinline__ void load_kqg(Raw<GK, NV> &R, const ChunkArgs &a, int64_t b, int64_t h,
+                                         int64_t t0, int seg, int cq) {
+    const auto rk = chain_rsrc(a.k, a, b, h, t0, D, 2, 0);
+    const auto rq = chain_rsrc(a.q, a, b, h, t0, D, 2, 0);
+    const int ga = decay_key(GK) ? D : 1, gr = rate_key(GK) ? D : 1;
+    const int rowk = static_cast<int>(a.H) * D;  // elements between consecutive tokens
+#pragma unroll
+    for (int i = 0; i < RPS; ++i) {
+        const int ok = ((seg * RPS + i) * rowk + 4 * cq) * 2;
         R.k[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, ok, 0, 0));
         R.q[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq, ok, 0, 0));
-        if constexpr (KEYG) {
-            const int og = (r * rowg + 4 * cq) * 4;
-            R.la.x[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rla, og, 0, 0));
-            R.eb.x[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(reb, og, 0, 0));
-            if (!TIED) R.wr.x[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rwr, og, 0, 0));
-        } else {
-            const int og = r * rowg * 4;
-            R.la.x[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rla, og, 0, 0));
-            R.eb.x[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(reb, og, 0, 0));
-            if (!TIED) R.wr.x[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rwr, og, 0, 0));
-        }
     }
+    load_gate_row(R.la, chain_rsrc(a.la, a, b, h, t0, ga, 4, 0), static_cast<int>(a.H) * ga, seg, cq);
+    load_gate_row(R.eb, chain_rsrc(a.eb, a, b, h, t0, gr, 4, 0), static_cast<int>(a.H) * gr, seg, cq);
+    if (!TIED) load_gate_row(R.wr, chain_rsrc(a.wr, a, b, h, t0, gr, 4, 0), static_cast<int>(a.H) * gr, seg, cq);
 }
 
 // Running log2-decay of my RPS rows (relative to the start of my segment);
 // the segment total goes to segtot[seg].
 // With logits, rows past the end of the sequence (which load as zero
 // logits, i.e. a real decay of 1/2) are given no decay: nvalid = T - t0.
-template <typename SM, bool KEYG, int NV>
-__device__ __forceinline__ void segment_cumsum(SM &S, const Raw<KEYG, NV> &R, f4 (&g)[RPS], int seg,
+template <typename SM, int GK, int NV>
+__device__ __forceinline__ void segment_cumsum(SM &S, const Raw<GK, NV> &R, f4 (&g)[RPS], int seg,
                                                int cq, int logits = 0, int64_t nvalid = C) {
     f4 run = splat(0.f);
 #pragma unroll
@@ -299,8 +311,8 @@ __device__ __forceinline__ float half_wave_sum(float x) {
 // along k; TIED holds) the row operand is b k and the column operand k.
 // With `logits` the gates are activated here; with `qknorm` every row of k
 // and q is divided by its L2 norm (the 32 lanes of a segment hold a row).
-template <typename SM, bool TIED, bool KEYG, int NV, bool VW = false>
-__device__ __forceinline__ void factored_operands(SM &S, const Raw<KEYG, NV> &R, f4 (&g)[RPS],
+template <typename SM, bool TIED, int GK, int NV, bool VW = false>
+__device__ __forceinline__ void factored_operands(SM &S, const Raw<GK, NV> &R, f4 (&g)[RPS],
                                                   f4 (&khf)[RPS], f4 (&qhf)[RPS], f4 &egm, int seg,
                                                   int cq, float qs, int logits = 0, int qknorm = 0) {
     static_assert(!VW || TIED, "the value-write form erases and writes along the same vector");

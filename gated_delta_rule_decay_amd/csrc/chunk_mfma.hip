@@ -1,7 +1,8 @@
 // chunk_mfma.hip -- chunkwise GDN-2 forward on the gfx950 matrix cores.
 //
-// Covers bf16 q/k/v with dk = dv = 128 and chunk C = 64, every gate of one
-// kind (all per key channel or all per head), tied or untied write gate.
+// Covers bf16 q/k/v with dk = dv = 128 and chunk C = 64, the gates all per
+// key channel, all per head, or the decay per key channel with per-head
+// erase / write rates (KDA's gates), tied or untied write gate.
 // One workgroup of 512 lanes (8 waves, two per SIMD) owns one (batch, head)
 // chain and a VT-wide slice of the value channels, and walks the chunks of
 // the sequence in order; the fp32 state slice (128 x VT) lives in MFMA
@@ -73,8 +74,8 @@ struct Smem {
 
 // Issue every load of one chunk (no waits: the values are first used by the
 // next chunk's prep).
-template <int VT, bool TIED, bool KEYG>
-__device__ __forceinline__ void load_raw(Raw<KEYG, 1> &R, const ChunkArgs &a, int64_t b, int64_t h,
+template <int VT, bool TIED, int GK>
+__device__ __forceinline__ void load_raw(Raw<GK, 1> &R, const ChunkArgs &a, int64_t b, int64_t h,
                                          int64_t t0, int col0, int seg, int cq, int tid) {
     load_kqg<TIED>(R, a, b, h, t0, seg, cq);
     const auto rv = chain_rsrc(a.v, a, b, h, t0, D, 2, col0);
@@ -86,7 +87,7 @@ __device__ __forceinline__ void load_raw(Raw<KEYG, 1> &R, const ChunkArgs &a, in
     }
 }
 
-template <int VT, bool TIED, bool KEYG>
+template <int VT, bool TIED, int GK>
 __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, int xcd_map) {
     __shared__ Smem<VT> S;
     constexpr int NCT = VT / 16;       // value column tiles
@@ -137,8 +138,8 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
         }
     }
 
-    Raw<KEYG, 1> R;
-    load_raw<VT, TIED, KEYG>(R, a, b, h, 0, col0, tid >> 5, tid & 31, tid);
+    Raw<GK, 1> R;
+    load_raw<VT, TIED, GK>(R, a, b, h, 0, col0, tid >> 5, tid & 31, tid);
 
     for (int64_t t0 = 0; t0 < a.T; t0 += C) {
         __syncthreads();  // previous chunk done with every buffer
@@ -195,7 +196,7 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
         }
         // prefetch the next chunk while this one is computed (rows past the
         // end come back as zeros)
-        load_raw<VT, TIED, KEYG>(R, a, b, h, t0 + C, col0, seg, cq, tid);
+        load_raw<VT, TIED, GK>(R, a, b, h, t0 + C, col0, seg, cq, tid);
 
         // Chunk-row outputs (X, M, O: C x VT): wave wv owns row block
         // rb = wv/2 and NCTW value tiles, so its row-side fragment is read
@@ -428,29 +429,34 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
     }
 }
 
-template <int VT, bool TIED, bool KEYG>
+template <int VT, bool TIED, int GK>
 hipError_t launch_vt(const ChunkArgs &a, hipStream_t s) {
     const int nt = D / VT;
     const int64_t chains = a.B * a.H;
     const int xcd_map = (chains % 8 == 0) ? 1 : 0;
     const dim3 grid(static_cast<unsigned>(chains * nt));
-    hipLaunchKernelGGL((chunk_mfma_kernel<VT, TIED, KEYG>), grid, dim3(NTH), 0, s, a, nt, xcd_map);
+    hipLaunchKernelGGL((chunk_mfma_kernel<VT, TIED, GK>), grid, dim3(NTH), 0, s, a, nt, xcd_map);
     return hipGetLastError();
+}
+
+template <int VT, bool TIED>
+hipError_t launch_tied(const ChunkArgs &a, hipStream_t s) {
+    const int gk = !a.la_key ? 0 : a.eb_key ? 1 : 2;
+    return gk == 1 ? launch_vt<VT, TIED, 1>(a, s) : gk == 2 ? launch_vt<VT, TIED, 2>(a, s) : launch_vt<VT, TIED, 0>(a, s);
 }
 
 template <int VT>
 hipError_t launch_kind(const ChunkArgs &a, hipStream_t s) {
-    const bool tied = a.wr == nullptr, keyg = a.la_key != 0;
-    if (tied) return keyg ? launch_vt<VT, true, true>(a, s) : launch_vt<VT, true, false>(a, s);
-    return keyg ? launch_vt<VT, false, true>(a, s) : launch_vt<VT, false, false>(a, s);
+    return a.wr == nullptr ? launch_tied<VT, true>(a, s) : launch_tied<VT, false>(a, s);
 }
 
 }  // namespace
 
 bool chunk_mfma_supported(const ChunkArgs &a) {
-    // every present gate of one kind (all per key channel or all per head)
+    // the erase and write gates of one kind, the decay of that kind or per
+    // key channel (gate kinds 0, 1, 2)
     const bool tied = a.wr == nullptr;
-    const bool same = a.la_key == a.eb_key && (tied || a.wr_key == a.eb_key);
+    const bool same = (a.la_key || !a.eb_key) && (tied || a.wr_key == a.eb_key);
     return a.bf16 && a.dk == D && a.dv == D && a.C == C && same && !a.value_write && !a.gate_logits && !a.qk_norm &&
            !a.cu &&
            a.H * D * 4 * C < (int64_t(1) << 31);

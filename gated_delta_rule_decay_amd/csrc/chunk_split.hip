@@ -29,6 +29,7 @@
 // range is flagged by pass 1; pass 2 runs it as the exact fp32 token
 // recurrence on the raw inputs instead (so does a chunk whose state or erase
 // read would overflow fp16).
+#include <type_traits>
 #include <utility>
 
 #include "chunk_common.h"
@@ -126,14 +127,16 @@ __device__ __forceinline__ TaskPos task_pos(const ChunkArgs &a, const SplitWs &w
     return p;
 }
 
-template <int PART, bool TIED, bool KEYG, bool VW = false, bool RAW = false>
-__device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, const TaskPos &tp0, int tid) {
+template <int PART, bool TIED, int GK, bool VW = false, bool RAW = false>
+__device__ __forceinline__ void load_part(Raw<GK, 2> &R, const ChunkArgs &a, const TaskPos &tp0, int tid) {
     const bool logits = RAW && a.gate_logits;  // bf16 gate logits (fused input preparation)
     const int64_t b = 0, h = tp0.h, t0 = tp0.t0, tl = tp0.tlim;
     const int seg = tid >> 5, cq = tid & 31;
-    const int gw = KEYG ? D : 1;
-    const int rowk = static_cast<int>(a.H) * D, rowg = static_cast<int>(a.H) * gw;
-    auto gates = [&](GateRow<KEYG> &x, const float *src) {
+    const int rowk = static_cast<int>(a.H) * D;
+    auto gates = [&](auto &x, const float *src) {
+        constexpr bool KEYG = std::decay_t<decltype(x)>::key;  // this gate per key channel
+        const int gw = KEYG ? D : 1;
+        const int rowg = static_cast<int>(a.H) * gw;
         if (logits) {  // bf16 logits: raw bits, activated where used
             const auto rs = chain_rsrc(src, a, b, h, t0, gw, 2, 0, tl);
 #pragma unroll
@@ -171,6 +174,8 @@ __device__ __forceinline__ void load_part(Raw<KEYG, 2> &R, const ChunkArgs &a, c
             // write gate of my two tokens' 8 value columns (per channel) or
             // of my two tokens (per head), into the unused wr registers
             // (bf16 logits: the 8 columns of token i in wr.x[2i])
+            constexpr bool KEYG = rate_key(GK);
+            const int gw = KEYG ? D : 1, rowg = static_cast<int>(a.H) * gw;
             const int es = logits ? 2 : 4;
             const auto rw = chain_rsrc(a.wr, a, b, h, t0, gw, es, 0, tl);
 #pragma unroll
@@ -265,7 +270,7 @@ __device__ __forceinline__ bool wq_tiles(const PrepSmem &S, _Float16 *rec, int k
     return big;
 }
 
-template <bool TIED, bool KEYG, bool VW, bool RAW>
+template <bool TIED, int GK, bool VW, bool RAW>
 __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w, int nc) {
     // RAW: fused input preparation (bf16 gate logits and / or q, k normalised here)
     const int logits = RAW ? a.gate_logits : 0, qknorm = RAW ? a.qk_norm : 0;
@@ -283,16 +288,16 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
     }
     if (tid == 0) S.wide = 0;
 
-    Raw<KEYG, 2> R;
+    Raw<GK, 2> R;
     int64_t task = blockIdx.x;
     TaskPos cur{0, 0, 0};
     if (task < ntask) {
         const TaskPos p0 = task_pos(a, w, task, nc);
         cur = p0;
-        load_part<0, TIED, KEYG, VW, RAW>(R, a, p0, tid);
-        load_part<1, TIED, KEYG, VW, RAW>(R, a, p0, tid);
-        load_part<2, TIED, KEYG, VW, RAW>(R, a, p0, tid);
-        load_part<3, TIED, KEYG, VW, RAW>(R, a, p0, tid);
+        load_part<0, TIED, GK, VW, RAW>(R, a, p0, tid);
+        load_part<1, TIED, GK, VW, RAW>(R, a, p0, tid);
+        load_part<2, TIED, GK, VW, RAW>(R, a, p0, tid);
+        load_part<3, TIED, GK, VW, RAW>(R, a, p0, tid);
     }
 
     for (; task < ntask; task += gridDim.x) {
@@ -316,7 +321,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             auto wg = [&](int i, int e, int s) -> float {
                 if constexpr (!VW) {
                     return 1.f;
-                } else if constexpr (KEYG) {
+                } else if constexpr (rate_key(GK)) {
                     if (logits) {  // column 2e+s of token i: half s of word e
                         const uint32_t u = __float_as_uint(R.wr.x[2 * i][e]);
                         return sigmoid_gate(__uint_as_float(s ? (u & 0xffff0000u) : (u << 16)));
@@ -345,7 +350,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
 
         // ---- factored fp16 Gram operands -------------------------------------
         f4 khf[RPS], qhf[RPS], egm;
-        factored_operands<PrepSmem, TIED, KEYG, 2, VW>(S, R, g, khf, qhf, egm, seg, cq, a.q_scale, logits, qknorm);
+        factored_operands<PrepSmem, TIED, GK, 2, VW>(S, R, g, khf, qhf, egm, seg, cq, a.q_scale, logits, qknorm);
         const int64_t next = task + gridDim.x;  // prefetched in four parts below
         TaskPos pn = task_pos(a, w, next < ntask ? next : task, nc);
         // Without a next task the loads still issue, over an empty range (they
@@ -353,7 +358,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         // has the same memory operations in flight, so the waits before the
         // first use of each part count only what was issued after it.
         if (next >= ntask) pn.tlim = pn.t0;
-        load_part<0, TIED, KEYG, VW, RAW>(R, a, pn, tid);
+        load_part<0, TIED, GK, VW, RAW>(R, a, pn, tid);
         __syncthreads();
 
         const bool wide = S.wide != 0;  // read by all before any later write
@@ -381,7 +386,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 *reinterpret_cast<h4 *>(&S.qh[r * KP + 4 * cq]) = to_h4(qhf[i] * egm);
             }
         }
-        load_part<1, TIED, KEYG, VW, RAW>(R, a, pn, tid);
+        load_part<1, TIED, GK, VW, RAW>(R, a, pn, tid);
 
         _Float16 *rec = w.frag + task * REC;
         bool big = false;
@@ -453,7 +458,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             if (big) S.wide = 1;
         }
         __syncthreads();  // U complete in u16
-        load_part<2, TIED, KEYG, VW, RAW>(R, a, pn, tid);
+        load_part<2, TIED, GK, VW, RAW>(R, a, pn, tid);
         if (!wide) {
             // ---- (4) Oe^T[ct, :] = V^T P^T - U^T R^T -> HBM (transposed, so
             //      the scan's output tiles hold adjacent columns per lane)
@@ -497,7 +502,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             }
             if (big) S.wide = 1;
         }
-        load_part<3, TIED, KEYG, VW, RAW>(R, a, pn, tid);
+        load_part<3, TIED, GK, VW, RAW>(R, a, pn, tid);
         __syncthreads();
         // e^gC per key channel; a chunk to be run exactly is marked by -1 in
         // channel 0 (e^gC is never negative)
@@ -554,7 +559,7 @@ constexpr int scan_threads(int mode) { return 64 * (SCAN_P + (mode ? 2 : 1) * SC
 // columns, from the raw inputs (the fallback when a chunk leaves the fp16
 // range; the columns of F drop the write term).  Kept out of line: its
 // registers do not burden the scan's fast path.
-template <bool TIED, bool KEYG, bool VW, bool WITH_O>
+template <bool TIED, int GK, bool VW, bool WITH_O>
 __device__ __noinline__ void exact_chunk(ChunkArgs a, f4 *sacc, int64_t h, int64_t t0, int64_t tlim, int ct,
                                          int lr, int lg, bool frun) {
     const uint16_t *kp = static_cast<const uint16_t *>(a.k);
@@ -564,8 +569,8 @@ __device__ __noinline__ void exact_chunk(ChunkArgs a, f4 *sacc, int64_t h, int64
         const int64_t row = (t0 + r) * a.H + h;
         // gates of channel c of this token (per channel or per head;
         // bf16 logits activated here)
-        auto gate = [&](const float *g, int c, int act) {
-            return load_gate_x(g, KEYG, row, D, c, a.gate_logits, act);
+        auto gate = [&](const float *g, int c, int act) {  // act 0: the decay, 1: a rate
+            return load_gate_x(g, act == 0 ? decay_key(GK) : rate_key(GK), row, D, c, a.gate_logits, act);
         };
         // 1 / ||k||, 1 / ||q|| of this token when normalised in the kernel
         float ik = 1.f, iq = 1.f;
@@ -664,7 +669,7 @@ __device__ __forceinline__ int seq_of(const int *pre, int n, int q) {
 // MODE 0: the scan proper (O and, for the last segment, the final state).
 // MODE 1: segment summaries; SCAN_W more compute waves carry the columns of
 // F (the first SCAN_W carry the state), no Qe / Oe / O.
-template <bool TIED, bool KEYG, bool VW, int MODE>
+template <bool TIED, int GK, bool VW, int MODE>
 __global__ void __launch_bounds__(scan_threads(MODE))
 chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     constexpr bool WITH_O = MODE == 0;
@@ -893,7 +898,7 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
             f4 st[8];
 #pragma unroll
             for (int it = 0; it < 8; ++it) st[it] = sacc[it];
-            exact_chunk<TIED, KEYG, VW, WITH_O>(a, st, h, t0, tlim, ct, lr, lg, frun);
+            exact_chunk<TIED, GK, VW, WITH_O>(a, st, h, t0, tlim, ct, lr, lg, frun);
 #pragma unroll
             for (int it = 0; it < 8; ++it) sacc[it] = st[it];
             // leave nothing of this (rare) path outstanding, so that the fast
@@ -1173,7 +1178,7 @@ int cu_count() {
     return n;
 }
 
-template <bool TIED, bool KEYG, bool VW = false>
+template <bool TIED, int GK, bool VW = false>
 hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
     const Layout l = a.cu ? layout_varlen(a.B, a.H, a.T) : layout(a.B, a.H, a.T);
     char *p = static_cast<char *>(ws);
@@ -1213,14 +1218,14 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
     const int nc = static_cast<int>(l.nc);
     const int64_t g1 = l.ntask < cu_count() ? l.ntask : cu_count();
     if (a.gate_logits || a.qk_norm)
-        hipLaunchKernelGGL((chunk_prep_kernel<TIED, KEYG, VW, true>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s, a, w, nc);
+        hipLaunchKernelGGL((chunk_prep_kernel<TIED, GK, VW, true>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s, a, w, nc);
     else
-        hipLaunchKernelGGL((chunk_prep_kernel<TIED, KEYG, VW, false>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s, a, w, nc);
+        hipLaunchKernelGGL((chunk_prep_kernel<TIED, GK, VW, false>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s, a, w, nc);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.cu) {  // packed: the units are bounded on the host, counted on the device
         const int64_t u1 = a.H * l.q1b, uc = a.H * l.c2b, u0 = a.H * (a.B + l.q1b);
-        hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG, VW, 1>), dim3(static_cast<unsigned>(u1 * 2)),
+        hipLaunchKernelGGL((chunk_scan_kernel<TIED, GK, VW, 1>), dim3(static_cast<unsigned>(u1 * 2)),
                            dim3(scan_threads(1)), 0, s, a, w, nc, sp, u1 % 8 == 0 ? 1 : 0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (uc > 0) {
@@ -1228,13 +1233,13 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
                                s, sp.xs, sp.fs, 0, sp, static_cast<int>(a.B), static_cast<int>(a.H));
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
-        hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG, VW, 0>), dim3(static_cast<unsigned>(u0 * 2)),
+        hipLaunchKernelGGL((chunk_scan_kernel<TIED, GK, VW, 0>), dim3(static_cast<unsigned>(u0 * 2)),
                            dim3(scan_threads(0)), 0, s, a, w, nc, sp, u0 % 8 == 0 ? 1 : 0);
         return hipGetLastError();
     }
     if (l.nseg > 1) {
         const int64_t units = l.chains * (l.nseg - 1);
-        hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG, VW, 1>), dim3(static_cast<unsigned>(units * 2)),
+        hipLaunchKernelGGL((chunk_scan_kernel<TIED, GK, VW, 1>), dim3(static_cast<unsigned>(units * 2)),
                            dim3(scan_threads(1)), 0, s, a, w, nc, sp, units % 8 == 0 ? 1 : 0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (l.nseg > 2) {
@@ -1244,7 +1249,7 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
         }
     }
     const int64_t units = l.chains * l.nseg;
-    hipLaunchKernelGGL((chunk_scan_kernel<TIED, KEYG, VW, 0>), dim3(static_cast<unsigned>(units * 2)),
+    hipLaunchKernelGGL((chunk_scan_kernel<TIED, GK, VW, 0>), dim3(static_cast<unsigned>(units * 2)),
                        dim3(scan_threads(0)), 0, s, a, w, nc, sp, units % 8 == 0 ? 1 : 0);
     return hipGetLastError();
 }
@@ -1252,10 +1257,11 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
 }  // namespace
 
 bool chunk_split_supported(const ChunkArgs &a) {
-    // every present gate of one kind (all per channel or all per head); the
-    // kernels index tasks (chain * chunks + chunk) with 32-bit arithmetic
+    // the erase and write gates of one kind, the decay of that kind or per
+    // key channel (gate kinds 0, 1, 2); the kernels index tasks (chain *
+    // chunks + chunk) with 32-bit arithmetic
     const bool tied = a.wr == nullptr;
-    const bool same = a.la_key == a.eb_key && (tied || a.wr_key == a.eb_key);
+    const bool same = (a.la_key || !a.eb_key) && (tied || a.wr_key == a.eb_key);
     const int64_t ntask = a.cu ? a.H * ((a.T + C - 1) / C + a.B) : a.B * a.H * ((a.T + C - 1) / C);
     return a.bf16 && a.dk == D && a.dv == D && a.C == C && same && (!a.value_write || !tied) &&
            a.H * D * 4 * C < (int64_t(1) << 31) && ntask > 0 && ntask < (int64_t(1) << 31);
@@ -1268,10 +1274,16 @@ size_t chunk_split_workspace_varlen(int64_t N, int64_t H, int64_t T) {
 }
 
 hipError_t launch_chunk_split(const ChunkArgs &a, void *ws, hipStream_t s) {
-    const bool tied = a.wr == nullptr, keyg = a.la_key != 0;
-    if (a.value_write) return keyg ? launch_kinds<true, true, true>(a, ws, s) : launch_kinds<true, false, true>(a, ws, s);
-    if (tied) return keyg ? launch_kinds<true, true>(a, ws, s) : launch_kinds<true, false>(a, ws, s);
-    return keyg ? launch_kinds<false, true>(a, ws, s) : launch_kinds<false, false>(a, ws, s);
+    const bool tied = a.wr == nullptr;
+    const int gk = !a.la_key ? 0 : a.eb_key ? 1 : 2;
+    if (a.value_write)
+        return gk == 1 ? launch_kinds<true, 1, true>(a, ws, s)
+             : gk == 2 ? launch_kinds<true, 2, true>(a, ws, s) : launch_kinds<true, 0, true>(a, ws, s);
+    if (tied)
+        return gk == 1 ? launch_kinds<true, 1>(a, ws, s)
+             : gk == 2 ? launch_kinds<true, 2>(a, ws, s) : launch_kinds<true, 0>(a, ws, s);
+    return gk == 1 ? launch_kinds<false, 1>(a, ws, s)
+         : gk == 2 ? launch_kinds<false, 2>(a, ws, s) : launch_kinds<false, 0>(a, ws, s);
 }
 
 }  // namespace gdn2

@@ -208,6 +208,10 @@ def test_workspace_query(lib):
     assert query(lib, good()) == split_bytes(2, 4, 128)
     assert query(lib, good(seqlen=100)) == split_bytes(2, 4, 100)
     assert query(lib, good(tied=True, decay_kind=0, erase_kind=0)) == split_bytes(2, 4, 128)
+    # KDA's gates: the decay per key channel, the rates one per head
+    assert query(lib, good(tied=True, erase_kind=0)) == split_bytes(2, 4, 128)
+    assert query(lib, good(erase_kind=0, write_kind=0)) == split_bytes(2, 4, 128)
+    assert query(lib, good(erase_kind=0, write_kind=1)) == 0          # rates of two kinds
     # long sequences on few chains add the segment states of the two-level scan
     assert query(lib, good(batch=1, seqlen=4096)) == split_bytes(1, 4, 4096) > split_bytes(1, 4, 64) * 64
     assert query(lib, good(batch=1, heads=16, seqlen=65536)) == split_bytes(1, 16, 65536)

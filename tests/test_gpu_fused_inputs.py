@@ -59,6 +59,17 @@ def test_logits_and_norm_bf16_d128(gates, tied, ws):
     _check(w, synth.make_raw_inputs(w, seed=700), ws=ws)
 
 
+@pytest.mark.parametrize("ws", [True, False], ids=["two-pass", "general"])
+def test_kda_gate_logits(ws):
+    # KDA's gates as logits: the decay logit per key channel, one erase-rate
+    # logit per token-head (tied write)
+    w = W[2].scaled(B=1, T=170, H=2, tied=True)
+    inp = synth.make_raw_inputs(w, seed=705)
+    inp["x_erase"] = np.ascontiguousarray(inp["x_erase"][..., 0])
+    inp["x_erase_bf16"] = np.ascontiguousarray(inp["x_erase_bf16"][..., 0])
+    _check(w, inp, ws=ws)
+
+
 def test_logits_without_norm():
     # q, k normalised on the host (the workload recipe), gates as logits
     w = W[2].scaled(B=1, T=150, H=2)

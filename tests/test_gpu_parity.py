@@ -71,6 +71,29 @@ def test_gate_kinds(gates, tied, ws):
     _check(w, synth.make_inputs(w, seed=5 + tied), 64, ws=ws)
 
 
+def _kda_gates(inp, tied):
+    # KDA's gates: the per-channel decay kept, one erase (and write) rate per
+    # token-head (the first channel's draw)
+    inp["erase"] = np.ascontiguousarray(inp["erase"][..., 0])
+    inp["write"] = None if tied else np.ascontiguousarray(inp["write"][..., 0])
+    return inp
+
+
+@pytest.mark.parametrize("ws", PATHS)
+@pytest.mark.parametrize("tied", [True, False])
+def test_kda_gates(tied, ws):
+    w = W[2].scaled(B=2, T=230, H=2)
+    _check(w, _kda_gates(synth.make_inputs(w, seed=61 + tied), tied), 64, ws=ws)
+
+
+def test_kda_gates_exact_chunks():
+    # a KDA chunk flagged for the exact recurrence (state beyond fp16 range)
+    w = W[2].scaled(B=1, T=150, H=2)
+    inp = _kda_gates(synth.make_inputs(w, seed=63), True)
+    inp["S0"] = inp["S0"] * 3.0e5
+    _check(w, inp, 64, ws=True)
+
+
 @pytest.mark.parametrize("ws", PATHS)
 def test_q_scale_and_zero_state(ws):
     w = W[2].scaled(B=1, T=96, H=2, s0_std=0.0)

@@ -11,18 +11,22 @@ import pytest
 
 from gated_delta_rule_decay_amd import synth
 from oracle.oracle import gdn2_forward
-from tests.parity_util import TOL_BF16, TOL_F32, rel_l2, to_device
+from tests.parity_util import TOL_BF16, TOL_F32, check_every_chain, rel_l2, to_device
 
 pytestmark = pytest.mark.gpu
 W = synth.WORKLOADS
 
 
 def _inputs(w, seed, gates="key"):
-    """The workload recipe, with the write gate drawn per value channel."""
-    inp = synth.make_inputs(w.scaled(gates=gates, tied=False), seed=seed)
+    """The workload recipe, with the write gate drawn per value channel
+    (``gates="kda"``: the decay per key channel, the erase and write rates
+    one per token-head)."""
+    inp = synth.make_inputs(w.scaled(gates="head" if gates == "head" else "key", tied=False), seed=seed)
     r = np.random.Generator(np.random.PCG64(seed + 1))
     shape = (w.B, w.T, w.H, w.dv) if gates == "key" else (w.B, w.T, w.H)
     inp["write"] = (1 / (1 + np.exp(-r.standard_normal(shape)))).astype(np.float32)
+    if gates == "kda":
+        inp["erase"] = np.ascontiguousarray(inp["erase"][..., 0])
     return inp
 
 
@@ -56,7 +60,7 @@ def _check(w, inp, chunk, ws=True, tol=None, chains=None):
 
 
 @pytest.mark.parametrize("ws", [True, False], ids=["two-pass", "general"])
-@pytest.mark.parametrize("gates", ["key", "head"])
+@pytest.mark.parametrize("gates", ["key", "head", "kda"])
 def test_bf16_d128(gates, ws):
     w = W[2].scaled(B=1, T=200, H=2)
     _check(w, _inputs(w, 600, gates), 64, ws=ws)
@@ -82,9 +86,20 @@ def test_segmented_scan_and_exact_chunks():
     _check(w, inp, 64, tol=1e-5)
 
 
-def test_full_size_sampled_chains():
+def test_full_size_every_chain():
+    import torch
+    from gated_delta_rule_decay_amd import chunk_fwd
+
     w = W[2]
-    _check(w, _inputs(w, 630), 64, chains=[(1, 5), (6, 14)])
+    inp = _inputs(w, 630)
+    d = to_device(inp)
+    o, S = chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], d["S0"],
+                     chunk=64, value_write=True)
+    torch.cuda.synchronize()
+    o_ref, S_ref = gdn2_forward(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"],
+                                inp["S0"], value_write=True)
+    check_every_chain("gdn2-bf16 value-write form", [("o", o.cpu().numpy(), o_ref, (1, 3)),
+                                                     ("S", S.cpu().numpy(), S_ref, (2, 3))], TOL_BF16)
 
 
 @pytest.mark.parametrize("dk,dv,dtype", [(128, 128, "bf16"), (48, 80, "f32")])

@@ -454,3 +454,48 @@ def test_segmented_scan_exact_chunks():
     w, inp = _bf16_case(52, T=64 * 48, H=1)
     inp["S0"] = inp["S0"] * 3.0e5
     _check(w, inp, 64, ws=True)
+
+
+def test_decode_steps_as_a_replayed_graph():
+    # consecutive decode steps captured as one HIP graph (no memset nodes:
+    # the step launches one kernel and nothing else) and replayed several
+    # times, with eager work and synchronisations between the replays; each
+    # replay reproduces the eager steps bit for bit
+    import torch
+    from gated_delta_rule_decay_amd import recurrent_step
+
+    w = W[4].scaled(B=8, H=4)
+    steps = 20
+    s0 = torch.from_numpy(synth.make_decode_state(w, seed=71)).cuda()
+    inps = [to_device(synth.make_decode_step(w, t, seed=71)) for t in range(steps)]
+    state = s0.clone()
+    outs = torch.empty((steps, w.B, w.H, w.dv), dtype=torch.float32, device="cuda")
+
+    def run():  # kernel launches only: every step writes its own slice of outs
+        for t, d in enumerate(inps):
+            recurrent_step(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], d["write"], state, out=outs[t])
+
+    run()
+    torch.cuda.synchronize()
+    ref_state, ref_outs = state.clone(), outs.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        state.copy_(s0)
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, capture_error_mode="thread_local"):
+        run()
+    for rep in range(3):
+        state.copy_(s0)
+        outs.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(state, ref_state) and torch.equal(outs, ref_outs), f"replay {rep}"
+        # eager work between replays
+        scratch = torch.randn(1 << 20, device="cuda").sum()
+        torch.cuda.synchronize()
+        del scratch

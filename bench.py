@@ -335,6 +335,7 @@ def main():
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain 256 MiB device copy three times (untimed) whose memory counters "
                          "calibrate the profiler's byte counts")
+    ap.add_argument("--no-graph", action="store_true", help="time the decode steps only as single launches")
     ap.add_argument("--plan-out", help="write the order of the library calls here (for --summarize)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="no GPU work: turn the rocprofv3 CSVs under DIR/{trace,fetch,write,mfma} into "
@@ -476,18 +477,19 @@ def main():
         # one replayed graph
         w4 = W[4]
         n = args.decode_steps
-        dec = decode_lines(w4, n, 3, torch, w4.name, graph=True)
-        ge = dec["graph"]
+        dec = decode_lines(w4, n, 3, torch, w4.name, graph=not args.no_graph)
         dh = source_hash(DECODE_SOURCES)
-        result["decode"] = {
-            **line(f"{w4.name}: {w4.B} sequences x H={w4.H}, dk=dv={w4.dk}, fp32 state (256 MiB) in HBM "
-                   f"updated in place, {n} consecutive steps, {dec['pool']} distinct step inputs", dec["eager"],
-                   w4.B, decode_bytes(w4), read_traffic("recurrent_step", w4.name, dh)),
-            "graph": {"ms_per_step": round(ge["ms"], 4), "kernel_ms": round(ge["kms"], 4),
-                      "value": round(w4.B / (ge["ms"] * 1e-3), 1), "unit": "tokens/s",
-                      "roofline": roofline_hbm(decode_bytes(w4), ge["kms"]),
-                      "replays_match_eager_bitwise": ge["matches_eager"],
-                      "what": f"the {n} steps captured as one HIP graph, replayed"}}
+        result["decode"] = line(f"{w4.name}: {w4.B} sequences x H={w4.H}, dk=dv={w4.dk}, fp32 state (256 MiB) in "
+                                f"HBM updated in place, {n} consecutive steps, {dec['pool']} distinct step inputs",
+                                dec["eager"], w4.B, decode_bytes(w4), read_traffic("recurrent_step", w4.name, dh))
+        if "graph" in dec:
+            ge = dec["graph"]
+            result["decode"]["graph"] = {
+                "ms_per_step": round(ge["ms"], 4), "kernel_ms": round(ge["kms"], 4),
+                "value": round(w4.B / (ge["ms"] * 1e-3), 1), "unit": "tokens/s",
+                "roofline": roofline_hbm(decode_bytes(w4), ge["kms"]),
+                "replays_match_eager_bitwise": ge["matches_eager"],
+                "what": f"the {n} steps captured as one HIP graph, replayed"}
         # the same step with a 1 GiB state (1024 sequences): beyond the 256 MB
         # Infinity Cache, so every step streams the state from HBM
         w5 = w4.scaled(B=1024, name="gdn2-decode-1gib-bf16")
@@ -748,6 +750,22 @@ def summarize(root: str):
                     f"hbm_bytes_per_launch: {hbm:.0f}"]
             open(os.path.join(PROFILES, f"traffic_{prof}.txt"), "w").write("\n".join(body) + "\n")
             log(f"[summarize] wrote profiles/traffic_{prof}.txt")
+    for sub in sorted(os.listdir(root)) if os.path.isdir(root) else []:
+        dd = os.path.join(root, sub)
+        if sub in ("trace", "fetch", "write", "mfma") or not os.path.exists(os.path.join(dd, "plan.json")):
+            continue
+        doc = json.load(open(os.path.join(dd, "plan.json")))
+        att = attribute(read_dispatches(dd), doc)
+        names = sorted({c for _, calls in att for x in calls[0] for c in x["counters"]})
+        lines = [f"# rocprofv3 counters per dispatch (median over the line's calls), MI355X (gfx950), one GPU",
+                 f"# command (repo root): {_header_cmd(dd)}",
+                 "line | kernel | " + " | ".join(names)]
+        for ln, calls in att:
+            for pos, x in enumerate(calls[0]):
+                vals = [statistics.median(cl[pos]["counters"].get(c, 0.0) for cl in calls) for c in names]
+                lines.append(f"{ln['label']} | {x['short']} | " + " | ".join(f"{v:.0f}" for v in vals))
+        open(os.path.join(PROFILES, f"counters_{sub}.txt"), "w").write("\n".join(lines) + "\n")
+        log(f"[summarize] wrote profiles/counters_{sub}.txt")
     if "mfma" in runs:
         dd, _, _, att = runs["mfma"]
         lines = ["# MFMA counters per dispatch (median over the line's calls), MI355X (gfx950), one GPU",

@@ -19,11 +19,11 @@ GDN2_F32, GDN2_BF16 = 0, 1
 GDN2_GATE_HEAD, GDN2_GATE_KEY = 0, 1
 GDN2_FORM_KEY, GDN2_FORM_VALUE_WRITE = 0, 1
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_UNSUPPORTED",
-          5: "ERR_ALIAS", 6: "ERR_WORKSPACE", 7: "ERR_HIP"}
+          5: "ERR_ALIAS", 6: "ERR_WORKSPACE", 7: "ERR_HIP", 8: "ERR_SCRATCH"}
 
 # Every entry point include/gdn2.h declares.
 EXPORTS = ("gdn2_abi_version", "gdn2_status_str", "gdn2_chunk_fwd_workspace",
-           "gdn2_chunk_fwd", "gdn2_chunk_fwd_varlen_workspace", "gdn2_chunk_fwd_varlen",
+           "gdn2_chunk_fwd", "gdn2_chunk_fwd_static", "gdn2_chunk_fwd_varlen_workspace", "gdn2_chunk_fwd_varlen",
            "gdn2_chunk_bwd_workspace", "gdn2_chunk_bwd", "gdn2_chunk_bwd_varlen_workspace",
            "gdn2_chunk_bwd_varlen", "gdn2_recurrent_step")
 
@@ -75,6 +75,8 @@ def load_library():
             lib.gdn2_chunk_fwd.restype = ctypes.c_int
             lib.gdn2_chunk_fwd.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp,
                                            ctypes.c_size_t, vp]
+            lib.gdn2_chunk_fwd_static.restype = ctypes.c_int
+            lib.gdn2_chunk_fwd_static.argtypes = [dp, vp, vp, vp, fp, fp, fp, fp, fp, fp, vp]
             lib.gdn2_chunk_fwd_varlen_workspace.restype = ctypes.c_int
             lib.gdn2_chunk_fwd_varlen_workspace.argtypes = [dp, ctypes.POINTER(ctypes.c_size_t)]
             lib.gdn2_chunk_fwd_varlen.restype = ctypes.c_int
@@ -242,6 +244,37 @@ def chunk_fwd(q, k, v, log_decay, erase, write=None, state0=None, chunk=64, q_sc
         _ptr(write), _ptr(state0), _ptr(out), _ptr(state_out), _ptr(ws), ws_bytes, _stream())
     if st != 0:
         raise Gdn2Error(st, "gdn2_chunk_fwd")
+    return out, state_out
+
+
+def chunk_fwd_static(q, k, v, log_decay, erase, write=None, state0=None, chunk=64, q_scale=1.0,
+                     out=None, state_out=None, return_state=True, value_write=False, qk_l2norm=False,
+                     out_dtype=None):
+    """``chunk_fwd`` through gdn2_chunk_fwd_static: the library's static
+    device scratch instead of a workspace.  Allocates nothing when ``out``
+    (and, with ``return_state``, ``state_out``) are given."""
+    import torch
+    B, T, H, dk = k.shape
+    dv = v.shape[-1]
+    odt, o_code = _out_dtype(out, out_dtype)
+    desc = _desc_for(q, k, v, log_decay, erase, write, (B, T, H), B, T, H, chunk, q_scale, value_write,
+                     qk_l2norm, o_code)
+    dev = k.device
+    if state0 is not None:
+        _check(state0, "state0", (B, H, dk, dv), (torch.float32,), dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=odt, device=dev)
+    else:
+        _check(out, "out", (B, T, H, dv), (odt,), dev)
+    if state_out is None and return_state:
+        state_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    elif state_out is not None:
+        _check(state_out, "state_out", (B, H, dk, dv), (torch.float32,), dev)
+    st = load_library().gdn2_chunk_fwd_static(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_decay), _ptr(erase),
+        _ptr(write), _ptr(state0), _ptr(out), _ptr(state_out), _stream())
+    if st != 0:
+        raise Gdn2Error(st, "gdn2_chunk_fwd_static")
     return out, state_out
 
 

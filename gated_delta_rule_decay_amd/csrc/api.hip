@@ -163,6 +163,7 @@ const char *gdn2_status_str(int status) {
         case GDN2_ERR_ALIAS: return "an output overlaps an input";
         case GDN2_ERR_WORKSPACE: return "workspace too small";
         case GDN2_ERR_HIP: return "a HIP launch failed";
+        case GDN2_ERR_SCRATCH: return "request too large for the library's static device scratch";
         default: return "unknown status";
     }
 }
@@ -220,6 +221,44 @@ gdn2_status gdn2_chunk_fwd(const gdn2_desc *d, const void *q, const void *k, con
     const ChunkArgs a = args_of(d, q, k, v, log_decay, erase, write, state0, o, state_out);
     if (a.B * a.H > 0x7fffffffLL) return GDN2_ERR_UNSUPPORTED;
     if (use_ws && need > 0) return hip_status(gdn2::launch_chunk_split(a, workspace, s));
+    if (gdn2::chunk_mfma_supported(a)) return hip_status(gdn2::launch_chunk_mfma(a, s));
+    return hip_status(gdn2::launch_chunk_general(a, s));
+}
+
+gdn2_status gdn2_chunk_fwd_static(const gdn2_desc *d, const void *q, const void *k, const void *v,
+                                  const float *log_decay, const float *erase, const float *write,
+                                  const float *state0, float *o, float *state_out, void *stream) {
+    size_t need = 0;
+    gdn2_status st = gdn2_chunk_fwd_workspace(d, &need);
+    if (st != GDN2_OK) return st;
+    const int64_t T = d->seqlen;
+    const bool work = d->batch * T > 0;
+    if (work && (!q || !k || !v || !log_decay || !erase || !o)) return GDN2_ERR_NULL;
+    if (work && !d->tie_write_to_erase && !write) return GDN2_ERR_NULL;
+    const Sizes sz = sizes_of(d, T);
+    const Span in[] = {span_of(q, sz.qk), span_of(k, sz.qk), span_of(v, sz.v),
+                       span_of(log_decay, sz.la), span_of(erase, sz.eb),
+                       span_of(d->tie_write_to_erase ? nullptr : write, sz.wr)};
+    const Span s_in = span_of(state0, sz.st), s_out = span_of(state_out, sz.st);
+    const Span o_sp = span_of(o, sz.o);
+    for (const Span &x : in) {
+        if (overlap(o_sp, x) || overlap(s_out, x)) return GDN2_ERR_ALIAS;
+    }
+    if (overlap(o_sp, s_in) || overlap(o_sp, s_out)) return GDN2_ERR_ALIAS;
+    if (overlap(s_out, s_in) && s_out.lo != s_in.lo) return GDN2_ERR_ALIAS;
+    if (need > 0 && !gdn2::chunk_split_static_fits(d->batch, d->heads, T)) return GDN2_ERR_SCRATCH;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!work) {
+        if (state_out && state_out != state0)
+            return hip_status(gdn2::launch_state_copy(state0, state_out, sz.st / 4, s));
+        return GDN2_OK;
+    }
+    const ChunkArgs a = args_of(d, q, k, v, log_decay, erase, write, state0, o, state_out);
+    if (a.B * a.H > 0x7fffffffLL) return GDN2_ERR_UNSUPPORTED;
+    // the two-pass kernels through the static scratch; every other request
+    // runs on kernels that use no scratch at all
+    if (need > 0) return hip_status(gdn2::launch_chunk_split_static(a, s));
     if (gdn2::chunk_mfma_supported(a)) return hip_status(gdn2::launch_chunk_mfma(a, s));
     return hip_status(gdn2::launch_chunk_general(a, s));
 }

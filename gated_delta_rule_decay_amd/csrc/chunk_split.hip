@@ -29,6 +29,8 @@
 // range is flagged by pass 1; pass 2 runs it as the exact fp32 token
 // recurrence on the raw inputs instead (so does a chunk whose state or erase
 // read would overflow fp16).
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -69,6 +71,10 @@ struct SplitWs {
     const int2 *vseq;  // [N]    token range [lo, hi) of each sequence
     const int *vpfx;   // [N+1]  chunks before each sequence; vpfx[N]: all chunks
     const int2 *vtab;  // [chunk] first token of each chunk, end of its sequence
+    // B sequences of T tokens: the launch covers chunks c0 .. c0 + nc - 1 of
+    // every chain (a window of the sequences; 0 and all chunks by default),
+    // and record `task` is chunk c0 + task % nc of chain task / nc
+    int c0;
 };
 
 struct PrepSmem {
@@ -121,7 +127,8 @@ __device__ __forceinline__ TaskPos task_pos(const ChunkArgs &a, const SplitWs &w
     } else {
         const uint32_t chain = t / static_cast<uint32_t>(nc), b = chain / H;
         p.h = chain - b * H;
-        p.t0 = static_cast<int64_t>(b) * a.T + static_cast<int64_t>(t - chain * static_cast<uint32_t>(nc)) * C;
+        p.t0 = static_cast<int64_t>(b) * a.T +
+               (static_cast<int64_t>(w.c0) + static_cast<int64_t>(t - chain * static_cast<uint32_t>(nc))) * C;
         p.tlim = static_cast<int64_t>(b) * a.T + a.T;
     }
     return p;
@@ -726,7 +733,7 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         n1 = min(nc, n0 + sp.seg_len);
         task0 = static_cast<int64_t>(chain) * nc;
         tstr = 1;
-        tbase = b * a.T;
+        tbase = b * a.T + static_cast<int64_t>(w.c0) * C;  // the window's first chunk
         tlim = tbase + a.T;
         xbase = (static_cast<int64_t>(chain) * sp.nseg + seg) * D * D;  // slot seg
         xstep = D * D;
@@ -1188,6 +1195,7 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
     w.vseq = nullptr;
     w.vpfx = nullptr;
     w.vtab = nullptr;
+    w.c0 = 0;
     ScanPlan sp;
     sp.nseg = static_cast<int>(l.nseg);
     sp.seg_len = static_cast<int>(l.seg_len);
@@ -1254,7 +1262,138 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ---- the allocation-free form ---------------------------------------------
+// The records live in one file-scope device array instead of a caller's
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends; every call on that GPU shares it (calls that overlap in time
+// on one GPU race).  Nothing in it needs clearing: every record a scan reads
+// is written by the prep launch before it, and the carried state is written
+// before it is read.
+static __device__ __align__(256) unsigned char scratch[STATIC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::atomic<unsigned char *> g_scratch[MAX_DEVICES];  // the array's address on each device
+std::mutex g_scratch_mu;
+
+// The scratch array's device address on the current device, looked up once
+// per device (host code never uses the array's own name as an address).
+hipError_t scratch_address(unsigned char **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+    unsigned char *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            void *addr = nullptr;
+            e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!addr) return hipErrorInvalidSymbol;
+            p = static_cast<unsigned char *>(addr);
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+// Windows of the allocation-free form: all ceil(T/64) chunks when their
+// records fit the scratch, else the most that fit beside the carried state
+// (B*H states); 0 when not even one chunk per chain fits.
+struct StaticPlan {
+    int64_t wn, state_bytes;
+};
+
+constexpr int64_t TASK_BYTES = REC * 2 + D * 4;  // one record and its e^gC row
+
+StaticPlan static_plan(int64_t B, int64_t H, int64_t T) {
+    const int64_t nc = (T + C - 1) / C, chains = B * H;
+    StaticPlan p{0, 0};
+    if (chains * nc == 0) return p;
+    if (align256(chains * nc * REC * 2) + align256(chains * nc * D * 4) <= static_cast<int64_t>(STATIC_SCRATCH_BYTES)) {
+        p.wn = nc;
+        return p;
+    }
+    p.state_bytes = align256(chains * D * D * 4);
+    const int64_t room = static_cast<int64_t>(STATIC_SCRATCH_BYTES) - p.state_bytes - 512;
+    p.wn = room > 0 ? room / (chains * TASK_BYTES) : 0;
+    if (p.wn > nc) p.wn = nc;
+    return p;
+}
+
+// One window: chunks c0 .. c0 + n - 1 of every chain, prep then the plain
+// scan from a.s0 (null: zeros) into a.s_out (null: not written).
+template <bool TIED, int GK, bool VW>
+hipError_t launch_window(const ChunkArgs &a, _Float16 *frag, float *gam, int64_t c0, int64_t n, hipStream_t s) {
+    SplitWs w;
+    w.frag = frag;
+    w.gam = gam;
+    w.vseq = nullptr;
+    w.vpfx = nullptr;
+    w.vtab = nullptr;
+    w.c0 = static_cast<int>(c0);
+    ScanPlan sp;
+    sp.nseg = 1;
+    sp.seg_len = static_cast<int>(n);
+    sp.xs = sp.fs = nullptr;
+    sp.qs = sp.q1 = sp.zs = sp.c2 = nullptr;
+    const int64_t ntask = a.B * a.H * n;
+    const int64_t g1 = ntask < cu_count() ? ntask : cu_count();
+    if (a.gate_logits || a.qk_norm)
+        hipLaunchKernelGGL((chunk_prep_kernel<TIED, GK, VW, true>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s,
+                           a, w, static_cast<int>(n));
+    else
+        hipLaunchKernelGGL((chunk_prep_kernel<TIED, GK, VW, false>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s,
+                           a, w, static_cast<int>(n));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t units = a.B * a.H;
+    hipLaunchKernelGGL((chunk_scan_kernel<TIED, GK, VW, 0>), dim3(static_cast<unsigned>(units * 2)),
+                       dim3(scan_threads(0)), 0, s, a, w, static_cast<int>(n), sp, units % 8 == 0 ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <bool TIED, int GK, bool VW = false>
+hipError_t launch_static_kinds(const ChunkArgs &a, hipStream_t s) {
+    unsigned char *base = nullptr;
+    hipError_t e = scratch_address(&base);
+    if (e != hipSuccess) return e;
+    const StaticPlan p = static_plan(a.B, a.H, a.T);
+    if (p.wn < 1) return hipErrorInvalidValue;  // the caller checks static_plan first
+    const int64_t nc = (a.T + C - 1) / C, chains = a.B * a.H;
+    float *carry = reinterpret_cast<float *>(base);  // B*H states when windowed
+    _Float16 *frag = reinterpret_cast<_Float16 *>(base + p.state_bytes);
+    float *gam = reinterpret_cast<float *>(base + p.state_bytes + align256(chains * p.wn * REC * 2));
+    for (int64_t c0 = 0; c0 < nc; c0 += p.wn) {
+        const int64_t n = p.wn < nc - c0 ? p.wn : nc - c0;
+        ChunkArgs aw = a;
+        aw.s0 = c0 == 0 ? a.s0 : carry;                 // each window resumes from the last
+        aw.s_out = c0 + n >= nc ? a.s_out : carry;      // in place: a workgroup reads its slice first
+        if ((e = launch_window<TIED, GK, VW>(aw, frag, gam, c0, n, s)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 }  // namespace
+
+bool chunk_split_static_fits(int64_t B, int64_t H, int64_t T) {
+    return B * H * ((T + C - 1) / C) == 0 || static_plan(B, H, T).wn >= 1;
+}
+
+hipError_t launch_chunk_split_static(const ChunkArgs &a, hipStream_t s) {
+    const bool tied = a.wr == nullptr;
+    const int gk = !a.la_key ? 0 : a.eb_key ? 1 : 2;
+    if (a.value_write)
+        return gk == 1 ? launch_static_kinds<true, 1, true>(a, s)
+             : gk == 2 ? launch_static_kinds<true, 2, true>(a, s) : launch_static_kinds<true, 0, true>(a, s);
+    if (tied)
+        return gk == 1 ? launch_static_kinds<true, 1>(a, s)
+             : gk == 2 ? launch_static_kinds<true, 2>(a, s) : launch_static_kinds<true, 0>(a, s);
+    return gk == 1 ? launch_static_kinds<false, 1>(a, s)
+         : gk == 2 ? launch_static_kinds<false, 2>(a, s) : launch_static_kinds<false, 0>(a, s);
+}
 
 bool chunk_split_supported(const ChunkArgs &a) {
     // the erase and write gates of one kind, the decay of that kind or per

@@ -60,6 +60,15 @@ hipError_t launch_chunk_split(const ChunkArgs &a, void *ws, hipStream_t s);
 // ceil(T/64) + B chunks per head.
 size_t chunk_split_workspace_varlen(int64_t N, int64_t H, int64_t T);
 
+// The two-pass form with its records in the library's static device scratch
+// of STATIC_SCRATCH_BYTES per GPU instead of a workspace (no allocation):
+// the chunks are processed in windows whose records fit, the state carried
+// from window to window in the scratch.  chunk_split_static_fits tells
+// whether one chunk per chain fits at all (B sequences of T tokens).
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(128) << 20;
+bool chunk_split_static_fits(int64_t B, int64_t H, int64_t T);
+hipError_t launch_chunk_split_static(const ChunkArgs &a, hipStream_t s);
+
 // Packed sequences: the plan built on the device from the offsets
 // (varlen.hip), for chunks of C tokens.
 struct VarPlan {

@@ -30,8 +30,10 @@
  *
  * Conventions shared by every call:
  *  - Every data pointer is DEVICE memory (hipMalloc'd or torch CUDA
- *    tensors) owned by the caller; the library allocates nothing, keeps no
- *    global mutable state and is safe to call from several host threads.
+ *    tensors) owned by the caller; the library allocates nothing and is
+ *    safe to call from several host threads.  Its only global state is the
+ *    static scratch of gdn2_chunk_fwd_static and that array's per-GPU
+ *    address, looked up once.
  *  - All tensors are contiguous, row-major, last index fastest:
  *        q, k           [B, T, H, dk]    bf16 or fp32 (desc->qkv_dtype)
  *        v              [B, T, H, dv]    same dtype as q, k
@@ -68,7 +70,7 @@
 extern "C" {
 #endif
 
-#define GDN2_ABI_VERSION 5
+#define GDN2_ABI_VERSION 6
 
 typedef enum gdn2_status {
     GDN2_OK = 0,
@@ -78,7 +80,9 @@ typedef enum gdn2_status {
     GDN2_ERR_UNSUPPORTED = 4, /* valid request no kernel of the library covers  */
     GDN2_ERR_ALIAS = 5,       /* an output overlaps an input (see each call)     */
     GDN2_ERR_WORKSPACE = 6,   /* workspace smaller than the query reported      */
-    GDN2_ERR_HIP = 7          /* a HIP launch or copy failed                     */
+    GDN2_ERR_HIP = 7,         /* a HIP launch or copy failed                     */
+    GDN2_ERR_SCRATCH = 8      /* too large for the static scratch of
+                                 gdn2_chunk_fwd_static                           */
 } gdn2_status;
 
 typedef enum gdn2_dtype { GDN2_F32 = 0, GDN2_BF16 = 1 } gdn2_dtype;
@@ -182,6 +186,33 @@ gdn2_status gdn2_chunk_fwd(const gdn2_desc *desc,
                            const float *log_decay, const float *erase, const float *write,
                            const float *state0, float *o, float *state_out,
                            void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * gdn2_chunk_fwd without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, layouts, rules and result as
+ * gdn2_chunk_fwd with workspace = NULL, except that requests of the
+ * two-pass form keep their per-chunk records in one static device array of
+ * the library, 128 MiB per GPU, held from the first such call on a GPU until
+ * the process ends.  When the records of all ceil(T/64) chunks of every
+ * chain do not fit there, the chunks are processed in consecutive windows
+ * that do, the state carried from window to window in the same array
+ * (more launches, the same arithmetic).  Each record takes 96.5 KiB and
+ * each carried state 64 KiB: a request fits in one window up to
+ * B*H*ceil(T/64) = 1358 records, in windows up to B*H = 816 chains; beyond
+ * both it returns GDN2_ERR_SCRATCH before anything is enqueued.  Requests without a two-pass
+ * kernel run the single-pass kernels, which use no scratch.
+ *
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other host threads) race and give undefined
+ * results; serialise them.  The array needs no initialisation.  The first
+ * call on each GPU looks up the array's device address (hipGetSymbolAddress)
+ * and keeps it; no call allocates or frees memory.
+ */
+gdn2_status gdn2_chunk_fwd_static(const gdn2_desc *desc,
+                                  const void *q, const void *k, const void *v,
+                                  const float *log_decay, const float *erase, const float *write,
+                                  const float *state0, float *o, float *state_out, void *stream);
 
 /* Device workspace, in bytes, for the two-pass form of gdn2_chunk_fwd_varlen
  * on `desc` (batch = N sequences, seqlen = T packed tokens); 0 when the

@@ -36,10 +36,11 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gdn2_abi_version() == 5
-    for s in range(8):
-        assert lib.gdn2_status_str(s)
+    assert lib.gdn2_abi_version() == 6
+    for s in range(9):
+        assert lib.gdn2_status_str(s) != b"unknown status"
     assert lib.gdn2_status_str(0) == b"ok"
+    assert lib.gdn2_status_str(9) == b"unknown status"
 
 
 def test_desc_layout_matches_header():
@@ -427,3 +428,29 @@ def test_bwd_varlen_workspace_and_checks(lib):
     assert bwd_varlen(lib, d, ds0=S0 + 3 * 4 * 128 * 128 * 4 - 256) == 5  # d_state0 over state0 ([N,H,dk,dv])
     # d_o [T,H,dv] is fp32 whatever o_dtype says
     assert bwd_varlen(lib, good(batch=N, seqlen=T, o_dtype=1), dq=DO + T * H * 128 * 4 - 64) == 5
+
+
+def fwd_static(lib, desc, q=Q, k=K, v=V, la=LA, eb=EB, wr=WR, s0=S0, o=O, so=SO):
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.gdn2_chunk_fwd_static(None if desc is None else ctypes.byref(desc), vp(q), vp(k), vp(v), vp(la),
+                                     vp(eb), vp(wr), vp(s0), vp(o), vp(so), None)
+
+
+def test_static_entry_point_checks(lib):
+    # the allocation-free forward validates like gdn2_chunk_fwd, before any
+    # HIP call (so before it looks up its scratch)
+    assert fwd_static(lib, None) == 1
+    assert fwd_static(lib, good(), q=None) == 1
+    assert fwd_static(lib, good(), wr=None) == 1
+    assert fwd_static(lib, good(form=2)) == 2
+    assert fwd_static(lib, good(o_dtype=2)) == 3
+    assert fwd_static(lib, good(dk=129)) == 4
+    assert fwd_static(lib, good(), o=Q + 16) == 5
+    assert fwd_static(lib, good(), so=S0 + 64) == 5
+    assert fwd_static(lib, good(seqlen=0), so=S0) == 0   # nothing to enqueue
+    # the 128 MiB scratch holds 1358 records of 96.5 KiB in one window, or
+    # one chunk per chain beside the carried 64 KiB states of up to 816
+    # chains; beyond both the check answers before any HIP call
+    assert fwd_static(lib, good(batch=1359, heads=1, seqlen=64)) == 8
+    assert fwd_static(lib, good(batch=817, heads=1, seqlen=128)) == 8
+    assert fwd_static(lib, good(batch=205, heads=4, seqlen=65)) == 8

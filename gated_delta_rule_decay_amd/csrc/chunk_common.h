@@ -34,9 +34,16 @@ constexpr int NTH = 512;       // 8 waves
 constexpr int NW = NTH / 64;
 constexpr int NSEG = NTH / 32; // 4-row segments of the chunk (16)
 constexpr int RPS = C / NSEG;  // rows per segment (4)
-constexpr int KP = D + 4;      // pitch (halves) of [token][channel] operands
+// LDS pitches.  Every row of an fp16 or fp32 array starts on a 16-byte
+// boundary (so 8- and 16-byte accesses can be single ds_read/ds_write
+// instructions), and the pitches keep the wide row reads of the MFMA
+// operand fragments free of bank conflicts or nearly so (measured on gfx950:
+// rows 272 bytes apart cost 4 extra cycles per 16-byte read, 264 bytes 12).
+constexpr int KP = D + 8;      // pitch (halves) of [token][channel] operands
 constexpr int SP = C + 8;      // pitch (halves) of [row][token] operands
 constexpr int AP = C + 4;      // pitch (floats) of the fp32 C x C matrix
+constexpr int IP = 18;         // pitch (floats) of the 16x16 inverse scratch
+                               // (read along its rows by the matrix unit)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float MAX_EXP2 = 14.f;        // largest |log2 factor| on the fast path
 constexpr float MAX_OPERAND = 16384.f;  // largest |fp16 operand| on the fast path
@@ -118,6 +125,18 @@ __device__ __forceinline__ f4 bf16x4_to_f4(uint2 p) {
 
 __device__ __forceinline__ f4 splat(float x) { return f4{x, x, x, x}; }
 
+// Vector LDS accesses at the alignment the layouts guarantee (each use's
+// offset is a multiple of the vector's size), so that they compile to single
+// wide ds_read / ds_write instructions rather than pairs of 4-byte accesses.
+template <typename V, typename T>
+__device__ __forceinline__ V lds_ld(const T *p) {
+    return *reinterpret_cast<const V *>(__builtin_assume_aligned(p, sizeof(V)));
+}
+template <typename V, typename T>
+__device__ __forceinline__ void lds_st(T *p, V x) {
+    *reinterpret_cast<V *>(__builtin_assume_aligned(p, sizeof(V))) = x;
+}
+
 // Whether a product about to be rounded to fp16 leaves the fast range (or is
 // not finite).
 __device__ __forceinline__ bool out_of_range(f4 x) {
@@ -156,7 +175,7 @@ __device__ __forceinline__ f4 mfma_f32_block(const float *X, int xp, const float
 // In-place inverse of a unit-lower-triangular 16x16 block I + N held (N
 // strictly lower, zero diagonal) in LDS at `na` with row pitch AP:
 // (I + N)^-1 = (I - N)(I + N^2)(I + N^4)(I + N^8) since N^16 = 0.  One wave;
-// `sa`, `sb` are two private 16x16 fp32 scratch blocks.  The result is written
+// `sa`, `sb` are two private 16x16 fp32 scratch blocks of row pitch IP.  The result is written
 // back to `na` (fp32) and to `th` (fp16, row pitch SP).
 __device__ __forceinline__ void invert_unit_lower16(float *na, _Float16 *th, float *sa, float *sb, int lr,
                                                     int lg) {
@@ -169,23 +188,23 @@ __device__ __forceinline__ void invert_unit_lower16(float *na, _Float16 *th, flo
     // a wave's LDS writes are seen by its later reads, so no barrier is needed
     const f4 n2 = mfma_f32_block(na, AP, na, AP, splat(0.f), lr, lg);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sa[(4 * lg + e) * 16 + lr] = n2[e];
-    const f4 n3 = mfma_f32_block(na, AP, sa, 16, splat(0.f), lr, lg);
+    for (int e = 0; e < 4; ++e) sa[(4 * lg + e) * IP + lr] = n2[e];
+    const f4 n3 = mfma_f32_block(na, AP, sa, IP, splat(0.f), lr, lg);
     const f4 t1 = eye - nn + n2 - n3;  // (I - N)(I + N^2)
-    const f4 n4 = mfma_f32_block(sa, 16, sa, 16, splat(0.f), lr, lg);
+    const f4 n4 = mfma_f32_block(sa, IP, sa, IP, splat(0.f), lr, lg);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        sb[(4 * lg + e) * 16 + lr] = t1[e];
-        sa[(4 * lg + e) * 16 + lr] = n4[e];
+        sb[(4 * lg + e) * IP + lr] = t1[e];
+        sa[(4 * lg + e) * IP + lr] = n4[e];
     }
-    const f4 t2 = mfma_f32_block(sb, 16, sa, 16, t1, lr, lg);  // T1 (I + N^4)
-    const f4 n8 = mfma_f32_block(sa, 16, sa, 16, splat(0.f), lr, lg);
+    const f4 t2 = mfma_f32_block(sb, IP, sa, IP, t1, lr, lg);  // T1 (I + N^4)
+    const f4 n8 = mfma_f32_block(sa, IP, sa, IP, splat(0.f), lr, lg);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        sb[(4 * lg + e) * 16 + lr] = t2[e];
-        sa[(4 * lg + e) * 16 + lr] = n8[e];
+        sb[(4 * lg + e) * IP + lr] = t2[e];
+        sa[(4 * lg + e) * IP + lr] = n8[e];
     }
-    const f4 t3 = mfma_f32_block(sb, 16, sa, 16, t2, lr, lg);  // T2 (I + N^8)
+    const f4 t3 = mfma_f32_block(sb, IP, sa, IP, t2, lr, lg);  // T2 (I + N^8)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         na[(4 * lg + e) * AP + lr] = t3[e];
@@ -257,7 +276,7 @@ __device__ __forceinline__ void segment_cumsum(SM &S, const Raw<GK, NV> &R, f4 (
         if (!logits || seg * RPS + i < nvalid) run += gate4a(R.la, i, logits, 0) * LOG2E;
         g[i] = run;
     }
-    *reinterpret_cast<f4 *>(&S.segtot[seg][4 * cq]) = run;
+    lds_st<f4>(&S.segtot[seg][4 * cq], run);
 }
 
 // Exclusive prefix of the segment totals, in place, one lane per key channel
@@ -317,8 +336,8 @@ __device__ __forceinline__ void factored_operands(SM &S, const Raw<GK, NV> &R, f
                                                   int cq, float qs, int logits = 0, int qknorm = 0) {
     static_assert(!VW || TIED, "the value-write form erases and writes along the same vector");
     const int blk = seg / 4;  // 16-row block of my rows
-    const f4 base = *reinterpret_cast<const f4 *>(&S.segtot[seg][4 * cq]);
-    const f4 gmv = *reinterpret_cast<const f4 *>(&S.segtot[4 * blk + 2][4 * cq]);
+    const f4 base = lds_ld<f4>(&S.segtot[seg][4 * cq]);
+    const f4 gmv = lds_ld<f4>(&S.segtot[4 * blk + 2][4 * cq]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) egm[j] = __builtin_amdgcn_exp2f(gmv[j]);
     bool bad = false;
@@ -354,10 +373,10 @@ __device__ __forceinline__ void factored_operands(SM &S, const Raw<GK, NV> &R, f
             bad |= !(m <= MAX_OPERAND);
         }
         const int r = RPS * seg + i;
-        *reinterpret_cast<h4 *>(&S.kh[r * KP + 4 * cq]) = to_h4(khf[i]);
-        *reinterpret_cast<h4 *>(&S.qh[r * KP + 4 * cq]) = to_h4(qhf[i]);
-        *reinterpret_cast<h4 *>(&S.eh[r * KP + 4 * cq]) = to_h4(ev);
-        if (!TIED) *reinterpret_cast<h4 *>(&S.uh[r * KP + 4 * cq]) = to_h4(uv);
+        lds_st<h4>(&S.kh[r * KP + 4 * cq], to_h4(khf[i]));
+        lds_st<h4>(&S.qh[r * KP + 4 * cq], to_h4(qhf[i]));
+        lds_st<h4>(&S.eh[r * KP + 4 * cq], to_h4(ev));
+        if (!TIED) lds_st<h4>(&S.uh[r * KP + 4 * cq], to_h4(uv));
     }
     if (bad) S.wide = 1;
 }
@@ -373,13 +392,13 @@ __device__ __forceinline__ bool gram_tile(SM &S, int i, int j, int lr, int lg) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const int cb = 32 * ks + 8 * lg;
-        const h8 xk = *reinterpret_cast<const h8 *>(&S.kh[(16 * i + lr) * KP + cb]);
-        const h8 xq = *reinterpret_cast<const h8 *>(&S.qh[(16 * i + lr) * KP + cb]);
-        h8 ye = *reinterpret_cast<const h8 *>(&S.eh[(16 * j + lr) * KP + cb]);
-        h8 yu = TIED ? ye : *reinterpret_cast<const h8 *>(&S.uh[(16 * j + lr) * KP + cb]);
+        const h8 xk = lds_ld<h8>(&S.kh[(16 * i + lr) * KP + cb]);
+        const h8 xq = lds_ld<h8>(&S.qh[(16 * i + lr) * KP + cb]);
+        h8 ye = lds_ld<h8>(&S.eh[(16 * j + lr) * KP + cb]);
+        h8 yu = TIED ? ye : lds_ld<h8>(&S.uh[(16 * j + lr) * KP + cb]);
         if (dj) {
-            const f4 d0 = *reinterpret_cast<const f4 *>(&dj[cb]);
-            const f4 d1 = *reinterpret_cast<const f4 *>(&dj[cb + 4]);
+            const f4 d0 = lds_ld<f4>(&dj[cb]);
+            const f4 d1 = lds_ld<f4>(&dj[cb + 4]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 ye[e] = (_Float16)((float)ye[e] * d0[e]);

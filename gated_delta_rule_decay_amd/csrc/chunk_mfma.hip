@@ -42,7 +42,7 @@ namespace {
 using namespace mfma;
 
 template <int VT>
-struct Smem {
+struct alignas(16) Smem {
     _Float16 kh[C * KP];   // row-side Gram operand k*2^(g-gm); later Kbar
     _Float16 qh[C * KP];   // q*2^(g-gm); later Qbar
     _Float16 eh[C * KP];   // column-side e*2^(gm-g)
@@ -64,7 +64,8 @@ struct Smem {
     _Float16 p16[C * SP];  // P
     union {
         float dtab[6][D];        // 2^(gm_i - gm_j), i > j (Gram phase)
-        float scr[8][16 * 16];   // solve scratch (after the Grams)
+        float scr[8][16 * IP];   // solve scratch (after the Grams); blocks
+                                 // 4..7 serve the diagonal inverses (pitch IP)
     };
     float fsc[4][D];         // 2^(g_C - gm_j)
     float gce[D];            // 2^g_C
@@ -157,7 +158,7 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             sbig |= !(fmaxf(fmaxf(fabsf(sacc[ct][0]), fabsf(sacc[ct][1])), fmaxf(fabsf(sacc[ct][2]), fabsf(sacc[ct][3]))) <= MAX_STATE);
-            *reinterpret_cast<h4 *>(&S.s16[(16 * ct + lr) * KP + 16 * wv + 4 * lg]) = to_h4(sacc[ct]);
+            lds_st<h4>(&S.s16[(16 * ct + lr) * KP + 16 * wv + 4 * lg], to_h4(sacc[ct]));
         }
         if (__ballot(sbig) != 0 && lane == 0) S.wide = 1;
         if (tid < C * PPR) {
@@ -190,8 +191,8 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
 #pragma unroll
             for (int i = 0; i < RPS; ++i) {
                 const int r = RPS * seg + i;
-                *reinterpret_cast<h4 *>(&S.kh[r * KP + 4 * cq]) = to_h4(khf[i] * egm);
-                *reinterpret_cast<h4 *>(&S.qh[r * KP + 4 * cq]) = to_h4(qhf[i] * egm);
+                lds_st<h4>(&S.kh[r * KP + 4 * cq], to_h4(khf[i] * egm));
+                lds_st<h4>(&S.qh[r * KP + 4 * cq], to_h4(qhf[i] * egm));
             }
         }
         // prefetch the next chunk while this one is computed (rows past the
@@ -219,23 +220,23 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int cb = 32 * ks + 8 * lg;
-                    const h8 xa = *reinterpret_cast<const h8 *>(&S.kh[(16 * rb + lr) * KP + cb]);
+                    const h8 xa = lds_ld<h8>(&S.kh[(16 * rb + lr) * KP + cb]);
 #pragma unroll
                     for (int n = 0; n < NCTW; ++n)
-                        acc[n] = mfma32(xa, *reinterpret_cast<const h8 *>(&S.s16[(16 * (ct0 + n) + lr) * KP + cb]), acc[n]);
+                        acc[n] = mfma32(xa, lds_ld<h8>(&S.s16[(16 * (ct0 + n) + lr) * KP + cb]), acc[n]);
                 }
                 for (int ks = 0; ks <= (rb >> 1); ++ks) {
                     const int sb = 32 * ks + 8 * lg;
-                    const h8 xa = *reinterpret_cast<const h8 *>(&S.b16[(16 * rb + lr) * SP + sb]);
+                    const h8 xa = lds_ld<h8>(&S.b16[(16 * rb + lr) * SP + sb]);
 #pragma unroll
                     for (int n = 0; n < NCTW; ++n)
-                        acc[n] = mfma32(xa, *reinterpret_cast<const h8 *>(&S.v16[(16 * (ct0 + n) + lr) * SP + sb]), acc[n]);
+                        acc[n] = mfma32(xa, lds_ld<h8>(&S.v16[(16 * (ct0 + n) + lr) * SP + sb]), acc[n]);
                 }
                 bool big = false;
 #pragma unroll
                 for (int n = 0; n < NCTW; ++n) {
                     big |= out_of_range(acc[n]);
-                    *reinterpret_cast<h4 *>(&S.xm16[(16 * (ct0 + n) + lr) * SP + 16 * rb + 4 * lg]) = to_h4(acc[n]);
+                    lds_st<h4>(&S.xm16[(16 * (ct0 + n) + lr) * SP + 16 * rb + 4 * lg], to_h4(acc[n]));
                 }
                 if (__ballot(big) != 0 && lane == 0) S.wide2 = 1;
             }
@@ -249,10 +250,10 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
                 for (int n = 0; n < NCTW; ++n) acc[n] = splat(0.f);
                 for (int ks = 0; ks <= (rb >> 1); ++ks) {
                     const int sb = 32 * ks + 8 * lg;
-                    const h8 xa = *reinterpret_cast<const h8 *>(&S.t16[(16 * rb + lr) * SP + sb]);
+                    const h8 xa = lds_ld<h8>(&S.t16[(16 * rb + lr) * SP + sb]);
 #pragma unroll
                     for (int n = 0; n < NCTW; ++n)
-                        acc[n] = mfma32(xa, *reinterpret_cast<const h8 *>(&S.xm16[(16 * (ct0 + n) + lr) * SP + sb]), acc[n]);
+                        acc[n] = mfma32(xa, lds_ld<h8>(&S.xm16[(16 * (ct0 + n) + lr) * SP + sb]), acc[n]);
                 }
                 bool big = false;
 #pragma unroll
@@ -266,7 +267,7 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
             if (rows_active) {
 #pragma unroll
                 for (int n = 0; n < NCTW; ++n)
-                    *reinterpret_cast<h4 *>(&S.xm16[(16 * (ct0 + n) + lr) * SP + 16 * rb + 4 * lg]) = to_h4(-acc[n]);
+                    lds_st<h4>(&S.xm16[(16 * (ct0 + n) + lr) * SP + 16 * rb + 4 * lg], to_h4(-acc[n]));
             }
             __syncthreads();
 
@@ -278,19 +279,19 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const int cb = 32 * ks + 8 * lg;
-                    const h8 xa = *reinterpret_cast<const h8 *>(&S.qh[(16 * rb + lr) * KP + cb]);
+                    const h8 xa = lds_ld<h8>(&S.qh[(16 * rb + lr) * KP + cb]);
 #pragma unroll
                     for (int n = 0; n < NCTW; ++n)
-                        acc[n] = mfma32(xa, *reinterpret_cast<const h8 *>(&S.s16[(16 * (ct0 + n) + lr) * KP + cb]), acc[n]);
+                        acc[n] = mfma32(xa, lds_ld<h8>(&S.s16[(16 * (ct0 + n) + lr) * KP + cb]), acc[n]);
                 }
                 for (int ks = 0; ks <= (rb >> 1); ++ks) {
                     const int sb = 32 * ks + 8 * lg;
-                    const h8 xp = *reinterpret_cast<const h8 *>(&pp[(16 * rb + lr) * SP + sb]);
-                    const h8 xr = *reinterpret_cast<const h8 *>(&S.r16[(16 * rb + lr) * SP + sb]);
+                    const h8 xp = lds_ld<h8>(&pp[(16 * rb + lr) * SP + sb]);
+                    const h8 xr = lds_ld<h8>(&S.r16[(16 * rb + lr) * SP + sb]);
 #pragma unroll
                     for (int n = 0; n < NCTW; ++n) {
-                        acc[n] = mfma32(xp, *reinterpret_cast<const h8 *>(&S.v16[(16 * (ct0 + n) + lr) * SP + sb]), acc[n]);
-                        acc[n] = mfma32(xr, *reinterpret_cast<const h8 *>(&S.xm16[(16 * (ct0 + n) + lr) * SP + sb]), acc[n]);
+                        acc[n] = mfma32(xp, lds_ld<h8>(&S.v16[(16 * (ct0 + n) + lr) * SP + sb]), acc[n]);
+                        acc[n] = mfma32(xr, lds_ld<h8>(&S.xm16[(16 * (ct0 + n) + lr) * SP + sb]), acc[n]);
                     }
                 }
 #pragma unroll
@@ -328,8 +329,8 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
                     for (int ct = 0; ct < NCT; ++ct) {
                         const int vb = (16 * ct + lr) * SP + 16 * j + 4 * lg;
                         f4 y = splat(0.f);
-                        y = mfma16(au, *reinterpret_cast<const h4 *>(&S.v16[vb]), y);
-                        y = mfma16(ae, *reinterpret_cast<const h4 *>(&S.xm16[vb]), y);
+                        y = mfma16(au, lds_ld<h4>(&S.v16[vb]), y);
+                        y = mfma16(ae, lds_ld<h4>(&S.xm16[vb]), y);
                         sacc[ct] += fs * y;
                     }
                 }

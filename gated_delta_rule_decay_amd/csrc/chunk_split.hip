@@ -77,7 +77,7 @@ struct SplitWs {
     int c0;
 };
 
-struct PrepSmem {
+struct alignas(16) PrepSmem {
     _Float16 kh[C * KP];   // Gram row operand k 2^(g-gm); later Kbar
     _Float16 qh[C * KP];   // q 2^(g-gm); later Qbar
     _Float16 eh[C * KP];   // Gram column operand e 2^(gm-g)
@@ -98,9 +98,10 @@ struct PrepSmem {
     };
     float fsc[4][D];  // 2^(g_C - gm_j)
     float gce[D];     // 2^g_C
-    float iscr[4][2][16 * 16];  // private scratch of the four diagonal inverses
+    float iscr[4][2][16 * IP];  // private scratch of the four diagonal inverses
     int wide;
 };
+static_assert(sizeof(PrepSmem) <= 160 * 1024, "LDS of the prep pass");
 
 // Loads of task `task` in four parts (no waits), so that a task's requests
 // are spread over the previous task instead of arriving at HBM in one burst:
@@ -222,7 +223,7 @@ __device__ __forceinline__ void load_part(Raw<GK, 2> &R, const ChunkArgs &a, con
 // pairs with a B operand built from two accumulator tiles).
 __device__ __forceinline__ h8 perm_frag(const _Float16 *m, int rt, int ks, int lr, int lg) {
     const _Float16 *p = &m[(16 * rt + lr) * SP + 32 * ks + 4 * lg];
-    return join(*reinterpret_cast<const h4 *>(p), *reinterpret_cast<const h4 *>(p + 16));
+    return join(lds_ld<h4>(p), lds_ld<h4>(p + 16));
 }
 
 // W^T and Qe^T = Qbar^T - W^T R^T for key channel tiles 2kb, 2kb+1 and token
@@ -244,7 +245,7 @@ __device__ __forceinline__ bool wq_tiles(const PrepSmem &S, _Float16 *rec, int k
     for (int st = 0; st < NST; ++st)
 #pragma unroll
         for (int ks = 0; ks <= RH; ++ks)
-            tn[st][ks] = *reinterpret_cast<const h8 *>(&S.t16[(16 * st + lr) * SP + 32 * ks + 8 * lg]);
+            tn[st][ks] = lds_ld<h8>(&S.t16[(16 * st + lr) * SP + 32 * ks + 8 * lg]);
     f4 wt[4][2];
 #pragma unroll
     for (int st = 0; st < NST; ++st)
@@ -262,7 +263,7 @@ __device__ __forceinline__ bool wq_tiles(const PrepSmem &S, _Float16 *rec, int k
         for (int cc = 0; cc < 2; ++cc) {
             wT[cc] = mfma32(kbf[cc][0], tn[rt][0], splat(0.f));
             if (RH) wT[cc] = mfma32(kbf[cc][RH], tn[rt][RH], wT[cc]);
-            qT[cc] = to_f4(*reinterpret_cast<const h4 *>(&S.qh[(16 * rt + lr) * KP + 16 * (2 * kb + cc) + 4 * lg]));
+            qT[cc] = to_f4(lds_ld<h4>(&S.qh[(16 * rt + lr) * KP + 16 * (2 * kb + cc) + 4 * lg]));
 #pragma unroll
             for (int ks = 0; ks <= RH; ++ks) {
                 const h8 wa = join(to_h4(wt[2 * ks][cc]), to_h4(wt[2 * ks + 1][cc]));
@@ -345,8 +346,8 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 const _Float16 b0 = (_Float16)(__uint_as_float(r0[e] & 0xffff0000u) * wg(0, e, 1));
                 const _Float16 b1 = (_Float16)(__uint_as_float(r1[e] & 0xffff0000u) * wg(1, e, 1));
                 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-                *reinterpret_cast<h2 *>(&S.v16[(8 * piece + 2 * e) * SP + 2 * tp]) = h2{a0, a1};
-                *reinterpret_cast<h2 *>(&S.v16[(8 * piece + 2 * e + 1) * SP + 2 * tp]) = h2{b0, b1};
+                lds_st<h2>(&S.v16[(8 * piece + 2 * e) * SP + 2 * tp], h2{a0, a1});
+                lds_st<h2>(&S.v16[(8 * piece + 2 * e + 1) * SP + 2 * tp], h2{b0, b1});
             }
         }
         f4 g[RPS];
@@ -389,8 +390,8 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
 #pragma unroll
             for (int i = 0; i < RPS; ++i) {
                 const int r = RPS * seg + i;
-                *reinterpret_cast<h4 *>(&S.kh[r * KP + 4 * cq]) = to_h4(khf[i] * egm);
-                *reinterpret_cast<h4 *>(&S.qh[r * KP + 4 * cq]) = to_h4(qhf[i] * egm);
+                lds_st<h4>(&S.kh[r * KP + 4 * cq], to_h4(khf[i] * egm));
+                lds_st<h4>(&S.qh[r * KP + 4 * cq], to_h4(qhf[i] * egm));
             }
         }
         load_part<1, TIED, GK, VW, RAW>(R, a, pn, tid);
@@ -411,14 +412,14 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             // ---- (1) value tile ct = wv: Y = Bm V, U = Tm Y ------------------
             // vb: V[:, ct] as a B operand, natural token order
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) vb[ks] = *reinterpret_cast<const h8 *>(&S.v16[(16 * ct + lr) * SP + 32 * ks + 8 * lg]);
+            for (int ks = 0; ks < 2; ++ks) vb[ks] = lds_ld<h8>(&S.v16[(16 * ct + lr) * SP + 32 * ks + 8 * lg]);
             f4 y[4];
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 y[rt] = splat(0.f);
 #pragma unroll
                 for (int ks = 0; ks <= (rt >> 1); ++ks)
-                    y[rt] = mfma32(*reinterpret_cast<const h8 *>(&S.b16[(16 * rt + lr) * SP + 32 * ks + 8 * lg]), vb[ks], y[rt]);
+                    y[rt] = mfma32(lds_ld<h8>(&S.b16[(16 * rt + lr) * SP + 32 * ks + 8 * lg]), vb[ks], y[rt]);
                 big |= out_of_range(y[rt]);
             }
             {
@@ -461,7 +462,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             // U -> u16 [j][s] for the value-column products of every wave
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
-                *reinterpret_cast<h4 *>(&S.u16[(16 * ct + lr) * SP + 16 * rt + 4 * lg]) = to_h4(uacc[rt]);
+                lds_st<h4>(&S.u16[(16 * ct + lr) * SP + 16 * rt + 4 * lg], to_h4(uacc[rt]));
             if (big) S.wide = 1;
         }
         __syncthreads();  // U complete in u16
@@ -478,7 +479,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                     acc[rt] = splat(0.f);
 #pragma unroll
                     for (int ks = 0; ks <= (rt >> 1); ++ks) {
-                        acc[rt] = mfma32(vb[ks], *reinterpret_cast<const h8 *>(&pp[(16 * rt + lr) * SP + 32 * ks + 8 * lg]), acc[rt]);
+                        acc[rt] = mfma32(vb[ks], lds_ld<h8>(&pp[(16 * rt + lr) * SP + 32 * ks + 8 * lg]), acc[rt]);
                         acc[rt] = mfma32(ks ? -ub1 : -ub0, perm_frag(S.r16, rt, ks, lr, lg), acc[rt]);
                     }
                     big |= out_of_range(acc[rt]);
@@ -498,8 +499,8 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                     for (int kb = 0; kb < 2; ++kb) {
                         const _Float16 *pv = &S.v16[(16 * c2 + lr) * SP + 32 * kb + 4 * lg];
                         const _Float16 *pu = &S.u16[(16 * c2 + lr) * SP + 32 * kb + 4 * lg];
-                        const h8 vp = join(*reinterpret_cast<const h4 *>(pv), *reinterpret_cast<const h4 *>(pv + 16));
-                        const h8 up = join(*reinterpret_cast<const h4 *>(pu), *reinterpret_cast<const h4 *>(pu + 16));
+                        const h8 vp = join(lds_ld<h4>(pv), lds_ld<h4>(pv + 16));
+                        const h8 up = join(lds_ld<h4>(pu), lds_ld<h4>(pu + 16));
                         acc = mfma32(uf[kb], vp, acc);
                         acc = mfma32(kb ? ne1 : ne0, up, acc);
                     }

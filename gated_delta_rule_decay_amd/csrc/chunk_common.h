@@ -273,7 +273,8 @@ __device__ __forceinline__ void segment_cumsum(SM &S, const Raw<GK, NV> &R, f4 (
     f4 run = splat(0.f);
 #pragma unroll
     for (int i = 0; i < RPS; ++i) {
-        if (!logits || seg * RPS + i < nvalid) run += gate4a(R.la, i, logits, 0) * LOG2E;
+        const f4 x = gate4a(R.la, i, logits, 0) * LOG2E;
+        run += (!logits || seg * RPS + i < nvalid) ? x : splat(0.f);  // a select, not a branch
         g[i] = run;
     }
     lds_st<f4>(&S.segtot[seg][4 * cq], run);

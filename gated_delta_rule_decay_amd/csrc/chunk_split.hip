@@ -135,9 +135,9 @@ __device__ __forceinline__ TaskPos task_pos(const ChunkArgs &a, const SplitWs &w
     return p;
 }
 
-template <int PART, bool TIED, int GK, bool VW = false, bool RAW = false>
+template <int PART, bool TIED, int GK, bool VW = false, int RAW = 0>
 __device__ __forceinline__ void load_part(Raw<GK, 2> &R, const ChunkArgs &a, const TaskPos &tp0, int tid) {
-    const bool logits = RAW && a.gate_logits;  // bf16 gate logits (fused input preparation)
+    constexpr bool logits = RAW & 1;  // bf16 gate logits (fused input preparation)
     const int64_t b = 0, h = tp0.h, t0 = tp0.t0, tl = tp0.tlim;
     const int seg = tid >> 5, cq = tid & 31;
     const int rowk = static_cast<int>(a.H) * D;
@@ -278,10 +278,11 @@ __device__ __forceinline__ bool wq_tiles(const PrepSmem &S, _Float16 *rec, int k
     return big;
 }
 
-template <bool TIED, int GK, bool VW, bool RAW>
+template <bool TIED, int GK, bool VW, int RAW>
 __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w, int nc) {
-    // RAW: fused input preparation (bf16 gate logits and / or q, k normalised here)
-    const int logits = RAW ? a.gate_logits : 0, qknorm = RAW ? a.qk_norm : 0;
+    // RAW: fused input preparation, bit 0 the gates as bf16 logits, bit 1 q
+    // and k normalised here (compile-time, so no branch tests either)
+    constexpr int logits = RAW & 1, qknorm = (RAW >> 1) & 1;
     __shared__ PrepSmem S;
     const int tid = threadIdx.x;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -351,7 +352,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             }
         }
         f4 g[RPS];
-        segment_cumsum(S, R, g, seg, cq, logits, RAW ? cur.tlim - cur.t0 : C);
+        segment_cumsum(S, R, g, seg, cq, logits, logits ? cur.tlim - cur.t0 : C);
         __syncthreads();
         if (tid < D) chunk_tables(S, tid);
         __syncthreads();
@@ -1186,6 +1187,17 @@ int cu_count() {
     return n;
 }
 
+// The prep pass for the request's input preparation: plain, or fused with
+// bf16 gate logits and / or in-kernel q, k normalisation (RAW bits 0 and 1).
+template <bool TIED, int GK, bool VW>
+void launch_prep(const ChunkArgs &a, const SplitWs &w, int nc, unsigned grid, hipStream_t s) {
+    const int raw = (a.gate_logits ? 1 : 0) | (a.qk_norm ? 2 : 0);
+    if (raw == 0) hipLaunchKernelGGL((chunk_prep_kernel<TIED, GK, VW, 0>), dim3(grid), dim3(NTH), 0, s, a, w, nc);
+    else if (raw == 1) hipLaunchKernelGGL((chunk_prep_kernel<TIED, GK, VW, 1>), dim3(grid), dim3(NTH), 0, s, a, w, nc);
+    else if (raw == 2) hipLaunchKernelGGL((chunk_prep_kernel<TIED, GK, VW, 2>), dim3(grid), dim3(NTH), 0, s, a, w, nc);
+    else hipLaunchKernelGGL((chunk_prep_kernel<TIED, GK, VW, 3>), dim3(grid), dim3(NTH), 0, s, a, w, nc);
+}
+
 template <bool TIED, int GK, bool VW = false>
 hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
     const Layout l = a.cu ? layout_varlen(a.B, a.H, a.T) : layout(a.B, a.H, a.T);
@@ -1226,10 +1238,7 @@ hipError_t launch_kinds(const ChunkArgs &a, void *ws, hipStream_t s) {
     }
     const int nc = static_cast<int>(l.nc);
     const int64_t g1 = l.ntask < cu_count() ? l.ntask : cu_count();
-    if (a.gate_logits || a.qk_norm)
-        hipLaunchKernelGGL((chunk_prep_kernel<TIED, GK, VW, true>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s, a, w, nc);
-    else
-        hipLaunchKernelGGL((chunk_prep_kernel<TIED, GK, VW, false>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s, a, w, nc);
+    launch_prep<TIED, GK, VW>(a, w, nc, static_cast<unsigned>(g1), s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.cu) {  // packed: the units are bounded on the host, counted on the device
@@ -1342,12 +1351,7 @@ hipError_t launch_window(const ChunkArgs &a, _Float16 *frag, float *gam, int64_t
     sp.qs = sp.q1 = sp.zs = sp.c2 = nullptr;
     const int64_t ntask = a.B * a.H * n;
     const int64_t g1 = ntask < cu_count() ? ntask : cu_count();
-    if (a.gate_logits || a.qk_norm)
-        hipLaunchKernelGGL((chunk_prep_kernel<TIED, GK, VW, true>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s,
-                           a, w, static_cast<int>(n));
-    else
-        hipLaunchKernelGGL((chunk_prep_kernel<TIED, GK, VW, false>), dim3(static_cast<unsigned>(g1)), dim3(NTH), 0, s,
-                           a, w, static_cast<int>(n));
+    launch_prep<TIED, GK, VW>(a, w, static_cast<int>(n), static_cast<unsigned>(g1), s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t units = a.B * a.H;

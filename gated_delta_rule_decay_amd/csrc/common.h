@@ -54,12 +54,19 @@ __device__ __forceinline__ float load_gate(const float *g, int per_key, int64_t 
 
 // Gate activations of the fused input preparation: log a = -softplus(x)
 // (so a = exp(log a) in (0, 1)) and sigmoid(x) for the erase / write gates,
-// with the hardware exp2 / log2 (a few ulp; log(1 + y) for tiny y rounds to
-// 0, an absolute error below 1e-7 in log a).
+// on the hardware exp2 / log2 / reciprocal (about 1 ulp each):
+//   -softplus(x) = -(max(x, 0) + ln 2 * log2(1 + 2^(-|x| log2 e))),
+// where the log2 argument lies in (1, 2] (no denormal or range handling is
+// needed; for large |x| it rounds to 1 and the result is max(x, 0) within
+// 2^-24), and sigmoid(x) = 1 / (1 + 2^(-x log2 e)), which is 0 or 1 where
+// the power overflows or vanishes.
 __device__ __forceinline__ float neg_softplus(float x) {
-    return -(fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x))));
+    const float t = __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f);
+    return -(fmaxf(x, 0.f) + 0.6931471805599453f * __builtin_amdgcn_logf(1.f + t));
 }
-__device__ __forceinline__ float sigmoid_gate(float x) { return __fdividef(1.f, 1.f + __expf(-x)); }
+__device__ __forceinline__ float sigmoid_gate(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
 
 // Gate value of token-head `row` at channel c: the fp32 value as stored, or,
 // with `logits`, the activation of the bf16 logit there (act 0: decay,

@@ -56,9 +56,14 @@
  *    (2048 instead of 2816 bytes per token-head for the full GDN-2 forward).
  *  - Preconditions not checked (they would need a device pass): log_decay
  *    finite and <= 0 (decay gate in (0, 1], course slides "Stability"),
- *    erase/write in [0, 1], all values finite.  On the bf16 path derived
- *    operands are held in fp16 inside the kernel, which also asks
- *    |v| < 2^15 and a state that stays below 2^15 in magnitude.
+ *    erase/write in [0, 1], all values finite.  These hold for every call
+ *    and every path.  The matrix-core forward kernels of gdn2_chunk_fwd,
+ *    gdn2_chunk_fwd_static and gdn2_chunk_fwd_varlen (bf16 q/k/v, dk = dv =
+ *    128) hold derived operands, intermediates and a copy of the state in
+ *    fp16; a chunk whose values would leave fp16's range is recomputed as
+ *    the exact fp32 token recurrence instead, with the workspace and without
+ *    it, so they ask nothing more (tested with |v| and states of 2^15).  The
+ *    backward, the decode step and the fp32 kernels compute in fp32.
  */
 #ifndef GDN2_H
 #define GDN2_H
@@ -141,7 +146,9 @@ const char *gdn2_status_str(int status);
 /* Device workspace, in bytes, for the two-pass form of gdn2_chunk_fwd on
  * `desc`; 0 when the request has no two-pass kernel (it then always runs in
  * one pass).  The two-pass form covers bf16 q/k/v, dk = dv = 128, chunk 64
- * and gates all of one kind; it needs B*H*ceil(T/64) records of about
+ * and gates per key channel or per head (a per-head decay only with
+ * per-head erase and write gates; untied, the write gate of the erase
+ * gate's kind); it needs B*H*ceil(T/64) records of about
  * 97 KiB, and, when B*H is small against T (long sequences on few chains,
  * scanned in parallel segments), two 64 KiB states per (chain, segment).
  * Same validation as gdn2_chunk_fwd. */

@@ -43,7 +43,19 @@ namespace {
 constexpr int BD = 128;   // dk = dv
 constexpr int BC = 16;    // tokens per chunk
 constexpr int BNT = 256;  // threads per workgroup (4 waves x 16 value columns)
-constexpr int RS = 132;   // LDS row stride of the 16 x 128 operands (2-way banked for the reads below)
+constexpr int RS = 132;   // LDS row stride of the scans' 16 x 128 operands
+// LDS layout of the gradient kernel.  The strides follow the measured gfx950
+// LDS banking (32 banks of 4 bytes; a 4-byte access is served per half-wave):
+// GS: 16 x 128 operands, whose rows are read 16 bytes per lane (lane (kq, m)
+//     at row m, column 4 kq) -- a stride of 8 banks mod 32 serves those
+//     without conflict;
+// OS: the raw per-(token, channel) operands, read at token 4 s + kq and
+//     channel 16 w + m -- the two tokens of a half-wave fall 16 banks apart;
+// TP: the record's 16 x 16 matrices, read at row 4 kq + j, column m -- the
+//     two rows of a half-wave fall 16 banks apart.
+constexpr int GS = 136;
+constexpr int OS = 144;
+constexpr int TP = 20;
 typedef float f4 __attribute__((ext_vector_type(4)));
 
 // record of one (chain, chunk), fp32, in this order
@@ -117,7 +129,7 @@ __device__ __forceinline__ BChain bchain(const ChunkArgs &f, const VarPlan &vp, 
 }
 
 // sum_c A[m][c] B[c][n] over the 128 key channels, A row m from LDS (row
-// stride RS) in the channel order of the state registers B; four independent
+// stride GS) in the channel order of the state registers B; four independent
 // accumulation chains (channel 16 it + 4 kq + i goes to chain i), so that the
 // matrix unit never waits on its own previous result for long.
 __device__ __forceinline__ f4 chan_product(const float *A, const f4 (&B)[8], int m, int kq, f4 init) {
@@ -125,7 +137,7 @@ __device__ __forceinline__ f4 chan_product(const float *A, const f4 (&B)[8], int
     f4 acc[4] = {init, z, z, z};
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-        const f4 a4 = *reinterpret_cast<const f4 *>(&A[m * RS + 16 * it + 4 * kq]);
+        const f4 a4 = *reinterpret_cast<const f4 *>(&A[m * GS + 16 * it + 4 * kq]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = mfma4(a4[i], B[it][i], acc[i]);
     }
@@ -617,33 +629,34 @@ __device__ __forceinline__ f4 load4_gate(const float *g, int per_key, int64_t ro
 }
 
 struct GradLds {
-    float kb[BC * RS], et[BC * RS], ut[BC * RS];       // record: Kbar, Etil, Util
-    float tm[BC * BC], bm[BC * BC], rr[BC * BC], pp[BC * BC];
+    float kb[BC * GS], et[BC * GS], ut[BC * GS];       // record: Kbar, Etil, Util
+    float tm[BC * TP], bm[BC * TP], rr[BC * TP], pp[BC * TP];
     float gm[BD];                                        // e^gC, later d gC's exit term
-    float k[BC * KS], q[BC * KS], e[BC * KS], u[BC * KS], g[BC * KS];  // raw operands; running log-decay
+    float k[BC * OS], q[BC * OS], e[BC * OS], u[BC * OS], g[BC * OS];  // raw operands; running log-decay
     float gc[BD];
-    float v[BC * RS], o[BC * RS];                        // V, dO
-    float mm[BC * RS], dm[BC * RS], y[BC * RS], bv[BC * RS];  // M, dM, Y, Bm V; later the per-(x, c) results
-    float dw[BC * RS];
+    float v[BC * GS], o[BC * GS];                        // V, dO
+    float mm[BC * GS], dm[BC * GS], y[BC * GS], bv[BC * GS];  // M, dM, Y, Bm V; later the per-(x, c) results
+    float dw[BC * GS];
     float dt[BC * BC], x1[BC * BC], da[BC * BC], dbm[BC * BC], dr[BC * BC], dp[BC * BC];
     float daT[BC * BC], dbmT[BC * BC], drT[BC * BC], dpT[BC * BC];  // transposes (columns as rows)
     float wpart[8 * BC];  // value-write form, one write gate per head: per-wave partial sums of dw
     int steep;            // some channel decays by more than STEEP within the chunk
 };
+static_assert(sizeof(GradLds) <= 160 * 1024, "gradient kernel LDS exceeds the CU's 160 KiB");
 
 // Largest decay (nats) of a channel over one chunk for which the Gram
 // gradients take the factored form below: its factors e^(+-(g - g_ref)) then
 // stay within fp32's normal range.
 constexpr float STEEP = 80.f;
 
-// 16 x 16 product over 128 columns of two [16][RS] LDS matrices, X Z^T
+// 16 x 16 product over 128 columns of two [16][GS] LDS matrices, X Z^T
 // (lane (kq, n) gets rows 4 kq + r, column n)
 __device__ __forceinline__ f4 gram16(const float *X, const float *Z, int m, int kq) {
     f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jt = 0; jt < 8; ++jt) {
-        const f4 xa = *reinterpret_cast<const f4 *>(&X[m * RS + 16 * jt + 4 * kq]);
-        const f4 zb = *reinterpret_cast<const f4 *>(&Z[m * RS + 16 * jt + 4 * kq]);
+        const f4 xa = *reinterpret_cast<const f4 *>(&X[m * GS + 16 * jt + 4 * kq]);
+        const f4 zb = *reinterpret_cast<const f4 *>(&Z[m * GS + 16 * jt + 4 * kq]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc = mfma4(xa[i], zb[i], acc);
     }
@@ -753,10 +766,10 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
             // the record parts into LDS
 #pragma unroll
             for (int p = 0; p < 3; ++p)
-                *reinterpret_cast<f4 *>(&(p == 0 ? L.kb : p == 1 ? L.et : L.ut)[(tid / 32) * RS + 4 * (tid % 32)]) = xr[p];
+                *reinterpret_cast<f4 *>(&(p == 0 ? L.kb : p == 1 ? L.et : L.ut)[(tid / 32) * GS + 4 * (tid % 32)]) = xr[p];
             if (tid < 256) {
                 float *dst = tid < 64 ? L.tm : tid < 128 ? L.bm : tid < 192 ? L.rr : L.pp;
-                *reinterpret_cast<f4 *>(&dst[4 * (tid & 63)]) = xt;
+                *reinterpret_cast<f4 *>(&dst[((tid & 63) >> 2) * TP + 4 * (tid & 3)]) = xt;
             } else if (tid < 256 + BD) {
                 L.gm[tid - 256] = xg;
             }
@@ -764,28 +777,28 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
             f4 vv = qkv(vw4);
             bb = gate(bw);
             ww = gate(ww4);  // value-write: per value column
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int li = r * KS + c4 + i;
-                L.q[li] = qv[i]; L.g[li] = la[i];
-                L.k[li] = vw ? bb[i] * kv[i] : kv[i];
-                L.e[li] = vw ? kv[i] : bb[i] * kv[i];
-                L.u[li] = vw ? kv[i] : ww[i] * kv[i];
+            {
+                const int li = r * OS + c4;
+                *reinterpret_cast<f4 *>(&L.q[li]) = qv;
+                *reinterpret_cast<f4 *>(&L.g[li]) = la;
+                *reinterpret_cast<f4 *>(&L.k[li]) = vw ? bb * kv : kv;
+                *reinterpret_cast<f4 *>(&L.e[li]) = vw ? kv : bb * kv;
+                *reinterpret_cast<f4 *>(&L.u[li]) = vw ? kv : ww * kv;
             }
             if (vw) {  // the raw values and write gates, for dv and dw after the value products
-                *reinterpret_cast<f4 *>(&L.mm[r * RS + c4]) = vv;
-                *reinterpret_cast<f4 *>(&L.dm[r * RS + c4]) = ww;
+                *reinterpret_cast<f4 *>(&L.mm[r * GS + c4]) = vv;
+                *reinterpret_cast<f4 *>(&L.dm[r * GS + c4]) = ww;
                 vv = vv * ww;
             }
-            *reinterpret_cast<f4 *>(&L.v[r * RS + c4]) = vv;
-            *reinterpret_cast<f4 *>(&L.o[r * RS + c4]) = ov;
+            *reinterpret_cast<f4 *>(&L.v[r * GS + c4]) = vv;
+            *reinterpret_cast<f4 *>(&L.o[r * GS + c4]) = ov;
         }
         lds_barrier();
         if (tid < BD) {  // running log-decay (read only by the last phase)
             float run = 0.f;
             for (int r = 0; r < BC; ++r) {
-                run += L.g[r * KS + tid];
-                L.g[r * KS + tid] = run;
+                run += L.g[r * OS + tid];
+                L.g[r * OS + tid] = run;
             }
             L.gc[tid] = run;
             if (L.g[tid] - run > STEEP) L.steep = 1;
@@ -797,41 +810,41 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
             float v4[4], o4[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                v4[j] = L.v[(4 * kq + j) * RS + col];
-                o4[j] = L.o[(4 * kq + j) * RS + col];
+                v4[j] = L.v[(4 * kq + j) * GS + col];
+                o4[j] = L.o[(4 * kq + j) * GS + col];
             }
             f4 BV = {0.f, 0.f, 0.f, 0.f};
             {
-                const f4 b4 = *reinterpret_cast<const f4 *>(&L.bm[m * BC + 4 * kq]);
+                const f4 b4 = *reinterpret_cast<const f4 *>(&L.bm[m * TP + 4 * kq]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) BV = mfma4(b4[j], v4[j], BV);
             }
             f4 X = chan_product(L.kb, S, m, kq, BV);
             f4 M = {0.f, 0.f, 0.f, 0.f};
             {
-                const f4 t4 = *reinterpret_cast<const f4 *>(&L.tm[m * BC + 4 * kq]);
+                const f4 t4 = *reinterpret_cast<const f4 *>(&L.tm[m * TP + 4 * kq]);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) M = mfma4(t4[j], X[j], M);
             }
             f4 dM = chan_product(L.et, dS, m, kq, f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int j = 0; j < 4; ++j) dM = mfma4(L.rr[(4 * kq + j) * BC + m], o4[j], dM);
+            for (int j = 0; j < 4; ++j) dM = mfma4(L.rr[(4 * kq + j) * TP + m], o4[j], dM);
             dM = -dM;
             f4 Y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) Y = mfma4(L.tm[(4 * kq + j) * BC + m], dM[j], Y);
+            for (int j = 0; j < 4; ++j) Y = mfma4(L.tm[(4 * kq + j) * TP + m], dM[j], Y);
             f4 dV = chan_product(L.ut, dS, m, kq, f4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                dV = mfma4(L.pp[(4 * kq + j) * BC + m], o4[j], dV);
-                dV = mfma4(L.bm[(4 * kq + j) * BC + m], Y[j], dV);
+                dV = mfma4(L.pp[(4 * kq + j) * TP + m], o4[j], dV);
+                dV = mfma4(L.bm[(4 * kq + j) * TP + m], Y[j], dV);
             }
             float wsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tok = 4 * kq + r;
                 if (vw) {  // dV is the gradient of w .* v
-                    const float vr = L.mm[tok * RS + col], wr = L.dm[tok * RS + col];
+                    const float vr = L.mm[tok * GS + col], wr = L.dm[tok * GS + col];
                     if (live(tok)) {
                         a.dv[row_of(tok) * BD + col] = dV[r] * wr;
                         if (wr_key) a.dwr[row_of(tok) * BD + col] = dV[r] * vr;
@@ -840,10 +853,10 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
                 } else if (live(tok)) {
                     a.dv[row_of(tok) * BD + col] = dV[r];
                 }
-                L.mm[tok * RS + col] = M[r];
-                L.dm[tok * RS + col] = dM[r];
-                L.y[tok * RS + col] = Y[r];
-                L.bv[tok * RS + col] = BV[r];
+                L.mm[tok * GS + col] = M[r];
+                L.dm[tok * GS + col] = dM[r];
+                L.y[tok * GS + col] = Y[r];
+                L.bv[tok * GS + col] = BV[r];
             }
             if (vw && !wr_key) {  // one write gate per head: partial sums over this wave's 16 columns
 #pragma unroll
@@ -876,7 +889,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
 #pragma unroll
             for (int jt = 0; jt < 8; ++jt) {
                 const f4 s4 = sr[jt], d4 = dr[jt];
-                const int lo = m * RS + 16 * jt + 4 * kq;
+                const int lo = m * GS + 16 * jt + 4 * kq;
                 const f4 am = *reinterpret_cast<const f4 *>(&L.dm[lo]), ao = *reinterpret_cast<const f4 *>(&L.o[lo]);
                 const f4 ax = *reinterpret_cast<const f4 *>(&L.mm[lo]), av = *reinterpret_cast<const f4 *>(&L.v[lo]);
 #pragma unroll
@@ -895,14 +908,14 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
             __builtin_amdgcn_wave_barrier();
             if (kq == 0) L.gm[c] = dgc;  // only this wave reads channel c's entry
 #pragma unroll
-            for (int r = 0; r < 4; ++r) L.dw[(4 * kq + r) * RS + c] = dW[r];
+            for (int r = 0; r < 4; ++r) L.dw[(4 * kq + r) * GS + c] = dW[r];
         }
         lds_barrier();
 
         // ---- dKbar = Tm^T dW (registers); the 16 x 16 gradients
         f4 dKb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dKb = mfma4(L.tm[(4 * kq + j) * BC + m], dW[j], dKb);
+        for (int j = 0; j < 4; ++j) dKb = mfma4(L.tm[(4 * kq + j) * TP + m], dW[j], dKb);
         if (wv < 4) {
             f4 x;
             float *dst, *dstT;
@@ -938,7 +951,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
         // channel there (V, dO, Kbar, Etil, Util and dW are no longer read)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int li = (4 * kq + r) * RS + c;
+            const int li = (4 * kq + r) * GS + c;
             L.kb[li] = dKb[r];
             L.et[li] = dQb[r];
             L.ut[li] = dEt[r];
@@ -946,13 +959,13 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
         }
         {  // the gates, into the regions of dO and dW (no longer read)
             const int r = tid >> 5, c4 = 4 * (tid & 31);
-            *reinterpret_cast<f4 *>(&L.o[r * RS + c4]) = bb;
-            *reinterpret_cast<f4 *>(&L.dw[r * RS + c4]) = ww;
+            *reinterpret_cast<f4 *>(&L.o[r * GS + c4]) = bb;
+            *reinterpret_cast<f4 *>(&L.dw[r * GS + c4]) = ww;
         }
         if (wv == 0) {  // X1 = Tm^T dT
             f4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x = mfma4(L.tm[(4 * kq + j) * BC + m], L.dt[(4 * kq + j) * BC + m], x);
+            for (int j = 0; j < 4; ++j) x = mfma4(L.tm[(4 * kq + j) * TP + m], L.dt[(4 * kq + j) * BC + m], x);
 #pragma unroll
             for (int r = 0; r < 4; ++r) L.x1[(4 * kq + r) * BC + m] = x[r];
         }
@@ -960,7 +973,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
         if (wv == 0) {  // dA = -X1 Tm^T, strictly lower
             f4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) x = mfma4(L.x1[m * BC + 4 * kq + j], L.tm[m * BC + 4 * kq + j], x);
+            for (int j = 0; j < 4; ++j) x = mfma4(L.x1[m * BC + 4 * kq + j], L.tm[m * TP + 4 * kq + j], x);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = 4 * kq + r;
@@ -980,7 +993,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
         //        gru[x] = sum_y d_xy (dBm[y][x] k_y + dP[y][x] q_y)   (y >= x)
         //      with the pairwise decay d_xy = e^-|g_x - g_y| of channel c.
         {
-            float *dgv = L.mm, *shr = L.dm, *dbs = L.y, *dws = L.bv;  // [16][RS] each, free now
+            float *dgv = L.mm, *shr = L.dm, *dbs = L.y, *dws = L.bv;  // [16][GS] each, free now
             const int cc = 16 * wv + m, x0 = 4 * kq;
             const float gcc = L.gc[cc];
             float glk[4], glq[4], gre[4], gru[4];
@@ -989,28 +1002,30 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
                 // for y <= x (the other way round for y >= x), so the four sums are
                 // 16 x 16 by 16 x 128 products on the matrix cores; every factor is
                 // below e^STEEP.  The B operand of lane (kq, m) is token 4 s + kq of
-                // channel c, the A operand row m of the 16 x 16 gradients.
-                const float gref = L.g[7 * KS + cc];
+                // channel c, the A operand row m of the 16 x 16 gradients, read as
+                // column m of the stored transpose (the half-wave's two tokens
+                // then fall 16 banks apart).
+                const float gref = L.g[7 * OS + cc];
                 const f4 z = {0.f, 0.f, 0.f, 0.f};
                 f4 GLK = z, GLQ = z, GRE = z, GRU = z;
 #pragma unroll
                 for (int s4 = 0; s4 < 4; ++s4) {
-                    const int y = 4 * s4 + kq, ly = y * KS + cc, ay = m * BC + y;
+                    const int y = 4 * s4 + kq, ly = y * OS + cc, ay = y * BC + m;
                     const float gy = L.g[ly];
                     const float fe = __expf(gref - gy), fk = __expf(gy - gref);
                     const float ey = L.e[ly] * fe, uy = L.u[ly] * fe, ky = L.k[ly] * fk, qy = L.q[ly] * fk;
-                    GLK = mfma4(L.da[ay], ey, GLK);
-                    GLQ = mfma4(L.dr[ay], ey, GLQ);
-                    GRE = mfma4(L.daT[ay], ky, GRE);
-                    GRU = mfma4(L.dbmT[ay], ky, GRU);
-                    GLK = mfma4(L.dbm[ay], uy, GLK);
-                    GLQ = mfma4(L.dp[ay], uy, GLQ);
-                    GRE = mfma4(L.drT[ay], qy, GRE);
-                    GRU = mfma4(L.dpT[ay], qy, GRU);
+                    GLK = mfma4(L.daT[ay], ey, GLK);   // dA[m][y]
+                    GLQ = mfma4(L.drT[ay], ey, GLQ);   // dR[m][y]
+                    GRE = mfma4(L.da[ay], ky, GRE);    // dA[y][m]
+                    GRU = mfma4(L.dbm[ay], ky, GRU);   // dBm[y][m]
+                    GLK = mfma4(L.dbmT[ay], uy, GLK);  // dBm[m][y]
+                    GLQ = mfma4(L.dpT[ay], uy, GLQ);   // dP[m][y]
+                    GRE = mfma4(L.dr[ay], qy, GRE);    // dR[y][m]
+                    GRU = mfma4(L.dp[ay], qy, GRU);    // dP[y][m]
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float gx = L.g[(x0 + r) * KS + cc];
+                    const float gx = L.g[(x0 + r) * OS + cc];
                     const float fr = __expf(gx - gref), fc = __expf(gref - gx);
                     glk[r] = fr * GLK[r];
                     glq[r] = fr * GLQ[r];
@@ -1022,7 +1037,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
                 // the operands are read where used (this path is rare)
                 for (int r = 0; r < 4; ++r) {
                     const int x = x0 + r;
-                    const float gx = L.g[x * KS + cc];
+                    const float gx = L.g[x * OS + cc];
                     float sk = 0.f, sq = 0.f, se = 0.f, su = 0.f;
                     for (int jj = 0; jj < 4; ++jj) {
                         const int o4 = x * BC + 4 * jj;
@@ -1032,7 +1047,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
                         const f4 cr = *reinterpret_cast<const f4 *>(&L.drT[o4]), cp = *reinterpret_cast<const f4 *>(&L.dpT[o4]);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const int yy = 4 * jj + e, ly = yy * KS + cc;
+                            const int yy = 4 * jj + e, ly = yy * OS + cc;
                             const float gy = L.g[ly], ey = L.e[ly], uy = L.u[ly], ky = L.k[ly], qy = L.q[ly];
                             const float d = __expf(yy < x ? gx - gy : gy - gx);
                             sk += (ra[e] * ey + rb[e] * uy) * d;
@@ -1050,8 +1065,8 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int x = x0 + r;
-                const float gx = L.g[x * KS + cc];
-                const int li = x * KS + cc, lr = x * RS + cc;
+                const float gx = L.g[x * OS + cc];
+                const int li = x * OS + cc, lr = x * GS + cc;
                 const float kx = L.k[li], qx = L.q[li], ex = L.e[li], ux = L.u[li];
                 const float eg = __expf(gx), ec = __expf(gcc - gx);
                 const float dkb = L.kb[lr], dqb = L.et[lr], det = L.ut[lr], dut = L.v[lr];
@@ -1090,13 +1105,13 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
         // ---- d log a: the reverse running sum of dg, d gC entering at the last row
         if (tid < BD) {
             float run = L.gm[tid];
-            for (int x = 0; x < BC; ++x) run += shr[x * RS + tid];
+            for (int x = 0; x < BC; ++x) run += shr[x * GS + tid];
             for (int x = BC - 1; x >= 0; --x) {
-                run += dgv[x * RS + tid];
+                run += dgv[x * GS + tid];
                 if (la_key) {
                     if (live(x)) a.dla[row_of(x) * BD + tid] = run;
                 } else {
-                    dgv[x * RS + tid] = run;
+                    dgv[x * GS + tid] = run;
                 }
             }
         }
@@ -1106,10 +1121,13 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
             if (tid < BC && live(tid)) {
                 const int x = tid;
                 float sl = 0.f, sb = 0.f, sw = 0.f;
-                for (int cc = 0; cc < BD; ++cc) {
-                    sl += dgv[x * RS + cc];
-                    sb += dbs[x * RS + cc];
-                    sw += dws[x * RS + cc];
+                // channel (j + x) mod 128 at step j: the 16 lanes' rows then fall
+                // on distinct banks (row stride GS is 8 banks mod 32)
+                for (int j = 0; j < BD; ++j) {
+                    const int cc = (j + x) & (BD - 1);
+                    sl += dgv[x * GS + cc];
+                    sb += dbs[x * GS + cc];
+                    sw += dws[x * GS + cc];
                 }
                 const int64_t row = row_of(x);
                 if (!la_key) a.dla[row] = sl;
@@ -1121,7 +1139,6 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
                 if (!tied && !wr_key) a.dwr[row] = sw;
             }
         }
-        // the next task's S and dSo columns, in flight across its staging
         if (task + gridDim.x < ntask) load_sd(task + gridDim.x);
     }
 }

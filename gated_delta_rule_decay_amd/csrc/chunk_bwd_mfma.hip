@@ -1153,7 +1153,9 @@ hipError_t launch_bwd_d128(const BwdArgs &a, const VarPlan &vp, float *rec, floa
     // (packed sequences: the bound on the task count; the kernels read the count)
     const int64_t tasks = f.cu ? f.H * varlen_chunk_bound(f.B, f.T, BC) : f.B * f.H * nch;
     int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
     // the record pass loops over tasks: as many workgroups as can be resident
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, bwd_record_kernel, BNT, 0) != hipSuccess || per_cu < 1)

@@ -385,48 +385,57 @@ __device__ __forceinline__ void factored_operands(SM &S, const Raw<GK, NV> &R, f
 // One 16x16 tile (block row i, block column j <= i) of the four Grams, A/Bm/R/P
 // sharing fragments; an off-diagonal tile folds the cross-block factor into
 // its column fragment.  Writes af (A, fp32), b16, r16 and p16, and returns
-// whether an entry stored in fp16 (Bm, R, P) left the fast range.
-template <typename SM, bool TIED>
+// whether an entry stored in fp16 (Bm, R, P) left the fast range.  PARTS
+// selects a share of the tile, so that two waves can split one: bit 0 the
+// Grams on the erase column operand (A and R), bit 1 those on the write
+// column operand (Bm and P); with tied gates (Bm = A, P = R) bit 0 is A, bit 1
+// is R.  Each Gram is accumulated in the same order whatever the share.
+template <typename SM, bool TIED, int PARTS = 3>
 __device__ __forceinline__ bool gram_tile(SM &S, int i, int j, int lr, int lg) {
+    constexpr bool doA = PARTS & 1, doR = TIED ? (PARTS & 2) != 0 : (PARTS & 1) != 0;
+    constexpr bool doB = !TIED && (PARTS & 2), doP = !TIED && (PARTS & 2);
+    constexpr bool useE = doA || doR, useU = doB || doP;
+    constexpr bool useK = doA || doB, useQ = doR || doP;
     const float *dj = (i != j) ? S.dtab[kPair[i][j]] : nullptr;
     f4 aA = splat(0.f), aB = splat(0.f), aR = splat(0.f), aP = splat(0.f);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         const int cb = 32 * ks + 8 * lg;
-        const h8 xk = lds_ld<h8>(&S.kh[(16 * i + lr) * KP + cb]);
-        const h8 xq = lds_ld<h8>(&S.qh[(16 * i + lr) * KP + cb]);
-        h8 ye = lds_ld<h8>(&S.eh[(16 * j + lr) * KP + cb]);
-        h8 yu = TIED ? ye : lds_ld<h8>(&S.uh[(16 * j + lr) * KP + cb]);
+        h8 xk{}, xq{}, ye{}, yu{};
+        if (useK) xk = lds_ld<h8>(&S.kh[(16 * i + lr) * KP + cb]);
+        if (useQ) xq = lds_ld<h8>(&S.qh[(16 * i + lr) * KP + cb]);
+        if (useE) ye = lds_ld<h8>(&S.eh[(16 * j + lr) * KP + cb]);
+        if (useU) yu = lds_ld<h8>(&S.uh[(16 * j + lr) * KP + cb]);
         if (dj) {
             const f4 d0 = lds_ld<f4>(&dj[cb]);
             const f4 d1 = lds_ld<f4>(&dj[cb + 4]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                ye[e] = (_Float16)((float)ye[e] * d0[e]);
-                ye[e + 4] = (_Float16)((float)ye[e + 4] * d1[e]);
-                if (!TIED) {
+                if (useE) {
+                    ye[e] = (_Float16)((float)ye[e] * d0[e]);
+                    ye[e + 4] = (_Float16)((float)ye[e + 4] * d1[e]);
+                }
+                if (useU) {
                     yu[e] = (_Float16)((float)yu[e] * d0[e]);
                     yu[e + 4] = (_Float16)((float)yu[e + 4] * d1[e]);
                 }
             }
         }
-        aA = mfma32(xk, ye, aA);
-        aR = mfma32(xq, ye, aR);
-        if (!TIED) {
-            aB = mfma32(xk, yu, aB);
-            aP = mfma32(xq, yu, aP);
-        }
+        if (doA) aA = mfma32(xk, ye, aA);
+        if (doR) aR = mfma32(xq, ye, aR);
+        if (doB) aB = mfma32(xk, yu, aB);
+        if (doP) aP = mfma32(xq, yu, aP);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int r = 16 * i + 4 * lg + e, s = 16 * j + lr;
         const bool strict = r > s, incl = r >= s;
-        S.af[r * AP + s] = strict ? aA[e] : 0.f;
-        S.b16[r * SP + s] = (_Float16)(strict ? (TIED ? aA[e] : aB[e]) : 0.f);
-        S.r16[r * SP + s] = (_Float16)(incl ? aR[e] : 0.f);
-        if (!TIED) S.p16[r * SP + s] = (_Float16)(incl ? aP[e] : 0.f);
+        if (doA) S.af[r * AP + s] = strict ? aA[e] : 0.f;
+        if (TIED ? doA : doB) S.b16[r * SP + s] = (_Float16)(strict ? (TIED ? aA[e] : aB[e]) : 0.f);
+        if (doR) S.r16[r * SP + s] = (_Float16)(incl ? aR[e] : 0.f);
+        if (doP) S.p16[r * SP + s] = (_Float16)(incl ? aP[e] : 0.f);
     }
-    return out_of_range(aR) || (!TIED && (out_of_range(aB) || out_of_range(aP)));
+    return (doR && out_of_range(aR)) || (doB && out_of_range(aB)) || (doP && out_of_range(aP));
 }
 
 // The four Grams with 8 waves: waves 0,1 take two diagonal tiles each (and

@@ -226,54 +226,46 @@ __device__ __forceinline__ h8 perm_frag(const _Float16 *m, int rt, int ks, int l
     return join(lds_ld<h4>(p), lds_ld<h4>(p + 16));
 }
 
-// W^T and Qe^T = Qbar^T - W^T R^T for key channel tiles 2kb, 2kb+1 and token
-// tiles 2RH, 2RH+1, written to the record; W = Tm Kbar comes first as tiles
-// (tokens x channels) whose registers are the A operand of W^T R^T.
-// Returns whether a result left the fp16 range.
-template <int RH>
-__device__ __forceinline__ bool wq_tiles(const PrepSmem &S, _Float16 *rec, int kb, int lane, int lr, int lg) {
-    constexpr int NST = 2 * RH + 2;  // token tiles of W needed
-    h8 kbf[2][RH + 1];               // Kbar[:, tile 2kb+cc] per 32-token block, natural order
+// W^T and Qe^T = Qbar^T - W^T R^T for key channel tile kt and every token
+// tile, written to the record (the fragment of a token tile pairs key tiles
+// 2m and 2m + 1: this tile's half of it); W = Tm Kbar comes first as tiles
+// (tokens x channels) whose registers are the A operand of W^T R^T.  One key
+// tile per wave keeps the waves' work equal (the lower token tiles need half
+// the products of the upper ones).  Returns whether a result left the fp16
+// range.
+__device__ __forceinline__ bool wq_tile(const PrepSmem &S, _Float16 *rec, int kt, int lane, int lr, int lg) {
+    h8 kbf[2];  // Kbar[:, tile kt] per 32-token block, natural order
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int ks = 0; ks <= RH; ++ks)
+        for (int e = 0; e < 8; ++e) kbf[ks][e] = S.kh[(32 * ks + 8 * lg + e) * KP + 16 * kt + lr];
+    h8 tn[4][2];  // Tm rows, natural token order (block 1 only below the diagonal blocks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kbf[cc][ks][e] = S.kh[(32 * ks + 8 * lg + e) * KP + 16 * (2 * kb + cc) + lr];
-    h8 tn[4][RH + 1];  // Tm rows, natural token order
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
-    for (int st = 0; st < NST; ++st)
+        for (int ks = 0; ks <= (st >> 1); ++ks) tn[st][ks] = lds_ld<h8>(&S.t16[(16 * st + lr) * SP + 32 * ks + 8 * lg]);
+    f4 wt[4];
 #pragma unroll
-        for (int ks = 0; ks <= RH; ++ks)
-            tn[st][ks] = lds_ld<h8>(&S.t16[(16 * st + lr) * SP + 32 * ks + 8 * lg]);
-    f4 wt[4][2];
-#pragma unroll
-    for (int st = 0; st < NST; ++st)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-            wt[st][cc] = mfma32(tn[st][0], kbf[cc][0], splat(0.f));
-            if (st >= 2) wt[st][cc] = mfma32(tn[st][RH], kbf[cc][RH], wt[st][cc]);
-        }
+    for (int st = 0; st < 4; ++st) {
+        wt[st] = mfma32(tn[st][0], kbf[0], splat(0.f));
+        if (st >= 2) wt[st] = mfma32(tn[st][1], kbf[1], wt[st]);
+    }
     bool big = false;
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-        const int rt = 2 * RH + rr;
-        f4 wT[2], qT[2];
+    for (int rt = 0; rt < 4; ++rt) {
+        const int rh = rt >> 1;
+        f4 wT = mfma32(kbf[0], tn[rt][0], splat(0.f));
+        if (rh) wT = mfma32(kbf[1], tn[rt][1], wT);
+        f4 qT = to_f4(lds_ld<h4>(&S.qh[(16 * rt + lr) * KP + 16 * kt + 4 * lg]));
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-            wT[cc] = mfma32(kbf[cc][0], tn[rt][0], splat(0.f));
-            if (RH) wT[cc] = mfma32(kbf[cc][RH], tn[rt][RH], wT[cc]);
-            qT[cc] = to_f4(lds_ld<h4>(&S.qh[(16 * rt + lr) * KP + 16 * (2 * kb + cc) + 4 * lg]));
-#pragma unroll
-            for (int ks = 0; ks <= RH; ++ks) {
-                const h8 wa = join(to_h4(wt[2 * ks][cc]), to_h4(wt[2 * ks + 1][cc]));
-                qT[cc] = mfma32(-wa, perm_frag(S.r16, rt, ks, lr, lg), qT[cc]);
-            }
-            big |= out_of_range(wT[cc]) || out_of_range(qT[cc]);
+        for (int ks = 0; ks <= rh; ++ks) {
+            const h8 wa = join(to_h4(wt[2 * ks]), to_h4(wt[2 * ks + 1]));
+            qT = mfma32(-wa, perm_frag(S.r16, rt, ks, lr, lg), qT);
         }
-        const int64_t o = ((rt * 4 + kb) * 64 + lane) * 8;
-        *reinterpret_cast<h8 *>(rec + OFF_W + o) = join(to_h4(wT[0]), to_h4(wT[1]));
-        *reinterpret_cast<h8 *>(rec + OFF_Q + o) = join(to_h4(qT[0]), to_h4(qT[1]));
+        big |= out_of_range(wT) || out_of_range(qT);
+        const int64_t o = ((rt * 4 + (kt >> 1)) * 64 + lane) * 8 + 4 * (kt & 1);
+        *reinterpret_cast<h4 *>(rec + OFF_W + o) = to_h4(wT);
+        *reinterpret_cast<h4 *>(rec + OFF_Q + o) = to_h4(qT);
     }
     return big;
 }
@@ -367,21 +359,26 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         // has the same memory operations in flight, so the waits before the
         // first use of each part count only what was issued after it.
         if (next >= ntask) pn.tlim = pn.t0;
-        load_part<0, TIED, GK, VW, RAW>(R, a, pn, tid);
+        load_part<3, TIED, GK, VW, RAW>(R, a, pn, tid);
         __syncthreads();
 
         const bool wide = S.wide != 0;  // read by all before any later write
         if (!wide) {
             // ---- Grams: waves 0..3 one diagonal tile each, inverted at once;
-            //      waves 4..7 the six off-diagonal tiles
+            //      waves 4..7 the six off-diagonal tiles: tile u each, and
+            //      half of the Grams of tile 4 + u / 2 (the two waves of a
+            //      pair take the two column operands)
             if (wv < 4) {
                 gram_tile<PrepSmem, TIED>(S, wv, wv, lr, lg);
                 invert_unit_lower16(&S.af[(16 * wv) * AP + 16 * wv], &S.t16[(16 * wv) * SP + 16 * wv],
                                     S.iscr[wv][0], S.iscr[wv][1], lr, lg);
             } else {
-                const int u = wv - 4;  // off-diagonal tiles u and u + 4 (< 6)
+                const int u = wv - 4, t2 = 4 + (u >> 1);
                 gram_tile<PrepSmem, TIED>(S, kOffI[u], kOffJ[u], lr, lg);
-                if (u < 2) gram_tile<PrepSmem, TIED>(S, kOffI[u + 4], kOffJ[u + 4], lr, lg);
+                if (u & 1)
+                    gram_tile<PrepSmem, TIED, 2>(S, kOffI[t2], kOffJ[t2], lr, lg);
+                else
+                    gram_tile<PrepSmem, TIED, 1>(S, kOffI[t2], kOffJ[t2], lr, lg);
             }
         }
         __syncthreads();
@@ -395,6 +392,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 lds_st<h4>(&S.qh[r * KP + 4 * cq], to_h4(qhf[i] * egm));
             }
         }
+        load_part<0, TIED, GK, VW, RAW>(R, a, pn, tid);
         load_part<1, TIED, GK, VW, RAW>(R, a, pn, tid);
 
         _Float16 *rec = w.frag + task * REC;
@@ -433,11 +431,8 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 }
             }
 
-            // ---- (2) key channel tiles 2kb, 2kb+1: W^T and Qe^T -> HBM -------
-            if (wv >= 4)
-                big |= wq_tiles<1>(S, rec, wv & 3, lane, lr, lg);
-            else
-                big |= wq_tiles<0>(S, rec, wv & 3, lane, lr, lg);
+            // ---- (2) key channel tile wv: W^T and Qe^T -> HBM ---------------
+            big |= wq_tile(S, rec, wv, lane, lr, lg);
 
             // ---- (3) key channel tile it = wv: Etil^T, Util^T fragments
             //      (chunk-end reference: column operand times 2^(gC - gm_j))
@@ -472,19 +467,31 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             // ---- (4) Oe^T[ct, :] = V^T P^T - U^T R^T -> HBM (transposed, so
             //      the scan's output tiles hold adjacent columns per lane)
             {
+                // every operand read first, then the four token tiles' products
+                // interleaved (independent accumulators), so that neither the
+                // LDS reads nor the matrix unit's latency serialise the phase
                 const _Float16 *pp = TIED ? S.r16 : S.p16;
                 const h8 ub0 = join(to_h4(uacc[0]), to_h4(uacc[1])), ub1 = join(to_h4(uacc[2]), to_h4(uacc[3]));
+                h8 pf[6], rf[6];  // (rt, ks) pairs 0,0 1,0 2,0 2,1 3,0 3,1
+#pragma unroll
+                for (int rt = 0, n = 0; rt < 4; ++rt)
+#pragma unroll
+                    for (int ks = 0; ks <= (rt >> 1); ++ks, ++n) {
+                        pf[n] = lds_ld<h8>(&pp[(16 * rt + lr) * SP + 32 * ks + 8 * lg]);
+                        rf[n] = perm_frag(S.r16, rt, ks, lr, lg);
+                    }
+                __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
                 f4 acc[4];
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    acc[rt] = splat(0.f);
+                for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma32(vb[0], pf[rt < 2 ? rt : 2 * rt - 2], splat(0.f));
 #pragma unroll
-                    for (int ks = 0; ks <= (rt >> 1); ++ks) {
-                        acc[rt] = mfma32(vb[ks], lds_ld<h8>(&pp[(16 * rt + lr) * SP + 32 * ks + 8 * lg]), acc[rt]);
-                        acc[rt] = mfma32(ks ? -ub1 : -ub0, perm_frag(S.r16, rt, ks, lr, lg), acc[rt]);
-                    }
-                    big |= out_of_range(acc[rt]);
-                }
+                for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma32(-ub0, rf[rt < 2 ? rt : 2 * rt - 2], acc[rt]);
+#pragma unroll
+                for (int rt = 2; rt < 4; ++rt) acc[rt] = mfma32(vb[1], pf[2 * rt - 1], acc[rt]);
+#pragma unroll
+                for (int rt = 2; rt < 4; ++rt) acc[rt] = mfma32(-ub1, rf[2 * rt - 1], acc[rt]);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) big |= out_of_range(acc[rt]);
 #pragma unroll
                 for (int rp = 0; rp < 2; ++rp)
                     *reinterpret_cast<h8 *>(rec + OFF_O + ((ct * 2 + rp) * 64 + lane) * 8) =
@@ -492,26 +499,41 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             }
             // ---- (5) G[it, :] = Util^T V - Etil^T U -> HBM -------------------
             {
+                // four value tiles at a time: their operand reads issued
+                // together, their products interleaved (same order per tile)
                 const h8 ne0 = -ef[0], ne1 = -ef[1];
 #pragma unroll
-                for (int c2 = 0; c2 < 8; ++c2) {
-                    f4 acc = splat(0.f);
+                for (int cb = 0; cb < 8; cb += 4) {
+                    h8 vp[4][2], up[4][2];
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb) {
-                        const _Float16 *pv = &S.v16[(16 * c2 + lr) * SP + 32 * kb + 4 * lg];
-                        const _Float16 *pu = &S.u16[(16 * c2 + lr) * SP + 32 * kb + 4 * lg];
-                        const h8 vp = join(lds_ld<h4>(pv), lds_ld<h4>(pv + 16));
-                        const h8 up = join(lds_ld<h4>(pu), lds_ld<h4>(pu + 16));
-                        acc = mfma32(uf[kb], vp, acc);
-                        acc = mfma32(kb ? ne1 : ne0, up, acc);
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb) {
+                            const _Float16 *pv = &S.v16[(16 * (cb + j) + lr) * SP + 32 * kb + 4 * lg];
+                            const _Float16 *pu = &S.u16[(16 * (cb + j) + lr) * SP + 32 * kb + 4 * lg];
+                            vp[j][kb] = join(lds_ld<h4>(pv), lds_ld<h4>(pv + 16));
+                            up[j][kb] = join(lds_ld<h4>(pu), lds_ld<h4>(pu + 16));
+                        }
+                    __builtin_amdgcn_sched_barrier(0);  // keep the four tiles' reads ahead of their products
+                    f4 acc[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[j] = mfma32(uf[0], vp[j][0], splat(0.f));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[j] = mfma32(ne0, up[j][0], acc[j]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[j] = mfma32(uf[1], vp[j][1], acc[j]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc[j] = mfma32(ne1, up[j][1], acc[j]);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        big |= out_of_range(acc[j]);
+                        *reinterpret_cast<h4 *>(rec + OFF_G + (((cb + j) * 4 + (it >> 1)) * 64 + lane) * 8 + 4 * (it & 1)) =
+                            to_h4(acc[j]);
                     }
-                    big |= out_of_range(acc);
-                    *reinterpret_cast<h4 *>(rec + OFF_G + ((c2 * 4 + (it >> 1)) * 64 + lane) * 8 + 4 * (it & 1)) = to_h4(acc);
                 }
             }
             if (big) S.wide = 1;
         }
-        load_part<3, TIED, GK, VW, RAW>(R, a, pn, tid);
         __syncthreads();
         // e^gC per key channel; a chunk to be run exactly is marked by -1 in
         // channel 0 (e^gC is never negative)

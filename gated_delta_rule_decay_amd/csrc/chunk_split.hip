@@ -62,6 +62,14 @@ constexpr int64_t OFF_E = 16384;
 constexpr int64_t OFF_G = 24576;
 constexpr int64_t OFF_O = 40960;
 constexpr int64_t REC = 49152;
+// Tied gates (u = e, so Bm = A and P = R; also the value-write form) keep a
+// slimmer record: with D = V - U, G = Etil^T D and Oe = R D, so the scan
+// forms both from D and R itself and the record holds W^T, Qbar^T (the scan
+// adds R (D - W S) to Qbar S), Etil^T, D and the six nonzero fragments of R:
+// 70 KiB written and read instead of 96 KiB.
+constexpr int64_t OFF_D = 24576;  // D in the scan's W S tile layout: [value tile][tile pair][lane][8]
+constexpr int64_t OFF_R = 32768;  // R as B operands of R X (perm_frag order), fragment n = (rt, ks)
+constexpr int R_FRAGS = 6;        // (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
 
 struct SplitWs {
     _Float16 *frag;  // [task][REC]
@@ -226,13 +234,14 @@ __device__ __forceinline__ h8 perm_frag(const _Float16 *m, int rt, int ks, int l
     return join(lds_ld<h4>(p), lds_ld<h4>(p + 16));
 }
 
-// W^T and Qe^T = Qbar^T - W^T R^T for key channel tile kt and every token
-// tile, written to the record (the fragment of a token tile pairs key tiles
+// W^T and Qe^T = Qbar^T - W^T R^T (the slim record: Qbar^T) for key channel
+// tile kt and every token tile, written to the record (the fragment of a token tile pairs key tiles
 // 2m and 2m + 1: this tile's half of it); W = Tm Kbar comes first as tiles
 // (tokens x channels) whose registers are the A operand of W^T R^T.  One key
 // tile per wave keeps the waves' work equal (the lower token tiles need half
 // the products of the upper ones).  Returns whether a result left the fp16
 // range.
+template <bool SLIM>
 __device__ __forceinline__ bool wq_tile(const PrepSmem &S, _Float16 *rec, int kt, int lane, int lr, int lg) {
     h8 kbf[2];  // Kbar[:, tile kt] per 32-token block, natural order
 #pragma unroll
@@ -257,10 +266,12 @@ __device__ __forceinline__ bool wq_tile(const PrepSmem &S, _Float16 *rec, int kt
         f4 wT = mfma32(kbf[0], tn[rt][0], splat(0.f));
         if (rh) wT = mfma32(kbf[1], tn[rt][1], wT);
         f4 qT = to_f4(lds_ld<h4>(&S.qh[(16 * rt + lr) * KP + 16 * kt + 4 * lg]));
+        if (!SLIM) {  // the slim record keeps Qbar^T
 #pragma unroll
-        for (int ks = 0; ks <= rh; ++ks) {
-            const h8 wa = join(to_h4(wt[2 * ks]), to_h4(wt[2 * ks + 1]));
-            qT = mfma32(-wa, perm_frag(S.r16, rt, ks, lr, lg), qT);
+            for (int ks = 0; ks <= rh; ++ks) {
+                const h8 wa = join(to_h4(wt[2 * ks]), to_h4(wt[2 * ks + 1]));
+                qT = mfma32(-wa, perm_frag(S.r16, rt, ks, lr, lg), qT);
+            }
         }
         big |= out_of_range(wT) || out_of_range(qT);
         const int64_t o = ((rt * 4 + (kt >> 1)) * 64 + lane) * 8 + 4 * (kt & 1);
@@ -432,7 +443,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             }
 
             // ---- (2) key channel tile wv: W^T and Qe^T -> HBM ---------------
-            big |= wq_tile(S, rec, wv, lane, lr, lg);
+            big |= wq_tile<TIED>(S, rec, wv, lane, lr, lg);
 
             // ---- (3) key channel tile it = wv: Etil^T, Util^T fragments
             //      (chunk-end reference: column operand times 2^(gC - gm_j))
@@ -455,15 +466,38 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                     *reinterpret_cast<h8 *>(rec + OFF_E + ((it * 2 + kb) * 64 + lane) * 8) = ef[kb];
                 }
             }
-            // U -> u16 [j][s] for the value-column products of every wave
+            if (!TIED) {
+                // U -> u16 [j][s] for the value-column products of every wave
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-                lds_st<h4>(&S.u16[(16 * ct + lr) * SP + 16 * rt + 4 * lg], to_h4(uacc[rt]));
+                for (int rt = 0; rt < 4; ++rt)
+                    lds_st<h4>(&S.u16[(16 * ct + lr) * SP + 16 * rt + 4 * lg], to_h4(uacc[rt]));
+            } else {
+                // the slim record: D = V - U of value tile ct, in the layout of
+                // the scan's W S tiles (token 16 rt + 4 lg + e, column 16 ct + lr),
+                // and R fragment wv as a B operand
+                f4 dd[4];
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) {
+                    dd[rt] = to_f4(lds_ld<h4>(&S.v16[(16 * ct + lr) * SP + 16 * rt + 4 * lg])) - uacc[rt];
+                    big |= out_of_range(dd[rt]);
+                }
+#pragma unroll
+                for (int rp = 0; rp < 2; ++rp)
+                    *reinterpret_cast<h8 *>(rec + OFF_D + ((ct * 2 + rp) * 64 + lane) * 8) =
+                        join(to_h4(dd[2 * rp]), to_h4(dd[2 * rp + 1]));
+                if (wv < R_FRAGS) {  // (R enters no product here: its range is checked as stored)
+                    const int rt = wv < 2 ? wv : (wv + 2) / 2, ks = wv < 2 ? 0 : wv & 1;
+                    const h8 rf = perm_frag(S.r16, rt, ks, lr, lg);
+                    big |= out_of_range(f4{(float)rf[0], (float)rf[1], (float)rf[2], (float)rf[3]}) ||
+                           out_of_range(f4{(float)rf[4], (float)rf[5], (float)rf[6], (float)rf[7]});
+                    *reinterpret_cast<h8 *>(rec + OFF_R + (wv * 64 + lane) * 8) = rf;
+                }
+            }
             if (big) S.wide = 1;
         }
         __syncthreads();  // U complete in u16
         load_part<2, TIED, GK, VW, RAW>(R, a, pn, tid);
-        if (!wide) {
+        if (!wide && !TIED) {
             // ---- (4) Oe^T[ct, :] = V^T P^T - U^T R^T -> HBM (transposed, so
             //      the scan's output tiles hold adjacent columns per lane)
             {
@@ -579,6 +613,15 @@ constexpr int SLOT_G = SCAN_W * 4 * 512;  // halves of G for my tiles (4 pair ro
 constexpr int SLOT_O = SCAN_W * 2 * 512;  // halves of Oe^T for my tiles
 constexpr int SLOT_H = SLOT_F + SLOT_G + SLOT_O;  // MODE 0 slot
 constexpr int SLOT_A = 2 * 8192 + SLOT_G;         // MODE 1 slot: W | EtT | G
+// the slim (tied) record: W | Qbar | EtT, my D tiles, the R fragments
+// (padded to 8 KiB); MODE 1: W | EtT | my D tiles
+constexpr int SLOT_D = SCAN_W * 2 * 512;
+constexpr int SLOT_R = 4096;
+constexpr int SLOT_HT = SLOT_F + SLOT_D + SLOT_R;
+constexpr int SLOT_AT = 2 * 8192 + SLOT_D;
+static_assert(R_FRAGS * 512 <= SLOT_R, "R fragments fit their slot part");
+static_assert(SLOT_HT * 2 % (1024 * SCAN_P) == 0 && SLOT_AT * 2 % (1024 * SCAN_P) == 0,
+              "slot copies must tile the copy waves");
 static_assert(SLOT_H * 2 % (1024 * SCAN_P) == 0 && SLOT_A * 2 % (1024 * SCAN_P) == 0,
               "slot copies must tile the copy waves");
 constexpr int SEG_MIN = 16;   // fewest chunks per segment
@@ -705,8 +748,9 @@ __global__ void __launch_bounds__(scan_threads(MODE))
 chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     constexpr bool WITH_O = MODE == 0;
     constexpr int NCOMP = (MODE ? 2 : 1) * SCAN_W;
-    constexpr int SH = MODE ? SLOT_A : SLOT_H;
+    constexpr int SH = TIED ? (MODE ? SLOT_AT : SLOT_HT) : (MODE ? SLOT_A : SLOT_H);
     constexpr int S_Q = 8192, S_E = MODE ? 8192 : 16384, S_G = MODE ? 16384 : SLOT_F, S_O = SLOT_F + SLOT_G;
+    constexpr int S_D = S_G, S_R = SLOT_F + SLOT_D;  // the slim record: my D tiles, the R fragments
     constexpr int PIECES = SH * 2 / 1024 / SCAN_P;  // 1 KiB copies per copy wave
     // two distinct slots (distinct objects, so the compiler can tell the slot
     // being filled from the one being read)
@@ -790,11 +834,20 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
                                                           0x00020000);
         const int og = 2 * (static_cast<int>(OFF_G) + SCAN_W * half * 4 * 512);
         const int oo = 2 * (static_cast<int>(OFF_O) + SCAN_W * half * 2 * 512);
+        const int od = 2 * (static_cast<int>(OFF_D) + SCAN_W * half * 2 * 512);
 #pragma unroll
         for (int i = 0; i < PIECES; ++i) {
             const int byte = 1024 * (SCAN_P * i + pw);  // my 1 KiB block of the slot
             int src;
-            if (MODE == 0)
+            if (TIED && MODE == 0)
+                src = byte < 2 * SLOT_F ? byte
+                    : byte < 2 * (SLOT_F + SLOT_D) ? od + (byte - 2 * SLOT_F)
+                                                   : 2 * static_cast<int>(OFF_R) + (byte - 2 * (SLOT_F + SLOT_D));
+            else if (TIED)
+                src = byte < 2 * 8192 ? byte
+                    : byte < 4 * 8192 ? 2 * static_cast<int>(OFF_E) + (byte - 2 * 8192)
+                                      : od + (byte - 4 * 8192);
+            else if (MODE == 0)
                 src = byte < 2 * SLOT_F ? byte
                     : byte < 2 * (SLOT_F + SLOT_G) ? og + (byte - 2 * SLOT_F)
                                                    : oo + (byte - 2 * (SLOT_F + SLOT_G));
@@ -863,13 +916,14 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
             for (int rt = 0; rt < 4; ++rt) {
                 if (rt < 3) read_wq(wq[(rt + 1) & 1], rt + 1);
                 h8 oe;
-                if (WITH_O) oe = *reinterpret_cast<const h8 *>(fo + ((rt >> 1) * 64 + lane) * 8);
+                if (WITH_O && !TIED) oe = *reinterpret_cast<const h8 *>(fo + ((rt >> 1) * 64 + lane) * 8);
                 __builtin_amdgcn_sched_barrier(0);
                 f4 p = splat(0.f);
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) p = mfma32(wq[rt & 1][0][kb], sb[kb], p);
                 if (WITH_O) {
-                    f4 o = (rt & 1) ? f4{(float)oe[4], (float)oe[5], (float)oe[6], (float)oe[7]}
+                    f4 o = TIED     ? splat(0.f)
+                         : (rt & 1) ? f4{(float)oe[4], (float)oe[5], (float)oe[6], (float)oe[7]}
                                     : f4{(float)oe[0], (float)oe[1], (float)oe[2], (float)oe[3]};
 #pragma unroll
                     for (int kb = 0; kb < 4; ++kb) o = mfma32(sb[kb], wq[rt & 1][1][kb], o);
@@ -880,6 +934,35 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+        // the slim record: X = D - W S (the columns of F: -W S), the B operand
+        // of the state update and, with R, the output's term R X
+        h8 xb[2];
+        const float gsel = frun ? 0.f : 1.f;
+        if (TIED && !bad) {
+            const _Float16 *fd = fr + S_D + wt * 2 * 512;
+            f4 x[4];
+#pragma unroll
+            for (int rp = 0; rp < 2; ++rp) {
+                const h8 d2 = *reinterpret_cast<const h8 *>(fd + (rp * 64 + lane) * 8);
+                x[2 * rp] = gsel * f4{(float)d2[0], (float)d2[1], (float)d2[2], (float)d2[3]} - p1[2 * rp];
+                x[2 * rp + 1] = gsel * f4{(float)d2[4], (float)d2[5], (float)d2[6], (float)d2[7]} - p1[2 * rp + 1];
+            }
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) big |= out_of_range(x[rt]);
+            xb[0] = join(to_h4(x[0]), to_h4(x[1]));
+            xb[1] = join(to_h4(x[2]), to_h4(x[3]));
+            if (WITH_O) {
+                // O^T += X^T R^T: the six nonzero 16 x 32 blocks of R
+                h8 rf[R_FRAGS];
+#pragma unroll
+                for (int n = 0; n < R_FRAGS; ++n) rf[n] = *reinterpret_cast<const h8 *>(fr + S_R + (n * 64 + lane) * 8);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) oacc[rt] = mfma32(xb[0], rf[rt < 2 ? rt : 2 * rt - 2], oacc[rt]);
+#pragma unroll
+                for (int rt = 2; rt < 4; ++rt) oacc[rt] = mfma32(xb[1], rf[2 * rt - 1], oacc[rt]);
+            }
+        }
         bad = bad || __ballot(big) != 0;
         if (!bad) {
             f4 gam[8];
@@ -887,8 +970,10 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
             if (MODE == 0) {
 #pragma unroll
                 for (int it = 0; it < 8; ++it) gam[it] = *reinterpret_cast<const f4 *>(&gm[16 * it + 4 * lg]);
+                if (!TIED) {
 #pragma unroll
-                for (int ip = 0; ip < 4; ++ip) gp[ip] = *reinterpret_cast<const h8 *>(fg + (ip * 64 + lane) * 8);
+                    for (int ip = 0; ip < 4; ++ip) gp[ip] = *reinterpret_cast<const h8 *>(fg + (ip * 64 + lane) * 8);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (WITH_O) {
@@ -903,22 +988,26 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
                 }
             }
             // S <- Diag(e^gC) S + G - Etil^T P1, tokens in permuted slots
-            // (the columns of F take no G)
-            const h8 pb0 = join(to_h4(-p1[0]), to_h4(-p1[1]));
-            const h8 pb1 = join(to_h4(-p1[2]), to_h4(-p1[3]));
-            const float gsel = frun ? 0.f : 1.f;
+            // (the columns of F take no G); the slim record: + Etil^T X
+            const h8 pb0 = TIED ? xb[0] : join(to_h4(-p1[0]), to_h4(-p1[1]));
+            const h8 pb1 = TIED ? xb[1] : join(to_h4(-p1[2]), to_h4(-p1[3]));
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
                 if (MODE) {
 #pragma unroll
                     for (int k2 = 0; k2 < 2; ++k2) ef[it][k2] = *reinterpret_cast<const h8 *>(fr + S_E + ((it * 2 + k2) * 64 + lane) * 8);
                     gam[it] = *reinterpret_cast<const f4 *>(&gm[16 * it + 4 * lg]);
-                    if ((it & 1) == 0) gp[it >> 1] = *reinterpret_cast<const h8 *>(fg + ((it >> 1) * 64 + lane) * 8);
+                    if (!TIED && (it & 1) == 0) gp[it >> 1] = *reinterpret_cast<const h8 *>(fg + ((it >> 1) * 64 + lane) * 8);
                 }
-                const h8 g2 = gp[it >> 1];
-                const f4 gv = (it & 1) ? f4{(float)g2[4], (float)g2[5], (float)g2[6], (float)g2[7]}
-                                       : f4{(float)g2[0], (float)g2[1], (float)g2[2], (float)g2[3]};
-                f4 sv = gam[it] * sacc[it] + (MODE ? gsel * gv : gv);
+                f4 sv;
+                if (TIED) {
+                    sv = gam[it] * sacc[it];
+                } else {
+                    const h8 g2 = gp[it >> 1];
+                    const f4 gv = (it & 1) ? f4{(float)g2[4], (float)g2[5], (float)g2[6], (float)g2[7]}
+                                           : f4{(float)g2[0], (float)g2[1], (float)g2[2], (float)g2[3]};
+                    sv = gam[it] * sacc[it] + (MODE ? gsel * gv : gv);
+                }
                 sv = mfma32(ef[it][0], pb0, sv);
                 sv = mfma32(ef[it][1], pb1, sv);
                 sacc[it] = sv;

@@ -72,17 +72,22 @@ def test_fp32_general_shapes():
 
 
 def test_segmented_scan_and_exact_chunks():
-    # 48 chunks on one chain: three segments.  Then queries scaled by 2^10
-    # (exact in bf16) and a write gate of ~1000 (values w .* v still in fp16
-    # range) drive the chunk product Oe = P V - R U past it, so every chunk is
-    # flagged and run as the exact fp32 token recurrence, which the error then
-    # shows (fp32 level, not fp16 level)
+    # 48 chunks on one chain: three segments.  Then queries scaled by 2^18
+    # (exact in bf16) put the factored query operand past the fp16 operand
+    # bound in every chunk, so every chunk is flagged and run as the exact
+    # fp32 token recurrence, which the error then shows (fp32 level, not fp16
+    # level).  Queries of 2^10 with a write gate of ~1000 stay on the fast
+    # path (every fp16 value in range) at fp16 accuracy.
     w = W[2].scaled(B=1, T=64 * 48, H=1)
     _check(w, _inputs(w, 620), 64)
     inp = _inputs(w, 621)
     inp["q"] = inp["q"] * 1024.0
     inp["q_bf16"] = (inp["q_bf16"].astype(np.uint32) + (10 << 7)).astype(np.uint16)
     inp["write"] = inp["write"] * 1000.0
+    _check(w, inp, 64)
+    inp = _inputs(w, 621)
+    inp["q"] = inp["q"] * np.float32(2.0 ** 18)
+    inp["q_bf16"] = (inp["q_bf16"].astype(np.uint32) + (18 << 7)).astype(np.uint16)
     _check(w, inp, 64, tol=1e-5)
 
 

@@ -405,6 +405,9 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         }
         load_part<0, TIED, GK, VW, RAW>(R, a, pn, tid);
         load_part<1, TIED, GK, VW, RAW>(R, a, pn, tid);
+        // tied gates end the task soon after the U barrier (no Oe, G): the
+        // values go out here, so that they arrive before the next task needs them
+        if constexpr (TIED) load_part<2, TIED, GK, VW, RAW>(R, a, pn, tid);
 
         _Float16 *rec = w.frag + task * REC;
         bool big = false;
@@ -496,7 +499,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             if (big) S.wide = 1;
         }
         __syncthreads();  // U complete in u16
-        load_part<2, TIED, GK, VW, RAW>(R, a, pn, tid);
+        if constexpr (!TIED) load_part<2, TIED, GK, VW, RAW>(R, a, pn, tid);
         if (!wide && !TIED) {
             // ---- (4) Oe^T[ct, :] = V^T P^T - U^T R^T -> HBM (transposed, so
             //      the scan's output tiles hold adjacent columns per lane)

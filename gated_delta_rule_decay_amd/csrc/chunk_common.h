@@ -43,6 +43,7 @@ constexpr int KP = D + 8;      // pitch (halves) of [token][channel] operands
 constexpr int SP = C + 8;      // pitch (halves) of [row][token] operands
 constexpr int AP = C + 4;      // pitch (floats) of the fp32 C x C matrix
 constexpr int IP = 18;         // pitch (floats) of the 16x16 inverse scratch
+constexpr int GP = D + 4;      // pitch (floats) of the segment totals (a quad's four rows: 2-way banked)
                                // (read along its rows by the matrix unit)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float MAX_EXP2 = 14.f;        // largest |log2 factor| on the fast path
@@ -280,34 +281,58 @@ __device__ __forceinline__ void segment_cumsum(SM &S, const Raw<GK, NV> &R, f4 (
     lds_st<f4>(&S.segtot[seg][4 * cq], run);
 }
 
-// Exclusive prefix of the segment totals, in place, one lane per key channel
-// (tid < D); the same lanes fill the per-chunk factor tables:
-//   gce[c] = 2^g_C, fsc[j][c] = 2^(g_C - gm_j), dtab = 2^(gm_i - gm_j), i > j.
-template <typename SM>
-__device__ __forceinline__ void chunk_tables(SM &S, int c) {
-    float gmc[4], cum = 0.f;
-#pragma unroll
-    for (int s = 0; s < NSEG; ++s) {
-        const float st = S.segtot[s][c];
-        S.segtot[s][c] = cum;
-        cum += st;
-        if ((s & 3) == 1) gmc[s >> 2] = cum;  // block reference: after row 16j+7
-    }
-    S.gce[c] = __builtin_amdgcn_exp2f(cum);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) S.fsc[j][c] = __builtin_amdgcn_exp2f(cum - gmc[j]);
-    S.dtab[0][c] = __builtin_amdgcn_exp2f(gmc[1] - gmc[0]);
-    S.dtab[1][c] = __builtin_amdgcn_exp2f(gmc[2] - gmc[0]);
-    S.dtab[2][c] = __builtin_amdgcn_exp2f(gmc[2] - gmc[1]);
-    S.dtab[3][c] = __builtin_amdgcn_exp2f(gmc[3] - gmc[0]);
-    S.dtab[4][c] = __builtin_amdgcn_exp2f(gmc[3] - gmc[1]);
-    S.dtab[5][c] = __builtin_amdgcn_exp2f(gmc[3] - gmc[2]);
-}
-
 // x moved across lanes by the DPP control CTRL (all rows and banks).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Exclusive prefix of the segment totals, in place, and the per-chunk factor
+// tables, four lanes per key channel (every thread of the workgroup: channel
+// c = tid / 4, lane j = tid % 4 of its quad takes segments 4j .. 4j+3, whose
+// second row ends block j's reference):
+//   gce[c] = 2^g_C, fsc[j][c] = 2^(g_C - gm_j), dtab = 2^(gm_i - gm_j), i > j.
+// The prefix is summed in segment order, as one lane would (three rounds pass
+// each quad lane's running total to the next lane), so the tables do not
+// depend on how the work is split.
+template <typename SM>
+__device__ __forceinline__ void chunk_tables(SM &S, int tid) {
+    const int c = tid >> 2, j = tid & 3;
+    float v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = S.segtot[4 * j + k][c];
+    float base = 0.f, tot = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        tot = base;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) tot += v[k];
+        if (r < 3) {
+            const float prev = dpp_f32<0x90>(tot);  // quad_perm [0, 0, 1, 2]: lane j - 1's total
+            base = j ? prev : 0.f;
+        }
+    }
+    float run = base, gm = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        S.segtot[4 * j + k][c] = run;
+        run += v[k];
+        if (k == 1) gm = run;  // block reference: after row 16j+7
+    }
+    const float cum = dpp_f32<0xFF>(tot);  // quad_perm [3, 3, 3, 3]: the chunk total
+    const float g0 = dpp_f32<0x00>(gm), g1 = dpp_f32<0x55>(gm), g2 = dpp_f32<0xAA>(gm);
+    if (j == 0) S.gce[c] = __builtin_amdgcn_exp2f(cum);
+    S.fsc[j][c] = __builtin_amdgcn_exp2f(cum - gm);
+    if (j == 1) {
+        S.dtab[0][c] = __builtin_amdgcn_exp2f(gm - g0);
+    } else if (j == 2) {
+        S.dtab[1][c] = __builtin_amdgcn_exp2f(gm - g0);
+        S.dtab[2][c] = __builtin_amdgcn_exp2f(gm - g1);
+    } else if (j == 3) {
+        S.dtab[3][c] = __builtin_amdgcn_exp2f(gm - g0);
+        S.dtab[4][c] = __builtin_amdgcn_exp2f(gm - g1);
+        S.dtab[5][c] = __builtin_amdgcn_exp2f(gm - g2);
+    }
 }
 
 // Sum over each half-wave's 32 lanes (the 32 lanes that hold one token row),

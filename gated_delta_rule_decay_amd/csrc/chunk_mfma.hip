@@ -52,7 +52,7 @@ struct alignas(16) Smem {
     union {
         float af[C * AP];         // A (strict lower), then Tm in place (fp32)
         _Float16 xm16[VT * SP];   // X, then -M, [v][s]
-        float segtot[NSEG][D];    // per-segment log2-decay totals
+        float segtot[NSEG][GP];    // per-segment log2-decay totals
         struct {
             float tok[6][D];      // token vectors of the exact fallback
             float red[2][NW][VT]; // its cross-wave reductions
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(NTH) chunk_mfma_kernel(ChunkArgs a, int nt, in
         f4 g[RPS];
         segment_cumsum(S, R, g, seg, cq);
         __syncthreads();
-        if (tid < D) chunk_tables(S, tid);
+        chunk_tables(S, tid);
         __syncthreads();
 
         // ---- prep 2: factored fp16 operands ----------------------------------

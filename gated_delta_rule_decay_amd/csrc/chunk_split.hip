@@ -94,7 +94,7 @@ struct alignas(16) PrepSmem {
     union {
         float af[C * AP];       // A (strict lower), then Tm in place (fp32)
         _Float16 u16[D * SP];   // U, [j][s]
-        float segtot[NSEG][D];  // per-segment log2-decay totals
+        float segtot[NSEG][GP];  // per-segment log2-decay totals
     };
     _Float16 t16[C * SP];  // Tm  [r][s]
     _Float16 b16[C * SP];  // Bm
@@ -357,7 +357,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         f4 g[RPS];
         segment_cumsum(S, R, g, seg, cq, logits, logits ? cur.tlim - cur.t0 : C);
         __syncthreads();
-        if (tid < D) chunk_tables(S, tid);
+        chunk_tables(S, tid);
         __syncthreads();
 
         // ---- factored fp16 Gram operands -------------------------------------

@@ -404,6 +404,35 @@ def test_large_grams_run_exactly(ws):
     _check(w, inp, 64, ws=ws)
 
 
+@pytest.mark.parametrize("ws", PATHS)
+def test_large_query_key_gram_tied(ws):
+    # tied gates (the slim two-pass record keeps R itself, not products of
+    # it): queries equal to the keys times 2^15 (exact in bf16) and an erase
+    # gate of 1 put every diagonal entry of R = (q e^T) at 2^15, past the fp16
+    # result bound, while a weak decay (log a = -1e-3) keeps every factored
+    # operand within the fp16 operand bound (largest query entry about 1.2e4).
+    # Each chunk must be flagged by the Gram's own range check and run as the
+    # exact fp32 recurrence: finite results at fp32 accuracy, on both paths.
+    w, inp = _bf16_case(48, T=150, tied=True)
+    inp["q_bf16"] = _shift_exponent(inp["k_bf16"], 15)
+    inp["q"] = inp["k"] * np.float32(2.0 ** 15)
+    inp["erase"] = np.ones_like(inp["erase"])
+    inp["log_decay"] = np.full_like(inp["log_decay"], -1e-3)
+    assert np.abs(inp["q"]).max() < 16384 * 0.99
+    o, S = gpu_chunk(inp, 64, workspace=ws)
+    o_ref, S_ref = oracle_chunk(inp)
+    eo, es = rel_l2(o, o_ref), rel_l2(S, S_ref)
+    print(f"  rel_l2 o={eo:.3e} S={es:.3e} (exact path, tol 1e-05)", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+    assert eo <= 1e-5 and es <= 1e-5
+
+
+def _shift_exponent(bits, log2):
+    """bf16 bits times 2^log2 (exact: the exponent field moves; zeros stay)."""
+    b = bits.astype(np.int32)
+    return np.where((b & 0x7fff) != 0, b + (log2 << 7), b).astype(np.uint16)
+
+
 def _scale_bf16(inp, name, log2):
     """Multiply a bf16 input by 2^log2 (exact: the exponent field moves)."""
     bits = inp[name + "_bf16"].astype(np.int32)

@@ -1,5 +1,6 @@
 // chunk_split.hip -- two-pass chunkwise GDN-2 forward on the gfx950 matrix
-// cores (bf16 q/k/v, dk = dv = 128, chunk C = 64, every gate of one kind).
+// cores (bf16 q/k/v, dk = dv = 128, chunk C = 64; gates per key channel or
+// per head, the decay per channel with per-head rates included).
 //
 // The chunk form (gist.science summary, "Technische Samenvatting" section 3:
 // cumulative decay absorbed into the erase and write factors, a
@@ -13,22 +14,25 @@
 // depend on the chunk alone, and then
 //   O = Qe S + Oe,   S <- Diag(e^gC) S + G - Etil^T (W S)
 // is all that the sequential scan over chunks has to do (M = W S + U is the
-// erase read of the token form).
+// erase read of the token form).  With tied gates (u = e, so P = R) and
+// D = V - U, X = D - W S: O = Qbar S + R X and S <- Diag(e^gC) S + Etil^T X,
+// so the record of a tied chunk keeps Qbar, D and R instead of Qe, Oe and G.
 //
 // Pass 1 (chunk_prep_kernel) runs every (chain, chunk) in parallel -- one
-// 512-lane workgroup per task, persistent, with the next task's inputs
-// prefetched into registers -- and writes W, Qe, Etil^T, G and Oe as fp16
+// 512-lane workgroup per CU, persistent over the tasks, with the next task's
+// inputs prefetched into registers -- and writes the record as fp16
 // fragments in exactly the register order the scan's MFMA operands take,
-// plus e^gC (which also carries the exact-path mark).  Pass 2 (chunk_scan_kernel) gives each wave one
-// chain and 16*NB value columns; the fp32 state slice (128 x 16*NB) stays in
-// MFMA accumulators, every operand is one coalesced 16-byte load per lane,
-// and waves never synchronise, so a chain's value columns proceed on as
-// many CUs as there are waves.
+// plus e^gC (which also carries the exact-path mark).  Pass 2
+// (chunk_scan_kernel) runs one workgroup per (chain, half of the value
+// columns): four compute waves keep their fp32 state slices in MFMA
+// accumulators while four copy waves stage the chunk records through two
+// LDS slots, one chunk ahead; long sequences on few chains are cut into
+// segments scanned in parallel and combined (the affine view of a chunk).
 //
 // A chunk whose fp16 factors, operands or results would leave the fast
 // range is flagged by pass 1; pass 2 runs it as the exact fp32 token
-// recurrence on the raw inputs instead (so does a chunk whose state or erase
-// read would overflow fp16).
+// recurrence on the raw inputs instead (so does a chunk whose state, erase
+// read or X would overflow fp16).
 #include <atomic>
 #include <mutex>
 #include <type_traits>

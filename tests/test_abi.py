@@ -205,7 +205,7 @@ def query(lib, d):
 
 
 def test_workspace_query(lib):
-    # the two-pass path covers bf16, dk = dv = 128, C = 64, gates of one kind
+    # the two-pass path covers bf16, dk = dv = 128, C = 64, gates of one kind or KDA's
     assert query(lib, good()) == split_bytes(2, 4, 128)
     assert query(lib, good(seqlen=100)) == split_bytes(2, 4, 100)
     assert query(lib, good(tied=True, decay_kind=0, erase_kind=0)) == split_bytes(2, 4, 128)

@@ -805,6 +805,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
         }
 
         // ---- value columns 16 wv + m: Bm V, X, M, dM, Y, dV
+        f4 sr[8], dr[8];  // rows c = 16 wv + m of S and dSo (loaded in the value phase)
         {
             const int col = vcol;
             float v4[4], o4[4];
@@ -834,6 +835,18 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
 #pragma unroll
             for (int j = 0; j < 4; ++j) Y = mfma4(L.tm[(4 * kq + j) * TP + m], dM[j], Y);
             f4 dV = chan_product(L.ut, dS, m, kq, f4{0.f, 0.f, 0.f, 0.f});
+            // S and dSo are consumed as columns: their rows, for the channel
+            // products below, are requested now, while the lines just read
+            // as columns are still in L2 (requested later, they came from
+            // HBM a second time)
+            {
+                const float *srow = Sg + (16 * wv + m) * BD, *drow = dSg + (16 * wv + m) * BD;
+#pragma unroll
+                for (int jt = 0; jt < 8; ++jt) {
+                    sr[jt] = *reinterpret_cast<const f4 *>(srow + 16 * jt + 4 * kq);
+                    dr[jt] = *reinterpret_cast<const f4 *>(drow + 16 * jt + 4 * kq);
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 dV = mfma4(L.pp[(4 * kq + j) * TP + m], o4[j], dV);
@@ -877,15 +890,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
         const int c = 16 * wv + m;
         f4 dW = {0.f, 0.f, 0.f, 0.f}, dQb = dW, dEt = dW, dUt = dW;
         {
-            const float *srow = Sg + c * BD, *drow = dSg + c * BD;
             float dot = 0.f;
-            // every row load goes out before the first product needs one
-            f4 sr[8], dr[8];
-#pragma unroll
-            for (int jt = 0; jt < 8; ++jt) {
-                sr[jt] = *reinterpret_cast<const f4 *>(srow + 16 * jt + 4 * kq);
-                dr[jt] = *reinterpret_cast<const f4 *>(drow + 16 * jt + 4 * kq);
-            }
 #pragma unroll
             for (int jt = 0; jt < 8; ++jt) {
                 const f4 s4 = sr[jt], d4 = dr[jt];

@@ -11,14 +11,15 @@
 //   forward:  X = Kbar S + Bm V,  M = Tm X,  S <- Diag(e^gC) S + Util^T V - Etil^T M
 //   reverse:  dM = -Etil dSo - R^T dO,  Y = Tm^T dM,
 //             dS = Diag(e^gC) dSo + Qbar^T dO + Kbar^T Y
-// Four launches:
+// Three launches:
 //   bwd_record_kernel   every chunk in parallel: the Grams (pairwise decays
 //                       formed directly, never above 1), Tm by forward
 //                       substitution, the decayed operands -> a record;
-//   bwd_state_kernel    per (chain, 64 value columns), chunks in order: S in
-//                       accumulator registers, recorded on entry to each chunk;
-//   bwd_dgrad_kernel    per (chain, 64 value columns), chunks in reverse: dS in
-//                       registers, recorded on entry (= each chunk's dSo), dS0;
+//   bwd_scans_kernel    two independent scans side by side, each per (chain,
+//                       64 value columns): chunks in order with S in
+//                       accumulator registers, recorded on entry to each
+//                       chunk; chunks in reverse with dS in registers,
+//                       recorded on entry (= each chunk's dSo), then dS0;
 //   bwd_grads128_kernel every chunk in parallel: all input gradients from the
 //                       record, S and dSo.
 // All arithmetic is fp32 (v_mfma_f32_16x16x4f32, fp32 accumulate), so the
@@ -422,18 +423,17 @@ __device__ __forceinline__ f4 pair_sum(f4 *xp, f4 mine, int wv, int lane, int kh
     return kh ? other + mine : mine + other;
 }
 
-// The chain and value half of a scan workgroup.  Workgroups are spread over
-// the 8 XCDs round robin; when the grid is a multiple of 16, the two halves
-// of a chain go to workgroups 8 apart, i.e. to one XCD, so the record parts
-// both read come into one L2.
+// The chain and value half of workgroup G among the `units` workgroups of one
+// scan.  Workgroups are spread over the 8 XCDs round robin; when `units` is a
+// multiple of 16, the two halves of a chain go to workgroups 8 apart, i.e. to
+// one XCD, so the record parts both read come into one L2.
 struct ScanUnit {
     int64_t chain;
     int half;
 };
 
-__device__ __forceinline__ ScanUnit scan_unit() {
-    const int64_t G = blockIdx.x;
-    if (gridDim.x % 16 == 0) return {(G / 16) * 8 + (G % 8), static_cast<int>((G / 8) & 1)};
+__device__ __forceinline__ ScanUnit scan_unit(int64_t G, int64_t units) {
+    if (units % 16 == 0) return {(G / 16) * 8 + (G % 8), static_cast<int>((G / 8) & 1)};
     return {G >> 1, static_cast<int>(G & 1)};
 }
 
@@ -443,14 +443,12 @@ struct ScanLds8 {
 };
 
 // The state entering every chunk, hist[chain][chunk][128][128], from S0.
-__global__ void __launch_bounds__(SNT) bwd_state_kernel(BwdArgs a, VarPlan vp, const float *rec, float *hist,
-                                                        int nch) {
-    __shared__ __attribute__((aligned(16))) ScanLds8 LL;
+__device__ __forceinline__ void state_scan(const BwdArgs &a, const VarPlan &vp, const float *rec, float *hist,
+                                           int nch, ScanLds8 &LL, const ScanUnit su) {
     ScanLds &L = LL.r;
     const ChunkArgs &f = a.f;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int m = lane & 15, kq = lane >> 4, kh = wv >> 2;
-    const ScanUnit su = scan_unit();
     const int64_t bh = su.chain;
     const BChain ch = bchain(f, vp, bh, nch);
     const int64_t h = ch.h;
@@ -525,14 +523,12 @@ __global__ void __launch_bounds__(SNT) bwd_state_kernel(BwdArgs a, VarPlan vp, c
 
 // The gradient of every chunk's exit state, dhist[chain][chunk][128][128],
 // carried backwards from d_sT; the gradient of S0 at the end.
-__global__ void __launch_bounds__(SNT) bwd_dgrad_kernel(BwdArgs a, VarPlan vp, const float *rec, float *dhist,
-                                                        int nch) {
-    __shared__ __attribute__((aligned(16))) ScanLds8 LL;
+__device__ __forceinline__ void dgrad_scan(const BwdArgs &a, const VarPlan &vp, const float *rec, float *dhist,
+                                           int nch, ScanLds8 &LL, const ScanUnit su) {
     ScanLds &L = LL.r;
     const ChunkArgs &f = a.f;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int m = lane & 15, kq = lane >> 4, kh = wv >> 2;
-    const ScanUnit su = scan_unit();
     const int64_t bh = su.chain;
     const BChain ch = bchain(f, vp, bh, nch);
     const int64_t h = ch.h;
@@ -598,6 +594,24 @@ __global__ void __launch_bounds__(SNT) bwd_dgrad_kernel(BwdArgs a, VarPlan vp, c
     if (a.ds0) put_half(a.ds0 + bh * BD * BD, dS, kq, kh, col);
 }
 
+// Both scans in one launch: neither reads what the other writes (the reverse
+// scan needs the record and d_o only), so the first half of the grid carries
+// the states forward while the second half carries their gradients back.  At
+// 36 KiB of LDS and 4 waves per SIMD two 8-wave workgroups share a CU, one of
+// each kind when the grid is twice the CU count, and each hides the other's
+// per-chunk load and barrier latency.  Every workgroup of the second half
+// keeps its index mod 8 (the XCD) from the first when the half-grid is a
+// multiple of 8.
+__global__ void __launch_bounds__(SNT) bwd_scans_kernel(BwdArgs a, VarPlan vp, const float *rec, float *hist,
+                                                        float *dhist, int nch) {
+    __shared__ __attribute__((aligned(16))) ScanLds8 LL;
+    const int64_t units = gridDim.x / 2, G = blockIdx.x;
+    if (G < units)
+        state_scan(a, vp, rec, hist, nch, LL, scan_unit(G, units));
+    else
+        dgrad_scan(a, vp, rec, dhist, nch, LL, scan_unit(G - units, units));
+}
+
 // ---------------------------------------------------------------------------
 // the per-chunk gradients
 //
@@ -628,8 +642,14 @@ __device__ __forceinline__ f4 load4_gate(const float *g, int per_key, int64_t ro
     return f4{x, x, x, x};
 }
 
+// TRP: the row pitch of the buffer that turns S and dSo from value columns
+// into key rows, 64 of the 128 columns at a time: written one element per
+// lane (lane (kq, m) at row 4 kq + i, column m -- the two row groups of a
+// half-wave fall 16 banks apart), read 16 bytes per lane along rows.
+constexpr int TRP = 68;
+
 struct GradLds {
-    float kb[BC * GS], et[BC * GS], ut[BC * GS];       // record: Kbar, Etil, Util
+    float kb[BC * GS];                                   // record: Kbar
     float tm[BC * TP], bm[BC * TP], rr[BC * TP], pp[BC * TP];
     float gm[BD];                                        // e^gC, later d gC's exit term
     float k[BC * OS], q[BC * OS], e[BC * OS], u[BC * OS], g[BC * OS];  // raw operands; running log-decay
@@ -637,11 +657,22 @@ struct GradLds {
     float v[BC * GS], o[BC * GS];                        // V, dO
     float mm[BC * GS], dm[BC * GS], y[BC * GS], bv[BC * GS];  // M, dM, Y, Bm V; later the per-(x, c) results
     float dw[BC * GS];
-    float dt[BC * BC], x1[BC * BC], da[BC * BC], dbm[BC * BC], dr[BC * BC], dp[BC * BC];
-    float daT[BC * BC], dbmT[BC * BC], drT[BC * BC], dpT[BC * BC];  // transposes (columns as rows)
     float wpart[8 * BC];  // value-write form, one write gate per head: per-wave partial sums of dw
-    int steep;            // some channel decays by more than STEEP within the chunk
+    // Etil and Util are last read by the value products, the 16 x 16
+    // gradients first written after the channel products: between the two the
+    // same bytes hold the transpose buffer (16-byte rows throughout)
+    union alignas(16) {
+        struct {
+            float et[BC * GS], ut[BC * GS];  // record: Etil, Util
+            float dt[BC * BC], x1[BC * BC], da[BC * BC], dbm[BC * BC], dr[BC * BC], dp[BC * BC];
+            float daT[BC * BC], dbmT[BC * BC], drT[BC * BC], dpT[BC * BC];  // transposes (columns as rows)
+        };
+        float tr[BD * TRP];  // 64 columns of S or dSo
+    };
+    int steep;  // some channel decays by more than STEEP within the chunk
 };
+static_assert(offsetof(GradLds, et) % 16 == 0 && offsetof(GradLds, tr) % 16 == 0 && offsetof(GradLds, da) % 16 == 0,
+              "16-byte LDS rows");
 static_assert(sizeof(GradLds) <= 160 * 1024, "gradient kernel LDS exceeds the CU's 160 KiB");
 
 // Largest decay (nats) of a channel over one chunk for which the Gram
@@ -707,7 +738,6 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
         const BTask tp = btask(f, vp, task, nch);
         const int64_t h = tp.h;
         const float *rc = rec + task * REC_BWD;
-        const float *Sg = hist + task * (BD * BD), *dSg = dhist + task * (BD * BD);
         auto row_of = [&](int r) { return (tp.tok0 + r) * H + h; };
         auto live = [&](int r) { return tp.tok0 + r < tp.tlim; };
         lds_barrier();  // the previous task is done with LDS
@@ -805,7 +835,7 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
         }
 
         // ---- value columns 16 wv + m: Bm V, X, M, dM, Y, dV
-        f4 sr[8], dr[8];  // rows c = 16 wv + m of S and dSo (loaded in the value phase)
+        f4 sr[8], dr[8];  // rows c = 16 wv + m of S and dSo (from the columns, through LDS)
         {
             const int col = vcol;
             float v4[4], o4[4];
@@ -835,18 +865,6 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
 #pragma unroll
             for (int j = 0; j < 4; ++j) Y = mfma4(L.tm[(4 * kq + j) * TP + m], dM[j], Y);
             f4 dV = chan_product(L.ut, dS, m, kq, f4{0.f, 0.f, 0.f, 0.f});
-            // S and dSo are consumed as columns: their rows, for the channel
-            // products below, are requested now, while the lines just read
-            // as columns are still in L2 (requested later, they came from
-            // HBM a second time)
-            {
-                const float *srow = Sg + (16 * wv + m) * BD, *drow = dSg + (16 * wv + m) * BD;
-#pragma unroll
-                for (int jt = 0; jt < 8; ++jt) {
-                    sr[jt] = *reinterpret_cast<const f4 *>(srow + 16 * jt + 4 * kq);
-                    dr[jt] = *reinterpret_cast<const f4 *>(drow + 16 * jt + 4 * kq);
-                }
-            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 dV = mfma4(L.pp[(4 * kq + j) * TP + m], o4[j], dV);
@@ -884,6 +902,31 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
             }
         }
         lds_barrier();
+
+        // ---- S and dSo from value columns (registers of the value products)
+        //      to key rows (the channel products'), through LDS, 64 columns at
+        //      a time (the four waves that own them write, every wave reads
+        //      its rows' part): each is read from HBM once
+        {
+            auto rows_half = [&](const f4 (&cols)[8], f4 (&rows)[8], int half) __attribute__((always_inline)) {
+                if ((wv >> 2) == half) {
+                    const int cl = 16 * (wv & 3) + m;
+#pragma unroll
+                    for (int it = 0; it < 8; ++it)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) L.tr[(16 * it + 4 * kq + i) * TRP + cl] = cols[it][i];
+                }
+                lds_barrier();
+                const float *src = &L.tr[(16 * wv + m) * TRP + 4 * kq];
+#pragma unroll
+                for (int jt = 0; jt < 4; ++jt) rows[4 * half + jt] = *reinterpret_cast<const f4 *>(src + 16 * jt);
+                lds_barrier();
+            };
+            rows_half(S, sr, 0);
+            rows_half(S, sr, 1);
+            rows_half(dS, dr, 0);
+            rows_half(dS, dr, 1);
+        }
 
         // ---- key channels c = 16 wv + m: dW, dQbar, dEtil, dUtil (over the
         //      value columns, S and dSo read as rows), the exit decay's term
@@ -1169,11 +1212,9 @@ hipError_t launch_bwd_d128(const BwdArgs &a, const VarPlan &vp, float *rec, floa
     hipLaunchKernelGGL(bwd_record_kernel, dim3(static_cast<unsigned>(g1)), dim3(BNT), 0, s, a, vp, rec, nch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned g2 = static_cast<unsigned>(f.B * f.H * 2);
-    hipLaunchKernelGGL(bwd_state_kernel, dim3(g2), dim3(SNT), 0, s, a, vp, static_cast<const float *>(rec), hist, nch);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dgrad_kernel, dim3(g2), dim3(SNT), 0, s, a, vp, static_cast<const float *>(rec), dhist,
-                       nch);
+    const unsigned g2 = static_cast<unsigned>(f.B * f.H * 4);  // (chain, value half) x (state, gradient)
+    hipLaunchKernelGGL(bwd_scans_kernel, dim3(g2), dim3(SNT), 0, s, a, vp, static_cast<const float *>(rec), hist,
+                       dhist, nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t g3 = tasks < cus ? tasks : cus;  // one 137 KiB workgroup per CU
     hipLaunchKernelGGL(bwd_grads128_kernel, dim3(static_cast<unsigned>(g3)), dim3(GNT), 0, s, a, vp,

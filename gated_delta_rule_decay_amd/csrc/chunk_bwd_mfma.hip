@@ -406,6 +406,22 @@ __device__ __forceinline__ f4 chan_half(const float *A, const f4 (&B)[4], int m,
     return (acc[0] + acc[1]) + (acc[2] + acc[3]);
 }
 
+// The state records (hist, dhist) are stored tile-major, in the accumulator
+// layout that writes and reads them: element (16 it + 4 kq + i, 16 cg + m) of
+// a 128 x 128 state sits at ((it * 8 + cg) * 64 + 16 kq + m) * 4 + i, so the
+// four rows a lane holds are one 16-byte word and a wave's key tile of its 16
+// value columns is 1 KiB of contiguous memory.
+__device__ __forceinline__ int64_t tile_off(int it, int cg, int lane) {
+    return static_cast<int64_t>((it * 8 + cg) * 64 + lane) * 4;
+}
+
+// Store a wave's half state slice (tiles 4 kh + t of its 16 columns, column
+// group cg) as a state record.
+__device__ __forceinline__ void put_tiles(float *dst, const f4 (&s)[4], int kh, int cg, int lane) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) *reinterpret_cast<f4 *>(dst + tile_off(4 * kh + t, cg, lane)) = s[t];
+}
+
 // Store a wave's half state slice (tiles 4 kh + t, 64 x 16) into a [128][128] matrix.
 __device__ __forceinline__ void put_half(float *dst, const f4 (&s)[4], int kq, int kh, int col) {
 #pragma unroll
@@ -442,7 +458,8 @@ struct ScanLds8 {
     f4 xp[8 * 64];  // the waves' half products
 };
 
-// The state entering every chunk, hist[chain][chunk][128][128], from S0.
+// The state entering every chunk (hist: one tile-major 128 x 128 record per
+// chain and chunk), from S0.
 __device__ __forceinline__ void state_scan(const BwdArgs &a, const VarPlan &vp, const float *rec, float *hist,
                                            int nch, ScanLds8 &LL, const ScanUnit su) {
     ScanLds &L = LL.r;
@@ -484,7 +501,7 @@ __device__ __forceinline__ void state_scan(const BwdArgs &a, const VarPlan &vp, 
             stage_load8(st, rc(n + 1), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
             load_vals_raw(vn, ch.tbase + (n + 1) * BC, ch.tlim, h, kq, col, f);
         }
-        put_half(hs(n), S, kq, kh, col);
+        put_tiles(hs(n), S, kh, col >> 4, lane);
         __syncthreads();  // chunk n's LDS copy complete
         // X = Kbar S + Bm V (token rows)
         f4 X = pair_sum(LL.xp, chan_half(L.m0, S, m, kq, kh), wv, lane, kh);
@@ -521,8 +538,8 @@ __device__ __forceinline__ void state_scan(const BwdArgs &a, const VarPlan &vp, 
     }
 }
 
-// The gradient of every chunk's exit state, dhist[chain][chunk][128][128],
-// carried backwards from d_sT; the gradient of S0 at the end.
+// The gradient of every chunk's exit state (dhist, tile-major like hist),
+// carried backwards from d_sT; the gradient of S0 (row-major) at the end.
 __device__ __forceinline__ void dgrad_scan(const BwdArgs &a, const VarPlan &vp, const float *rec, float *dhist,
                                            int nch, ScanLds8 &LL, const ScanUnit su) {
     ScanLds &L = LL.r;
@@ -561,7 +578,7 @@ __device__ __forceinline__ void dgrad_scan(const BwdArgs &a, const VarPlan &vp, 
             stage_load8(st, rc(n - 1), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
             load_rows_raw(on.x, a.d_o, 0, f.H, h, ch.tbase + static_cast<int64_t>(n - 1) * BC, ch.tlim, kq, col);
         }
-        put_half(hs(n), dS, kq, kh, col);
+        put_tiles(hs(n), dS, kh, col >> 4, lane);
         __syncthreads();  // chunk n's LDS copy complete
         // dM = -(Etil dSo + R^T dO)  (token rows)
         f4 dM = pair_sum(LL.xp, chan_half(L.m0, dS, m, kq, kh), wv, lane, kh);
@@ -714,18 +731,17 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
     const bool la_key = f.la_key, eb_key = f.eb_key, wr_key = f.wr_key, tied = f.wr == nullptr;
     const bool vw = f.value_write;  // read along b k, erase / write along k, values w .* v
     // this wave's value columns of S and dSo, consumed by the value products;
-    // the next task's are loaded while this one finishes
+    // the next task's are loaded during this one's second half
     f4 S[8], dS[8];
     auto load_sd = [&](int64_t t) __attribute__((always_inline)) {
-        const int vc = 16 * (threadIdx.x >> 6) + (threadIdx.x & 15), kk = (threadIdx.x >> 4) & 3;
+        // the state records' tiles of column group (wave) threadIdx.x / 64
+        const int cg = threadIdx.x >> 6, ln = threadIdx.x & 63;
         const float *sg = hist + t * (BD * BD), *dsg = dhist + t * (BD * BD);
 #pragma unroll
-        for (int it = 0; it < 8; ++it)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                S[it][i] = sg[(16 * it + 4 * kk + i) * BD + vc];
-                dS[it][i] = dsg[(16 * it + 4 * kk + i) * BD + vc];
-            }
+        for (int it = 0; it < 8; ++it) {
+            S[it] = *reinterpret_cast<const f4 *>(sg + tile_off(it, cg, ln));
+            dS[it] = *reinterpret_cast<const f4 *>(dsg + tile_off(it, cg, ln));
+        }
     };
     if (static_cast<int64_t>(blockIdx.x) < ntask) load_sd(blockIdx.x);
     for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
@@ -740,14 +756,14 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
         const float *rc = rec + task * REC_BWD;
         auto row_of = [&](int r) { return (tp.tok0 + r) * H + h; };
         auto live = [&](int r) { return tp.tok0 + r < tp.tlim; };
-        lds_barrier();  // the previous task is done with LDS
-
         const int vcol = 16 * wv + m;
 
         // ---- the chunk's record, raw operands, V and dO.  Every load is issued
         //      before any is used (rows past the sequence end read as zero
         //      through the buffer range; bf16 / fp32 and per-channel / per-head
-        //      operands differ only in offsets), then converted into LDS.
+        //      operands differ only in offsets), and before the barrier that
+        //      waits for the previous task's last LDS reads, then converted
+        //      into LDS.
         f4 xr[3], xt;
         float xg;
 #pragma unroll
@@ -759,7 +775,6 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
             xg = rc[R_GM + tid - 256];
         f4 bb, ww;  // erase / write gates of token tid / 32, channels c4 .. c4 + 3 (for the last phase)
         const int r = tid >> 5, c4 = 4 * (tid & 31);
-        if (tid == 0) L.steep = 0;
         {
             const int es = f.bf16 ? 2 : 4;
             // dword j of my four channels: bf16 takes two words, fp32 four
@@ -793,6 +808,8 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
             auto gate = [&](const uint32_t (&w)[4]) {
                 return f4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3])};
             };
+            lds_barrier();  // the previous task is done with LDS
+            if (tid == 0) L.steep = 0;
             // the record parts into LDS
 #pragma unroll
             for (int p = 0; p < 3; ++p)
@@ -960,6 +977,10 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
         }
         lds_barrier();
 
+        // the next task's state records: requested here, once the rows have
+        // gone through LDS, so that they arrive while this task's 16 x 16 and
+        // Gram gradients run
+        if (task + gridDim.x < ntask) load_sd(task + gridDim.x);
         // ---- dKbar = Tm^T dW (registers); the 16 x 16 gradients
         f4 dKb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1187,7 +1208,6 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
                 if (!tied && !wr_key) a.dwr[row] = sw;
             }
         }
-        if (task + gridDim.x < ntask) load_sd(task + gridDim.x);
     }
 }
 

@@ -455,7 +455,8 @@ def main():
         result["packed_long"] = packed_line(w, d, torch, es, ew, lengths=[28000, 2000, 1500, 1268])
     del d, inp
     if not args.no_extra:
-        result["fused_inputs"] = fused_line(w, torch, es, ew)
+        # timed like the main line (same steps and warmup), so the two compare
+        result["fused_inputs"] = fused_line(w, torch, args.steps, args.warmup, tm["kms"])
         # long context: one sequence per head, T = 65536 (two-level scan)
         w3 = W[3]
         log(f"[bench] generating {w3.name} inputs")
@@ -571,9 +572,10 @@ def packed_line(w, d, torch, steps, warmup, n_seq=12, lengths=None):
                 t, tot, nbytes, read_traffic(f"chunk_fwd_{tag}", w.name, source_hash(CHUNK_SOURCES)))
 
 
-def fused_line(w, torch, steps, warmup):
+def fused_line(w, torch, steps, warmup, plain_kms):
     """The forward on raw inputs: bf16 gate logits activated and q, k
-    L2-normalised inside the kernels (same draws as the main workload)."""
+    L2-normalised inside the kernels (same draws as the main workload);
+    `plain_kms` is the main line's event time per call, for the ratio."""
     from gated_delta_rule_decay_amd import binding, chunk_fwd, synth
 
     log(f"[bench] generating raw {w.name} inputs")
@@ -593,7 +595,8 @@ def fused_line(w, torch, steps, warmup):
                    torch, f"chunk_fwd_raw_inputs_{w.name}")
     return line(f"{w.name} on raw inputs: bf16 gate logits (-softplus / sigmoid in-kernel), q and k "
                 f"L2-normalised in-kernel", t, w.B * w.T, fused_bytes(w),
-                read_traffic("chunk_fwd_raw_inputs", w.name, source_hash(CHUNK_SOURCES)))
+                read_traffic("chunk_fwd_raw_inputs", w.name, source_hash(CHUNK_SOURCES)),
+                fused_over_plain_time=round(t["kms"] / plain_kms, 3))
 
 
 # ---- profiles: rocprofv3 CSVs -> profiles/*.txt ------------------------------

@@ -151,6 +151,17 @@ __device__ __forceinline__ int64_t btask_count(const ChunkArgs &f, const VarPlan
     return f.cu ? f.H * vp.pfx[f.B] : f.B * f.H * nch;
 }
 
+// Buffer resource over rows tok0 .. tlim-1 (at most one chunk) of head h of
+// a [tokens, H, width] tensor with elements of es bytes: the hardware returns
+// zero for rows past tlim, so loads through it need no select (and no wait).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void *p, int64_t H, int64_t h, int64_t tok0,
+                                                           int64_t tlim, int width, int es) {
+    const int64_t n = tlim - tok0 < BC ? (tlim - tok0 > 0 ? tlim - tok0 : 0) : BC;
+    const char *base = static_cast<const char *>(p) + (tok0 * H + h) * width * es;
+    const int bytes = n > 0 ? static_cast<int>(((n - 1) * H * width + width) * es) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, bytes, 0x00020000);
+}
+
 // ---------------------------------------------------------------------------
 // the record pass
 
@@ -190,40 +201,91 @@ struct RecLds {
     float A[BC * BC];
 };
 
+// The raw input words of one record task for a thread's two channel quads
+// (rows tid / 32 and tid / 32 + 8, channels 4 (tid % 32) .. + 3): q and k as
+// bf16 pairs (words 0, 1) or fp32 (words 0..3), the gates as fp32 (element 0
+// only for a gate per head).  Loaded through buffer ranges (rows past the
+// sequence end read as zero), converted only when the task is staged, so a
+// task's loads stay in flight while the previous task computes.
+struct RecRaw {
+    uint32_t k[2][4], q[2][4];
+    f4 la[2], eb[2], wr[2];
+};
+
+__device__ __forceinline__ void rec_issue(RecRaw &R, const ChunkArgs &f, const BTask &tp, int tid) {
+    const int64_t H = f.H, h = tp.h;
+    const int es = f.bf16 ? 2 : 4;
+    const auto rk = rows_rsrc(f.k, H, h, tp.tok0, tp.tlim, BD, es);
+    const auto rq = rows_rsrc(f.q, H, h, tp.tok0, tp.tlim, BD, es);
+    const int lw = f.la_key ? BD : 1, ew = f.eb_key ? BD : 1, ww = f.wr && f.wr_key ? BD : 1;
+    const auto rla = rows_rsrc(f.la, H, h, tp.tok0, tp.tlim, lw, 4);
+    const auto reb = rows_rsrc(f.eb, H, h, tp.tok0, tp.tlim, ew, 4);
+    const auto rwr = rows_rsrc(f.wr ? f.wr : f.eb, H, h, tp.tok0, tp.tlim, f.wr ? ww : ew, 4);
+    auto gate = [&](__amdgpu_buffer_rsrc_t rs, int width, int r, int c4) {
+        if (width == BD)
+            return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>((r * H * BD + 4 * c4) * 4), 0, 0));
+        return f4{__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, static_cast<int>(r * H * 4), 0, 0)), 0.f, 0.f, 0.f};
+    };
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int qd = tid + BNT * p, r = qd / 32, c4 = qd % 32;
+        const int off = static_cast<int>((r * H * BD + 4 * c4) * es);
+        if (f.bf16) {
+            const uint2 a = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, off, 0, 0));
+            const uint2 b = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rq, off, 0, 0));
+            R.k[p][0] = a.x; R.k[p][1] = a.y; R.k[p][2] = R.k[p][3] = 0;
+            R.q[p][0] = b.x; R.q[p][1] = b.y; R.q[p][2] = R.q[p][3] = 0;
+        } else {
+            const uint4 a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+            const uint4 b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+            R.k[p][0] = a.x; R.k[p][1] = a.y; R.k[p][2] = a.z; R.k[p][3] = a.w;
+            R.q[p][0] = b.x; R.q[p][1] = b.y; R.q[p][2] = b.z; R.q[p][3] = b.w;
+        }
+        R.la[p] = gate(rla, lw, r, c4);
+        R.eb[p] = gate(reb, ew, r, c4);
+        R.wr[p] = f.wr ? gate(rwr, ww, r, c4) : R.eb[p];
+    }
+}
+
 __global__ void __launch_bounds__(BNT) bwd_record_kernel(BwdArgs a, VarPlan vp, float *rec, int nch) {
     __shared__ RecLds L;
     const ChunkArgs &f = a.f;
-    const int64_t H = f.H;
     const int64_t ntask = btask_count(f, vp, nch);
     const int tid = threadIdx.x;
+    RecRaw R;
+    if (static_cast<int64_t>(blockIdx.x) < ntask) rec_issue(R, f, btask(f, vp, blockIdx.x, nch), tid);
     for (int64_t task = blockIdx.x; task < ntask; task += gridDim.x) {
-        const BTask tp = btask(f, vp, task, nch);
-        const int64_t h = tp.h;
         float *out = rec + task * REC_BWD;
         __syncthreads();  // the previous task is done with LDS
         // ---- operands: thread = channel quad c4 of rows r (two quads each)
+        auto qkv = [&](const uint32_t (&w)[4]) {
+            return f.bf16 ? f4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                               __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)}
+                          : f4{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]),
+                               __uint_as_float(w[3])};
+        };
+        auto bcast = [](f4 x, int key) { return key ? x : f4{x[0], x[0], x[0], x[0]}; };
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const int qd = tid + BNT * p, r = qd / 32, c4 = qd % 32;
-            f4 kv = {0.f, 0.f, 0.f, 0.f}, qv = kv, la = kv, e = kv, u = kv;
-            if (tp.tok0 + r < tp.tlim) {
-                const int64_t row = (tp.tok0 + r) * H + h;
-                kv = load_qkv4(f.k, row * BD + 4 * c4, f.bf16);
-                qv = f.q_scale * load_qkv4(f.q, row * BD + 4 * c4, f.bf16);
-                la = LOG2E * load_gate4(f.la, f.la_key, row, 4 * c4);
-                const f4 bb = load_gate4(f.eb, f.eb_key, row, 4 * c4);
-                if (f.value_write) {  // read along b k, erase and write along k
-                    e = u = kv;
-                    kv *= bb;
-                } else {
-                    const f4 ww = f.wr ? load_gate4(f.wr, f.wr_key, row, 4 * c4) : bb;
-                    e = bb * kv;
-                    u = ww * kv;
-                }
+            f4 kv = qkv(R.k[p]);
+            const f4 qv = f.q_scale * qkv(R.q[p]);
+            const f4 la = LOG2E * bcast(R.la[p], f.la_key);
+            const f4 bb = bcast(R.eb[p], f.eb_key);
+            f4 e, u;
+            if (f.value_write) {  // read along b k, erase and write along k
+                e = u = kv;
+                kv *= bb;
+            } else {
+                const f4 ww = f.wr ? bcast(R.wr[p], f.wr_key) : bb;
+                e = bb * kv;
+                u = ww * kv;
             }
             const int li = c4 * QP + r;
             L.K[li] = kv; L.Q[li] = qv; L.G[li] = la; L.E[li] = e; L.U[li] = u;
         }
+        // the next task's loads go out now, to arrive while this one computes
+        if (task + gridDim.x < ntask) rec_issue(R, f, btask(f, vp, task + gridDim.x, nch), tid);
         __syncthreads();
         if (tid < BD) {  // running log2-decay per channel (padded rows add 0)
             float *g = reinterpret_cast<float *>(L.G) + (tid / 4) * QP * 4 + (tid % 4);
@@ -301,17 +363,6 @@ struct ScanLds {
     float t0[BC * BC], t1[BC * BC];
     float gm[BD];
 };
-
-// Buffer resource over rows tok0 .. tlim-1 (at most one chunk) of head h of
-// a [tokens, H, width] tensor with elements of es bytes: the hardware returns
-// zero for rows past tlim, so loads through it need no select (and no wait).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void *p, int64_t H, int64_t h, int64_t tok0,
-                                                           int64_t tlim, int width, int es) {
-    const int64_t n = tlim - tok0 < BC ? (tlim - tok0 > 0 ? tlim - tok0 : 0) : BC;
-    const char *base = static_cast<const char *>(p) + (tok0 * H + h) * width * es;
-    const int bytes = n > 0 ? static_cast<int>(((n - 1) * H * width + width) * es) : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, bytes, 0x00020000);
-}
 
 // The raw words of lane (kq, n)'s rows 4 kq + j of a chunk at column col of a
 // [tokens, H, 128] tensor (bf16 bits in the low half, or fp32 bits), zero

@@ -318,6 +318,15 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
 
     for (; task < ntask; task += gridDim.x) {
         __syncthreads();  // previous task done with every buffer (and with S.wide)
+        // the next task's position, for its loads (prefetched in four parts
+        // below); formed first, since for packed sequences it is read from the
+        // chunk table.  Without a next task the loads still issue, over an
+        // empty range (they read zeros and touch no memory): every path through
+        // the loop then has the same memory operations in flight, so the waits
+        // before the first use of each part count only what was issued after it.
+        const int64_t next = task + gridDim.x;
+        TaskPos pn = task_pos(a, w, next < ntask ? next : task, nc);
+        if (next >= ntask) pn.tlim = pn.t0;
         if (tid == 0) S.wide = 0;
         // lane coordinates, re-derived every task so that the LDS addresses
         // built from them are not hoisted out of the loop (and spilled)
@@ -367,13 +376,6 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         // ---- factored fp16 Gram operands -------------------------------------
         f4 khf[RPS], qhf[RPS], egm;
         factored_operands<PrepSmem, TIED, GK, 2, VW>(S, R, g, khf, qhf, egm, seg, cq, a.q_scale, logits, qknorm);
-        const int64_t next = task + gridDim.x;  // prefetched in four parts below
-        TaskPos pn = task_pos(a, w, next < ntask ? next : task, nc);
-        // Without a next task the loads still issue, over an empty range (they
-        // read zeros and touch no memory): every path through the loop then
-        // has the same memory operations in flight, so the waits before the
-        // first use of each part count only what was issued after it.
-        if (next >= ntask) pn.tlim = pn.t0;
         load_part<3, TIED, GK, VW, RAW>(R, a, pn, tid);
         __syncthreads();
 

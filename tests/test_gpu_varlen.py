@@ -11,8 +11,9 @@ batched forward (bit-exact: the same chunks through the same kernels) and a
 drawn length mix on every (sequence, head) chain.  The backward over packed
 sequences (gdn2_chunk_bwd_varlen) likewise: every sequence's gradients against
 the gradient oracle on that sequence alone (both paths, the value-write form
-and fused input preparation), and bit-exact against the batched backward at
-equal lengths.
+and fused input preparation), bit-exact against the batched backward at
+equal lengths, and at the full size a drawn length mix on every (sequence,
+head) chain against the C oracle's reverse pass.
 """
 import numpy as np
 import pytest
@@ -305,3 +306,41 @@ def test_backward_full_size_equal_lengths_match_batched():
     for key in ("dq", "dk", "dv", "d_log_decay", "d_erase", "d_write"):
         assert torch.equal(flat(gb[key]), gp[key]), key
     assert torch.equal(gb["d_state0"], gp["d_state0"])
+
+
+def test_backward_full_size_length_mix_every_sequence():
+    # the GDN-2 workload's 32768 tokens cut into 12 drawn lengths, 16 heads:
+    # every (sequence, head) chain's gradients against the C oracle's reverse
+    # pass on that sequence alone, per chain (ragged last chunks, and the
+    # scans' and gradient kernel's chain mapping over packed sequences)
+    import torch
+    from gated_delta_rule_decay_amd import chunk_bwd_varlen
+    from oracle.oracle import gdn2_backward_c
+    from tests.parity_util import check_every_chain
+
+    w = W[2]
+    lengths = synth.draw_lengths(w.B * w.T, 12, seed=950)
+    inp = synth.make_packed_inputs(w, lengths, seed=955)
+    cu = inp["cu_seqlens"]
+    r = np.random.Generator(np.random.PCG64(956))
+    d_o = r.standard_normal(inp["v"].shape).astype(np.float32)
+    d_st = r.standard_normal(inp["S0"].shape).astype(np.float32)
+    d = _dev(inp)
+    gn = _gates(inp, False)
+    sq = lambda x: None if x is None else x[0]
+    g = chunk_bwd_varlen(sq(d["q"]), sq(d["k"]), sq(d["v"]), *[sq(d.get(x)) for x in gn], d["cu"], d["S0"],
+                         torch.from_numpy(d_o[0]).cuda(), torch.from_numpy(d_st).cuda())
+    torch.cuda.synchronize()
+    got = {k: (None if x is None else x.cpu().numpy()) for k, x in g.items()}
+    names = ("dq", "dk", "dv", "d_log_decay", "d_erase", "d_write")
+    for i in range(len(lengths)):
+        lo, hi = int(cu[i]), int(cu[i + 1])
+        if hi == lo:  # an empty sequence passes its state gradient through
+            assert np.array_equal(got["d_state0"][i], d_st[i])
+            continue
+        sl = lambda x: None if x is None else x[:, lo:hi]
+        ref = gdn2_backward_c(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), *[sl(inp.get(x)) for x in gn],
+                              inp["S0"][i:i + 1], sl(d_o), d_st[i:i + 1])
+        tensors = [(n, got[n][lo:hi], ref[n][0], (0, 2)) for n in names if got[n] is not None]
+        tensors.append(("d_state0", got["d_state0"][i], ref["d_state0"][0], (1, 2)))
+        check_every_chain(f"packed backward, sequence {i} ({hi - lo} tokens)", tensors, TOL_F32)

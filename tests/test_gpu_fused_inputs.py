@@ -12,7 +12,7 @@ import pytest
 
 from gated_delta_rule_decay_amd import synth
 from oracle.oracle import gdn2_forward_raw
-from tests.parity_util import TOL_BF16, TOL_F32, rel_l2
+from tests.parity_util import TOL_BF16, TOL_F32, check_every_chain, rel_l2
 
 pytestmark = pytest.mark.gpu
 W = synth.WORKLOADS
@@ -68,6 +68,26 @@ def test_kda_gate_logits(ws):
     inp["x_erase"] = np.ascontiguousarray(inp["x_erase"][..., 0])
     inp["x_erase_bf16"] = np.ascontiguousarray(inp["x_erase_bf16"][..., 0])
     _check(w, inp, ws=ws)
+
+
+def test_full_size_every_chain():
+    # the GDN-2 workload's draws as raw inputs (bf16 gate logits, q and k
+    # unnormalised), as the bench times them: the two-pass kernels with both
+    # preparations fused, every chain against the oracle's fp64 preparation
+    # and recurrence
+    import torch
+    from gated_delta_rule_decay_amd import chunk_fwd
+
+    w = W[2]
+    inp = synth.make_raw_inputs(w, wid=2)
+    d = _dev(inp)
+    o, S = chunk_fwd(d["q"], d["k"], d["v"], d["x_decay"], d["x_erase"], d["x_write"], d["S0"], chunk=w.chunk,
+                     qk_l2norm=True)
+    torch.cuda.synchronize()
+    o_ref, S_ref = gdn2_forward_raw(inp["q"], inp["k"], inp["v"], inp["x_decay"], inp["x_erase"],
+                                    inp["x_write"], inp["S0"], qk_l2norm=True)
+    check_every_chain(f"{w.name} raw inputs", [("o", o.cpu().numpy(), o_ref, (1, 3)),
+                                             ("S", S.cpu().numpy(), S_ref, (2, 3))], TOL_BF16)
 
 
 def test_logits_without_norm():

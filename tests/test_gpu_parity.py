@@ -256,6 +256,26 @@ def test_full_size_every_chain(wid):
         del o, S
 
 
+def test_full_size_kda_every_chain():
+    # KDA's gates on the GDN-2 workload's shape, as the bench times them: the
+    # per-channel decay kept, one tied rate per token-head (the first
+    # channel's erase draw), the two-pass kernels; every chain against the
+    # oracle
+    import torch
+    from gated_delta_rule_decay_amd import chunk_fwd
+
+    w = W[2]
+    inp = synth.make_inputs(w, wid=2)
+    inp["erase"] = np.ascontiguousarray(inp["erase"][..., 0])
+    inp["write"] = None
+    o_ref, S_ref = oracle_chunk(inp)
+    d = to_device(inp)
+    o, S = chunk_fwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], None, d["S0"], chunk=w.chunk)
+    torch.cuda.synchronize()
+    check_every_chain(f"{w.name} KDA gates", [("o", o.cpu().numpy(), o_ref, (1, 3)),
+                                            ("S", S.cpu().numpy(), S_ref, (2, 3))], TOL_BF16)
+
+
 def test_full_size_decode_every_head():
     # the decode workload as written: 256 sequences x 16 heads, the fp32 state
     # carried in place across 1024 consecutive steps; every head is checked

@@ -169,3 +169,24 @@ def test_full_size_every_chain():
     again = _bwd_full(w, inp, d_o, d_st)
     for n in NAMES:
         assert np.array_equal(got[n], again[n]), f"{n} differs between two identical calls"
+
+
+def test_full_size_gated_deltanet_every_chain():
+    # the Gated DeltaNet workload (B4 H16 T4096: one decay and one tied rate
+    # per token-head, zero initial state) through the matrix-core backward,
+    # every one of its 64 chains against the C oracle's reverse pass
+    from oracle.oracle import gdn2_backward_c
+
+    w = W[1]
+    inp = synth.make_inputs(w, wid=1)
+    r = np.random.Generator(np.random.PCG64(535))
+    d_o = r.standard_normal((w.B, w.T, w.H, w.dv)).astype(np.float32)
+    d_st = r.standard_normal((w.B, w.H, w.dk, w.dv)).astype(np.float32)
+    got = _bwd_full(w, inp, d_o, d_st)
+    ref = gdn2_backward_c(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"],
+                          inp["S0"], d_o, d_st)
+    tok = (1, 3)
+    head = (1,)  # per-head gates [B,T,H]: a chain is (b, h), its tokens on axis 1
+    axes = {"d_state0": (2, 3), "d_log_decay": head, "d_erase": head}
+    check_every_chain("gdn-scalar backward", [(n, got[n], ref[n], axes.get(n, tok))
+                                              for n in NAMES if ref[n] is not None], TOL)

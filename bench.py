@@ -464,6 +464,8 @@ def main():
         t = chunk_line(w3, d3, w3.name, es, ew, torch, profile="chunk_fwd_" + w3.name)
         result["long_context"] = line(f"{w3.name}: B={w3.B} H={w3.H} T={w3.T}, decay spikes", t, w3.B * w3.T,
                                       chunk_bytes(w3), read_traffic("chunk_fwd", w3.name, chunk_hash))
+        # its backward: 16 chains, so the state scans run in segments
+        result["long_context_backward"] = backward_line(w3, d3, torch, max(2, args.steps // 8), ew)
         del d3
         # Gated DeltaNet mode: scalar gates tied, zero initial state, B=4
         w1 = W[1]

@@ -813,21 +813,30 @@ static int64_t record_chunks(const ChunkArgs &f, int Cg) {
 }
 
 // Regions of the backward's own workspace: the state records, the
-// gradient records, the per-chunk records (dk = dv = 128), the plan (packed).
+// gradient records, the per-chunk records (dk = dv = 128), the plan (packed),
+// the segment summaries (dk = dv = 128, long sequences on few chains).
 struct CoreLayout {
-    int64_t hist, dhist, rec, plan, bytes;
+    int64_t hist, dhist, rec, plan, segs, bytes;
 };
+
+// Segments per chain of the matrix-core scans (B sequences of T tokens).
+static int core_segments(const ChunkArgs &f, int Cg) {
+    if (f.cu || !matrix_scans(f.dk, f.dv, Cg)) return 1;
+    return bwd_segments(f.B * f.H, static_cast<int>((f.T + Cg - 1) / Cg));
+}
 
 static CoreLayout core_layout(const ChunkArgs &f, int Cg) {
     const int64_t chunks = record_chunks(f, Cg);
     const int64_t one = (chunks * f.dk * f.dv * 4 + 255) & ~int64_t(255);
     const int64_t rec = matrix_scans(f.dk, f.dv, Cg) ? static_cast<int64_t>(bwd_record_bytes(chunks)) : 0;
+    const int nseg = core_segments(f, Cg);
     CoreLayout l;
     l.hist = 0;
     l.dhist = one;
     l.rec = 2 * one;
     l.plan = l.rec + ((rec + 255) & ~int64_t(255));
-    l.bytes = l.plan + (f.cu ? static_cast<int64_t>(varlen_plan_bytes(f.B, f.T, Cg)) : 0);
+    l.segs = l.plan + (f.cu ? static_cast<int64_t>(varlen_plan_bytes(f.B, f.T, Cg)) : 0);
+    l.bytes = l.segs + (nseg > 1 ? static_cast<int64_t>(bwd_segment_bytes(f.B * f.H, nseg)) : 0);
     return l;
 }
 
@@ -931,7 +940,9 @@ static hipError_t launch_core(const BwdArgs &a, void *ws, hipStream_t s) {
     hipError_t e;
     if (f.cu && (e = launch_varlen_plan(f.cu, f.B, f.T, Cg, w + l.plan, &vp, s)) != hipSuccess) return e;
     const int nch = static_cast<int>((f.T + Cg - 1) / Cg);
-    if (matrix_scans(dk, dv, Cg)) return launch_bwd_d128(a, vp, reinterpret_cast<float *>(w + l.rec), hist, dhist, nch, s);
+    if (matrix_scans(dk, dv, Cg))
+        return launch_bwd_d128(a, vp, reinterpret_cast<float *>(w + l.rec), hist, dhist,
+                               reinterpret_cast<float *>(w + l.segs), nch, s);
     if ((e = launch_bwd_scans_general(a, vp, Cg, hist, dhist, s)) != hipSuccess) return e;
     const size_t lds = static_cast<size_t>(grad_layout(Cg, dk, dv).total) * 4;
     if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(bwd_grads_kernel),

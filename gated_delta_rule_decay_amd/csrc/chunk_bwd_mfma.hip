@@ -509,10 +509,35 @@ struct ScanLds8 {
     f4 xp[8 * 64];  // the waves' half products
 };
 
-// The state entering every chunk (hist: one tile-major 128 x 128 record per
-// chain and chunk), from S0.
-__device__ __forceinline__ void state_scan(const BwdArgs &a, const VarPlan &vp, const float *rec, float *hist,
-                                           int nch, ScanLds8 &LL, const ScanUnit su) {
+// One scan of a chain's value half: over chunks n0 .. n1 - 1 (n1 < 0: all of
+// the chain's chunks), in order for the states, in reverse for their
+// gradients.  The matrix carried starts as `init` (row-major [128][128]), or
+// as zero, or with `ident` as the identity; `inputs` switches the terms in V
+// (states) or d_o (gradients) on, off for a segment's transition.  `recs`
+// receives the per-chunk records (tile-major; null: none), `out` the matrix
+// leaving the scan (row-major; null: none).
+struct ScanJob {
+    int n0, n1;
+    const float *init;
+    int ident, inputs;
+    float *recs, *out;
+};
+
+// The matrix a job starts from, in this lane's registers (rows 16 (4 kh + t)
+// + 4 kq + i of column col).
+__device__ __forceinline__ void scan_init(f4 (&S)[4], const ScanJob &job, int kq, int kh, int col) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * (4 * kh + t) + 4 * kq + i;
+            S[t][i] = job.init ? job.init[row * BD + col] : (job.ident && row == col ? 1.f : 0.f);
+        }
+}
+
+// The states: entering each chunk (recorded), carried forward.
+__device__ __forceinline__ void state_scan(const BwdArgs &a, const VarPlan &vp, const float *rec, int nch,
+                                           ScanLds8 &LL, const ScanUnit su, const ScanJob &job) {
     ScanLds &L = LL.r;
     const ChunkArgs &f = a.f;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -521,15 +546,12 @@ __device__ __forceinline__ void state_scan(const BwdArgs &a, const VarPlan &vp, 
     const BChain ch = bchain(f, vp, bh, nch);
     const int64_t h = ch.h;
     const int col = 64 * su.half + 16 * (wv & 3) + m;  // this lane's value column (as n)
+    const int n0 = job.n0, n1 = job.n1 < 0 ? ch.nc : job.n1;
     auto rc = [&](int n) { return rec + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(REC_BWD); };
-    auto hs = [&](int n) { return hist + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(BD * BD); };
+    auto hs = [&](int n) { return job.recs + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(BD * BD); };
 
     f4 S[4];  // key channel tiles 4 kh + t
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[t][i] = f.s0 ? f.s0[bh * BD * BD + (16 * (4 * kh + t) + 4 * kq + i) * BD + col] : 0.f;
+    scan_init(S, job, kq, kh, col);
     // the initial state is complete before the loop: no wait inside the loop
     // has to allow for its loads
     __builtin_amdgcn_s_waitcnt(VMCNT0);
@@ -537,22 +559,22 @@ __device__ __forceinline__ void state_scan(const BwdArgs &a, const VarPlan &vp, 
     // m0 = Kbar, m1 = Etil, m2 = Util; t0 = Tm, t1 = Bm
     Staged8 st;
     RawRows vn;
-    float v[4];
-    if (ch.nc > 0) {
-        stage_load8(st, rc(0), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
-        load_vals_raw(vn, ch.tbase, ch.tlim, h, kq, col, f);
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (n0 < n1) {
+        stage_load8(st, rc(n0), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
+        if (job.inputs) load_vals_raw(vn, ch.tbase + static_cast<int64_t>(n0) * BC, ch.tlim, h, kq, col, f);
         stage_store8(st, L, tid);
-        raw_rows4(v, vn, f.bf16, f.value_write);
+        if (job.inputs) raw_rows4(v, vn, f.bf16, f.value_write);
     }
-    for (int n = 0; n < ch.nc; ++n) {
+    for (int n = n0; n < n1; ++n) {
         // the next chunk's loads go out before this chunk's state stores, so
         // that waiting for them (after this chunk's products) never waits
         // for the stores
-        if (n + 1 < ch.nc) {
+        if (n + 1 < n1) {
             stage_load8(st, rc(n + 1), R_KB, R_ET, R_UT, R_TM, R_BM, tid);
-            load_vals_raw(vn, ch.tbase + (n + 1) * BC, ch.tlim, h, kq, col, f);
+            if (job.inputs) load_vals_raw(vn, ch.tbase + (n + 1) * BC, ch.tlim, h, kq, col, f);
         }
-        put_tiles(hs(n), S, kh, col >> 4, lane);
+        if (job.recs) put_tiles(hs(n), S, kh, col >> 4, lane);
         __syncthreads();  // chunk n's LDS copy complete
         // X = Kbar S + Bm V (token rows)
         f4 X = pair_sum(LL.xp, chan_half(L.m0, S, m, kq, kh), wv, lane, kh);
@@ -582,17 +604,18 @@ __device__ __forceinline__ void state_scan(const BwdArgs &a, const VarPlan &vp, 
             S[t] = s;
         }
         __syncthreads();  // every wave done with chunk n's LDS copy
-        if (n + 1 < ch.nc) {
+        if (n + 1 < n1) {
             stage_store8(st, L, tid);
-            raw_rows4(v, vn, f.bf16, f.value_write);
+            if (job.inputs) raw_rows4(v, vn, f.bf16, f.value_write);
         }
     }
+    if (job.out) put_half(job.out, S, kq, kh, col);
 }
 
-// The gradient of every chunk's exit state (dhist, tile-major like hist),
-// carried backwards from d_sT; the gradient of S0 (row-major) at the end.
-__device__ __forceinline__ void dgrad_scan(const BwdArgs &a, const VarPlan &vp, const float *rec, float *dhist,
-                                           int nch, ScanLds8 &LL, const ScanUnit su) {
+// The state gradients: each chunk's exit gradient dSo recorded on entry to
+// its step, carried backwards.
+__device__ __forceinline__ void dgrad_scan(const BwdArgs &a, const VarPlan &vp, const float *rec, int nch,
+                                           ScanLds8 &LL, const ScanUnit su, const ScanJob &job) {
     ScanLds &L = LL.r;
     const ChunkArgs &f = a.f;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -601,35 +624,33 @@ __device__ __forceinline__ void dgrad_scan(const BwdArgs &a, const VarPlan &vp, 
     const BChain ch = bchain(f, vp, bh, nch);
     const int64_t h = ch.h;
     const int col = 64 * su.half + 16 * (wv & 3) + m;
+    const int n0 = job.n0, nl = (job.n1 < 0 ? ch.nc : job.n1) - 1;
     auto rc = [&](int n) { return rec + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(REC_BWD); };
-    auto hs = [&](int n) { return dhist + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(BD * BD); };
+    auto hs = [&](int n) { return job.recs + (ch.task0 + n * ch.tstr) * static_cast<int64_t>(BD * BD); };
 
     f4 dS[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            dS[t][i] = a.d_sT ? a.d_sT[bh * BD * BD + (16 * (4 * kh + t) + 4 * kq + i) * BD + col] : 0.f;
+    scan_init(dS, job, kq, kh, col);
     __builtin_amdgcn_s_waitcnt(VMCNT0);
 
     // m0 = Etil, m1 = Qbar, m2 = Kbar; t0 = Tm, t1 = R
     Staged8 st;
     RawRows on;
-    float o[4];
-    const int nl = ch.nc - 1;
-    if (nl >= 0) {
+    float o[4] = {0.f, 0.f, 0.f, 0.f};
+    if (nl >= n0) {
         stage_load8(st, rc(nl), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
-        load_rows_raw(on.x, a.d_o, 0, f.H, h, ch.tbase + static_cast<int64_t>(nl) * BC, ch.tlim, kq, col);
+        if (job.inputs)
+            load_rows_raw(on.x, a.d_o, 0, f.H, h, ch.tbase + static_cast<int64_t>(nl) * BC, ch.tlim, kq, col);
         stage_store8(st, L, tid);
-        raw_rows4(o, on, 0, 0);
+        if (job.inputs) raw_rows4(o, on, 0, 0);
     }
-    for (int n = nl; n >= 0; --n) {
+    for (int n = nl; n >= n0; --n) {
         // loads of the chunk before go out ahead of this chunk's stores
-        if (n > 0) {
+        if (n > n0) {
             stage_load8(st, rc(n - 1), R_ET, R_QB, R_KB, R_TM, R_RR, tid);
-            load_rows_raw(on.x, a.d_o, 0, f.H, h, ch.tbase + static_cast<int64_t>(n - 1) * BC, ch.tlim, kq, col);
+            if (job.inputs)
+                load_rows_raw(on.x, a.d_o, 0, f.H, h, ch.tbase + static_cast<int64_t>(n - 1) * BC, ch.tlim, kq, col);
         }
-        put_tiles(hs(n), dS, kh, col >> 4, lane);
+        if (job.recs) put_tiles(hs(n), dS, kh, col >> 4, lane);
         __syncthreads();  // chunk n's LDS copy complete
         // dM = -(Etil dSo + R^T dO)  (token rows)
         f4 dM = pair_sum(LL.xp, chan_half(L.m0, dS, m, kq, kh), wv, lane, kh);
@@ -654,12 +675,12 @@ __device__ __forceinline__ void dgrad_scan(const BwdArgs &a, const VarPlan &vp, 
             dS[t] = s;
         }
         __syncthreads();  // every wave done with chunk n's LDS copy
-        if (n > 0) {
+        if (n > n0) {
             stage_store8(st, L, tid);
-            raw_rows4(o, on, 0, 0);
+            if (job.inputs) raw_rows4(o, on, 0, 0);
         }
     }
-    if (a.ds0) put_half(a.ds0 + bh * BD * BD, dS, kq, kh, col);
+    if (job.out) put_half(job.out, dS, kq, kh, col);
 }
 
 // Both scans in one launch: neither reads what the other writes (the reverse
@@ -674,10 +695,99 @@ __global__ void __launch_bounds__(SNT) bwd_scans_kernel(BwdArgs a, VarPlan vp, c
                                                         float *dhist, int nch) {
     __shared__ __attribute__((aligned(16))) ScanLds8 LL;
     const int64_t units = gridDim.x / 2, G = blockIdx.x;
-    if (G < units)
-        state_scan(a, vp, rec, hist, nch, LL, scan_unit(G, units));
+    if (G < units) {
+        const ScanUnit su = scan_unit(G, units);
+        const ScanJob job{0, -1, a.f.s0 ? a.f.s0 + su.chain * BD * BD : nullptr, 0, 1, hist, nullptr};
+        state_scan(a, vp, rec, nch, LL, su, job);
+    } else {
+        const ScanUnit su = scan_unit(G - units, units);
+        const ScanJob job{0, -1, a.d_sT ? a.d_sT + su.chain * BD * BD : nullptr, 0, 1, dhist,
+                          a.ds0 ? a.ds0 + su.chain * BD * BD : nullptr};
+        dgrad_scan(a, vp, rec, nch, LL, su, job);
+    }
+}
+
+// Long sequences on few chains: both scans in segments of `len` chunks (the
+// last may be shorter).  Each step of either scan is affine in the matrix it
+// carries (S <- F_n S + G_n forward, dS <- P_n dSo + H_n backward, F_n and P_n
+// acting on the key rows), and affine maps compose ("Gated DeltaNet" page,
+// "What makes the architecture more than a recurrence"):
+//   summaries  every segment is scanned from zero with its inputs (the states'
+//              first segment from S0, the gradients' last from d_sT, which
+//              makes those results exact already), and the identity through
+//              each inner segment without inputs gives its transition;
+//   combine    the exact entry of every segment follows in order;
+//   rescan     every segment from its exact entry, recording its chunks.
+// Slots: xs, fs hold [2 chains][nseg] row-major 128 x 128 matrices, the
+// states' (chains 0 .. C-1) with segment j's end state in slot j + 1 and its
+// transition in slot j, the gradients' (chains C .. 2C-1) in reverse segment
+// order: segment j's start gradient in slot nseg - j, its transition in slot
+// nseg - 1 - j.  Then "X[s+1] <- F[s] X[s] + X[s+1], s = 1 .. nseg - 2"
+// combines both, and slot 1 of each is exact from the summaries.
+struct BwdSegs {
+    int nseg, len;
+    float *xs, *fs;
+};
+
+// MODE 1: the summaries, 2 nseg - 3 units per (chain, value half) and
+// direction; MODE 0: the rescan, nseg units.  The grid's first half runs the
+// states, the second their gradients.
+template <int MODE>
+__global__ void __launch_bounds__(SNT) bwd_seg_scans_kernel(BwdArgs a, VarPlan vp, const float *rec, float *hist,
+                                                            float *dhist, int nch, BwdSegs sg) {
+    __shared__ __attribute__((aligned(16))) ScanLds8 LL;
+    const int64_t units = gridDim.x / 2, G = blockIdx.x;
+    const bool grad = G >= units;
+    const ScanUnit u = scan_unit(grad ? G - units : G, units);
+    const int nseg = sg.nseg, per = MODE ? 2 * nseg - 3 : nseg;
+    const int64_t C = a.f.B * a.f.H, chain = u.chain / per;
+    const int k = static_cast<int>(u.chain - chain * per);
+    const ScanUnit su{chain, u.half};
+    constexpr int64_t DD = BD * BD;
+    float *xs = sg.xs + (grad ? C + chain : chain) * nseg * DD;
+    float *fs = sg.fs + (grad ? C + chain : chain) * nseg * DD;
+    ScanJob job{0, 0, nullptr, 0, 1, nullptr, nullptr};
+    int j;
+    if (MODE) {
+        const bool from_zero = k < nseg - 1;  // else a transition
+        if (!grad) {
+            j = from_zero ? k : 1 + (k - (nseg - 1));
+            if (from_zero) {
+                job.init = j == 0 && a.f.s0 ? a.f.s0 + chain * DD : nullptr;
+                job.out = xs + (j + 1) * DD;
+            } else {
+                job.ident = 1;
+                job.inputs = 0;
+                job.out = fs + j * DD;
+            }
+        } else {
+            j = from_zero ? nseg - 1 - k : nseg - 2 - (k - (nseg - 1));
+            if (from_zero) {
+                job.init = j == nseg - 1 && a.d_sT ? a.d_sT + chain * DD : nullptr;
+                job.out = xs + (nseg - j) * DD;
+            } else {
+                job.ident = 1;
+                job.inputs = 0;
+                job.out = fs + (nseg - 1 - j) * DD;
+            }
+        }
+    } else {
+        j = k;
+        if (!grad) {
+            job.init = j > 0 ? xs + j * DD : (a.f.s0 ? a.f.s0 + chain * DD : nullptr);
+            job.recs = hist;
+        } else {
+            job.init = j < nseg - 1 ? xs + (nseg - 1 - j) * DD : (a.d_sT ? a.d_sT + chain * DD : nullptr);
+            job.recs = dhist;
+            job.out = j == 0 && a.ds0 ? a.ds0 + chain * DD : nullptr;
+        }
+    }
+    job.n0 = j * sg.len;
+    job.n1 = job.n0 + sg.len < nch ? job.n0 + sg.len : nch;
+    if (!grad)
+        state_scan(a, vp, rec, nch, LL, su, job);
     else
-        dgrad_scan(a, vp, rec, dhist, nch, LL, scan_unit(G - units, units));
+        dgrad_scan(a, vp, rec, nch, LL, su, job);
 }
 
 // ---------------------------------------------------------------------------
@@ -1266,8 +1376,29 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
 
 size_t bwd_record_bytes(int64_t chunks) { return static_cast<size_t>(chunks * REC_BWD * 4); }
 
-hipError_t launch_bwd_d128(const BwdArgs &a, const VarPlan &vp, float *rec, float *hist, float *dhist, int nch,
-                           hipStream_t s) {
+// Segments per chain for the scans: about 128 / chains (so that a
+// direction's rescan has some 256 workgroups), each of at least 64 chunks;
+// one (a single pass) from 32 chains up.  The summaries run about twice the
+// scan work in two rounds of workgroups and the rescan once, at some 4.5
+// against 3.2 us per step for a single pass with its CUs to itself, so the
+// segments pay below about 30 chains (16 chains of 4096 chunks: 7.4 against
+// 13.1 ms).
+int bwd_segments(int64_t chains, int nch) {
+    constexpr int MIN_LEN = 64;
+    if (chains <= 0 || chains >= 32) return 1;
+    int64_t n = 128 / chains;
+    if (n > nch / MIN_LEN) n = nch / MIN_LEN;
+    if (n < 2) return 1;
+    const int64_t len = (nch + n - 1) / n;
+    return static_cast<int>((nch + len - 1) / len);  // no empty segment
+}
+
+size_t bwd_segment_bytes(int64_t chains, int nseg) {
+    return static_cast<size_t>(2 * 2 * chains * nseg) * BD * BD * 4;  // xs, fs; states and gradients
+}
+
+hipError_t launch_bwd_d128(const BwdArgs &a, const VarPlan &vp, float *rec, float *hist, float *dhist, float *segs,
+                           int nch, hipStream_t s) {
     const ChunkArgs &f = a.f;
     // (packed sequences: the bound on the task count; the kernels read the count)
     const int64_t tasks = f.cu ? f.H * varlen_chunk_bound(f.B, f.T, BC) : f.B * f.H * nch;
@@ -1283,9 +1414,29 @@ hipError_t launch_bwd_d128(const BwdArgs &a, const VarPlan &vp, float *rec, floa
     hipLaunchKernelGGL(bwd_record_kernel, dim3(static_cast<unsigned>(g1)), dim3(BNT), 0, s, a, vp, rec, nch);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const unsigned g2 = static_cast<unsigned>(f.B * f.H * 4);  // (chain, value half) x (state, gradient)
-    hipLaunchKernelGGL(bwd_scans_kernel, dim3(g2), dim3(SNT), 0, s, a, vp, static_cast<const float *>(rec), hist,
-                       dhist, nch);
+    const int64_t chains = f.B * f.H;
+    const int nseg = f.cu ? 1 : bwd_segments(chains, nch);
+    if (nseg > 1) {
+        BwdSegs sg;
+        sg.nseg = nseg;
+        sg.len = (nch + nseg - 1) / nseg;
+        sg.xs = segs;
+        sg.fs = segs + 2 * chains * nseg * BD * BD;
+        // (chain, value half, summary) x (state, gradient); then the exact
+        // entries; then (chain, value half, segment) x (state, gradient)
+        const unsigned g1s = static_cast<unsigned>(chains * 2 * (2 * nseg - 3) * 2);
+        hipLaunchKernelGGL(bwd_seg_scans_kernel<1>, dim3(g1s), dim3(SNT), 0, s, a, vp, static_cast<const float *>(rec),
+                           hist, dhist, nch, sg);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = launch_segment_combine(sg.xs, sg.fs, 2 * chains, nseg, s)) != hipSuccess) return e;
+        const unsigned g0s = static_cast<unsigned>(chains * 2 * nseg * 2);
+        hipLaunchKernelGGL(bwd_seg_scans_kernel<0>, dim3(g0s), dim3(SNT), 0, s, a, vp, static_cast<const float *>(rec),
+                           hist, dhist, nch, sg);
+    } else {
+        const unsigned g2 = static_cast<unsigned>(chains * 4);  // (chain, value half) x (state, gradient)
+        hipLaunchKernelGGL(bwd_scans_kernel, dim3(g2), dim3(SNT), 0, s, a, vp, static_cast<const float *>(rec), hist,
+                           dhist, nch);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t g3 = tasks < cus ? tasks : cus;  // one 137 KiB workgroup per CU
     hipLaunchKernelGGL(bwd_grads128_kernel, dim3(static_cast<unsigned>(g3)), dim3(GNT), 0, s, a, vp,

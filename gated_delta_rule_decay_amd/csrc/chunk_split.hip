@@ -1503,6 +1503,14 @@ hipError_t launch_static_kinds(const ChunkArgs &a, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_segment_combine(float *xs, const float *fs, int64_t chains, int nseg, hipStream_t s) {
+    if (nseg <= 2 || chains <= 0) return hipSuccess;
+    ScanPlan sp{};  // no packed plan: slot j of chain c at (c nseg + j) 128 x 128
+    hipLaunchKernelGGL(segment_combine_kernel, dim3(static_cast<unsigned>(chains * (D / CMB_COLS))), dim3(CMB_NTH), 0,
+                       s, xs, fs, nseg, sp, 0, 1);
+    return hipGetLastError();
+}
+
 bool chunk_split_static_fits(int64_t B, int64_t H, int64_t T) {
     return B * H * ((T + C - 1) / C) == 0 || static_plan(B, H, T).wn >= 1;
 }

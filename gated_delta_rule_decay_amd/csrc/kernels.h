@@ -104,8 +104,16 @@ hipError_t launch_chunk_bwd(const BwdArgs &a, void *ws, hipStream_t s);
 // (state and state-gradient scans, per-chunk gradients), through per-chunk
 // records of bwd_record_bytes(B*H*chunks) bytes.
 size_t bwd_record_bytes(int64_t chunks);
-hipError_t launch_bwd_d128(const BwdArgs &a, const VarPlan &vp, float *rec, float *hist, float *dhist, int nch,
-                           hipStream_t s);
+// Long sequences on few chains: the two scans in bwd_segments(chains, nch)
+// segments per chain (1: one pass), through bwd_segment_bytes of segment
+// summaries (B sequences of T tokens only).
+int bwd_segments(int64_t chains, int nch);
+size_t bwd_segment_bytes(int64_t chains, int nseg);
+hipError_t launch_bwd_d128(const BwdArgs &a, const VarPlan &vp, float *rec, float *hist, float *dhist, float *segs,
+                           int nch, hipStream_t s);
+// X[j+1] <- F[j] X[j] + X[j+1] for j = 1 .. nseg - 2, in order, for each of
+// `chains` chains of nseg row-major 128 x 128 slots in xs and fs
+hipError_t launch_segment_combine(float *xs, const float *fs, int64_t chains, int nseg, hipStream_t s);
 
 // Recurrent decode step.
 hipError_t launch_step(const StepArgs &a, hipStream_t s);

@@ -190,3 +190,40 @@ def test_full_size_gated_deltanet_every_chain():
     axes = {"d_state0": (2, 3), "d_log_decay": head, "d_erase": head}
     check_every_chain("gdn-scalar backward", [(n, got[n], ref[n], axes.get(n, tok))
                                               for n in NAMES if ref[n] is not None], TOL)
+
+
+@pytest.mark.parametrize("T", [2048, 4001, 4096])
+def test_segmented_scans(T):
+    # two chains over long sequences: the scans run as segment summaries, the
+    # combine and a rescan (2, 3 and 4 segments of 64 to 85 chunks; T = 4001
+    # ends in a one-token chunk); every chain against the C reverse pass
+    from oracle.oracle import gdn2_backward_c
+
+    w = W[2].scaled(B=1, T=T, H=2)
+    inp = synth.make_inputs(w, seed=620 + T)
+    r = np.random.Generator(np.random.PCG64(621 + T))
+    d_o = r.standard_normal((w.B, w.T, w.H, w.dv)).astype(np.float32)
+    d_st = r.standard_normal((w.B, w.H, w.dk, w.dv)).astype(np.float32)
+    got = _bwd_full(w, inp, d_o, d_st)
+    ref = gdn2_backward_c(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"],
+                          inp["S0"], d_o, d_st)
+    check_every_chain(f"segmented backward T={T}", [(n, got[n], ref[n], (2, 3) if n == "d_state0" else (1, 3))
+                                                    for n in NAMES], TOL)
+
+
+def test_full_size_long_context_every_chain():
+    # the long-context workload (B1 H16 T65536, decay spikes): 16 chains, so
+    # the scans run in 8 segments of 512 chunks; every chain against the C
+    # reverse pass
+    from oracle.oracle import gdn2_backward_c
+
+    w = W[3]
+    inp = synth.make_inputs(w, wid=3)
+    r = np.random.Generator(np.random.PCG64(640))
+    d_o = r.standard_normal((w.B, w.T, w.H, w.dv)).astype(np.float32)
+    d_st = r.standard_normal((w.B, w.H, w.dk, w.dv)).astype(np.float32)
+    got = _bwd_full(w, inp, d_o, d_st)
+    ref = gdn2_backward_c(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], inp["write"],
+                          inp["S0"], d_o, d_st)
+    check_every_chain("long-context backward", [(n, got[n], ref[n], (2, 3) if n == "d_state0" else (1, 3))
+                                                for n in NAMES], TOL)

@@ -87,6 +87,15 @@ def test_value_write_d128(gates):
     _run(w, inp, 64, seed=802, vw=True)
 
 
+def test_value_write_segmented():
+    # one chain of 3072 tokens: the scans in 3 segments (summaries, combine,
+    # rescan) with the value-write form's w .* v in the state terms
+    w = W[2].scaled(B=1, T=3072, H=1)
+    inp = synth.make_inputs(w, seed=810)
+    _value_gate(inp, "write", w, 811, raw=False)
+    _run(w, inp, 64, seed=812, vw=True)
+
+
 @pytest.mark.parametrize("gates", ["key", "head"])
 def test_value_write_general_shapes(gates):
     w = W[2].scaled(B=2, T=37, H=1, dk=48, dv=80, qkv_dtype="f32", gates=gates)

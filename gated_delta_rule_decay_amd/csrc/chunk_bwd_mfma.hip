@@ -473,6 +473,14 @@ __device__ __forceinline__ void put_tiles(float *dst, const f4 (&s)[4], int kh, 
     for (int t = 0; t < 4; ++t) *reinterpret_cast<f4 *>(dst + tile_off(4 * kh + t, cg, lane)) = s[t];
 }
 
+// Store a wave's half state slice (tiles 4 kh + t, 64 x 16) transposed into
+// a [128][128] matrix (element (row, col) at col * 128 + row).
+__device__ __forceinline__ void put_half_t(float *dst, const f4 (&s)[4], int kq, int kh, int col) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        *reinterpret_cast<f4 *>(&dst[col * BD + 16 * (4 * kh + t) + 4 * kq]) = s[t];
+}
+
 // Store a wave's half state slice (tiles 4 kh + t, 64 x 16) into a [128][128] matrix.
 __device__ __forceinline__ void put_half(float *dst, const f4 (&s)[4], int kq, int kh, int col) {
 #pragma unroll
@@ -515,12 +523,12 @@ struct ScanLds8 {
 // as zero, or with `ident` as the identity; `inputs` switches the terms in V
 // (states) or d_o (gradients) on, off for a segment's transition.  `recs`
 // receives the per-chunk records (tile-major; null: none), `out` the matrix
-// leaving the scan (row-major; null: none).
+// leaving the scan (row-major; null: none), `out_t` its transpose (null: none).
 struct ScanJob {
     int n0, n1;
     const float *init;
     int ident, inputs;
-    float *recs, *out;
+    float *recs, *out, *out_t;
 };
 
 // The matrix a job starts from, in this lane's registers (rows 16 (4 kh + t)
@@ -610,6 +618,7 @@ __device__ __forceinline__ void state_scan(const BwdArgs &a, const VarPlan &vp, 
         }
     }
     if (job.out) put_half(job.out, S, kq, kh, col);
+    if (job.out_t) put_half_t(job.out_t, S, kq, kh, col);
 }
 
 // The state gradients: each chunk's exit gradient dSo recorded on entry to
@@ -697,12 +706,12 @@ __global__ void __launch_bounds__(SNT) bwd_scans_kernel(BwdArgs a, VarPlan vp, c
     const int64_t units = gridDim.x / 2, G = blockIdx.x;
     if (G < units) {
         const ScanUnit su = scan_unit(G, units);
-        const ScanJob job{0, -1, a.f.s0 ? a.f.s0 + su.chain * BD * BD : nullptr, 0, 1, hist, nullptr};
+        const ScanJob job{0, -1, a.f.s0 ? a.f.s0 + su.chain * BD * BD : nullptr, 0, 1, hist, nullptr, nullptr};
         state_scan(a, vp, rec, nch, LL, su, job);
     } else {
         const ScanUnit su = scan_unit(G - units, units);
         const ScanJob job{0, -1, a.d_sT ? a.d_sT + su.chain * BD * BD : nullptr, 0, 1, dhist,
-                          a.ds0 ? a.ds0 + su.chain * BD * BD : nullptr};
+                          a.ds0 ? a.ds0 + su.chain * BD * BD : nullptr, nullptr};
         dgrad_scan(a, vp, rec, nch, LL, su, job);
     }
 }
@@ -715,7 +724,10 @@ __global__ void __launch_bounds__(SNT) bwd_scans_kernel(BwdArgs a, VarPlan vp, c
 //   summaries  every segment is scanned from zero with its inputs (the states'
 //              first segment from S0, the gradients' last from d_sT, which
 //              makes those results exact already), and the identity through
-//              each inner segment without inputs gives its transition;
+//              each inner segment without inputs gives its transition; the
+//              gradients' step is the adjoint of the states' (P_n = F_n^T, as
+//              Diag(e^gC) is symmetric), so a segment's gradient transition
+//              is the transpose of its state transition and is not scanned;
 //   combine    the exact entry of every segment follows in order;
 //   rescan     every segment from its exact entry, recording its chunks.
 // Slots: xs, fs hold [2 chains][nseg] row-major 128 x 128 matrices, the
@@ -727,26 +739,27 @@ __global__ void __launch_bounds__(SNT) bwd_scans_kernel(BwdArgs a, VarPlan vp, c
 struct BwdSegs {
     int nseg, len;
     float *xs, *fs;
+    int64_t us;  // workgroups of the states (the grid's first part; the rest: the gradients)
 };
 
-// MODE 1: the summaries, 2 nseg - 3 units per (chain, value half) and
-// direction; MODE 0: the rescan, nseg units.  The grid's first half runs the
-// states, the second their gradients.
+// MODE 1: the summaries, per (chain, value half) 2 nseg - 3 units of the
+// states (nseg - 1 from zero, nseg - 2 transitions) and nseg - 1 of the
+// gradients; MODE 0: the rescan, nseg units of each.
 template <int MODE>
 __global__ void __launch_bounds__(SNT) bwd_seg_scans_kernel(BwdArgs a, VarPlan vp, const float *rec, float *hist,
                                                             float *dhist, int nch, BwdSegs sg) {
     __shared__ __attribute__((aligned(16))) ScanLds8 LL;
-    const int64_t units = gridDim.x / 2, G = blockIdx.x;
-    const bool grad = G >= units;
-    const ScanUnit u = scan_unit(grad ? G - units : G, units);
-    const int nseg = sg.nseg, per = MODE ? 2 * nseg - 3 : nseg;
+    const int64_t G = blockIdx.x;
+    const bool grad = G >= sg.us;
+    const ScanUnit u = grad ? scan_unit(G - sg.us, gridDim.x - sg.us) : scan_unit(G, sg.us);
+    const int nseg = sg.nseg, per = MODE ? (grad ? nseg - 1 : 2 * nseg - 3) : nseg;
     const int64_t C = a.f.B * a.f.H, chain = u.chain / per;
     const int k = static_cast<int>(u.chain - chain * per);
     const ScanUnit su{chain, u.half};
     constexpr int64_t DD = BD * BD;
     float *xs = sg.xs + (grad ? C + chain : chain) * nseg * DD;
     float *fs = sg.fs + (grad ? C + chain : chain) * nseg * DD;
-    ScanJob job{0, 0, nullptr, 0, 1, nullptr, nullptr};
+    ScanJob job{0, 0, nullptr, 0, 1, nullptr, nullptr, nullptr};
     int j;
     if (MODE) {
         const bool from_zero = k < nseg - 1;  // else a transition
@@ -755,21 +768,16 @@ __global__ void __launch_bounds__(SNT) bwd_seg_scans_kernel(BwdArgs a, VarPlan v
             if (from_zero) {
                 job.init = j == 0 && a.f.s0 ? a.f.s0 + chain * DD : nullptr;
                 job.out = xs + (j + 1) * DD;
-            } else {
+            } else {  // the transition, and transposed the gradients' (their slot nseg - 1 - j)
                 job.ident = 1;
                 job.inputs = 0;
                 job.out = fs + j * DD;
+                job.out_t = sg.fs + ((C + chain) * nseg + nseg - 1 - j) * DD;
             }
         } else {
-            j = from_zero ? nseg - 1 - k : nseg - 2 - (k - (nseg - 1));
-            if (from_zero) {
-                job.init = j == nseg - 1 && a.d_sT ? a.d_sT + chain * DD : nullptr;
-                job.out = xs + (nseg - j) * DD;
-            } else {
-                job.ident = 1;
-                job.inputs = 0;
-                job.out = fs + (nseg - 1 - j) * DD;
-            }
+            j = nseg - 1 - k;
+            job.init = j == nseg - 1 && a.d_sT ? a.d_sT + chain * DD : nullptr;
+            job.out = xs + (nseg - j) * DD;
         }
     } else {
         j = k;
@@ -1376,17 +1384,16 @@ __global__ void __launch_bounds__(GNT) bwd_grads128_kernel(BwdArgs a, VarPlan vp
 
 size_t bwd_record_bytes(int64_t chunks) { return static_cast<size_t>(chunks * REC_BWD * 4); }
 
-// Segments per chain for the scans: about 128 / chains (so that a
-// direction's rescan has some 256 workgroups), each of at least 64 chunks;
-// one (a single pass) from 32 chains up.  The summaries run about twice the
-// scan work in two rounds of workgroups and the rescan once, at some 4.5
-// against 3.2 us per step for a single pass with its CUs to itself, so the
-// segments pay below about 30 chains (16 chains of 4096 chunks: 7.4 against
-// 13.1 ms).
+// Segments per chain for the scans: as many as keep the summaries' 6 nseg - 8
+// workgroups per chain within one round of two per CU, each of at least 64
+// chunks; one (a single pass) from 32 chains up.  The summaries and the
+// rescan each walk one segment at some 4.5 us per step (two workgroups per
+// CU), a single pass the whole chain at 3.2 us (its CUs to itself), so the
+// segments pay below about 30 chains.
 int bwd_segments(int64_t chains, int nch) {
     constexpr int MIN_LEN = 64;
     if (chains <= 0 || chains >= 32) return 1;
-    int64_t n = 128 / chains;
+    int64_t n = (512 / chains + 8) / 6;
     if (n > nch / MIN_LEN) n = nch / MIN_LEN;
     if (n < 2) return 1;
     const int64_t len = (nch + n - 1) / n;
@@ -1424,12 +1431,14 @@ hipError_t launch_bwd_d128(const BwdArgs &a, const VarPlan &vp, float *rec, floa
         sg.fs = segs + 2 * chains * nseg * BD * BD;
         // (chain, value half, summary) x (state, gradient); then the exact
         // entries; then (chain, value half, segment) x (state, gradient)
-        const unsigned g1s = static_cast<unsigned>(chains * 2 * (2 * nseg - 3) * 2);
+        sg.us = chains * 2 * (2 * nseg - 3);
+        const unsigned g1s = static_cast<unsigned>(sg.us + chains * 2 * (nseg - 1));
         hipLaunchKernelGGL(bwd_seg_scans_kernel<1>, dim3(g1s), dim3(SNT), 0, s, a, vp, static_cast<const float *>(rec),
                            hist, dhist, nch, sg);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = launch_segment_combine(sg.xs, sg.fs, 2 * chains, nseg, s)) != hipSuccess) return e;
-        const unsigned g0s = static_cast<unsigned>(chains * 2 * nseg * 2);
+        sg.us = chains * 2 * nseg;
+        const unsigned g0s = static_cast<unsigned>(2 * sg.us);
         hipLaunchKernelGGL(bwd_seg_scans_kernel<0>, dim3(g0s), dim3(SNT), 0, s, a, vp, static_cast<const float *>(rec),
                            hist, dhist, nch, sg);
     } else {

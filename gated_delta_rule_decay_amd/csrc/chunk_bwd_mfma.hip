@@ -22,6 +22,9 @@
 //                       recorded on entry (= each chunk's dSo), then dS0;
 //   bwd_grads128_kernel every chunk in parallel: all input gradients from the
 //                       record, S and dSo.
+// With few chains and long sequences the middle launch becomes three
+// (bwd_seg_scans_kernel<1>, the segment combine, bwd_seg_scans_kernel<0>):
+// the scans run in segments, summarised, combined and rescanned.
 // All arithmetic is fp32 (v_mfma_f32_16x16x4f32, fp32 accumulate), so the
 // gradients keep the fp32 tolerance.
 //

@@ -227,3 +227,28 @@ def test_full_size_long_context_every_chain():
                           inp["S0"], d_o, d_st)
     check_every_chain("long-context backward", [(n, got[n], ref[n], (2, 3) if n == "d_state0" else (1, 3))
                                                 for n in NAMES], TOL)
+
+
+def test_segmented_scans_zero_ends_head_gates():
+    # 3 segments with no initial state and no final-state cotangent (the
+    # summaries and the rescan then start from zero at both ends), one decay
+    # per token-head and a tied per-channel rate
+    import torch
+    from gated_delta_rule_decay_amd import chunk_bwd
+    from oracle.oracle import gdn2_backward_c
+
+    w = W[2].scaled(B=1, T=3072, H=2, tied=True)
+    inp = synth.make_inputs(w, seed=650)
+    inp["S0"] = None
+    inp["log_decay"] = np.ascontiguousarray(inp["log_decay"][..., 0])
+    r = np.random.Generator(np.random.PCG64(651))
+    d_o = r.standard_normal((w.B, w.T, w.H, w.dv)).astype(np.float32)
+    d = to_device(inp)
+    g = chunk_bwd(d["q"], d["k"], d["v"], d["log_decay"], d["erase"], None, None,
+                  torch.from_numpy(d_o).cuda(), None, chunk=w.chunk)
+    torch.cuda.synchronize()
+    got = {k: (None if v is None else v.cpu().numpy()) for k, v in g.items()}
+    ref = gdn2_backward_c(inp["q"], inp["k"], inp["v"], inp["log_decay"], inp["erase"], None, None, d_o, None)
+    axes = {"d_state0": (2, 3), "d_log_decay": (1,)}
+    check_every_chain("segmented backward, zero ends", [(n, got[n], ref[n], axes.get(n, (1, 3)))
+                                                        for n in NAMES if ref[n] is not None], TOL)

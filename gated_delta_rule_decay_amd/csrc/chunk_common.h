@@ -415,7 +415,8 @@ __device__ __forceinline__ void factored_operands(SM &S, const Raw<GK, NV> &R, f
 // Grams on the erase column operand (A and R), bit 1 those on the write
 // column operand (Bm and P); with tied gates (Bm = A, P = R) bit 0 is A, bit 1
 // is R.  Each Gram is accumulated in the same order whatever the share.
-template <typename SM, bool TIED, int PARTS = 3>
+// With BT the write Gram Bm is also stored transposed (S.ut.bt, [s][r]).
+template <typename SM, bool TIED, int PARTS = 3, bool BT = false>
 __device__ __forceinline__ bool gram_tile(SM &S, int i, int j, int lr, int lg) {
     constexpr bool doA = PARTS & 1, doR = TIED ? (PARTS & 2) != 0 : (PARTS & 1) != 0;
     constexpr bool doB = !TIED && (PARTS & 2), doP = !TIED && (PARTS & 2);
@@ -459,6 +460,13 @@ __device__ __forceinline__ bool gram_tile(SM &S, int i, int j, int lr, int lg) {
         if (TIED ? doA : doB) S.b16[r * SP + s] = (_Float16)(strict ? (TIED ? aA[e] : aB[e]) : 0.f);
         if (doR) S.r16[r * SP + s] = (_Float16)(incl ? aR[e] : 0.f);
         if (doP) S.p16[r * SP + s] = (_Float16)(incl ? aP[e] : 0.f);
+    }
+    if constexpr (BT && doB) {
+        // Bm^T: lane (lr, lg) holds rows 16i+4lg..+3 of column 16j+lr, one row of the transpose
+        h4 t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = (_Float16)((16 * i + 4 * lg + e > 16 * j + lr) ? aB[e] : 0.f);
+        lds_st<h4>(&S.ut.bt[(16 * j + lr) * SP + 16 * i + 4 * lg], t);
     }
     return (doR && out_of_range(aR)) || (doB && out_of_range(aB)) || (doP && out_of_range(aP));
 }

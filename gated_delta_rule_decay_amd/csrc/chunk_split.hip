@@ -8,15 +8,17 @@
 // into work that needs the incoming state S and work that does not.  With
 // Tm = (I + A)^-1, Kbar = k e^g, Qbar = q e^g, Util = u e^(gC-g),
 // Etil = e e^(gC-g):
-//   W  = Tm Kbar           U  = Tm Bm V          (the pseudo-value solve)
-//   Qe = Qbar - R W        Oe = P V - R U
-//   G  = Util^T V - Etil^T U
-// depend on the chunk alone, and then
-//   O = Qe S + Oe,   S <- Diag(e^gC) S + G - Etil^T (W S)
+//   W  = Tm Kbar           T2 = Tm Bm            (the pseudo-value solve:
+//   Qe = Qbar - R W        Y  = P - R T2          U = Tm Bm V = T2 V)
+//   Z^T = Util^T - Etil^T T2
+// depend on the chunk alone (none of them on the values), and then
+//   O = Qe S + Y V,   S <- Diag(e^gC) S + Z^T V - Etil^T (W S)
 // is all that the sequential scan over chunks has to do (M = W S + U is the
-// erase read of the token form).  With tied gates (u = e, so P = R) and
+// erase read of the token form; Y V = P V - R U and Z^T V = Util^T V -
+// Etil^T U).  The scan reads the values itself, so the record holds no
+// C x dv or dk x dv product of them.  With tied gates (u = e, so P = R) and
 // D = V - U, X = D - W S: O = Qbar S + R X and S <- Diag(e^gC) S + Etil^T X,
-// so the record of a tied chunk keeps Qbar, D and R instead of Qe, Oe and G.
+// so the record of a tied chunk keeps Qbar, D and R instead of Qe, Y and Z.
 //
 // Pass 1 (chunk_prep_kernel) runs every (chain, chunk) in parallel -- one
 // 512-lane workgroup per CU, persistent over the tasks, with the next task's
@@ -25,9 +27,10 @@
 // plus e^gC (which also carries the exact-path mark).  Pass 2
 // (chunk_scan_kernel) runs one workgroup per (chain, half of the value
 // columns): four compute waves keep their fp32 state slices in MFMA
-// accumulators while four copy waves stage the chunk records through two
-// LDS slots, one chunk ahead; long sequences on few chains are cut into
-// segments scanned in parallel and combined (the affine view of a chunk).
+// accumulators while four copy waves stage the chunk records (and, untied,
+// the chunk's values) through two LDS slots, one chunk ahead; long
+// sequences on few chains are cut into segments scanned in parallel and
+// combined (the affine view of a chunk).
 //
 // A chunk whose fp16 factors, operands or results would leave the fast
 // range is flagged by pass 1; pass 2 runs it as the exact fp32 token
@@ -53,27 +56,36 @@ using namespace mfma;
 //                                    of block kb in slots 8m..8m+7
 //   EtT    [it 8][kb 2][lane 64][8]  lane i+16m: key channel 16it+i, tokens
 //                                    of block kb in slots 8m..8m+7
-//   G      [ct 8][ip 4][lane 64][8]  accumulator tiles it = 2ip, 2ip+1: lane
-//                                    j+16m holds G[16it+4m+e][16ct+j] in
-//                                    elements 4(it&1)+e
-//   OeT    [ct 8][rp 2][lane 64][8]  transposed tiles rt = 2rp, 2rp+1: lane
-//                                    t+16m holds Oe[16rt+t][16ct+4m+e] in
-//                                    elements 4(rt&1)+e (four adjacent value
-//                                    columns of one token)
+//   ZT     [it 8][kb 2][lane 64][8]  Z^T, the same layout
+//   YT     [n 6][lane 64][8]         fragment n = (rt, kb) of Y^T, (0,0) (1,0)
+//                                    (2,0) (2,1) (3,0) (3,1): lane t+16m holds
+//                                    Y[16rt+t][s] for the tokens s of block kb
+//                                    in slots 8m..8m+7 (the B operand of
+//                                    V^T Y^T, which gives O^T tiles whose
+//                                    lanes hold four adjacent value columns
+//                                    of one token)
+// 70 KiB per chunk-head: the scan reads it and the chunk's values (16 KiB of
+// bf16), where a record of the value products Oe = Y V and G = Z^T V would
+// take 96 KiB.
 constexpr int64_t OFF_W = 0;
 constexpr int64_t OFF_Q = 8192;
 constexpr int64_t OFF_E = 16384;
-constexpr int64_t OFF_G = 24576;
-constexpr int64_t OFF_O = 40960;
-constexpr int64_t REC = 49152;
+constexpr int64_t OFF_Z = 24576;
+constexpr int64_t OFF_Y = 32768;
+constexpr int64_t REC = 35840;
 // Tied gates (u = e, so Bm = A and P = R; also the value-write form) keep a
-// slimmer record: with D = V - U, G = Etil^T D and Oe = R D, so the scan
-// forms both from D and R itself and the record holds W^T, Qbar^T (the scan
-// adds R (D - W S) to Qbar S), Etil^T, D and the six nonzero fragments of R:
-// 70 KiB written and read instead of 96 KiB.
+// record of the same size: with D = V - U, G = Etil^T D and Oe = R D, so the
+// scan forms both from D and R itself and the record holds W^T, Qbar^T (the
+// scan adds R (D - W S) to Qbar S), Etil^T, D and the six nonzero fragments
+// of R, and the scan reads no values.
 constexpr int64_t OFF_D = 24576;  // D in the scan's W S tile layout: [value tile][tile pair][lane][8]
 constexpr int64_t OFF_R = 32768;  // R as B operands of R X (perm_frag order), fragment n = (rt, ks)
 constexpr int R_FRAGS = 6;        // (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+// the ten lower 16 x 16 tiles (jt, st) of T2 = Tm Bm, in the order the
+// prep pass's waves take them
+__constant__ int kT2J[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+__constant__ int kT2S[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+static_assert(OFF_Y + R_FRAGS * 512 == REC && OFF_R + R_FRAGS * 512 == REC, "both records fill REC");
 
 struct SplitWs {
     _Float16 *frag;  // [task][REC]
@@ -94,10 +106,15 @@ struct alignas(16) PrepSmem {
     _Float16 qh[C * KP];   // q 2^(g-gm); later Qbar
     _Float16 eh[C * KP];   // Gram column operand e 2^(gm-g)
     _Float16 uh[C * KP];   // u 2^(gm-g)
-    _Float16 v16[D * SP];  // values, [j][s]
+    union {
+        _Float16 v16[D * SP];  // values, [j][s] (tied gates)
+        struct {
+            _Float16 bt[C * SP];  // Bm^T [s][r]          (untied gates: the scan
+            _Float16 t2[C * SP];  // T2^T = (Tm Bm)^T [s][j]  reads the values)
+        } ut;
+    };
     union {
         float af[C * AP];       // A (strict lower), then Tm in place (fp32)
-        _Float16 u16[D * SP];   // U, [j][s]
         float segtot[NSEG][GP];  // per-segment log2-decay totals
     };
     _Float16 t16[C * SP];  // Tm  [r][s]
@@ -185,11 +202,13 @@ __device__ __forceinline__ void load_part(Raw<GK, 2> &R, const ChunkArgs &a, con
     if constexpr (PART == 1) gates(R.eb, a.eb);
     if constexpr (PART == 2) {
         if (!TIED) gates(R.wr, a.wr);
-        const auto rv = chain_rsrc(a.v, a, b, h, t0, D, 2, 0, tl);
         const int tp = tid & 31, piece = tid >> 5;
+        if constexpr (TIED) {  // untied gates: the scan reads the values
+            const auto rv = chain_rsrc(a.v, a, b, h, t0, D, 2, 0, tl);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            R.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, ((2 * tp + i) * rowk + 8 * piece) * 2, 0, 0));
+            for (int i = 0; i < 2; ++i)
+                R.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, ((2 * tp + i) * rowk + 8 * piece) * 2, 0, 0));
+        }
         if constexpr (VW) {
             // write gate of my two tokens' 8 value columns (per channel) or
             // of my two tokens (per head), into the unused wr registers
@@ -301,6 +320,10 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         S.b16[idx] = (_Float16)0.f;
         S.r16[idx] = (_Float16)0.f;
         S.p16[idx] = (_Float16)0.f;
+        if (!TIED) {
+            S.ut.bt[idx] = (_Float16)0.f;
+            S.ut.t2[idx] = (_Float16)0.f;
+        }
     }
     if (tid == 0) S.wide = 0;
 
@@ -335,10 +358,10 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         const int lane = tl & 63, lr = lane & 15, lg = lane >> 4;
         const int seg = tl >> 5, cq = tl & 31;
 
-        // ---- values [j][s]: each thread packs its two tokens of one column
-        //      into a 32-bit word (a wave's writes then hit 64 distinct banks);
-        //      segment log2-decay totals
-        {
+        // ---- values [j][s] (tied gates): each thread packs its two tokens of
+        //      one column into a 32-bit word (a wave's writes then hit 64
+        //      distinct banks); segment log2-decay totals
+        if constexpr (TIED) {
             const int tp = tl & 31, piece = tl >> 5;
             const uint32_t r0[4] = {R.v[0].x, R.v[0].y, R.v[0].z, R.v[0].w};
             const uint32_t r1[4] = {R.v[1].x, R.v[1].y, R.v[1].z, R.v[1].w};
@@ -386,14 +409,14 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             //      half of the Grams of tile 4 + u / 2 (the two waves of a
             //      pair take the two column operands)
             if (wv < 4) {
-                gram_tile<PrepSmem, TIED>(S, wv, wv, lr, lg);
+                gram_tile<PrepSmem, TIED, 3, !TIED>(S, wv, wv, lr, lg);
                 invert_unit_lower16(&S.af[(16 * wv) * AP + 16 * wv], &S.t16[(16 * wv) * SP + 16 * wv],
                                     S.iscr[wv][0], S.iscr[wv][1], lr, lg);
             } else {
                 const int u = wv - 4, t2 = 4 + (u >> 1);
-                gram_tile<PrepSmem, TIED>(S, kOffI[u], kOffJ[u], lr, lg);
+                gram_tile<PrepSmem, TIED, 3, !TIED>(S, kOffI[u], kOffJ[u], lr, lg);
                 if (u & 1)
-                    gram_tile<PrepSmem, TIED, 2>(S, kOffI[t2], kOffJ[t2], lr, lg);
+                    gram_tile<PrepSmem, TIED, 2, !TIED>(S, kOffI[t2], kOffJ[t2], lr, lg);
                 else
                     gram_tile<PrepSmem, TIED, 1>(S, kOffI[t2], kOffJ[t2], lr, lg);
             }
@@ -428,26 +451,43 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             // into inf or NaN.  All LDS reads of this phase come before its
             // LDS writes, so the compiler may issue them early.
 
-            // ---- (1) value tile ct = wv: Y = Bm V, U = Tm Y ------------------
-            // vb: V[:, ct] as a B operand, natural token order
+            if constexpr (TIED) {
+                // ---- (1) value tile ct = wv: Y = Bm V, U = Tm Y --------------
+                // vb: V[:, ct] as a B operand, natural token order
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) vb[ks] = lds_ld<h8>(&S.v16[(16 * ct + lr) * SP + 32 * ks + 8 * lg]);
-            f4 y[4];
+                for (int ks = 0; ks < 2; ++ks) vb[ks] = lds_ld<h8>(&S.v16[(16 * ct + lr) * SP + 32 * ks + 8 * lg]);
+                f4 y[4];
 #pragma unroll
-            for (int rt = 0; rt < 4; ++rt) {
-                y[rt] = splat(0.f);
+                for (int rt = 0; rt < 4; ++rt) {
+                    y[rt] = splat(0.f);
 #pragma unroll
-                for (int ks = 0; ks <= (rt >> 1); ++ks)
-                    y[rt] = mfma32(lds_ld<h8>(&S.b16[(16 * rt + lr) * SP + 32 * ks + 8 * lg]), vb[ks], y[rt]);
-                big |= out_of_range(y[rt]);
-            }
-            {
+                    for (int ks = 0; ks <= (rt >> 1); ++ks)
+                        y[rt] = mfma32(lds_ld<h8>(&S.b16[(16 * rt + lr) * SP + 32 * ks + 8 * lg]), vb[ks], y[rt]);
+                    big |= out_of_range(y[rt]);
+                }
                 const h8 yb0 = join(to_h4(y[0]), to_h4(y[1])), yb1 = join(to_h4(y[2]), to_h4(y[3]));
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     uacc[rt] = mfma32(perm_frag(S.t16, rt, 0, lr, lg), yb0, splat(0.f));
                     if (rt >= 2) uacc[rt] = mfma32(perm_frag(S.t16, rt, 1, lr, lg), yb1, uacc[rt]);
                     big |= out_of_range(uacc[rt]);
+                }
+            } else {
+                // ---- (1) T2 = Tm Bm, the ten lower 16 x 16 tiles (jt, st) over
+                //      the waves (wave u: tile u, waves 0, 1 also tile u + 8),
+                //      stored transposed ([s][j]) for the Z and Y products;
+                //      natural token order (Tm rows, Bm^T rows)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    const int u = wv + 8 * n;
+                    if (u >= 10) break;
+                    const int jt = kT2J[u], st = kT2S[u];
+                    f4 acc = splat(0.f);
+                    for (int kb = st >> 1; kb <= (jt >> 1); ++kb)
+                        acc = mfma32(lds_ld<h8>(&S.t16[(16 * jt + lr) * SP + 32 * kb + 8 * lg]),
+                                     lds_ld<h8>(&S.ut.bt[(16 * st + lr) * SP + 32 * kb + 8 * lg]), acc);
+                    big |= out_of_range(acc);
+                    lds_st<h4>(&S.ut.t2[(16 * st + lr) * SP + 16 * jt + 4 * lg], to_h4(acc));
                 }
             }
 
@@ -475,12 +515,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                     *reinterpret_cast<h8 *>(rec + OFF_E + ((it * 2 + kb) * 64 + lane) * 8) = ef[kb];
                 }
             }
-            if (!TIED) {
-                // U -> u16 [j][s] for the value-column products of every wave
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    lds_st<h4>(&S.u16[(16 * ct + lr) * SP + 16 * rt + 4 * lg], to_h4(uacc[rt]));
-            } else {
+            if constexpr (TIED) {
                 // the slim record: D = V - U of value tile ct, in the layout of
                 // the scan's W S tiles (token 16 rt + 4 lg + e, column 16 ct + lr),
                 // and R fragment wv as a B operand
@@ -504,76 +539,54 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             }
             if (big) S.wide = 1;
         }
-        __syncthreads();  // U complete in u16
+        __syncthreads();  // T2 complete (untied)
         if constexpr (!TIED) load_part<2, TIED, GK, VW, RAW>(R, a, pn, tid);
         if (!wide && !TIED) {
-            // ---- (4) Oe^T[ct, :] = V^T P^T - U^T R^T -> HBM (transposed, so
-            //      the scan's output tiles hold adjacent columns per lane)
+            // ---- (4) Z = Util - T2^T Etil for key channel tile it = wv, as
+            //      token x channel tiles st: tiles 2kb, 2kb+1 of a lane are
+            //      the record's Z^T fragment kb (the EtT layout).  The Etil
+            //      fragments ef[kb] are the B operands (channel 16it+lr,
+            //      permuted token slots); Util's start the accumulators.
             {
-                // every operand read first, then the four token tiles' products
-                // interleaved (independent accumulators), so that neither the
-                // LDS reads nor the matrix unit's latency serialise the phase
-                const _Float16 *pp = TIED ? S.r16 : S.p16;
-                const h8 ub0 = join(to_h4(uacc[0]), to_h4(uacc[1])), ub1 = join(to_h4(uacc[2]), to_h4(uacc[3]));
-                h8 pf[6], rf[6];  // (rt, ks) pairs 0,0 1,0 2,0 2,1 3,0 3,1
+                h8 tf[4][2];  // rows of T2^T (token s), permuted j slots; T2[j][s] = 0 unless j > s
 #pragma unroll
-                for (int rt = 0, n = 0; rt < 4; ++rt)
+                for (int st = 0; st < 4; ++st)
 #pragma unroll
-                    for (int ks = 0; ks <= (rt >> 1); ++ks, ++n) {
-                        pf[n] = lds_ld<h8>(&pp[(16 * rt + lr) * SP + 32 * ks + 8 * lg]);
-                        rf[n] = perm_frag(S.r16, rt, ks, lr, lg);
-                    }
-                __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the products
-                f4 acc[4];
+                    for (int kb = st >> 1; kb < 2; ++kb) tf[st][kb] = perm_frag(S.ut.t2, st, kb, lr, lg);
+                __builtin_amdgcn_sched_barrier(0);  // every read ahead of the products
+                f4 z[4];
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma32(vb[0], pf[rt < 2 ? rt : 2 * rt - 2], splat(0.f));
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) acc[rt] = mfma32(-ub0, rf[rt < 2 ? rt : 2 * rt - 2], acc[rt]);
-#pragma unroll
-                for (int rt = 2; rt < 4; ++rt) acc[rt] = mfma32(vb[1], pf[2 * rt - 1], acc[rt]);
-#pragma unroll
-                for (int rt = 2; rt < 4; ++rt) acc[rt] = mfma32(-ub1, rf[2 * rt - 1], acc[rt]);
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) big |= out_of_range(acc[rt]);
-#pragma unroll
-                for (int rp = 0; rp < 2; ++rp)
-                    *reinterpret_cast<h8 *>(rec + OFF_O + ((ct * 2 + rp) * 64 + lane) * 8) =
-                        join(to_h4(acc[2 * rp]), to_h4(acc[2 * rp + 1]));
-            }
-            // ---- (5) G[it, :] = Util^T V - Etil^T U -> HBM -------------------
-            {
-                // four value tiles at a time: their operand reads issued
-                // together, their products interleaved (same order per tile)
+                for (int kb = 0; kb < 2; ++kb) {
+                    z[2 * kb] = f4{(float)uf[kb][0], (float)uf[kb][1], (float)uf[kb][2], (float)uf[kb][3]};
+                    z[2 * kb + 1] = f4{(float)uf[kb][4], (float)uf[kb][5], (float)uf[kb][6], (float)uf[kb][7]};
+                }
                 const h8 ne0 = -ef[0], ne1 = -ef[1];
 #pragma unroll
-                for (int cb = 0; cb < 8; cb += 4) {
-                    h8 vp[4][2], up[4][2];
+                for (int st = 0; st < 2; ++st) z[st] = mfma32(tf[st][0], ne0, z[st]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                for (int st = 0; st < 4; ++st) z[st] = mfma32(tf[st][1], ne1, z[st]);
 #pragma unroll
-                        for (int kb = 0; kb < 2; ++kb) {
-                            const _Float16 *pv = &S.v16[(16 * (cb + j) + lr) * SP + 32 * kb + 4 * lg];
-                            const _Float16 *pu = &S.u16[(16 * (cb + j) + lr) * SP + 32 * kb + 4 * lg];
-                            vp[j][kb] = join(lds_ld<h4>(pv), lds_ld<h4>(pv + 16));
-                            up[j][kb] = join(lds_ld<h4>(pu), lds_ld<h4>(pu + 16));
-                        }
-                    __builtin_amdgcn_sched_barrier(0);  // keep the four tiles' reads ahead of their products
-                    f4 acc[4];
+                for (int st = 0; st < 4; ++st) big |= out_of_range(z[st]);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[j] = mfma32(uf[0], vp[j][0], splat(0.f));
+                for (int kb = 0; kb < 2; ++kb)
+                    *reinterpret_cast<h8 *>(rec + OFF_Z + ((it * 2 + kb) * 64 + lane) * 8) =
+                        join(to_h4(z[2 * kb]), to_h4(z[2 * kb + 1]));
+            }
+            // ---- (5) Y^T = P^T - T2^T R^T, fragment wv = (rt, kb) for waves
+            //      0..5: tiles st = 2kb, 2kb+1 of token block rt, contracted
+            //      over the tokens j with s < j <= r (blocks st/2 .. rt/2)
+            if (wv < R_FRAGS) {
+                const int rt = wv < 2 ? wv : (wv + 2) / 2, kb = wv < 2 ? 0 : wv & 1;
+                f4 y[2];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[j] = mfma32(ne0, up[j][0], acc[j]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[j] = mfma32(uf[1], vp[j][1], acc[j]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) acc[j] = mfma32(ne1, up[j][1], acc[j]);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        big |= out_of_range(acc[j]);
-                        *reinterpret_cast<h4 *>(rec + OFF_G + (((cb + j) * 4 + (it >> 1)) * 64 + lane) * 8 + 4 * (it & 1)) =
-                            to_h4(acc[j]);
-                    }
+                for (int q = 0; q < 2; ++q) {
+                    const int st = 2 * kb + q;
+                    y[q] = to_f4(lds_ld<h4>(&S.p16[(16 * rt + lr) * SP + 16 * st + 4 * lg]));
+                    for (int k2 = st >> 1; k2 <= (rt >> 1); ++k2)
+                        y[q] = mfma32(-perm_frag(S.ut.t2, st, k2, lr, lg), perm_frag(S.r16, rt, k2, lr, lg), y[q]);
+                    big |= out_of_range(y[q]);
                 }
+                *reinterpret_cast<h8 *>(rec + OFF_Y + (wv * 64 + lane) * 8) = join(to_h4(y[0]), to_h4(y[1]));
             }
             if (big) S.wide = 1;
         }
@@ -618,10 +631,13 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
 constexpr int SCAN_W = 4;                 // compute waves per value half (one tile each)
 constexpr int SCAN_P = 4;                 // copy waves
 constexpr int SLOT_F = 3 * 8192;          // halves of W | Qe | EtT
-constexpr int SLOT_G = SCAN_W * 4 * 512;  // halves of G for my tiles (4 pair rows of 512)
-constexpr int SLOT_O = SCAN_W * 2 * 512;  // halves of Oe^T for my tiles
-constexpr int SLOT_H = SLOT_F + SLOT_G + SLOT_O;  // MODE 0 slot
-constexpr int SLOT_A = 2 * 8192 + SLOT_G;         // MODE 1 slot: W | EtT | G
+// untied gates: the whole record (W | Qe | EtT | Z^T | Y^T), MODE 1 W | EtT |
+// Z^T, then the workgroup's 64 value columns of the chunk in fp16, [column]
+// [token pair] words at a pitch of V_PW words
+constexpr int SLOT_U = static_cast<int>(REC);
+constexpr int SLOT_UA = 3 * 8192;
+constexpr int V_PW = 36;
+constexpr int SLOT_V = 64 * V_PW * 2;
 // the slim (tied) record: W | Qbar | EtT, my D tiles, the R fragments
 // (padded to 8 KiB); MODE 1: W | EtT | my D tiles
 constexpr int SLOT_D = SCAN_W * 2 * 512;
@@ -631,8 +647,8 @@ constexpr int SLOT_AT = 2 * 8192 + SLOT_D;
 static_assert(R_FRAGS * 512 <= SLOT_R, "R fragments fit their slot part");
 static_assert(SLOT_HT * 2 % (1024 * SCAN_P) == 0 && SLOT_AT * 2 % (1024 * SCAN_P) == 0,
               "slot copies must tile the copy waves");
-static_assert(SLOT_H * 2 % (1024 * SCAN_P) == 0 && SLOT_A * 2 % (1024 * SCAN_P) == 0,
-              "slot copies must tile the copy waves");
+static_assert(SLOT_U * 2 % 1024 == 0 && SLOT_UA * 2 % 1024 == 0, "record parts are whole 1 KiB pieces");
+static_assert(2 * (SLOT_U + SLOT_V) * 2 + 2 * 2 * 128 * 4 <= 160 * 1024, "two untied slots fit the LDS");
 constexpr int SEG_MIN = 16;   // fewest chunks per segment
 constexpr int SEG_WG = 256;   // scan workgroups aimed at when chains are few
 
@@ -757,10 +773,14 @@ __global__ void __launch_bounds__(scan_threads(MODE))
 chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     constexpr bool WITH_O = MODE == 0;
     constexpr int NCOMP = (MODE ? 2 : 1) * SCAN_W;
-    constexpr int SH = TIED ? (MODE ? SLOT_AT : SLOT_HT) : (MODE ? SLOT_A : SLOT_H);
-    constexpr int S_Q = 8192, S_E = MODE ? 8192 : 16384, S_G = MODE ? 16384 : SLOT_F, S_O = SLOT_F + SLOT_G;
-    constexpr int S_D = S_G, S_R = SLOT_F + SLOT_D;  // the slim record: my D tiles, the R fragments
-    constexpr int PIECES = SH * 2 / 1024 / SCAN_P;  // 1 KiB copies per copy wave
+    // the record part of a slot, then (untied) the chunk's values
+    constexpr int SREC = TIED ? (MODE ? SLOT_AT : SLOT_HT) : (MODE ? SLOT_UA : SLOT_U);
+    constexpr int SH = SREC + (TIED ? 0 : SLOT_V);
+    constexpr int S_Q = 8192, S_E = MODE ? 8192 : 16384;
+    constexpr int S_Z = MODE ? 16384 : 24576, S_Y = 32768, S_V = SREC;  // untied: Z^T, Y^T, values
+    constexpr int S_D = MODE ? 16384 : SLOT_F, S_R = SLOT_F + SLOT_D;  // the slim record: my D tiles, the R fragments
+    constexpr int NPC = SREC * 2 / 1024;                   // 1 KiB pieces of the record part
+    constexpr int PIECES = (NPC + SCAN_P - 1) / SCAN_P;    // per copy wave (the last round may be partial)
     // two distinct slots (distinct objects, so the compiler can tell the slot
     // being filled from the one being read)
     __shared__ __attribute__((aligned(16))) _Float16 fr0[SH], fr1[SH];
@@ -830,22 +850,23 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     // compute waves work on chunk n (one slot), the copy waves write chunk
     // n+1 from their registers into the other slot and issue the loads of
     // chunk n+2 into their registers, so two chunks' memory latency is always
-    // in flight.  A slot holds W | Qe | EtT (MODE 1: W | EtT), then my
-    // workgroup's G and Oe^T tiles (contiguous in the record), then e^gC.
-    // Each wave moves 1 KiB per instruction (lane l -> bytes 16l..16l+15).
+    // in flight.  A slot holds the record (untied: all of it; MODE 1 W | EtT
+    // | Z^T; tied: W | Qbar | EtT and my workgroup's D tiles and the R
+    // fragments), then (untied) my 64 value columns of the chunk, then e^gC.
+    // Each wave moves 1 KiB of record per instruction (lane l -> bytes
+    // 16l..16l+15); the values come as two rows of 8 columns per lane.
     typedef uint32_t u4v __attribute__((ext_vector_type(4)));
-    u4v cr[PIECES];
+    u4v cr[PIECES], vr[TIED ? 1 : 2];
     float cgam = 0.f;
-    auto load_regs = [&](int64_t task, int pw) __attribute__((always_inline)) {
+    auto load_regs = [&](int64_t task, int n, int pw) __attribute__((always_inline)) {
         // one buffer resource per record: every piece is the same lane offset
         // plus a uniform byte offset, so no per-piece address registers
         const auto rs = __builtin_amdgcn_make_buffer_rsrc(w.frag + task * REC, (short)0, static_cast<int>(REC * 2),
                                                           0x00020000);
-        const int og = 2 * (static_cast<int>(OFF_G) + SCAN_W * half * 4 * 512);
-        const int oo = 2 * (static_cast<int>(OFF_O) + SCAN_W * half * 2 * 512);
         const int od = 2 * (static_cast<int>(OFF_D) + SCAN_W * half * 2 * 512);
 #pragma unroll
         for (int i = 0; i < PIECES; ++i) {
+            if (NPC % SCAN_P != 0 && i == PIECES - 1 && SCAN_P * i + pw >= NPC) break;  // (wave-uniform)
             const int byte = 1024 * (SCAN_P * i + pw);  // my 1 KiB block of the slot
             int src;
             if (TIED && MODE == 0)
@@ -857,22 +878,53 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
                     : byte < 4 * 8192 ? 2 * static_cast<int>(OFF_E) + (byte - 2 * 8192)
                                       : od + (byte - 4 * 8192);
             else if (MODE == 0)
-                src = byte < 2 * SLOT_F ? byte
-                    : byte < 2 * (SLOT_F + SLOT_G) ? og + (byte - 2 * SLOT_F)
-                                                   : oo + (byte - 2 * (SLOT_F + SLOT_G));
+                src = byte;
             else
                 src = byte < 2 * 8192 ? byte
                     : byte < 4 * 8192 ? 2 * static_cast<int>(OFF_E) + (byte - 2 * 8192)
-                                      : og + (byte - 4 * 8192);
+                                      : 2 * static_cast<int>(OFF_Z) + (byte - 4 * 8192);
             cr[i] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, src, 0));
+        }
+        if constexpr (!TIED) {
+            // values: lane (token pair pa, column group cg) of the 256 copy
+            // lanes loads tokens 2pa, 2pa+1, my columns 8cg..8cg+7 (rows past
+            // the sequence read as zero)
+            const int idx = 64 * pw + lane, pa = idx & 31, cg = idx >> 5;
+            const int rowk = static_cast<int>(a.H) * D;
+            const auto rv = chain_rsrc(a.v, a, 0, h, tbase + static_cast<int64_t>(n) * C, D, 2, 64 * half, tlim);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                vr[i] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rv, ((2 * pa + i) * rowk + 8 * cg) * 2, 0, 0));
         }
         // e^gC: copy waves 0,1 bring channels 0..127
         if (pw < 2) cgam = w.gam[task * D + 64 * pw + lane];
     };
     auto store_regs = [&](_Float16 *fr, float *gm, int pw) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < PIECES; ++i)
+        for (int i = 0; i < PIECES; ++i) {
+            if (NPC % SCAN_P != 0 && i == PIECES - 1 && SCAN_P * i + pw >= NPC) break;
             *reinterpret_cast<u4v *>(reinterpret_cast<char *>(fr) + 1024 * (SCAN_P * i + pw) + 16 * lane) = cr[i];
+        }
+        if constexpr (!TIED) {
+            // values in fp16, [column][token pair] words: column 8cg+j of my
+            // two tokens in one word (the 32 lanes of a half-wave write 32
+            // consecutive words).  A value beyond fp16's range marks the
+            // chunk for the exact path (gm[D + pw] < 0).
+            const int idx = 64 * pw + lane, pa = idx & 31, cg = idx >> 5;
+            uint32_t *vw = reinterpret_cast<uint32_t *>(fr + S_V);
+            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+            bool vbig = false;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t x0 = vr[0][j >> 1], x1 = vr[1][j >> 1];
+                const float f0 = __uint_as_float((j & 1) ? (x0 & 0xffff0000u) : (x0 << 16));
+                const float f1 = __uint_as_float((j & 1) ? (x1 & 0xffff0000u) : (x1 << 16));
+                vbig |= !(fmaxf(fabsf(f0), fabsf(f1)) <= 65504.f);
+                vw[(8 * cg + j) * V_PW + pa] = __builtin_bit_cast(uint32_t, h2{(_Float16)f0, (_Float16)f1});
+            }
+            const bool anyv = __ballot(vbig) != 0;
+            if (lane == 0) gm[D + pw] = anyv ? -1.f : 0.f;
+        }
         if (pw < 2) gm[64 * pw + lane] = cgam;
     };
 
@@ -883,8 +935,6 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         int lane_ = lane;
         asm volatile("" : "+v"(lane_));
         const int lane = lane_, lr = lane & 15, lg = lane >> 4;
-        const _Float16 *fg = fr + S_G + wt * 4 * 512;  // my G pairs
-        const _Float16 *fo = fr + S_O + wt * 2 * 512;  // my Oe^T pairs (MODE 0)
         const int64_t t0 = tbase + static_cast<int64_t>(n) * C;
         // the fp16 copies of the state and of the erase read must stay finite
         bool big = false;
@@ -892,8 +942,16 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         for (int it = 0; it < 8; ++it)
             big |= !(fmaxf(fmaxf(fabsf(sacc[it][0]), fabsf(sacc[it][1])), fmaxf(fabsf(sacc[it][2]), fabsf(sacc[it][3]))) <= MAX_STATE);
         bool bad = gm[0] < 0.f || __ballot(big) != 0;  // chunk marked for the exact path
+        if constexpr (!TIED) {
+            const f4 vf = *reinterpret_cast<const f4 *>(&gm[D]);  // the copy waves' value checks
+            bad = bad || fminf(fminf(vf[0], vf[1]), fminf(vf[2], vf[3])) < 0.f;
+        }
         f4 p1[4], oacc[4];
         h8 ef[8][2];
+        // untied: my value column 16wt+lr of the chunk, tokens in the
+        // record's permuted slot order -- the B operand of Z^T V and the A
+        // operand of V^T Y^T
+        h8 vfr[2];
         big = false;
         if (!bad) {
             // Fragments are read from LDS ahead of use (W/Qe of the next row
@@ -909,11 +967,29 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
             };
             h8 wq[2][2][4];
             read_wq(wq[0], 0);
+            if constexpr (!TIED) {
+                const uint32_t *vw = reinterpret_cast<const uint32_t *>(fr + S_V) + (16 * wt + lr) * V_PW + 2 * lg;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    vfr[kb] = join(lds_ld<h4>(vw + 16 * kb), lds_ld<h4>(vw + 16 * kb + 8));
+            }
             if (MODE == 0) {  // MODE 1 reads EtT where it is used (register budget of 12 waves)
 #pragma unroll
                 for (int it = 0; it < 8; ++it)
 #pragma unroll
                     for (int k2 = 0; k2 < 2; ++k2) ef[it][k2] = *reinterpret_cast<const h8 *>(fr + S_E + ((it * 2 + k2) * 64 + lane) * 8);
+            }
+            // untied: O^T starts from Oe^T = V^T Y^T (Y lower triangular: token
+            // block rt takes the value blocks kb <= rt / 2)
+            f4 oy[4];
+            if constexpr (WITH_O && !TIED) {
+                h8 yf[R_FRAGS];
+#pragma unroll
+                for (int m = 0; m < R_FRAGS; ++m) yf[m] = *reinterpret_cast<const h8 *>(fr + S_Y + (m * 64 + lane) * 8);
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) oy[rt] = mfma32(vfr[0], yf[rt < 2 ? rt : 2 * rt - 2], splat(0.f));
+#pragma unroll
+                for (int rt = 2; rt < 4; ++rt) oy[rt] = mfma32(vfr[1], yf[2 * rt - 1], oy[rt]);
             }
             // P1 = W S and O^T = S^T Qe^T + Oe^T.  State tiles 2kb, 2kb+1 in
             // the record's permuted slot order are both the B operand of key
@@ -924,16 +1000,12 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 if (rt < 3) read_wq(wq[(rt + 1) & 1], rt + 1);
-                h8 oe;
-                if (WITH_O && !TIED) oe = *reinterpret_cast<const h8 *>(fo + ((rt >> 1) * 64 + lane) * 8);
                 __builtin_amdgcn_sched_barrier(0);
                 f4 p = splat(0.f);
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb) p = mfma32(wq[rt & 1][0][kb], sb[kb], p);
                 if (WITH_O) {
-                    f4 o = TIED     ? splat(0.f)
-                         : (rt & 1) ? f4{(float)oe[4], (float)oe[5], (float)oe[6], (float)oe[7]}
-                                    : f4{(float)oe[0], (float)oe[1], (float)oe[2], (float)oe[3]};
+                    f4 o = TIED ? splat(0.f) : oy[rt];
 #pragma unroll
                     for (int kb = 0; kb < 4; ++kb) o = mfma32(sb[kb], wq[rt & 1][1][kb], o);
                     oacc[rt] = o;
@@ -975,14 +1047,9 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         bad = bad || __ballot(big) != 0;
         if (!bad) {
             f4 gam[8];
-            h8 gp[4];
             if (MODE == 0) {
 #pragma unroll
                 for (int it = 0; it < 8; ++it) gam[it] = *reinterpret_cast<const f4 *>(&gm[16 * it + 4 * lg]);
-                if (!TIED) {
-#pragma unroll
-                    for (int ip = 0; ip < 4; ++ip) gp[ip] = *reinterpret_cast<const h8 *>(fg + (ip * 64 + lane) * 8);
-                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (WITH_O) {
@@ -996,8 +1063,9 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
                                    oacc[rt][3], a.o_bf16);
                 }
             }
-            // S <- Diag(e^gC) S + G - Etil^T P1, tokens in permuted slots
-            // (the columns of F take no G); the slim record: + Etil^T X
+            // S <- Diag(e^gC) S + Z^T V - Etil^T P1, tokens in permuted slots
+            // (the columns of F take no write term); the slim record:
+            // + Etil^T X
             const h8 pb0 = TIED ? xb[0] : join(to_h4(-p1[0]), to_h4(-p1[1]));
             const h8 pb1 = TIED ? xb[1] : join(to_h4(-p1[2]), to_h4(-p1[3]));
 #pragma unroll
@@ -1006,16 +1074,13 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
 #pragma unroll
                     for (int k2 = 0; k2 < 2; ++k2) ef[it][k2] = *reinterpret_cast<const h8 *>(fr + S_E + ((it * 2 + k2) * 64 + lane) * 8);
                     gam[it] = *reinterpret_cast<const f4 *>(&gm[16 * it + 4 * lg]);
-                    if (!TIED && (it & 1) == 0) gp[it >> 1] = *reinterpret_cast<const h8 *>(fg + ((it >> 1) * 64 + lane) * 8);
                 }
-                f4 sv;
-                if (TIED) {
-                    sv = gam[it] * sacc[it];
-                } else {
-                    const h8 g2 = gp[it >> 1];
-                    const f4 gv = (it & 1) ? f4{(float)g2[4], (float)g2[5], (float)g2[6], (float)g2[7]}
-                                           : f4{(float)g2[0], (float)g2[1], (float)g2[2], (float)g2[3]};
-                    sv = gam[it] * sacc[it] + (MODE ? gsel * gv : gv);
+                f4 sv = gam[it] * sacc[it];
+                if (!TIED && !frun) {
+                    const h8 z0 = *reinterpret_cast<const h8 *>(fr + S_Z + ((it * 2) * 64 + lane) * 8);
+                    const h8 z1 = *reinterpret_cast<const h8 *>(fr + S_Z + ((it * 2 + 1) * 64 + lane) * 8);
+                    sv = mfma32(z0, vfr[0], sv);
+                    sv = mfma32(z1, vfr[1], sv);
                 }
                 sv = mfma32(ef[it][0], pb0, sv);
                 sv = mfma32(ef[it][1], pb1, sv);
@@ -1047,16 +1112,16 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     if (copier) {
         const int pw = wv - NCOMP;
         if (n0 < n1) {
-            load_regs(task0 + n0 * tstr, pw);
+            load_regs(task0 + n0 * tstr, n0, pw);
             store_regs(fr0, gm0, pw);
         }
-        if (n0 + 1 < n1) load_regs(task0 + (n0 + 1) * tstr, pw);
+        if (n0 + 1 < n1) load_regs(task0 + (n0 + 1) * tstr, n0 + 1, pw);
         __builtin_amdgcn_s_waitcnt(LGKM0);
 #define GDN2_COPY_STEP(N, FRN, GMN)                                                \
         do {                                                                      \
             slot_barrier();                                                       \
             if ((N) + 1 < n1) store_regs(FRN, GMN, pw);                           \
-            if ((N) + 2 < n1) load_regs(task0 + ((N) + 2) * tstr, pw);            \
+            if ((N) + 2 < n1) load_regs(task0 + ((N) + 2) * tstr, (N) + 2, pw);    \
             __builtin_amdgcn_s_waitcnt(LGKM0);                                    \
         } while (0)
         int n = n0;

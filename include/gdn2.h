@@ -149,7 +149,7 @@ const char *gdn2_status_str(int status);
  * and gates per key channel or per head (a per-head decay only with
  * per-head erase and write gates; untied, the write gate of the erase
  * gate's kind); it needs B*H*ceil(T/64) records of about
- * 97 KiB, and, when B*H is small against T (long sequences on few chains,
+ * 71 KiB, and, when B*H is small against T (long sequences on few chains,
  * scanned in parallel segments), two 64 KiB states per (chain, segment).
  * Same validation as gdn2_chunk_fwd. */
 gdn2_status gdn2_chunk_fwd_workspace(const gdn2_desc *desc, size_t *bytes);
@@ -204,9 +204,9 @@ gdn2_status gdn2_chunk_fwd(const gdn2_desc *desc,
  * the process ends.  When the records of all ceil(T/64) chunks of every
  * chain do not fit there, the chunks are processed in consecutive windows
  * that do, the state carried from window to window in the same array
- * (more launches, the same arithmetic).  Each record takes 96.5 KiB and
+ * (more launches, the same arithmetic).  Each record takes 70.5 KiB and
  * each carried state 64 KiB: a request fits in one window up to
- * B*H*ceil(T/64) = 1358 records, in windows up to B*H = 816 chains; beyond
+ * B*H*ceil(T/64) = 1859 records, in windows up to B*H = 974 chains; beyond
  * both it returns GDN2_ERR_SCRATCH before anything is enqueued.  Requests without a two-pass
  * kernel run the single-pass kernels, which use no scratch.
  *

@@ -178,7 +178,7 @@ def segments(chains, nc):
 
 
 def split_bytes(B, H, T):
-    """Two-pass workspace: per (chain, chunk) a 96 KiB fp16 record and 128
+    """Two-pass workspace: per (chain, chunk) a 70 KiB fp16 record and 128
     fp32 chunk-end decays; with several segments per chain, two fp32 states
     per (chain, segment); each region 256-byte aligned."""
     a = lambda x: (x + 255) // 256 * 256
@@ -186,7 +186,7 @@ def split_bytes(B, H, T):
     n = B * H * nc
     ns = segments(B * H, nc)
     extra = 2 * a(B * H * ns * 128 * 128 * 4) if ns > 1 else 0
-    return a(n * 98304) + a(n * 512) + extra
+    return a(n * 71680) + a(n * 512) + extra
 
 
 def test_segment_rule():
@@ -348,7 +348,7 @@ def varlen_bytes(N, H, T):
     L = max(16, -(-H * ct // 128))
     long_max = -(-T // (64 * L))
     zb = (ct + long_max) // L + 1 + long_max
-    return (a(n * 98304) + a(n * 512) + a(N * 8) + a((N + 1) * 4) + a(nc * 8) + 4 * a((N + 1) * 4)
+    return (a(n * 71680) + a(n * 512) + a(N * 8) + a((N + 1) * 4) + a(nc * 8) + 4 * a((N + 1) * 4)
             + 2 * a(zb * H * 128 * 128 * 4))
 
 
@@ -448,9 +448,9 @@ def test_static_entry_point_checks(lib):
     assert fwd_static(lib, good(), o=Q + 16) == 5
     assert fwd_static(lib, good(), so=S0 + 64) == 5
     assert fwd_static(lib, good(seqlen=0), so=S0) == 0   # nothing to enqueue
-    # the 128 MiB scratch holds 1358 records of 96.5 KiB in one window, or
-    # one chunk per chain beside the carried 64 KiB states of up to 816
+    # the 128 MiB scratch holds 1859 records of 70.5 KiB in one window, or
+    # one chunk per chain beside the carried 64 KiB states of up to 974
     # chains; beyond both the check answers before any HIP call
-    assert fwd_static(lib, good(batch=1359, heads=1, seqlen=64)) == 8
-    assert fwd_static(lib, good(batch=817, heads=1, seqlen=128)) == 8
-    assert fwd_static(lib, good(batch=205, heads=4, seqlen=65)) == 8
+    assert fwd_static(lib, good(batch=1860, heads=1, seqlen=64)) == 8
+    assert fwd_static(lib, good(batch=975, heads=1, seqlen=128)) == 8
+    assert fwd_static(lib, good(batch=244, heads=4, seqlen=65)) == 8

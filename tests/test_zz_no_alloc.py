@@ -36,8 +36,8 @@ def _both(w, inp, state0=True, state_out=True):
 
 
 def test_static_forward_equals_the_workspace_forward_two_calls():
-    # first call: the full GDN-2 workload (128 chains x 64 chunks: 790 MiB of
-    # records, so the static form runs 9-chunk windows, the state carried
+    # first call: the full GDN-2 workload (128 chains x 64 chunks: 564 MiB of
+    # records, so the static form runs 13-chunk windows, the state carried
     # between them); second call smaller (one window)
     w = W[2]
     o_ws, s_ws, o_st, s_st = _both(w, synth.make_inputs(w, wid=2))
@@ -51,7 +51,7 @@ def test_static_forward_equals_the_workspace_forward_two_calls():
 def test_static_forward_windows_without_state_tensors():
     # no initial state and no final state requested: the windows still carry
     # the state through the scratch
-    w = W[2].scaled(B=16, T=2048, H=16)   # 256 chains x 32 chunks: windows of 4
+    w = W[2].scaled(B=16, T=2048, H=16)   # 256 chains x 32 chunks: windows of 6
     o_ws, s_ws, o_st, s_st = _both(w, synth.make_inputs(w, seed=1202), state0=False, state_out=False)
     assert s_st is None and np.array_equal(o_ws, o_st)
 

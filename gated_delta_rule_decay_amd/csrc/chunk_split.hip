@@ -434,8 +434,8 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         }
         load_part<0, TIED, GK, VW, RAW>(R, a, pn, tid);
         load_part<1, TIED, GK, VW, RAW>(R, a, pn, tid);
-        // tied gates end the task soon after the U barrier (no Oe, G): the
-        // values go out here, so that they arrive before the next task needs them
+        // tied gates end the task soon after the U barrier: the values go
+        // out here, so that they arrive before the next task needs them
         if constexpr (TIED) load_part<2, TIED, GK, VW, RAW>(R, a, pn, tid);
 
         _Float16 *rec = w.frag + task * REC;
@@ -603,12 +603,13 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
 // Pass 2: the scan over chunks.  A workgroup of SCAN_W compute waves owns one
 // chain (or one segment of it, below) and SCAN_W value tiles (16 columns
 // each, one per wave); each wave keeps its 128 x 16 fp32 state slice in
-// accumulators.  Everything a chunk needs -- W, Qe, EtT (48 KiB, shared by
-// the waves), the workgroup's slices of G and Oe and e^gC -- is copied by the
-// memory unit straight into LDS (global_load_lds) one chunk ahead, into one
-// of two slots, by SCAN_P copy waves of the same workgroup, so the compute
-// waves never wait behind memory instructions; one barrier per chunk hands a
-// slot over.
+// accumulators.  Everything a chunk needs -- the record (untied gates: W,
+// Qe, EtT, Z^T and Y^T, 70 KiB shared by the waves; tied: W, Qbar, EtT, the
+// workgroup's D tiles and R), e^gC and, untied, the workgroup's 64 value
+// columns of the chunk -- is brought into LDS one chunk ahead, into one of
+// two slots, by SCAN_P copy waves of the same workgroup (buffer loads into
+// registers, then LDS stores), so the compute waves never wait behind
+// memory instructions; one barrier per chunk hands a slot over.
 //
 // Long sequences on few chains use the affine view of a chunk (the Gated
 // DeltaNet page, "What makes the architecture more than a recurrence": each

@@ -888,9 +888,10 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         }
         if constexpr (!TIED) {
             // values: lane (token pair pa, column group cg) of the 256 copy
-            // lanes loads tokens 2pa, 2pa+1, my columns 8cg..8cg+7 (rows past
+            // lanes loads tokens 2pa, 2pa+1, my columns 8cg..8cg+7, so that
+            // each load instruction reads eight whole 128-byte rows (rows past
             // the sequence read as zero)
-            const int idx = 64 * pw + lane, pa = idx & 31, cg = idx >> 5;
+            const int pa = 8 * pw + (lane >> 3), cg = lane & 7;
             const int rowk = static_cast<int>(a.H) * D;
             const auto rv = chain_rsrc(a.v, a, 0, h, tbase + static_cast<int64_t>(n) * C, D, 2, 64 * half, tlim);
 #pragma unroll
@@ -908,10 +909,11 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         }
         if constexpr (!TIED) {
             // values in fp16, [column][token pair] words: column 8cg+j of my
-            // two tokens in one word (the 32 lanes of a half-wave write 32
-            // consecutive words).  A value beyond fp16's range marks the
-            // chunk for the exact path (gm[D + pw] < 0).
-            const int idx = 64 * pw + lane, pa = idx & 31, cg = idx >> 5;
+            // two tokens in one word, at pair slot pa ^ 4cg (the XOR spreads
+            // the eight column groups of a half-wave over distinct banks).  A
+            // value beyond fp16's range marks the chunk for the exact path
+            // (gm[D + pw] < 0).
+            const int pa = 8 * pw + (lane >> 3), cg = lane & 7;
             uint32_t *vw = reinterpret_cast<uint32_t *>(fr + S_V);
             typedef _Float16 h2 __attribute__((ext_vector_type(2)));
             bool vbig = false;
@@ -921,7 +923,7 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
                 const float f0 = __uint_as_float((j & 1) ? (x0 & 0xffff0000u) : (x0 << 16));
                 const float f1 = __uint_as_float((j & 1) ? (x1 & 0xffff0000u) : (x1 << 16));
                 vbig |= !(fmaxf(fabsf(f0), fabsf(f1)) <= 65504.f);
-                vw[(8 * cg + j) * V_PW + pa] = __builtin_bit_cast(uint32_t, h2{(_Float16)f0, (_Float16)f1});
+                vw[(8 * cg + j) * V_PW + (pa ^ (4 * cg))] = __builtin_bit_cast(uint32_t, h2{(_Float16)f0, (_Float16)f1});
             }
             const bool anyv = __ballot(vbig) != 0;
             if (lane == 0) gm[D + pw] = anyv ? -1.f : 0.f;
@@ -969,10 +971,13 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
             h8 wq[2][2][4];
             read_wq(wq[0], 0);
             if constexpr (!TIED) {
-                const uint32_t *vw = reinterpret_cast<const uint32_t *>(fr + S_V) + (16 * wt + lr) * V_PW + 2 * lg;
+                // column c = 16wt+lr: token pairs 16kb+2lg, +1 and 16kb+8+2lg, +1
+                // at their slots (XOR with 4 (c / 8) keeps each pair adjacent)
+                const int c = 16 * wt + lr, sw = 4 * (c >> 3);
+                const uint32_t *vw = reinterpret_cast<const uint32_t *>(fr + S_V) + c * V_PW;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
-                    vfr[kb] = join(lds_ld<h4>(vw + 16 * kb), lds_ld<h4>(vw + 16 * kb + 8));
+                    vfr[kb] = join(lds_ld<h4>(vw + ((16 * kb + 2 * lg) ^ sw)), lds_ld<h4>(vw + ((16 * kb + 8 + 2 * lg) ^ sw)));
             }
             if (MODE == 0) {  // MODE 1 reads EtT where it is used (register budget of 12 waves)
 #pragma unroll

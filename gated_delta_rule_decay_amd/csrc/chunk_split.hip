@@ -857,9 +857,9 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     // Each wave moves 1 KiB of record per instruction (lane l -> bytes
     // 16l..16l+15); the values come as two rows of 8 columns per lane.
     typedef uint32_t u4v __attribute__((ext_vector_type(4)));
-    u4v cr[PIECES], vr[TIED ? 1 : 2];
+    u4v cr[PIECES];
     float cgam = 0.f;
-    auto load_regs = [&](int64_t task, int n, int pw) __attribute__((always_inline)) {
+    auto load_regs = [&](int64_t task, int pw) __attribute__((always_inline)) {
         // one buffer resource per record: every piece is the same lane offset
         // plus a uniform byte offset, so no per-piece address registers
         const auto rs = __builtin_amdgcn_make_buffer_rsrc(w.frag + task * REC, (short)0, static_cast<int>(REC * 2),
@@ -886,11 +886,17 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
                                       : 2 * static_cast<int>(OFF_Z) + (byte - 4 * 8192);
             cr[i] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, src, 0));
         }
+        // e^gC: copy waves 0,1 bring channels 0..127
+        if (pw < 2) cgam = w.gam[task * D + 64 * pw + lane];
+    };
+    // untied: the values of chunk n.  Lane (token pair pa, column group cg)
+    // of the 256 copy lanes loads tokens 2pa, 2pa+1, my columns 8cg..8cg+7,
+    // so that each load instruction reads eight whole 128-byte rows (rows
+    // past the sequence read as zero).  They are requested one chunk earlier
+    // than the record (their rows are scattered over the token axis, so they
+    // take longer to arrive).
+    auto load_vals = [&](int n, int pw, u4v (&vr)[2]) __attribute__((always_inline)) {
         if constexpr (!TIED) {
-            // values: lane (token pair pa, column group cg) of the 256 copy
-            // lanes loads tokens 2pa, 2pa+1, my columns 8cg..8cg+7, so that
-            // each load instruction reads eight whole 128-byte rows (rows past
-            // the sequence read as zero)
             const int pa = 8 * pw + (lane >> 3), cg = lane & 7;
             const int rowk = static_cast<int>(a.H) * D;
             const auto rv = chain_rsrc(a.v, a, 0, h, tbase + static_cast<int64_t>(n) * C, D, 2, 64 * half, tlim);
@@ -898,8 +904,6 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
             for (int i = 0; i < 2; ++i)
                 vr[i] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rv, ((2 * pa + i) * rowk + 8 * cg) * 2, 0, 0));
         }
-        // e^gC: copy waves 0,1 bring channels 0..127
-        if (pw < 2) cgam = w.gam[task * D + 64 * pw + lane];
     };
     auto store_regs = [&](_Float16 *fr, float *gm, int pw) __attribute__((always_inline)) {
 #pragma unroll
@@ -907,6 +911,9 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
             if (NPC % SCAN_P != 0 && i == PIECES - 1 && SCAN_P * i + pw >= NPC) break;
             *reinterpret_cast<u4v *>(reinterpret_cast<char *>(fr) + 1024 * (SCAN_P * i + pw) + 16 * lane) = cr[i];
         }
+        if (pw < 2) gm[64 * pw + lane] = cgam;
+    };
+    auto store_vals = [&](_Float16 *fr, float *gm, int pw, const u4v (&vr)[2]) __attribute__((always_inline)) {
         if constexpr (!TIED) {
             // values in fp16, [column][token pair] words: column 8cg+j of my
             // two tokens in one word, at pair slot pa ^ 4cg (the XOR spreads
@@ -928,7 +935,6 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
             const bool anyv = __ballot(vbig) != 0;
             if (lane == 0) gm[D + pw] = anyv ? -1.f : 0.f;
         }
-        if (pw < 2) gm[64 * pw + lane] = cgam;
     };
 
     // One chunk n on this wave, from slot (fr, gm).
@@ -1117,25 +1123,36 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     constexpr int LGKM0 = 15 | (7 << 4) | (3 << 14);  // s_waitcnt lgkmcnt(0), other counters untouched
     if (copier) {
         const int pw = wv - NCOMP;
+        u4v va[2], vb[2];  // values of the chunks one and two ahead of the record
         if (n0 < n1) {
-            load_regs(task0 + n0 * tstr, n0, pw);
+            load_regs(task0 + n0 * tstr, pw);
+            load_vals(n0, pw, va);
             store_regs(fr0, gm0, pw);
+            store_vals(fr0, gm0, pw, va);
         }
-        if (n0 + 1 < n1) load_regs(task0 + (n0 + 1) * tstr, n0 + 1, pw);
+        if (n0 + 1 < n1) {
+            load_regs(task0 + (n0 + 1) * tstr, pw);
+            load_vals(n0 + 1, pw, va);
+        }
+        if (n0 + 2 < n1) load_vals(n0 + 2, pw, vb);
         __builtin_amdgcn_s_waitcnt(LGKM0);
-#define GDN2_COPY_STEP(N, FRN, GMN)                                                \
+#define GDN2_COPY_STEP(N, FRN, GMN, VS)                                           \
         do {                                                                      \
             slot_barrier();                                                       \
-            if ((N) + 1 < n1) store_regs(FRN, GMN, pw);                           \
-            if ((N) + 2 < n1) load_regs(task0 + ((N) + 2) * tstr, (N) + 2, pw);    \
+            if ((N) + 1 < n1) {                                                   \
+                store_regs(FRN, GMN, pw);                                         \
+                store_vals(FRN, GMN, pw, VS);                                     \
+            }                                                                     \
+            if ((N) + 2 < n1) load_regs(task0 + ((N) + 2) * tstr, pw);            \
+            if ((N) + 3 < n1) load_vals((N) + 3, pw, VS);                         \
             __builtin_amdgcn_s_waitcnt(LGKM0);                                    \
         } while (0)
         int n = n0;
         for (; n + 1 < n1; n += 2) {
-            GDN2_COPY_STEP(n, fr1, gm1);
-            GDN2_COPY_STEP(n + 1, fr0, gm0);
+            GDN2_COPY_STEP(n, fr1, gm1, va);
+            GDN2_COPY_STEP(n + 1, fr0, gm0, vb);
         }
-        if (n < n1) GDN2_COPY_STEP(n, fr1, gm1);
+        if (n < n1) GDN2_COPY_STEP(n, fr1, gm1, va);
 #undef GDN2_COPY_STEP
     } else {
         const float *init = nullptr;

@@ -202,7 +202,9 @@ __device__ __forceinline__ void load_part(Raw<GK, 2> &R, const ChunkArgs &a, con
     if constexpr (PART == 1) gates(R.eb, a.eb);
     if constexpr (PART == 2) {
         if (!TIED) gates(R.wr, a.wr);
-        const int tp = tid & 31, piece = tid >> 5;
+        // thread (token pair tp, 8-column piece): the 16 threads of a pair
+        // read its two whole 256-byte rows
+        const int tp = tid >> 4, piece = tid & 15;
         if constexpr (TIED) {  // untied gates: the scan reads the values
             const auto rv = chain_rsrc(a.v, a, b, h, t0, D, 2, 0, tl);
 #pragma unroll
@@ -248,6 +250,12 @@ __device__ __forceinline__ void load_part(Raw<GK, 2> &R, const ChunkArgs &a, con
         }
     }
 }
+
+// Token position swizzle of the values' LDS copy [j][s] (tied gates): value
+// column j keeps token s at s ^ vswz(j).  The XOR moves whole 8-token groups,
+// so the 4- and 8-token reads stay contiguous, and it spreads the columns a
+// half-wave writes (16 pieces of 8 columns, two token pairs) over 16 banks.
+__device__ __forceinline__ int vswz(int j) { return 8 * ((j >> 3) & 7); }
 
 // Row block rt of a C x C fp16 matrix (pitch SP) as a 16x16x32 A operand
 // over token block ks, token slots permuted as in the record (so that it
@@ -359,10 +367,10 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         const int seg = tl >> 5, cq = tl & 31;
 
         // ---- values [j][s] (tied gates): each thread packs its two tokens of
-        //      one column into a 32-bit word (a wave's writes then hit 64
-        //      distinct banks); segment log2-decay totals
+        //      one column into a 32-bit word, stored at token position
+        //      s ^ vswz(j) (see vswz); segment log2-decay totals
         if constexpr (TIED) {
-            const int tp = tl & 31, piece = tl >> 5;
+            const int tp = tl >> 4, piece = tl & 15;
             const uint32_t r0[4] = {R.v[0].x, R.v[0].y, R.v[0].z, R.v[0].w};
             const uint32_t r1[4] = {R.v[1].x, R.v[1].y, R.v[1].z, R.v[1].w};
             // the value-write form writes w .* v: gate of token i, column 2e + s
@@ -386,8 +394,8 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 const _Float16 b0 = (_Float16)(__uint_as_float(r0[e] & 0xffff0000u) * wg(0, e, 1));
                 const _Float16 b1 = (_Float16)(__uint_as_float(r1[e] & 0xffff0000u) * wg(1, e, 1));
                 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-                lds_st<h2>(&S.v16[(8 * piece + 2 * e) * SP + 2 * tp], h2{a0, a1});
-                lds_st<h2>(&S.v16[(8 * piece + 2 * e + 1) * SP + 2 * tp], h2{b0, b1});
+                lds_st<h2>(&S.v16[(8 * piece + 2 * e) * SP + (2 * tp ^ vswz(8 * piece))], h2{a0, a1});
+                lds_st<h2>(&S.v16[(8 * piece + 2 * e + 1) * SP + (2 * tp ^ vswz(8 * piece))], h2{b0, b1});
             }
         }
         f4 g[RPS];
@@ -455,7 +463,8 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 // ---- (1) value tile ct = wv: Y = Bm V, U = Tm Y --------------
                 // vb: V[:, ct] as a B operand, natural token order
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) vb[ks] = lds_ld<h8>(&S.v16[(16 * ct + lr) * SP + 32 * ks + 8 * lg]);
+                for (int ks = 0; ks < 2; ++ks)
+                    vb[ks] = lds_ld<h8>(&S.v16[(16 * ct + lr) * SP + ((32 * ks + 8 * lg) ^ vswz(16 * ct + lr))]);
                 f4 y[4];
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
@@ -522,7 +531,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                 f4 dd[4];
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
-                    dd[rt] = to_f4(lds_ld<h4>(&S.v16[(16 * ct + lr) * SP + 16 * rt + 4 * lg])) - uacc[rt];
+                    dd[rt] = to_f4(lds_ld<h4>(&S.v16[(16 * ct + lr) * SP + ((16 * rt + 4 * lg) ^ vswz(16 * ct + lr))])) - uacc[rt];
                     big |= out_of_range(dd[rt]);
                 }
 #pragma unroll

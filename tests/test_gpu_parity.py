@@ -474,6 +474,24 @@ def test_header_bound_values_and_state(ws):
     assert np.abs(S).max() < 2 ** 15
 
 
+@pytest.mark.parametrize("tied", [False, True])
+def test_values_past_fp16_run_exactly(tied):
+    # values past fp16's range on three tokens of the second chunk (beyond the
+    # stated bound |v| < 2^15): untied, the two-pass scan stages the values
+    # itself and marks such a chunk for the exact recurrence; tied, the prep
+    # pass's D leaves the fp16 range.  Either way the results stay finite and
+    # within the bf16 bar (the state then exceeds the fp16 bound, so the later
+    # chunks run exactly too)
+    w, inp = _bf16_case(49, T=200, tied=tied)
+    bits = inp["v_bf16"].astype(np.int32)
+    sub = bits[:, 70:73]
+    bits[:, 70:73] = np.where((sub & 0x7fff) != 0, sub + (17 << 7), sub)
+    inp["v_bf16"] = bits.astype(np.uint16)
+    inp["v"][:, 70:73] *= np.float32(2.0 ** 17)
+    assert np.abs(inp["v"]).max() > 65504
+    _check(w, inp, 64, ws=True)
+
+
 # ---- the two-level scan: long sequences on few chains ----------------------
 # Few (batch, head) chains with many chunks are cut into segments (see
 # tests/test_abi.py::segments): 33 chunks -> 2 segments, 48 -> 3, 100 -> 6,

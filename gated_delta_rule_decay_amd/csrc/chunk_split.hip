@@ -460,7 +460,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             // LDS writes, so the compiler may issue them early.
 
             if constexpr (TIED) {
-                // ---- (1) value tile ct = wv: Y = Bm V, U = Tm Y --------------
+                // ---- (1) value tile ct = wv: Bm V, then U = Tm (Bm V) --------
                 // vb: V[:, ct] as a B operand, natural token order
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)

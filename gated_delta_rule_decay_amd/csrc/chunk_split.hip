@@ -81,6 +81,13 @@ constexpr int64_t REC = 35840;
 constexpr int64_t OFF_D = 24576;  // D in the scan's W S tile layout: [value tile][tile pair][lane][8]
 constexpr int64_t OFF_R = 32768;  // R as B operands of R X (perm_frag order), fragment n = (rt, ks)
 constexpr int R_FRAGS = 6;        // (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+// Tied gates outside the value-write form: D = V - Tm A V = Tm V (since
+// Tm (I + A) = I), so the scan forms D from the values with the six nonzero
+// 16 x 32 fragments of Tm (A operands, perm_frag order), and the record holds
+// W^T, Qbar^T, Etil^T and the Tm and R fragments (60 KiB).  The value-write
+// form keeps D in the record (its values carry the write gate).
+constexpr int64_t OFF_TMF = 24576;
+constexpr int64_t OFF_RTM = 27648;
 // the ten lower 16 x 16 tiles (jt, st) of T2 = Tm Bm, in the order the
 // prep pass's waves take them
 __constant__ int kT2J[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
@@ -205,7 +212,7 @@ __device__ __forceinline__ void load_part(Raw<GK, 2> &R, const ChunkArgs &a, con
         // thread (token pair tp, 8-column piece): the 16 threads of a pair
         // read its two whole 256-byte rows
         const int tp = tid >> 4, piece = tid & 15;
-        if constexpr (TIED) {  // untied gates: the scan reads the values
+        if constexpr (VW) {  // otherwise the scan reads the values
             const auto rv = chain_rsrc(a.v, a, b, h, t0, D, 2, 0, tl);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
@@ -366,10 +373,10 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         const int lane = tl & 63, lr = lane & 15, lg = lane >> 4;
         const int seg = tl >> 5, cq = tl & 31;
 
-        // ---- values [j][s] (tied gates): each thread packs its two tokens of
-        //      one column into a 32-bit word, stored at token position
-        //      s ^ vswz(j) (see vswz); segment log2-decay totals
-        if constexpr (TIED) {
+        // ---- values [j][s] (the value-write form): each thread packs its two
+        //      tokens of one column into a 32-bit word, stored at token
+        //      position s ^ vswz(j) (see vswz); segment log2-decay totals
+        if constexpr (VW) {
             const int tp = tl >> 4, piece = tl & 15;
             const uint32_t r0[4] = {R.v[0].x, R.v[0].y, R.v[0].z, R.v[0].w};
             const uint32_t r1[4] = {R.v[1].x, R.v[1].y, R.v[1].z, R.v[1].w};
@@ -442,9 +449,9 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
         }
         load_part<0, TIED, GK, VW, RAW>(R, a, pn, tid);
         load_part<1, TIED, GK, VW, RAW>(R, a, pn, tid);
-        // tied gates end the task soon after the U barrier: the values go
-        // out here, so that they arrive before the next task needs them
-        if constexpr (TIED) load_part<2, TIED, GK, VW, RAW>(R, a, pn, tid);
+        // the value-write form ends the task soon after the U barrier: its
+        // values go out here, so that they arrive before the next task needs them
+        if constexpr (VW) load_part<2, TIED, GK, VW, RAW>(R, a, pn, tid);
 
         _Float16 *rec = w.frag + task * REC;
         bool big = false;
@@ -459,7 +466,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
             // into inf or NaN.  All LDS reads of this phase come before its
             // LDS writes, so the compiler may issue them early.
 
-            if constexpr (TIED) {
+            if constexpr (VW) {
                 // ---- (1) value tile ct = wv: Bm V, then U = Tm (Bm V) --------
                 // vb: V[:, ct] as a B operand, natural token order
 #pragma unroll
@@ -481,7 +488,7 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                     if (rt >= 2) uacc[rt] = mfma32(perm_frag(S.t16, rt, 1, lr, lg), yb1, uacc[rt]);
                     big |= out_of_range(uacc[rt]);
                 }
-            } else {
+            } else if constexpr (!TIED) {
                 // ---- (1) T2 = Tm Bm, the ten lower 16 x 16 tiles (jt, st) over
                 //      the waves (wave u: tile u, waves 0, 1 also tile u + 8),
                 //      stored transposed ([s][j]) for the Z and Y products;
@@ -524,8 +531,22 @@ __global__ void __launch_bounds__(NTH) chunk_prep_kernel(ChunkArgs a, SplitWs w,
                     *reinterpret_cast<h8 *>(rec + OFF_E + ((it * 2 + kb) * 64 + lane) * 8) = ef[kb];
                 }
             }
-            if constexpr (TIED) {
-                // the slim record: D = V - U of value tile ct, in the layout of
+            if constexpr (TIED && !VW) {
+                // the Tm and R fragments (waves 0..5: fragment wv = (rt, kb)),
+                // range-checked as stored
+                if (wv < R_FRAGS) {
+                    const int rt = wv < 2 ? wv : (wv + 2) / 2, ks = wv < 2 ? 0 : wv & 1;
+                    const h8 tf = perm_frag(S.t16, rt, ks, lr, lg);
+                    const h8 rf = perm_frag(S.r16, rt, ks, lr, lg);
+                    big |= out_of_range(f4{(float)tf[0], (float)tf[1], (float)tf[2], (float)tf[3]}) ||
+                           out_of_range(f4{(float)tf[4], (float)tf[5], (float)tf[6], (float)tf[7]}) ||
+                           out_of_range(f4{(float)rf[0], (float)rf[1], (float)rf[2], (float)rf[3]}) ||
+                           out_of_range(f4{(float)rf[4], (float)rf[5], (float)rf[6], (float)rf[7]});
+                    *reinterpret_cast<h8 *>(rec + OFF_TMF + (wv * 64 + lane) * 8) = tf;
+                    *reinterpret_cast<h8 *>(rec + OFF_RTM + (wv * 64 + lane) * 8) = rf;
+                }
+            } else if constexpr (TIED) {
+                // the value-write record: D = V - U of value tile ct, in the layout of
                 // the scan's W S tiles (token 16 rt + 4 lg + e, column 16 ct + lr),
                 // and R fragment wv as a B operand
                 f4 dd[4];
@@ -654,6 +675,10 @@ constexpr int SLOT_D = SCAN_W * 2 * 512;
 constexpr int SLOT_R = 4096;
 constexpr int SLOT_HT = SLOT_F + SLOT_D + SLOT_R;
 constexpr int SLOT_AT = 2 * 8192 + SLOT_D;
+// tied gates outside the value-write form: W | Qbar | EtT and the Tm and R
+// fragments (MODE 1: W | EtT | the Tm fragments), then the values
+constexpr int SLOT_HM = SLOT_F + 2 * R_FRAGS * 512;
+constexpr int SLOT_AM = 2 * 8192 + R_FRAGS * 512;
 static_assert(R_FRAGS * 512 <= SLOT_R, "R fragments fit their slot part");
 static_assert(SLOT_HT * 2 % (1024 * SCAN_P) == 0 && SLOT_AT * 2 % (1024 * SCAN_P) == 0,
               "slot copies must tile the copy waves");
@@ -783,12 +808,16 @@ __global__ void __launch_bounds__(scan_threads(MODE))
 chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     constexpr bool WITH_O = MODE == 0;
     constexpr int NCOMP = (MODE ? 2 : 1) * SCAN_W;
-    // the record part of a slot, then (untied) the chunk's values
-    constexpr int SREC = TIED ? (MODE ? SLOT_AT : SLOT_HT) : (MODE ? SLOT_UA : SLOT_U);
-    constexpr int SH = SREC + (TIED ? 0 : SLOT_V);
+    // the record part of a slot, then (all but the value-write form) the
+    // chunk's values
+    constexpr bool SV = !VW;  // the scan reads the values
+    constexpr int SREC = VW ? (MODE ? SLOT_AT : SLOT_HT) : TIED ? (MODE ? SLOT_AM : SLOT_HM) : (MODE ? SLOT_UA : SLOT_U);
+    constexpr int SH = SREC + (SV ? SLOT_V : 0);
     constexpr int S_Q = 8192, S_E = MODE ? 8192 : 16384;
-    constexpr int S_Z = MODE ? 16384 : 24576, S_Y = 32768, S_V = SREC;  // untied: Z^T, Y^T, values
-    constexpr int S_D = MODE ? 16384 : SLOT_F, S_R = SLOT_F + SLOT_D;  // the slim record: my D tiles, the R fragments
+    constexpr int S_Z = MODE ? 16384 : 24576, S_Y = 32768, S_V = SREC;  // untied: Z^T, Y^T; the values
+    constexpr int S_T = MODE ? 16384 : SLOT_F;                          // tied: the Tm fragments
+    constexpr int S_D = MODE ? 16384 : SLOT_F;                          // value-write: my D tiles
+    constexpr int S_R = VW ? SLOT_F + SLOT_D : SLOT_F + R_FRAGS * 512;  // tied: the R fragments
     constexpr int NPC = SREC * 2 / 1024;                   // 1 KiB pieces of the record part
     constexpr int PIECES = (NPC + SCAN_P - 1) / SCAN_P;    // per copy wave (the last round may be partial)
     // two distinct slots (distinct objects, so the compiler can tell the slot
@@ -879,20 +908,20 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
             if (NPC % SCAN_P != 0 && i == PIECES - 1 && SCAN_P * i + pw >= NPC) break;  // (wave-uniform)
             const int byte = 1024 * (SCAN_P * i + pw);  // my 1 KiB block of the slot
             int src;
-            if (TIED && MODE == 0)
+            if (VW && MODE == 0)
                 src = byte < 2 * SLOT_F ? byte
                     : byte < 2 * (SLOT_F + SLOT_D) ? od + (byte - 2 * SLOT_F)
                                                    : 2 * static_cast<int>(OFF_R) + (byte - 2 * (SLOT_F + SLOT_D));
-            else if (TIED)
+            else if (VW)
                 src = byte < 2 * 8192 ? byte
                     : byte < 4 * 8192 ? 2 * static_cast<int>(OFF_E) + (byte - 2 * 8192)
                                       : od + (byte - 4 * 8192);
             else if (MODE == 0)
-                src = byte;
+                src = byte;  // a prefix of the record
             else
                 src = byte < 2 * 8192 ? byte
                     : byte < 4 * 8192 ? 2 * static_cast<int>(OFF_E) + (byte - 2 * 8192)
-                                      : 2 * static_cast<int>(OFF_Z) + (byte - 4 * 8192);
+                                      : 2 * static_cast<int>(TIED ? OFF_TMF : OFF_Z) + (byte - 4 * 8192);
             cr[i] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(rs, 16 * lane, src, 0));
         }
         // e^gC: copy waves 0,1 bring channels 0..127
@@ -905,7 +934,7 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
     // than the record (their rows are scattered over the token axis, so they
     // take longer to arrive).
     auto load_vals = [&](int n, int pw, u4v (&vr)[2]) __attribute__((always_inline)) {
-        if constexpr (!TIED) {
+        if constexpr (SV) {
             const int pa = 8 * pw + (lane >> 3), cg = lane & 7;
             const int rowk = static_cast<int>(a.H) * D;
             const auto rv = chain_rsrc(a.v, a, 0, h, tbase + static_cast<int64_t>(n) * C, D, 2, 64 * half, tlim);
@@ -923,7 +952,7 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         if (pw < 2) gm[64 * pw + lane] = cgam;
     };
     auto store_vals = [&](_Float16 *fr, float *gm, int pw, const u4v (&vr)[2]) __attribute__((always_inline)) {
-        if constexpr (!TIED) {
+        if constexpr (SV) {
             // values in fp16, [column][token pair] words: column 8cg+j of my
             // two tokens in one word, at pair slot pa ^ 4cg (the XOR spreads
             // the eight column groups of a half-wave over distinct banks).  A
@@ -960,7 +989,7 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         for (int it = 0; it < 8; ++it)
             big |= !(fmaxf(fmaxf(fabsf(sacc[it][0]), fabsf(sacc[it][1])), fmaxf(fabsf(sacc[it][2]), fabsf(sacc[it][3]))) <= MAX_STATE);
         bool bad = gm[0] < 0.f || __ballot(big) != 0;  // chunk marked for the exact path
-        if constexpr (!TIED) {
+        if constexpr (SV) {
             const f4 vf = *reinterpret_cast<const f4 *>(&gm[D]);  // the copy waves' value checks
             bad = bad || fminf(fminf(vf[0], vf[1]), fminf(vf[2], vf[3])) < 0.f;
         }
@@ -970,6 +999,7 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
         // record's permuted slot order -- the B operand of Z^T V and the A
         // operand of V^T Y^T
         h8 vfr[2];
+        f4 dv[4];  // tied gates outside the value-write form: D = Tm V
         big = false;
         if (!bad) {
             // Fragments are read from LDS ahead of use (W/Qe of the next row
@@ -985,7 +1015,7 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
             };
             h8 wq[2][2][4];
             read_wq(wq[0], 0);
-            if constexpr (!TIED) {
+            if constexpr (SV) {
                 // column c = 16wt+lr: token pairs 16kb+2lg, +1 and 16kb+8+2lg, +1
                 // at their slots (XOR with 4 (c / 8) keeps each pair adjacent)
                 const int c = 16 * wt + lr, sw = 4 * (c >> 3);
@@ -999,6 +1029,21 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
                 for (int it = 0; it < 8; ++it)
 #pragma unroll
                     for (int k2 = 0; k2 < 2; ++k2) ef[it][k2] = *reinterpret_cast<const h8 *>(fr + S_E + ((it * 2 + k2) * 64 + lane) * 8);
+            }
+            // tied gates: D = Tm V, token tile rt over the value blocks kb <=
+            // rt / 2 (the columns of F take none), ahead of the state products
+            if constexpr (TIED && !VW) {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) dv[rt] = splat(0.f);
+                if (!frun) {
+                    h8 tf[R_FRAGS];
+#pragma unroll
+                    for (int m = 0; m < R_FRAGS; ++m) tf[m] = *reinterpret_cast<const h8 *>(fr + S_T + (m * 64 + lane) * 8);
+#pragma unroll
+                    for (int rt = 0; rt < 4; ++rt) dv[rt] = mfma32(tf[rt < 2 ? rt : 2 * rt - 2], vfr[0], dv[rt]);
+#pragma unroll
+                    for (int rt = 2; rt < 4; ++rt) dv[rt] = mfma32(tf[2 * rt - 1], vfr[1], dv[rt]);
+                }
             }
             // untied: O^T starts from Oe^T = V^T Y^T (Y lower triangular: token
             // block rt takes the value blocks kb <= rt / 2)
@@ -1036,18 +1081,24 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // the slim record: X = D - W S (the columns of F: -W S), the B operand
-        // of the state update and, with R, the output's term R X
+        // tied gates: X = D - W S (the columns of F: -W S), the B operand of
+        // the state update and, with R, the output's term R X; D = Tm V
+        // (the value-write form: D from the record)
         h8 xb[2];
-        const float gsel = frun ? 0.f : 1.f;
         if (TIED && !bad) {
-            const _Float16 *fd = fr + S_D + wt * 2 * 512;
             f4 x[4];
+            if constexpr (VW) {
+                const float gsel = frun ? 0.f : 1.f;
+                const _Float16 *fd = fr + S_D + wt * 2 * 512;
 #pragma unroll
-            for (int rp = 0; rp < 2; ++rp) {
-                const h8 d2 = *reinterpret_cast<const h8 *>(fd + (rp * 64 + lane) * 8);
-                x[2 * rp] = gsel * f4{(float)d2[0], (float)d2[1], (float)d2[2], (float)d2[3]} - p1[2 * rp];
-                x[2 * rp + 1] = gsel * f4{(float)d2[4], (float)d2[5], (float)d2[6], (float)d2[7]} - p1[2 * rp + 1];
+                for (int rp = 0; rp < 2; ++rp) {
+                    const h8 d2 = *reinterpret_cast<const h8 *>(fd + (rp * 64 + lane) * 8);
+                    x[2 * rp] = gsel * f4{(float)d2[0], (float)d2[1], (float)d2[2], (float)d2[3]} - p1[2 * rp];
+                    x[2 * rp + 1] = gsel * f4{(float)d2[4], (float)d2[5], (float)d2[6], (float)d2[7]} - p1[2 * rp + 1];
+                }
+            } else {
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt) x[rt] = dv[rt] - p1[rt];
             }
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) big |= out_of_range(x[rt]);

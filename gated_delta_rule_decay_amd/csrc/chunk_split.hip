@@ -1226,6 +1226,10 @@ chunk_scan_kernel(ChunkArgs a, SplitWs w, int nc, ScanPlan sp, int xcd_map) {
                 sacc[it][e] = init ? init[c * D + v] : (frun && c == v) ? 1.f : 0.f;
                 if (MODE == 1 && !frun && seg == 0) sp.xs[xbase + c * D + v] = sacc[it][e];
             }
+        // the initial state is in before the loop: a load still pending at the
+        // loop's entry would make the compiler wait on the vector-memory
+        // counter at every chunk, which then also waits for the output stores
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         int n = n0;
         for (; n + 1 < n1; n += 2) {
             slot_barrier();

@@ -152,12 +152,23 @@ struct TaskPos {
 // for packed sequences chunk-major (task = chunk * H + head, chunks of all
 // sequences in order), placed by the chunk table.  32-bit division (the task
 // count is checked to fit on the host).
+// One chunk-table entry through the scalar data cache (the index is the
+// same for the whole wave).  A vector load here would be waited for with the
+// vector-memory counter, which also waits for the previous task's record
+// stores; the scalar load is waited for, in the same asm block, on the
+// counter of LDS and scalar loads alone.
+__device__ __forceinline__ int2 table_entry(const int2 *p) {
+    uint64_t r;
+    asm volatile("s_load_dwordx2 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(r) : "s"(p) : "memory");
+    return int2{static_cast<int>(static_cast<uint32_t>(r)), static_cast<int>(static_cast<uint32_t>(r >> 32))};
+}
+
 __device__ __forceinline__ TaskPos task_pos(const ChunkArgs &a, const SplitWs &w, int64_t task, int nc) {
     const uint32_t t = static_cast<uint32_t>(task), H = static_cast<uint32_t>(a.H);
     TaskPos p;
     if (a.cu) {
         const uint32_t gc = t / H;
-        const int2 e = w.vtab[gc];
+        const int2 e = table_entry(w.vtab + gc);
         p.h = t - gc * H;
         p.t0 = e.x;
         p.tlim = e.y;

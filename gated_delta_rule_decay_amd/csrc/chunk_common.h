@@ -372,11 +372,19 @@ __device__ __forceinline__ void factored_operands(SM &S, const Raw<GK, NV> &R, f
         g[i] += base;
         const f4 x = g[i] - gmv;
         f4 e1, e2;
+        if constexpr (!decay_key(GK)) {
+            // one decay per token-head: the running sums, and so the four
+            // channels' factors, are equal (the same values, summed alike)
+            bad |= !(fabsf(x[0]) <= MAX_EXP2);
+            e1 = splat(__builtin_amdgcn_exp2f(x[0]));
+            e2 = splat(__builtin_amdgcn_exp2f(-x[0]));
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            bad |= !(fabsf(x[j]) <= MAX_EXP2);
-            e1[j] = __builtin_amdgcn_exp2f(x[j]);
-            e2[j] = __builtin_amdgcn_exp2f(-x[j]);
+            for (int j = 0; j < 4; ++j) {
+                bad |= !(fabsf(x[j]) <= MAX_EXP2);
+                e1[j] = __builtin_amdgcn_exp2f(x[j]);
+                e2[j] = __builtin_amdgcn_exp2f(-x[j]);
+            }
         }
         f4 kraw = bf16x4_to_f4(R.k[i]);
         f4 qraw = bf16x4_to_f4(R.q[i]);

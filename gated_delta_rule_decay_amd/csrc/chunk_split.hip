@@ -73,11 +73,12 @@ constexpr int64_t OFF_E = 16384;
 constexpr int64_t OFF_Z = 24576;
 constexpr int64_t OFF_Y = 32768;
 constexpr int64_t REC = 35840;
-// Tied gates (u = e, so Bm = A and P = R; also the value-write form) keep a
-// record of the same size: with D = V - U, G = Etil^T D and Oe = R D, so the
-// scan forms both from D and R itself and the record holds W^T, Qbar^T (the
-// scan adds R (D - W S) to Qbar S), Etil^T, D and the six nonzero fragments
-// of R, and the scan reads no values.
+// Tied gates (u = e, so Bm = A and P = R; also the value-write form): with
+// D = V - U, G = Etil^T D and Oe = R D, so the scan forms both from D and R
+// itself.  The value-write form's record holds W^T, Qbar^T (the scan adds
+// R (D - W S) to Qbar S), Etil^T, D and the six nonzero fragments of R (70
+// KiB), and its scan reads no values; other tied gates keep Tm in place of
+// D (below).
 constexpr int64_t OFF_D = 24576;  // D in the scan's W S tile layout: [value tile][tile pair][lane][8]
 constexpr int64_t OFF_R = 32768;  // R as B operands of R X (perm_frag order), fragment n = (rt, ks)
 constexpr int R_FRAGS = 6;        // (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
